@@ -1,0 +1,688 @@
+/*
+ * oracle.c -- plain, slow fp64 CPU reference for block-sparse causal attention
+ * with learned block selection (block summaries -> scores -> optional softmax
+ * log gate -> top-K -> exact softmax attention -> backward incl. gate grad).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark do.  It shares no code, header, table or helper with the HIP
+ * library: it decodes its own inputs, rounds with its own routines and
+ * follows the definitions below loop by loop.
+ *
+ * Sources (pages of the reference, cited by title and section):
+ *  [SAS]  "SAS: Simple Attention Sparsification via End-to-End Optimization of
+ *         Context Ranking" (review page).  Background §3 Eq. 1-3 (attention,
+ *         block-sparse attention, C = n/b blocks + selector + top-K);
+ *         §4.1 Eq. 4 (historical set H, current block B0 with gate 1);
+ *         §4.2.2 Eq. 5 (inner-gate gradient), softmax gate
+ *         log g = s - LSE(s); §4.3 Eq. 9 (log-gate bias inside the softmax);
+ *         Alg. 1 / Alg. 2 and the worked example (n=256, b=64, K=2).
+ *  [FS]   "FreeSolo ... zero-shot retrieval up to 64x the training length"
+ *         (review page), section "How it works": cells of s tokens, mean key,
+ *         centre position, max key norm, query-block prefix of B=128,
+ *         r_ic = q_i.kbar_c/sqrt(d) + lambda_h a_c erf((i-p_c)/(2 sigma_h)),
+ *         per-query top-K cells read with one softmax, sliding-window branch
+ *         of w tokens, per-head alpha_h mix.
+ *  [MONO] "Monodratic claims learned routing ..." (news page): guaranteed
+ *         local block + exact causal softmax over the selected set.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - 1/sqrt(d) scaling of every dot product (stated only on [FS]).
+ *  - n context positions form C historical blocks; the query sits in the
+ *    current block B0 = floor(i/b); candidates are c < floor(i/b) [SAS].
+ *    [FS] candidates are cells fully before the query block:
+ *    (c+1) s <= B floor(i/B).
+ *  - GQA: with share_group=1 one selection per kv head from the mean of
+ *    its G query heads (score = mean of the per-head scores).
+ *  - Gate LSE runs over ALL candidates (the worked example normalises over
+ *    all four blocks, then biases the two chosen ones).
+ *  - Ties: higher score first, lower block index wins; indices are emitted
+ *    in ascending order, -1 padded; K_eff = min(K, #candidates).
+ *  - Summaries: exact mean rounded to nearest-even in the key dtype;
+ *    a_c = max over the block of the L2 norm, rounded to fp32;
+ *    p_c = c b + (b-1)/2.
+ *  - Mix: o = alpha_h o_L + (1 - alpha_h) o_S, o_L = 0 when no cell exists.
+ *  - Backward: dS_ij = p_ij (do_i.v_j - do_i.o_i); dg_m = sum_{j in B_m}
+ *    dS_ij / g_m, summed over the query heads sharing the gate.
+ *
+ * Layouts (all row-major, contiguous):
+ *   q [B, Hq, nq, d], k/v [B, Hkv, L, d], kbar [B, Hkv, Ccap, d],
+ *   max_norm [B, Hkv, Ccap], centre [Ccap], idx/logg [B, Hsel, nq, K].
+ *   dtype 0 = fp32, 1 = bf16 (raw uint16 bit patterns).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <fenv.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+/* ---------------------------------------------------------------- decode */
+
+static double orc_bf16_to_double(uint16_t h)
+{
+    uint32_t bits = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static double orc_load(const void *p, int dtype, int64_t i)
+{
+    if (dtype == ORC_BF16)
+        return orc_bf16_to_double(((const uint16_t *)p)[i]);
+    return (double)((const float *)p)[i];
+}
+
+/* Round a double to the nearest bf16 (ties to even), directly from the
+ * double: quantum = 2^(e-8) for x = m 2^e, m in [0.5, 1), floored at the
+ * bf16 subnormal spacing 2^-133.  The rounded value is exact in fp32. */
+static uint16_t orc_double_to_bf16_rne(double x)
+{
+    if (x == 0.0) {
+        return signbit(x) ? 0x8000u : 0u;
+    }
+    int e;
+    (void)frexp(x, &e);
+    int qexp = e - 8;
+    if (qexp < -133)
+        qexp = -133;
+    double scaled = ldexp(x, -qexp);          /* exact: power-of-two scale */
+    double r = nearbyint(scaled);             /* ties-to-even (default mode) */
+    double v = ldexp(r, qexp);
+    float f = (float)v;                       /* exact: v has <= 8 bits */
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    return (uint16_t)(bits >> 16);
+}
+
+static void orc_store_key_dtype(void *p, int dtype, int64_t i, double x)
+{
+    if (dtype == ORC_BF16)
+        ((uint16_t *)p)[i] = orc_double_to_bf16_rne(x);
+    else
+        ((float *)p)[i] = (float)x;           /* C conversion rounds to nearest even */
+}
+
+/* Exposed so the tests can pin the rounding against known bit patterns. */
+uint16_t orc_round_bf16(double x) { return orc_double_to_bf16_rne(x); }
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------ a1: summaries */
+/*
+ * [SAS] §3 Eq. 3 partitions the context into blocks of b tokens and the
+ * selector reads a pooled key summary of each; [FS] "How it works" names the
+ * three cell summaries: mean key, centre position, max key norm.
+ * Summarises blocks c in [0, nblocks) (each must be full: (c+1) b <= L).
+ */
+void orc_block_summaries(const void *k, int dtype, int B, int Hkv, int64_t L,
+                         int d, int b, int64_t nblocks, int64_t Ccap,
+                         void *kbar, float *max_norm, float *centre)
+{
+    int64_t bh;
+#pragma omp parallel for schedule(dynamic)
+    for (bh = 0; bh < (int64_t)B * Hkv; ++bh) {
+        const int64_t kbase = bh * L * d;
+        for (int64_t c = 0; c < nblocks; ++c) {
+            /* mean key: exact fp64 sum, divided by b (a power of two) */
+            for (int e = 0; e < d; ++e) {
+                double sum = 0.0;
+                for (int j = 0; j < b; ++j)
+                    sum += orc_load(k, dtype, kbase + (c * b + j) * (int64_t)d + e);
+                orc_store_key_dtype(kbar, dtype, (bh * Ccap + c) * (int64_t)d + e,
+                                    sum / (double)b);
+            }
+            /* max key norm over the block */
+            double best = 0.0;
+            for (int j = 0; j < b; ++j) {
+                double ss = 0.0;
+                for (int e = 0; e < d; ++e) {
+                    double x = orc_load(k, dtype, kbase + (c * b + j) * (int64_t)d + e);
+                    ss += x * x;
+                }
+                double nrm = sqrt(ss);
+                if (nrm > best)
+                    best = nrm;
+            }
+            max_norm[bh * Ccap + c] = (float)best;
+        }
+    }
+    if (centre) {
+        for (int64_t c = 0; c < nblocks; ++c)
+            centre[c] = (float)((double)c * b + (double)(b - 1) / 2.0);
+    }
+}
+
+/* ------------------------------------------------------ candidates */
+/* prefix_mode 0 = current block ([SAS] historical blocks before B0),
+ *             1 = query-block prefix ([FS] cells before the query block). */
+int64_t orc_num_candidates(int64_t i, int b, int prefix_mode, int qblock)
+{
+    if (prefix_mode == 0)
+        return i / b;
+    return (qblock * (i / qblock)) / b;
+}
+
+/* ---------------------------------------- a3 + a4: gate and top-K select */
+/*
+ * [SAS] Alg. 1 and the worked example: g = softmax(s) over the historical
+ * blocks, top-K of the scores, the chosen blocks get the bias log g.
+ * Selection order: higher score first, lower index on ties; the K chosen
+ * indices are emitted ascending, the remaining slots hold -1.
+ * Returns K_eff.  gap = s_(K) - s_(K+1) (INFINITY when nothing is left out).
+ * logg (nullable) receives s_c - LSE(s) for the chosen blocks, 0 in pads;
+ * lse_out (nullable) receives LSE over all candidates.
+ */
+int orc_select_from_scores(const double *s, int64_t ncand, int K, int gate,
+                           int32_t *idx, double *logg, double *gap,
+                           double *lse_out)
+{
+    int keff = (int)((int64_t)K < ncand ? K : ncand);
+    char *taken = (char *)calloc((size_t)(ncand > 0 ? ncand : 1), 1);
+    int32_t *chosen = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K > 0 ? K : 1));
+    double kth = INFINITY;
+    for (int t = 0; t < keff; ++t) {
+        int64_t best = -1;
+        for (int64_t c = 0; c < ncand; ++c) {
+            if (taken[c])
+                continue;
+            if (best < 0 || s[c] > s[best])   /* strict: lower index wins ties */
+                best = c;
+        }
+        taken[best] = 1;
+        chosen[t] = (int32_t)best;
+        kth = s[best];
+    }
+    /* best score left out */
+    double rest = -INFINITY;
+    for (int64_t c = 0; c < ncand; ++c)
+        if (!taken[c] && s[c] > rest)
+            rest = s[c];
+    if (gap)
+        *gap = (keff < ncand) ? (kth - rest) : INFINITY;
+
+    /* ascending order of the chosen indices (insertion sort) */
+    for (int a = 1; a < keff; ++a) {
+        int32_t x = chosen[a];
+        int bpos = a - 1;
+        while (bpos >= 0 && chosen[bpos] > x) {
+            chosen[bpos + 1] = chosen[bpos];
+            --bpos;
+        }
+        chosen[bpos + 1] = x;
+    }
+
+    /* log-sum-exp over every candidate (max-shifted) */
+    double lse = -INFINITY;
+    if (ncand > 0) {
+        double m = -INFINITY;
+        for (int64_t c = 0; c < ncand; ++c)
+            if (s[c] > m)
+                m = s[c];
+        double acc = 0.0;
+        for (int64_t c = 0; c < ncand; ++c)
+            acc += exp(s[c] - m);
+        lse = m + log(acc);
+    }
+    if (lse_out)
+        *lse_out = lse;
+
+    for (int t = 0; t < K; ++t) {
+        if (t < keff) {
+            idx[t] = chosen[t];
+            if (logg)
+                logg[t] = gate ? (s[chosen[t]] - lse) : 0.0;
+        } else {
+            idx[t] = -1;
+            if (logg)
+                logg[t] = 0.0;
+        }
+    }
+    free(taken);
+    free(chosen);
+    return keff;
+}
+
+/* ----------------------------------------------------------- a2: scores */
+/*
+ * Scores of every candidate of one query row, for one selection head hs.
+ * [SAS] §3 Eq. 3: s_c = R(q, summary_c); here R is q_hat . ktilde_c / sqrt(d)
+ * with q_hat = q_h (share_group=0) or the mean over the G query heads of kv
+ * head hs (share_group=1), and ktilde_c = kbar_c, or W kbar_c when a
+ * projection W [d, d] (row-major, ktilde_e = sum_f W[e][f] kbar_f) is given.
+ * [FS] adds lambda_h a_c erf((i - p_c) / (2 sigma_h)).
+ */
+static void orc_scores_row(const void *q, int qdtype, int Hq, int Hkv, int nq, int d,
+                           int bidx, int hs, int64_t row, int64_t pos,
+                           const void *kbar, int kdtype, const float *max_norm,
+                           const float *centre, int64_t Ccap, int share_group,
+                           const float *proj_w, const float *erf_lambda,
+                           const float *erf_sigma, int64_t ncand, double *s_out)
+{
+    double *qh = (double *)calloc((size_t)d, sizeof(double));
+    int G = Hq / Hkv;
+    int kvh = share_group ? hs : hs / G;
+    if (share_group) {
+        for (int g = 0; g < G; ++g) {
+            int h = hs * G + g;
+            for (int e = 0; e < d; ++e)
+                qh[e] += orc_load(q, qdtype, (((int64_t)bidx * Hq + h) * nq + row) * d + e);
+        }
+        for (int e = 0; e < d; ++e)
+            qh[e] /= (double)G;
+    } else {
+        for (int e = 0; e < d; ++e)
+            qh[e] = orc_load(q, qdtype, (((int64_t)bidx * Hq + hs) * nq + row) * d + e);
+    }
+    double scale = 1.0 / sqrt((double)d);
+    double *kt = (double *)malloc(sizeof(double) * (size_t)d);
+    for (int64_t c = 0; c < ncand; ++c) {
+        const int64_t kb = (((int64_t)bidx * Hkv + kvh) * Ccap + c) * d;
+        if (proj_w) {
+            for (int e = 0; e < d; ++e) {
+                double acc = 0.0;
+                for (int f = 0; f < d; ++f)
+                    acc += (double)proj_w[e * d + f] * orc_load(kbar, kdtype, kb + f);
+                kt[e] = acc;
+            }
+        } else {
+            for (int e = 0; e < d; ++e)
+                kt[e] = orc_load(kbar, kdtype, kb + e);
+        }
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e)
+            dot += qh[e] * kt[e];
+        double sc = dot * scale;
+        if (erf_lambda) {
+            double lam = (double)erf_lambda[hs];
+            double sig = (double)erf_sigma[hs];
+            double a = (double)max_norm[((int64_t)bidx * Hkv + kvh) * Ccap + c];
+            double p = (double)centre[c];
+            sc += lam * a * erf(((double)pos - p) / (2.0 * sig));
+        }
+        s_out[c] = sc;
+    }
+    free(kt);
+    free(qh);
+}
+
+/*
+ * a2-a4 for a set of rows.  rows (nullable) lists row numbers r in [0, nq)
+ * to evaluate (all rows when NULL, nrows ignored); outputs are written at
+ * the full-size positions [B, Hsel, nq, K] / [B, Hsel, nq].
+ * Hsel = Hkv when share_group else Hq.
+ */
+void orc_score_select(const void *q, int qdtype, int B, int Hq, int Hkv, int nq,
+                      int d, int64_t q_pos0, const void *kbar, int kdtype,
+                      const float *max_norm, const float *centre, int64_t Ccap,
+                      int b, int prefix_mode, int qblock, int share_group,
+                      const float *proj_w, const float *erf_lambda,
+                      const float *erf_sigma, int K, int gate,
+                      const int64_t *rows, int64_t nrows,
+                      int32_t *idx, double *logg, int32_t *k_eff, double *gap,
+                      double *lse_cand)
+{
+    int Hsel = share_group ? Hkv : Hq;
+    int64_t nr = rows ? nrows : nq;
+    int64_t total = (int64_t)B * Hsel * nr;
+    int64_t w;
+#pragma omp parallel for schedule(dynamic)
+    for (w = 0; w < total; ++w) {
+        int64_t rr = w % nr;
+        int hs = (int)((w / nr) % Hsel);
+        int bidx = (int)(w / nr / Hsel);
+        int64_t row = rows ? rows[rr] : rr;
+        int64_t pos = q_pos0 + row;
+        int64_t ncand = orc_num_candidates(pos, b, prefix_mode, qblock);
+        double *s = (double *)malloc(sizeof(double) * (size_t)(ncand > 0 ? ncand : 1));
+        orc_scores_row(q, qdtype, Hq, Hkv, nq, d, bidx, hs, row, pos, kbar, kdtype,
+                       max_norm, centre, Ccap, share_group, proj_w, erf_lambda,
+                       erf_sigma, ncand, s);
+        int64_t o = ((int64_t)bidx * Hsel + hs) * nq + row;
+        double lse = 0.0, gp = 0.0;
+        int ke = orc_select_from_scores(s, ncand, K, gate, idx + o * K,
+                                        logg ? logg + o * K : NULL, &gp, &lse);
+        if (k_eff)
+            k_eff[o] = ke;
+        if (gap)
+            gap[o] = gp;
+        if (lse_cand)
+            lse_cand[o] = lse;
+        free(s);
+    }
+}
+
+/* Full score vector of one row (for tests that enumerate subsets). */
+void orc_scores_one_row(const void *q, int qdtype, int B, int Hq, int Hkv, int nq,
+                        int d, int64_t q_pos0, const void *kbar, int kdtype,
+                        const float *max_norm, const float *centre, int64_t Ccap,
+                        int b, int prefix_mode, int qblock, int share_group,
+                        const float *proj_w, const float *erf_lambda,
+                        const float *erf_sigma, int bidx, int hs, int64_t row,
+                        double *s_out)
+{
+    (void)B;
+    int64_t pos = q_pos0 + row;
+    int64_t ncand = orc_num_candidates(pos, b, prefix_mode, qblock);
+    orc_scores_row(q, qdtype, Hq, Hkv, nq, d, bidx, hs, row, pos, kbar, kdtype,
+                   max_norm, centre, Ccap, share_group, proj_w, erf_lambda,
+                   erf_sigma, ncand, s_out);
+}
+
+/* ------------------------------------------------ a5/a6: attention keys */
+/*
+ * Key set of query row at absolute position i for query head h.
+ * Branch "L" (long / sparse):
+ *   local == 0: the current block {j : floor(j/b) = floor(i/b), j <= i}
+ *               with bias 0 ([SAS] §4.1: B0 always kept, gate 1), plus
+ *   every selected unit c that is a valid candidate of i, whole (b tokens),
+ *   with bias logg (0 when logg is NULL) ([SAS] §4.3 Eq. 9; [FS] routed cells).
+ * Branch "S" (window): {j : i - w < j <= i} ([FS] sliding-window branch).
+ * Builds arrays of key positions and biases; returns the count.
+ */
+static int64_t orc_branch_L_keys(int64_t i, int b, int local, int prefix_mode,
+                                 int qblock, const int32_t *sel, const double *lg,
+                                 int K, int64_t *keys, double *bias, int *slot)
+{
+    int64_t n = 0;
+    if (local == 0) {
+        int64_t c0 = i / b;
+        for (int64_t j = c0 * b; j <= i; ++j) {
+            keys[n] = j;
+            bias[n] = 0.0;
+            slot[n] = -1;
+            ++n;
+        }
+    }
+    int64_t ncand = orc_num_candidates(i, b, prefix_mode, qblock);
+    for (int t = 0; t < K; ++t) {
+        int32_t c = sel[t];
+        if (c < 0 || (int64_t)c >= ncand)
+            continue;                      /* only candidate units are read */
+        for (int64_t j = (int64_t)c * b; j < (int64_t)(c + 1) * b; ++j) {
+            keys[n] = j;
+            bias[n] = lg ? lg[t] : 0.0;
+            slot[n] = t;
+            ++n;
+        }
+    }
+    return n;
+}
+
+/* softmax attention of one row over an explicit key list (fp64) */
+static void orc_softmax_attend(const void *q, const void *k, const void *v, int dtype,
+                               int64_t qoff, int64_t kvbase, int d,
+                               const int64_t *keys, const double *bias, int64_t nk,
+                               double *z, double *o, double *lse)
+{
+    double scale = 1.0 / sqrt((double)d);
+    for (int e = 0; e < d; ++e)
+        o[e] = 0.0;
+    if (nk == 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    double m = -INFINITY;
+    for (int64_t t = 0; t < nk; ++t) {
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e)
+            dot += orc_load(q, dtype, qoff + e) * orc_load(k, dtype, kvbase + keys[t] * d + e);
+        z[t] = dot * scale + bias[t];
+        if (z[t] > m)
+            m = z[t];
+    }
+    double l = 0.0;
+    for (int64_t t = 0; t < nk; ++t)
+        l += exp(z[t] - m);
+    for (int64_t t = 0; t < nk; ++t) {
+        double p = exp(z[t] - m) / l;
+        for (int e = 0; e < d; ++e)
+            o[e] += p * orc_load(v, dtype, kvbase + keys[t] * d + e);
+    }
+    *lse = m + log(l);
+}
+
+/*
+ * Forward attention for a set of rows.
+ *   local: 0 = current block kept, 1 = none.
+ *   window > 0 with alpha != NULL: o = alpha_h o_L + (1 - alpha_h) o_S.
+ *   idx/logg are [B, Hsel, nq, K]; logg may be NULL (no bias).
+ *   Outputs o [B, Hq, nq, d] and lse [B, Hq, nq] (lse of branch L), fp64.
+ */
+void orc_attn_fwd(const void *q, const void *k, const void *v, int dtype,
+                  int B, int Hq, int Hkv, int nq, int d, int64_t L, int64_t q_pos0,
+                  int b, int prefix_mode, int qblock, const int32_t *idx,
+                  const double *logg, int K, int share_group, int local, int window,
+                  const float *alpha, const int64_t *rows, int64_t nrows,
+                  double *o, double *lse)
+{
+    int G = Hq / Hkv;
+    int Hsel = share_group ? Hkv : Hq;
+    int64_t nr = rows ? nrows : nq;
+    int64_t total = (int64_t)B * Hq * nr;
+    int64_t maxk = (int64_t)b + (int64_t)K * b + (window > 0 ? window : 0) + 1;
+    int64_t w;
+#pragma omp parallel for schedule(dynamic)
+    for (w = 0; w < total; ++w) {
+        int64_t rr = w % nr;
+        int h = (int)((w / nr) % Hq);
+        int bidx = (int)(w / nr / Hq);
+        int64_t row = rows ? rows[rr] : rr;
+        int64_t i = q_pos0 + row;
+        int kvh = h / G;
+        int hs = share_group ? kvh : h;
+        int64_t so = (((int64_t)bidx * Hsel + hs) * nq + row) * K;
+        int64_t qoff = (((int64_t)bidx * Hq + h) * nq + row) * d;
+        int64_t kvbase = ((int64_t)bidx * Hkv + kvh) * L * d;
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)maxk);
+        double *bias = (double *)malloc(sizeof(double) * (size_t)maxk);
+        double *z = (double *)malloc(sizeof(double) * (size_t)maxk);
+        int *slot = (int *)malloc(sizeof(int) * (size_t)maxk);
+        double *oL = (double *)malloc(sizeof(double) * (size_t)d);
+        double *oS = (double *)malloc(sizeof(double) * (size_t)d);
+        double lseL, lseS;
+        int64_t nk = orc_branch_L_keys(i, b, local, prefix_mode, qblock, idx + so,
+                                       logg ? logg + so : NULL, K, keys, bias, slot);
+        orc_softmax_attend(q, k, v, dtype, qoff, kvbase, d, keys, bias, nk, z, oL, &lseL);
+        int64_t oo = ((int64_t)bidx * Hq + h) * nq + row;
+        if (window > 0 && alpha) {
+            int64_t ns = 0;
+            int64_t j0 = i - window + 1;
+            if (j0 < 0)
+                j0 = 0;
+            for (int64_t j = j0; j <= i; ++j) {
+                keys[ns] = j;
+                bias[ns] = 0.0;
+                ++ns;
+            }
+            orc_softmax_attend(q, k, v, dtype, qoff, kvbase, d, keys, bias, ns, z, oS, &lseS);
+            double a = (double)alpha[h];
+            for (int e = 0; e < d; ++e)
+                o[oo * d + e] = a * oL[e] + (1.0 - a) * oS[e];
+        } else {
+            for (int e = 0; e < d; ++e)
+                o[oo * d + e] = oL[e];
+        }
+        if (lse)
+            lse[oo] = lseL;
+        free(keys); free(bias); free(z); free(slot); free(oL); free(oS);
+    }
+}
+
+/* ------------------------------------------------------ a7: backward */
+/*
+ * Backward of the SAS branch (local = current block, no window), fp64.
+ *   z_ij = q_i.k_j/sqrt(d) + [j in B_m, m selected] log g_m
+ *   p_ij = softmax_j(z_ij), o_i = sum_j p_ij v_j, D_i = do_i . o_i
+ *   dS_ij = p_ij (do_i . v_j - D_i)
+ *   dq_i = sum_j dS_ij k_j / sqrt(d); dk_j = sum_i dS_ij q_i / sqrt(d);
+ *   dv_j = sum_i p_ij do_i
+ *   dg_m = sum_{j in B_m} dS_ij / g_m  ([SAS] §4.2.2 Eq. 5, inner gate:
+ *          p~_j/g_m do.(v_j - o) summed over the block = dS summed / g_m),
+ *   summed over the G query heads when the gate is shared by a kv head.
+ * With logg NULL the gate is 1 and dg is the gradient at g = 1.
+ * Pass 1 runs per row (dq, dg, saves lse and D); pass 2 per key block
+ * (dk, dv) gathers every row that reads the block.
+ * kv_slice >= 0 restricts the work to one (batch, kv head) pair given as
+ * b*Hkv + kvh (outputs of other pairs are left untouched).
+ */
+void orc_attn_bwd(const void *q, const void *k, const void *v, const void *dout,
+                  int dtype, int B, int Hq, int Hkv, int nq, int d, int64_t L,
+                  int64_t q_pos0, int b, const int32_t *idx, const double *logg,
+                  int K, int share_group, int64_t kv_slice,
+                  double *dq, double *dk, double *dv, double *dg)
+{
+    int G = Hq / Hkv;
+    int Hsel = share_group ? Hkv : Hq;
+    double scale = 1.0 / sqrt((double)d);
+    int64_t maxk = (int64_t)b + (int64_t)K * b + 1;
+    double *lse_all = (double *)malloc(sizeof(double) * (size_t)B * Hq * nq);
+    double *D_all = (double *)malloc(sizeof(double) * (size_t)B * Hq * nq);
+    /* per (b, q head, row, slot) block sums of dS, combined over heads below */
+    double *dgh = (double *)calloc((size_t)B * Hq * nq * K, sizeof(double));
+
+    int64_t total = (int64_t)B * Hq * nq;
+    int64_t w;
+#pragma omp parallel for schedule(dynamic)
+    for (w = 0; w < total; ++w) {
+        int64_t row = w % nq;
+        int h = (int)((w / nq) % Hq);
+        int bidx = (int)(w / nq / Hq);
+        int kvh = h / G;
+        if (kv_slice >= 0 && (int64_t)bidx * Hkv + kvh != kv_slice)
+            continue;
+        int hs = share_group ? kvh : h;
+        int64_t i = q_pos0 + row;
+        int64_t so = (((int64_t)bidx * Hsel + hs) * nq + row) * K;
+        int64_t qoff = (((int64_t)bidx * Hq + h) * nq + row) * d;
+        int64_t kvbase = ((int64_t)bidx * Hkv + kvh) * L * d;
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)maxk);
+        double *bias = (double *)malloc(sizeof(double) * (size_t)maxk);
+        double *z = (double *)malloc(sizeof(double) * (size_t)maxk);
+        int *slot = (int *)malloc(sizeof(int) * (size_t)maxk);
+        double *o = (double *)malloc(sizeof(double) * (size_t)d);
+        double lse;
+        int64_t nk = orc_branch_L_keys(i, b, 0, 0, 1, idx + so, logg ? logg + so : NULL,
+                                       K, keys, bias, slot);
+        orc_softmax_attend(q, k, v, dtype, qoff, kvbase, d, keys, bias, nk, z, o, &lse);
+        double D = 0.0;
+        for (int e = 0; e < d; ++e)
+            D += orc_load(dout, dtype, qoff + e) * o[e];
+        lse_all[w] = lse;
+        D_all[w] = D;
+        for (int e = 0; e < d; ++e)
+            dq[qoff + e] = 0.0;
+        for (int64_t t = 0; t < nk; ++t) {
+            double p = exp(z[t] - lse);
+            double dp = 0.0;
+            for (int e = 0; e < d; ++e)
+                dp += orc_load(dout, dtype, qoff + e) * orc_load(v, dtype, kvbase + keys[t] * d + e);
+            double ds = p * (dp - D);
+            for (int e = 0; e < d; ++e)
+                dq[qoff + e] += ds * orc_load(k, dtype, kvbase + keys[t] * d + e) * scale;
+            if (slot[t] >= 0)
+                dgh[w * K + slot[t]] += ds;
+        }
+        free(keys); free(bias); free(z); free(slot); free(o);
+    }
+
+    /* dg: divide by g_m and sum over the heads that share the selection */
+    int64_t nsel = (int64_t)B * Hsel * nq;
+#pragma omp parallel for schedule(static)
+    for (w = 0; w < nsel; ++w) {
+        int64_t row = w % nq;
+        int hs = (int)((w / nq) % Hsel);
+        int bidx = (int)(w / nq / Hsel);
+        int kvh = share_group ? hs : hs / G;
+        if (kv_slice >= 0 && (int64_t)bidx * Hkv + kvh != kv_slice)
+            continue;
+        for (int t = 0; t < K; ++t) {
+            double acc = 0.0;
+            if (idx[w * K + t] >= 0) {
+                double g = logg ? exp(logg[w * K + t]) : 1.0;
+                int h0 = share_group ? hs * G : hs;
+                int h1 = share_group ? hs * G + G : hs + 1;
+                for (int h = h0; h < h1; ++h)
+                    acc += dgh[(((int64_t)bidx * Hq + h) * nq + row) * K + t] / g;
+            }
+            dg[w * K + t] = acc;
+        }
+    }
+
+    /* pass 2: dk, dv per (batch, kv head, key block) */
+    int64_t nblk = (L + b - 1) / b;
+    int64_t tot2 = (int64_t)B * Hkv * nblk;
+#pragma omp parallel for schedule(dynamic)
+    for (w = 0; w < tot2; ++w) {
+        int64_t c = w % nblk;
+        int kvh = (int)((w / nblk) % Hkv);
+        int bidx = (int)(w / nblk / Hkv);
+        if (kv_slice >= 0 && (int64_t)bidx * Hkv + kvh != kv_slice)
+            continue;
+        int64_t kvbase = ((int64_t)bidx * Hkv + kvh) * L * d;
+        int64_t j0 = c * b, j1 = (c + 1) * b < L ? (c + 1) * b : L;
+        for (int64_t j = j0; j < j1; ++j)
+            for (int e = 0; e < d; ++e) {
+                dk[kvbase + j * d + e] = 0.0;
+                dv[kvbase + j * d + e] = 0.0;
+            }
+        for (int g = 0; g < G; ++g) {
+            int h = kvh * G + g;
+            int hs = share_group ? kvh : h;
+            for (int64_t row = 0; row < nq; ++row) {
+                int64_t i = q_pos0 + row;
+                int64_t so = (((int64_t)bidx * Hsel + hs) * nq + row) * K;
+                double bias_c;
+                int reads = 0;
+                if (i / b == c) {
+                    reads = 1;                 /* current block, causal */
+                    bias_c = 0.0;
+                } else {
+                    int64_t ncand = i / b;
+                    for (int t = 0; t < K; ++t) {
+                        if (idx[so + t] == (int32_t)c && c < ncand) {
+                            reads = 2;
+                            bias_c = logg ? logg[so + t] : 0.0;
+                            break;
+                        }
+                    }
+                }
+                if (!reads)
+                    continue;
+                int64_t ww = ((int64_t)bidx * Hq + h) * nq + row;
+                int64_t qoff = ww * d;
+                for (int64_t j = j0; j < j1; ++j) {
+                    if (reads == 1 && j > i)
+                        continue;
+                    double dot = 0.0, dp = 0.0;
+                    for (int e = 0; e < d; ++e) {
+                        dot += orc_load(q, dtype, qoff + e) * orc_load(k, dtype, kvbase + j * d + e);
+                        dp += orc_load(dout, dtype, qoff + e) * orc_load(v, dtype, kvbase + j * d + e);
+                    }
+                    double p = exp(dot * scale + bias_c - lse_all[ww]);
+                    double ds = p * (dp - D_all[ww]);
+                    for (int e = 0; e < d; ++e) {
+                        dk[kvbase + j * d + e] += ds * orc_load(q, dtype, qoff + e) * scale;
+                        dv[kvbase + j * d + e] += p * orc_load(dout, dtype, qoff + e);
+                    }
+                }
+            }
+        }
+    }
+    free(lse_all);
+    free(D_all);
+    free(dgh);
+}
