@@ -1,0 +1,268 @@
+// api.hip -- the extern "C" entry points of libsparse_attn (declared in
+// include/sparse_attn.h): argument validation, status codes, workspace
+// sizing and kernel dispatch on the caller's stream.  Nothing here allocates,
+// frees, synchronises or reads device memory.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "spa_launch.h"
+#include "../../include/sparse_attn.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SPA_OK;
+}
+
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define SPA_REQUIRE(cond, code, ...) \
+  do {                               \
+    if (!(cond)) return fail((code), __VA_ARGS__); \
+  } while (0)
+
+int check_heads(int B, int Hq, int Hkv, int d, int dtype) {
+  SPA_REQUIRE(dtype == SPA_DTYPE_F32 || dtype == SPA_DTYPE_BF16, SPA_ERR_UNSUPPORTED,
+              "dtype %d not supported (0 = fp32, 1 = bf16)", dtype);
+  SPA_REQUIRE(d == 64 || d == 128, SPA_ERR_UNSUPPORTED, "head dim d = %d not supported (64 or 128)", d);
+  SPA_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1, SPA_ERR_INVALID_ARG, "B, Hq, Hkv must be >= 1");
+  SPA_REQUIRE(Hq % Hkv == 0, SPA_ERR_INVALID_ARG, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
+  SPA_REQUIRE(Hq / Hkv <= 8 && pow2(Hq / Hkv), SPA_ERR_UNSUPPORTED,
+              "group size G = %d not supported (1, 2, 4 or 8)", Hq / Hkv);
+  SPA_REQUIRE(static_cast<int64_t>(B) * Hq <= 65535, SPA_ERR_UNSUPPORTED, "B * Hq = %lld exceeds 65535",
+              static_cast<long long>(B) * Hq);
+  return SPA_OK;
+}
+
+int check_select(const spa_select_args* a, spa::SelectLaunch* p) {
+  SPA_REQUIRE(a != nullptr, SPA_ERR_INVALID_ARG, "args is NULL");
+  int st = check_heads(a->B, a->Hq, a->Hkv, a->d, a->dtype);
+  if (st != SPA_OK) return st;
+  SPA_REQUIRE(a->q && a->kbar && a->idx, SPA_ERR_INVALID_ARG, "q, kbar and idx must be non-NULL");
+  SPA_REQUIRE(aligned16(a->q) && aligned16(a->kbar), SPA_ERR_INVALID_ARG, "q and kbar must be 16-byte aligned");
+  SPA_REQUIRE(a->nq >= 1 && a->q_pos0 >= 0, SPA_ERR_INVALID_ARG, "nq must be >= 1 and q_pos0 >= 0");
+  SPA_REQUIRE(pow2(a->b) && a->b >= 16 && a->b <= 128, SPA_ERR_UNSUPPORTED,
+              "block size b = %d not supported (power of two in [16, 128])", a->b);
+  SPA_REQUIRE(a->K >= 1 && a->K <= 64, SPA_ERR_UNSUPPORTED, "K = %d not supported (1..64)", a->K);
+  SPA_REQUIRE(a->gate == SPA_GATE_NONE || a->gate == SPA_GATE_SOFTMAX_LOG, SPA_ERR_INVALID_ARG,
+              "gate = %d invalid", a->gate);
+  SPA_REQUIRE(a->gate == SPA_GATE_NONE || a->logg != nullptr, SPA_ERR_INVALID_ARG,
+              "logg must be non-NULL when the gate is on");
+  SPA_REQUIRE(a->prefix_mode == SPA_PREFIX_CURRENT_BLOCK || a->prefix_mode == SPA_PREFIX_QUERY_BLOCK,
+              SPA_ERR_INVALID_ARG, "prefix_mode = %d invalid", a->prefix_mode);
+  if (a->prefix_mode == SPA_PREFIX_QUERY_BLOCK)
+    SPA_REQUIRE(a->qblock >= a->b && a->qblock % a->b == 0, SPA_ERR_INVALID_ARG,
+                "qblock = %d must be a positive multiple of b = %d", a->qblock, a->b);
+  SPA_REQUIRE((a->erf_lambda == nullptr) == (a->erf_sigma == nullptr), SPA_ERR_INVALID_ARG,
+              "erf_lambda and erf_sigma must both be given or both be NULL");
+  if (a->erf_lambda != nullptr)
+    SPA_REQUIRE(a->max_norm != nullptr && a->centre != nullptr, SPA_ERR_INVALID_ARG,
+                "the erf term needs max_norm and centre");
+  SPA_REQUIRE(a->ccap >= 1, SPA_ERR_INVALID_ARG, "ccap must be >= 1");
+  const int Hsel = a->share_group ? a->Hkv : a->Hq;
+  const int64_t last = a->q_pos0 + a->nq - 1;
+  const int64_t max_cand = spa::num_candidates(last, a->b, a->prefix_mode,
+                                               a->prefix_mode == SPA_PREFIX_QUERY_BLOCK ? a->qblock : 1);
+  SPA_REQUIRE(max_cand <= a->ccap, SPA_ERR_INVALID_ARG,
+              "kbar holds %lld blocks but the last row has %lld candidates",
+              static_cast<long long>(a->ccap), static_cast<long long>(max_cand));
+  SPA_REQUIRE(static_cast<int64_t>(a->B) * Hsel <= 65535, SPA_ERR_UNSUPPORTED, "B * Hsel exceeds 65535");
+  SPA_REQUIRE(max_cand < (static_cast<int64_t>(1) << 31), SPA_ERR_UNSUPPORTED, "too many candidates");
+  *p = spa::SelectLaunch{a->q, a->dtype, a->B, a->Hq, a->Hkv, a->nq, a->d, a->q_pos0, a->kbar,
+                         a->max_norm, a->centre, a->ccap, a->b, a->prefix_mode,
+                         a->prefix_mode == SPA_PREFIX_QUERY_BLOCK ? a->qblock : 1, a->share_group ? 1 : 0,
+                         a->proj_w, a->erf_lambda, a->erf_sigma, a->K, a->gate, a->idx, a->logg,
+                         a->k_eff, Hsel, max_cand};
+  return SPA_OK;
+}
+
+int check_attn(const spa_attn_args* a, spa::AttnLaunch* p) {
+  SPA_REQUIRE(a != nullptr, SPA_ERR_INVALID_ARG, "args is NULL");
+  int st = check_heads(a->B, a->Hq, a->Hkv, a->d, a->dtype);
+  if (st != SPA_OK) return st;
+  SPA_REQUIRE(a->q && a->k && a->v && a->o && a->idx, SPA_ERR_INVALID_ARG,
+              "q, k, v, o and idx must be non-NULL");
+  SPA_REQUIRE(aligned16(a->q) && aligned16(a->k) && aligned16(a->v), SPA_ERR_INVALID_ARG,
+              "q, k and v must be 16-byte aligned");
+  SPA_REQUIRE(a->nq >= 1 && a->q_pos0 >= 0 && a->L >= 1 && a->q_pos0 + a->nq <= a->L,
+              SPA_ERR_INVALID_ARG, "need nq >= 1, q_pos0 >= 0 and q_pos0 + nq <= L");
+  SPA_REQUIRE(pow2(a->b) && a->b >= 16 && a->b <= 128, SPA_ERR_UNSUPPORTED,
+              "block size b = %d not supported (power of two in [16, 128])", a->b);
+  SPA_REQUIRE(a->K >= 1 && a->K <= 64, SPA_ERR_UNSUPPORTED, "K = %d not supported (1..64)", a->K);
+  SPA_REQUIRE(a->prefix_mode == SPA_PREFIX_CURRENT_BLOCK || a->prefix_mode == SPA_PREFIX_QUERY_BLOCK,
+              SPA_ERR_INVALID_ARG, "prefix_mode = %d invalid", a->prefix_mode);
+  if (a->prefix_mode == SPA_PREFIX_QUERY_BLOCK)
+    SPA_REQUIRE(a->qblock >= a->b && a->qblock % a->b == 0, SPA_ERR_INVALID_ARG,
+                "qblock = %d must be a positive multiple of b = %d", a->qblock, a->b);
+  const bool sas = a->local == SPA_LOCAL_CURRENT_BLOCK && a->window == 0 && a->alpha == nullptr;
+  const bool mix = a->local == SPA_LOCAL_NONE && a->window > 0 && a->alpha != nullptr;
+  SPA_REQUIRE(sas || mix, SPA_ERR_UNSUPPORTED,
+              "supported modes: (local=CURRENT_BLOCK, window=0, alpha=NULL) or "
+              "(local=NONE, window>0, alpha!=NULL)");
+  SPA_REQUIRE(a->L < (static_cast<int64_t>(1) << 31), SPA_ERR_UNSUPPORTED, "L must be < 2^31");
+  const int Hsel = a->share_group ? a->Hkv : a->Hq;
+  *p = spa::AttnLaunch{a->q, a->k, a->v, a->dtype, a->B, a->Hq, a->Hkv, a->nq, a->d, a->L, a->q_pos0,
+                       a->b, a->prefix_mode, a->prefix_mode == SPA_PREFIX_QUERY_BLOCK ? a->qblock : 1,
+                       a->idx, a->logg, a->K, a->share_group ? 1 : 0, a->local, a->window, a->alpha,
+                       a->o, a->lse, Hsel};
+  return SPA_OK;
+}
+
+int check_bwd(const spa_attn_args* a, const void* o, const void* dout, const float* lse, void* dq, void* dk,
+              void* dv, float* dg, spa::BwdLaunch* p) {
+  spa::AttnLaunch al;
+  int st = check_attn(a, &al);
+  if (st != SPA_OK) return st;
+  SPA_REQUIRE(a->local == SPA_LOCAL_CURRENT_BLOCK && a->window == 0 && a->alpha == nullptr,
+              SPA_ERR_UNSUPPORTED, "the backward supports the current-block + selected-blocks mode only");
+  SPA_REQUIRE(a->prefix_mode == SPA_PREFIX_CURRENT_BLOCK, SPA_ERR_UNSUPPORTED,
+              "the backward supports prefix_mode = CURRENT_BLOCK only");
+  SPA_REQUIRE(a->b <= 64, SPA_ERR_UNSUPPORTED, "the backward supports b <= 64");
+  SPA_REQUIRE(o && dout && lse && dq && dk && dv && dg, SPA_ERR_INVALID_ARG,
+              "o, dout, lse, dq, dk, dv and dg must be non-NULL");
+  *p = spa::BwdLaunch{al, o, dout, lse, dq, dk, dv, dg};
+  return SPA_OK;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return SPA_OK;
+  SPA_REQUIRE(ws != nullptr && have >= need, SPA_ERR_WORKSPACE,
+              "workspace of %zu bytes needed, %zu given%s", need, have, ws ? "" : " (NULL)");
+  return SPA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int spa_abi_version(void) { return SPA_ABI_VERSION; }
+
+const char* spa_last_error(void) { return g_last_error.c_str(); }
+
+int sparse_block_summaries(const void* k, int dtype, int B, int Hkv, int64_t L, int d, int b,
+                           int64_t first_block, int64_t num_blocks, int64_t ccap, void* kbar,
+                           float* max_norm, float* centre, spa_stream_t stream) {
+  int st = check_heads(B, Hkv, Hkv, d, dtype);
+  if (st != SPA_OK) return st;
+  SPA_REQUIRE(k && kbar && max_norm, SPA_ERR_INVALID_ARG, "k, kbar and max_norm must be non-NULL");
+  SPA_REQUIRE(aligned16(k), SPA_ERR_INVALID_ARG, "k must be 16-byte aligned");
+  SPA_REQUIRE(pow2(b) && b >= 16 && b <= 128, SPA_ERR_UNSUPPORTED,
+              "block size b = %d not supported (power of two in [16, 128])", b);
+  SPA_REQUIRE(first_block >= 0 && num_blocks >= 0, SPA_ERR_INVALID_ARG,
+              "first_block and num_blocks must be >= 0");
+  SPA_REQUIRE((first_block + num_blocks) * b <= L, SPA_ERR_INVALID_ARG,
+              "blocks [%lld, %lld) are not all full in L = %lld", static_cast<long long>(first_block),
+              static_cast<long long>(first_block + num_blocks), static_cast<long long>(L));
+  SPA_REQUIRE(first_block + num_blocks <= ccap, SPA_ERR_INVALID_ARG, "ccap = %lld too small",
+              static_cast<long long>(ccap));
+  SPA_REQUIRE(num_blocks < (static_cast<int64_t>(1) << 31), SPA_ERR_UNSUPPORTED, "too many blocks");
+  if (num_blocks == 0) return ok();
+  spa::SummaryLaunch p{k, dtype, B, Hkv, L, d, b, first_block, num_blocks, ccap, kbar, max_norm, centre};
+  return hip_status(spa::launch_block_summaries(p, static_cast<hipStream_t>(stream)), "sparse_block_summaries");
+}
+
+int sparse_score_select(const spa_select_args* a, void* workspace, size_t ws_bytes, spa_stream_t stream) {
+  spa::SelectLaunch p;
+  int st = check_select(a, &p);
+  if (st != SPA_OK) return st;
+  st = check_ws(workspace, ws_bytes, spa::select_workspace_bytes(p));
+  if (st != SPA_OK) return st;
+  return hip_status(spa::launch_score_select(p, workspace, static_cast<hipStream_t>(stream)),
+                    "sparse_score_select");
+}
+
+int sparse_attn_fwd(const spa_attn_args* a, void* workspace, size_t ws_bytes, spa_stream_t stream) {
+  spa::AttnLaunch p;
+  int st = check_attn(a, &p);
+  if (st != SPA_OK) return st;
+  st = check_ws(workspace, ws_bytes, spa::attn_fwd_workspace_bytes(p));
+  if (st != SPA_OK) return st;
+  return hip_status(spa::launch_attn_fwd(p, workspace, static_cast<hipStream_t>(stream)), "sparse_attn_fwd");
+}
+
+int sparse_attn_bwd(const spa_attn_args* a, const void* o, const void* dout, const float* lse, void* dq,
+                    void* dk, void* dv, float* dg, void* workspace, size_t ws_bytes, spa_stream_t stream) {
+  spa::BwdLaunch p;
+  int st = check_bwd(a, o, dout, lse, dq, dk, dv, dg, &p);
+  if (st != SPA_OK) return st;
+  st = check_ws(workspace, ws_bytes, spa::attn_bwd_workspace_bytes(p));
+  if (st != SPA_OK) return st;
+  return hip_status(spa::launch_attn_bwd(p, workspace, static_cast<hipStream_t>(stream)), "sparse_attn_bwd");
+}
+
+size_t sparse_workspace_bytes(int op, const void* args) {
+  switch (op) {
+    case SPA_OP_SCORE_SELECT: {
+      spa::SelectLaunch p;
+      if (check_select(static_cast<const spa_select_args*>(args), &p) != SPA_OK) return 0;
+      return spa::select_workspace_bytes(p);
+    }
+    case SPA_OP_ATTN_FWD: {
+      spa::AttnLaunch p;
+      if (check_attn(static_cast<const spa_attn_args*>(args), &p) != SPA_OK) return 0;
+      return spa::attn_fwd_workspace_bytes(p);
+    }
+    case SPA_OP_ATTN_BWD: {
+      spa::AttnLaunch p;
+      if (check_attn(static_cast<const spa_attn_args*>(args), &p) != SPA_OK) return 0;
+      spa::BwdLaunch bp{p, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+      return spa::attn_bwd_workspace_bytes(bp);
+    }
+    default:
+      fail(SPA_ERR_INVALID_ARG, "unknown op %d", op);
+      return 0;
+  }
+}
+
+int sparse_workspace_init(void* workspace, size_t ws_bytes, spa_stream_t stream) {
+  if (ws_bytes == 0) return ok();
+  SPA_REQUIRE(workspace != nullptr, SPA_ERR_INVALID_ARG, "workspace is NULL");
+  SPA_REQUIRE(aligned16(workspace) && ws_bytes % 16 == 0, SPA_ERR_INVALID_ARG,
+              "workspace must be 16-byte aligned with a size multiple of 16");
+  return hip_status(spa::launch_zero_fill(workspace, ws_bytes, static_cast<hipStream_t>(stream)),
+                    "sparse_workspace_init");
+}
+
+}  // extern "C"
+
+namespace spa {
+
+__global__ void zero_fill_kernel(uint4* p, size_t n) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_zero_fill(void* ptr, size_t bytes, hipStream_t st) {
+  const size_t n = bytes / 16;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                     static_cast<uint4*>(ptr), n);
+  return hipGetLastError();
+}
+
+}  // namespace spa

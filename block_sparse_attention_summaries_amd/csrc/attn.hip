@@ -1,0 +1,632 @@
+// attn.hip -- exact softmax attention over the kept keys, forward and
+// backward, on gfx950.
+//
+// Keys of a query row at position i:
+//   branch L: the current block {j : floor(j/b) = floor(i/b), j <= i} (when
+//             kept) plus every selected unit, each selected logit biased by its
+//             log gate ("SAS" review §4.1 Eq. 4, §4.3 Eq. 9; "Monodratic" news
+//             page: guaranteed local block + exact causal softmax on the set);
+//   branch S: the window i - w < j <= i, mixed o = alpha o_L + (1 - alpha) o_S
+//             ("FreeSolo" review, "How it works").
+// Backward (SAS branch): D = do.o, dS = p (do.v - D), dq, dk, dv and the
+// inner-gate gradient dg_m = sum_{j in B_m} dS_j / g_m ("SAS" review §4.2.2
+// Eq. 5), summed over the query heads that share a selection.
+//
+// Decode (one query row): split-K over the K+1 kept blocks.  One workgroup per
+// (selection head, kept block, 64-token tile) stages the K and V tile in LDS
+// once for all G query heads of the group (GQA-shared gather), writes an
+// online-softmax partial (m, l, acc); a combine kernel merges the partials.
+// Rows (prefill / training): one wave per (query head, row) streaming its key
+// segments 64 keys at a time with an online softmax.
+#include "spa_device.h"
+#include "spa_launch.h"
+
+namespace spa {
+
+// LDS ordering among the lanes of one wave (no workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ======================================================== decode: split-K
+constexpr int kTileTok = 64;
+
+template <typename T, int D, int HPW>
+__global__ __launch_bounds__(256) void decode_attn_partial_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ idx, const float* __restrict__ logg, int Hq, int Hkv, int Hsel,
+    int share_group, int64_t L, int64_t pos, int b, int K, int tpu, float* __restrict__ ws_acc,
+    float2* __restrict__ ws_ml) {
+  constexpr int kVec = Elem<T>::kVec;
+  constexpr int kVPR = D / kVec;                     // 16-byte vectors per row
+  constexpr int kPadRow = D + kVec;                  // padded LDS row (elements)
+  constexpr int kIters = kTileTok * kVPR / 256;
+  __shared__ __align__(16) T s_k[kTileTok * kPadRow];
+  __shared__ __align__(16) T s_v[kTileTok * D];
+  __shared__ float s_q[HPW][D];
+  __shared__ float s_p[HPW][kTileTok];
+
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int bh = blockIdx.y;
+  const int bi = bh / Hsel, hs = bh % Hsel;
+  const int G = Hq / Hkv;
+  const int kvh = share_group ? hs : hs / G;
+  const int unit = blockIdx.x / tpu, sub = blockIdx.x % tpu;
+  const int ntiles = (K + 1) * tpu;
+  const int tile = blockIdx.x;
+
+  int64_t start = 0;
+  int ntok = 0;
+  float bias = 0.f;
+  const int64_t c0 = pos / b;
+  if (unit < K) {
+    const int32_t c = idx[static_cast<int64_t>(bh) * K + unit];
+    if (c >= 0 && c < c0) {
+      start = static_cast<int64_t>(c) * b + sub * kTileTok;
+      ntok = b - sub * kTileTok < kTileTok ? b - sub * kTileTok : kTileTok;
+      if (logg != nullptr) bias = logg[static_cast<int64_t>(bh) * K + unit];
+    }
+  } else {
+    start = c0 * b + sub * kTileTok;
+    const int64_t n = pos + 1 - start;
+    const int cap = b - sub * kTileTok < kTileTok ? b - sub * kTileTok : kTileTok;
+    ntok = n <= 0 ? 0 : (n < cap ? static_cast<int>(n) : cap);
+  }
+
+  const int64_t obase = (static_cast<int64_t>(bh) * ntiles + tile) * HPW;
+  if (ntok == 0) {
+    for (int x = tid; x < HPW * D; x += 256) ws_acc[obase * D + x] = 0.f;
+    if (tid < HPW) ws_ml[obase + tid] = make_float2(-INFINITY, 0.f);
+    return;
+  }
+
+  // issue every K / V load of the tile before touching LDS
+  const int64_t kvrow0 = (static_cast<int64_t>(bi) * Hkv + kvh) * L + start;
+  uint4 rk[kIters], rv[kIters];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int x = tid + it * 256;
+    const int r = x / kVPR, cv = x % kVPR;
+    if (r < ntok) {
+      rk[it] = *reinterpret_cast<const uint4*>(k + (kvrow0 + r) * D + cv * kVec);
+      rv[it] = *reinterpret_cast<const uint4*>(v + (kvrow0 + r) * D + cv * kVec);
+    } else {
+      rk[it] = make_uint4(0, 0, 0, 0);
+      rv[it] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  for (int x = tid; x < HPW * D; x += 256) {
+    const int hh = x / D, e = x % D;
+    const int hq = share_group ? hs * G + hh : hs;
+    s_q[hh][e] = ld_f(q + (static_cast<int64_t>(bi) * Hq + hq) * D + e);
+  }
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int x = tid + it * 256;
+    const int r = x / kVPR, cv = x % kVPR;
+    *reinterpret_cast<uint4*>(&s_k[r * kPadRow + cv * kVec]) = rk[it];
+    *reinterpret_cast<uint4*>(&s_v[r * D + cv * kVec]) = rv[it];
+  }
+  __syncthreads();
+
+  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+  for (int h0 = 0; h0 < HPW; h0 += 4) {
+    const int hh = h0 + wave;
+    if (hh < HPW) {
+      const int j = lane;
+      float z = -INFINITY;
+      if (j < ntok) {
+        float acc = 0.f;
+#pragma unroll
+        for (int cv = 0; cv < kVPR; ++cv) {
+          float x[kVec];
+          Elem<T>::unpack(*reinterpret_cast<const uint4*>(&s_k[j * kPadRow + cv * kVec]), x);
+#pragma unroll
+          for (int i = 0; i < kVec; ++i) acc = fmaf(x[i], s_q[hh][cv * kVec + i], acc);
+        }
+        z = acc * scale + bias;
+      }
+      const float m = wave_max(z);
+      const float p = j < ntok ? __expf(z - m) : 0.f;
+      const float l = wave_sum(p);
+      s_p[hh][j] = p;
+      if (lane == 0) ws_ml[obase + hh] = make_float2(m, l);
+    }
+  }
+  __syncthreads();
+  for (int h0 = 0; h0 < HPW; h0 += 4) {
+    const int hh = h0 + wave;
+    if (hh < HPW) {
+#pragma unroll
+      for (int t = 0; t < D / kWave; ++t) {
+        const int e = lane + t * kWave;
+        float acc = 0.f;
+        for (int j = 0; j < ntok; ++j) acc = fmaf(s_p[hh][j], ld_f(&s_v[j * D + e]), acc);
+        ws_acc[(obase + hh) * D + e] = acc;
+      }
+    }
+  }
+}
+
+template <typename T, int D, int HPW>
+__global__ __launch_bounds__(256) void decode_combine_kernel(
+    const float* __restrict__ ws_acc, const float2* __restrict__ ws_ml, int Hq, int Hkv, int Hsel,
+    int share_group, int ntiles, T* __restrict__ o, float* __restrict__ lse) {
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int bi = bh / Hsel, hs = bh % Hsel;
+  const int G = Hq / Hkv;
+  for (int x = tid; x < HPW * D; x += 256) {
+    const int hh = x / D, e = x % D;
+    float M = -INFINITY;
+    for (int t = 0; t < ntiles; ++t)
+      M = fmaxf(M, ws_ml[(static_cast<int64_t>(bh) * ntiles + t) * HPW + hh].x);
+    float lsum = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
+      for (int t = 0; t < ntiles; ++t) {
+        const int64_t pi = (static_cast<int64_t>(bh) * ntiles + t) * HPW + hh;
+        const float2 ml = ws_ml[pi];
+        const float w = ml.x == -INFINITY ? 0.f : __expf(ml.x - M);
+        lsum = fmaf(ml.y, w, lsum);
+        acc = fmaf(ws_acc[pi * D + e], w, acc);
+      }
+    }
+    const int hq = share_group ? hs * G + hh : hs;
+    const int64_t orow = static_cast<int64_t>(bi) * Hq + hq;   // nq == 1
+    o[orow * D + e] = Elem<T>::from_float(lsum > 0.f ? acc / lsum : 0.f);
+    if (e == 0 && lse != nullptr) lse[orow] = lsum > 0.f ? M + __logf(lsum) : -INFINITY;
+  }
+}
+
+// ======================================================== rows: forward
+struct OnlineState {
+  float m, l;
+};
+
+// Attend the keys [start, start + n) of one row (one wave), updating the
+// running (m, l) and the lane's accumulator columns lane + 64 t.
+template <typename T, int D>
+__device__ __forceinline__ void attend_segment(const T* __restrict__ kbase, const T* __restrict__ vbase,
+                                               const float* s_q, int64_t start, int64_t n,
+                                               float bias, float scale, int lane, OnlineState& st,
+                                               float (&acc)[D / kWave]) {
+  constexpr int kVec = Elem<T>::kVec;
+  for (int64_t off = 0; off < n; off += kWave) {
+    const int64_t cnt = n - off < kWave ? n - off : kWave;
+    const int64_t key = start + off + lane;
+    float z = -INFINITY;
+    if (lane < cnt) {
+      const T* kr = kbase + key * D;
+      float a = 0.f;
+#pragma unroll
+      for (int cv = 0; cv < D / kVec; ++cv) {
+        float x[kVec];
+        Elem<T>::unpack(*reinterpret_cast<const uint4*>(kr + cv * kVec), x);
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) a = fmaf(x[i], s_q[cv * kVec + i], a);
+      }
+      z = a * scale + bias;
+    }
+    const float mc = wave_max(z);
+    const float mn = fmaxf(st.m, mc);
+    const float corr = __expf(st.m - mn);
+    const float p = lane < cnt ? __expf(z - mn) : 0.f;
+    st.l = st.l * corr + wave_sum(p);
+    st.m = mn;
+#pragma unroll
+    for (int t = 0; t < D / kWave; ++t) acc[t] *= corr;
+    for (int jj = 0; jj < cnt; ++jj) {
+      const float pj = __shfl(p, jj, kWave);
+      const T* vr = vbase + (start + off + jj) * D;
+#pragma unroll
+      for (int t = 0; t < D / kWave; ++t) acc[t] = fmaf(pj, ld_f(vr + lane + t * kWave), acc[t]);
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rows_attn_fwd_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ idx, const float* __restrict__ logg, const float* __restrict__ alpha,
+    int Hq, int Hkv, int Hsel, int share_group, int nq, int64_t q_pos0, int64_t L, int b,
+    int prefix_mode, int qblock, int K, int local, int window, T* __restrict__ o,
+    float* __restrict__ lse) {
+  __shared__ float s_q[4][D];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= nq) return;
+  const int bh = blockIdx.y;
+  const int bi = bh / Hq, h = bh % Hq;
+  const int G = Hq / Hkv;
+  const int kvh = h / G;
+  const int hs = share_group ? kvh : h;
+  const int64_t i = q_pos0 + row;
+  const int64_t qrow = (static_cast<int64_t>(bi) * Hq + h) * nq + row;
+  for (int e = lane; e < D; e += kWave) s_q[wave][e] = ld_f(q + qrow * D + e);
+  wave_lds_sync();
+
+  const T* kb = k + (static_cast<int64_t>(bi) * Hkv + kvh) * L * D;
+  const T* vb = v + (static_cast<int64_t>(bi) * Hkv + kvh) * L * D;
+  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+  const int64_t ncand = num_candidates(i, b, prefix_mode, qblock);
+  const int64_t so = ((static_cast<int64_t>(bi) * Hsel + hs) * nq + row) * K;
+
+  OnlineState st{-INFINITY, 0.f};
+  float acc[D / kWave];
+#pragma unroll
+  for (int t = 0; t < D / kWave; ++t) acc[t] = 0.f;
+  if (local == 0) {
+    const int64_t c0 = i / b;
+    attend_segment<T, D>(kb, vb, s_q[wave], c0 * b, i - c0 * b + 1, 0.f, scale, lane, st, acc);
+  }
+  for (int t = 0; t < K; ++t) {
+    const int32_t c = idx[so + t];
+    if (c < 0 || c >= ncand) continue;
+    const float bias = logg != nullptr ? logg[so + t] : 0.f;
+    attend_segment<T, D>(kb, vb, s_q[wave], static_cast<int64_t>(c) * b, b, bias, scale, lane, st, acc);
+  }
+  const float invl = st.l > 0.f ? 1.f / st.l : 0.f;
+  float out[D / kWave];
+#pragma unroll
+  for (int t = 0; t < D / kWave; ++t) out[t] = acc[t] * invl;
+  if (lse != nullptr && lane == 0) lse[qrow] = st.l > 0.f ? st.m + __logf(st.l) : -INFINITY;
+
+  if (window > 0 && alpha != nullptr) {
+    OnlineState sw{-INFINITY, 0.f};
+    float accw[D / kWave];
+#pragma unroll
+    for (int t = 0; t < D / kWave; ++t) accw[t] = 0.f;
+    const int64_t j0 = i - window + 1 > 0 ? i - window + 1 : 0;
+    attend_segment<T, D>(kb, vb, s_q[wave], j0, i - j0 + 1, 0.f, scale, lane, sw, accw);
+    const float a = alpha[h];
+    const float invw = sw.l > 0.f ? 1.f / sw.l : 0.f;
+#pragma unroll
+    for (int t = 0; t < D / kWave; ++t) out[t] = a * out[t] + (1.f - a) * (accw[t] * invw);
+  }
+#pragma unroll
+  for (int t = 0; t < D / kWave; ++t) o[qrow * D + lane + t * kWave] = Elem<T>::from_float(out[t]);
+}
+
+// ======================================================== rows: backward
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dout,
+                                                      int64_t rows, float* __restrict__ Dbuf) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (r >= rows) return;
+  float a = 0.f;
+  for (int e = lane; e < D; e += kWave) a = fmaf(ld_f(o + r * D + e), ld_f(dout + r * D + e), a);
+  a = wave_sum(a);
+  if (lane == 0) Dbuf[r] = a;
+}
+
+// dq and the block sums of dS for one segment of keys (one wave)
+template <typename T, int D>
+__device__ __forceinline__ float dq_segment(const T* __restrict__ kbase, const T* __restrict__ vbase,
+                                            const float* s_q, const float* s_do, int64_t start,
+                                            int64_t n, float bias, float scale, float lse_i,
+                                            float D_i, int lane, float (&dq)[D / kWave]) {
+  constexpr int kVec = Elem<T>::kVec;
+  float dsum = 0.f;
+  for (int64_t off = 0; off < n; off += kWave) {
+    const int64_t cnt = n - off < kWave ? n - off : kWave;
+    const int64_t key = start + off + lane;
+    float ds = 0.f;
+    if (lane < cnt) {
+      const T* kr = kbase + key * D;
+      const T* vr = vbase + key * D;
+      float a = 0.f, dp = 0.f;
+#pragma unroll
+      for (int cv = 0; cv < D / kVec; ++cv) {
+        float x[kVec], y[kVec];
+        Elem<T>::unpack(*reinterpret_cast<const uint4*>(kr + cv * kVec), x);
+        Elem<T>::unpack(*reinterpret_cast<const uint4*>(vr + cv * kVec), y);
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) {
+          a = fmaf(x[i], s_q[cv * kVec + i], a);
+          dp = fmaf(y[i], s_do[cv * kVec + i], dp);
+        }
+      }
+      const float p = __expf(a * scale + bias - lse_i);
+      ds = p * (dp - D_i);
+    }
+    dsum += wave_sum(ds);
+    for (int jj = 0; jj < cnt; ++jj) {
+      const float dsj = __shfl(ds, jj, kWave);
+      const T* kr = kbase + (start + off + jj) * D;
+#pragma unroll
+      for (int t = 0; t < D / kWave; ++t) dq[t] = fmaf(dsj, ld_f(kr + lane + t * kWave), dq[t]);
+    }
+  }
+  return dsum;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dbuf,
+    const int32_t* __restrict__ idx, const float* __restrict__ logg, int Hq, int Hkv, int Hsel,
+    int share_group, int nq, int64_t q_pos0, int64_t L, int b, int K, T* __restrict__ dq,
+    float* __restrict__ dg) {
+  __shared__ float s_q[4][D];
+  __shared__ float s_do[4][D];
+  __shared__ float s_dg[4][64];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= nq) return;
+  const int bh = blockIdx.y;                 // b * Hsel + hs
+  const int bi = bh / Hsel, hs = bh % Hsel;
+  const int G = Hq / Hkv;
+  const int kvh = share_group ? hs : hs / G;
+  const int nheads = share_group ? G : 1;
+  const int64_t i = q_pos0 + row;
+  const int64_t so = (static_cast<int64_t>(bh) * nq + row) * K;
+  const T* kb = k + (static_cast<int64_t>(bi) * Hkv + kvh) * L * D;
+  const T* vb = v + (static_cast<int64_t>(bi) * Hkv + kvh) * L * D;
+  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+  const int64_t ncand = i / b;
+  const int64_t c0 = i / b;
+  s_dg[wave][lane] = 0.f;
+
+  for (int hh = 0; hh < nheads; ++hh) {
+    const int h = share_group ? hs * G + hh : hs;
+    const int64_t qrow = (static_cast<int64_t>(bi) * Hq + h) * nq + row;
+    wave_lds_sync();
+    for (int e = lane; e < D; e += kWave) {
+      s_q[wave][e] = ld_f(q + qrow * D + e);
+      s_do[wave][e] = ld_f(dout + qrow * D + e);
+    }
+    wave_lds_sync();
+    const float lse_i = lse[qrow], D_i = Dbuf[qrow];
+    float dqa[D / kWave];
+#pragma unroll
+    for (int t = 0; t < D / kWave; ++t) dqa[t] = 0.f;
+    dq_segment<T, D>(kb, vb, s_q[wave], s_do[wave], c0 * b, i - c0 * b + 1, 0.f, scale, lse_i, D_i,
+                     lane, dqa);
+    for (int t = 0; t < K; ++t) {
+      const int32_t c = idx[so + t];
+      if (c < 0 || c >= ncand) continue;
+      const float bias = logg != nullptr ? logg[so + t] : 0.f;
+      const float sum = dq_segment<T, D>(kb, vb, s_q[wave], s_do[wave], static_cast<int64_t>(c) * b, b,
+                                         bias, scale, lse_i, D_i, lane, dqa);
+      if (lane == 0) s_dg[wave][t] += sum;
+    }
+#pragma unroll
+    for (int t = 0; t < D / kWave; ++t)
+      dq[qrow * D + lane + t * kWave] = Elem<T>::from_float(dqa[t] * scale);
+  }
+  wave_lds_sync();
+  if (lane < K) {
+    const int32_t c = idx[so + lane];
+    float g = 0.f;
+    if (c >= 0 && c < ncand) {
+      const float lg = logg != nullptr ? logg[so + lane] : 0.f;
+      g = s_dg[wave][lane] * __expf(-lg);
+    }
+    dg[so + lane] = g;
+  }
+}
+
+// dk, dv of one key block: every (query head, row) that reads the block is
+// gathered in row order (current-block rows first, then rows that selected
+// the block, found by an ordered compaction) so the sums are deterministic.
+// 256 threads: key j of the block = tid / (256/BS), columns split over the
+// 256/BS lanes that share a key.
+template <typename T, int D, int BS>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dbuf,
+    const int32_t* __restrict__ idx, const float* __restrict__ logg, int Hq, int Hkv, int Hsel,
+    int share_group, int nq, int64_t q_pos0, int64_t L, int K, T* __restrict__ dk,
+    T* __restrict__ dv) {
+  constexpr int kParts = 256 / BS;           // lanes sharing one key
+  constexpr int kCP = D / kParts;            // columns per lane
+  static_assert(kCP >= 1 && kCP <= 32, "block size out of range for this kernel");
+  __shared__ int s_row[256];
+  __shared__ float s_bias[256];
+  __shared__ int s_wcount[4];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int j = tid / kParts, part = tid % kParts;
+  const int64_t c = blockIdx.x;
+  const int bkv = blockIdx.y;
+  const int bi = bkv / Hkv, kvh = bkv % Hkv;
+  const int G = Hq / Hkv;
+  const int64_t kpos = c * BS + j;
+  const bool kvalid = kpos < L;
+  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+  const int64_t kvoff = ((static_cast<int64_t>(bi) * Hkv + kvh) * L + (kvalid ? kpos : 0)) * D + part * kCP;
+
+  float kr[kCP], vr[kCP], dka[kCP], dva[kCP];
+#pragma unroll
+  for (int t = 0; t < kCP; ++t) {
+    kr[t] = kvalid ? ld_f(k + kvoff + t) : 0.f;
+    vr[t] = kvalid ? ld_f(v + kvoff + t) : 0.f;
+    dka[t] = 0.f;
+    dva[t] = 0.f;
+  }
+
+  auto process = [&](int h, int row, float bias, bool causal) {
+    const int64_t qrow = (static_cast<int64_t>(bi) * Hq + h) * nq + row;
+    const T* qp = q + qrow * D + part * kCP;
+    const T* dp = dout + qrow * D + part * kCP;
+    float a = 0.f, dpv = 0.f;
+#pragma unroll
+    for (int t = 0; t < kCP; ++t) {
+      a = fmaf(ld_f(qp + t), kr[t], a);
+      dpv = fmaf(ld_f(dp + t), vr[t], dpv);
+    }
+#pragma unroll
+    for (int m = 1; m < kParts; m <<= 1) {
+      a += __shfl_xor(a, m, kWave);
+      dpv += __shfl_xor(dpv, m, kWave);
+    }
+    const int64_t ipos = q_pos0 + row;
+    if (kvalid && (!causal || kpos <= ipos)) {
+      const float p = __expf(a * scale + bias - lse[qrow]);
+      const float ds = p * (dpv - Dbuf[qrow]) * scale;
+#pragma unroll
+      for (int t = 0; t < kCP; ++t) {
+        dka[t] = fmaf(ds, ld_f(qp + t), dka[t]);
+        dva[t] = fmaf(p, ld_f(dp + t), dva[t]);
+      }
+    }
+  };
+
+  for (int g = 0; g < G; ++g) {
+    const int h = kvh * G + g;
+    const int hs = share_group ? kvh : h;
+    // (a) rows whose current block is c
+    {
+      int64_t r0 = c * BS - q_pos0, r1 = c * BS + BS - q_pos0;
+      if (r0 < 0) r0 = 0;
+      if (r1 > nq) r1 = nq;
+      for (int64_t r = r0; r < r1; ++r) process(h, static_cast<int>(r), 0.f, true);
+    }
+    // (b) rows after block c that selected it
+    int64_t rstart = (c + 1) * BS - q_pos0;
+    if (rstart < 0) rstart = 0;
+    for (int64_t r0 = rstart; r0 < nq; r0 += 256) {
+      const int64_t r = r0 + tid;
+      int slot = -1;
+      if (r < nq) {
+        const int32_t* ir = idx + ((static_cast<int64_t>(bi) * Hsel + hs) * nq + r) * K;
+        for (int t = 0; t < K; ++t)
+          if (ir[t] == static_cast<int32_t>(c)) { slot = t; break; }
+      }
+      const bool hit = slot >= 0;
+      const uint64_t mask = __ballot(hit);
+      const int before = __popcll(mask & ((1ull << lane) - 1ull));
+      __syncthreads();
+      if (lane == 0) s_wcount[wave] = __popcll(mask);
+      __syncthreads();
+      int base = 0;
+      for (int w = 0; w < wave; ++w) base += s_wcount[w];
+      const int total = s_wcount[0] + s_wcount[1] + s_wcount[2] + s_wcount[3];
+      if (hit) {
+        s_row[base + before] = static_cast<int>(r);
+        s_bias[base + before] =
+            logg != nullptr ? logg[((static_cast<int64_t>(bi) * Hsel + hs) * nq + r) * K + slot] : 0.f;
+      }
+      __syncthreads();
+      for (int x = 0; x < total; ++x) process(h, s_row[x], s_bias[x], false);
+    }
+  }
+  if (kvalid) {
+#pragma unroll
+    for (int t = 0; t < kCP; ++t) {
+      dk[kvoff + t] = Elem<T>::from_float(dka[t]);
+      dv[kvoff + t] = Elem<T>::from_float(dva[t]);
+    }
+  }
+}
+
+// ======================================================== launchers
+static bool use_decode_attn(const AttnLaunch& p) {
+  return p.nq == 1 && p.local == 0 && p.window == 0 && p.alpha == nullptr && p.b <= 128;
+}
+
+static int decode_tpu(const AttnLaunch& p) { return p.b > kTileTok ? p.b / kTileTok : 1; }
+
+static int heads_per_wg(const AttnLaunch& p) { return p.share_group ? p.Hq / p.Hkv : 1; }
+
+size_t attn_fwd_workspace_bytes(const AttnLaunch& p) {
+  if (!use_decode_attn(p)) return 0;
+  const size_t heads = static_cast<size_t>(p.B) * p.Hsel;
+  const size_t ntiles = static_cast<size_t>(p.K + 1) * decode_tpu(p);
+  const size_t hpw = heads_per_wg(p);
+  return align256(heads * ntiles * hpw * p.d * sizeof(float)) +
+         align256(heads * ntiles * hpw * sizeof(float2));
+}
+
+size_t attn_bwd_workspace_bytes(const BwdLaunch& p) {
+  return align256(static_cast<size_t>(p.a.B) * p.a.Hq * p.a.nq * sizeof(float));
+}
+
+template <typename T, int D, int HPW>
+static hipError_t launch_decode_attn_h(const AttnLaunch& p, void* ws, hipStream_t st) {
+  const int tpu = decode_tpu(p);
+  const int ntiles = (p.K + 1) * tpu;
+  const size_t heads = static_cast<size_t>(p.B) * p.Hsel;
+  float* acc = static_cast<float*>(ws);
+  float2* ml = reinterpret_cast<float2*>(static_cast<char*>(ws) +
+                                         align256(heads * ntiles * HPW * p.d * sizeof(float)));
+  hipLaunchKernelGGL((decode_attn_partial_kernel<T, D, HPW>), dim3(ntiles, static_cast<unsigned>(heads)),
+                     dim3(256), 0, st, static_cast<const T*>(p.q), static_cast<const T*>(p.k),
+                     static_cast<const T*>(p.v), p.idx, p.logg, p.Hq, p.Hkv, p.Hsel, p.share_group,
+                     p.L, p.q_pos0, p.b, p.K, tpu, acc, ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D, HPW>), dim3(static_cast<unsigned>(heads)), dim3(256), 0,
+                     st, acc, ml, p.Hq, p.Hkv, p.Hsel, p.share_group, ntiles, static_cast<T*>(p.o),
+                     p.lse);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_decode_attn_t(const AttnLaunch& p, void* ws, hipStream_t st) {
+  switch (heads_per_wg(p)) {
+    case 1: return launch_decode_attn_h<T, D, 1>(p, ws, st);
+    case 2: return launch_decode_attn_h<T, D, 2>(p, ws, st);
+    case 4: return launch_decode_attn_h<T, D, 4>(p, ws, st);
+    default: return launch_decode_attn_h<T, D, 8>(p, ws, st);
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_rows_fwd_t(const AttnLaunch& p, hipStream_t st) {
+  dim3 grid((p.nq + 3) / 4, static_cast<unsigned>(p.B * p.Hq));
+  hipLaunchKernelGGL((rows_attn_fwd_kernel<T, D>), grid, dim3(256), 0, st, static_cast<const T*>(p.q),
+                     static_cast<const T*>(p.k), static_cast<const T*>(p.v), p.idx, p.logg, p.alpha, p.Hq,
+                     p.Hkv, p.Hsel, p.share_group, p.nq, p.q_pos0, p.L, p.b, p.prefix_mode, p.qblock,
+                     p.K, p.local, p.window, static_cast<T*>(p.o), p.lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd(const AttnLaunch& p, void* ws, hipStream_t st) {
+  if (use_decode_attn(p)) {
+    if (p.dtype == 1) return p.d == 64 ? launch_decode_attn_t<bf16_t, 64>(p, ws, st) : launch_decode_attn_t<bf16_t, 128>(p, ws, st);
+    return p.d == 64 ? launch_decode_attn_t<float, 64>(p, ws, st) : launch_decode_attn_t<float, 128>(p, ws, st);
+  }
+  if (p.dtype == 1) return p.d == 64 ? launch_rows_fwd_t<bf16_t, 64>(p, st) : launch_rows_fwd_t<bf16_t, 128>(p, st);
+  return p.d == 64 ? launch_rows_fwd_t<float, 64>(p, st) : launch_rows_fwd_t<float, 128>(p, st);
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_t(const BwdLaunch& p, void* ws, hipStream_t st) {
+  const AttnLaunch& a = p.a;
+  float* Dbuf = static_cast<float*>(ws);
+  const int64_t rows = static_cast<int64_t>(a.B) * a.Hq * a.nq;
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, st,
+                     static_cast<const T*>(p.o), static_cast<const T*>(p.dout), rows, Dbuf);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((a.nq + 3) / 4, static_cast<unsigned>(a.B * a.Hsel)),
+                     dim3(256), 0, st, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                     static_cast<const T*>(a.v), static_cast<const T*>(p.dout), p.lse, Dbuf, a.idx,
+                     a.logg, a.Hq, a.Hkv, a.Hsel, a.share_group, a.nq, a.q_pos0, a.L, a.b, a.K,
+                     static_cast<T*>(p.dq), p.dg);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nblk = (a.L + a.b - 1) / a.b;
+  const dim3 grid(static_cast<unsigned>(nblk), static_cast<unsigned>(a.B * a.Hkv));
+#define SPA_DKDV(BSV)                                                                              \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, BSV>), grid, dim3(256), 0, st, static_cast<const T*>(a.q), \
+                     static_cast<const T*>(a.k), static_cast<const T*>(a.v),                        \
+                     static_cast<const T*>(p.dout), p.lse, Dbuf, a.idx, a.logg, a.Hq, a.Hkv, a.Hsel, \
+                     a.share_group, a.nq, a.q_pos0, a.L, a.K, static_cast<T*>(p.dk),               \
+                     static_cast<T*>(p.dv))
+  if (a.b == 16) SPA_DKDV(16);
+  else if (a.b == 32) SPA_DKDV(32);
+  else SPA_DKDV(64);
+#undef SPA_DKDV
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd(const BwdLaunch& p, void* ws, hipStream_t st) {
+  if (p.a.dtype == 1) return p.a.d == 64 ? launch_bwd_t<bf16_t, 64>(p, ws, st) : launch_bwd_t<bf16_t, 128>(p, ws, st);
+  return p.a.d == 64 ? launch_bwd_t<float, 64>(p, ws, st) : launch_bwd_t<float, 128>(p, ws, st);
+}
+
+}  // namespace spa

@@ -1,0 +1,194 @@
+// spa_device.h -- device helpers shared by the gfx950 kernels of libsparse_attn:
+// element decoding, rounding, orderable score keys and wave-level (64 lane)
+// bitonic networks.  Device code only; no host logic lives here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spa {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// ------------------------------------------------------------- element types
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_float(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// fp64 -> bf16, round to nearest even, without double rounding: first round
+// the double to fp32 with round-to-odd (truncate, then set the sticky bit if
+// anything was cut), which keeps enough bits (24 >= 8 + 2) for the second,
+// nearest-even rounding to 8 significant bits to be exact (Boldo & Melquiond,
+// "Emulation of FMA and correctly rounded sums: proved algorithms using
+// rounding to odd", 2008).
+__device__ __forceinline__ uint16_t double_to_bf16_rne(double x) {
+  float t = __double2float_rz(x);
+  uint32_t u = __float_as_uint(t);
+  if (static_cast<double>(t) != x) u |= 1u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+  static constexpr int kVec = 4;  // elements per 16-byte load
+  __device__ __forceinline__ static float to_float(float x) { return x; }
+  __device__ __forceinline__ static float from_float(float x) { return x; }
+  __device__ __forceinline__ static float from_double(double x) { return __double2float_rn(x); }
+  // unpack a 16-byte vector into kVec floats
+  __device__ __forceinline__ static void unpack(const uint4& v, float* out) {
+    out[0] = __uint_as_float(v.x);
+    out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z);
+    out[3] = __uint_as_float(v.w);
+  }
+};
+
+template <>
+struct Elem<bf16_t> {
+  static constexpr int kVec = 8;
+  __device__ __forceinline__ static float to_float(bf16_t x) { return bf16_to_float(x.bits); }
+  __device__ __forceinline__ static bf16_t from_float(float x) { return bf16_t{float_to_bf16_rne(x)}; }
+  __device__ __forceinline__ static bf16_t from_double(double x) { return bf16_t{double_to_bf16_rne(x)}; }
+  __device__ __forceinline__ static void unpack(const uint4& v, float* out) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ float ld_f(const T* p) {
+  return Elem<T>::to_float(*p);
+}
+
+// --------------------------------------------------------------- score keys
+// A 64-bit key that orders (score desc, index asc) as an unsigned integer:
+// high word = order-preserving image of the fp32 score, low word = ~index.
+// Key 0 is below every real key and marks "no candidate".
+__device__ __forceinline__ uint32_t orderable_f32(float f) {
+  if (f == 0.0f) f = 0.0f;  // +0 and -0 compare equal
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_orderable_f32(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ uint64_t make_key(float score, int32_t index) {
+  return (static_cast<uint64_t>(orderable_f32(score)) << 32) |
+         static_cast<uint64_t>(~static_cast<uint32_t>(index));
+}
+__device__ __forceinline__ int32_t key_index(uint64_t key) {
+  return static_cast<int32_t>(~static_cast<uint32_t>(key & 0xFFFFFFFFull));
+}
+__device__ __forceinline__ float key_score(uint64_t key) {
+  return from_orderable_f32(static_cast<uint32_t>(key >> 32));
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+  lo = __shfl_xor(lo, mask, kWave);
+  hi = __shfl_xor(hi, mask, kWave);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+  lo = __shfl(lo, src, kWave);
+  hi = __shfl(hi, src, kWave);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Sort one key per lane across the wave, descending (lane 0 = largest).
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key, int lane) {
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      uint64_t other = shfl_xor_u64(key, j);
+      bool desc = (lane & k) == 0;
+      bool lower = (lane & j) == 0;
+      uint64_t hi = key > other ? key : other;
+      uint64_t lo = key > other ? other : key;
+      key = (lower == desc) ? hi : lo;
+    }
+  }
+  return key;
+}
+
+// Given two descending wave lists a (this lane's element a[lane]) and
+// b_rev = b[63 - lane], return the descending list of the 64 largest keys of
+// a U b.  max(a[i], b[63-i]) is bitonic and holds the top 64; a bitonic merge
+// sorts it.
+__device__ __forceinline__ uint64_t wave_merge_top_desc(uint64_t a, uint64_t b_rev, int lane) {
+  uint64_t key = a > b_rev ? a : b_rev;
+#pragma unroll
+  for (int j = kWave >> 1; j > 0; j >>= 1) {
+    uint64_t other = shfl_xor_u64(key, j);
+    bool lower = (lane & j) == 0;
+    uint64_t hi = key > other ? key : other;
+    uint64_t lo = key > other ? other : key;
+    key = lower ? hi : lo;
+  }
+  return key;
+}
+
+// Ascending sort of one 32-bit value per lane.
+__device__ __forceinline__ uint32_t wave_sort_asc_u32(uint32_t key, int lane) {
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      uint32_t other = __shfl_xor(key, j, kWave);
+      bool asc = (lane & k) == 0;
+      bool lower = (lane & j) == 0;
+      uint32_t hi = key > other ? key : other;
+      uint32_t lo = key > other ? other : key;
+      key = (lower == asc) ? lo : hi;
+    }
+  }
+  return key;
+}
+
+// ----------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = kWave / 2; m > 0; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = kWave / 2; m > 0; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Online-softmax combine of (m, l) pairs: result represents l e^m.
+__device__ __forceinline__ void ml_combine(float& m, float& l, float m2, float l2) {
+  float mm = fmaxf(m, m2);
+  if (mm == -INFINITY) {
+    m = mm;
+    l = 0.f;
+    return;
+  }
+  l = l * __expf(m - mm) + l2 * __expf(m2 - mm);
+  m = mm;
+}
+
+}  // namespace spa

@@ -1,0 +1,96 @@
+// spa_launch.h -- internal launch descriptors passed from the C-ABI layer
+// (api.hip) to the kernel translation units.  Arguments are already
+// validated when these are filled in.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace spa {
+
+// Candidate blocks of a query row at absolute position pos: blocks before the
+// row's own block (prefix_mode 0) or cells before its query block (mode 1).
+__host__ __device__ inline int64_t num_candidates(int64_t pos, int b, int prefix_mode, int qblock) {
+  return prefix_mode == 0 ? pos / b : (static_cast<int64_t>(qblock) * (pos / qblock)) / b;
+}
+
+struct SummaryLaunch {
+  const void* k;
+  int dtype, B, Hkv;
+  int64_t L;
+  int d, b;
+  int64_t first_block, num_blocks, ccap;
+  void* kbar;
+  float* max_norm;
+  float* centre;
+};
+
+struct SelectLaunch {
+  const void* q;
+  int dtype, B, Hq, Hkv, nq, d;
+  int64_t q_pos0;
+  const void* kbar;
+  const float* max_norm;
+  const float* centre;
+  int64_t ccap;
+  int b, prefix_mode, qblock, share_group;
+  const float* proj_w;
+  const float* erf_lambda;
+  const float* erf_sigma;
+  int K, gate;
+  int32_t* idx;
+  float* logg;
+  int32_t* k_eff;
+  int Hsel;
+  int64_t max_cand;   // candidates of the last row (the largest count)
+};
+
+struct AttnLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  int dtype, B, Hq, Hkv, nq, d;
+  int64_t L, q_pos0;
+  int b, prefix_mode, qblock;
+  const int32_t* idx;
+  const float* logg;
+  int K, share_group, local, window;
+  const float* alpha;
+  void* o;
+  float* lse;
+  int Hsel;
+};
+
+struct BwdLaunch {
+  AttnLaunch a;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+};
+
+// Decode selection: chunked scoring + per-chunk top-K, then a merge.
+constexpr int kDecodeChunk = 256;  // candidate blocks per scoring workgroup
+
+inline int64_t decode_num_chunks(int64_t max_cand) {
+  return (max_cand + kDecodeChunk - 1) / kDecodeChunk;
+}
+
+// Workspace layout helpers (bytes, 256-aligned sections).
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t select_workspace_bytes(const SelectLaunch& p);
+size_t attn_fwd_workspace_bytes(const AttnLaunch& p);
+size_t attn_bwd_workspace_bytes(const BwdLaunch& p);
+
+hipError_t launch_block_summaries(const SummaryLaunch& p, hipStream_t st);
+hipError_t launch_score_select(const SelectLaunch& p, void* ws, hipStream_t st);
+hipError_t launch_attn_fwd(const AttnLaunch& p, void* ws, hipStream_t st);
+hipError_t launch_attn_bwd(const BwdLaunch& p, void* ws, hipStream_t st);
+hipError_t launch_zero_fill(void* ptr, size_t bytes, hipStream_t st);
+
+}  // namespace spa

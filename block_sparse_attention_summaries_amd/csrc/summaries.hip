@@ -1,0 +1,99 @@
+// summaries.hip -- block / cell summaries of the key cache on gfx950.
+//
+// Per (batch, kv head, full block c): mean key (exact fp64 sum, rounded to
+// nearest even in the key dtype), max L2 key norm (fp64, rounded to fp32) and
+// centre position c b + (b-1)/2.  ("SAS" review §3 Eq. 3: pooled block
+// summaries read by the selector; "FreeSolo" review, "How it works": mean
+// key, centre position and max key norm of each cell.)
+//
+// HBM-bound streaming reduction: one 256-thread workgroup per block, 16-byte
+// coalesced loads (a block of b rows x d elements is one contiguous span),
+// fp64 column sums in registers, a cross-lane sum of squares per row and an
+// LDS reduction of the column sums.
+#include "spa_device.h"
+#include "spa_launch.h"
+
+namespace spa {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void block_summaries_kernel(
+    const T* __restrict__ k, int Hkv, int64_t L, int b, int64_t first_block, int64_t num_blocks,
+    int64_t ccap, T* __restrict__ kbar, float* __restrict__ max_norm, float* __restrict__ centre) {
+  constexpr int kVec = Elem<T>::kVec;
+  constexpr int kLanesPerRow = D / kVec;        // lanes covering one key row
+  constexpr int kRowsPerPass = 256 / kLanesPerRow;
+  static_assert(kLanesPerRow <= kWave, "row must fit in one wave");
+
+  __shared__ double s_col[kRowsPerPass][D];
+  __shared__ float s_max[256 / kWave];
+
+  const int64_t c = first_block + blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int cg = tid % kLanesPerRow;            // which kVec columns
+  const int rg = tid / kLanesPerRow;            // which row within a pass
+  const T* base = k + (bh * L + c * b) * D;
+
+  double acc[kVec];
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) acc[i] = 0.0;
+  float best = 0.f;
+
+  for (int r = rg; r < b; r += kRowsPerPass) {
+    uint4 raw = *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(r) * D + cg * kVec);
+    float x[kVec];
+    Elem<T>::unpack(raw, x);
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+      double xd = static_cast<double>(x[i]);
+      acc[i] += xd;
+      ss = fma(xd, xd, ss);
+    }
+    // sum of squares over the lanes of this row (aligned groups of kLanesPerRow)
+#pragma unroll
+    for (int m = kLanesPerRow / 2; m > 0; m >>= 1) ss += __shfl_xor(ss, m, kWave);
+    float nrm = __double2float_rn(sqrt(ss));
+    best = fmaxf(best, nrm);
+  }
+  // rows not covered when b < kRowsPerPass leave acc = 0 and best = 0: harmless.
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) s_col[rg][cg * kVec + i] = acc[i];
+  best = wave_max(best);
+  if ((tid % kWave) == 0) s_max[tid / kWave] = best;
+  __syncthreads();
+
+  const int64_t out = bh * ccap + c;
+  if (tid < D) {
+    double sum = 0.0;
+    const int groups = b < kRowsPerPass ? b : kRowsPerPass;
+    for (int g = 0; g < groups; ++g) sum += s_col[g][tid];
+    kbar[out * D + tid] = Elem<T>::from_double(sum * (1.0 / static_cast<double>(b)));
+  }
+  if (tid == 0) {
+    float m = s_max[0];
+#pragma unroll
+    for (int w = 1; w < 256 / kWave; ++w) m = fmaxf(m, s_max[w]);
+    max_norm[out] = m;
+    if (centre != nullptr && bh == 0)
+      centre[c] = static_cast<float>(static_cast<double>(c) * b + 0.5 * (b - 1));
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_summaries_t(const SummaryLaunch& p, hipStream_t st) {
+  dim3 grid(static_cast<unsigned>(p.num_blocks), static_cast<unsigned>(p.B * p.Hkv));
+  hipLaunchKernelGGL((block_summaries_kernel<T, D>), grid, dim3(256), 0, st,
+                     static_cast<const T*>(p.k), p.Hkv, p.L, p.b, p.first_block, p.num_blocks,
+                     p.ccap, static_cast<T*>(p.kbar), p.max_norm, p.centre);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_summaries(const SummaryLaunch& p, hipStream_t st) {
+  if (p.dtype == 1) {
+    return p.d == 64 ? launch_summaries_t<bf16_t, 64>(p, st) : launch_summaries_t<bf16_t, 128>(p, st);
+  }
+  return p.d == 64 ? launch_summaries_t<float, 64>(p, st) : launch_summaries_t<float, 128>(p, st);
+}
+
+}  // namespace spa

@@ -1,0 +1,240 @@
+"""Thin Python binding of libsparse_attn.so (C ABI in include/sparse_attn.h).
+
+Argument marshalling only: PyTorch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is missing or its call fails, these
+functions raise.
+
+Function names match the C entry points: sparse_block_summaries,
+sparse_score_select, sparse_attn_fwd, sparse_attn_bwd.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
+
+SPA_OK, SPA_ERR_INVALID_ARG, SPA_ERR_UNSUPPORTED, SPA_ERR_HIP, SPA_ERR_WORKSPACE = 0, -1, -2, -3, -4
+SPA_DTYPE_F32, SPA_DTYPE_BF16 = 0, 1
+SPA_PREFIX_CURRENT_BLOCK, SPA_PREFIX_QUERY_BLOCK = 0, 1
+SPA_GATE_NONE, SPA_GATE_SOFTMAX_LOG = 0, 1
+SPA_LOCAL_CURRENT_BLOCK, SPA_LOCAL_NONE = 0, 1
+SPA_OP_SCORE_SELECT, SPA_OP_ATTN_FWD, SPA_OP_ATTN_BWD = 1, 2, 3
+
+EXPORTED = ["spa_abi_version", "spa_last_error", "sparse_block_summaries", "sparse_score_select",
+            "sparse_attn_fwd", "sparse_attn_bwd", "sparse_workspace_bytes", "sparse_workspace_init"]
+
+_vp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+
+
+class SelectArgs(ctypes.Structure):
+    _fields_ = [("q", _vp), ("dtype", _i), ("B", _i), ("Hq", _i), ("Hkv", _i), ("nq", _i), ("d", _i),
+                ("q_pos0", _i64), ("kbar", _vp), ("max_norm", _vp), ("centre", _vp), ("ccap", _i64),
+                ("b", _i), ("prefix_mode", _i), ("qblock", _i), ("share_group", _i), ("proj_w", _vp),
+                ("erf_lambda", _vp), ("erf_sigma", _vp), ("K", _i), ("gate", _i), ("idx", _vp),
+                ("logg", _vp), ("k_eff", _vp)]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [("q", _vp), ("k", _vp), ("v", _vp), ("dtype", _i), ("B", _i), ("Hq", _i), ("Hkv", _i),
+                ("nq", _i), ("d", _i), ("L", _i64), ("q_pos0", _i64), ("b", _i), ("prefix_mode", _i),
+                ("qblock", _i), ("idx", _vp), ("logg", _vp), ("K", _i), ("share_group", _i),
+                ("local", _i), ("window", _i), ("alpha", _vp), ("o", _vp), ("lse", _vp)]
+
+
+class SpaError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"libsparse_attn error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load libsparse_attn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(hipcc --offload-arch=gfx950); there is no CPU fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        L.spa_abi_version.restype = _i
+        L.spa_abi_version.argtypes = []
+        L.spa_last_error.restype = ctypes.c_char_p
+        L.spa_last_error.argtypes = []
+        L.sparse_block_summaries.restype = _i
+        L.sparse_block_summaries.argtypes = [_vp, _i, _i, _i, _i64, _i, _i, _i64, _i64, _i64, _vp, _vp,
+                                             _vp, _vp]
+        L.sparse_score_select.restype = _i
+        L.sparse_score_select.argtypes = [ctypes.POINTER(SelectArgs), _vp, _sz, _vp]
+        L.sparse_attn_fwd.restype = _i
+        L.sparse_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), _vp, _sz, _vp]
+        L.sparse_attn_bwd.restype = _i
+        L.sparse_attn_bwd.argtypes = [ctypes.POINTER(AttnArgs), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _sz, _vp]
+        L.sparse_workspace_bytes.restype = _sz
+        L.sparse_workspace_bytes.argtypes = [_i, _vp]
+        L.sparse_workspace_init.restype = _i
+        L.sparse_workspace_init.argtypes = [_vp, _sz, _vp]
+        _lib = L
+    return _lib
+
+
+def _check(code):
+    if code != SPA_OK:
+        raise SpaError(code, lib().spa_last_error().decode())
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype(t):
+    if t.dtype == torch.bfloat16:
+        return SPA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return SPA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors passed to libsparse_attn must be contiguous")
+
+
+class Workspace:
+    """A zero-initialised device buffer reused across calls (grown on demand).
+    Calls that share one Workspace must not overlap in time."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes):
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes:
+            n = (nbytes + 255) // 256 * 256
+            self.buf = torch.zeros(n, dtype=torch.uint8, device=self.device)
+        return self.buf, self.buf.numel()
+
+
+_default_ws = {}
+
+
+def _ws(workspace, op, args, device):
+    need = lib().sparse_workspace_bytes(op, ctypes.byref(args))
+    if need == 0:          # none needed (invalid arguments are reported by the call itself)
+        return None, 0
+    if workspace is None:
+        key = (str(device), op)
+        workspace = _default_ws.setdefault(key, Workspace(device))
+    buf, size = workspace.get(need)
+    return buf, size
+
+
+def sparse_block_summaries(k, b, first_block=0, num_blocks=None, ccap=None, kbar=None,
+                           max_norm=None, centre=None, stream=None):
+    """Summaries of full blocks [first_block, first_block + num_blocks) of
+    k [B, Hkv, L, d]: mean key (k dtype), max key norm (fp32), centre (fp32).
+    Outputs are allocated when not given (kbar [B,Hkv,ccap,d], max_norm
+    [B,Hkv,ccap], centre [ccap])."""
+    _contig(k, kbar, max_norm, centre)
+    B, Hkv, L, d = k.shape
+    if num_blocks is None:
+        num_blocks = L // b - first_block
+    if ccap is None:
+        ccap = kbar.shape[2] if kbar is not None else first_block + num_blocks
+    if kbar is None:
+        kbar = torch.zeros((B, Hkv, ccap, d), dtype=k.dtype, device=k.device)
+    if max_norm is None:
+        max_norm = torch.zeros((B, Hkv, ccap), dtype=torch.float32, device=k.device)
+    if centre is None:
+        centre = torch.zeros((ccap,), dtype=torch.float32, device=k.device)
+    _check(lib().sparse_block_summaries(_p(k), _dtype(k), B, Hkv, L, d, b, first_block, num_blocks,
+                                        ccap, _p(kbar), _p(max_norm), _p(centre), _stream(stream)))
+    return kbar, max_norm, centre
+
+
+def select_args(q, kbar, max_norm, centre, *, Hkv, b, K, q_pos0, gate=True, prefix_mode=0,
+                qblock=128, share_group=True, proj_w=None, erf_lambda=None, erf_sigma=None,
+                idx=None, logg=None, k_eff=None):
+    _contig(q, kbar, max_norm, centre, proj_w, erf_lambda, erf_sigma, idx, logg, k_eff)
+    B, Hq, nq, d = q.shape
+    Hsel = Hkv if share_group else Hq
+    dev = q.device
+    if idx is None:
+        idx = torch.empty((B, Hsel, nq, K), dtype=torch.int32, device=dev)
+    if logg is None and gate:
+        logg = torch.empty((B, Hsel, nq, K), dtype=torch.float32, device=dev)
+    if k_eff is None:
+        k_eff = torch.empty((B, Hsel, nq), dtype=torch.int32, device=dev)
+    a = SelectArgs(q=_p(q), dtype=_dtype(q), B=B, Hq=Hq, Hkv=Hkv, nq=nq, d=d, q_pos0=q_pos0,
+                   kbar=_p(kbar), max_norm=_p(max_norm), centre=_p(centre), ccap=kbar.shape[2], b=b,
+                   prefix_mode=prefix_mode, qblock=qblock, share_group=int(bool(share_group)),
+                   proj_w=_p(proj_w), erf_lambda=_p(erf_lambda), erf_sigma=_p(erf_sigma), K=K,
+                   gate=int(bool(gate)), idx=_p(idx), logg=_p(logg), k_eff=_p(k_eff))
+    return a, (idx, logg, k_eff)
+
+
+def sparse_score_select(q, kbar, max_norm, centre, *, workspace=None, stream=None, **kw):
+    """Scores + softmax log gate + top-K for every row of q [B, Hq, nq, d].
+    Returns (idx [B,Hsel,nq,K] int32, logg fp32 or None, k_eff int32)."""
+    a, outs = select_args(q, kbar, max_norm, centre, **kw)
+    buf, size = _ws(workspace, SPA_OP_SCORE_SELECT, a, q.device)
+    _check(lib().sparse_score_select(ctypes.byref(a), _p(buf), size, _stream(stream)))
+    return outs
+
+
+def attn_args(q, k, v, idx, logg, *, b, K, q_pos0, share_group=True, local=0, window=0,
+              alpha=None, prefix_mode=0, qblock=128, o=None, lse=None):
+    _contig(q, k, v, idx, logg, alpha, o, lse)
+    B, Hq, nq, d = q.shape
+    _, Hkv, L, _ = k.shape
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, nq), dtype=torch.float32, device=q.device)
+    a = AttnArgs(q=_p(q), k=_p(k), v=_p(v), dtype=_dtype(q), B=B, Hq=Hq, Hkv=Hkv, nq=nq, d=d, L=L,
+                 q_pos0=q_pos0, b=b, prefix_mode=prefix_mode, qblock=qblock, idx=_p(idx),
+                 logg=_p(logg), K=K, share_group=int(bool(share_group)), local=local, window=window,
+                 alpha=_p(alpha), o=_p(o), lse=_p(lse))
+    return a, (o, lse)
+
+
+def sparse_attn_fwd(q, k, v, idx, logg, *, workspace=None, stream=None, **kw):
+    """Exact softmax attention over the current block + selected blocks (or the
+    routed-cell branch mixed with a window).  Returns (o, lse)."""
+    a, outs = attn_args(q, k, v, idx, logg, **kw)
+    buf, size = _ws(workspace, SPA_OP_ATTN_FWD, a, q.device)
+    _check(lib().sparse_attn_fwd(ctypes.byref(a), _p(buf), size, _stream(stream)))
+    return outs
+
+
+def sparse_attn_bwd(q, k, v, idx, logg, o, dout, lse, *, dq=None, dk=None, dv=None, dg=None,
+                    workspace=None, stream=None, **kw):
+    """Backward of sparse_attn_fwd (current block + selected blocks with the log
+    gate).  Returns (dq, dk, dv, dg)."""
+    _contig(o, dout, lse, dq, dk, dv, dg)
+    a, _ = attn_args(q, k, v, idx, logg, o=o, lse=lse, **kw)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if dg is None:
+        dg = torch.empty(idx.shape, dtype=torch.float32, device=q.device)
+    buf, size = _ws(workspace, SPA_OP_ATTN_BWD, a, q.device)
+    _check(lib().sparse_attn_bwd(ctypes.byref(a), _p(o), _p(dout), _p(lse), _p(dq), _p(dk), _p(dv),
+                                 _p(dg), _p(buf), size, _stream(stream)))
+    return dq, dk, dv, dg

@@ -1,0 +1,220 @@
+/*
+ * sparse_attn.h -- C ABI of the MI355X (gfx950) block-sparse causal attention
+ * library with learned block selection (libsparse_attn.so).
+ *
+ * What it computes (pages of the reference, cited by title and section):
+ *  - "SAS: Simple Attention Sparsification via End-to-End Optimization of
+ *    Context Ranking" (review page): §3 Eq. 1-3 (attention restricted to a
+ *    selected block set; n positions split into C = n/b blocks; a selector
+ *    scores every block, the top K are kept), §4.1 Eq. 4 (the current block
+ *    B0 is always kept with gate 1), §4.2.2 (softmax gate
+ *    log g = s - LSE(s); inner-gate gradient Eq. 5), §4.3 Eq. 9 (log g added
+ *    to the logits of the selected blocks inside the softmax), Alg. 1-2.
+ *  - "FreeSolo ... zero-shot retrieval up to 64x the training length"
+ *    (review page), "How it works": cells of s tokens summarised by mean key,
+ *    centre position and max key norm; query-block prefix of B tokens;
+ *    r_ic = q_i.kbar_c/sqrt(d) + lambda_h a_c erf((i - p_c)/(2 sigma_h));
+ *    top-K cells read with one softmax; sliding window of w tokens; per-head
+ *    alpha_h mix of the two branches.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers, row-major and contiguous:
+ *      q, o, dq, dout   [B, Hq,  nq, d]
+ *      k, v, dk, dv     [B, Hkv, L,  d]
+ *      kbar             [B, Hkv, ccap, d]     (same dtype as k)
+ *      max_norm         [B, Hkv, ccap]        fp32
+ *      centre           [ccap]                fp32
+ *      idx              [B, Hsel, nq, K]      int32, ascending, -1 padded
+ *      logg, dg         [B, Hsel, nq, K]      fp32
+ *      k_eff            [B, Hsel, nq]         int32
+ *      lse              [B, Hq, nq]           fp32
+ *    with Hsel = Hkv when share_group != 0 (one selection per kv head from
+ *    the mean of its G = Hq/Hkv query heads) and Hsel = Hq otherwise.
+ *  - Query row r sits at absolute position i = q_pos0 + r of the K/V
+ *    sequence (q_pos0 + nq <= L); decode is nq = 1, q_pos0 = L - 1.
+ *  - Candidates of row i: prefix_mode SPA_PREFIX_CURRENT_BLOCK: blocks
+ *    c < floor(i/b); SPA_PREFIX_QUERY_BLOCK: cells with
+ *    (c+1) b <= qblock floor(i/qblock).
+ *  - Selection order: higher score first, lower index on equal scores;
+ *    K_eff = min(K, #candidates) indices are stored ascending.
+ *  - Dot products are scaled by 1/sqrt(d).
+ *  - dtype: SPA_DTYPE_F32 or SPA_DTYPE_BF16; d in {64, 128}; b a power of two
+ *    in [16, 128]; 1 <= K <= 64; Hq a multiple of Hkv with G <= 8.
+ *
+ * Ownership: the caller allocates and frees every buffer (tensors and
+ * workspace).  The library never allocates, frees or synchronises, never
+ * reads device memory on the host, and launches only on the given stream
+ * (spa_stream_t is a hipStream_t; NULL means the null stream).  Calls are
+ * safe to capture in a HIP graph.
+ *
+ * Errors: every entry point validates its arguments before launching
+ * anything and returns a spa_status.  On error nothing is launched and
+ * spa_last_error() returns a message (per calling thread).  Launch failures
+ * reported by the HIP runtime return SPA_ERR_HIP.  Kernels never trap: block
+ * indices outside a row's candidate set are ignored.  NaN/Inf inputs give
+ * unspecified values but never out-of-bounds accesses.
+ *
+ * Workspace: sparse_workspace_bytes() gives the size a call needs;
+ * a workspace must be zero-filled once before its first use
+ * (sparse_workspace_init does it with a kernel); every call leaves it in that
+ * state again.  Calls that overlap in time must use distinct workspaces.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPA_ABI_VERSION 1
+
+typedef void *spa_stream_t;
+
+typedef enum {
+    SPA_OK = 0,
+    SPA_ERR_INVALID_ARG = -1,  /* null pointer, bad shape/size, out-of-range parameter */
+    SPA_ERR_UNSUPPORTED = -2,  /* valid but not implemented combination (dtype, d, mode) */
+    SPA_ERR_HIP = -3,          /* the HIP runtime reported a launch error */
+    SPA_ERR_WORKSPACE = -4     /* workspace null or smaller than sparse_workspace_bytes() */
+} spa_status;
+
+typedef enum { SPA_DTYPE_F32 = 0, SPA_DTYPE_BF16 = 1 } spa_dtype;
+typedef enum { SPA_PREFIX_CURRENT_BLOCK = 0, SPA_PREFIX_QUERY_BLOCK = 1 } spa_prefix_mode;
+typedef enum { SPA_GATE_NONE = 0, SPA_GATE_SOFTMAX_LOG = 1 } spa_gate;
+typedef enum { SPA_LOCAL_CURRENT_BLOCK = 0, SPA_LOCAL_NONE = 1 } spa_local;
+typedef enum { SPA_OP_SCORE_SELECT = 1, SPA_OP_ATTN_FWD = 2, SPA_OP_ATTN_BWD = 3 } spa_op;
+
+/* Version of this ABI (SPA_ABI_VERSION). */
+int spa_abi_version(void);
+
+/* Message describing the last failed call made by this thread ("" if none).
+ * The pointer stays valid until the next call on the same thread. */
+const char *spa_last_error(void);
+
+/*
+ * sparse_block_summaries -- per (batch, kv head, full block c) in
+ * [first_block, first_block + num_blocks):
+ *   kbar[c]     = mean of the b keys of block c, computed exactly (fp64 sum)
+ *                 and rounded to nearest even in the key dtype;
+ *   max_norm[c] = max over the block of ||k_j||_2 (fp64, rounded to fp32);
+ *   centre[c]   = c b + (b - 1)/2 (centre may be NULL).
+ * ("SAS" review §3 Eq. 3 block partition with pooled key summaries; "FreeSolo"
+ * review, "How it works": mean key, centre position, max key norm.)
+ * Every summarised block must be full: (first_block + num_blocks) b <= L,
+ * and first_block + num_blocks <= ccap.  Decode calls it with num_blocks = 1
+ * when a block closes.  Output rows outside the range are not touched.
+ * Returns SPA_ERR_INVALID_ARG on null pointers or out-of-range sizes.
+ */
+int sparse_block_summaries(const void *k, int dtype, int B, int Hkv, int64_t L, int d,
+                           int b, int64_t first_block, int64_t num_blocks, int64_t ccap,
+                           void *kbar, float *max_norm, float *centre,
+                           spa_stream_t stream);
+
+typedef struct spa_select_args {
+    const void *q;            /* [B, Hq, nq, d], dtype */
+    int dtype;                /* spa_dtype of q and kbar */
+    int B, Hq, Hkv, nq, d;
+    int64_t q_pos0;           /* absolute position of query row 0 */
+    const void *kbar;         /* [B, Hkv, ccap, d] */
+    const float *max_norm;    /* [B, Hkv, ccap]; required when erf_lambda != NULL */
+    const float *centre;      /* [ccap]; required when erf_lambda != NULL */
+    int64_t ccap;             /* rows allocated in kbar; must cover every candidate */
+    int b;                    /* block / cell size */
+    int prefix_mode;          /* spa_prefix_mode */
+    int qblock;               /* query-block size for SPA_PREFIX_QUERY_BLOCK */
+    int share_group;          /* 1: selection per kv head from the mean of its G q heads */
+    const float *proj_w;      /* NULL or [d, d] fp32 W: score uses W kbar_c */
+    const float *erf_lambda;  /* NULL or [Hsel] fp32: adds lambda a_c erf((i-p_c)/(2 sigma)) */
+    const float *erf_sigma;   /* [Hsel] fp32 (required with erf_lambda), > 0 */
+    int K;                    /* budget in blocks, 1..64 */
+    int gate;                 /* spa_gate */
+    int32_t *idx;             /* out [B, Hsel, nq, K] */
+    float *logg;              /* out [B, Hsel, nq, K]: s_c - LSE over all candidates, 0 in pads;
+                                 may be NULL when gate == SPA_GATE_NONE */
+    int32_t *k_eff;           /* out [B, Hsel, nq], may be NULL */
+} spa_select_args;
+
+/*
+ * sparse_score_select -- scores, optional softmax log gate and top-K block
+ * selection for every query row ("SAS" review §3 Eq. 3, §4.2.2 softmax gate,
+ * Alg. 1 and the worked example; "FreeSolo" review cell score with the erf
+ * position bias).  Score of candidate c for row i and selection head hs:
+ *   s_c = q_hat . ktilde_c / sqrt(d)  [+ lambda_hs a_c erf((i - p_c)/(2 sigma_hs))]
+ * q_hat = q_hs or the mean of the G query heads of kv head hs; ktilde = kbar
+ * or W kbar.  Needs a workspace of sparse_workspace_bytes(SPA_OP_SCORE_SELECT).
+ */
+int sparse_score_select(const spa_select_args *a, void *workspace, size_t ws_bytes,
+                        spa_stream_t stream);
+
+typedef struct spa_attn_args {
+    const void *q;            /* [B, Hq, nq, d] */
+    const void *k;            /* [B, Hkv, L, d] */
+    const void *v;            /* [B, Hkv, L, d] */
+    int dtype;                /* spa_dtype of q, k, v, o (and dq, dk, dv, dout) */
+    int B, Hq, Hkv, nq, d;
+    int64_t L;                /* tokens in K / V */
+    int64_t q_pos0;           /* absolute position of query row 0 */
+    int b;                    /* block / cell size of idx */
+    int prefix_mode;          /* candidate rule used to validate idx entries */
+    int qblock;
+    const int32_t *idx;       /* [B, Hsel, nq, K] selected units (entries that are not
+                                 candidates of their row are ignored) */
+    const float *logg;        /* NULL (no bias) or [B, Hsel, nq, K] log gates */
+    int K;
+    int share_group;
+    int local;                /* spa_local: SPA_LOCAL_CURRENT_BLOCK keeps B0 causally */
+    int window;               /* 0, or sliding-window width w (keys i-w < j <= i) */
+    const float *alpha;       /* NULL, or [Hq] mix: o = alpha o_L + (1 - alpha) o_S */
+    void *o;                  /* out [B, Hq, nq, d] */
+    float *lse;               /* out [B, Hq, nq] log-sum-exp of branch L, may be NULL */
+} spa_attn_args;
+
+/*
+ * sparse_attn_fwd -- exact softmax attention of every query row over
+ *   branch L: the current block {j : floor(j/b) = floor(i/b), j <= i}
+ *             (local = SPA_LOCAL_CURRENT_BLOCK, bias 0) plus every selected
+ *             unit, each logit biased by its log g ("SAS" review §4.3 Eq. 9;
+ *             "Monodratic" news page: local block + exact causal softmax on
+ *             the selected set);
+ *   branch S: keys i - w < j <= i (window > 0), mixed with alpha
+ *             ("FreeSolo" review, two-branch head).
+ * Supported modes: (local = CURRENT_BLOCK, window = 0, alpha = NULL) and
+ * (local = NONE, window > 0, alpha != NULL).  A row with no key in branch L
+ * gets o_L = 0 and lse = -inf.  nq = 1 uses the split-K decode kernels.
+ */
+int sparse_attn_fwd(const spa_attn_args *a, void *workspace, size_t ws_bytes,
+                    spa_stream_t stream);
+
+/*
+ * sparse_attn_bwd -- backward of sparse_attn_fwd in the SAS mode
+ * (local = CURRENT_BLOCK, window = 0, alpha = NULL), recomputing the
+ * probabilities from lse:
+ *   D_i = do_i . o_i,  dS_ij = p_ij (do_i . v_j - D_i),
+ *   dq = sum_j dS k_j / sqrt(d), dk_j = sum_i dS q_i / sqrt(d),
+ *   dv_j = sum_i p_ij do_i,
+ *   dg[slot of block m] = sum_{j in B_m} dS_ij / g_m  ("SAS" review §4.2.2
+ *   Eq. 5, inner gate), summed over the query heads sharing the selection.
+ * o and lse are the outputs of sparse_attn_fwd on the same arguments.
+ * dq, dk, dv are written (not accumulated) in the input dtype; dg in fp32
+ * (0 in padded slots; with logg NULL the gradient is taken at g = 1).
+ */
+int sparse_attn_bwd(const spa_attn_args *a, const void *o, const void *dout,
+                    const float *lse, void *dq, void *dk, void *dv, float *dg,
+                    void *workspace, size_t ws_bytes, spa_stream_t stream);
+
+/* Workspace bytes needed by `op` (spa_op) for the given argument struct
+ * (spa_select_args* for SPA_OP_SCORE_SELECT, spa_attn_args* otherwise).
+ * Returns 0 for invalid arguments (see spa_last_error()). */
+size_t sparse_workspace_bytes(int op, const void *args);
+
+/* Zero-fill a workspace with a kernel on `stream` (graph-capture safe). */
+int sparse_workspace_init(void *workspace, size_t ws_bytes, spa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

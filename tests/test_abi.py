@@ -1,0 +1,143 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every entry point declared in include/sparse_attn.h, and rejects invalid
+arguments with the documented status codes before launching anything."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_summaries_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced (validation fails first)
+FAKE_ODD = ctypes.c_void_p(0x10001)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_]+)\s*\([^;{]*\)\s*;", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ops.lib()
+    names = declared_functions()
+    assert set(names) == set(ops.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.spa_abi_version() == 1
+
+
+def _sel(**kw):
+    a = ops.SelectArgs(q=FAKE, dtype=1, B=1, Hq=32, Hkv=8, nq=1, d=128, q_pos0=32831, kbar=FAKE,
+                       max_norm=FAKE, centre=FAKE, ccap=513, b=64, prefix_mode=0, qblock=128,
+                       share_group=1, proj_w=None, erf_lambda=None, erf_sigma=None, K=16, gate=1,
+                       idx=FAKE, logg=FAKE, k_eff=None)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _attn(**kw):
+    a = ops.AttnArgs(q=FAKE, k=FAKE, v=FAKE, dtype=1, B=1, Hq=32, Hkv=8, nq=1, d=128, L=32832,
+                     q_pos0=32831, b=64, prefix_mode=0, qblock=128, idx=FAKE, logg=FAKE, K=16,
+                     share_group=1, local=0, window=0, alpha=None, o=FAKE, lse=FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _select_status(a, ws=None, n=0):
+    return ops.lib().sparse_score_select(ctypes.byref(a), ws, n, None)
+
+
+def _attn_status(a, ws=None, n=0):
+    return ops.lib().sparse_attn_fwd(ctypes.byref(a), ws, n, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), ops.SPA_ERR_INVALID_ARG),
+    (dict(idx=None), ops.SPA_ERR_INVALID_ARG),
+    (dict(q=FAKE_ODD), ops.SPA_ERR_INVALID_ARG),
+    (dict(d=96), ops.SPA_ERR_UNSUPPORTED),
+    (dict(dtype=7), ops.SPA_ERR_UNSUPPORTED),
+    (dict(b=48), ops.SPA_ERR_UNSUPPORTED),
+    (dict(b=256), ops.SPA_ERR_UNSUPPORTED),
+    (dict(K=0), ops.SPA_ERR_UNSUPPORTED),
+    (dict(K=65), ops.SPA_ERR_UNSUPPORTED),
+    (dict(Hq=30), ops.SPA_ERR_INVALID_ARG),          # G does not divide
+    (dict(Hq=8 * 16), ops.SPA_ERR_UNSUPPORTED),      # G = 16
+    (dict(logg=None), ops.SPA_ERR_INVALID_ARG),      # gate on needs logg
+    (dict(gate=3), ops.SPA_ERR_INVALID_ARG),
+    (dict(ccap=100), ops.SPA_ERR_INVALID_ARG),       # candidates beyond kbar
+    (dict(erf_lambda=FAKE), ops.SPA_ERR_INVALID_ARG),  # sigma missing
+    (dict(prefix_mode=1, qblock=100), ops.SPA_ERR_INVALID_ARG),
+    (dict(nq=0), ops.SPA_ERR_INVALID_ARG),
+])
+def test_select_rejects_invalid_arguments(kw, code):
+    assert _select_status(_sel(**kw)) == code
+    assert ops.lib().spa_last_error().decode() != ""
+
+
+def test_select_workspace_too_small():
+    a = _sel()
+    need = ops.lib().sparse_workspace_bytes(ops.SPA_OP_SCORE_SELECT, ctypes.byref(a))
+    # decode path: 512 candidates -> 8 heads x 2 chunks of 256 blocks x K keys + (m, l) per chunk
+    assert need == 256 * ((8 * 2 * 16 * 8 + 255) // 256) + 256 * ((8 * 2 * 8 + 255) // 256)
+    assert _select_status(a, None, 0) == ops.SPA_ERR_WORKSPACE
+    assert _select_status(a, FAKE, need - 1) == ops.SPA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v=None), ops.SPA_ERR_INVALID_ARG),
+    (dict(o=None), ops.SPA_ERR_INVALID_ARG),
+    (dict(q_pos0=32832), ops.SPA_ERR_INVALID_ARG),   # row beyond L
+    (dict(local=1), ops.SPA_ERR_UNSUPPORTED),         # no window, no alpha
+    (dict(window=512), ops.SPA_ERR_UNSUPPORTED),      # window without alpha / local
+    (dict(d=32), ops.SPA_ERR_UNSUPPORTED),
+    (dict(b=24), ops.SPA_ERR_UNSUPPORTED),
+])
+def test_attn_rejects_invalid_arguments(kw, code):
+    assert _attn_status(_attn(**kw)) == code
+
+
+def test_attn_workspace_sizes():
+    a = _attn()
+    need = ops.lib().sparse_workspace_bytes(ops.SPA_OP_ATTN_FWD, ctypes.byref(a))
+    # decode split-K: 8 heads x 17 tiles x 4 q heads x (128 acc floats) + (m, l)
+    acc = 8 * 17 * 4 * 128 * 4
+    ml = 8 * 17 * 4 * 8
+    assert need == 256 * ((acc + 255) // 256) + 256 * ((ml + 255) // 256)
+    assert _attn_status(a, None, 0) == ops.SPA_ERR_WORKSPACE
+    pre = _attn(nq=8192, q_pos0=0, L=8192)
+    assert ops.lib().sparse_workspace_bytes(ops.SPA_OP_ATTN_FWD, ctypes.byref(pre)) == 0
+    assert ops.lib().sparse_workspace_bytes(ops.SPA_OP_ATTN_BWD, ctypes.byref(pre)) == 32 * 8192 * 4
+
+
+def test_bwd_rejects_unsupported_modes():
+    lib = ops.lib()
+    a = _attn(nq=256, q_pos0=0, L=256, local=1, window=64, alpha=FAKE)
+    assert lib.sparse_attn_bwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                               None) == ops.SPA_ERR_UNSUPPORTED
+    a = _attn(nq=256, q_pos0=0, L=256, b=128)
+    assert lib.sparse_attn_bwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                               None) == ops.SPA_ERR_UNSUPPORTED
+    a = _attn(nq=256, q_pos0=0, L=256)
+    assert lib.sparse_attn_bwd(ctypes.byref(a), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                               None) == ops.SPA_ERR_INVALID_ARG
+
+
+def test_summaries_rejects_invalid_arguments():
+    lib = ops.lib()
+    f = lib.sparse_block_summaries
+    assert f(None, 1, 1, 8, 4096, 128, 64, 0, 64, 64, FAKE, FAKE, None, None) == ops.SPA_ERR_INVALID_ARG
+    assert f(FAKE, 1, 1, 8, 4096, 128, 64, 0, 65, 65, FAKE, FAKE, None, None) == ops.SPA_ERR_INVALID_ARG
+    assert f(FAKE, 1, 1, 8, 4096, 128, 64, 0, 64, 63, FAKE, FAKE, None, None) == ops.SPA_ERR_INVALID_ARG
+    assert f(FAKE, 1, 1, 8, 4096, 100, 64, 0, 64, 64, FAKE, FAKE, None, None) == ops.SPA_ERR_UNSUPPORTED
+    assert f(FAKE, 1, 1, 8, 4096, 128, 64, 0, 0, 64, FAKE, FAKE, None, None) == ops.SPA_OK  # nothing to do
+    assert ops.lib().spa_last_error().decode() == ""

@@ -1,0 +1,372 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 CPU oracle
+on the same seeded inputs.
+
+Bars: summaries bit-exact; selected indices bit-exact except rows whose
+oracle K-boundary gap is below 1e-6; outputs and gradients within a relative
+error (per (batch, head) slice, max-norm) of 2e-2 for bf16 inputs and 1e-4 for
+fp32 inputs.  Attention and backward parity feed the oracle's selection to
+both sides, so they test attention alone; the end-to-end cases chain the
+GPU's own summaries -> selection -> attention and compare the rows whose
+selection matches.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from block_sparse_attention_summaries_amd import ops
+from block_sparse_attention_summaries_amd.inputs import config, make_inputs
+from tests.gpu_util import as_f64, check_indices, dev, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _tol(cfg):
+    return TOL[cfg["dtype"]]
+
+
+# ------------------------------------------------------------------ summaries
+SUMMARY_CASES = [
+    ("tiny_decode", {}),
+    ("decode_32k", {}),
+    ("prefill_cells", dict(n=2048, Hq=4, Hkv=4)),
+    ("train", dict(B=2, n=1024, Hq=8, Hkv=2)),
+    ("train", dict(B=1, n=1024, Hq=4, Hkv=2, b=16, d=64)),
+    ("tiny_decode", dict(b=32, d=128)),
+]
+
+
+@pytest.mark.parametrize("name,over", SUMMARY_CASES)
+def test_summaries_bit_exact(name, over):
+    cfg = config(name, **over)
+    _say(f"[summaries] {name} {over}")
+    x = make_inputs(cfg)
+    k, b = x["k"], cfg["b"]
+    nblk = x["L"] // b
+    kb_o, mx_o, ce_o = oracle.block_summaries(k, b, nblocks=nblk)
+    kb_g, mx_g, ce_g = ops.sparse_block_summaries(dev(k), b)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(kb_g), kb_o)
+    assert np.array_equal(host(mx_g), mx_o)
+    assert np.array_equal(host(ce_g), ce_o)
+
+
+def test_summaries_incremental_range_only():
+    cfg = config("decode_32k", n=4096)
+    x = make_inputs(cfg)
+    k, b = x["k"], cfg["b"]
+    ccap = x["L"] // b
+    kb_o, mx_o, _ = oracle.block_summaries(k, b, nblocks=ccap)
+    kbar = torch.full((1, 8, ccap, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    mx = torch.full((1, 8, ccap), -1.0, device="cuda")
+    ops.sparse_block_summaries(dev(k), b, first_block=5, num_blocks=4, kbar=kbar, max_norm=mx)
+    kb, m = host(kbar), host(mx)
+    assert np.array_equal(kb[:, :, 5:9], kb_o[:, :, 5:9])
+    assert np.array_equal(m[:, :, 5:9], mx_o[:, :, 5:9])
+    untouched = np.ones(ccap, bool)
+    untouched[5:9] = False
+    assert np.all(as_f64(kb[:, :, untouched]) == 7.0) and np.all(m[:, :, untouched] == -1.0)
+
+
+def test_summaries_full_512k():
+    cfg = config("decode_512k")
+    _say("[summaries] decode_512k full size")
+    x = make_inputs(cfg)
+    b = cfg["b"]
+    nblk = x["L"] // b
+    kb_o, mx_o, _ = oracle.block_summaries(x["k"], b, nblocks=nblk)
+    kb_g, mx_g, _ = ops.sparse_block_summaries(dev(x["k"]), b)
+    assert np.array_equal(host(kb_g), kb_o)
+    assert np.array_equal(host(mx_g), mx_o)
+
+
+# ------------------------------------------------------------------ decode
+def _decode_run(cfg, x, K=None):
+    """GPU chain and oracle chain for one decode step."""
+    K = K or cfg["K"]
+    b, L = cfg["b"], x["L"]
+    nblk = L // b
+    q_pos0 = x["q_pos0"]
+    gate = cfg["gate"]
+    proj = x.get("proj_w")
+    kw = dict(Hkv=cfg["Hkv"], b=b, K=K, q_pos0=q_pos0, gate=gate, share_group=cfg["share_group"])
+    kb_o, mx_o, ce_o = oracle.block_summaries(x["k"], b, nblocks=nblk, ccap=max(nblk, 1))
+    ora = oracle.score_select(x["q"], kb_o, mx_o, ce_o, proj_w=proj, **kw)
+    o_o, lse_o = oracle.attn_fwd(x["q"], x["k"], x["v"], ora["idx"], ora["logg"] if gate else None,
+                                 b=b, K=K, q_pos0=q_pos0, share_group=cfg["share_group"])
+    qd, kd, vd = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    kb_g, mx_g, ce_g = ops.sparse_block_summaries(kd, b, num_blocks=max(nblk, 1) if nblk else 0,
+                                                  ccap=max(nblk, 1))
+    idx_g, logg_g, keff_g = ops.sparse_score_select(qd, kb_g, mx_g, ce_g,
+                                                    proj_w=None if proj is None else dev(proj), **kw)
+    o_g, lse_g = ops.sparse_attn_fwd(qd, kd, vd, idx_g, logg_g if gate else None, b=b, K=K,
+                                     q_pos0=q_pos0, share_group=cfg["share_group"])
+    # attention alone, on the oracle's selection
+    lg_in = dev(ora["logg"].astype(np.float32)) if gate else None
+    o_g2, lse_g2 = ops.sparse_attn_fwd(qd, kd, vd, dev(ora["idx"]), lg_in, b=b, K=K, q_pos0=q_pos0,
+                                       share_group=cfg["share_group"])
+    torch.cuda.synchronize()
+    return dict(ora=ora, o_o=o_o, lse_o=lse_o, idx=host(idx_g), logg=None if logg_g is None else host(logg_g),
+                keff=host(keff_g), o=host(o_g), lse=host(lse_g), o2=host(o_g2), lse2=host(lse_g2),
+                kb_o=kb_o, mx_o=mx_o, ce_o=ce_o)
+
+
+def _check_decode(cfg, x, r):
+    ora, tol = r["ora"], _tol(cfg)
+    ex = check_indices(r["idx"], ora)
+    assert np.array_equal(r["keff"], ora["k_eff"])
+    match = np.all(r["idx"] == ora["idx"], axis=-1)            # [B, Hsel, 1]
+    if cfg["gate"]:
+        d = np.abs(r["logg"].astype(np.float64) - ora["logg"])
+        assert d[match].max(initial=0.0) <= 1e-4 * max(1.0, np.abs(ora["logg"]).max())
+    # attention alone (oracle selection on both sides)
+    assert rel_err(r["o2"], r["o_o"]) <= tol, rel_err(r["o2"], r["o_o"])
+    assert np.abs(r["lse2"] - r["lse_o"]).max() <= 10 * tol
+    # end-to-end, on heads whose selection matches
+    G = cfg["Hq"] // cfg["Hkv"]
+    hmatch = np.repeat(match[:, :, 0], G if cfg["share_group"] else 1, axis=1)
+    for bi in range(cfg["B"]):
+        for h in range(cfg["Hq"]):
+            if hmatch[bi, h]:
+                e = rel_err(r["o"][bi:bi + 1, h:h + 1], r["o_o"][bi:bi + 1, h:h + 1])
+                assert e <= tol, (bi, h, e)
+    return ex
+
+
+@pytest.mark.parametrize("name,over", [
+    ("tiny_decode", {}),
+    ("tiny_decode", dict(t=1)),
+    ("tiny_decode", dict(t=17, K=5)),
+    ("tiny_decode", dict(gate=True, seed=7)),
+    ("decode_32k", {}),
+    ("decode_32k", dict(n=4096, t=33, seed=9)),
+    ("decode_32k", dict(n=8192, b=32, K=24, share_group=False, Hq=8, Hkv=8, seed=10)),
+    ("decode_32k", dict(n=2048, b=128, K=6, Hq=16, Hkv=2, seed=11)),
+    ("decode_32k", dict(n=256, K=16, seed=12)),           # K > candidates -> K_eff = 4
+    ("decode_32k", dict(n=0, t=40, seed=13)),             # first block: no candidates
+    ("decode_512k", dict(n=65536, seed=14)),
+    ("decode_32k", dict(d=64, dtype="f32", n=4096, Hq=8, Hkv=4, proj=True, seed=15)),
+])
+def test_decode_step_parity(name, over):
+    cfg = config(name, **over)
+    _say(f"[decode] {name} {over}")
+    x = make_inputs(cfg)
+    r = _decode_run(cfg, x)
+    ex = _check_decode(cfg, x, r)
+    _say(f"  exempt rows {ex}")
+
+
+def test_decode_512k_full_size():
+    cfg = config("decode_512k")
+    _say("[decode] decode_512k full size")
+    x = make_inputs(cfg)
+    r = _decode_run(cfg, x)
+    ex = _check_decode(cfg, x, r)
+    _say(f"  exempt rows {ex}")
+
+
+def test_decode_all_blocks_is_dense_attention():
+    """K = C on the tiny decode workload reproduces full causal attention
+    (torch fp64 SDPA over the whole context)."""
+    cfg = config("tiny_decode")
+    x = make_inputs(cfg)
+    C = x["L"] // cfg["b"] - 1
+    r = _decode_run(cfg, x, K=C)
+    assert np.all(r["idx"][0, 0, 0] == np.arange(C))
+    qt = torch.from_numpy(as_f64(x["q"]))
+    kt = torch.from_numpy(as_f64(x["k"]))
+    vt = torch.from_numpy(as_f64(x["v"]))
+    ref = F.scaled_dot_product_attention(qt, kt, vt).numpy()
+    assert rel_err(r["o"], ref) <= 1e-4
+
+
+def test_decode_is_deterministic():
+    cfg = config("decode_32k", n=8192)
+    x = make_inputs(cfg)
+    a = _decode_run(cfg, x)
+    b = _decode_run(cfg, x)
+    assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["logg"], b["logg"])
+    assert np.array_equal(a["o"], b["o"])
+
+
+# ------------------------------------------------------------------ prefill with cells
+def _prefill_run(cfg, x, rows=None):
+    b, qb = cfg["b"], cfg["qblock"]
+    L = x["L"]
+    nblk = L // b
+    kw = dict(Hkv=cfg["Hkv"], b=b, K=cfg["K"], q_pos0=0, gate=False, prefix_mode=1, qblock=qb,
+              share_group=False)
+    kb_o, mx_o, ce_o = oracle.block_summaries(x["k"], b, nblocks=nblk)
+    ora = oracle.score_select(x["q"], kb_o, mx_o, ce_o, erf_lambda=x["erf_lambda"],
+                              erf_sigma=x["erf_sigma"], rows=rows, **kw)
+    akw = dict(b=b, K=cfg["K"], q_pos0=0, share_group=False, local=1, window=cfg["window"],
+               prefix_mode=1, qblock=qb)
+    o_o, _ = oracle.attn_fwd(x["q"], x["k"], x["v"], ora["idx"], None, alpha=x["alpha"], rows=rows, **akw)
+    qd, kd, vd = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    kb_g, mx_g, ce_g = ops.sparse_block_summaries(kd, b)
+    idx_g, _, keff_g = ops.sparse_score_select(qd, kb_g, mx_g, ce_g, erf_lambda=dev(x["erf_lambda"]),
+                                               erf_sigma=dev(x["erf_sigma"]), **kw)
+    o_g, _ = ops.sparse_attn_fwd(qd, kd, vd, idx_g, None, alpha=dev(x["alpha"]), **akw)
+    o_g2, _ = ops.sparse_attn_fwd(qd, kd, vd, dev(ora["idx"]), None, alpha=dev(x["alpha"]), **akw)
+    torch.cuda.synchronize()
+    return ora, o_o, host(idx_g), host(keff_g), host(o_g), host(o_g2)
+
+
+def _check_prefill(cfg, x, rows=None):
+    ora, o_o, idx, keff, o, o2 = _prefill_run(cfg, x, rows)
+    sel = slice(None) if rows is None else rows
+    r_idx = idx[:, :, sel]
+    sub = {k: v[:, :, sel] for k, v in ora.items() if k in ("idx", "gap", "k_eff")}
+    ex = check_indices(r_idx, sub)
+    assert np.array_equal(keff[:, :, sel], sub["k_eff"])
+    tol = _tol(cfg)
+    assert rel_err(o2[:, :, sel], o_o[:, :, sel]) <= tol
+    match = np.all(r_idx == sub["idx"], axis=-1)
+    for h in range(cfg["Hq"]):
+        m = match[0, h]
+        e = rel_err(o[:, h:h + 1, sel][:, :, m], o_o[:, h:h + 1, sel][:, :, m])
+        assert e <= tol, (h, e)
+    return ex
+
+
+@pytest.mark.parametrize("over", [
+    dict(n=2048, Hq=4, Hkv=4),
+    dict(n=1000, Hq=2, Hkv=2, seed=21),                  # ragged tail (n not a multiple of 128)
+    dict(n=1024, Hq=2, Hkv=2, d=128, window=100, K=7, seed=22),
+    dict(n=640, Hq=2, Hkv=2, dtype="f32", seed=23),
+])
+def test_prefill_cells_parity(over):
+    cfg = config("prefill_cells", **over)
+    _say(f"[prefill] {over}")
+    x = make_inputs(cfg)
+    _say(f"  exempt rows {_check_prefill(cfg, x)}")
+
+
+def test_prefill_cells_full_size_sampled_rows():
+    cfg = config("prefill_cells")
+    _say("[prefill] full size, sampled rows")
+    x = make_inputs(cfg)
+    rng = np.random.Generator(np.random.PCG64(99))
+    n = x["L"]
+    rows = np.unique(np.concatenate([np.arange(0, 130), np.arange(n - 130, n),
+                                     rng.integers(0, n, 1500)])).astype(np.int64)
+    _say(f"  exempt rows {_check_prefill(cfg, x, rows)}")
+
+
+# ------------------------------------------------------------------ training fwd + bwd
+def _train_case(cfg, x, kv_slice=-1, fwd_rows=None):
+    b, K = cfg["b"], cfg["K"]
+    gate, sg = cfg["gate"], cfg["share_group"]
+    kw = dict(Hkv=cfg["Hkv"], b=b, K=K, q_pos0=0, gate=gate, share_group=sg)
+    nblk = x["L"] // b
+    kb_o, mx_o, ce_o = oracle.block_summaries(x["k"], b, nblocks=nblk)
+    ora = oracle.score_select(x["q"], kb_o, mx_o, ce_o, **kw)
+    logg_o = ora["logg"] if gate else None
+    akw = dict(b=b, K=K, q_pos0=0, share_group=sg)
+    o_o, lse_o = oracle.attn_fwd(x["q"], x["k"], x["v"], ora["idx"], logg_o, rows=fwd_rows, **akw)
+    dq_o, dk_o, dv_o, dg_o = oracle.attn_bwd(x["q"], x["k"], x["v"], x["dout"], ora["idx"], logg_o,
+                                             kv_slice=kv_slice, **akw)
+    qd, kd, vd, dod = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["dout"])
+    # GPU selection chain
+    kb_g, mx_g, ce_g = ops.sparse_block_summaries(kd, b)
+    idx_g, logg_g, _ = ops.sparse_score_select(qd, kb_g, mx_g, ce_g, **kw)
+    # GPU attention fwd + bwd on the oracle's selection
+    idx_in = dev(ora["idx"])
+    lg_in = dev(ora["logg"].astype(np.float32)) if gate else None
+    o_g, lse_g = ops.sparse_attn_fwd(qd, kd, vd, idx_in, lg_in, **akw)
+    dq, dk, dv, dg = ops.sparse_attn_bwd(qd, kd, vd, idx_in, lg_in, o_g, dod, lse_g, **akw)
+    torch.cuda.synchronize()
+    return dict(ora=ora, o_o=o_o, lse_o=lse_o, dq_o=dq_o, dk_o=dk_o, dv_o=dv_o, dg_o=dg_o,
+                idx=host(idx_g), logg=None if logg_g is None else host(logg_g), o=host(o_g),
+                lse=host(lse_g), dq=host(dq), dk=host(dk), dv=host(dv), dg=host(dg))
+
+
+def _check_train(cfg, r, kv_slice=-1, fwd_rows=None):
+    tol = _tol(cfg)
+    ex = check_indices(r["idx"], r["ora"])
+    if cfg["gate"]:
+        m = np.all(r["idx"] == r["ora"]["idx"], axis=-1)
+        d = np.abs(r["logg"].astype(np.float64) - r["ora"]["logg"])
+        assert d[m].max(initial=0.0) <= 1e-4 * max(1.0, np.abs(r["ora"]["logg"]).max())
+    rs = slice(None) if fwd_rows is None else fwd_rows
+    assert rel_err(r["o"][:, :, rs], r["o_o"][:, :, rs]) <= tol
+    assert np.abs(r["lse"][:, :, rs] - r["lse_o"][:, :, rs]).max() <= 10 * tol
+    B, Hkv, G = cfg["B"], cfg["Hkv"], cfg["Hq"] // cfg["Hkv"]
+    Hsel = Hkv if cfg["share_group"] else cfg["Hq"]
+    if kv_slice < 0:
+        pairs = [(bi, kh) for bi in range(B) for kh in range(Hkv)]
+    else:
+        pairs = [divmod(kv_slice, Hkv)]
+    for bi, kh in pairs:
+        hq = slice(kh * G, kh * G + G)
+        hs = slice(kh, kh + 1) if cfg["share_group"] else hq
+        e_dq = rel_err(r["dq"][bi:bi + 1, hq], r["dq_o"][bi:bi + 1, hq])
+        e_dk = rel_err(r["dk"][bi:bi + 1, kh:kh + 1], r["dk_o"][bi:bi + 1, kh:kh + 1])
+        e_dv = rel_err(r["dv"][bi:bi + 1, kh:kh + 1], r["dv_o"][bi:bi + 1, kh:kh + 1])
+        e_dg = rel_err(r["dg"][bi:bi + 1, hs], r["dg_o"][bi:bi + 1, hs])
+        _say(f"  b={bi} kvh={kh}: dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e} dg {e_dg:.2e}")
+        assert max(e_dq, e_dk, e_dv, e_dg) <= tol, (bi, kh, e_dq, e_dk, e_dv, e_dg)
+    assert Hsel == r["dg"].shape[1]
+    return ex
+
+
+@pytest.mark.parametrize("over", [
+    dict(B=2, n=1024, Hq=8, Hkv=2),
+    dict(B=1, n=1000, Hq=4, Hkv=4, K=5, share_group=False, seed=31),     # ragged tail, per-head gate
+    dict(B=1, n=512, Hq=8, Hkv=1, b=32, K=6, seed=32),                    # G = 8, b = 32
+    dict(B=1, n=384, Hq=2, Hkv=1, d=64, dtype="f32", K=3, seed=33),      # fp32 -> 1e-4
+    dict(B=1, n=256, Hq=2, Hkv=2, b=16, d=64, K=4, gate=False, seed=34),  # gate off, b = 16
+])
+def test_train_fwd_bwd_parity(over):
+    cfg = config("train", **over)
+    _say(f"[train] {over}")
+    x = make_inputs(cfg)
+    r = _train_case(cfg, x)
+    _say(f"  exempt rows {_check_train(cfg, r)}")
+
+
+def test_train_full_size_one_slice():
+    """Full training workload; the oracle computes the backward of one
+    (batch, kv head) slice and the forward of sampled rows."""
+    cfg = config("train")
+    _say("[train] full size, slice b=1 kvh=5")
+    x = make_inputs(cfg)
+    rng = np.random.Generator(np.random.PCG64(77))
+    rows = np.unique(np.concatenate([np.arange(0, 70), rng.integers(0, x["L"], 400),
+                                     np.arange(x["L"] - 70, x["L"])])).astype(np.int64)
+    kv_slice = 1 * cfg["Hkv"] + 5
+    r = _train_case(cfg, x, kv_slice=kv_slice, fwd_rows=rows)
+    _say(f"  exempt rows {_check_train(cfg, r, kv_slice=kv_slice, fwd_rows=rows)}")
+
+
+def test_chunked_prefill_rows_after_offset():
+    """Rows at positions q_pos0..L-1 of a longer cache (nq < L): selection and
+    attention use absolute positions."""
+    cfg = config("train", B=1, n=1024, Hq=4, Hkv=2, K=4, seed=41)
+    x = make_inputs(cfg)
+    q_pos0 = 600
+    q = np.ascontiguousarray(x["q"][:, :, q_pos0:])
+    b, K = cfg["b"], cfg["K"]
+    kw = dict(Hkv=2, b=b, K=K, q_pos0=q_pos0, gate=True, share_group=True)
+    kb_o, mx_o, ce_o = oracle.block_summaries(x["k"], b)
+    ora = oracle.score_select(q, kb_o, mx_o, ce_o, **kw)
+    o_o, lse_o = oracle.attn_fwd(q, x["k"], x["v"], ora["idx"], ora["logg"], b=b, K=K, q_pos0=q_pos0)
+    kd = dev(x["k"])
+    kb_g, mx_g, ce_g = ops.sparse_block_summaries(kd, b)
+    idx_g, logg_g, _ = ops.sparse_score_select(dev(q), kb_g, mx_g, ce_g, **kw)
+    o_g, lse_g = ops.sparse_attn_fwd(dev(q), kd, dev(x["v"]), dev(ora["idx"]),
+                                     dev(ora["logg"].astype(np.float32)), b=b, K=K, q_pos0=q_pos0)
+    check_indices(host(idx_g), ora)
+    assert rel_err(host(o_g), o_o) <= 2e-2
