@@ -1,0 +1,449 @@
+"""Benchmark: decode attention step at 512K context on one MI355X, plus prefill
+tokens/s (cell routing, n = 16384) and training fwd+bwd tokens/s.
+
+One decode step = the hot path for one query token of one layer:
+  score + softmax log gate + top-K select over all C = 8192 block summaries
+  (sparse_score_select), then exact attention over the current block + the
+  K = 32 selected blocks for all 32 query heads (sparse_attn_fwd), plus, on
+  every b-th step, the summary of the block that closes (sparse_block_summaries).
+Steps rotate over 16 layers' KV caches (2.15 GB each) and 64 query vectors so
+that every step reads its summaries and selected K/V cold from HBM, as a
+multi-layer decoder would.  Inputs are resident in HBM before timing starts.
+The steps are captured once in a HIP graph and replayed (the pages measured
+decode with graph replay); that replay is the timed region.  Per-kernel
+durations for the roofline come from the same steps run once more eagerly,
+each kernel launched with start/stop events attached to its dispatch
+(spa_profile_next_call), i.e. the kernel's own begin/end timestamps.
+
+Prints one JSON line.  Only N = 1 GPU is supported.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from block_sparse_attention_summaries_amd import ops  # noqa: E402
+from block_sparse_attention_summaries_amd.inputs import config, decode_queries, make_inputs  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0         # dense bf16 MFMA, vendor figure
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_512k_hbm_counters.json")
+CSRC = os.path.join(ROOT, "block_sparse_attention_summaries_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        self.made.append(ev)
+        return ev
+
+    def elapsed(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy_all(self):
+        for ev in self.made:
+            self.hip.hipEventDestroy(ev)
+        self.made = []
+
+
+# ---------------------------------------------------------------- decode workload
+class DecodeWorkload:
+    """Layers of a 512K-token KV cache with their block summaries, rotating
+    queries, and preallocated outputs/workspaces for graph capture."""
+
+    def __init__(self, cfg, n_layers, n_queries, host_layer0):
+        self.cfg = cfg
+        B, Hq, Hkv, d, b = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["b"]
+        x = host_layer0
+        self.L, self.pos = x["L"], x["q_pos0"]
+        self.ccap = self.L // b
+        self.C = self.pos // b                      # historical candidates of the query
+        self.K, self.b = cfg["K"], b
+        g = torch.Generator(device="cuda")
+        self.k, self.v, self.w = [dev(x["k"])], [dev(x["v"])], [dev(x["proj_w"])]
+        for layer in range(1, n_layers):
+            g.manual_seed(cfg["seed"] * 1000 + layer)
+            self.k.append(torch.randn((B, Hkv, self.L, d), generator=g, device="cuda").to(torch.bfloat16))
+            self.v.append(torch.randn((B, Hkv, self.L, d), generator=g, device="cuda").to(torch.bfloat16))
+            self.w.append(torch.randn((d, d), generator=g, device="cuda") / float(np.sqrt(d)))
+        self.q = dev(decode_queries(cfg, n_queries))  # [nQ, B, Hq, 1, d]
+        self.kbar, self.mx, self.ce = [], [], []
+        for layer in range(n_layers):
+            kb, mx, ce = ops.sparse_block_summaries(self.k[layer], b, num_blocks=self.ccap - 1,
+                                                    ccap=self.ccap)
+            self.kbar.append(kb)
+            self.mx.append(mx)
+            self.ce.append(ce)
+        self.idx = torch.empty((B, Hkv, 1, self.K), dtype=torch.int32, device="cuda")
+        self.logg = torch.empty((B, Hkv, 1, self.K), dtype=torch.float32, device="cuda")
+        self.keff = torch.empty((B, Hkv, 1), dtype=torch.int32, device="cuda")
+        self.o = torch.empty((B, Hq, 1, d), dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty((B, Hq, 1), dtype=torch.float32, device="cuda")
+        self.ws_sel = ops.Workspace()
+        self.ws_att = ops.Workspace()
+        torch.cuda.synchronize()
+
+    def close_block(self, layer):
+        """Summary of the block that just closed (the current block, now full)."""
+        ops.sparse_block_summaries(self.k[layer], self.b, first_block=self.ccap - 1, num_blocks=1,
+                                   kbar=self.kbar[layer], max_norm=self.mx[layer], centre=self.ce[layer])
+
+    def select(self, layer, qi):
+        ops.sparse_score_select(self.q[qi], self.kbar[layer], self.mx[layer], self.ce[layer],
+                                Hkv=self.cfg["Hkv"], b=self.b, K=self.K, q_pos0=self.pos, gate=True,
+                                proj_w=self.w[layer], idx=self.idx, logg=self.logg, k_eff=self.keff,
+                                workspace=self.ws_sel)
+
+    def attend(self, layer, qi):
+        ops.sparse_attn_fwd(self.q[qi], self.k[layer], self.v[layer], self.idx, self.logg, b=self.b,
+                            K=self.K, q_pos0=self.pos, o=self.o, lse=self.lse, workspace=self.ws_att)
+
+    def selected_kv_bytes(self):
+        c = self.cfg
+        t = self.pos - (self.pos // self.b) * self.b + 1    # tokens of the current block
+        keff = min(self.K, self.C)
+        kv = c["B"] * c["Hkv"] * (keff * self.b + t) * c["d"] * 2 * 2   # K and V, bf16
+        qo = c["B"] * c["Hq"] * c["d"] * 2 * 2 + c["B"] * c["Hkv"] * self.K * 8
+        return kv + qo
+
+    def scoring_bytes(self):
+        c = self.cfg
+        return c["B"] * c["Hkv"] * self.C * (c["d"] * 2) + c["d"] * c["d"] * 4 + c["B"] * c["Hq"] * c["d"] * 2
+
+
+def run_decode(args):
+    cfg = config("decode_512k")
+    t0 = time.time()
+    x = make_inputs(cfg)
+    log(f"[bench] host inputs for {cfg['name']} in {time.time() - t0:.1f}s")
+    wl = DecodeWorkload(cfg, args.layers, args.queries, x)
+    log(f"[bench] {args.layers} layers of L={wl.L} resident; C={wl.C} candidates, K={wl.K}")
+
+    # summaries of a whole 512K cache (prefill-time work), timed eagerly
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for layer in range(args.layers):
+        ops.sparse_block_summaries(wl.k[layer], wl.b, num_blocks=wl.ccap, ccap=wl.ccap,
+                                   kbar=wl.kbar[layer], max_norm=wl.mx[layer], centre=wl.ce[layer])
+    e1.record()
+    torch.cuda.synchronize()
+    summ_ms = e0.elapsed_time(e1) / args.layers
+    summ_bytes = cfg["B"] * cfg["Hkv"] * (wl.ccap * wl.b * cfg["d"] * 2 + wl.ccap * (cfg["d"] * 2 + 4))
+
+    # warm-up (eager), also builds the workspaces
+    for s in range(args.warmup):
+        wl.select(s % args.layers, s % args.queries)
+        wl.attend(s % args.layers, s % args.queries)
+    torch.cuda.synchronize()
+
+    # capture one graph of `steps` decode steps
+    steps = args.steps
+
+    def step(s):
+        layer, qi = s % args.layers, s % args.queries
+        if s % wl.b == wl.b - 1:
+            wl.close_block(layer)
+        wl.select(layer, qi)
+        wl.attend(layer, qi)
+
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        graph.capture_begin()
+        for s in range(steps):
+            step(s)
+        graph.capture_end()
+    torch.cuda.current_stream().wait_stream(stream)
+    graph.replay()                                  # untimed replay (graph upload)
+    torch.cuda.synchronize()
+
+    # timed region: one replay of the whole sequence of steps
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    g0.record()
+    graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    total_ms = g0.elapsed_time(g1)
+
+    # per-kernel durations over the same steps (eager), from each kernel's own
+    # dispatch timestamps (start/stop events attached to its launch)
+    hip = HipEvents()
+    EvArr = ctypes.c_void_p * 4
+    evs = [(EvArr(*[hip.create() for _ in range(4)]), EvArr(*[hip.create() for _ in range(4)]))
+           for _ in range(steps)]
+    lib = ops.lib()
+    for s in range(steps):
+        layer, qi = s % args.layers, s % args.queries
+        if s % wl.b == wl.b - 1:
+            wl.close_block(layer)
+        lib.spa_profile_next_call(evs[s][0], 2)
+        wl.select(layer, qi)
+        lib.spa_profile_next_call(evs[s][1], 2)
+        wl.attend(layer, qi)
+    torch.cuda.synchronize()
+    k_ms = {name: np.array([hip.elapsed(evs[s][c][2 * i], evs[s][c][2 * i + 1]) for s in range(steps)])
+            for name, c, i in (("chunk", 0, 0), ("merge", 0, 1), ("partial", 1, 0), ("combine", 1, 1))}
+    sel_ms = np.array([hip.elapsed(evs[s][0][0], evs[s][0][3]) for s in range(steps)])
+    att_ms = np.array([hip.elapsed(evs[s][1][0], evs[s][1][3]) for s in range(steps)])
+    hip.destroy_all()
+
+    # a hot-cache variant (one layer, one query) for context
+    hot = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        hot.capture_begin()
+        for s in range(64):
+            wl.select(0, 0)
+            wl.attend(0, 0)
+        hot.capture_end()
+    torch.cuda.current_stream().wait_stream(stream)
+    hot.replay()
+    torch.cuda.synchronize()
+    g0.record()
+    hot.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    hot_us = g0.elapsed_time(g1) * 1e3 / 64
+
+    return dict(wl=wl, cfg=cfg, x=x, total_ms=total_ms, sel_ms=sel_ms, att_ms=att_ms, k_ms=k_ms,
+                summ_ms=summ_ms, summ_bytes=summ_bytes, hot_us=hot_us)
+
+
+# ---------------------------------------------------------------- prefill / training
+def run_prefill(reps):
+    cfg = config("prefill_cells")
+    x = make_inputs(cfg)
+    b, qb, K = cfg["b"], cfg["qblock"], cfg["K"]
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    lam, sig, alpha = dev(x["erf_lambda"]), dev(x["erf_sigma"]), dev(x["alpha"])
+    ws1, ws2 = ops.Workspace(), ops.Workspace()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    times = []
+
+    def once():
+        ev[0].record()
+        kb, mx, ce = ops.sparse_block_summaries(k, b)
+        ev[1].record()
+        idx, _, _ = ops.sparse_score_select(q, kb, mx, ce, Hkv=cfg["Hkv"], b=b, K=K, q_pos0=0, gate=False,
+                                            prefix_mode=1, qblock=qb, share_group=False,
+                                            erf_lambda=lam, erf_sigma=sig, workspace=ws1)
+        ev[2].record()
+        ops.sparse_attn_fwd(q, k, v, idx, None, b=b, K=K, q_pos0=0, share_group=False, local=1,
+                            window=cfg["window"], alpha=alpha, prefix_mode=1, qblock=qb, workspace=ws2)
+        ev[3].record()
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(3)]
+
+    once()
+    for _ in range(reps):
+        times.append(once())
+    t = np.median(np.array(times), axis=0)
+    n = x["L"]
+    # algorithmic work: 2d flops per causal (query, cell) score; 4d per (q, k) pair
+    scores = sum((qb * (i // qb)) // b for i in range(n)) * cfg["Hq"]      # causal (query, cell) pairs
+    return dict(ms=dict(summaries=t[0], score_select=t[1], attention=t[2]),
+                tokens_per_s=n / (t.sum() * 1e-3), score_gflop=2 * cfg["d"] * scores / 1e9)
+
+
+def run_train(reps):
+    cfg = config("train")
+    x = make_inputs(cfg)
+    b, K = cfg["b"], cfg["K"]
+    q, k, v, do = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["dout"])
+    ws = [ops.Workspace() for _ in range(3)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    times = []
+
+    def once():
+        ev[0].record()
+        kb, mx, ce = ops.sparse_block_summaries(k, b)
+        idx, logg, _ = ops.sparse_score_select(q, kb, mx, ce, Hkv=cfg["Hkv"], b=b, K=K, q_pos0=0,
+                                               gate=True, workspace=ws[0])
+        ev[1].record()
+        o, lse = ops.sparse_attn_fwd(q, k, v, idx, logg, b=b, K=K, q_pos0=0, workspace=ws[1])
+        ev[2].record()
+        ops.sparse_attn_bwd(q, k, v, idx, logg, o, do, lse, b=b, K=K, q_pos0=0, workspace=ws[2])
+        ev[3].record()
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(3)]
+
+    once()
+    for _ in range(reps):
+        times.append(once())
+    t = np.median(np.array(times), axis=0)
+    tokens = cfg["B"] * x["L"]
+    return dict(ms=dict(select=t[0], fwd=t[1], bwd=t[2]), tokens_per_s=tokens / (t.sum() * 1e-3))
+
+
+# ---------------------------------------------------------------- CPU oracle baseline
+def run_cpu_baseline(res, seconds):
+    """The fp64 oracle's decode step (score + gate + top-K + attention) on the
+    host for layer 0 of the same workload, rotating the same queries."""
+    import oracle
+    cfg, x, wl = res["cfg"], res["x"], res["wl"]
+    b, K, pos = cfg["b"], cfg["K"], x["q_pos0"]
+    t0 = time.time()
+    kb, mx, ce = oracle.block_summaries(x["k"], b, nblocks=wl.ccap)
+    log(f"[bench] oracle summaries of layer 0 in {time.time() - t0:.1f}s")
+    qs = decode_queries(cfg, 64)
+    n = 0
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        qn = np.ascontiguousarray(qs[n % 64])
+        sel = oracle.score_select(qn, kb, mx, ce, Hkv=cfg["Hkv"], b=b, K=K, q_pos0=pos, gate=True,
+                                  proj_w=x["proj_w"])
+        oracle.attn_fwd(qn, x["k"], x["v"], sel["idx"], sel["logg"], b=b, K=K, q_pos0=pos)
+        n += 1
+    dt = time.time() - t0
+    return dict(value=dt / n * 1e6, unit="us/step", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{n} decode steps of layer 0 (512K context, 8 kv heads, C=8192, K=32), "
+                       f"rotating 64 queries; block summaries precomputed")
+
+
+def hbm_traffic(kernel, algorithmic):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, if it was taken on the current kernel sources."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    try:
+        c = json.load(open(COUNTERS_FILE))
+    except (OSError, ValueError):
+        return None
+    if c.get("source_sha") != source_hash() or kernel not in c.get("kernels", {}):
+        return None
+    k = c["kernels"][kernel]
+    scale = c.get("copy_scale", 1.0)
+    return (k["fetch_kib"] + k["write_kib"]) * 1024 * scale
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--layers", type=int, default=16)
+    ap.add_argument("--queries", type=int, default=64)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        sys.exit("bench.py measures one GPU only: the method has no cross-GPU exchange on this path "
+                 "(see the sharding note in the design document); run with --gpus 1")
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    ops.lib()
+
+    res = run_decode(args)
+    wl, steps = res["wl"], args.steps
+    us_per_step = res["total_ms"] * 1e3 / steps
+    att_bytes, sel_bytes = wl.selected_kv_bytes(), wl.scoring_bytes()
+    heads = wl.cfg["B"] * wl.cfg["Hkv"]
+    nch = (wl.C + 255) // 256
+    kbytes = {
+        "chunk": sel_bytes,
+        "merge": heads * nch * (wl.K * 8 + 8) + heads * wl.K * 8,
+        "partial": att_bytes,
+        "combine": heads * (wl.K + 1) * 4 * (wl.cfg["d"] + 2) * 4 + wl.cfg["Hq"] * wl.cfg["d"] * 2,
+    }
+    names = {"chunk": "decode_chunk_kernel", "merge": "decode_merge_kernel",
+             "partial": "decode_attn_partial_kernel", "combine": "decode_combine_kernel"}
+    kern = {}
+    for k, v in res["k_ms"].items():
+        us = float(v.mean() * 1e3)
+        kern[k] = dict(kernel=names[k], us=us, p99_us=float(np.percentile(v, 99) * 1e3),
+                       bytes=kbytes[k], gbps=kbytes[k] / (us * 1e-6) / 1e9)
+    sel_us, att_us = float(res["sel_ms"].mean() * 1e3), float(res["att_ms"].mean() * 1e3)
+    dom = max(kern, key=lambda n: kern[n]["us"])
+    achieved = kern[dom]["gbps"]
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBPS, 4),
+                    traffic=hbm_traffic(names[dom], kern[dom]["bytes"]), kernel=names[dom],
+                    algorithmic_bytes=kern[dom]["bytes"], launch_us=round(kern[dom]["us"], 3))
+    out = {
+        "metric": "decode attn µs/step + selected-KV HBM GB/s at 512K ctx; prefill tokens/s",
+        "value": round(us_per_step, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["total_ms"] / steps, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 K/V/q, N(0,1/128) fp32 selector projection)",
+        "config": {"workload": "decode_512k", "batch": 1, "context": wl.L - 1, "q_heads": 32,
+                   "kv_heads": 8, "head_dim": 128, "block": wl.b, "K": wl.K, "gate": "softmax_log",
+                   "layers_rotated": args.layers, "queries_rotated": args.queries, "graph_replay": True},
+        "selected_kv_gbps": round(att_bytes / (kern["partial"]["us"] * 1e-6) / 1e9, 1),
+        "stage_us": {"score_select": round(sel_us, 3), "attention": round(att_us, 3)},
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kern.items()},
+        "hot_cache_us_per_step": round(res["hot_us"], 3),
+        "summaries_512k_ms": round(res["summ_ms"], 3),
+        "summaries_gbps": round(res["summ_bytes"] / (res["summ_ms"] * 1e-3) / 1e9, 1),
+        "roofline": roofline,
+    }
+    if not args.no_prefill:
+        pf = run_prefill(3)
+        out["prefill_tokens_per_s"] = round(pf["tokens_per_s"], 1)
+        out["prefill_ms"] = {k: round(v, 3) for k, v in pf["ms"].items()}
+        out["prefill_score_mfma_frac"] = round(pf["score_gflop"] / (pf["ms"]["score_select"] * 1e-3)
+                                               / (BF16_PEAK_TFLOPS * 1e3), 5)
+        tr = run_train(2)
+        out["train_tokens_per_s"] = round(tr["tokens_per_s"], 1)
+        out["train_ms"] = {k: round(v, 3) for k, v in tr["ms"].items()}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = run_cpu_baseline(res, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -14,6 +14,7 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local spa::ProfileEvents g_profile = {nullptr, 0, 0};
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -29,6 +30,11 @@ int ok() {
   g_last_error.clear();
   return SPA_OK;
 }
+
+// A profiling request applies to one call only, launched or not.
+struct ProfileScope {
+  ~ProfileScope() { g_profile = spa::ProfileEvents{nullptr, 0, 0}; }
+};
 
 bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -159,11 +165,19 @@ extern "C" {
 
 int spa_abi_version(void) { return SPA_ABI_VERSION; }
 
+int spa_profile_next_call(void** events, int count) {
+  SPA_REQUIRE(count >= 0 && (count == 0 || events != nullptr), SPA_ERR_INVALID_ARG,
+              "events must hold 2 * count handles");
+  g_profile = spa::ProfileEvents{reinterpret_cast<hipEvent_t*>(events), count, 0};
+  return ok();
+}
+
 const char* spa_last_error(void) { return g_last_error.c_str(); }
 
 int sparse_block_summaries(const void* k, int dtype, int B, int Hkv, int64_t L, int d, int b,
                            int64_t first_block, int64_t num_blocks, int64_t ccap, void* kbar,
                            float* max_norm, float* centre, spa_stream_t stream) {
+  ProfileScope profile_scope;
   int st = check_heads(B, Hkv, Hkv, d, dtype);
   if (st != SPA_OK) return st;
   SPA_REQUIRE(k && kbar && max_norm, SPA_ERR_INVALID_ARG, "k, kbar and max_norm must be non-NULL");
@@ -184,6 +198,7 @@ int sparse_block_summaries(const void* k, int dtype, int B, int Hkv, int64_t L, 
 }
 
 int sparse_score_select(const spa_select_args* a, void* workspace, size_t ws_bytes, spa_stream_t stream) {
+  ProfileScope profile_scope;
   spa::SelectLaunch p;
   int st = check_select(a, &p);
   if (st != SPA_OK) return st;
@@ -194,6 +209,7 @@ int sparse_score_select(const spa_select_args* a, void* workspace, size_t ws_byt
 }
 
 int sparse_attn_fwd(const spa_attn_args* a, void* workspace, size_t ws_bytes, spa_stream_t stream) {
+  ProfileScope profile_scope;
   spa::AttnLaunch p;
   int st = check_attn(a, &p);
   if (st != SPA_OK) return st;
@@ -204,6 +220,7 @@ int sparse_attn_fwd(const spa_attn_args* a, void* workspace, size_t ws_bytes, sp
 
 int sparse_attn_bwd(const spa_attn_args* a, const void* o, const void* dout, const float* lse, void* dq,
                     void* dk, void* dv, float* dg, void* workspace, size_t ws_bytes, spa_stream_t stream) {
+  ProfileScope profile_scope;
   spa::BwdLaunch p;
   int st = check_bwd(a, o, dout, lse, dq, dk, dv, dg, &p);
   if (st != SPA_OK) return st;
@@ -237,6 +254,7 @@ size_t sparse_workspace_bytes(int op, const void* args) {
 }
 
 int sparse_workspace_init(void* workspace, size_t ws_bytes, spa_stream_t stream) {
+  ProfileScope profile_scope;
   if (ws_bytes == 0) return ok();
   SPA_REQUIRE(workspace != nullptr, SPA_ERR_INVALID_ARG, "workspace is NULL");
   SPA_REQUIRE(aligned16(workspace) && ws_bytes % 16 == 0, SPA_ERR_INVALID_ARG,
@@ -249,6 +267,8 @@ int sparse_workspace_init(void* workspace, size_t ws_bytes, spa_stream_t stream)
 
 namespace spa {
 
+ProfileEvents& profile_events() { return g_profile; }
+
 __global__ void zero_fill_kernel(uint4* p, size_t n) {
   for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
        i += static_cast<size_t>(gridDim.x) * blockDim.x)
@@ -260,9 +280,8 @@ hipError_t launch_zero_fill(void* ptr, size_t bytes, hipStream_t st) {
   size_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks == 0) blocks = 1;
-  hipLaunchKernelGGL(zero_fill_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
-                     static_cast<uint4*>(ptr), n);
-  return hipGetLastError();
+  return launch(true, zero_fill_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), st,
+                static_cast<uint4*>(ptr), n);
 }
 
 }  // namespace spa

@@ -15,7 +15,8 @@
 // Decode (one query row): split-K over the K+1 kept blocks.  One workgroup per
 // (selection head, kept block, 64-token tile) stages the K and V tile in LDS
 // once for all G query heads of the group (GQA-shared gather), writes an
-// online-softmax partial (m, l, acc); a combine kernel merges the partials.
+// online-softmax partial (m, l, acc); a combine kernel (one workgroup per
+// query head) merges the partials.
 // Rows (prefill / training): one wave per (query head, row) streaming its key
 // segments 64 keys at a time with an online softmax.
 #include "spa_device.h"
@@ -33,12 +34,14 @@ __device__ __forceinline__ void wave_lds_sync() {
 // ======================================================== decode: split-K
 constexpr int kTileTok = 64;
 
+// Online-softmax partial of one K/V tile for the HPW query heads of a group:
+// loads the tile into LDS once, then scores, (m, l) and acc per head.
 template <typename T, int D, int HPW>
-__global__ __launch_bounds__(256) void decode_attn_partial_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const int32_t* __restrict__ idx, const float* __restrict__ logg, int Hq, int Hkv, int Hsel,
-    int share_group, int64_t L, int64_t pos, int b, int K, int tpu, float* __restrict__ ws_acc,
-    float2* __restrict__ ws_ml) {
+__device__ __forceinline__ void tile_partial(const T* __restrict__ q, const T* __restrict__ k,
+                                             const T* __restrict__ v, int bi, int hs, int kvh, int G,
+                                             int Hq, int Hkv, int share_group, int64_t L, int64_t start,
+                                             int ntok, float bias, float* __restrict__ ws_acc,
+                                             float2* __restrict__ ws_ml, int64_t obase) {
   constexpr int kVec = Elem<T>::kVec;
   constexpr int kVPR = D / kVec;                     // 16-byte vectors per row
   constexpr int kPadRow = D + kVec;                  // padded LDS row (elements)
@@ -47,40 +50,7 @@ __global__ __launch_bounds__(256) void decode_attn_partial_kernel(
   __shared__ __align__(16) T s_v[kTileTok * D];
   __shared__ float s_q[HPW][D];
   __shared__ float s_p[HPW][kTileTok];
-
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int bh = blockIdx.y;
-  const int bi = bh / Hsel, hs = bh % Hsel;
-  const int G = Hq / Hkv;
-  const int kvh = share_group ? hs : hs / G;
-  const int unit = blockIdx.x / tpu, sub = blockIdx.x % tpu;
-  const int ntiles = (K + 1) * tpu;
-  const int tile = blockIdx.x;
-
-  int64_t start = 0;
-  int ntok = 0;
-  float bias = 0.f;
-  const int64_t c0 = pos / b;
-  if (unit < K) {
-    const int32_t c = idx[static_cast<int64_t>(bh) * K + unit];
-    if (c >= 0 && c < c0) {
-      start = static_cast<int64_t>(c) * b + sub * kTileTok;
-      ntok = b - sub * kTileTok < kTileTok ? b - sub * kTileTok : kTileTok;
-      if (logg != nullptr) bias = logg[static_cast<int64_t>(bh) * K + unit];
-    }
-  } else {
-    start = c0 * b + sub * kTileTok;
-    const int64_t n = pos + 1 - start;
-    const int cap = b - sub * kTileTok < kTileTok ? b - sub * kTileTok : kTileTok;
-    ntok = n <= 0 ? 0 : (n < cap ? static_cast<int>(n) : cap);
-  }
-
-  const int64_t obase = (static_cast<int64_t>(bh) * ntiles + tile) * HPW;
-  if (ntok == 0) {
-    for (int x = tid; x < HPW * D; x += 256) ws_acc[obase * D + x] = 0.f;
-    if (tid < HPW) ws_ml[obase + tid] = make_float2(-INFINITY, 0.f);
-    return;
-  }
 
   // issue every K / V load of the tile before touching LDS
   const int64_t kvrow0 = (static_cast<int64_t>(bi) * Hkv + kvh) * L + start;
@@ -150,34 +120,93 @@ __global__ __launch_bounds__(256) void decode_attn_partial_kernel(
   }
 }
 
+// Split-K combine: one workgroup per (selection head, query head of its
+// group).  All ntiles partial accumulators of that query head are staged in
+// LDS with one round of independent loads, then each output element sums
+// them with the softmax weights exp(m_t - M).
+constexpr int kMaxTiles = 130;   // (K + 1) * tiles per unit for K <= 64, b <= 128
+
 template <typename T, int D, int HPW>
-__global__ __launch_bounds__(256) void decode_combine_kernel(
-    const float* __restrict__ ws_acc, const float2* __restrict__ ws_ml, int Hq, int Hkv, int Hsel,
-    int share_group, int ntiles, T* __restrict__ o, float* __restrict__ lse) {
+__global__ __launch_bounds__(256) void decode_attn_partial_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ idx, const float* __restrict__ logg, int Hq, int Hkv, int Hsel,
+    int share_group, int64_t L, int64_t pos, int b, int K, int tpu, float* __restrict__ ws_acc,
+    float2* __restrict__ ws_ml) {
   const int tid = threadIdx.x;
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.y;
   const int bi = bh / Hsel, hs = bh % Hsel;
   const int G = Hq / Hkv;
-  for (int x = tid; x < HPW * D; x += 256) {
-    const int hh = x / D, e = x % D;
-    float M = -INFINITY;
-    for (int t = 0; t < ntiles; ++t)
-      M = fmaxf(M, ws_ml[(static_cast<int64_t>(bh) * ntiles + t) * HPW + hh].x);
-    float lsum = 0.f, acc = 0.f;
-    if (M != -INFINITY) {
-      for (int t = 0; t < ntiles; ++t) {
-        const int64_t pi = (static_cast<int64_t>(bh) * ntiles + t) * HPW + hh;
-        const float2 ml = ws_ml[pi];
-        const float w = ml.x == -INFINITY ? 0.f : __expf(ml.x - M);
-        lsum = fmaf(ml.y, w, lsum);
-        acc = fmaf(ws_acc[pi * D + e], w, acc);
-      }
+  const int kvh = share_group ? hs : hs / G;
+  const int unit = blockIdx.x / tpu, sub = blockIdx.x % tpu;
+  const int ntiles = (K + 1) * tpu;
+  const int tile = blockIdx.x;
+
+  int64_t start = 0;
+  int ntok = 0;
+  float bias = 0.f;
+  const int64_t c0 = pos / b;
+  if (unit < K) {
+    const int32_t c = idx[static_cast<int64_t>(bh) * K + unit];
+    if (c >= 0 && c < c0) {
+      start = static_cast<int64_t>(c) * b + sub * kTileTok;
+      ntok = b - sub * kTileTok < kTileTok ? b - sub * kTileTok : kTileTok;
+      if (logg != nullptr) bias = logg[static_cast<int64_t>(bh) * K + unit];
     }
-    const int hq = share_group ? hs * G + hh : hs;
-    const int64_t orow = static_cast<int64_t>(bi) * Hq + hq;   // nq == 1
-    o[orow * D + e] = Elem<T>::from_float(lsum > 0.f ? acc / lsum : 0.f);
-    if (e == 0 && lse != nullptr) lse[orow] = lsum > 0.f ? M + __logf(lsum) : -INFINITY;
+  } else {
+    start = c0 * b + sub * kTileTok;
+    const int64_t n = pos + 1 - start;
+    const int cap = b - sub * kTileTok < kTileTok ? b - sub * kTileTok : kTileTok;
+    ntok = n <= 0 ? 0 : (n < cap ? static_cast<int>(n) : cap);
   }
+
+  const int64_t obase = (static_cast<int64_t>(bh) * ntiles + tile) * HPW;
+  if (ntok == 0) {
+    for (int x = tid; x < HPW * D; x += 256) ws_acc[obase * D + x] = 0.f;
+    if (tid < HPW) ws_ml[obase + tid] = make_float2(-INFINITY, 0.f);
+  } else {
+    tile_partial<T, D, HPW>(q, k, v, bi, hs, kvh, G, Hq, Hkv, share_group, L, start, ntok, bias,
+                            ws_acc, ws_ml, obase);
+  }
+}
+
+template <typename T, int D, int HPW>
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ ws_acc,
+                                                             const float2* __restrict__ ws_ml, int Hq,
+                                                             int Hkv, int Hsel, int share_group,
+                                                             int ntiles, T* __restrict__ o,
+                                                             float* __restrict__ lse) {
+  __shared__ __align__(16) float s_acc[kMaxTiles * D];
+  __shared__ float2 s_ml[kMaxTiles];
+  const int tid = threadIdx.x;
+  const int hh = blockIdx.x, bh = blockIdx.y;
+  const int bi = bh / Hsel, hs = bh % Hsel;
+  const int G = Hq / Hkv;
+  const int64_t base = static_cast<int64_t>(bh) * ntiles * HPW;   // partial (tile t, head hh) at base + t*HPW + hh
+  constexpr int kV4 = D / 4;
+  const int n4 = ntiles * kV4;
+#pragma unroll 8
+  for (int x = tid; x < n4; x += 256) {
+    const int t = x / kV4, c = x % kV4;
+    reinterpret_cast<float4*>(s_acc)[x] = reinterpret_cast<const float4*>(ws_acc + (base + t * HPW + hh) * D)[c];
+  }
+  for (int t = tid; t < ntiles; t += 256) s_ml[t] = ws_ml[base + t * HPW + hh];
+  __syncthreads();
+  if (tid >= D) return;
+  float M = -INFINITY;
+  for (int t = 0; t < ntiles; ++t) M = fmaxf(M, s_ml[t].x);
+  float lsum = 0.f, acc = 0.f;
+  if (M != -INFINITY) {
+    for (int t = 0; t < ntiles; ++t) {
+      const float2 ml = s_ml[t];
+      const float w = ml.x == -INFINITY ? 0.f : __expf(ml.x - M);
+      lsum = fmaf(ml.y, w, lsum);
+      acc = fmaf(s_acc[t * D + tid], w, acc);
+    }
+  }
+  const int hq = share_group ? hs * G + hh : hs;
+  const int64_t orow = static_cast<int64_t>(bi) * Hq + hq;   // one query row
+  o[orow * D + tid] = Elem<T>::from_float(lsum > 0.f ? acc / lsum : 0.f);
+  if (tid == 0 && lse != nullptr) lse[orow] = lsum > 0.f ? M + __logf(lsum) : -INFINITY;
 }
 
 // ======================================================== rows: forward
@@ -549,19 +578,16 @@ static hipError_t launch_decode_attn_h(const AttnLaunch& p, void* ws, hipStream_
   const int tpu = decode_tpu(p);
   const int ntiles = (p.K + 1) * tpu;
   const size_t heads = static_cast<size_t>(p.B) * p.Hsel;
-  float* acc = static_cast<float*>(ws);
-  float2* ml = reinterpret_cast<float2*>(static_cast<char*>(ws) +
-                                         align256(heads * ntiles * HPW * p.d * sizeof(float)));
-  hipLaunchKernelGGL((decode_attn_partial_kernel<T, D, HPW>), dim3(ntiles, static_cast<unsigned>(heads)),
-                     dim3(256), 0, st, static_cast<const T*>(p.q), static_cast<const T*>(p.k),
-                     static_cast<const T*>(p.v), p.idx, p.logg, p.Hq, p.Hkv, p.Hsel, p.share_group,
-                     p.L, p.q_pos0, p.b, p.K, tpu, acc, ml);
-  hipError_t e = hipGetLastError();
+  char* base = static_cast<char*>(ws);
+  float* acc = reinterpret_cast<float*>(base);
+  float2* ml = reinterpret_cast<float2*>(base + align256(heads * ntiles * HPW * p.d * sizeof(float)));
+  hipError_t e = launch(false, decode_attn_partial_kernel<T, D, HPW>, dim3(ntiles, static_cast<unsigned>(heads)),
+                        dim3(256), st, static_cast<const T*>(p.q), static_cast<const T*>(p.k),
+                        static_cast<const T*>(p.v), p.idx, p.logg, p.Hq, p.Hkv, p.Hsel, p.share_group, p.L,
+                        p.q_pos0, p.b, p.K, tpu, acc, ml);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D, HPW>), dim3(static_cast<unsigned>(heads)), dim3(256), 0,
-                     st, acc, ml, p.Hq, p.Hkv, p.Hsel, p.share_group, ntiles, static_cast<T*>(p.o),
-                     p.lse);
-  return hipGetLastError();
+  return launch(true, decode_combine_kernel<T, D, HPW>, dim3(HPW, static_cast<unsigned>(heads)), dim3(256), st,
+                acc, ml, p.Hq, p.Hkv, p.Hsel, p.share_group, ntiles, static_cast<T*>(p.o), p.lse);
 }
 
 template <typename T, int D>
@@ -577,11 +603,10 @@ static hipError_t launch_decode_attn_t(const AttnLaunch& p, void* ws, hipStream_
 template <typename T, int D>
 static hipError_t launch_rows_fwd_t(const AttnLaunch& p, hipStream_t st) {
   dim3 grid((p.nq + 3) / 4, static_cast<unsigned>(p.B * p.Hq));
-  hipLaunchKernelGGL((rows_attn_fwd_kernel<T, D>), grid, dim3(256), 0, st, static_cast<const T*>(p.q),
-                     static_cast<const T*>(p.k), static_cast<const T*>(p.v), p.idx, p.logg, p.alpha, p.Hq,
-                     p.Hkv, p.Hsel, p.share_group, p.nq, p.q_pos0, p.L, p.b, p.prefix_mode, p.qblock,
-                     p.K, p.local, p.window, static_cast<T*>(p.o), p.lse);
-  return hipGetLastError();
+  return launch(true, rows_attn_fwd_kernel<T, D>, grid, dim3(256), st, static_cast<const T*>(p.q),
+                static_cast<const T*>(p.k), static_cast<const T*>(p.v), p.idx, p.logg, p.alpha, p.Hq,
+                p.Hkv, p.Hsel, p.share_group, p.nq, p.q_pos0, p.L, p.b, p.prefix_mode, p.qblock, p.K,
+                p.local, p.window, static_cast<T*>(p.o), p.lse);
 }
 
 hipError_t launch_attn_fwd(const AttnLaunch& p, void* ws, hipStream_t st) {
@@ -598,30 +623,22 @@ static hipError_t launch_bwd_t(const BwdLaunch& p, void* ws, hipStream_t st) {
   const AttnLaunch& a = p.a;
   float* Dbuf = static_cast<float*>(ws);
   const int64_t rows = static_cast<int64_t>(a.B) * a.Hq * a.nq;
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, st,
-                     static_cast<const T*>(p.o), static_cast<const T*>(p.dout), rows, Dbuf);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch(false, bwd_pre_kernel<T, D>, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256),
+                        st, static_cast<const T*>(p.o), static_cast<const T*>(p.dout), rows, Dbuf);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((a.nq + 3) / 4, static_cast<unsigned>(a.B * a.Hsel)),
-                     dim3(256), 0, st, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                     static_cast<const T*>(a.v), static_cast<const T*>(p.dout), p.lse, Dbuf, a.idx,
-                     a.logg, a.Hq, a.Hkv, a.Hsel, a.share_group, a.nq, a.q_pos0, a.L, a.b, a.K,
-                     static_cast<T*>(p.dq), p.dg);
-  e = hipGetLastError();
+  e = launch(false, bwd_dq_kernel<T, D>, dim3((a.nq + 3) / 4, static_cast<unsigned>(a.B * a.Hsel)), dim3(256),
+             st, static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+             static_cast<const T*>(p.dout), p.lse, Dbuf, a.idx, a.logg, a.Hq, a.Hkv, a.Hsel, a.share_group,
+             a.nq, a.q_pos0, a.L, a.b, a.K, static_cast<T*>(p.dq), p.dg);
   if (e != hipSuccess) return e;
   const int64_t nblk = (a.L + a.b - 1) / a.b;
   const dim3 grid(static_cast<unsigned>(nblk), static_cast<unsigned>(a.B * a.Hkv));
-#define SPA_DKDV(BSV)                                                                              \
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, BSV>), grid, dim3(256), 0, st, static_cast<const T*>(a.q), \
-                     static_cast<const T*>(a.k), static_cast<const T*>(a.v),                        \
-                     static_cast<const T*>(p.dout), p.lse, Dbuf, a.idx, a.logg, a.Hq, a.Hkv, a.Hsel, \
-                     a.share_group, a.nq, a.q_pos0, a.L, a.K, static_cast<T*>(p.dk),               \
-                     static_cast<T*>(p.dv))
-  if (a.b == 16) SPA_DKDV(16);
-  else if (a.b == 32) SPA_DKDV(32);
-  else SPA_DKDV(64);
-#undef SPA_DKDV
-  return hipGetLastError();
+  auto kern = a.b == 16 ? bwd_dkdv_kernel<T, D, 16> : (a.b == 32 ? bwd_dkdv_kernel<T, D, 32>
+                                                                  : bwd_dkdv_kernel<T, D, 64>);
+  return launch(true, kern, grid, dim3(256), st, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                static_cast<const T*>(a.v), static_cast<const T*>(p.dout), p.lse, Dbuf, a.idx, a.logg,
+                a.Hq, a.Hkv, a.Hsel, a.share_group, a.nq, a.q_pos0, a.L, a.K, static_cast<T*>(p.dk),
+                static_cast<T*>(p.dv));
 }
 
 hipError_t launch_attn_bwd(const BwdLaunch& p, void* ws, hipStream_t st) {

@@ -11,10 +11,13 @@
 //  * decode (one query row, current-block prefix, no erf term): the candidate
 //    blocks of each selection head are split into chunks of 256; one
 //    workgroup per chunk streams the bf16 summaries (16-byte loads, several
-//    lanes per block), keeps the chunk's online (max, sum exp) and its top-K
-//    as packed 64-bit keys (wave bitonic sort + bitonic merges).  A second
-//    kernel merges the chunk lists per head, finishes the LSE and writes the
-//    ascending indices and log gates.
+//    lanes per block) and keeps the chunk's (max, sum exp) and its top-K.  A
+//    second small kernel (one wave per head) selects the top-K among the
+//    chunk winners, finishes the LSE and writes the ascending indices and log
+//    gates.  Both selections are threshold searches over ballot counts with
+//    an ordered compaction (no sorting network).  The kernel boundary
+//    publishes the chunk results; an in-kernel hand-off would need an
+//    agent-scope release per workgroup, which on gfx950 writes back the L2.
 //  * rows (any number of rows): one thread per query row, summaries staged in
 //    LDS 64 candidates at a time and read as broadcasts, a sorted top-K held
 //    in registers; the erf term is formed in fp64 so the ranking of scores
@@ -27,6 +30,36 @@
 namespace spa {
 
 // ------------------------------------------------------------------ decode
+// Top-K by threshold: the k-th largest score T is found with a bitwise
+// search over ballot counts (wave_kth_largest); the kept set is every score
+// > T plus the lowest-index scores == T.  Candidates are laid out so that
+// position order is index order, which makes the lower-index tie rule and
+// the ascending output a single ordered compaction (ballot + mbcnt).
+
+// Ordered compaction of one wave's NV x 64 positions (position i*64 + lane):
+// keeps keys > t and the first `need_eq` keys == t; calls emit(slot, i) for
+// every kept position.  Returns the number kept.
+template <int NV, typename Emit>
+__device__ __forceinline__ int wave_select_ordered(const uint32_t (&key)[NV], uint32_t t, int need_eq,
+                                                   Emit&& emit) {
+  int kept = 0, eq_seen = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const uint64_t eq = __ballot(key[i] == t && key[i] != 0u);
+    const bool take = key[i] > t || (key[i] == t && key[i] != 0u && eq_seen + lanes_below(eq) < need_eq);
+    const uint64_t tm = __ballot(take);
+    if (take) emit(kept + lanes_below(tm), i);
+    kept += __popcll(tm);
+    eq_seen += __popcll(eq);
+  }
+  return kept;
+}
+
+// One workgroup per (chunk of 256 candidate blocks, selection head).  All
+// global reads of the workgroup (the chunk's summaries, the query heads and,
+// with a projection, W) are issued before any of them is consumed.  Output:
+// the chunk's top-min(K, n) candidates in index order as 64-bit
+// (orderable score << 32 | block index) records (0 pads), and its (max, sum exp).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_chunk_kernel(
     const T* __restrict__ q, const T* __restrict__ kbar, const float* __restrict__ proj_w,
@@ -36,11 +69,11 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(
   constexpr int kLPB = D / kVec;           // lanes per block row
   constexpr int kBPR = kWave / kLPB;       // blocks per load round of a wave
   constexpr int kRounds = kWave / kBPR;    // rounds to cover the wave's 64 blocks
+  constexpr int kWVec = D * D / 4 / 256;   // 16-byte pieces of W per thread
+  __shared__ __align__(16) float s_w[D * D];
   __shared__ float s_q[D];
-  __shared__ float s_u[D];
+  __shared__ float s_u2[2][D];
   __shared__ float s_score[kDecodeChunk];
-  __shared__ uint64_t s_keys[4][kWave];
-  __shared__ float2 s_ml[4];
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int chunk = blockIdx.x;
@@ -48,46 +81,57 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(
   const int bi = bh / Hsel, hs = bh % Hsel;
   const int G = Hq / Hkv;
   const int kvh = share_group ? hs : hs / G;
+  const bool proj = proj_w != nullptr;
 
-  // q_hat (mean over the group's query heads when shared), then u = W^T q_hat
-  if (tid < D) {
-    float acc = 0.f;
-    if (share_group) {
-      for (int g = 0; g < G; ++g)
-        acc += ld_f(q + (static_cast<int64_t>(bi) * Hq + hs * G + g) * D + tid);
-      acc = acc / static_cast<float>(G);
-    } else {
-      acc = ld_f(q + (static_cast<int64_t>(bi) * Hq + hs) * D + tid);
-    }
-    s_q[tid] = acc;
-  }
-  __syncthreads();
-  if (tid < D) {
-    float u = s_q[tid];
-    if (proj_w != nullptr) {
-      u = 0.f;
-      for (int e = 0; e < D; ++e) u = fmaf(proj_w[e * D + tid], s_q[e], u);
-    }
-    s_u[tid] = u;
-  }
-  __syncthreads();
-
+  // 1. issue the chunk's summary loads
   const int cg = lane % kLPB, bl = lane / kLPB;
-  float uc[kVec];
-#pragma unroll
-  for (int i = 0; i < kVec; ++i) uc[i] = s_u[cg * kVec + i];
-
-  const int64_t wbase = static_cast<int64_t>(chunk) * kDecodeChunk + wave * kWave;
+  const int64_t cbase = static_cast<int64_t>(chunk) * kDecodeChunk;
+  const int64_t wbase = cbase + wave * kWave;
   const T* kb = kbar + (static_cast<int64_t>(bi) * Hkv + kvh) * ccap * D;
   uint4 raw[kRounds];
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
-    int64_t c = wbase + r * kBPR + bl;
-    if (c < ncand)
-      raw[r] = *reinterpret_cast<const uint4*>(kb + c * D + cg * kVec);
-    else
-      raw[r] = make_uint4(0, 0, 0, 0);
+    const int64_t c = wbase + r * kBPR + bl;
+    raw[r] = c < ncand ? *reinterpret_cast<const uint4*>(kb + c * D + cg * kVec) : make_uint4(0, 0, 0, 0);
   }
+  // 2. issue the query and projection loads
+  float qsum = 0.f;
+  if (tid < D) {
+    if (share_group) {
+      for (int g = 0; g < G; ++g) qsum += ld_f(q + (static_cast<int64_t>(bi) * Hq + hs * G + g) * D + tid);
+    } else {
+      qsum = ld_f(q + (static_cast<int64_t>(bi) * Hq + hs) * D + tid);
+    }
+  }
+  if (proj) {
+    uint4 wv[kWVec];
+#pragma unroll
+    for (int i = 0; i < kWVec; ++i) wv[i] = reinterpret_cast<const uint4*>(proj_w)[tid + i * 256];
+#pragma unroll
+    for (int i = 0; i < kWVec; ++i) reinterpret_cast<uint4*>(s_w)[tid + i * 256] = wv[i];
+  }
+  if (tid < D) s_q[tid] = share_group ? qsum / static_cast<float>(G) : qsum;
+  __syncthreads();
+  // 3. u = W^T q_hat (two half sums per output), or u = q_hat
+  {
+    const int f = tid % D, half = tid / D;
+    if (proj && half < 2) {
+      float a = 0.f;
+      const int e0 = half * (D / 2);
+#pragma unroll 16
+      for (int e = e0; e < e0 + D / 2; ++e) a = fmaf(s_w[e * D + f], s_q[e], a);
+      s_u2[half][f] = a;
+    }
+  }
+  __syncthreads();
+  float uc[kVec];
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) {
+    const int e = cg * kVec + i;
+    uc[i] = proj ? s_u2[0][e] + s_u2[1][e] : s_q[e];
+  }
+
+  // 4. scores of the chunk's blocks
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
@@ -96,98 +140,95 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(
     float p = 0.f;
 #pragma unroll
     for (int i = 0; i < kVec; ++i) p = fmaf(x[i], uc[i], p);
-#pragma unroll
-    for (int m = kLPB / 2; m > 0; m >>= 1) p += __shfl_xor(p, m, kWave);
+    p = group_sum<kLPB>(p);
     if (cg == 0) s_score[wave * kWave + r * kBPR + bl] = p * scale;
   }
   __syncthreads();
-
-  const int64_t c = wbase + lane;
-  const bool valid = c < ncand;
-  const float s = s_score[wave * kWave + lane];
-  uint64_t key = valid ? make_key(s, static_cast<int32_t>(c)) : 0ull;
-  key = wave_sort_desc(key, lane);
-  s_keys[wave][lane] = key;
-  float m = wave_max(valid ? s : -INFINITY);
-  float l = wave_sum(valid ? __expf(s - m) : 0.f);
-  if (m == -INFINITY) l = 0.f;
-  if (lane == 0) s_ml[wave] = make_float2(m, l);
-  __syncthreads();
-
-  if (wave == 0) {
-    uint64_t top = s_keys[0][lane];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) top = wave_merge_top_desc(top, s_keys[w][kWave - 1 - lane], lane);
-    const int64_t o = static_cast<int64_t>(bh) * nchunks + chunk;
-    if (lane < K) ws_keys[o * K + lane] = top;
-    if (lane == 0) {
-      float mm = s_ml[0].x, ll = s_ml[0].y;
-      for (int w = 1; w < 4; ++w) ml_combine(mm, ll, s_ml[w].x, s_ml[w].y);
-      ws_ml[o] = make_float2(mm, ll);
-    }
-  }
-}
-
-__global__ __launch_bounds__(256) void decode_merge_kernel(
-    const uint64_t* __restrict__ ws_keys, const float2* __restrict__ ws_ml, int nchunks, int K,
-    int64_t ncand, int gate, int nq, int row, int32_t* __restrict__ idx, float* __restrict__ logg,
-    int32_t* __restrict__ k_eff) {
-  __shared__ uint64_t s_top[4][kWave];
-  __shared__ float2 s_ml[4];
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int bh = blockIdx.x;
-  const uint64_t* keys = ws_keys + static_cast<int64_t>(bh) * nchunks * K;
-
-  uint64_t top = 0ull;
-  for (int ch = wave; ch < nchunks; ch += 4) {
-    const int r = kWave - 1 - lane;
-    uint64_t brev = r < K ? keys[static_cast<int64_t>(ch) * K + r] : 0ull;
-    top = wave_merge_top_desc(top, brev, lane);
-  }
-  s_top[wave][lane] = top;
-
-  float m = -INFINITY, l = 0.f;
-  for (int ch = tid; ch < nchunks; ch += 256) {
-    float2 v = ws_ml[static_cast<int64_t>(bh) * nchunks + ch];
-    ml_combine(m, l, v.x, v.y);
-  }
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    float m2 = __shfl_xor(m, off, kWave), l2 = __shfl_xor(l, off, kWave);
-    ml_combine(m, l, m2, l2);
-  }
-  if (lane == 0) s_ml[wave] = make_float2(m, l);
-  __syncthreads();
   if (wave != 0) return;
 
-  top = s_top[0][lane];
+  // 5. wave 0: chunk (max, sum exp) and top-min(K, n) in index order
+  const int nvalid = static_cast<int>(ncand - cbase < kDecodeChunk ? ncand - cbase : kDecodeChunk);
+  uint32_t key[4];
+  float sc[4];
+  float mloc = -INFINITY;
 #pragma unroll
-  for (int w = 1; w < 4; ++w) top = wave_merge_top_desc(top, s_top[w][kWave - 1 - lane], lane);
-  float mm = s_ml[0].x, ll = s_ml[0].y;
-  for (int w = 1; w < 4; ++w) ml_combine(mm, ll, s_ml[w].x, s_ml[w].y);
-  const float lse = mm + __logf(ll);
+  for (int i = 0; i < 4; ++i) {
+    const int pidx = i * kWave + lane;
+    sc[i] = s_score[pidx];
+    const bool ok = pidx < nvalid;
+    key[i] = ok ? orderable_f32(sc[i]) : 0u;
+    if (ok) mloc = fmaxf(mloc, sc[i]);
+  }
+  const float m = wave_max(mloc);
+  float lloc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i * kWave + lane < nvalid) lloc += __expf(sc[i] - m);
+  const float l = m == -INFINITY ? 0.f : wave_sum(lloc);
+  const int kk = nvalid < K ? (nvalid > 0 ? nvalid : 0) : K;
+  const uint32_t t = wave_kth_largest<4>(key, kk);
+  int ngt = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ngt += __popcll(__ballot(key[i] > t));
+  uint64_t* out = ws_keys + (static_cast<int64_t>(bh) * nchunks + chunk) * K;
+  const int kept = wave_select_ordered<4>(key, t, kk - ngt, [&](int slot, int i) {
+    out[slot] = (static_cast<uint64_t>(key[i]) << 32) | static_cast<uint32_t>(cbase + i * kWave + lane);
+  });
+  for (int x = kept + lane; x < K; x += kWave) out[x] = 0ull;
+  if (lane == 0) ws_ml[static_cast<int64_t>(bh) * nchunks + chunk] = make_float2(m, l);
+}
 
-  const int keff = static_cast<int>(ncand < K ? ncand : K);
-  // re-sort the kept keys by index ascending: key2 = (~index << 32) | score bits
-  uint64_t key2 = 0ull;
-  if (lane < keff && top != 0ull) {
-    const uint32_t ci = static_cast<uint32_t>(key_index(top));
-    key2 = (static_cast<uint64_t>(~ci) << 32) | __float_as_uint(key_score(top));
+// One wave per selection head: the k-th largest score among all chunk
+// winners (laid out chunk by chunk, each in index order, so position order is
+// index order), the LSE from the chunk partials, then the ascending indices
+// and log gates.  NV = candidate records per lane.
+template <int NV>
+__global__ __launch_bounds__(64) void decode_merge_kernel(
+    const uint64_t* __restrict__ ws_keys, const float2* __restrict__ ws_ml, int nchunks, int K,
+    int64_t ncand, int gate, int32_t* __restrict__ idx, float* __restrict__ logg,
+    int32_t* __restrict__ k_eff) {
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int total = nchunks * K;
+  const uint64_t* rec = ws_keys + static_cast<int64_t>(bh) * total;
+  uint64_t r[NV];
+  uint32_t key[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int pidx = i * kWave + lane;
+    r[i] = pidx < total ? rec[pidx] : 0ull;
   }
-  key2 = wave_sort_desc(key2, lane);
-  const int64_t o = (static_cast<int64_t>(bh) * nq + row) * K;
-  if (lane < K) {
-    if (lane < keff) {
-      const int32_t ci = static_cast<int32_t>(~static_cast<uint32_t>(key2 >> 32));
-      const float sc = __uint_as_float(static_cast<uint32_t>(key2));
-      idx[o + lane] = ci;
-      if (logg != nullptr) logg[o + lane] = gate ? (sc - lse) : 0.f;
-    } else {
-      idx[o + lane] = -1;
-      if (logg != nullptr) logg[o + lane] = 0.f;
-    }
+  float m = -INFINITY, l = 0.f;
+  for (int ch = lane; ch < nchunks; ch += kWave) {
+    const float2 v = ws_ml[static_cast<int64_t>(bh) * nchunks + ch];
+    ml_combine(m, l, v.x, v.y);
   }
-  if (lane == 0 && k_eff != nullptr) k_eff[static_cast<int64_t>(bh) * nq + row] = keff;
+  {
+    float m2 = xor_lanes_f<32>(m), l2 = xor_lanes_f<32>(l); ml_combine(m, l, m2, l2);
+    m2 = xor_lanes_f<16>(m); l2 = xor_lanes_f<16>(l); ml_combine(m, l, m2, l2);
+    m2 = xor_lanes_f<8>(m); l2 = xor_lanes_f<8>(l); ml_combine(m, l, m2, l2);
+    m2 = xor_lanes_f<4>(m); l2 = xor_lanes_f<4>(l); ml_combine(m, l, m2, l2);
+    m2 = xor_lanes_f<2>(m); l2 = xor_lanes_f<2>(l); ml_combine(m, l, m2, l2);
+    m2 = xor_lanes_f<1>(m); l2 = xor_lanes_f<1>(l); ml_combine(m, l, m2, l2);
+  }
+  const float lse = m + __logf(l);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) key[i] = static_cast<uint32_t>(r[i] >> 32);
+  const int kk = static_cast<int>(ncand < K ? ncand : K);
+  const uint32_t t = wave_kth_largest<NV>(key, kk);
+  int ngt = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) ngt += __popcll(__ballot(key[i] > t));
+  const int64_t o = static_cast<int64_t>(bh) * K;          // one query row
+  const int kept = wave_select_ordered<NV>(key, t, kk - ngt, [&](int slot, int i) {
+    idx[o + slot] = static_cast<int32_t>(static_cast<uint32_t>(r[i]));
+    if (logg != nullptr) logg[o + slot] = gate ? from_orderable_f32(key[i]) - lse : 0.f;
+  });
+  for (int x = kept + lane; x < K; x += kWave) {
+    idx[o + x] = -1;
+    if (logg != nullptr) logg[o + x] = 0.f;
+  }
+  if (lane == 0 && k_eff != nullptr) k_eff[bh] = kk;
 }
 
 // -------------------------------------------------------------------- rows
@@ -349,8 +390,19 @@ __global__ __launch_bounds__(256) void rows_select_kernel(
 }
 
 // ------------------------------------------------------------------ launch
+// Records per lane the merge kernel may hold (up to 64 x 64 chunk winners).
+constexpr int kMergeMaxNV = 64;
+
+static int merge_nv(const SelectLaunch& p) {
+  const int64_t nch = decode_num_chunks(p.max_cand > 0 ? p.max_cand : 1);
+  const int64_t total = nch * p.K;
+  int nv = 1;
+  while (static_cast<int64_t>(nv) * kWave < total) nv *= 2;
+  return nv;
+}
+
 static bool use_decode_path(const SelectLaunch& p) {
-  return p.nq == 1 && p.prefix_mode == 0 && p.erf_lambda == nullptr;
+  return p.nq == 1 && p.prefix_mode == 0 && p.erf_lambda == nullptr && merge_nv(p) <= kMergeMaxNV;
 }
 
 size_t select_workspace_bytes(const SelectLaunch& p) {
@@ -365,36 +417,36 @@ static hipError_t launch_decode_t(const SelectLaunch& p, void* ws, hipStream_t s
   const int64_t ncand = p.max_cand;
   const int nch = static_cast<int>(decode_num_chunks(ncand > 0 ? ncand : 1));
   const size_t heads = static_cast<size_t>(p.B) * p.Hsel;
-  uint64_t* keys = static_cast<uint64_t*>(ws);
-  float2* ml = reinterpret_cast<float2*>(static_cast<char*>(ws) +
-                                         align256(heads * nch * p.K * sizeof(uint64_t)));
-  hipLaunchKernelGGL((decode_chunk_kernel<T, D>), dim3(nch, static_cast<unsigned>(heads)), dim3(256),
-                     0, st, static_cast<const T*>(p.q), static_cast<const T*>(p.kbar), p.proj_w,
-                     p.Hq, p.Hkv, p.Hsel, p.share_group, p.ccap, ncand, p.K, keys, ml, nch);
-  hipError_t e = hipGetLastError();
+  char* base = static_cast<char*>(ws);
+  uint64_t* keys = reinterpret_cast<uint64_t*>(base);
+  float2* ml = reinterpret_cast<float2*>(base + align256(heads * nch * p.K * sizeof(uint64_t)));
+  hipError_t e = launch(false, decode_chunk_kernel<T, D>, dim3(nch, static_cast<unsigned>(heads)), dim3(256),
+                        st, static_cast<const T*>(p.q), static_cast<const T*>(p.kbar), p.proj_w, p.Hq,
+                        p.Hkv, p.Hsel, p.share_group, p.ccap, ncand, p.K, keys, ml, nch);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(static_cast<unsigned>(heads)), dim3(256), 0, st,
-                     keys, ml, nch, p.K, ncand, p.gate, 1, 0, p.idx, p.logg, p.k_eff);
-  return hipGetLastError();
+  void (*merge)(const uint64_t*, const float2*, int, int, int64_t, int, int32_t*, float*, int32_t*);
+  switch (merge_nv(p)) {
+    case 1: merge = decode_merge_kernel<1>; break;
+    case 2: merge = decode_merge_kernel<2>; break;
+    case 4: merge = decode_merge_kernel<4>; break;
+    case 8: merge = decode_merge_kernel<8>; break;
+    case 16: merge = decode_merge_kernel<16>; break;
+    case 32: merge = decode_merge_kernel<32>; break;
+    default: merge = decode_merge_kernel<64>; break;
+  }
+  return launch(true, merge, dim3(static_cast<unsigned>(heads)), dim3(kWave), st, keys, ml, nch, p.K, ncand,
+                p.gate, p.idx, p.logg, p.k_eff);
 }
 
 template <typename T, int D, int KMAX>
 static hipError_t launch_rows_k(const SelectLaunch& p, hipStream_t st) {
   dim3 grid((p.nq + 255) / 256, static_cast<unsigned>(p.B * p.Hsel));
-  if (p.erf_lambda != nullptr) {
-    hipLaunchKernelGGL((rows_select_kernel<T, D, KMAX, true>), grid, dim3(256), 0, st,
-                       static_cast<const T*>(p.q), static_cast<const T*>(p.kbar), p.max_norm,
-                       p.centre, p.proj_w, p.erf_lambda, p.erf_sigma, p.Hq, p.Hkv, p.Hsel, p.nq,
-                       p.q_pos0, p.ccap, p.b, p.prefix_mode, p.qblock, p.share_group, p.K, p.gate,
-                       p.idx, p.logg, p.k_eff);
-  } else {
-    hipLaunchKernelGGL((rows_select_kernel<T, D, KMAX, false>), grid, dim3(256), 0, st,
-                       static_cast<const T*>(p.q), static_cast<const T*>(p.kbar), p.max_norm,
-                       p.centre, p.proj_w, p.erf_lambda, p.erf_sigma, p.Hq, p.Hkv, p.Hsel, p.nq,
-                       p.q_pos0, p.ccap, p.b, p.prefix_mode, p.qblock, p.share_group, p.K, p.gate,
-                       p.idx, p.logg, p.k_eff);
-  }
-  return hipGetLastError();
+  auto kern = p.erf_lambda != nullptr ? rows_select_kernel<T, D, KMAX, true>
+                                       : rows_select_kernel<T, D, KMAX, false>;
+  return launch(true, kern, grid, dim3(256), st, static_cast<const T*>(p.q),
+                static_cast<const T*>(p.kbar), p.max_norm, p.centre, p.proj_w, p.erf_lambda,
+                p.erf_sigma, p.Hq, p.Hkv, p.Hsel, p.nq, p.q_pos0, p.ccap, p.b, p.prefix_mode, p.qblock,
+                p.share_group, p.K, p.gate, p.idx, p.logg, p.k_eff);
 }
 
 template <typename T, int D>

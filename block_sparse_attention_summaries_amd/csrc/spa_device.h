@@ -167,16 +167,86 @@ __device__ __forceinline__ uint32_t wave_sort_asc_u32(uint32_t key, int lane) {
   return key;
 }
 
+// ------------------------------------------------------- lane exchanges (VALU)
+// v from lane (lane ^ M), without going through LDS: DPP row permutes for
+// M = 1, 2, 4, 8 (xor 4 = xor 3 then xor 7; xor 8 = xor 7 then xor 15) and the
+// gfx950 permlane16/32 swaps for M = 16, 32.
+template <int M>
+__device__ __forceinline__ uint32_t xor_lanes(uint32_t v) {
+  if constexpr (M == 1) {
+    return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);            // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);            // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4) {
+    const uint32_t t = __builtin_amdgcn_mov_dpp(v, 0x1B, 0xF, 0xF, false); // quad_perm [3,2,1,0]
+    return __builtin_amdgcn_mov_dpp(t, 0x141, 0xF, 0xF, false);           // row_half_mirror
+  } else if constexpr (M == 8) {
+    const uint32_t t = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);
+    return __builtin_amdgcn_mov_dpp(t, 0x140, 0xF, 0xF, false);           // row_mirror
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (__lane_id() & 16) ? r[0] : r[1];
+  } else {
+    static_assert(M == 32, "xor distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (__lane_id() & 32) ? r[0] : r[1];
+  }
+}
+template <int M>
+__device__ __forceinline__ float xor_lanes_f(float v) {
+  return __uint_as_float(xor_lanes<M>(__float_as_uint(v)));
+}
+
 // ----------------------------------------------------------- wave reductions
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = kWave / 2; m > 0; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
+  v = fmaxf(v, xor_lanes_f<32>(v));
+  v = fmaxf(v, xor_lanes_f<16>(v));
+  v = fmaxf(v, xor_lanes_f<8>(v));
+  v = fmaxf(v, xor_lanes_f<4>(v));
+  v = fmaxf(v, xor_lanes_f<2>(v));
+  return fmaxf(v, xor_lanes_f<1>(v));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = kWave / 2; m > 0; m >>= 1) v += __shfl_xor(v, m, kWave);
+  v += xor_lanes_f<32>(v);
+  v += xor_lanes_f<16>(v);
+  v += xor_lanes_f<8>(v);
+  v += xor_lanes_f<4>(v);
+  v += xor_lanes_f<2>(v);
+  return v + xor_lanes_f<1>(v);
+}
+// Sum over aligned groups of G lanes (G a power of two <= 64).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 64) v += xor_lanes_f<32>(v);
+  if constexpr (G >= 32) v += xor_lanes_f<16>(v);
+  if constexpr (G >= 16) v += xor_lanes_f<8>(v);
+  if constexpr (G >= 8) v += xor_lanes_f<4>(v);
+  if constexpr (G >= 4) v += xor_lanes_f<2>(v);
+  if constexpr (G >= 2) v += xor_lanes_f<1>(v);
   return v;
+}
+
+// Number of set bits of a wave-uniform mask held by lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u)));
+}
+
+// Largest value T such that at least k of the wave's NV x 64 keys are >= T
+// (the k-th largest key; 0 if k == 0 or nothing qualifies).  Bitwise search
+// from the top bit; each step counts with ballots, so the count never leaves
+// the scalar unit.  Keys equal to 0 never count.
+template <int NV>
+__device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t (&key)[NV], int k) {
+  uint32_t t = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+    if (cnt >= k) t = cand;
+  }
+  return k > 0 ? t : 0xFFFFFFFFu;
 }
 
 // Online-softmax combine of (m, l) pairs: result represents l e^m.

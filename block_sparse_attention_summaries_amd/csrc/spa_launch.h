@@ -3,6 +3,7 @@
 // validated when these are filled in.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -73,6 +74,34 @@ struct BwdLaunch {
   float* dg;
 };
 
+// Optional per-call profiling events (see spa_profile_next_call): the i-th
+// kernel launched by the next entry-point call records events[2i] when it
+// begins and events[2i+1] when it ends (dispatch timestamps).  Thread-local.
+struct ProfileEvents {
+  hipEvent_t* events;   // 2 * count handles, or nullptr
+  int count;            // kernels to bracket
+  int next;             // launches made so far in this call
+};
+ProfileEvents& profile_events();
+
+// Launch `kernel` on `st`.  Arguments are converted to the kernel's parameter
+// types.  (`last` marks the final kernel of an entry-point call.)
+template <typename... KArgs, typename... Args>
+hipError_t launch(bool last, void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
+                  Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  (void)last;
+  ProfileEvents& pe = profile_events();
+  hipEvent_t s = nullptr, e = nullptr;
+  if (pe.events != nullptr && pe.next < pe.count) {
+    s = pe.events[2 * pe.next];
+    e = pe.events[2 * pe.next + 1];
+  }
+  ++pe.next;
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, st, s, e, 0, static_cast<KArgs>(args)...);
+  return hipGetLastError();
+}
+
 // Decode selection: chunked scoring + per-chunk top-K, then a merge.
 constexpr int kDecodeChunk = 256;  // candidate blocks per scoring workgroup
 
@@ -82,6 +111,7 @@ inline int64_t decode_num_chunks(int64_t max_cand) {
 
 // Workspace layout helpers (bytes, 256-aligned sections).
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
 
 size_t select_workspace_bytes(const SelectLaunch& p);
 size_t attn_fwd_workspace_bytes(const AttnLaunch& p);

@@ -83,10 +83,9 @@ __global__ __launch_bounds__(256) void block_summaries_kernel(
 template <typename T, int D>
 static hipError_t launch_summaries_t(const SummaryLaunch& p, hipStream_t st) {
   dim3 grid(static_cast<unsigned>(p.num_blocks), static_cast<unsigned>(p.B * p.Hkv));
-  hipLaunchKernelGGL((block_summaries_kernel<T, D>), grid, dim3(256), 0, st,
-                     static_cast<const T*>(p.k), p.Hkv, p.L, p.b, p.first_block, p.num_blocks,
-                     p.ccap, static_cast<T*>(p.kbar), p.max_norm, p.centre);
-  return hipGetLastError();
+  return launch(true, block_summaries_kernel<T, D>, grid, dim3(256), st, static_cast<const T*>(p.k),
+                p.Hkv, p.L, p.b, p.first_block, p.num_blocks, p.ccap, static_cast<T*>(p.kbar),
+                p.max_norm, p.centre);
 }
 
 hipError_t launch_block_summaries(const SummaryLaunch& p, hipStream_t st) {

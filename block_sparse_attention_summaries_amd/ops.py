@@ -25,7 +25,7 @@ SPA_GATE_NONE, SPA_GATE_SOFTMAX_LOG = 0, 1
 SPA_LOCAL_CURRENT_BLOCK, SPA_LOCAL_NONE = 0, 1
 SPA_OP_SCORE_SELECT, SPA_OP_ATTN_FWD, SPA_OP_ATTN_BWD = 1, 2, 3
 
-EXPORTED = ["spa_abi_version", "spa_last_error", "sparse_block_summaries", "sparse_score_select",
+EXPORTED = ["spa_abi_version", "spa_profile_next_call", "spa_last_error", "sparse_block_summaries", "sparse_score_select",
             "sparse_attn_fwd", "sparse_attn_bwd", "sparse_workspace_bytes", "sparse_workspace_init"]
 
 _vp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -65,6 +65,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.spa_abi_version.restype = _i
         L.spa_abi_version.argtypes = []
+        L.spa_profile_next_call.restype = _i
+        L.spa_profile_next_call.argtypes = [ctypes.POINTER(_vp), _i]
         L.spa_last_error.restype = ctypes.c_char_p
         L.spa_last_error.argtypes = []
         L.sparse_block_summaries.restype = _i

@@ -54,10 +54,10 @@
  * indices outside a row's candidate set are ignored.  NaN/Inf inputs give
  * unspecified values but never out-of-bounds accesses.
  *
- * Workspace: sparse_workspace_bytes() gives the size a call needs;
- * a workspace must be zero-filled once before its first use
- * (sparse_workspace_init does it with a kernel); every call leaves it in that
- * state again.  Calls that overlap in time must use distinct workspaces.
+ * Workspace: sparse_workspace_bytes() gives the size a call needs (device
+ * memory owned by the caller, 256-byte aligned).  Its contents are scratch:
+ * no initialisation is needed and nothing is kept between calls.  Calls that
+ * overlap in time must use distinct workspaces.
  */
 #ifndef SPARSE_ATTN_H
 #define SPARSE_ATTN_H
@@ -89,6 +89,19 @@ typedef enum { SPA_OP_SCORE_SELECT = 1, SPA_OP_ATTN_FWD = 2, SPA_OP_ATTN_BWD = 3
 
 /* Version of this ABI (SPA_ABI_VERSION). */
 int spa_abi_version(void);
+
+/* Kernel timing for callers that measure it (benchmarks, profilers).  Per
+ * calling thread: the next call of an entry point below launches its i-th
+ * kernel (i < count) with events[2i] recorded when that kernel begins and
+ * events[2i+1] when it ends, from the kernel's own dispatch timestamps
+ * (hipExtLaunchKernelGGL).  events holds 2*count hipEvent_t handles created
+ * by the caller; NULL entries are skipped.  The request is used up by that
+ * call whether or not it launches.  Do not use under graph capture.
+ * Kernels per call: summaries 1; score_select 2 on the decode path (chunk
+ * scoring, merge), else 1; attn_fwd 2 on the decode path (tile partials,
+ * combine), else 1; attn_bwd 3 (D, dq and dg, dk and dv).
+ * Returns SPA_ERR_INVALID_ARG if count < 0 or events is NULL with count > 0. */
+int spa_profile_next_call(void **events, int count);
 
 /* Message describing the last failed call made by this thread ("" if none).
  * The pointer stays valid until the next call on the same thread. */
@@ -210,7 +223,9 @@ int sparse_attn_bwd(const spa_attn_args *a, const void *o, const void *dout,
  * Returns 0 for invalid arguments (see spa_last_error()). */
 size_t sparse_workspace_bytes(int op, const void *args);
 
-/* Zero-fill a workspace with a kernel on `stream` (graph-capture safe). */
+/* Zero-fill a workspace with a kernel on `stream` (graph-capture safe).  Not
+ * required by any entry point; provided for callers that want deterministic
+ * scratch contents. */
 int sparse_workspace_init(void *workspace, size_t ws_bytes, spa_stream_t stream);
 
 #ifdef __cplusplus

@@ -370,3 +370,31 @@ def test_chunked_prefill_rows_after_offset():
                                      dev(ora["logg"].astype(np.float32)), b=b, K=K, q_pos0=q_pos0)
     check_indices(host(idx_g), ora)
     assert rel_err(host(o_g), o_o) <= 2e-2
+
+
+def test_one_workspace_shared_across_shapes_and_entry_points():
+    """A single workspace serves select and attention calls of different
+    shapes in turn (its contents are scratch, nothing carries over)."""
+    ws = ops.Workspace()
+    cases = [("decode_32k", dict(n=4096, K=16)), ("tiny_decode", dict(K=5, t=17)),
+             ("decode_32k", dict(n=2048, K=7, Hq=8, Hkv=8, share_group=False, seed=3)),
+             ("decode_32k", dict(n=8192, K=32, seed=4)), ("tiny_decode", dict(K=8))]
+    for name, over in cases:
+        cfg = config(name, **over)
+        x = make_inputs(cfg)
+        b, K, pos, gate, sg = cfg["b"], cfg["K"], x["q_pos0"], cfg["gate"], cfg["share_group"]
+        nblk = x["L"] // b
+        kw = dict(Hkv=cfg["Hkv"], b=b, K=K, q_pos0=pos, gate=gate, share_group=sg)
+        kb_o, mx_o, ce_o = oracle.block_summaries(x["k"], b, nblocks=nblk)
+        ora = oracle.score_select(x["q"], kb_o, mx_o, ce_o, **kw)
+        o_o, _ = oracle.attn_fwd(x["q"], x["k"], x["v"], ora["idx"], ora["logg"] if gate else None,
+                                 b=b, K=K, q_pos0=pos, share_group=sg)
+        kd = dev(x["k"])
+        kb, mx, ce = ops.sparse_block_summaries(kd, b)
+        idx, logg, _ = ops.sparse_score_select(dev(x["q"]), kb, mx, ce, workspace=ws, **kw)
+        lg = dev(ora["logg"].astype(np.float32)) if gate else None
+        o, _ = ops.sparse_attn_fwd(dev(x["q"]), kd, dev(x["v"]), dev(ora["idx"]), lg, b=b, K=K, q_pos0=pos,
+                                   share_group=sg, workspace=ws)
+        torch.cuda.synchronize()
+        check_indices(host(idx), ora)
+        assert rel_err(host(o), o_o) <= _tol(cfg), (name, over)
