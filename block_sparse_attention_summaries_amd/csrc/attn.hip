@@ -35,7 +35,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 constexpr int kTileTok = 64;
 
 // Online-softmax partial of one K/V tile for the HPW query heads of a group:
-// loads the tile into LDS once, then scores, (m, l) and acc per head.
+// loads the tile into LDS once, then scores, (m, l) and acc per head.  All
+// global loads are unconditional (rows past ntok are clamped to the last
+// valid row and masked out of the softmax).
 template <typename T, int D, int HPW>
 __device__ __forceinline__ void tile_partial(const T* __restrict__ q, const T* __restrict__ k,
                                              const T* __restrict__ v, int bi, int hs, int kvh, int G,
@@ -46,31 +48,38 @@ __device__ __forceinline__ void tile_partial(const T* __restrict__ q, const T* _
   constexpr int kVPR = D / kVec;                     // 16-byte vectors per row
   constexpr int kPadRow = D + kVec;                  // padded LDS row (elements)
   constexpr int kIters = kTileTok * kVPR / 256;
+  constexpr int kQIters = (HPW * D + 255) / 256;
+  constexpr int kCPL = D / kWave;                    // output columns per lane
   __shared__ __align__(16) T s_k[kTileTok * kPadRow];
   __shared__ __align__(16) T s_v[kTileTok * D];
   __shared__ float s_q[HPW][D];
   __shared__ float s_p[HPW][kTileTok];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
 
-  // issue every K / V load of the tile before touching LDS
+  // query heads first, then the K / V tile
+  float qv[kQIters];
+#pragma unroll
+  for (int it = 0; it < kQIters; ++it) {
+    int x = tid + it * 256;
+    x = x < HPW * D ? x : HPW * D - 1;
+    const int hh = x / D, e = x % D;
+    const int hq = share_group ? hs * G + hh : hs;
+    qv[it] = ld_f(q + (static_cast<int64_t>(bi) * Hq + hq) * D + e);
+  }
   const int64_t kvrow0 = (static_cast<int64_t>(bi) * Hkv + kvh) * L + start;
   uint4 rk[kIters], rv[kIters];
 #pragma unroll
   for (int it = 0; it < kIters; ++it) {
     const int x = tid + it * 256;
     const int r = x / kVPR, cv = x % kVPR;
-    if (r < ntok) {
-      rk[it] = *reinterpret_cast<const uint4*>(k + (kvrow0 + r) * D + cv * kVec);
-      rv[it] = *reinterpret_cast<const uint4*>(v + (kvrow0 + r) * D + cv * kVec);
-    } else {
-      rk[it] = make_uint4(0, 0, 0, 0);
-      rv[it] = make_uint4(0, 0, 0, 0);
-    }
+    const int rr = r < ntok ? r : ntok - 1;
+    rk[it] = *reinterpret_cast<const uint4*>(k + (kvrow0 + rr) * D + cv * kVec);
+    rv[it] = *reinterpret_cast<const uint4*>(v + (kvrow0 + rr) * D + cv * kVec);
   }
-  for (int x = tid; x < HPW * D; x += 256) {
-    const int hh = x / D, e = x % D;
-    const int hq = share_group ? hs * G + hh : hs;
-    s_q[hh][e] = ld_f(q + (static_cast<int64_t>(bi) * Hq + hq) * D + e);
+#pragma unroll
+  for (int it = 0; it < kQIters; ++it) {
+    const int x = tid + it * 256;
+    if (x < HPW * D) s_q[x / D][x % D] = qv[it];
   }
 #pragma unroll
   for (int it = 0; it < kIters; ++it) {
@@ -86,18 +95,15 @@ __device__ __forceinline__ void tile_partial(const T* __restrict__ q, const T* _
     const int hh = h0 + wave;
     if (hh < HPW) {
       const int j = lane;
-      float z = -INFINITY;
-      if (j < ntok) {
-        float acc = 0.f;
+      float acc = 0.f;
 #pragma unroll
-        for (int cv = 0; cv < kVPR; ++cv) {
-          float x[kVec];
-          Elem<T>::unpack(*reinterpret_cast<const uint4*>(&s_k[j * kPadRow + cv * kVec]), x);
+      for (int cv = 0; cv < kVPR; ++cv) {
+        float x[kVec];
+        Elem<T>::unpack(*reinterpret_cast<const uint4*>(&s_k[j * kPadRow + cv * kVec]), x);
 #pragma unroll
-          for (int i = 0; i < kVec; ++i) acc = fmaf(x[i], s_q[hh][cv * kVec + i], acc);
-        }
-        z = acc * scale + bias;
+        for (int i = 0; i < kVec; ++i) acc = fmaf(x[i], s_q[hh][cv * kVec + i], acc);
       }
+      const float z = j < ntok ? acc * scale + bias : -INFINITY;
       const float m = wave_max(z);
       const float p = j < ntok ? __expf(z - m) : 0.f;
       const float l = wave_sum(p);
@@ -109,13 +115,18 @@ __device__ __forceinline__ void tile_partial(const T* __restrict__ q, const T* _
   for (int h0 = 0; h0 < HPW; h0 += 4) {
     const int hh = h0 + wave;
     if (hh < HPW) {
+      // lane owns columns kCPL*lane .. +kCPL (adjacent, read together)
+      float acc[kCPL];
 #pragma unroll
-      for (int t = 0; t < D / kWave; ++t) {
-        const int e = lane + t * kWave;
-        float acc = 0.f;
-        for (int j = 0; j < ntok; ++j) acc = fmaf(s_p[hh][j], ld_f(&s_v[j * D + e]), acc);
-        ws_acc[(obase + hh) * D + e] = acc;
+      for (int c = 0; c < kCPL; ++c) acc[c] = 0.f;
+#pragma unroll 16
+      for (int j = 0; j < kTileTok; ++j) {
+        const float pj = s_p[hh][j];                 // 0 beyond ntok
+#pragma unroll
+        for (int c = 0; c < kCPL; ++c) acc[c] = fmaf(pj, ld_f(&s_v[j * D + kCPL * lane + c]), acc[c]);
       }
+#pragma unroll
+      for (int c = 0; c < kCPL; ++c) ws_acc[(obase + hh) * D + kCPL * lane + c] = acc[c];
     }
   }
 }
@@ -191,17 +202,28 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
   }
   for (int t = tid; t < ntiles; t += 256) s_ml[t] = ws_ml[base + t * HPW + hh];
   __syncthreads();
-  if (tid >= D) return;
-  float M = -INFINITY;
-  for (int t = 0; t < ntiles; ++t) M = fmaxf(M, s_ml[t].x);
-  float lsum = 0.f, acc = 0.f;
-  if (M != -INFINITY) {
-    for (int t = 0; t < ntiles; ++t) {
-      const float2 ml = s_ml[t];
-      const float w = ml.x == -INFINITY ? 0.f : __expf(ml.x - M);
-      lsum = fmaf(ml.y, w, lsum);
-      acc = fmaf(s_acc[t * D + tid], w, acc);
+  // softmax weights of the partials, once
+  __shared__ float s_wt[kMaxTiles];
+  __shared__ float s_M;
+  if (tid < kWave) {
+    float mloc = -INFINITY;
+    for (int t = tid; t < ntiles; t += kWave) mloc = fmaxf(mloc, s_ml[t].x);
+    const float M = wave_max(mloc);
+    for (int t = tid; t < ntiles; t += kWave) {
+      const float mt = s_ml[t].x;
+      s_wt[t] = (M == -INFINITY || mt == -INFINITY) ? 0.f : __expf(mt - M);
     }
+    if (tid == 0) s_M = M;
+  }
+  __syncthreads();
+  if (tid >= D) return;
+  const float M = s_M;
+  float lsum = 0.f, acc = 0.f;
+#pragma unroll 8
+  for (int t = 0; t < ntiles; ++t) {
+    const float w = s_wt[t];
+    lsum = fmaf(s_ml[t].y, w, lsum);
+    acc = fmaf(s_acc[t * D + tid], w, acc);
   }
   const int hq = share_group ? hs * G + hh : hs;
   const int64_t orow = static_cast<int64_t>(bi) * Hq + hq;   // one query row
@@ -614,6 +636,7 @@ hipError_t launch_attn_fwd(const AttnLaunch& p, void* ws, hipStream_t st) {
     if (p.dtype == 1) return p.d == 64 ? launch_decode_attn_t<bf16_t, 64>(p, ws, st) : launch_decode_attn_t<bf16_t, 128>(p, ws, st);
     return p.d == 64 ? launch_decode_attn_t<float, 64>(p, ws, st) : launch_decode_attn_t<float, 128>(p, ws, st);
   }
+  if (attn_tile_fwd_supported(p)) return launch_attn_tile_fwd(p, st);
   if (p.dtype == 1) return p.d == 64 ? launch_rows_fwd_t<bf16_t, 64>(p, st) : launch_rows_fwd_t<bf16_t, 128>(p, st);
   return p.d == 64 ? launch_rows_fwd_t<float, 64>(p, st) : launch_rows_fwd_t<float, 128>(p, st);
 }

@@ -1,0 +1,356 @@
+// attn_mfma.hip -- MFMA (bf16, gfx950 v_mfma_f32_32x32x16_bf16) forward of
+// the exact softmax attention over kept keys, for many query rows at once
+// (prefill / training).  Same semantics as the per-row kernel in attn.hip:
+//   branch L: current block (causal, bias 0) + selected units with their log
+//             gate ("SAS" review §4.1 Eq. 4, §4.3 Eq. 9);
+//   branch S: window i - w < j <= i, mixed o = alpha o_L + (1 - alpha) o_S
+//             ("FreeSolo" review, "How it works").
+//
+// Work decomposition.  A workgroup of 4 waves covers 32-row query tiles of
+// up to 4 query heads of one kv head (heads of a group share the K / V
+// tiles).  It first builds, in LDS, the ascending list of 32-key tiles that
+// any of its rows reads (current blocks, selected units, window band), then
+// streams those tiles through LDS (double buffered): K row-major, V
+// transposed.  Each wave computes S^T = K Q^T (keys x queries) so that one
+// lane owns one query row: the softmax max / sum are in-lane plus one
+// exchange between the two half-waves.  K rows are fed to the MFMA in a
+// permuted order so that the probabilities a lane holds are exactly the
+// B operand of O^T += V^T P^T for keys 16s + 8h .. +7 (h = half-wave), whose
+// A operand is then one 16-byte read of the transposed V tile.  Per-row
+// masks / biases come from a cursor walk over the row's ascending selection.
+#include "spa_device.h"
+#include "spa_launch.h"
+
+namespace spa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16_t;
+
+constexpr int kKT = 32;               // keys per tile
+constexpr int kMaxKeyTiles = 2048;    // key tiles per sequence (L <= 65536)
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// key (within a 32-key tile) held in S^T register r by half-wave h: the
+// MFMA A row m = 8a + 4h + c (r = 4a + c) is fed K row pi(m) with
+// pi(8a + 4h + c) = 16 floor(a/2) + 8h + 4 (a mod 2) + c.
+__device__ __forceinline__ int tile_key(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
+__device__ __forceinline__ int perm_row(int m) {
+  const int a = m >> 3, h = (m >> 2) & 1, c = m & 3;
+  return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + c;
+}
+
+template <int D>
+struct TileSmem {
+  static constexpr int kKPitch = D + 8;      // bf16 elements per K row in LDS
+  static constexpr int kVPitch = kKT + 8;    // bf16 elements per V^T row in LDS
+  __bf16 k[2][kKT * kKPitch];
+  __bf16 vt[2][D * kVPitch];
+};
+
+// Selection data of one (wave) query tile: per row the ascending units and
+// their log gates, read with a cursor as key tiles ascend.
+constexpr int kMaxSelK = 32;
+
+template <int D, bool kMix>
+__global__ __launch_bounds__(256) void attn_tile_fwd_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const int32_t* __restrict__ idx, const float* __restrict__ logg, const float* __restrict__ alpha,
+    int Hq, int Hkv, int Hsel, int share_group, int nq, int64_t q_pos0, int64_t L, int b,
+    int prefix_mode, int qblock, int K, int local, int window, __bf16* __restrict__ o,
+    float* __restrict__ lse, int NH, int NT) {
+  __shared__ TileSmem<D> sm;
+  __shared__ uint32_t s_bits[2][kMaxKeyTiles / 32];
+  __shared__ uint16_t s_list[2][kMaxKeyTiles];
+  __shared__ int s_count[2];
+  __shared__ int32_t s_idx[4][32][kMaxSelK / 2 + 1];   // packed pairs of int16 units
+  __shared__ float s_lg[4][32][kMaxSelK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, ql = lane & 31;              // half-wave, query lane
+  const int G = Hq / Hkv;
+  const int hgroups = G / NH;
+  const int bz = blockIdx.y;
+  const int bi = bz / (Hkv * hgroups);
+  const int kvh = (bz / hgroups) % Hkv;
+  const int hg = bz % hgroups;
+  const int h = kvh * G + hg * NH + (wave % NH);          // this wave's query head
+  const int hs = share_group ? kvh : h;
+  const int tile = blockIdx.x * NT + wave / NH;            // this wave's 32-row tile
+  const int row = tile * 32 + ql;
+  const bool row_ok = row < nq;
+  const int rowc = row_ok ? row : nq - 1;
+  const int64_t pos = q_pos0 + rowc;
+  const int64_t ncand = num_candidates(pos, b, prefix_mode, qblock);
+  const int nkt = static_cast<int>((L + kKT - 1) / kKT);
+  const int nwords = (nkt + 31) / 32;
+  constexpr bool mix = kMix;
+
+  // ---- per-row selection tables (this wave's rows), unit = -1 when unused
+  const int64_t so = ((static_cast<int64_t>(bi) * Hsel + hs) * nq + rowc) * K;
+  for (int t = hl; t < K; t += 2) {
+    const int32_t c = idx[so + t];
+    const bool ok = row_ok && c >= 0 && c < ncand;
+    reinterpret_cast<int16_t*>(s_idx[wave][ql])[t] = static_cast<int16_t>(ok ? c : -1);
+    s_lg[wave][ql][t] = (ok && logg != nullptr) ? logg[so + t] : 0.f;
+  }
+  // ---- key-tile lists: list 0 = branch L, list 1 = window branch
+  for (int x = tid; x < 2 * (kMaxKeyTiles / 32); x += 256) (&s_bits[0][0])[x] = 0u;
+  __syncthreads();
+  // row range of the workgroup (positions)
+  const int64_t wg_row0 = static_cast<int64_t>(blockIdx.x) * NT * 32;
+  const int64_t wg_row1 = (wg_row0 + NT * 32 < nq ? wg_row0 + NT * 32 : nq) - 1;
+  const int64_t p0 = q_pos0 + wg_row0, p1 = q_pos0 + wg_row1;
+  if (local == 0) {
+    // current blocks of the rows: keys [floor(p0/b) b, p1]
+    const int64_t k0 = (p0 / b) * b;
+    for (int64_t t = k0 / kKT + tid; t <= p1 / kKT; t += 256)
+      atomicOr(&s_bits[0][t >> 5], 1u << (t & 31));
+  }
+  if (mix) {
+    const int64_t k0 = p0 - window + 1 > 0 ? p0 - window + 1 : 0;
+    for (int64_t t = k0 / kKT + tid; t <= p1 / kKT; t += 256)
+      atomicOr(&s_bits[1][t >> 5], 1u << (t & 31));
+  }
+  for (int t = hl; t < K; t += 2) {
+    const int c = reinterpret_cast<int16_t*>(s_idx[wave][ql])[t];
+    if (c >= 0) {
+      const int64_t a0 = static_cast<int64_t>(c) * b, a1 = a0 + b - 1;
+      for (int64_t kt = a0 / kKT; kt <= a1 / kKT; ++kt) atomicOr(&s_bits[0][kt >> 5], 1u << (kt & 31));
+    }
+  }
+  __syncthreads();
+  // compaction into ascending lists (wave 0: list 0, wave 1: list 1)
+  if (wave < 2) {
+    int base = 0;
+    for (int w0 = 0; w0 < nwords; w0 += 64) {
+      const int wi = w0 + lane;
+      const uint32_t bits = wi < nwords ? s_bits[wave][wi] : 0u;
+      const int cnt = __popc(bits);
+      // inclusive scan of cnt over the wave
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int up = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += up;
+      }
+      int wpos = base + incl - cnt;
+      uint32_t bb = bits;
+      while (bb) {
+        const int bit = __ffs(bb) - 1;
+        bb &= bb - 1;
+        s_list[wave][wpos++] = static_cast<uint16_t>(wi * 32 + bit);
+      }
+      base += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) s_count[wave] = base;
+  }
+  __syncthreads();
+
+  // ---- Q^T operand (B of S^T = K Q^T): lane holds Q[row][16 ks + 8 hl .. +8]
+  constexpr int kKS = D / 16;
+  uint4 qreg[kKS];
+  const __bf16* qrow = q + ((static_cast<int64_t>(bi) * Hq + h) * nq + rowc) * D;
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) qreg[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hl);
+
+  const float scale2 = kLog2e / sqrtf(static_cast<float>(D));
+  const int64_t kvbase = (static_cast<int64_t>(bi) * Hkv + kvh) * L * D;
+  constexpr int kDB = D / 32;
+  float out[kMix ? kDB * 16 : 1];
+  float lse_L = -INFINITY;
+
+  for (int branch = 0; branch < (mix ? 2 : 1); ++branch) {
+    const int ntl = s_count[branch];
+    const uint16_t* list = s_list[branch];
+    floatx16_t acc[kDB];
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    float m2 = -INFINITY, lsum = 0.f;     // running max (log2 domain), sum
+    int cur = 0;                           // cursor into this row's units
+    const int64_t c_cur = pos / b;         // current unit of the row
+
+    // staging: 2 x 16 B of K and of V per thread per tile (D = 128), 1 (D = 64)
+    constexpr int kLd = kKT * D / 8 / 256;
+    uint4 kld[kLd > 0 ? kLd : 1], vld[kLd > 0 ? kLd : 1];
+    auto issue = [&](int it) {
+      const int64_t ks0 = static_cast<int64_t>(list[it]) * kKT;
+#pragma unroll
+      for (int i = 0; i < kLd; ++i) {
+        const int x = tid + i * 256;
+        const int kr = x / (D / 8), cv = x % (D / 8);
+        int64_t key = ks0 + kr;
+        key = key < L ? key : L - 1;
+        kld[i] = *reinterpret_cast<const uint4*>(k + kvbase + key * D + cv * 8);
+        vld[i] = *reinterpret_cast<const uint4*>(v + kvbase + key * D + cv * 8);
+      }
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < kLd; ++i) {
+        const int x = tid + i * 256;
+        const int kr = x / (D / 8), cv = x % (D / 8);
+        *reinterpret_cast<uint4*>(&sm.k[buf][kr * TileSmem<D>::kKPitch + cv * 8]) = kld[i];
+        const __bf16* vv = reinterpret_cast<const __bf16*>(&vld[i]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) sm.vt[buf][(cv * 8 + t) * TileSmem<D>::kVPitch + kr] = vv[t];
+      }
+    };
+    if (ntl > 0) {
+      issue(0);
+      stage(0);
+    }
+    __syncthreads();
+    for (int it = 0; it < ntl; ++it) {
+      const int buf = it & 1;
+      if (it + 1 < ntl) issue(it + 1);
+      const int64_t ks0 = static_cast<int64_t>(list[it]) * kKT;
+
+      // S^T = K Q^T for this wave's 32 rows
+      floatx16_t st;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[r] = 0.f;
+      const __bf16* krow = &sm.k[buf][perm_row(ql) * TileSmem<D>::kKPitch];
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        const uint4 a = *reinterpret_cast<const uint4*>(krow + 16 * ks + 8 * hl);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[ks]), st, 0, 0, 0);
+      }
+      // masks and biases (log2 domain)
+      float z[16];
+      if (branch == 0) {
+        // unit of the keys this lane holds: keys < 16 and >= 16 of the tile
+        float bias_lo = -INFINITY, bias_hi = -INFINITY;
+        const int64_t u_lo = (ks0 + 8 * hl) / b, u_hi = (ks0 + 16 + 8 * hl) / b;
+        const int16_t* ur = reinterpret_cast<const int16_t*>(s_idx[wave][ql]);
+        int64_t uu[2] = {u_lo, u_hi};
+        float bb[2];
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          const int64_t u = uu[part];
+          float bv = -INFINITY;
+          if (local == 0 && u == c_cur) {
+            bv = 0.f;   // causal mask applied per key below
+          } else {
+            while (cur < K && ur[cur] < u) ++cur;        // unused slots hold -1
+            if (cur < K && ur[cur] == u) bv = s_lg[wave][ql][cur] * kLog2e;
+          }
+          bb[part] = bv;
+        }
+        bias_lo = bb[0];
+        bias_hi = bb[1];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t key = ks0 + tile_key(r, hl);
+          float bz2 = r < 8 ? bias_lo : bias_hi;
+          if (local == 0 && key / b == c_cur && key > pos) bz2 = -INFINITY;
+          z[r] = row_ok ? fmaf(st[r], scale2, bz2) : -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t key = ks0 + tile_key(r, hl);
+          const bool in = key <= pos && key > pos - window;
+          z[r] = (row_ok && in) ? st[r] * scale2 : -INFINITY;
+        }
+      }
+      // online softmax for this lane's row (two half-waves hold its 32 keys)
+      float mt = z[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, z[r]);
+      mt = fmaxf(mt, xor_lanes_f<32>(mt));
+      const float mnew = fmaxf(m2, mt);
+      const float corr = mnew == -INFINITY ? 1.f : exp2f(m2 - mnew);
+      float p[16], ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = mnew == -INFINITY ? 0.f : exp2f(z[r] - mnew);
+        ps += p[r];
+      }
+      ps += xor_lanes_f<32>(ps);
+      lsum = lsum * corr + ps;
+      m2 = mnew;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= corr;
+      // O^T += V^T P^T: B = P^T (keys 16s + 8hl + t of this lane's row)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8_t pb;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) pb[t] = static_cast<__bf16>(p[8 * s2 + t]);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const uint4 a = *reinterpret_cast<const uint4*>(
+              &sm.vt[buf][(32 * db + ql) * TileSmem<D>::kVPitch + 16 * s2 + 8 * hl]);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb, acc[db], 0, 0, 0);
+        }
+      }
+      // next tile into the other buffer (last read two iterations ago)
+      if (it + 1 < ntl) stage(buf ^ 1);
+      __syncthreads();
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    if (branch == 0) lse_L = lsum > 0.f ? (m2 + __log2f(lsum)) / kLog2e : -INFINITY;
+    if constexpr (kMix) {
+      if (branch == 0) {
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) out[db * 16 + r] = acc[db][r] * inv;
+      } else {
+        const float a = alpha[h];
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] = a * out[db * 16 + r] + (1.f - a) * (acc[db][r] * inv);
+      }
+    } else {
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= inv;
+    }
+    if (branch + 1 == (mix ? 2 : 1) && row_ok) {
+      // O^T register r of block db holds d = 32 db + 8 (r / 4) + 4 hl + (r % 4)
+      __bf16* orow = o + ((static_cast<int64_t>(bi) * Hq + h) * nq + row) * D;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 w4;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) w4[c] = static_cast<__bf16>(acc[db][4 * a4 + c]);
+          *reinterpret_cast<decltype(w4)*>(orow + 32 * db + 8 * a4 + 4 * hl) = w4;
+        }
+    }
+  }
+  if (!row_ok) return;
+  if (lse != nullptr && hl == 0) lse[(static_cast<int64_t>(bi) * Hq + h) * nq + row] = lse_L;
+}
+
+bool attn_tile_fwd_supported(const AttnLaunch& p) {
+  return p.dtype == 1 && p.nq > 1 && p.K <= kMaxSelK && p.b >= 16 &&
+         (p.L + kKT - 1) / kKT <= kMaxKeyTiles && (p.d == 64 || p.d == 128);
+}
+
+hipError_t launch_attn_tile_fwd(const AttnLaunch& p, hipStream_t st) {
+  const int G = p.Hq / p.Hkv;
+  const int NH = G < 4 ? G : 4;
+  const int NT = 4 / NH;
+  const int ntiles = (p.nq + 31) / 32;
+  dim3 grid((ntiles + NT - 1) / NT, static_cast<unsigned>(p.B * p.Hkv * (G / NH)));
+  const bool mix = p.window > 0 && p.alpha != nullptr;
+  auto kern = p.d == 64 ? (mix ? attn_tile_fwd_kernel<64, true> : attn_tile_fwd_kernel<64, false>)
+                        : (mix ? attn_tile_fwd_kernel<128, true> : attn_tile_fwd_kernel<128, false>);
+  return launch(true, kern, grid, dim3(256), st, static_cast<const __bf16*>(p.q),
+                static_cast<const __bf16*>(p.k), static_cast<const __bf16*>(p.v), p.idx, p.logg, p.alpha,
+                p.Hq, p.Hkv, p.Hsel, p.share_group, p.nq, p.q_pos0, p.L, p.b, p.prefix_mode, p.qblock,
+                p.K, p.local, p.window, static_cast<__bf16*>(p.o), p.lse, NH, NT);
+}
+
+}  // namespace spa

@@ -12,9 +12,9 @@
 //    blocks of each selection head are split into chunks of 256; one
 //    workgroup per chunk streams the bf16 summaries (16-byte loads, several
 //    lanes per block) and keeps the chunk's (max, sum exp) and its top-K.  A
-//    second small kernel (one wave per head) selects the top-K among the
-//    chunk winners, finishes the LSE and writes the ascending indices and log
-//    gates.  Both selections are threshold searches over ballot counts with
+//    second small kernel (one workgroup per head) selects the top-K among the
+//    chunk winners in two levels (4 waves, then one), finishes the LSE and
+//    writes the ascending indices and log gates.  Both selections are threshold searches over ballot counts with
 //    an ordered compaction (no sorting network).  The kernel boundary
 //    publishes the chunk results; an in-kernel hand-off would need an
 //    agent-scope release per workgroup, which on gfx950 writes back the L2.
@@ -69,10 +69,11 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(
   constexpr int kLPB = D / kVec;           // lanes per block row
   constexpr int kBPR = kWave / kLPB;       // blocks per load round of a wave
   constexpr int kRounds = kWave / kBPR;    // rounds to cover the wave's 64 blocks
-  constexpr int kWVec = D * D / 4 / 256;   // 16-byte pieces of W per thread
-  __shared__ __align__(16) float s_w[D * D];
+  constexpr int kQuads = D / 4;             // float4 column groups of W
+  constexpr int kEGroups = 256 / kQuads;    // row groups (one per thread slice)
+  constexpr int kEPG = D / kEGroups;        // rows of W per thread
   __shared__ float s_q[D];
-  __shared__ float s_u2[2][D];
+  __shared__ float s_u[kEGroups][D];
   __shared__ float s_score[kDecodeChunk];
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -83,52 +84,73 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(
   const int kvh = share_group ? hs : hs / G;
   const bool proj = proj_w != nullptr;
 
-  // 1. issue the chunk's summary loads
+  // All loads are unconditional (clamped addresses) and issued in the order
+  // they are consumed: query heads, projection rows, then summaries.
+  // 1. query heads (q_hat = their mean when the selection is shared)
+  constexpr int kGMax = 8;
+  const int gq = share_group ? G : 1;
+  const int hq0 = share_group ? hs * G : hs;
+  const int eq = tid % D;
+  float qv[kGMax];
+#pragma unroll
+  for (int g = 0; g < kGMax; ++g) {
+    const int h = hq0 + (g < gq ? g : gq - 1);
+    qv[g] = ld_f(q + (static_cast<int64_t>(bi) * Hq + h) * D + eq);
+  }
+  // 2. this thread's slice of W: rows eg*kEPG .. +kEPG, columns 4j .. 4j+3
+  const int jq = tid % kQuads, eg = tid / kQuads;
+  float4 wq[kEPG];
+  if (proj) {
+#pragma unroll
+    for (int i = 0; i < kEPG; ++i)
+      wq[i] = reinterpret_cast<const float4*>(proj_w + static_cast<int64_t>(eg * kEPG + i) * D)[jq];
+  }
+  // 3. the chunk's summaries (rows beyond the candidates are zeroed later)
   const int cg = lane % kLPB, bl = lane / kLPB;
   const int64_t cbase = static_cast<int64_t>(chunk) * kDecodeChunk;
   const int64_t wbase = cbase + wave * kWave;
   const T* kb = kbar + (static_cast<int64_t>(bi) * Hkv + kvh) * ccap * D;
+  const int64_t clast = ncand > 0 ? ncand - 1 : 0;
   uint4 raw[kRounds];
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const int64_t c = wbase + r * kBPR + bl;
-    raw[r] = c < ncand ? *reinterpret_cast<const uint4*>(kb + c * D + cg * kVec) : make_uint4(0, 0, 0, 0);
+    raw[r] = *reinterpret_cast<const uint4*>(kb + (c < clast ? c : clast) * D + cg * kVec);
   }
-  // 2. issue the query and projection loads
-  float qsum = 0.f;
+  // 4. q_hat, then u = W^T q_hat from the row slices, summed over slices
   if (tid < D) {
-    if (share_group) {
-      for (int g = 0; g < G; ++g) qsum += ld_f(q + (static_cast<int64_t>(bi) * Hq + hs * G + g) * D + tid);
-    } else {
-      qsum = ld_f(q + (static_cast<int64_t>(bi) * Hq + hs) * D + tid);
-    }
+    float qsum = 0.f;
+#pragma unroll
+    for (int g = 0; g < kGMax; ++g)
+      if (g < gq) qsum += qv[g];
+    s_q[tid] = qsum / static_cast<float>(gq);
   }
+  lds_barrier();
   if (proj) {
-    uint4 wv[kWVec];
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int i = 0; i < kWVec; ++i) wv[i] = reinterpret_cast<const uint4*>(proj_w)[tid + i * 256];
-#pragma unroll
-    for (int i = 0; i < kWVec; ++i) reinterpret_cast<uint4*>(s_w)[tid + i * 256] = wv[i];
-  }
-  if (tid < D) s_q[tid] = share_group ? qsum / static_cast<float>(G) : qsum;
-  __syncthreads();
-  // 3. u = W^T q_hat (two half sums per output), or u = q_hat
-  {
-    const int f = tid % D, half = tid / D;
-    if (proj && half < 2) {
-      float a = 0.f;
-      const int e0 = half * (D / 2);
-#pragma unroll 16
-      for (int e = e0; e < e0 + D / 2; ++e) a = fmaf(s_w[e * D + f], s_q[e], a);
-      s_u2[half][f] = a;
+    for (int i = 0; i < kEPG; ++i) {
+      const float qe = s_q[eg * kEPG + i];
+      a.x = fmaf(wq[i].x, qe, a.x);
+      a.y = fmaf(wq[i].y, qe, a.y);
+      a.z = fmaf(wq[i].z, qe, a.z);
+      a.w = fmaf(wq[i].w, qe, a.w);
     }
+    reinterpret_cast<float4*>(s_u[eg])[jq] = a;
   }
-  __syncthreads();
+  lds_barrier();
   float uc[kVec];
 #pragma unroll
   for (int i = 0; i < kVec; ++i) {
     const int e = cg * kVec + i;
-    uc[i] = proj ? s_u2[0][e] + s_u2[1][e] : s_q[e];
+    float u = 0.f;
+    if (proj) {
+#pragma unroll
+      for (int g = 0; g < kEGroups; ++g) u += s_u[g][e];
+    } else {
+      u = s_q[e];
+    }
+    uc[i] = u;
   }
 
   // 4. scores of the chunk's blocks
@@ -178,28 +200,34 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(
   if (lane == 0) ws_ml[static_cast<int64_t>(bh) * nchunks + chunk] = make_float2(m, l);
 }
 
-// One wave per selection head: the k-th largest score among all chunk
-// winners (laid out chunk by chunk, each in index order, so position order is
-// index order), the LSE from the chunk partials, then the ascending indices
-// and log gates.  NV = candidate records per lane.
-template <int NV>
-__global__ __launch_bounds__(64) void decode_merge_kernel(
+// One workgroup (4 waves) per selection head.  The chunk winners are laid
+// out chunk by chunk, each in index order, so position order is index
+// order.  Wave w keeps the top-min(K, n) of its quarter of the chunks
+// (threshold search + ordered compaction), then wave 0 does the same over the
+// 4 x K survivors and writes the ascending indices and log gates; the LSE
+// comes from the chunk partials.  NV = records per lane in a quarter.
+template <int NV, int NV2>
+__global__ __launch_bounds__(256) void decode_merge_kernel(
     const uint64_t* __restrict__ ws_keys, const float2* __restrict__ ws_ml, int nchunks, int K,
     int64_t ncand, int gate, int32_t* __restrict__ idx, float* __restrict__ logg,
     int32_t* __restrict__ k_eff) {
-  const int lane = threadIdx.x;
+  __shared__ uint64_t s_win[4 * 64];
+  __shared__ float2 s_ml[4];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int bh = blockIdx.x;
-  const int total = nchunks * K;
-  const uint64_t* rec = ws_keys + static_cast<int64_t>(bh) * total;
+  const uint64_t* rec = ws_keys + static_cast<int64_t>(bh) * nchunks * K;
+  // this wave's quarter of the chunks
+  const int c0 = (nchunks * wave) / 4, c1 = (nchunks * (wave + 1)) / 4;
+  const int n = (c1 - c0) * K;
   uint64_t r[NV];
   uint32_t key[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int pidx = i * kWave + lane;
-    r[i] = pidx < total ? rec[pidx] : 0ull;
+    r[i] = pidx < n ? rec[static_cast<int64_t>(c0) * K + pidx] : 0ull;
   }
   float m = -INFINITY, l = 0.f;
-  for (int ch = lane; ch < nchunks; ch += kWave) {
+  for (int ch = tid; ch < nchunks; ch += 256) {
     const float2 v = ws_ml[static_cast<int64_t>(bh) * nchunks + ch];
     ml_combine(m, l, v.x, v.y);
   }
@@ -211,18 +239,48 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     m2 = xor_lanes_f<2>(m); l2 = xor_lanes_f<2>(l); ml_combine(m, l, m2, l2);
     m2 = xor_lanes_f<1>(m); l2 = xor_lanes_f<1>(l); ml_combine(m, l, m2, l2);
   }
-  const float lse = m + __logf(l);
+  if (lane == 0) s_ml[wave] = make_float2(m, l);
+  // level 1: this wave's top-min(K, valid) in index order
+  int nvalid = 0;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) key[i] = static_cast<uint32_t>(r[i] >> 32);
+  for (int i = 0; i < NV; ++i) {
+    key[i] = static_cast<uint32_t>(r[i] >> 32);
+    nvalid += __popcll(__ballot(key[i] != 0u));
+  }
+  const int k1 = nvalid < K ? nvalid : K;
+  const uint32_t t1 = wave_kth_largest<NV>(key, k1);
+  int ngt1 = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) ngt1 += __popcll(__ballot(key[i] > t1));
+  const int kept1 = wave_select_ordered<NV>(key, t1, k1 - ngt1, [&](int slot, int i) {
+    s_win[wave * K + slot] = r[i];
+  });
+  for (int x = kept1 + lane; x < K; x += kWave) s_win[wave * K + x] = 0ull;
+  __syncthreads();
+  if (wave != 0) return;
+
+  // level 2: over the 4 x K survivors (positions in index order)
+  float mm = s_ml[0].x, ll = s_ml[0].y;
+  for (int w = 1; w < 4; ++w) ml_combine(mm, ll, s_ml[w].x, s_ml[w].y);
+  const float lse = mm + __logf(ll);
+  constexpr int kNV2 = NV2;                // 4 x K survivors: NV2 * 64 >= 4K
+  uint64_t r2[kNV2];
+  uint32_t key2[kNV2];
+#pragma unroll
+  for (int i = 0; i < kNV2; ++i) {
+    const int pidx = i * kWave + lane;
+    r2[i] = pidx < 4 * K ? s_win[pidx] : 0ull;
+    key2[i] = static_cast<uint32_t>(r2[i] >> 32);
+  }
   const int kk = static_cast<int>(ncand < K ? ncand : K);
-  const uint32_t t = wave_kth_largest<NV>(key, kk);
+  const uint32_t t = wave_kth_largest<kNV2>(key2, kk);
   int ngt = 0;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) ngt += __popcll(__ballot(key[i] > t));
+  for (int i = 0; i < kNV2; ++i) ngt += __popcll(__ballot(key2[i] > t));
   const int64_t o = static_cast<int64_t>(bh) * K;          // one query row
-  const int kept = wave_select_ordered<NV>(key, t, kk - ngt, [&](int slot, int i) {
-    idx[o + slot] = static_cast<int32_t>(static_cast<uint32_t>(r[i]));
-    if (logg != nullptr) logg[o + slot] = gate ? from_orderable_f32(key[i]) - lse : 0.f;
+  const int kept = wave_select_ordered<kNV2>(key2, t, kk - ngt, [&](int slot, int i) {
+    idx[o + slot] = static_cast<int32_t>(static_cast<uint32_t>(r2[i]));
+    if (logg != nullptr) logg[o + slot] = gate ? from_orderable_f32(key2[i]) - lse : 0.f;
   });
   for (int x = kept + lane; x < K; x += kWave) {
     idx[o + x] = -1;
@@ -390,14 +448,15 @@ __global__ __launch_bounds__(256) void rows_select_kernel(
 }
 
 // ------------------------------------------------------------------ launch
-// Records per lane the merge kernel may hold (up to 64 x 64 chunk winners).
+// Records per lane each merge wave may hold (a quarter of the chunk winners;
+// up to 4 x 64 x 64 records per head).
 constexpr int kMergeMaxNV = 64;
 
 static int merge_nv(const SelectLaunch& p) {
   const int64_t nch = decode_num_chunks(p.max_cand > 0 ? p.max_cand : 1);
-  const int64_t total = nch * p.K;
+  const int64_t quarter = ((nch + 3) / 4) * p.K;
   int nv = 1;
-  while (static_cast<int64_t>(nv) * kWave < total) nv *= 2;
+  while (static_cast<int64_t>(nv) * kWave < quarter) nv *= 2;
   return nv;
 }
 
@@ -425,16 +484,19 @@ static hipError_t launch_decode_t(const SelectLaunch& p, void* ws, hipStream_t s
                         p.Hkv, p.Hsel, p.share_group, p.ccap, ncand, p.K, keys, ml, nch);
   if (e != hipSuccess) return e;
   void (*merge)(const uint64_t*, const float2*, int, int, int64_t, int, int32_t*, float*, int32_t*);
+  const bool small_k = p.K <= 32;
+#define SPA_MERGE(NVV) (small_k ? decode_merge_kernel<NVV, 2> : decode_merge_kernel<NVV, 4>)
   switch (merge_nv(p)) {
-    case 1: merge = decode_merge_kernel<1>; break;
-    case 2: merge = decode_merge_kernel<2>; break;
-    case 4: merge = decode_merge_kernel<4>; break;
-    case 8: merge = decode_merge_kernel<8>; break;
-    case 16: merge = decode_merge_kernel<16>; break;
-    case 32: merge = decode_merge_kernel<32>; break;
-    default: merge = decode_merge_kernel<64>; break;
+    case 1: merge = SPA_MERGE(1); break;
+    case 2: merge = SPA_MERGE(2); break;
+    case 4: merge = SPA_MERGE(4); break;
+    case 8: merge = SPA_MERGE(8); break;
+    case 16: merge = SPA_MERGE(16); break;
+    case 32: merge = SPA_MERGE(32); break;
+    default: merge = SPA_MERGE(64); break;
   }
-  return launch(true, merge, dim3(static_cast<unsigned>(heads)), dim3(kWave), st, keys, ml, nch, p.K, ncand,
+#undef SPA_MERGE
+  return launch(true, merge, dim3(static_cast<unsigned>(heads)), dim3(256), st, keys, ml, nch, p.K, ncand,
                 p.gate, p.idx, p.logg, p.k_eff);
 }
 

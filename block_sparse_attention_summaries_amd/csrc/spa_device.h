@@ -226,6 +226,14 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Workgroup barrier that orders LDS only: outstanding global loads stay in
+// flight across it (a plain __syncthreads also waits for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Number of set bits of a wave-uniform mask held by lanes below this one.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
