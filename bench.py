@@ -358,9 +358,67 @@ def hbm_traffic(kernel, algorithmic):
         return None
     if c.get("source_sha") != source_hash() or kernel not in c.get("kernels", {}):
         return None
-    k = c["kernels"][kernel]
-    scale = c.get("copy_scale", 1.0)
-    return (k["fetch_kib"] + k["write_kib"]) * 1024 * scale
+    return c["kernels"][kernel]["traffic_bytes"]
+
+
+COPY_BYTES = 256 << 20
+
+
+def calibrate_copy():
+    """One plain device-to-device copy of COPY_BYTES, for scaling the HBM
+    byte counters of a rocprofv3 --pmc run."""
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _read_pmc_csv(path, counter):
+    """Mean counter value (KiB) per dispatch, keyed by kernel name, from a
+    rocprofv3 counter_collection.csv."""
+    import csv
+    vals = {}
+    with open(path) as fh:
+        for row in csv.DictReader(fh):
+            name = row.get("Kernel_Name") or row.get("Kernel-Name") or ""
+            cname = row.get("Counter_Name") or row.get("Counter-Name") or ""
+            if cname != counter:
+                continue
+            v = float(row.get("Counter_Value") or row.get("Counter-Value") or 0.0)
+            vals.setdefault(name, []).append(v)
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def write_counters(fetch_csv, write_csv):
+    """profiles/decode_512k_hbm_counters.json from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE) of `bench.py --calibrate-copy ...`."""
+    fetch = _read_pmc_csv(fetch_csv, "FETCH_SIZE")
+    write = _read_pmc_csv(write_csv, "WRITE_SIZE")
+
+    def pick(table, key):
+        hits = [v for k, v in table.items() if key in k]
+        return hits[0] if hits else None
+
+    copy_key = "copyBuffer"          # the runtime's device-to-device copy kernel
+    cf = [v for k, v in fetch.items() if copy_key in k]
+    cw = [v for k, v in write.items() if copy_key in k]
+    if not cf or not cw:
+        raise SystemExit("no copy kernel found in the counter files")
+    kib = COPY_BYTES / 1024.0
+    out = {"source_sha": source_hash(), "copy_bytes": COPY_BYTES,
+           "copy_fetch_kib": max(cf), "copy_write_kib": max(cw),
+           "fetch_scale": kib / max(cf), "write_scale": kib / max(cw), "kernels": {}}
+    out["copy_scale"] = 1.0
+    for kname in ("decode_chunk_kernel", "decode_merge_kernel", "decode_attn_partial_kernel",
+                  "decode_combine_kernel"):
+        f, w = pick(fetch, kname), pick(write, kname)
+        if f is not None and w is not None:
+            out["kernels"][kname] = {"fetch_kib": f, "write_kib": w,
+                                     "traffic_bytes": f * 1024 * out["fetch_scale"] + w * 1024 * out["write_scale"]}
+    with open(COUNTERS_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def main():
@@ -373,7 +431,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 256 MiB device copy (for scaling rocprofv3 byte counters)")
+    ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM counters file from two rocprofv3 --pmc CSVs and exit")
     args = ap.parse_args()
+    if args.write_counters:
+        write_counters(*args.write_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         sys.exit("bench.py measures one GPU only: the method has no cross-GPU exchange on this path "
                  "(see the sharding note in the design document); run with --gpus 1")
@@ -381,6 +446,8 @@ def main():
     ops.lib()
 
     res = run_decode(args)
+    if args.calibrate_copy:
+        calibrate_copy()
     wl, steps = res["wl"], args.steps
     us_per_step = res["total_ms"] * 1e3 / steps
     att_bytes, sel_bytes = wl.selected_kv_bytes(), wl.scoring_bytes()
