@@ -24,12 +24,6 @@
 
 namespace spa {
 
-// LDS ordering among the lanes of one wave (no workgroup barrier).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // ======================================================== decode: split-K
 constexpr int kTileTok = 64;

@@ -290,11 +290,6 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 }
 
 // -------------------------------------------------------------------- rows
-template <typename S>
-__device__ __forceinline__ bool better(S s1, int i1, S s2, int i2) {
-  return s1 > s2 || (s1 == s2 && i1 < i2);
-}
-
 template <typename T, int D, int KMAX, bool kErf>
 __global__ __launch_bounds__(256) void rows_select_kernel(
     const T* __restrict__ q, const T* __restrict__ kbar, const float* __restrict__ max_norm,
@@ -404,17 +399,7 @@ __global__ __launch_bounds__(256) void rows_select_kernel(
         }
       }
       const int ci = static_cast<int>(c);
-      if (better(sc, ci, ts[KMAX - 1], ti[KMAX - 1])) {
-        ts[KMAX - 1] = sc;
-        ti[KMAX - 1] = ci;
-#pragma unroll
-        for (int t = KMAX - 1; t > 0; --t) {
-          if (better(ts[t], ti[t], ts[t - 1], ti[t - 1])) {
-            S xs = ts[t]; ts[t] = ts[t - 1]; ts[t - 1] = xs;
-            int xi = ti[t]; ti[t] = ti[t - 1]; ti[t - 1] = xi;
-          }
-        }
-      }
+      if (sel_better(sc, ci, ts[KMAX - 1], ti[KMAX - 1])) topk_push(ts, ti, sc, ci);
     }
   }
   if (!active) return;
@@ -424,16 +409,7 @@ __global__ __launch_bounds__(256) void rows_select_kernel(
 #pragma unroll
   for (int t = 0; t < KMAX; ++t)
     if (t >= keff) ti[t] = 0x7FFFFFFF;
-#pragma unroll
-  for (int a = 0; a < KMAX; ++a) {
-#pragma unroll
-    for (int t = KMAX - 1; t > a; --t) {
-      if (ti[t] < ti[t - 1]) {
-        S xs = ts[t]; ts[t] = ts[t - 1]; ts[t - 1] = xs;
-        int xi = ti[t]; ti[t] = ti[t - 1]; ti[t - 1] = xi;
-      }
-    }
-  }
+  sort_by_index(ts, ti);
   const float lse = m_run + __logf(l_run);
   const int64_t o = ((static_cast<int64_t>(bi) * Hsel + hs) * nq + row) * K;
 #pragma unroll
@@ -525,6 +501,7 @@ hipError_t launch_score_select(const SelectLaunch& p, void* ws, hipStream_t st) 
     if (p.dtype == 1) return p.d == 64 ? launch_decode_t<bf16_t, 64>(p, ws, st) : launch_decode_t<bf16_t, 128>(p, ws, st);
     return p.d == 64 ? launch_decode_t<float, 64>(p, ws, st) : launch_decode_t<float, 128>(p, ws, st);
   }
+  if (rows_select_mfma_supported(p)) return launch_rows_select_mfma(p, st);
   if (p.dtype == 1) return p.d == 64 ? launch_rows_t<bf16_t, 64>(p, st) : launch_rows_t<bf16_t, 128>(p, st);
   return p.d == 64 ? launch_rows_t<float, 64>(p, st) : launch_rows_t<float, 128>(p, st);
 }

@@ -234,6 +234,13 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// LDS ordering among the lanes of one wave (no workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Number of set bits of a wave-uniform mask held by lanes below this one.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
@@ -267,6 +274,86 @@ __device__ __forceinline__ void ml_combine(float& m, float& l, float m2, float l
   }
   l = l * __expf(m - mm) + l2 * __expf(m2 - mm);
   m = mm;
+}
+
+// ------------------------------------------------------ per-lane top-K lists
+// (score, index) pairs; better = higher score, then lower index.
+template <typename S>
+__device__ __forceinline__ bool sel_better(S s1, int i1, S s2, int i2) {
+  return s1 > s2 || (s1 == s2 && i1 < i2);
+}
+
+// Insert (s, c) into a list sorted best-first (caller checked it qualifies).
+// Branch-free: with w[t] = "(s, c) beats entry t" (false up to the insertion
+// point, true after it), slot t keeps its entry, takes (s, c), or takes entry
+// t - 1; every slot is decided independently of the others.
+template <typename S, int KMAX>
+__device__ __forceinline__ void topk_push(S (&ts)[KMAX], int (&ti)[KMAX], S s, int c) {
+  bool w[KMAX];
+#pragma unroll
+  for (int t = 0; t < KMAX; ++t) w[t] = sel_better(s, c, ts[t], ti[t]);
+#pragma unroll
+  for (int t = KMAX - 1; t > 0; --t) {
+    const S up_s = w[t - 1] ? ts[t - 1] : s;
+    const int up_i = w[t - 1] ? ti[t - 1] : c;
+    ts[t] = w[t] ? up_s : ts[t];
+    ti[t] = w[t] ? up_i : ti[t];
+  }
+  ts[0] = w[0] ? s : ts[0];
+  ti[0] = w[0] ? c : ti[0];
+}
+
+// The same for a candidate that arrives after every held entry in index
+// order, so a tie keeps the held entry (plain score comparisons).
+template <typename S, int KMAX>
+__device__ __forceinline__ void topk_push_later(S (&ts)[KMAX], int (&ti)[KMAX], S s, int c) {
+  bool w[KMAX];
+#pragma unroll
+  for (int t = 0; t < KMAX; ++t) w[t] = s > ts[t];
+#pragma unroll
+  for (int t = KMAX - 1; t > 0; --t) {
+    const S up_s = w[t - 1] ? ts[t - 1] : s;
+    const int up_i = w[t - 1] ? ti[t - 1] : c;
+    ts[t] = w[t] ? up_s : ts[t];
+    ti[t] = w[t] ? up_i : ti[t];
+  }
+  ts[0] = w[0] ? s : ts[0];
+  ti[0] = w[0] ? c : ti[0];
+}
+
+// Sort a bitonic list best-first (Batcher's half-cleaner cascade).
+template <typename S, int N>
+__device__ __forceinline__ void bitonic_clean_best_first(S (&ts)[N], int (&ti)[N]) {
+#pragma unroll
+  for (int j = N / 2; j > 0; j >>= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if ((i & j) == 0 && sel_better(ts[i + j], ti[i + j], ts[i], ti[i])) {
+        const S xs = ts[i]; ts[i] = ts[i + j]; ts[i + j] = xs;
+        const int xi = ti[i]; ti[i] = ti[i + j]; ti[i + j] = xi;
+      }
+    }
+  }
+}
+
+// Sort by ascending index (Batcher's bitonic sorting network; indices distinct
+// apart from the 0x7FFFFFFF fill).
+template <typename S, int N>
+__device__ __forceinline__ void sort_by_index(S (&ts)[N], int (&ti)[N]) {
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int l = i ^ j;
+        if (l > i && ((ti[i] > ti[l]) == ((i & k) == 0))) {
+          const S xs = ts[i]; ts[i] = ts[l]; ts[l] = xs;
+          const int xi = ti[i]; ti[i] = ti[l]; ti[l] = xi;
+        }
+      }
+    }
+  }
 }
 
 }  // namespace spa

@@ -119,6 +119,8 @@ size_t attn_bwd_workspace_bytes(const BwdLaunch& p);
 
 hipError_t launch_block_summaries(const SummaryLaunch& p, hipStream_t st);
 hipError_t launch_score_select(const SelectLaunch& p, void* ws, hipStream_t st);
+bool rows_select_mfma_supported(const SelectLaunch& p);
+hipError_t launch_rows_select_mfma(const SelectLaunch& p, hipStream_t st);
 hipError_t launch_attn_fwd(const AttnLaunch& p, void* ws, hipStream_t st);
 bool attn_tile_fwd_supported(const AttnLaunch& p);
 hipError_t launch_attn_tile_fwd(const AttnLaunch& p, hipStream_t st);

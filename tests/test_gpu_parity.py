@@ -398,3 +398,71 @@ def test_one_workspace_shared_across_shapes_and_entry_points():
         torch.cuda.synchronize()
         check_indices(host(idx), ora)
         assert rel_err(host(o), o_o) <= _tol(cfg), (name, over)
+
+
+# ------------------------------------------------------------------ selection alone (row kernels)
+def _select_only(cfg, x, *, gate, share_group, erf=True, prefix_mode=1, rows=None):
+    b, qb, K = cfg["b"], cfg.get("qblock", 128), cfg["K"]
+    Hsel = cfg["Hkv"] if share_group else cfg["Hq"]
+    kw = dict(Hkv=cfg["Hkv"], b=b, K=K, q_pos0=0, gate=gate, prefix_mode=prefix_mode, qblock=qb,
+              share_group=share_group)
+    ekw = {}
+    if erf:
+        lam = np.ascontiguousarray(x["erf_lambda"][:Hsel])
+        sig = np.ascontiguousarray(x["erf_sigma"][:Hsel])
+        ekw = dict(erf_lambda=lam, erf_sigma=sig)
+    kb_o, mx_o, ce_o = oracle.block_summaries(x["k"], b, nblocks=x["L"] // b)
+    ora = oracle.score_select(x["q"], kb_o, mx_o, ce_o, rows=rows, **kw, **ekw)
+    kb_g, mx_g, ce_g = ops.sparse_block_summaries(dev(x["k"]), b)
+    idx_g, logg_g, keff_g = ops.sparse_score_select(dev(x["q"]), kb_g, mx_g, ce_g, **kw,
+                                                    **{k: dev(v) for k, v in ekw.items()})
+    torch.cuda.synchronize()
+    idx, keff = host(idx_g), host(keff_g)
+    sel = slice(None) if rows is None else rows
+    sub = {k: v[:, :, sel] for k, v in ora.items() if k in ("idx", "gap", "k_eff", "logg")}
+    n_ex = check_indices(idx[:, :, sel], sub)
+    assert np.array_equal(keff[:, :, sel], sub["k_eff"])
+    if gate:
+        lg = host(logg_g)[:, :, sel].astype(np.float64)
+        m = np.all(idx[:, :, sel] == sub["idx"], axis=-1)
+        d = np.abs(lg - sub["logg"])[m]
+        assert d.max(initial=0.0) <= 1e-4 * max(1.0, np.abs(sub["logg"]).max())
+    return n_ex
+
+
+@pytest.mark.parametrize("over", [
+    dict(n=1536, Hq=4, Hkv=2, seed=51),                        # group mean (3 bf16 terms), K=4
+    dict(n=1200, Hq=8, Hkv=2, d=128, K=8, seed=52),            # G=4, d=128, K=8 (list of 16)
+    dict(n=700, Hq=2, Hkv=2, K=6, b=16, qblock=64, seed=53),   # ragged, small cells
+])
+def test_select_erf_group_gate_parity(over):
+    """erf position bias with a group-shared selection and the softmax log
+    gate: the exact fp64 re-ranking of the fp32 list."""
+    cfg = config("prefill_cells", **over)
+    _say(f"[select erf group gate] {over}")
+    x = make_inputs(cfg)
+    _say(f"  exempt rows {_select_only(cfg, x, gate=True, share_group=True)}")
+
+
+def test_select_erf_identical_keys():
+    """Every key equal: all cells tie in fp32 far from the query, so the fp32
+    list cannot separate the budget from the rest and rows are re-scored
+    exactly in full; ties go to the lower index."""
+    cfg = config("prefill_cells", n=2048, Hq=2, Hkv=2, seed=54)
+    x = make_inputs(cfg)
+    x["k"] = np.ascontiguousarray(np.broadcast_to(x["k"][:, :, :1, :], x["k"].shape))
+    _say(f"  exempt rows {_select_only(cfg, x, gate=False, share_group=False)}")
+
+
+@pytest.mark.parametrize("over,share_group,gate", [
+    (dict(n=1024, Hq=4, Hkv=2, K=16, seed=55), False, True),   # one head per selection, gate on
+    (dict(n=900, Hq=8, Hkv=2, K=32, b=16, seed=56), True, False),  # K=32, ragged
+    (dict(n=512, Hq=2, Hkv=1, K=3, b=32, d=64, seed=57), True, True),
+])
+def test_select_rows_no_erf_parity(over, share_group, gate):
+    """Causal block selection for many rows (training / prefill): MFMA scores,
+    per-lane lists merged across half-waves."""
+    cfg = config("train", **over)
+    _say(f"[select rows] {over} share_group={share_group} gate={gate}")
+    x = make_inputs(cfg)
+    _say(f"  exempt rows {_select_only(cfg, x, gate=gate, share_group=share_group, erf=False, prefix_mode=0)}")
