@@ -18,6 +18,8 @@
 // B operand of O^T += V^T P^T for keys 16s + 8h .. +7 (h = half-wave), whose
 // A operand is then one 16-byte read of the transposed V tile.  Per-row
 // masks / biases come from a cursor walk over the row's ascending selection.
+#include <type_traits>
+
 #include "spa_device.h"
 #include "spa_launch.h"
 
@@ -171,129 +173,201 @@ __global__ __launch_bounds__(256) void attn_tile_fwd_kernel(
       for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
     float m2 = -INFINITY, lsum = 0.f;     // running max (log2 domain), sum
     int cur = 0;                           // cursor into this row's units
-    const int64_t c_cur = pos / b;         // current unit of the row
+    const int pos32 = static_cast<int>(pos);
+    const int c_cur = pos32 / b;           // current unit of the row
+    const int c_end = (c_cur + 1) * b;     // first key after it
 
-    // staging: 2 x 16 B of K and of V per thread per tile (D = 128), 1 (D = 64)
+    // staging: 2 x 16 B of K and of V per thread per tile (D = 128), 1 (D = 64).
+    // Loads run kP - 1 tiles ahead of the tile being computed, in a ring of kP
+    // register slots (the loop is unrolled kP times so every slot index is a
+    // constant); LDS holds two tiles (computed / being staged).
     constexpr int kLd = kKT * D / 8 / 256;
-    uint4 kld[kLd > 0 ? kLd : 1], vld[kLd > 0 ? kLd : 1];
-    auto issue = [&](int it) {
-      const int64_t ks0 = static_cast<int64_t>(list[it]) * kKT;
-#pragma unroll
-      for (int i = 0; i < kLd; ++i) {
-        const int x = tid + i * 256;
-        const int kr = x / (D / 8), cv = x % (D / 8);
-        int64_t key = ks0 + kr;
-        key = key < L ? key : L - 1;
-        kld[i] = *reinterpret_cast<const uint4*>(k + kvbase + key * D + cv * 8);
-        vld[i] = *reinterpret_cast<const uint4*>(v + kvbase + key * D + cv * 8);
-      }
-    };
-    auto stage = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < kLd; ++i) {
-        const int x = tid + i * 256;
-        const int kr = x / (D / 8), cv = x % (D / 8);
-        *reinterpret_cast<uint4*>(&sm.k[buf][kr * TileSmem<D>::kKPitch + cv * 8]) = kld[i];
-        const __bf16* vv = reinterpret_cast<const __bf16*>(&vld[i]);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) sm.vt[buf][(cv * 8 + t) * TileSmem<D>::kVPitch + kr] = vv[t];
-      }
-    };
-    if (ntl > 0) {
-      issue(0);
-      stage(0);
+    constexpr int kP = (D == 64 && !kMix) ? 4 : 2;    // 2 or 4 (register budget)
+    constexpr int kL1 = kLd > 0 ? kLd : 1;
+    uint4 kq0[kL1], vq0[kL1], kq1[kL1], vq1[kL1], kq2[kL1], vq2[kL1], kq3[kL1], vq3[kL1];
+    static_assert(kLd == 1 || kLd == 2, "one or two 16-byte vectors per thread per tile");
+    // vector i of a tile: thread tid moves key row (tid + 256 i) / (D / 8), column group tid % (D / 8)
+    // K: thread x takes key row x / (D / 8), columns 8 (x % (D / 8)) .. +7 (rows
+    // contiguous in LDS).  V: key x % 32, columns 8 (x / 32) .. +7, so that each
+    // transposed 2-byte LDS write of a wave covers 32 consecutive keys of a
+    // V^T row and the other half-wave lands 8 rows (a half bank cycle) away.
+#define SPA_ISSUE_ONE(KS, VS, IT, I)                                                         \
+  do {                                                                                       \
+    const int x = tid + (I) * 256;                                                           \
+    const int64_t kb0 = static_cast<int64_t>(list[IT]) * kKT;                                \
+    int64_t key = kb0 + x / (D / 8), vkey = kb0 + x % kKT;                                   \
+    key = key < L ? key : L - 1;                                                             \
+    vkey = vkey < L ? vkey : L - 1;                                                          \
+    KS[I] = *reinterpret_cast<const uint4*>(k + kvbase + key * D + (x % (D / 8)) * 8);       \
+    VS[I] = *reinterpret_cast<const uint4*>(v + kvbase + vkey * D + (x / kKT) * 8);          \
+  } while (0)
+#define SPA_ISSUE(KS, VS, IT)                                                                \
+  do {                                                                                       \
+    SPA_ISSUE_ONE(KS, VS, IT, 0);                                                            \
+    if constexpr (kLd == 2) SPA_ISSUE_ONE(KS, VS, IT, 1);                                    \
+  } while (0)
+#define SPA_STAGE_ONE(KS, VS, BUF, I)                                                        \
+  do {                                                                                       \
+    const int x = tid + (I) * 256;                                                           \
+    const int kr = x / (D / 8), cv = x % (D / 8);                                            \
+    *reinterpret_cast<uint4*>(&sm.k[BUF][kr * TileSmem<D>::kKPitch + cv * 8]) = KS[I];      \
+    const uint4 vw = VS[I];                                                                  \
+    uint16_t* vt = reinterpret_cast<uint16_t*>(sm.vt[BUF]) + (x / kKT) * 8 * TileSmem<D>::kVPitch + x % kKT; \
+    vt[0 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.x);                              \
+    vt[1 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.x >> 16);                        \
+    vt[2 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.y);                              \
+    vt[3 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.y >> 16);                        \
+    vt[4 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.z);                              \
+    vt[5 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.z >> 16);                        \
+    vt[6 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.w);                              \
+    vt[7 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.w >> 16);                        \
+  } while (0)
+#define SPA_STAGE(KS, VS, BUF)                                                               \
+  do {                                                                                       \
+    SPA_STAGE_ONE(KS, VS, BUF, 0);                                                           \
+    if constexpr (kLd == 2) SPA_STAGE_ONE(KS, VS, BUF, 1);                                   \
+  } while (0)
+    if (ntl > 0) SPA_ISSUE(kq0, vq0, 0);
+    if constexpr (kP == 4) {
+      if (ntl > 1) SPA_ISSUE(kq1, vq1, 1);
+      if (ntl > 2) SPA_ISSUE(kq2, vq2, 2);
     }
+    if (ntl > 0) SPA_STAGE(kq0, vq0, 0);
     __syncthreads();
-    for (int it = 0; it < ntl; ++it) {
-      const int buf = it & 1;
-      if (it + 1 < ntl) issue(it + 1);
-      const int64_t ks0 = static_cast<int64_t>(list[it]) * kKT;
+    // one tile of the ring; u (the slot of tile it) is a compile-time constant
+    int it0 = 0;
+    auto tile_step = [&](auto uc, uint4 (&ki)[kL1], uint4 (&vi)[kL1], uint4 (&kn)[kL1],
+                         uint4 (&vn)[kL1]) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;   // ki / vi: slot issued, kn / vn: slot staged
+      const int it = it0 + u;
+      if (it < ntl) {
+      const int buf = u & 1;               // it0 is a multiple of kP (even)
+      if (it + kP - 1 < ntl) SPA_ISSUE(ki, vi, it + kP - 1);
+      const int ks0 = static_cast<int>(list[it]) * kKT;   // positions fit int32 (L <= 65536)
 
-      // S^T = K Q^T for this wave's 32 rows
-      floatx16_t st;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = 0.f;
-      const __bf16* krow = &sm.k[buf][perm_row(ql) * TileSmem<D>::kKPitch];
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(krow + 16 * ks + 8 * hl);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[ks]), st, 0, 0, 0);
-      }
-      // masks and biases (log2 domain)
-      float z[16];
+      // Which of this wave's rows read the tile, with what bias (log2 domain).
+      // A tile that none of them reads is skipped (the workgroup's list is the
+      // union over all its waves).
+      float bias_lo = 0.f, bias_hi = 0.f;
+      bool need, masked = false;
       if (branch == 0) {
-        // unit of the keys this lane holds: keys < 16 and >= 16 of the tile
-        float bias_lo = -INFINITY, bias_hi = -INFINITY;
-        const int64_t u_lo = (ks0 + 8 * hl) / b, u_hi = (ks0 + 16 + 8 * hl) / b;
+        const int u_lo = (ks0 + 8 * hl) / b, u_hi = (ks0 + 16 + 8 * hl) / b;
         const int16_t* ur = reinterpret_cast<const int16_t*>(s_idx[wave][ql]);
-        int64_t uu[2] = {u_lo, u_hi};
+        const int uu[2] = {u_lo, u_hi};
         float bb[2];
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
-          const int64_t u = uu[part];
+          const int uv = uu[part];
           float bv = -INFINITY;
-          if (local == 0 && u == c_cur) {
+          if (local == 0 && uv == c_cur) {
             bv = 0.f;   // causal mask applied per key below
           } else {
-            while (cur < K && ur[cur] < u) ++cur;        // unused slots hold -1
-            if (cur < K && ur[cur] == u) bv = s_lg[wave][ql][cur] * kLog2e;
+            while (cur < K && ur[cur] < uv) ++cur;        // unused slots hold -1
+            if (cur < K && ur[cur] == uv) bv = s_lg[wave][ql][cur] * kLog2e;
           }
           bb[part] = bv;
         }
-        bias_lo = bb[0];
-        bias_hi = bb[1];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t key = ks0 + tile_key(r, hl);
-          float bz2 = r < 8 ? bias_lo : bias_hi;
-          if (local == 0 && key / b == c_cur && key > pos) bz2 = -INFINITY;
-          z[r] = row_ok ? fmaf(st[r], scale2, bz2) : -INFINITY;
-        }
+        bias_lo = row_ok ? bb[0] : -INFINITY;
+        bias_hi = row_ok ? bb[1] : -INFINITY;
+        need = bias_lo != -INFINITY || bias_hi != -INFINITY;
+        masked = local == 0 && (u_lo == c_cur || u_hi == c_cur) && ks0 + kKT - 1 > pos32;
       } else {
+        need = row_ok && ks0 <= pos32 && ks0 + kKT - 1 > pos32 - window;
+        masked = !(ks0 + kKT - 1 <= pos32 && ks0 > pos32 - window);
+        bias_lo = bias_hi = row_ok ? 0.f : -INFINITY;
+      }
+      if (__ballot(need) != 0) {
+        // S^T = K Q^T for this wave's 32 rows
+        floatx16_t st;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] = 0.f;
+        const __bf16* krow = &sm.k[buf][perm_row(ql) * TileSmem<D>::kKPitch];
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) {
+          const uint4 a = *reinterpret_cast<const uint4*>(krow + 16 * ks + 8 * hl);
+          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[ks]), st, 0, 0, 0);
+        }
+        float z[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) z[r] = fmaf(st[r], scale2, r < 8 ? bias_lo : bias_hi);
+        if (__ballot(masked) != 0) {
+          // branch L: keys of the current unit after the row; branch S: keys
+          // outside (pos - window, pos]
+          if (branch == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = ks0 + tile_key(r, hl);
+              z[r] = (key > pos32 && key < c_end) ? -INFINITY : z[r];
+            }
+          } else {
+            const int wlo = pos32 - window + 1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = ks0 + tile_key(r, hl);
+              z[r] = (key > pos32 || key < wlo) ? -INFINITY : z[r];
+            }
+          }
+        }
+        // online softmax for this lane's row (two half-waves hold its 32 keys)
+        float mt = z[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, z[r]);
+        mt = fmaxf(mt, xor_lanes_f<32>(mt));
+        const float mnew = fmaxf(m2, mt);
+        // hardware exp2 (exp2(-inf) = 0); a row with no key yet keeps zeros
+        const float msub = mnew == -INFINITY ? 0.f : mnew;
+        const float corr = __builtin_amdgcn_exp2f(m2 - msub);
+        float p[16], ps = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t key = ks0 + tile_key(r, hl);
-          const bool in = key <= pos && key > pos - window;
-          z[r] = (row_ok && in) ? st[r] * scale2 : -INFINITY;
+          p[r] = __builtin_amdgcn_exp2f(z[r] - msub);
+          ps += p[r];
+        }
+        ps += xor_lanes_f<32>(ps);
+        lsum = lsum * corr + ps;
+        m2 = mnew;
+        if (__ballot(corr != 1.f) != 0) {
+#pragma unroll
+          for (int db = 0; db < kDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[db][r] *= corr;
+        }
+        // O^T += V^T P^T: B = P^T (keys 16s + 8hl + t of this lane's row)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          bf16x8_t pb;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) pb[t] = static_cast<__bf16>(p[8 * s2 + t]);
+#pragma unroll
+          for (int db = 0; db < kDB; ++db) {
+            const uint4 a = *reinterpret_cast<const uint4*>(
+                &sm.vt[buf][(32 * db + ql) * TileSmem<D>::kVPitch + 16 * s2 + 8 * hl]);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb, acc[db], 0, 0, 0);
+          }
         }
       }
-      // online softmax for this lane's row (two half-waves hold its 32 keys)
-      float mt = z[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, z[r]);
-      mt = fmaxf(mt, xor_lanes_f<32>(mt));
-      const float mnew = fmaxf(m2, mt);
-      const float corr = mnew == -INFINITY ? 1.f : exp2f(m2 - mnew);
-      float p[16], ps = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = mnew == -INFINITY ? 0.f : exp2f(z[r] - mnew);
-        ps += p[r];
+      // next tile into the other buffer (last read two iterations ago); the
+      // barrier orders LDS only, so later tiles' loads stay in flight
+      if (it + 1 < ntl) SPA_STAGE(kn, vn, buf ^ 1);
+      lds_barrier();
       }
-      ps += xor_lanes_f<32>(ps);
-      lsum = lsum * corr + ps;
-      m2 = mnew;
-#pragma unroll
-      for (int db = 0; db < kDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= corr;
-      // O^T += V^T P^T: B = P^T (keys 16s + 8hl + t of this lane's row)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        bf16x8_t pb;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) pb[t] = static_cast<__bf16>(p[8 * s2 + t]);
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          const uint4 a = *reinterpret_cast<const uint4*>(
-              &sm.vt[buf][(32 * db + ql) * TileSmem<D>::kVPitch + 16 * s2 + 8 * hl]);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb, acc[db], 0, 0, 0);
-        }
+    };
+    for (it0 = 0; it0 < ntl; it0 += kP) {
+      if constexpr (kP == 4) {
+        // tile it0 + u lives in slot u; step u issues into slot u + 3, stages slot u + 1
+        tile_step(std::integral_constant<int, 0>{}, kq3, vq3, kq1, vq1);
+        tile_step(std::integral_constant<int, 1>{}, kq0, vq0, kq2, vq2);
+        tile_step(std::integral_constant<int, 2>{}, kq1, vq1, kq3, vq3);
+        tile_step(std::integral_constant<int, 3>{}, kq2, vq2, kq0, vq0);
+      } else {
+        tile_step(std::integral_constant<int, 0>{}, kq1, vq1, kq1, vq1);
+        tile_step(std::integral_constant<int, 1>{}, kq0, vq0, kq0, vq0);
       }
-      // next tile into the other buffer (last read two iterations ago)
-      if (it + 1 < ntl) stage(buf ^ 1);
-      __syncthreads();
     }
+#undef SPA_ISSUE
+#undef SPA_ISSUE_ONE
+#undef SPA_STAGE
+#undef SPA_STAGE_ONE
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     if (branch == 0) lse_L = lsum > 0.f ? (m2 + __log2f(lsum)) / kLog2e : -INFINITY;
     if constexpr (kMix) {
