@@ -19,6 +19,8 @@
 // query head) merges the partials.
 // Rows (prefill / training): one wave per (query head, row) streaming its key
 // segments 64 keys at a time with an online softmax.
+#include <type_traits>
+
 #include "spa_device.h"
 #include "spa_launch.h"
 
@@ -586,7 +588,8 @@ size_t attn_fwd_workspace_bytes(const AttnLaunch& p) {
 }
 
 size_t attn_bwd_workspace_bytes(const BwdLaunch& p) {
-  return align256(static_cast<size_t>(p.a.B) * p.a.Hq * p.a.nq * sizeof(float));
+  const size_t dbuf = align256(static_cast<size_t>(p.a.B) * p.a.Hq * p.a.nq * sizeof(float));
+  return attn_tile_bwd_supported(p) ? dbuf + attn_tile_bwd_bitmap_bytes(p) : dbuf;
 }
 
 template <typename T, int D, int HPW>
@@ -643,6 +646,13 @@ static hipError_t launch_bwd_t(const BwdLaunch& p, void* ws, hipStream_t st) {
   hipError_t e = launch(false, bwd_pre_kernel<T, D>, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256),
                         st, static_cast<const T*>(p.o), static_cast<const T*>(p.dout), rows, Dbuf);
   if (e != hipSuccess) return e;
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (attn_tile_bwd_supported(p)) {
+      uint32_t* bits = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) +
+                                                   align256(static_cast<size_t>(rows) * sizeof(float)));
+      return launch_attn_tile_bwd(p, Dbuf, bits, st);
+    }
+  }
   e = launch(false, bwd_dq_kernel<T, D>, dim3((a.nq + 3) / 4, static_cast<unsigned>(a.B * a.Hsel)), dim3(256),
              st, static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
              static_cast<const T*>(p.dout), p.lse, Dbuf, a.idx, a.logg, a.Hq, a.Hkv, a.Hsel, a.share_group,

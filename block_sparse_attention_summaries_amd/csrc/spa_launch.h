@@ -125,6 +125,9 @@ hipError_t launch_attn_fwd(const AttnLaunch& p, void* ws, hipStream_t st);
 bool attn_tile_fwd_supported(const AttnLaunch& p);
 hipError_t launch_attn_tile_fwd(const AttnLaunch& p, hipStream_t st);
 hipError_t launch_attn_bwd(const BwdLaunch& p, void* ws, hipStream_t st);
+bool attn_tile_bwd_supported(const BwdLaunch& p);
+size_t attn_tile_bwd_bitmap_bytes(const BwdLaunch& p);
+hipError_t launch_attn_tile_bwd(const BwdLaunch& p, const float* Dbuf, uint32_t* bits, hipStream_t st);
 hipError_t launch_zero_fill(void* ptr, size_t bytes, hipStream_t st);
 
 }  // namespace spa

@@ -116,7 +116,12 @@ def test_attn_workspace_sizes():
     assert _attn_status(a, None, 0) == ops.SPA_ERR_WORKSPACE
     pre = _attn(nq=8192, q_pos0=0, L=8192)
     assert ops.lib().sparse_workspace_bytes(ops.SPA_OP_ATTN_FWD, ctypes.byref(pre)) == 0
-    assert ops.lib().sparse_workspace_bytes(ops.SPA_OP_ATTN_BWD, ctypes.byref(pre)) == 32 * 8192 * 4
+    # backward: D_i per (head, row); the bf16 MFMA path adds one selection bit
+    # per (selection head, block, row): 8 heads x 128 blocks x 256 words
+    dbuf = 32 * 8192 * 4
+    assert ops.lib().sparse_workspace_bytes(ops.SPA_OP_ATTN_BWD, ctypes.byref(pre)) == dbuf + 8 * 128 * 256 * 4
+    pre32 = _attn(nq=8192, q_pos0=0, L=8192, dtype=0)
+    assert ops.lib().sparse_workspace_bytes(ops.SPA_OP_ATTN_BWD, ctypes.byref(pre32)) == dbuf
 
 
 def test_bwd_rejects_unsupported_modes():
