@@ -328,6 +328,9 @@ def _check_train(cfg, r, kv_slice=-1, fwd_rows=None):
     dict(B=1, n=512, Hq=8, Hkv=1, b=32, K=6, seed=32),                    # G = 8, b = 32
     dict(B=1, n=384, Hq=2, Hkv=1, d=64, dtype="f32", K=3, seed=33),      # fp32 -> 1e-4
     dict(B=1, n=256, Hq=2, Hkv=2, b=16, d=64, K=4, gate=False, seed=34),  # gate off, b = 16
+    dict(B=1, n=700, Hq=4, Hkv=2, b=32, d=64, K=8, seed=35),             # G = 2, b = 32, d = 64, ragged
+    dict(B=1, n=2100, Hq=4, Hkv=1, K=6, seed=36),                         # > 2048 rows: two bitmap passes
+    dict(B=1, n=640, Hq=2, Hkv=2, K=32, gate=False, seed=37),             # K = 32, gate off (MFMA path)
 ])
 def test_train_fwd_bwd_parity(over):
     cfg = config("train", **over)
@@ -370,6 +373,31 @@ def test_chunked_prefill_rows_after_offset():
                                      dev(ora["logg"].astype(np.float32)), b=b, K=K, q_pos0=q_pos0)
     check_indices(host(idx_g), ora)
     assert rel_err(host(o_g), o_o) <= 2e-2
+
+
+def test_backward_rows_after_offset():
+    """Backward of rows q_pos0..L-1 of a longer cache (nq < L): dk / dv collect
+    only those rows, and each block's own rows start at q_pos0."""
+    cfg = config("train", B=1, n=1024, Hq=4, Hkv=2, K=4, seed=42)
+    x = make_inputs(cfg)
+    q_pos0 = 600
+    q = np.ascontiguousarray(x["q"][:, :, q_pos0:])
+    do = np.ascontiguousarray(x["dout"][:, :, q_pos0:])
+    b, K = cfg["b"], cfg["K"]
+    kw = dict(Hkv=2, b=b, K=K, q_pos0=q_pos0, gate=True, share_group=True)
+    kb_o, mx_o, ce_o = oracle.block_summaries(x["k"], b)
+    ora = oracle.score_select(q, kb_o, mx_o, ce_o, **kw)
+    akw = dict(b=b, K=K, q_pos0=q_pos0, share_group=True)
+    dq_o, dk_o, dv_o, dg_o = oracle.attn_bwd(q, x["k"], x["v"], do, ora["idx"], ora["logg"], **akw)
+    qd, kd, vd = dev(q), dev(x["k"]), dev(x["v"])
+    idx_in, lg_in = dev(ora["idx"]), dev(ora["logg"].astype(np.float32))
+    o_g, lse_g = ops.sparse_attn_fwd(qd, kd, vd, idx_in, lg_in, **akw)
+    dq, dk, dv, dg = ops.sparse_attn_bwd(qd, kd, vd, idx_in, lg_in, o_g, dev(do), lse_g, **akw)
+    torch.cuda.synchronize()
+    for name, got, want in (("dq", dq, dq_o), ("dk", dk, dk_o), ("dv", dv, dv_o), ("dg", dg, dg_o)):
+        e = rel_err(host(got), want)
+        _say(f"  {name} {e:.2e}")
+        assert e <= 2e-2, (name, e)
 
 
 def test_one_workspace_shared_across_shapes_and_entry_points():
