@@ -56,7 +56,7 @@ struct TileSmem {
 constexpr int kMaxSelK = 32;
 
 template <int D, bool kMix>
-__global__ __launch_bounds__(256) void attn_tile_fwd_kernel(
+__global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ logg, const float* __restrict__ alpha,
     int Hq, int Hkv, int Hsel, int share_group, int nq, int64_t q_pos0, int64_t L, int b,
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void attn_tile_fwd_kernel(
     // register slots (the loop is unrolled kP times so every slot index is a
     // constant); LDS holds two tiles (computed / being staged).
     constexpr int kLd = kKT * D / 8 / 256;
-    constexpr int kP = (D == 64 && !kMix) ? 4 : 2;    // 2 or 4 (register budget)
+    constexpr int kP = D == 64 ? 4 : 2;    // 2 or 4 (register budget)
     constexpr int kL1 = kLd > 0 ? kLd : 1;
     uint4 kq0[kL1], vq0[kL1], kq1[kL1], vq1[kL1], kq2[kL1], vq2[kL1], kq3[kL1], vq3[kL1];
     static_assert(kLd == 1 || kLd == 2, "one or two 16-byte vectors per thread per tile");
