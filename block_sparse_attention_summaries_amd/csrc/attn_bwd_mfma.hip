@@ -204,7 +204,14 @@ __global__ __launch_bounds__(256) void attn_tile_dq_kernel(
   for (int db = 0; db < kDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  int cur = 0;                             // cursor into this row's units
+  int cur = 0;                             // cursor into this row's units; the unit
+  int nu;                                  // there (past the end: INT_MAX) and its
+  float nlg;                               // log2 gate are kept in registers
+  {
+    const int16_t* urow = reinterpret_cast<const int16_t*>(s_idx[wave][ql]);
+    nu = K > 0 ? urow[0] : 0x7FFFFFFF;
+    nlg = K > 0 ? s_lg[wave][ql][0] * kBLog2e : 0.f;
+  }
 
   // staging: 16-byte vectors x and x + 256 of the K and V tiles per thread
   constexpr int kLd = kBT * D / 8 / 256;
@@ -259,9 +266,13 @@ __global__ __launch_bounds__(256) void attn_tile_dq_kernel(
         if (uv == c_cur) {
           bv = 0.f;
         } else {
-          while (cur < K && ur[cur] < uv) ++cur;
-          if (cur < K && ur[cur] == uv) {
-            bv = s_lg[wave][ql][cur] * kBLog2e;
+          while (nu < uv) {   // advance past smaller units (unused slots hold -1)
+            ++cur;
+            nu = cur < K ? ur[cur] : 0x7FFFFFFF;
+            nlg = cur < K ? s_lg[wave][ql][cur] * kBLog2e : 0.f;
+          }
+          if (nu == uv) {
+            bv = nlg;
             sl = cur;
           }
         }

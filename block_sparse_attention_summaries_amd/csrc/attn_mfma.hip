@@ -55,7 +55,7 @@ struct TileSmem {
 // their log gates, read with a cursor as key tiles ascend.
 constexpr int kMaxSelK = 32;
 
-template <int D, bool kMix>
+template <int D, bool kMix, int NW>
 __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ logg, const float* __restrict__ alpha,
@@ -98,7 +98,8 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
     s_lg[wave][ql][t] = (ok && logg != nullptr) ? logg[so + t] : 0.f;
   }
   // ---- key-tile lists: list 0 = branch L, list 1 = window branch
-  for (int x = tid; x < 2 * (kMaxKeyTiles / 32); x += 256) (&s_bits[0][0])[x] = 0u;
+  constexpr int kThreads = 64 * NW;      // NW waves of 64
+  for (int x = tid; x < 2 * (kMaxKeyTiles / 32); x += kThreads) (&s_bits[0][0])[x] = 0u;
   __syncthreads();
   // row range of the workgroup (positions)
   const int64_t wg_row0 = static_cast<int64_t>(blockIdx.x) * NT * 32;
@@ -107,12 +108,12 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
   if (local == 0) {
     // current blocks of the rows: keys [floor(p0/b) b, p1]
     const int64_t k0 = (p0 / b) * b;
-    for (int64_t t = k0 / kKT + tid; t <= p1 / kKT; t += 256)
+    for (int64_t t = k0 / kKT + tid; t <= p1 / kKT; t += kThreads)
       atomicOr(&s_bits[0][t >> 5], 1u << (t & 31));
   }
   if (mix) {
     const int64_t k0 = p0 - window + 1 > 0 ? p0 - window + 1 : 0;
-    for (int64_t t = k0 / kKT + tid; t <= p1 / kKT; t += 256)
+    for (int64_t t = k0 / kKT + tid; t <= p1 / kKT; t += kThreads)
       atomicOr(&s_bits[1][t >> 5], 1u << (t & 31));
   }
   for (int t = hl; t < K; t += 2) {
@@ -124,11 +125,12 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
   }
   __syncthreads();
   // compaction into ascending lists (wave 0: list 0, wave 1: list 1)
-  if (wave < 2) {
+  // list li is built by wave li (NW >= 2), or both by wave 0 (NW == 1)
+  for (int li = wave; li < 2; li += NW) {
     int base = 0;
     for (int w0 = 0; w0 < nwords; w0 += 64) {
       const int wi = w0 + lane;
-      const uint32_t bits = wi < nwords ? s_bits[wave][wi] : 0u;
+      const uint32_t bits = wi < nwords ? s_bits[li][wi] : 0u;
       const int cnt = __popc(bits);
       // inclusive scan of cnt over the wave
       int incl = cnt;
@@ -142,11 +144,11 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
       while (bb) {
         const int bit = __ffs(bb) - 1;
         bb &= bb - 1;
-        s_list[wave][wpos++] = static_cast<uint16_t>(wi * 32 + bit);
+        s_list[li][wpos++] = static_cast<uint16_t>(wi * 32 + bit);
       }
       base += __shfl(incl, 63, 64);
     }
-    if (lane == 0) s_count[wave] = base;
+    if (lane == 0) s_count[li] = base;
   }
   __syncthreads();
 
@@ -172,7 +174,14 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
     float m2 = -INFINITY, lsum = 0.f;     // running max (log2 domain), sum
-    int cur = 0;                           // cursor into this row's units
+    int cur = 0;                           // cursor into this row's units, whose
+    int nu;                                // unit (past the end: INT_MAX) and
+    float nlg;                             // log2 gate are kept in registers
+    {
+      const int16_t* urow = reinterpret_cast<const int16_t*>(s_idx[wave][ql]);
+      nu = K > 0 ? urow[0] : 0x7FFFFFFF;
+      nlg = K > 0 ? s_lg[wave][ql][0] * kLog2e : 0.f;
+    }
     const int pos32 = static_cast<int>(pos);
     const int c_cur = pos32 / b;           // current unit of the row
     const int c_end = (c_cur + 1) * b;     // first key after it
@@ -181,37 +190,38 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
     // Loads run kP - 1 tiles ahead of the tile being computed, in a ring of kP
     // register slots (the loop is unrolled kP times so every slot index is a
     // constant); LDS holds two tiles (computed / being staged).
-    constexpr int kLd = kKT * D / 8 / 256;
-    constexpr int kP = D == 64 ? 4 : 2;    // 2 or 4 (register budget)
-    constexpr int kL1 = kLd > 0 ? kLd : 1;
-    uint4 kq0[kL1], vq0[kL1], kq1[kL1], vq1[kL1], kq2[kL1], vq2[kL1], kq3[kL1], vq3[kL1];
+    constexpr int kLd = kKT * D / 8 / kThreads;
+    constexpr int kP = kLd == 1 ? 4 : 2;   // ring depth within the register budget
+    // ring slots s = 0..3: K vectors s##k0, s##k1 and V vectors s##v0, s##v1
+    uint4 sl0k0, sl0k1, sl0v0, sl0v1, sl1k0, sl1k1, sl1v0, sl1v1;
+    uint4 sl2k0, sl2k1, sl2v0, sl2v1, sl3k0, sl3k1, sl3v0, sl3v1;
     static_assert(kLd == 1 || kLd == 2, "one or two 16-byte vectors per thread per tile");
-    // vector i of a tile: thread tid moves key row (tid + 256 i) / (D / 8), column group tid % (D / 8)
+    // vector i of a tile: thread tid moves key row (tid + kThreads i) / (D / 8), column group tid % (D / 8)
     // K: thread x takes key row x / (D / 8), columns 8 (x % (D / 8)) .. +7 (rows
     // contiguous in LDS).  V: key x % 32, columns 8 (x / 32) .. +7, so that each
     // transposed 2-byte LDS write of a wave covers 32 consecutive keys of a
     // V^T row and the other half-wave lands 8 rows (a half bank cycle) away.
-#define SPA_ISSUE_ONE(KS, VS, IT, I)                                                         \
+#define SPA_ISSUE_ONE(R, IT, I)                                                               \
   do {                                                                                       \
-    const int x = tid + (I) * 256;                                                           \
+    const int x = tid + (I) * kThreads;                                                      \
     const int64_t kb0 = static_cast<int64_t>(list[IT]) * kKT;                                \
     int64_t key = kb0 + x / (D / 8), vkey = kb0 + x % kKT;                                   \
     key = key < L ? key : L - 1;                                                             \
     vkey = vkey < L ? vkey : L - 1;                                                          \
-    KS[I] = *reinterpret_cast<const uint4*>(k + kvbase + key * D + (x % (D / 8)) * 8);       \
-    VS[I] = *reinterpret_cast<const uint4*>(v + kvbase + vkey * D + (x / kKT) * 8);          \
+    R##k##I = *reinterpret_cast<const uint4*>(k + kvbase + key * D + (x % (D / 8)) * 8);      \
+    R##v##I = *reinterpret_cast<const uint4*>(v + kvbase + vkey * D + (x / kKT) * 8);         \
   } while (0)
-#define SPA_ISSUE(KS, VS, IT)                                                                \
+#define SPA_ISSUE(R, IT)                                                                     \
   do {                                                                                       \
-    SPA_ISSUE_ONE(KS, VS, IT, 0);                                                            \
-    if constexpr (kLd == 2) SPA_ISSUE_ONE(KS, VS, IT, 1);                                    \
+    SPA_ISSUE_ONE(R, IT, 0);                                                                 \
+    if constexpr (kLd == 2) SPA_ISSUE_ONE(R, IT, 1);                                         \
   } while (0)
-#define SPA_STAGE_ONE(KS, VS, BUF, I)                                                        \
+#define SPA_STAGE_ONE(R, BUF, I)                                                             \
   do {                                                                                       \
-    const int x = tid + (I) * 256;                                                           \
+    const int x = tid + (I) * kThreads;                                                      \
     const int kr = x / (D / 8), cv = x % (D / 8);                                            \
-    *reinterpret_cast<uint4*>(&sm.k[BUF][kr * TileSmem<D>::kKPitch + cv * 8]) = KS[I];      \
-    const uint4 vw = VS[I];                                                                  \
+    *reinterpret_cast<uint4*>(&sm.k[BUF][kr * TileSmem<D>::kKPitch + cv * 8]) = R##k##I;     \
+    const uint4 vw = R##v##I;                                                                 \
     uint16_t* vt = reinterpret_cast<uint16_t*>(sm.vt[BUF]) + (x / kKT) * 8 * TileSmem<D>::kVPitch + x % kKT; \
     vt[0 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.x);                              \
     vt[1 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.x >> 16);                        \
@@ -222,148 +232,148 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
     vt[6 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.w);                              \
     vt[7 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.w >> 16);                        \
   } while (0)
-#define SPA_STAGE(KS, VS, BUF)                                                               \
+#define SPA_STAGE(R, BUF)                                                                    \
   do {                                                                                       \
-    SPA_STAGE_ONE(KS, VS, BUF, 0);                                                           \
-    if constexpr (kLd == 2) SPA_STAGE_ONE(KS, VS, BUF, 1);                                   \
+    SPA_STAGE_ONE(R, BUF, 0);                                                                \
+    if constexpr (kLd == 2) SPA_STAGE_ONE(R, BUF, 1);                                        \
   } while (0)
-    if (ntl > 0) SPA_ISSUE(kq0, vq0, 0);
+    if (ntl > 0) SPA_ISSUE(sl0, 0);
     if constexpr (kP == 4) {
-      if (ntl > 1) SPA_ISSUE(kq1, vq1, 1);
-      if (ntl > 2) SPA_ISSUE(kq2, vq2, 2);
+      if (ntl > 1) SPA_ISSUE(sl1, 1);
+      if (ntl > 2) SPA_ISSUE(sl2, 2);
     }
-    if (ntl > 0) SPA_STAGE(kq0, vq0, 0);
+    if (ntl > 0) SPA_STAGE(sl0, 0);
     __syncthreads();
-    // one tile of the ring; u (the slot of tile it) is a compile-time constant
+    // one tile of the ring: tile it0 + u lives in slot u; the step issues the
+    // loads of tile it0 + u + kP - 1 into slot ri and stages slot rn (tile it0 + u + 1)
     int it0 = 0;
-    auto tile_step = [&](auto uc, uint4 (&ki)[kL1], uint4 (&vi)[kL1], uint4 (&kn)[kL1],
-                         uint4 (&vn)[kL1]) __attribute__((always_inline)) {
-      constexpr int u = decltype(uc)::value;   // ki / vi: slot issued, kn / vn: slot staged
-      const int it = it0 + u;
-      if (it < ntl) {
-      const int buf = u & 1;               // it0 is a multiple of kP (even)
-      if (it + kP - 1 < ntl) SPA_ISSUE(ki, vi, it + kP - 1);
-      const int ks0 = static_cast<int>(list[it]) * kKT;   // positions fit int32 (L <= 65536)
-
-      // Which of this wave's rows read the tile, with what bias (log2 domain).
-      // A tile that none of them reads is skipped (the workgroup's list is the
-      // union over all its waves).
-      float bias_lo = 0.f, bias_hi = 0.f;
-      bool need, masked = false;
-      if (branch == 0) {
-        const int u_lo = (ks0 + 8 * hl) / b, u_hi = (ks0 + 16 + 8 * hl) / b;
-        const int16_t* ur = reinterpret_cast<const int16_t*>(s_idx[wave][ql]);
-        const int uu[2] = {u_lo, u_hi};
-        float bb[2];
-#pragma unroll
-        for (int part = 0; part < 2; ++part) {
-          const int uv = uu[part];
-          float bv = -INFINITY;
-          if (local == 0 && uv == c_cur) {
-            bv = 0.f;   // causal mask applied per key below
-          } else {
-            while (cur < K && ur[cur] < uv) ++cur;        // unused slots hold -1
-            if (cur < K && ur[cur] == uv) bv = s_lg[wave][ql][cur] * kLog2e;
-          }
-          bb[part] = bv;
-        }
-        bias_lo = row_ok ? bb[0] : -INFINITY;
-        bias_hi = row_ok ? bb[1] : -INFINITY;
-        need = bias_lo != -INFINITY || bias_hi != -INFINITY;
-        masked = local == 0 && (u_lo == c_cur || u_hi == c_cur) && ks0 + kKT - 1 > pos32;
-      } else {
-        need = row_ok && ks0 <= pos32 && ks0 + kKT - 1 > pos32 - window;
-        masked = !(ks0 + kKT - 1 <= pos32 && ks0 > pos32 - window);
-        bias_lo = bias_hi = row_ok ? 0.f : -INFINITY;
-      }
-      if (__ballot(need) != 0) {
-        // S^T = K Q^T for this wave's 32 rows
-        floatx16_t st;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[r] = 0.f;
-        const __bf16* krow = &sm.k[buf][perm_row(ql) * TileSmem<D>::kKPitch];
-#pragma unroll
-        for (int ks = 0; ks < kKS; ++ks) {
-          const uint4 a = *reinterpret_cast<const uint4*>(krow + 16 * ks + 8 * hl);
-          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[ks]), st, 0, 0, 0);
-        }
-        float z[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) z[r] = fmaf(st[r], scale2, r < 8 ? bias_lo : bias_hi);
-        if (__ballot(masked) != 0) {
-          // branch L: keys of the current unit after the row; branch S: keys
-          // outside (pos - window, pos]
-          if (branch == 0) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = ks0 + tile_key(r, hl);
-              z[r] = (key > pos32 && key < c_end) ? -INFINITY : z[r];
-            }
-          } else {
-            const int wlo = pos32 - window + 1;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = ks0 + tile_key(r, hl);
-              z[r] = (key > pos32 || key < wlo) ? -INFINITY : z[r];
-            }
-          }
-        }
-        // online softmax for this lane's row (two half-waves hold its 32 keys)
-        float mt = z[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, z[r]);
-        mt = fmaxf(mt, xor_lanes_f<32>(mt));
-        const float mnew = fmaxf(m2, mt);
-        // hardware exp2 (exp2(-inf) = 0); a row with no key yet keeps zeros
-        const float msub = mnew == -INFINITY ? 0.f : mnew;
-        const float corr = __builtin_amdgcn_exp2f(m2 - msub);
-        float p[16], ps = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(z[r] - msub);
-          ps += p[r];
-        }
-        ps += xor_lanes_f<32>(ps);
-        lsum = lsum * corr + ps;
-        m2 = mnew;
-        if (__ballot(corr != 1.f) != 0) {
-#pragma unroll
-          for (int db = 0; db < kDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[db][r] *= corr;
-        }
-        // O^T += V^T P^T: B = P^T (keys 16s + 8hl + t of this lane's row)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          bf16x8_t pb;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) pb[t] = static_cast<__bf16>(p[8 * s2 + t]);
-#pragma unroll
-          for (int db = 0; db < kDB; ++db) {
-            const uint4 a = *reinterpret_cast<const uint4*>(
-                &sm.vt[buf][(32 * db + ql) * TileSmem<D>::kVPitch + 16 * s2 + 8 * hl]);
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb, acc[db], 0, 0, 0);
-          }
-        }
-      }
-      // next tile into the other buffer (last read two iterations ago); the
-      // barrier orders LDS only, so later tiles' loads stay in flight
-      if (it + 1 < ntl) SPA_STAGE(kn, vn, buf ^ 1);
-      lds_barrier();
-      }
-    };
+#define SPA_TILE_STEP(u, ri, rn)\
+  do {                                                                                                   \
+      const int it = it0 + u;                                                                            \
+      if (it < ntl) {                                                                                    \
+      const int buf = u & 1;               /* it0 is a multiple of kP (even) */                          \
+      if (it + kP - 1 < ntl) SPA_ISSUE(ri, it + kP - 1);                                                 \
+      const int ks0 = static_cast<int>(list[it]) * kKT;   /* positions fit int32 (L <= 65536) */         \
+      /* Which of this wave's rows read the tile, with what bias (log2 domain). */                       \
+      /* A tile that none of them reads is skipped (the workgroup's list is the */                       \
+      /* union over all its waves). */                                                                   \
+      float bias_lo = 0.f, bias_hi = 0.f;                                                                \
+      bool need, masked = false;                                                                         \
+      if (branch == 0) {                                                                                 \
+        const int u_lo = (ks0 + 8 * hl) / b, u_hi = (ks0 + 16 + 8 * hl) / b;                             \
+        const int16_t* ur = reinterpret_cast<const int16_t*>(s_idx[wave][ql]);                           \
+        const int uu[2] = {u_lo, u_hi};                                                                  \
+        float bb[2];                                                                                     \
+_Pragma("unroll")                                                                                        \
+        for (int part = 0; part < 2; ++part) {                                                           \
+          const int uv = uu[part];                                                                       \
+          float bv = -INFINITY;                                                                          \
+          if (local == 0 && uv == c_cur) {                                                               \
+            bv = 0.f;   /* causal mask applied per key below */                                          \
+          } else {                                                                                       \
+            while (nu < uv) {   /* advance past smaller units (unused slots hold -1) */                  \
+              ++cur; nu = cur < K ? ur[cur] : 0x7FFFFFFF; nlg = cur < K ? s_lg[wave][ql][cur] * kLog2e : 0.f; }\
+            if (nu == uv) bv = nlg;                                                                            \
+          }                                                                                              \
+          bb[part] = bv;                                                                                 \
+        }                                                                                                \
+        bias_lo = row_ok ? bb[0] : -INFINITY;                                                            \
+        bias_hi = row_ok ? bb[1] : -INFINITY;                                                            \
+        need = bias_lo != -INFINITY || bias_hi != -INFINITY;                                             \
+        masked = local == 0 && (u_lo == c_cur || u_hi == c_cur) && ks0 + kKT - 1 > pos32;                \
+      } else {                                                                                           \
+        need = row_ok && ks0 <= pos32 && ks0 + kKT - 1 > pos32 - window;                                 \
+        masked = !(ks0 + kKT - 1 <= pos32 && ks0 > pos32 - window);                                      \
+        bias_lo = bias_hi = row_ok ? 0.f : -INFINITY;                                                    \
+      }                                                                                                  \
+      if (__ballot(need) != 0) {                                                                         \
+        /* S^T = K Q^T for this wave's 32 rows */                                                        \
+        floatx16_t st;                                                                                   \
+_Pragma("unroll")                                                                                        \
+        for (int r = 0; r < 16; ++r) st[r] = 0.f;                                                        \
+        const __bf16* krow = &sm.k[buf][perm_row(ql) * TileSmem<D>::kKPitch];                            \
+_Pragma("unroll")                                                                                        \
+        for (int ks = 0; ks < kKS; ++ks) {                                                               \
+          const uint4 a = *reinterpret_cast<const uint4*>(krow + 16 * ks + 8 * hl);                      \
+          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[ks]), st, 0, 0, 0);  \
+        }                                                                                                \
+        float z[16];                                                                                     \
+_Pragma("unroll")                                                                                        \
+        for (int r = 0; r < 16; ++r) z[r] = fmaf(st[r], scale2, r < 8 ? bias_lo : bias_hi);              \
+        if (__ballot(masked) != 0) {                                                                     \
+          /* branch L: keys of the current unit after the row; branch S: keys */                         \
+          /* outside (pos - window, pos] */                                                              \
+          if (branch == 0) {                                                                             \
+_Pragma("unroll")                                                                                        \
+            for (int r = 0; r < 16; ++r) {                                                               \
+              const int key = ks0 + tile_key(r, hl);                                                     \
+              z[r] = (key > pos32 && key < c_end) ? -INFINITY : z[r];                                    \
+            }                                                                                            \
+          } else {                                                                                       \
+            const int wlo = pos32 - window + 1;                                                          \
+_Pragma("unroll")                                                                                        \
+            for (int r = 0; r < 16; ++r) {                                                               \
+              const int key = ks0 + tile_key(r, hl);                                                     \
+              z[r] = (key > pos32 || key < wlo) ? -INFINITY : z[r];                                      \
+            }                                                                                            \
+          }                                                                                              \
+        }                                                                                                \
+        /* online softmax for this lane's row (two half-waves hold its 32 keys) */                       \
+        float mt = z[0];                                                                                 \
+_Pragma("unroll")                                                                                        \
+        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, z[r]);                                               \
+        mt = fmaxf(mt, xor_lanes_f<32>(mt));                                                             \
+        const float mnew = fmaxf(m2, mt);                                                                \
+        /* hardware exp2 (exp2(-inf) = 0); a row with no key yet keeps zeros */                          \
+        const float msub = mnew == -INFINITY ? 0.f : mnew;                                               \
+        const float corr = __builtin_amdgcn_exp2f(m2 - msub);                                            \
+        float p[16], ps = 0.f;                                                                           \
+_Pragma("unroll")                                                                                        \
+        for (int r = 0; r < 16; ++r) {                                                                   \
+          p[r] = __builtin_amdgcn_exp2f(z[r] - msub);                                                    \
+          ps += p[r];                                                                                    \
+        }                                                                                                \
+        ps += xor_lanes_f<32>(ps);                                                                       \
+        lsum = lsum * corr + ps;                                                                         \
+        m2 = mnew;                                                                                       \
+        if (__ballot(corr != 1.f) != 0) {                                                                \
+_Pragma("unroll")                                                                                        \
+          for (int db = 0; db < kDB; ++db)                                                               \
+_Pragma("unroll")                                                                                        \
+            for (int r = 0; r < 16; ++r) acc[db][r] *= corr;                                             \
+        }                                                                                                \
+        /* O^T += V^T P^T: B = P^T (keys 16s + 8hl + t of this lane's row) */                            \
+_Pragma("unroll")                                                                                        \
+        for (int s2 = 0; s2 < 2; ++s2) {                                                                 \
+          bf16x8_t pb;                                                                                   \
+_Pragma("unroll")                                                                                        \
+          for (int t = 0; t < 8; ++t) pb[t] = static_cast<__bf16>(p[8 * s2 + t]);                        \
+_Pragma("unroll")                                                                                        \
+          for (int db = 0; db < kDB; ++db) {                                                             \
+            const uint4 a = *reinterpret_cast<const uint4*>(                                             \
+                &sm.vt[buf][(32 * db + ql) * TileSmem<D>::kVPitch + 16 * s2 + 8 * hl]);                  \
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb, acc[db], 0, 0, 0);       \
+          }                                                                                              \
+        }                                                                                                \
+      }                                                                                                  \
+      /* next tile into the other buffer (last read two iterations ago); the */                          \
+      /* barrier orders LDS only, so later tiles' loads stay in flight */                                \
+      if (it + 1 < ntl) SPA_STAGE(rn, buf ^ 1);                                                          \
+      lds_barrier();                                                                                     \
+      }                                                                                                  \
+  } while (0)
     for (it0 = 0; it0 < ntl; it0 += kP) {
       if constexpr (kP == 4) {
-        // tile it0 + u lives in slot u; step u issues into slot u + 3, stages slot u + 1
-        tile_step(std::integral_constant<int, 0>{}, kq3, vq3, kq1, vq1);
-        tile_step(std::integral_constant<int, 1>{}, kq0, vq0, kq2, vq2);
-        tile_step(std::integral_constant<int, 2>{}, kq1, vq1, kq3, vq3);
-        tile_step(std::integral_constant<int, 3>{}, kq2, vq2, kq0, vq0);
+        SPA_TILE_STEP(0, sl3, sl1);
+        SPA_TILE_STEP(1, sl0, sl2);
+        SPA_TILE_STEP(2, sl1, sl3);
+        SPA_TILE_STEP(3, sl2, sl0);
       } else {
-        tile_step(std::integral_constant<int, 0>{}, kq1, vq1, kq1, vq1);
-        tile_step(std::integral_constant<int, 1>{}, kq0, vq0, kq0, vq0);
+        SPA_TILE_STEP(0, sl1, sl1);
+        SPA_TILE_STEP(1, sl0, sl0);
       }
     }
+#undef SPA_TILE_STEP
 #undef SPA_ISSUE
 #undef SPA_ISSUE_ONE
 #undef SPA_STAGE
@@ -412,19 +422,31 @@ bool attn_tile_fwd_supported(const AttnLaunch& p) {
          (p.L + kKT - 1) / kKT <= kMaxKeyTiles && (p.d == 64 || p.d == 128);
 }
 
-hipError_t launch_attn_tile_fwd(const AttnLaunch& p, hipStream_t st) {
+template <int D, bool kMix, int NW>
+static hipError_t launch_tile_fwd_k(const AttnLaunch& p, int NH, int NT, hipStream_t st) {
   const int G = p.Hq / p.Hkv;
-  const int NH = G < 4 ? G : 4;
-  const int NT = 4 / NH;
   const int ntiles = (p.nq + 31) / 32;
   dim3 grid((ntiles + NT - 1) / NT, static_cast<unsigned>(p.B * p.Hkv * (G / NH)));
-  const bool mix = p.window > 0 && p.alpha != nullptr;
-  auto kern = p.d == 64 ? (mix ? attn_tile_fwd_kernel<64, true> : attn_tile_fwd_kernel<64, false>)
-                        : (mix ? attn_tile_fwd_kernel<128, true> : attn_tile_fwd_kernel<128, false>);
-  return launch(true, kern, grid, dim3(256), st, static_cast<const __bf16*>(p.q),
+  return launch(true, attn_tile_fwd_kernel<D, kMix, NW>, grid, dim3(64 * NW), st, static_cast<const __bf16*>(p.q),
                 static_cast<const __bf16*>(p.k), static_cast<const __bf16*>(p.v), p.idx, p.logg, p.alpha,
                 p.Hq, p.Hkv, p.Hsel, p.share_group, p.nq, p.q_pos0, p.L, p.b, p.prefix_mode, p.qblock,
                 p.K, p.local, p.window, static_cast<__bf16*>(p.o), p.lse, NH, NT);
+}
+
+// Heads of a group share K / V tiles: up to 4 of them in a workgroup, one wave
+// each.  A single head (d = 64) takes two row tiles per workgroup: the
+// workgroup walks the union of its rows' key tiles, so fewer rows per union
+// mean fewer tiles a wave waits through without needing them.
+hipError_t launch_attn_tile_fwd(const AttnLaunch& p, hipStream_t st) {
+  const int G = p.Hq / p.Hkv;
+  const bool mix = p.window > 0 && p.alpha != nullptr;
+  if (G == 1 && p.d == 64) {
+    return mix ? launch_tile_fwd_k<64, true, 2>(p, 1, 2, st) : launch_tile_fwd_k<64, false, 2>(p, 1, 2, st);
+  }
+  const int NH = G < 4 ? G : 4;
+  const int NT = 4 / NH;
+  if (p.d == 64) return mix ? launch_tile_fwd_k<64, true, 4>(p, NH, NT, st) : launch_tile_fwd_k<64, false, 4>(p, NH, NT, st);
+  return mix ? launch_tile_fwd_k<128, true, 4>(p, NH, NT, st) : launch_tile_fwd_k<128, false, 4>(p, NH, NT, st);
 }
 
 }  // namespace spa
