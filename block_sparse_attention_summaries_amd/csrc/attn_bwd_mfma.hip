@@ -131,7 +131,8 @@ __global__ __launch_bounds__(256) void attn_tile_dq_kernel(
   const bool row_ok = row < nq;
   const int rowc = row_ok ? row : nq - 1;
   const int pos32 = static_cast<int>(q_pos0 + rowc);
-  const int c_cur = pos32 / b;
+  const int lb = __builtin_ctz(b);         // b is a power of two
+  const int c_cur = pos32 >> lb;
   const int c_end = (c_cur + 1) * b;
   const int nkt = static_cast<int>((L + kBT - 1) / kBT);
   const int nwords = (nkt + 31) / 32;
@@ -250,9 +251,11 @@ __global__ __launch_bounds__(256) void attn_tile_dq_kernel(
     SPA_DQ_STAGE();
   }
   __syncthreads();
+  int ks0n = ntl > 0 ? static_cast<int>(s_list[0]) * kBT : 0;
   for (int it = 0; it < ntl; ++it) {
     if (it + 1 < ntl) SPA_DQ_ISSUE(it + 1);
-    const int ks0 = static_cast<int>(s_list[it]) * kBT;
+    const int ks0 = ks0n;                     // list entry read one tile ahead
+    if (it + 1 < ntl) ks0n = static_cast<int>(s_list[it + 1]) * kBT;
     // bias (log2 domain) and gate slot of the two 16-key halves this lane holds
     float bias[2];
     int slot[2];
@@ -260,7 +263,7 @@ __global__ __launch_bounds__(256) void attn_tile_dq_kernel(
       const int16_t* ur = reinterpret_cast<const int16_t*>(s_idx[wave][ql]);
 #pragma unroll
       for (int part = 0; part < 2; ++part) {
-        const int uv = (ks0 + 16 * part + 8 * hl) / b;
+        const int uv = (ks0 + 16 * part + 8 * hl) >> lb;
         float bv = -INFINITY;
         int sl = -1;
         if (uv == c_cur) {

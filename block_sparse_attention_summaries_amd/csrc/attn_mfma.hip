@@ -183,7 +183,8 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
       nlg = K > 0 ? s_lg[wave][ql][0] * kLog2e : 0.f;
     }
     const int pos32 = static_cast<int>(pos);
-    const int c_cur = pos32 / b;           // current unit of the row
+    const int lb = __builtin_ctz(b);       // b is a power of two
+    const int c_cur = pos32 >> lb;         // current unit of the row
     const int c_end = (c_cur + 1) * b;     // first key after it
 
     // staging: 2 x 16 B of K and of V per thread per tile (D = 128), 1 (D = 64).
@@ -247,20 +248,22 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
     // one tile of the ring: tile it0 + u lives in slot u; the step issues the
     // loads of tile it0 + u + kP - 1 into slot ri and stages slot rn (tile it0 + u + 1)
     int it0 = 0;
+    int ks0n = ntl > 0 ? static_cast<int>(list[0]) * kKT : 0;
 #define SPA_TILE_STEP(u, ri, rn)\
   do {                                                                                                   \
       const int it = it0 + u;                                                                            \
       if (it < ntl) {                                                                                    \
       const int buf = u & 1;               /* it0 is a multiple of kP (even) */                          \
       if (it + kP - 1 < ntl) SPA_ISSUE(ri, it + kP - 1);                                                 \
-      const int ks0 = static_cast<int>(list[it]) * kKT;   /* positions fit int32 (L <= 65536) */         \
+      const int ks0 = ks0n;   /* list entry read one tile ahead */                                       \
+      if (it + 1 < ntl) ks0n = static_cast<int>(list[it + 1]) * kKT;                                     \
       /* Which of this wave's rows read the tile, with what bias (log2 domain). */                       \
       /* A tile that none of them reads is skipped (the workgroup's list is the */                       \
       /* union over all its waves). */                                                                   \
       float bias_lo = 0.f, bias_hi = 0.f;                                                                \
       bool need, masked = false;                                                                         \
       if (branch == 0) {                                                                                 \
-        const int u_lo = (ks0 + 8 * hl) / b, u_hi = (ks0 + 16 + 8 * hl) / b;                             \
+        const int u_lo = (ks0 + 8 * hl) >> lb, u_hi = (ks0 + 16 + 8 * hl) >> lb;                         \
         const int16_t* ur = reinterpret_cast<const int16_t*>(s_idx[wave][ql]);                           \
         const int uu[2] = {u_lo, u_hi};                                                                  \
         float bb[2];                                                                                     \
