@@ -99,7 +99,7 @@ struct DqSmem {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_tile_dq_kernel(
+__global__ __launch_bounds__(256, 2) void attn_tile_dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dbuf,
     const int32_t* __restrict__ idx, const float* __restrict__ logg, int Hq, int Hkv, int Hsel,
@@ -394,7 +394,7 @@ struct DkvSmem {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_tile_dkdv_kernel(
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_tile_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dbuf,
     const int32_t* __restrict__ idx, const float* __restrict__ logg, const uint32_t* __restrict__ bits,
