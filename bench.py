@@ -252,8 +252,33 @@ def run_decode(args):
     torch.cuda.synchronize()
     hot_us = g0.elapsed_time(g1) * 1e3 / 64
 
+    floor_us = latency_floor_us(stream, steps)
     return dict(wl=wl, cfg=cfg, x=x, total_ms=total_ms, sel_ms=sel_ms, att_ms=att_ms, k_ms=k_ms,
-                summ_ms=summ_ms, summ_bytes=summ_bytes, hot_us=hot_us)
+                summ_ms=summ_ms, summ_bytes=summ_bytes, hot_us=hot_us, floor_us=floor_us)
+
+
+def latency_floor_us(stream, steps):
+    """Graph replay of `steps` x 4 dependent 256-workgroup kernels that do next
+    to nothing (the library's workspace fill of 1 MiB): the launch and
+    dependency cost a four-kernel decode step pays before moving any bytes."""
+    buf = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    lib = ops.lib()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        g.capture_begin()
+        for _ in range(4 * steps):
+            lib.sparse_workspace_init(ctypes.c_void_p(buf.data_ptr()), buf.numel(),
+                                      ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        g.capture_end()
+    torch.cuda.current_stream().wait_stream(stream)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
 
 
 # ---------------------------------------------------------------- prefill / training
@@ -497,6 +522,12 @@ def main():
         "summaries_512k_ms": round(res["summ_ms"], 3),
         "summaries_gbps": round(res["summ_bytes"] / (res["summ_ms"] * 1e-3) / 1e9, 1),
         "roofline": roofline,
+        # t >= (launch + dependency cost of the four kernels) + (all bytes at peak)
+        "latency_floor": {
+            "four_kernel_step_us": round(res["floor_us"], 3),
+            "bytes_at_peak_us": round(sum(k["bytes"] for k in kern.values()) / (HBM_PEAK_GBPS * 1e3), 3),
+            "bound_us": round(res["floor_us"] + sum(k["bytes"] for k in kern.values()) / (HBM_PEAK_GBPS * 1e3), 3),
+        },
     }
     if not args.no_prefill:
         pf = run_prefill(3)
