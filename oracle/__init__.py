@@ -80,6 +80,8 @@ def _declare(lib):
     lib.orc_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, I, I64, I64, I, I, I, P, P, I, I, I, I,
                                  P, P, I64, P, P]
     lib.orc_attn_fwd.restype = None
+    lib.orc_select_bwd.restype = None
+    lib.orc_select_bwd.argtypes = [P, I, I, I, I, I, I, I64, P, I, I64, I, I, I, P, P, P, P]
     lib.orc_attn_bwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I64, I64, I, P, P, I, I, I64,
                                  P, P, P, P]
     lib.orc_attn_bwd.restype = None
@@ -236,3 +238,21 @@ def attn_bwd(q, k, v, dout, idx, logg, *, b, K, q_pos0, share_group=True, kv_sli
                      L, int(q_pos0), b, _ptr(idx), _ptr(logg_a), K, int(bool(share_group)),
                      int(kv_slice), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg))
     return dq, dk, dv, dg
+
+
+def select_bwd(q, kbar, idx, dg, *, Hkv, b, K, q_pos0, share_group=True):
+    """Selector-side backward: the gate gradient dg [B, Hsel, nq, K] (w.r.t. g)
+    through log g = s - LSE(s) into q (dq [B, Hq, nq, d]) and the block
+    summaries (dkbar [B, Hkv, ccap, d]), fp64.  Current-block candidates, no
+    projection and no erf term."""
+    lib = _load()
+    B, Hq, nq, d = q.shape
+    ccap = kbar.shape[2]
+    dq = np.zeros((B, Hq, nq, d), np.float64)
+    dkbar = np.zeros((B, Hkv, ccap, d), np.float64)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    dg = np.ascontiguousarray(dg, dtype=np.float64)
+    lib.orc_select_bwd(_ptr(q), _dtype_code(q), B, Hq, Hkv, nq, d, int(q_pos0), _ptr(kbar),
+                       _dtype_code(kbar), ccap, b, int(bool(share_group)), K, _ptr(idx), _ptr(dg),
+                       _ptr(dq), _ptr(dkbar))
+    return dq, dkbar

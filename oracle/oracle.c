@@ -686,3 +686,107 @@ void orc_attn_bwd(const void *q, const void *k, const void *v, const void *dout,
     free(D_all);
     free(dgh);
 }
+
+/* ------------------------------------------- next: selector-side backward */
+/*
+ * Gradient of the gate into the selector's inputs ([SAS] "How it works",
+ * step 5: the loss flows o -> g -> s -> selector, §4.3 Eq. 9; the gate is
+ * log g_m = s_m - LSE(s) over every candidate of the row, §4.2.2).  With the
+ * selection S of a row fixed and dg_m the gradient of the loss with respect
+ * to g_m (what orc_attn_bwd returns), let dl_m = g_m dg_m (the gradient with
+ * respect to log g_m) and p = softmax(s) over the candidates (so g_m = p_m).
+ * Then
+ *   ds_c = [c in S] dl_c - p_c sum_{m in S} dl_m
+ *   dq_hat = sum_c ds_c kbar_c / sqrt(d),   dkbar_c += ds_c q_hat / sqrt(d),
+ * and each of the G query heads averaged into q_hat receives dq_hat / G.
+ * Scores are recomputed here in fp64 (orc_scores_row, no projection, no erf
+ * term); idx is the forward's selection, dg is [B, Hsel, nq, K] (padded slots
+ * ignored).  Outputs (fp64, written): dq [B, Hq, nq, d], dkbar [B, Hkv, Ccap, d].
+ */
+void orc_select_bwd(const void *q, int qdtype, int B, int Hq, int Hkv, int nq, int d,
+                    int64_t q_pos0, const void *kbar, int kdtype, int64_t Ccap, int b,
+                    int share_group, int K, const int32_t *idx, const double *dg,
+                    double *dq, double *dkbar)
+{
+    const int G = Hq / Hkv;
+    const int Hsel = share_group ? Hkv : Hq;
+    const double scale = 1.0 / sqrt((double)d);
+    memset(dq, 0, sizeof(double) * (size_t)B * Hq * nq * d);
+    memset(dkbar, 0, sizeof(double) * (size_t)B * Hkv * Ccap * d);
+    /* one task per (batch, kv head): it owns dkbar of that head */
+#pragma omp parallel for schedule(dynamic, 1) num_threads(orc_num_threads())
+    for (int t = 0; t < B * Hkv; ++t) {
+        const int bidx = t / Hkv, kvh = t % Hkv;
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Ccap > 0 ? Ccap : 1));
+        double *ds = (double *)malloc(sizeof(double) * (size_t)(Ccap > 0 ? Ccap : 1));
+        double *qh = (double *)malloc(sizeof(double) * (size_t)d);
+        const int hs0 = share_group ? kvh : kvh * G;
+        const int hs1 = share_group ? kvh + 1 : kvh * G + G;
+        for (int hs = hs0; hs < hs1; ++hs) {
+            for (int64_t row = 0; row < nq; ++row) {
+                const int64_t pos = q_pos0 + row;
+                int64_t ncand = orc_num_candidates(pos, b, 0, 128);
+                if (ncand > Ccap)
+                    ncand = Ccap;
+                if (ncand <= 0)
+                    continue;
+                orc_scores_row(q, qdtype, Hq, Hkv, nq, d, bidx, hs, row, pos, kbar, kdtype, NULL,
+                               NULL, Ccap, share_group, NULL, NULL, NULL, ncand, s);
+                double mx = s[0];
+                for (int64_t c = 1; c < ncand; ++c)
+                    if (s[c] > mx)
+                        mx = s[c];
+                double sum = 0.0;
+                for (int64_t c = 0; c < ncand; ++c)
+                    sum += exp(s[c] - mx);
+                const double lse = mx + log(sum);
+                const int64_t so = (((int64_t)bidx * Hsel + hs) * nq + row) * K;
+                double dl_sum = 0.0;
+                for (int64_t c = 0; c < ncand; ++c)
+                    ds[c] = 0.0;
+                for (int k = 0; k < K; ++k) {
+                    const int32_t c = idx[so + k];
+                    if (c < 0 || c >= ncand)
+                        continue;
+                    const double dl = exp(s[c] - lse) * dg[so + k];
+                    ds[c] += dl;
+                    dl_sum += dl;
+                }
+                for (int64_t c = 0; c < ncand; ++c)
+                    ds[c] -= exp(s[c] - lse) * dl_sum;
+                /* q_hat as the scores saw it */
+                for (int e = 0; e < d; ++e)
+                    qh[e] = 0.0;
+                if (share_group) {
+                    for (int g = 0; g < G; ++g)
+                        for (int e = 0; e < d; ++e)
+                            qh[e] += orc_load(q, qdtype, (((int64_t)bidx * Hq + hs * G + g) * nq + row) * d + e);
+                    for (int e = 0; e < d; ++e)
+                        qh[e] /= (double)G;
+                } else {
+                    for (int e = 0; e < d; ++e)
+                        qh[e] = orc_load(q, qdtype, (((int64_t)bidx * Hq + hs) * nq + row) * d + e);
+                }
+                const int64_t kb0 = ((int64_t)bidx * Hkv + kvh) * Ccap;
+                for (int e = 0; e < d; ++e) {
+                    double acc = 0.0;
+                    for (int64_t c = 0; c < ncand; ++c)
+                        acc += ds[c] * orc_load(kbar, kdtype, (kb0 + c) * d + e);
+                    acc *= scale;
+                    if (share_group) {
+                        for (int g = 0; g < G; ++g)
+                            dq[(((int64_t)bidx * Hq + hs * G + g) * nq + row) * d + e] += acc / (double)G;
+                    } else {
+                        dq[(((int64_t)bidx * Hq + hs) * nq + row) * d + e] += acc;
+                    }
+                }
+                for (int64_t c = 0; c < ncand; ++c)
+                    for (int e = 0; e < d; ++e)
+                        dkbar[(kb0 + c) * d + e] += ds[c] * qh[e] * scale;
+            }
+        }
+        free(s);
+        free(ds);
+        free(qh);
+    }
+}
