@@ -322,7 +322,7 @@ def run_train(reps):
     x = make_inputs(cfg)
     b, K = cfg["b"], cfg["K"]
     q, k, v, do = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["dout"])
-    ws = [ops.Workspace() for _ in range(3)]
+    ws = [ops.Workspace() for _ in range(4)]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     times = []
 
@@ -334,17 +334,22 @@ def run_train(reps):
         ev[1].record()
         o, lse = ops.sparse_attn_fwd(q, k, v, idx, logg, b=b, K=K, q_pos0=0, workspace=ws[1])
         ev[2].record()
-        ops.sparse_attn_bwd(q, k, v, idx, logg, o, do, lse, b=b, K=K, q_pos0=0, workspace=ws[2])
+        _, _, _, dg = ops.sparse_attn_bwd(q, k, v, idx, logg, o, do, lse, b=b, K=K, q_pos0=0,
+                                          workspace=ws[2])
         ev[3].record()
+        # selector side: dg through the gate into q and the summaries
+        ops.sparse_select_bwd(q, kb, mx, ce, idx, logg, dg, Hkv=cfg["Hkv"], b=b, K=K, q_pos0=0, gate=True,
+                              workspace=ws[3])
+        ev[4].record()
         torch.cuda.synchronize()
-        return [ev[i].elapsed_time(ev[i + 1]) for i in range(3)]
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
 
     once()
     for _ in range(reps):
         times.append(once())
     t = np.median(np.array(times), axis=0)
     tokens = cfg["B"] * x["L"]
-    return dict(ms=dict(select=t[0], fwd=t[1], bwd=t[2]), tokens_per_s=tokens / (t.sum() * 1e-3))
+    return dict(ms=dict(select=t[0], fwd=t[1], bwd=t[2], select_bwd=t[3]), tokens_per_s=tokens / (t.sum() * 1e-3))
 
 
 # ---------------------------------------------------------------- CPU oracle baseline

@@ -147,6 +147,20 @@ int check_bwd(const spa_attn_args* a, const void* o, const void* dout, const flo
   return SPA_OK;
 }
 
+int check_select_bwd(const spa_select_args* a, const float* dg, float* dq, float* dkbar, spa::SelectLaunch* p) {
+  int st = check_select(a, p);
+  if (st != SPA_OK) return st;
+  SPA_REQUIRE(a->gate == SPA_GATE_SOFTMAX_LOG, SPA_ERR_UNSUPPORTED,
+              "the selector backward needs the softmax log gate (gate = SOFTMAX_LOG)");
+  SPA_REQUIRE(a->prefix_mode == SPA_PREFIX_CURRENT_BLOCK && a->proj_w == nullptr && a->erf_lambda == nullptr,
+              SPA_ERR_UNSUPPORTED,
+              "the selector backward supports current-block candidates without projection or erf term");
+  SPA_REQUIRE(a->dtype == SPA_DTYPE_BF16, SPA_ERR_UNSUPPORTED, "the selector backward supports bf16 only");
+  SPA_REQUIRE(dg && dq && dkbar, SPA_ERR_INVALID_ARG, "dg, dq and dkbar must be non-NULL");
+  SPA_REQUIRE(aligned16(dq) && aligned16(dkbar), SPA_ERR_INVALID_ARG, "dq and dkbar must be 16-byte aligned");
+  return SPA_OK;
+}
+
 int check_ws(void* ws, size_t have, size_t need) {
   if (need == 0) return SPA_OK;
   SPA_REQUIRE(ws != nullptr && have >= need, SPA_ERR_WORKSPACE,
@@ -229,6 +243,18 @@ int sparse_attn_bwd(const spa_attn_args* a, const void* o, const void* dout, con
   return hip_status(spa::launch_attn_bwd(p, workspace, static_cast<hipStream_t>(stream)), "sparse_attn_bwd");
 }
 
+int sparse_select_bwd(const spa_select_args* a, const float* dg, float* dq, float* dkbar, void* workspace,
+                      size_t ws_bytes, spa_stream_t stream) {
+  ProfileScope profile_scope;
+  spa::SelectLaunch p;
+  int st = check_select_bwd(a, dg, dq, dkbar, &p);
+  if (st != SPA_OK) return st;
+  st = check_ws(workspace, ws_bytes, spa::select_bwd_workspace_bytes(p));
+  if (st != SPA_OK) return st;
+  return hip_status(spa::launch_select_bwd(p, dg, dq, dkbar, workspace, static_cast<hipStream_t>(stream)),
+                    "sparse_select_bwd");
+}
+
 size_t sparse_workspace_bytes(int op, const void* args) {
   switch (op) {
     case SPA_OP_SCORE_SELECT: {
@@ -246,6 +272,11 @@ size_t sparse_workspace_bytes(int op, const void* args) {
       if (check_attn(static_cast<const spa_attn_args*>(args), &p) != SPA_OK) return 0;
       spa::BwdLaunch bp{p, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
       return spa::attn_bwd_workspace_bytes(bp);
+    }
+    case SPA_OP_SELECT_BWD: {
+      spa::SelectLaunch p;
+      if (check_select(static_cast<const spa_select_args*>(args), &p) != SPA_OK) return 0;
+      return spa::select_bwd_workspace_bytes(p);
     }
     default:
       fail(SPA_ERR_INVALID_ARG, "unknown op %d", op);

@@ -1,0 +1,439 @@
+// select_bwd.hip -- selector-side backward (bf16, gfx950 MFMA): the gate
+// gradient dg carried back through log g = s - LSE(s) into the query and the
+// block summaries ("SAS" review, "How it works", step 5: the loss reaches the
+// selector through g; §4.2.2 softmax gate; §4.3 Eq. 9).  With p = softmax(s)
+// over a row's candidates (so g_m = p_m) and its selection S fixed:
+//   ds_c = p_c ([c in S] dg_c - sum_{m in S} p_m dg_m),
+//   dq_hat = sum_c ds_c kbar_c / sqrt(d)   (each head of a shared selection
+//            receives dq_hat / G),
+//   dkbar_c = sum_rows ds_c q_hat / sqrt(d).
+// Scores are recomputed from q_hat rounded to bf16 (a gradient needs ~1e-3,
+// not the ranking accuracy of the forward selection).
+//
+// Two launches:
+//   rows        4 waves x 32 rows of one selection head; pass 1 over the
+//               candidate tiles gives each row's LSE and sum_S p dg (saved to
+//               the workspace), pass 2 accumulates dq_hat^T += Kbar^T dS^T;
+//   candidates  one 32-candidate tile per workgroup; the four waves take the
+//               later rows 32 at a time, S = Q_hat Kbar^T puts one candidate
+//               per lane, dKbar += dS^T Q_hat, and the waves' sums are added in
+//               wave order.
+#include "spa_device.h"
+#include "spa_launch.h"
+
+namespace spa {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 sbbf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float sbfloatx16_t;
+
+constexpr int kST = 32;               // candidates / rows per tile
+constexpr float kSLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ sbbf16x8_t sb_bf16x8(uint4 v) { return __builtin_bit_cast(sbbf16x8_t, v); }
+// tile element held by register r of half-wave h when A rows are fed permuted
+__device__ __forceinline__ int sb_elem(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
+__device__ __forceinline__ int sb_perm(int m) {
+  const int a = m >> 3, h = (m >> 2) & 1, c = m & 3;
+  return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + c;
+}
+__device__ __forceinline__ uint4 sb_pack8(const float* x) {
+  sbbf16x8_t v;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) v[t] = static_cast<__bf16>(x[t]);
+  return __builtin_bit_cast(uint4, v);
+}
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): two MFMA operands that
+// carry x to about 16 significant bits
+__device__ __forceinline__ void sb_split8(const float* x, uint4& hi, uint4& lo) {
+  sbbf16x8_t h, l;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    h[t] = static_cast<__bf16>(x[t]);
+    l[t] = static_cast<__bf16>(x[t] - static_cast<float>(h[t]));
+  }
+  hi = __builtin_bit_cast(uint4, h);
+  lo = __builtin_bit_cast(uint4, l);
+}
+__device__ __forceinline__ void sb_store_t8(uint16_t* dst, int pitch, uint4 w) {
+  dst[0 * pitch] = static_cast<uint16_t>(w.x);
+  dst[1 * pitch] = static_cast<uint16_t>(w.x >> 16);
+  dst[2 * pitch] = static_cast<uint16_t>(w.y);
+  dst[3 * pitch] = static_cast<uint16_t>(w.y >> 16);
+  dst[4 * pitch] = static_cast<uint16_t>(w.z);
+  dst[5 * pitch] = static_cast<uint16_t>(w.z >> 16);
+  dst[6 * pitch] = static_cast<uint16_t>(w.w);
+  dst[7 * pitch] = static_cast<uint16_t>(w.w >> 16);
+}
+
+// q_hat of one row as 8 bf16 (columns 8 j .. 8 j + 7): the mean of nh heads
+// (summed in head order in fp32), rounded to nearest even.
+__device__ __forceinline__ uint4 qhat8(const __bf16* __restrict__ q0, int64_t head_stride, int nh, int j) {
+  float a[8];
+  Elem<bf16_t>::unpack(*reinterpret_cast<const uint4*>(q0 + 8 * j), a);
+  for (int g = 1; g < nh; ++g) {
+    float f[8];
+    Elem<bf16_t>::unpack(*reinterpret_cast<const uint4*>(q0 + g * head_stride + 8 * j), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] += f[e];
+  }
+  if (nh > 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = a[e] / static_cast<float>(nh);
+  }
+  return sb_pack8(a);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- rows
+template <int D>
+struct SbRowSmem {
+  static constexpr int kKPitch = D + 8;
+  static constexpr int kTPitch = kST + 8;
+  __bf16 k[kST * kKPitch];                 // Kbar tile, row-major
+  __bf16 kt[D * kTPitch];                  // Kbar tile, transposed
+  float dgt[4][32][kST + 4];               // per wave: dg of (row, candidate), 0 if not selected
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void select_bwd_rows_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ kbar, int Hq, int Hkv, int Hsel, int nq,
+    int64_t q_pos0, int64_t ccap, int b, int share_group, int K, const int32_t* __restrict__ idx,
+    const float* __restrict__ dg, float* __restrict__ dq, float2* __restrict__ ws_row) {
+  __shared__ SbRowSmem<D> sm;
+  constexpr int kKS = D / 16;
+  constexpr int kDB = D / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, ql = lane & 31;
+  const int bh = blockIdx.y;
+  const int bi = bh / Hsel, hs = bh % Hsel;
+  const int G = Hq / Hkv;
+  const int kvh = share_group ? hs : hs / G;
+  const int nh = share_group ? G : 1;
+  const int h0 = share_group ? hs * G : hs;
+  const int row = (blockIdx.x * 4 + wave) * 32 + ql;
+  const bool row_ok = row < nq;
+  const int rowc = row_ok ? row : nq - 1;
+  const int64_t pos = q_pos0 + rowc;
+  const int lb = __builtin_ctz(b);          // b is a power of two
+  const int ncand = row_ok ? static_cast<int>(pos >> lb) : 0;
+  const int last_row = ((blockIdx.x * 4 + 4) * 32 < nq ? (blockIdx.x * 4 + 4) * 32 : nq) - 1;
+  const int wg_cand = static_cast<int>((q_pos0 + last_row) >> lb);
+  const __bf16* kb = kbar + (static_cast<int64_t>(bi) * Hkv + kvh) * ccap * D;
+  const int64_t so = ((static_cast<int64_t>(bi) * Hsel + hs) * nq + rowc) * K;
+  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+  const float scale2 = scale * kSLog2e;
+
+  // B operand q_hat^T (lane: row, k-slice 16 ks + 8 hl .. +7)
+  uint4 qreg[kKS];
+  {
+    const __bf16* q0 = q + ((static_cast<int64_t>(bi) * Hq + h0) * nq + rowc) * D;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) qreg[ks] = qhat8(q0, static_cast<int64_t>(nq) * D, nh, 2 * ks + hl);
+  }
+  // staging: 16-byte vectors x and x + 256 of the tile (key x % 32, columns 8 (x / 32) ..)
+  constexpr int kLd = kST * D / 8 / 256;
+  static_assert(kLd == 1 || kLd == 2, "one or two vectors per thread");
+  auto stage = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < kLd; ++i) {
+      const int x = tid + 256 * i;
+      const int kr = x % kST, cv = x / kST;
+      int c = c0 + kr;
+      c = c < wg_cand ? c : wg_cand - 1;
+      const uint4 w = *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(c) * D + cv * 8);
+      *reinterpret_cast<uint4*>(&sm.k[kr * SbRowSmem<D>::kKPitch + cv * 8]) = w;
+      sb_store_t8(reinterpret_cast<uint16_t*>(sm.kt) + cv * 8 * SbRowSmem<D>::kTPitch + kr,
+                  SbRowSmem<D>::kTPitch, w);
+    }
+  };
+  // dg of this row's selected candidates in [c0, c0 + 32), 0 elsewhere
+  auto fill_dgt = [&](int c0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sm.dgt[wave][ql][16 * hl + e] = 0.f;
+    wave_lds_sync();
+    if (row_ok) {
+      for (int t = hl; t < K; t += 2) {
+        const int c = idx[so + t];
+        if (c >= c0 && c < c0 + kST && c < ncand) sm.dgt[wave][ql][c - c0] = dg[so + t];
+      }
+    }
+    wave_lds_sync();
+  };
+  // S^T = Kbar_perm q_hat^T: register r holds candidate c0 + sb_elem(r, hl)
+  auto scores = [&](sbfloatx16_t& st) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[r] = 0.f;
+    const __bf16* krow = &sm.k[sb_perm(ql) * SbRowSmem<D>::kKPitch];
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      const uint4 a = *reinterpret_cast<const uint4*>(krow + 16 * ks + 8 * hl);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sb_bf16x8(a), sb_bf16x8(qreg[ks]), st, 0, 0, 0);
+    }
+  };
+
+  // ---- pass 1: LSE and T = sum_S exp(s - m) dg (log2 domain, online)
+  float m2 = -INFINITY, l = 0.f, T = 0.f;
+  for (int c0 = 0; c0 < wg_cand; c0 += kST) {
+    __syncthreads();
+    stage(c0);
+    fill_dgt(c0);
+    __syncthreads();
+    sbfloatx16_t st;
+    scores(st);
+    float z[16], dgv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = sb_elem(r, hl);
+      z[r] = c0 + m < ncand ? st[r] * scale2 : -INFINITY;
+      dgv[r] = sm.dgt[wave][ql][m];
+    }
+    float tm = m2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tm = fmaxf(tm, z[r]);
+    if (tm != -INFINITY) {
+      const float corr = __builtin_amdgcn_exp2f(m2 - tm);
+      float ls = 0.f, ts = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(z[r] - tm);
+        ls += p;
+        ts = fmaf(p, dgv[r], ts);
+      }
+      l = l * corr + ls;
+      T = T * corr + ts;
+      m2 = tm;
+    }
+  }
+  {
+    // merge the two half-waves of each row
+    const float mo = xor_lanes_f<32>(m2), lo = xor_lanes_f<32>(l), to = xor_lanes_f<32>(T);
+    const float mm = fmaxf(m2, mo);
+    if (mm != -INFINITY) {
+      const float a = __builtin_amdgcn_exp2f(m2 - mm), bb = __builtin_amdgcn_exp2f(mo - mm);
+      l = l * a + lo * bb;
+      T = T * a + to * bb;
+      m2 = mm;
+    }
+  }
+  const float lse2 = l > 0.f ? m2 + __log2f(l) : 0.f;
+  const float sig = l > 0.f ? T / l : 0.f;                   // sum_S p_m dg_m
+  if (row_ok && hl == 0) ws_row[(static_cast<int64_t>(bi) * Hsel + hs) * nq + row] = make_float2(lse2, sig);
+
+  // ---- pass 2: dq_hat^T += Kbar^T dS^T
+  sbfloatx16_t acc[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  for (int c0 = 0; c0 < wg_cand; c0 += kST) {
+    __syncthreads();
+    stage(c0);
+    fill_dgt(c0);
+    __syncthreads();
+    sbfloatx16_t st;
+    scores(st);
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = sb_elem(r, hl);
+      const float p = c0 + m < ncand ? __builtin_amdgcn_exp2f(st[r] * scale2 - lse2) : 0.f;
+      ds[r] = p * (sm.dgt[wave][ql][m] - sig);
+    }
+    // ds sums to zero over a row's candidates, so dq_hat only sees how the
+    // summaries differ; rounding ds to one bf16 would leak the summaries'
+    // common part, hence the hi + lo split
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      uint4 pbh, pbl;
+      sb_split8(&ds[8 * s2], pbh, pbl);
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const uint4 a = *reinterpret_cast<const uint4*>(
+            &sm.kt[(32 * db + ql) * SbRowSmem<D>::kTPitch + 16 * s2 + 8 * hl]);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sb_bf16x8(a), sb_bf16x8(pbh), acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sb_bf16x8(a), sb_bf16x8(pbl), acc[db], 0, 0, 0);
+      }
+    }
+  }
+  if (!row_ok) return;
+  // dq_hat^T register r of block db holds d = 32 db + 8 (r / 4) + 4 hl + (r % 4)
+  const float f = scale / static_cast<float>(nh);
+  for (int g = 0; g < nh; ++g) {
+    float* orow = dq + ((static_cast<int64_t>(bi) * Hq + h0 + g) * nq + row) * D;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+        *reinterpret_cast<float4*>(orow + 32 * db + 8 * a4 + 4 * hl) =
+            make_float4(acc[db][4 * a4] * f, acc[db][4 * a4 + 1] * f, acc[db][4 * a4 + 2] * f,
+                        acc[db][4 * a4 + 3] * f);
+  }
+}
+
+// ---------------------------------------------------------------- candidates
+template <int D>
+struct SbCandSmem {
+  static constexpr int kTPitch = kST + 8;
+  __bf16 qt[4][D * kTPitch];               // per wave: q_hat^T of its row tile
+  float dgt[4][32][kST + 4];               // per wave: dg of (row, candidate)
+  float2 rs[4][32];                        // per wave: (lse2, sum_S p dg) per row
+  float red[kST * D];                      // cross-wave sum
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void select_bwd_cands_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ kbar, int Hq, int Hkv, int Hsel, int nq,
+    int64_t q_pos0, int64_t ccap, int64_t ncap, int b, int share_group, int K,
+    const int32_t* __restrict__ idx, const float* __restrict__ dg, const float2* __restrict__ ws_row,
+    float* __restrict__ dkbar) {
+  __shared__ SbCandSmem<D> sm;
+  constexpr int kKS = D / 16;
+  constexpr int kDB = D / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, ql = lane & 31;
+  const int c0 = blockIdx.x * kST;                 // this candidate tile
+  const int bkv = blockIdx.y;
+  const int bi = bkv / Hkv, kvh = bkv % Hkv;
+  const int G = Hq / Hkv;
+  const int nsel = share_group ? 1 : G;            // selection heads reading this kv head
+  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+  const float scale2 = scale * kSLog2e;
+  const __bf16* kb = kbar + (static_cast<int64_t>(bi) * Hkv + kvh) * ccap * D;
+  const int myc = c0 + ql;                         // this lane's candidate
+  const int lb = __builtin_ctz(b);                 // b is a power of two
+  // B operand Kbar^T: lane = candidate, k-slice 16 ks + 8 hl .. +7
+  uint4 kreg[kKS];
+  {
+    const int cc = myc < ncap ? myc : static_cast<int>(ncap) - 1;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks)
+      kreg[ks] = *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(cc) * D + 16 * ks + 8 * hl);
+  }
+  sbfloatx16_t acc[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  uint16_t* tw = reinterpret_cast<uint16_t*>(sm.qt[wave]);
+  // rows that have candidate c0 as a candidate: pos >= (c0 + 1) b
+  int64_t r0 = (c0 + 1) * static_cast<int64_t>(b) - q_pos0;
+  r0 = r0 < 0 ? 0 : r0;
+  const int ntile = r0 < nq ? static_cast<int>((nq - r0 + 31) / 32) : 0;
+  for (int sh = 0; sh < nsel; ++sh) {
+    const int hs = share_group ? kvh : kvh * G + sh;
+    const int nh = share_group ? G : 1;
+    const int h0 = share_group ? kvh * G : hs;
+    for (int rt = wave; rt < ntile; rt += 4) {
+      const int e0 = static_cast<int>(r0) + rt * 32;
+      // per-row scalars and the dg table of this row tile (lane ql = tile row)
+      const int er = e0 + ql;
+      const bool rok = er < nq;
+      const int64_t sr = ((static_cast<int64_t>(bi) * Hsel + hs) * nq + (rok ? er : nq - 1));
+      if (hl == 0) sm.rs[wave][ql] = rok ? ws_row[sr] : make_float2(0.f, 0.f);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sm.dgt[wave][ql][16 * hl + e] = 0.f;
+      wave_lds_sync();
+      if (rok) {
+        const int nc = static_cast<int>((q_pos0 + er) >> lb);
+        for (int t = hl; t < K; t += 2) {
+          const int c = idx[sr * K + t];
+          if (c >= c0 && c < c0 + kST && c < nc) sm.dgt[wave][ql][c - c0] = dg[sr * K + t];
+        }
+      }
+      // A operand: q_hat rows pi(ql) (rows past nq are zero); also q_hat^T into LDS
+      const int ea = e0 + sb_perm(ql);
+      uint4 qa[kKS];
+      if (ea < nq) {
+        const __bf16* q0 = q + ((static_cast<int64_t>(bi) * Hq + h0) * nq + ea) * D;
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) qa[ks] = qhat8(q0, static_cast<int64_t>(nq) * D, nh, 2 * ks + hl);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) qa[ks] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks)
+        sb_store_t8(tw + (16 * ks + 8 * hl) * SbCandSmem<D>::kTPitch + sb_perm(ql), SbCandSmem<D>::kTPitch, qa[ks]);
+      wave_lds_sync();
+      // S = q_hat Kbar^T: lane = candidate, register r = tile row sb_elem(r, hl)
+      sbfloatx16_t s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sb_bf16x8(qa[ks]), sb_bf16x8(kreg[ks]), s, 0, 0, 0);
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = sb_elem(r, hl);
+        const int er2 = e0 + m;
+        const bool cand = er2 < nq && myc < ((q_pos0 + er2) >> lb);
+        const float2 rsv = sm.rs[wave][m];
+        const float p = cand ? __builtin_amdgcn_exp2f(s[r] * scale2 - rsv.x) : 0.f;
+        ds[r] = p * (sm.dgt[wave][m][ql] - rsv.y);
+      }
+      // dKbar += dS^T q_hat: B = q_hat (lane: d = 32 db + ql, k-slice rows 16 s2 + 8 hl .. +7)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const uint4 pa = sb_pack8(&ds[8 * s2]);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const uint4 bt = *reinterpret_cast<const uint4*>(tw + (32 * db + ql) * SbCandSmem<D>::kTPitch + 16 * s2 + 8 * hl);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sb_bf16x8(pa), sb_bf16x8(bt), acc[db], 0, 0, 0);
+        }
+      }
+      wave_lds_sync();
+    }
+  }
+  // waves' sums in wave order; register r of block db holds candidate
+  // 8 (r / 4) + 4 hl + (r % 4), column d = 32 db + ql
+  __syncthreads();
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 8 * (r >> 2) + 4 * hl + (r & 3);
+          float* p = &sm.red[c * D + 32 * db + ql];
+          *p = (w == 0) ? acc[db][r] : *p + acc[db][r];
+        }
+    }
+    __syncthreads();
+  }
+  for (int x = tid; x < kST * D; x += 256) {
+    const int c = x / D, e = x % D;
+    if (c0 + c < ccap) dkbar[((static_cast<int64_t>(bi) * Hkv + kvh) * ccap + c0 + c) * D + e] = sm.red[x] * scale;
+  }
+}
+
+// ---------------------------------------------------------------- launch
+size_t select_bwd_workspace_bytes(const SelectLaunch& p) {
+  return align256(static_cast<size_t>(p.B) * p.Hsel * p.nq * sizeof(float2));
+}
+
+template <int D>
+static hipError_t launch_select_bwd_d(const SelectLaunch& p, const float* dg, float* dq, float* dkbar, void* ws,
+                                      hipStream_t st) {
+  float2* ws_row = static_cast<float2*>(ws);
+  hipError_t e = launch(false, select_bwd_rows_kernel<D>, dim3((p.nq + 127) / 128, static_cast<unsigned>(p.B * p.Hsel)),
+                        dim3(256), st, static_cast<const __bf16*>(p.q), static_cast<const __bf16*>(p.kbar), p.Hq,
+                        p.Hkv, p.Hsel, p.nq, p.q_pos0, p.ccap, p.b, p.share_group, p.K, p.idx, dg, dq, ws_row);
+  if (e != hipSuccess) return e;
+  // candidate tiles cover every summary slot (slots that are no row's
+  // candidate get zero gradient)
+  const int ntile = static_cast<int>((p.ccap + kST - 1) / kST);
+  return launch(true, select_bwd_cands_kernel<D>, dim3(ntile, static_cast<unsigned>(p.B * p.Hkv)), dim3(256), st,
+                static_cast<const __bf16*>(p.q), static_cast<const __bf16*>(p.kbar), p.Hq, p.Hkv, p.Hsel, p.nq,
+                p.q_pos0, p.ccap, p.ccap, p.b, p.share_group, p.K, p.idx, dg, ws_row, dkbar);
+}
+
+hipError_t launch_select_bwd(const SelectLaunch& p, const float* dg, float* dq, float* dkbar, void* ws,
+                             hipStream_t st) {
+  return p.d == 64 ? launch_select_bwd_d<64>(p, dg, dq, dkbar, ws, st)
+                   : launch_select_bwd_d<128>(p, dg, dq, dkbar, ws, st);
+}
+
+}  // namespace spa

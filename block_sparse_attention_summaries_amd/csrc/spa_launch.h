@@ -114,11 +114,14 @@ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 
 
 size_t select_workspace_bytes(const SelectLaunch& p);
+size_t select_bwd_workspace_bytes(const SelectLaunch& p);
 size_t attn_fwd_workspace_bytes(const AttnLaunch& p);
 size_t attn_bwd_workspace_bytes(const BwdLaunch& p);
 
 hipError_t launch_block_summaries(const SummaryLaunch& p, hipStream_t st);
 hipError_t launch_score_select(const SelectLaunch& p, void* ws, hipStream_t st);
+hipError_t launch_select_bwd(const SelectLaunch& p, const float* dg, float* dq, float* dkbar, void* ws,
+                             hipStream_t st);
 bool rows_select_mfma_supported(const SelectLaunch& p);
 hipError_t launch_rows_select_mfma(const SelectLaunch& p, hipStream_t st);
 hipError_t launch_attn_fwd(const AttnLaunch& p, void* ws, hipStream_t st);

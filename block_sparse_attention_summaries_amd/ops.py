@@ -6,7 +6,7 @@ There is no fallback: if the library is missing or its call fails, these
 functions raise.
 
 Function names match the C entry points: sparse_block_summaries,
-sparse_score_select, sparse_attn_fwd, sparse_attn_bwd.
+sparse_score_select, sparse_attn_fwd, sparse_attn_bwd, sparse_select_bwd.
 """
 from __future__ import annotations
 
@@ -23,10 +23,11 @@ SPA_DTYPE_F32, SPA_DTYPE_BF16 = 0, 1
 SPA_PREFIX_CURRENT_BLOCK, SPA_PREFIX_QUERY_BLOCK = 0, 1
 SPA_GATE_NONE, SPA_GATE_SOFTMAX_LOG = 0, 1
 SPA_LOCAL_CURRENT_BLOCK, SPA_LOCAL_NONE = 0, 1
-SPA_OP_SCORE_SELECT, SPA_OP_ATTN_FWD, SPA_OP_ATTN_BWD = 1, 2, 3
+SPA_OP_SCORE_SELECT, SPA_OP_ATTN_FWD, SPA_OP_ATTN_BWD, SPA_OP_SELECT_BWD = 1, 2, 3, 4
 
 EXPORTED = ["spa_abi_version", "spa_profile_next_call", "spa_last_error", "sparse_block_summaries", "sparse_score_select",
-            "sparse_attn_fwd", "sparse_attn_bwd", "sparse_workspace_bytes", "sparse_workspace_init"]
+            "sparse_attn_fwd", "sparse_attn_bwd", "sparse_select_bwd", "sparse_workspace_bytes",
+            "sparse_workspace_init"]
 
 _vp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
 
@@ -79,6 +80,8 @@ def lib():
         L.sparse_attn_bwd.restype = _i
         L.sparse_attn_bwd.argtypes = [ctypes.POINTER(AttnArgs), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _sz, _vp]
+        L.sparse_select_bwd.restype = _i
+        L.sparse_select_bwd.argtypes = [ctypes.POINTER(SelectArgs), _vp, _vp, _vp, _vp, _sz, _vp]
         L.sparse_workspace_bytes.restype = _sz
         L.sparse_workspace_bytes.argtypes = [_i, _vp]
         L.sparse_workspace_init.restype = _i
@@ -240,3 +243,19 @@ def sparse_attn_bwd(q, k, v, idx, logg, o, dout, lse, *, dq=None, dk=None, dv=No
     _check(lib().sparse_attn_bwd(ctypes.byref(a), _p(o), _p(dout), _p(lse), _p(dq), _p(dk), _p(dv),
                                  _p(dg), _p(buf), size, _stream(stream)))
     return dq, dk, dv, dg
+
+
+def sparse_select_bwd(q, kbar, max_norm, centre, idx, logg, dg, *, dq=None, dkbar=None, workspace=None,
+                      stream=None, **kw):
+    """Selector side of the backward: dg [B,Hsel,nq,K] (from sparse_attn_bwd)
+    through log g = s - LSE(s) into q and kbar.  Takes the arguments of the
+    sparse_score_select call that produced idx / logg.  Returns (dq, dkbar),
+    both fp32."""
+    _contig(dg, dq, dkbar)
+    a, _ = select_args(q, kbar, max_norm, centre, idx=idx, logg=logg, **kw)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
+    dkbar = torch.empty(kbar.shape, dtype=torch.float32, device=q.device) if dkbar is None else dkbar
+    buf, size = _ws(workspace, SPA_OP_SELECT_BWD, a, q.device)
+    _check(lib().sparse_select_bwd(ctypes.byref(a), _p(dg), _p(dq), _p(dkbar), _p(buf), size,
+                                   _stream(stream)))
+    return dq, dkbar

@@ -85,7 +85,9 @@ typedef enum { SPA_DTYPE_F32 = 0, SPA_DTYPE_BF16 = 1 } spa_dtype;
 typedef enum { SPA_PREFIX_CURRENT_BLOCK = 0, SPA_PREFIX_QUERY_BLOCK = 1 } spa_prefix_mode;
 typedef enum { SPA_GATE_NONE = 0, SPA_GATE_SOFTMAX_LOG = 1 } spa_gate;
 typedef enum { SPA_LOCAL_CURRENT_BLOCK = 0, SPA_LOCAL_NONE = 1 } spa_local;
-typedef enum { SPA_OP_SCORE_SELECT = 1, SPA_OP_ATTN_FWD = 2, SPA_OP_ATTN_BWD = 3 } spa_op;
+typedef enum {
+    SPA_OP_SCORE_SELECT = 1, SPA_OP_ATTN_FWD = 2, SPA_OP_ATTN_BWD = 3, SPA_OP_SELECT_BWD = 4
+} spa_op;
 
 /* Version of this ABI (SPA_ABI_VERSION). */
 int spa_abi_version(void);
@@ -218,8 +220,34 @@ int sparse_attn_bwd(const spa_attn_args *a, const void *o, const void *dout,
                     const float *lse, void *dq, void *dk, void *dv, float *dg,
                     void *workspace, size_t ws_bytes, spa_stream_t stream);
 
+/*
+ * sparse_select_bwd -- selector side of the backward: the gate gradient dg
+ * (as written by sparse_attn_bwd) carried back through log g = s - LSE(s)
+ * into the query and the block summaries ("SAS" review, "How it works"
+ * step 5: the loss reaches the selector only through the gates; §4.2.2
+ * softmax gate; §3 Eq. 3 scores).  With p = softmax(s) over all candidates
+ * of a row (so g_m = p_m) and its selected set S held fixed:
+ *   ds_c   = p_c ([c in S] dg_c - sum_{m in S} p_m dg_m),
+ *   dq     = sum_c ds_c kbar_c / sqrt(d), given to each of the G query heads
+ *            of a shared selection as dq_hat / G (q_hat is their mean),
+ *   dkbar_c = sum over rows and selection heads of ds_c q_hat / sqrt(d).
+ * `a` is the argument struct of the sparse_score_select call that produced
+ * idx, validated the same way (its outputs logg and k_eff are not read).  Supported: bf16, gate = SOFTMAX_LOG,
+ * prefix_mode = CURRENT_BLOCK, no projection, no erf term; otherwise
+ * SPA_ERR_UNSUPPORTED.  dg: fp32 [B, Hsel, nq, K] (entries of slots that are
+ * not candidates of their row are ignored).  Outputs, written not
+ * accumulated, fp32, 16-byte aligned: dq [B, Hq, nq, d]; dkbar
+ * [B, Hkv, ccap, d] (0 for summaries that are no row's candidate).  Scores
+ * are recomputed from q_hat rounded to bf16.  Needs a workspace of
+ * sparse_workspace_bytes(SPA_OP_SELECT_BWD); caller-owned, contents on entry
+ * are ignored.
+ */
+int sparse_select_bwd(const spa_select_args *a, const float *dg, float *dq, float *dkbar,
+                      void *workspace, size_t ws_bytes, spa_stream_t stream);
+
 /* Workspace bytes needed by `op` (spa_op) for the given argument struct
- * (spa_select_args* for SPA_OP_SCORE_SELECT, spa_attn_args* otherwise).
+ * (spa_select_args* for SPA_OP_SCORE_SELECT and SPA_OP_SELECT_BWD,
+ * spa_attn_args* otherwise).
  * Returns 0 for invalid arguments (see spa_last_error()). */
 size_t sparse_workspace_bytes(int op, const void *args);
 

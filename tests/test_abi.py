@@ -137,6 +137,24 @@ def test_bwd_rejects_unsupported_modes():
                                None) == ops.SPA_ERR_INVALID_ARG
 
 
+def test_select_bwd_rejects_unsupported_modes():
+    lib = ops.lib()
+    def st(a, dg=FAKE, dq=FAKE, dk=FAKE):
+        return lib.sparse_select_bwd(ctypes.byref(a), dg, dq, dk, FAKE, 1 << 20, None)
+    base = dict(nq=8192, q_pos0=0, ccap=128)
+    assert st(_sel(**base, gate=0, logg=None)) == ops.SPA_ERR_UNSUPPORTED
+    assert st(_sel(**base, dtype=0)) == ops.SPA_ERR_UNSUPPORTED
+    assert st(_sel(**base, prefix_mode=1, qblock=128)) == ops.SPA_ERR_UNSUPPORTED
+    assert st(_sel(**base, proj_w=FAKE)) == ops.SPA_ERR_UNSUPPORTED
+    assert st(_sel(**base), dg=None) == ops.SPA_ERR_INVALID_ARG
+    assert st(_sel(**base), dq=FAKE_ODD) == ops.SPA_ERR_INVALID_ARG
+    a = _sel(**base)
+    # one (LSE, sum_S p dg) pair per (batch, selection head, row)
+    need = lib.sparse_workspace_bytes(ops.SPA_OP_SELECT_BWD, ctypes.byref(a))
+    assert need == 8 * 8192 * 8
+    assert lib.sparse_select_bwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, need - 1, None) == ops.SPA_ERR_WORKSPACE
+
+
 def test_summaries_rejects_invalid_arguments():
     lib = ops.lib()
     f = lib.sparse_block_summaries
