@@ -81,7 +81,7 @@ def _declare(lib):
                                  P, P, I64, P, P]
     lib.orc_attn_fwd.restype = None
     lib.orc_select_bwd.restype = None
-    lib.orc_select_bwd.argtypes = [P, I, I, I, I, I, I, I64, P, I, I64, I, I, I, P, P, P, P]
+    lib.orc_select_bwd.argtypes = [P, I, I, I, I, I, I, I64, P, I, I64, I, I, I, P, P, P, P, P, P]
     lib.orc_attn_bwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I64, I64, I, P, P, I, I, I64,
                                  P, P, P, P]
     lib.orc_attn_bwd.restype = None
@@ -240,19 +240,38 @@ def attn_bwd(q, k, v, dout, idx, logg, *, b, K, q_pos0, share_group=True, kv_sli
     return dq, dk, dv, dg
 
 
-def select_bwd(q, kbar, idx, dg, *, Hkv, b, K, q_pos0, share_group=True):
+def select_bwd(q, kbar, idx, dg, *, Hkv, b, K, q_pos0, share_group=True, proj_w=None):
     """Selector-side backward: the gate gradient dg [B, Hsel, nq, K] (w.r.t. g)
     through log g = s - LSE(s) into q (dq [B, Hq, nq, d]) and the block
     summaries (dkbar [B, Hkv, ccap, d]), fp64.  Current-block candidates, no
-    projection and no erf term."""
+    erf term.  With the projection proj_w [d, d] (fp32, ktilde = W kbar) also
+    returns dW [d, d]: (dq, dkbar, dW)."""
     lib = _load()
     B, Hq, nq, d = q.shape
     ccap = kbar.shape[2]
     dq = np.zeros((B, Hq, nq, d), np.float64)
     dkbar = np.zeros((B, Hkv, ccap, d), np.float64)
+    dW = np.zeros((d, d), np.float64)
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     dg = np.ascontiguousarray(dg, dtype=np.float64)
+    W = None if proj_w is None else np.ascontiguousarray(proj_w, dtype=np.float32)
     lib.orc_select_bwd(_ptr(q), _dtype_code(q), B, Hq, Hkv, nq, d, int(q_pos0), _ptr(kbar),
-                       _dtype_code(kbar), ccap, b, int(bool(share_group)), K, _ptr(idx), _ptr(dg),
-                       _ptr(dq), _ptr(dkbar))
-    return dq, dkbar
+                       _dtype_code(kbar), ccap, b, int(bool(share_group)), K, _ptr(W), _ptr(idx),
+                       _ptr(dg), _ptr(dq), _ptr(dkbar), _ptr(dW))
+    if W is None:
+        return dq, dkbar
+    return dq, dkbar, dW
+
+
+def mean_bwd(dkbar, b, L):
+    """Gradient of the block mean kbar_c = (1/b) sum_{j in block c} k_j with
+    respect to the keys ([SAS] §3, the mean-key summary): dk_j = dkbar_c / b
+    for each token j of block c < ccap, 0 for tokens past ccap * b.  fp64
+    [B, Hkv, L, d].  The rounding of kbar to the key dtype is passed straight
+    through."""
+    B, Hkv, ccap, d = dkbar.shape
+    assert ccap * b <= L
+    dk = np.zeros((B, Hkv, L, d), np.float64)
+    for c in range(ccap):
+        dk[:, :, c * b:(c + 1) * b, :] = np.asarray(dkbar[:, :, c:c + 1, :], np.float64) / b
+    return dk

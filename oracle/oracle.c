@@ -697,29 +697,52 @@ void orc_attn_bwd(const void *q, const void *k, const void *v, const void *dout,
  * respect to log g_m) and p = softmax(s) over the candidates (so g_m = p_m).
  * Then
  *   ds_c = [c in S] dl_c - p_c sum_{m in S} dl_m
- *   dq_hat = sum_c ds_c kbar_c / sqrt(d),   dkbar_c += ds_c q_hat / sqrt(d),
+ *   dq_hat = sum_c ds_c ktilde_c / sqrt(d),   dktilde_c += ds_c q_hat / sqrt(d),
  * and each of the G query heads averaged into q_hat receives dq_hat / G.
- * Scores are recomputed here in fp64 (orc_scores_row, no projection, no erf
- * term); idx is the forward's selection, dg is [B, Hsel, nq, K] (padded slots
- * ignored).  Outputs (fp64, written): dq [B, Hq, nq, d], dkbar [B, Hkv, Ccap, d].
+ * ktilde = kbar, or W kbar with the learned projection ("SAS" review, the
+ * 128 -> 128 projection of the mean keys); then dkbar_c = W^T dktilde_c and
+ * dW = sum over (batch, kv head, summary) of dktilde_c kbar_c^T.
+ * Scores are recomputed here in fp64 (orc_scores_row, no erf term); idx is
+ * the forward's selection, dg is [B, Hsel, nq, K] (padded slots ignored).
+ * Outputs (fp64, written): dq [B, Hq, nq, d], dkbar [B, Hkv, Ccap, d], and
+ * dW [d, d] when proj_w is given (summed over the (batch, kv head) tasks in
+ * task order).
  */
 void orc_select_bwd(const void *q, int qdtype, int B, int Hq, int Hkv, int nq, int d,
                     int64_t q_pos0, const void *kbar, int kdtype, int64_t Ccap, int b,
-                    int share_group, int K, const int32_t *idx, const double *dg,
-                    double *dq, double *dkbar)
+                    int share_group, int K, const float *proj_w, const int32_t *idx,
+                    const double *dg, double *dq, double *dkbar, double *dW)
 {
     const int G = Hq / Hkv;
     const int Hsel = share_group ? Hkv : Hq;
     const double scale = 1.0 / sqrt((double)d);
+    const int ntask = B * Hkv;
     memset(dq, 0, sizeof(double) * (size_t)B * Hq * nq * d);
     memset(dkbar, 0, sizeof(double) * (size_t)B * Hkv * Ccap * d);
+    /* per-task partial dW, summed in task order below */
+    double *dw_part = proj_w ? (double *)calloc((size_t)ntask * d * d, sizeof(double)) : NULL;
     /* one task per (batch, kv head): it owns dkbar of that head */
 #pragma omp parallel for schedule(dynamic, 1) num_threads(orc_num_threads())
-    for (int t = 0; t < B * Hkv; ++t) {
+    for (int t = 0; t < ntask; ++t) {
         const int bidx = t / Hkv, kvh = t % Hkv;
+        const int64_t kb0 = ((int64_t)bidx * Hkv + kvh) * Ccap;
         double *s = (double *)malloc(sizeof(double) * (size_t)(Ccap > 0 ? Ccap : 1));
         double *ds = (double *)malloc(sizeof(double) * (size_t)(Ccap > 0 ? Ccap : 1));
         double *qh = (double *)malloc(sizeof(double) * (size_t)d);
+        /* the summaries as the scores see them, and their gradient */
+        double *kt = (double *)malloc(sizeof(double) * (size_t)(Ccap > 0 ? Ccap : 1) * d);
+        double *dkt = (double *)calloc((size_t)(Ccap > 0 ? Ccap : 1) * d, sizeof(double));
+        for (int64_t c = 0; c < Ccap; ++c)
+            for (int e = 0; e < d; ++e) {
+                double acc = 0.0;
+                if (proj_w) {
+                    for (int f = 0; f < d; ++f)
+                        acc += (double)proj_w[e * d + f] * orc_load(kbar, kdtype, (kb0 + c) * d + f);
+                } else {
+                    acc = orc_load(kbar, kdtype, (kb0 + c) * d + e);
+                }
+                kt[c * d + e] = acc;
+            }
         const int hs0 = share_group ? kvh : kvh * G;
         const int hs1 = share_group ? kvh + 1 : kvh * G + G;
         for (int hs = hs0; hs < hs1; ++hs) {
@@ -731,7 +754,7 @@ void orc_select_bwd(const void *q, int qdtype, int B, int Hq, int Hkv, int nq, i
                 if (ncand <= 0)
                     continue;
                 orc_scores_row(q, qdtype, Hq, Hkv, nq, d, bidx, hs, row, pos, kbar, kdtype, NULL,
-                               NULL, Ccap, share_group, NULL, NULL, NULL, ncand, s);
+                               NULL, Ccap, share_group, proj_w, NULL, NULL, ncand, s);
                 double mx = s[0];
                 for (int64_t c = 1; c < ncand; ++c)
                     if (s[c] > mx)
@@ -767,11 +790,10 @@ void orc_select_bwd(const void *q, int qdtype, int B, int Hq, int Hkv, int nq, i
                     for (int e = 0; e < d; ++e)
                         qh[e] = orc_load(q, qdtype, (((int64_t)bidx * Hq + hs) * nq + row) * d + e);
                 }
-                const int64_t kb0 = ((int64_t)bidx * Hkv + kvh) * Ccap;
                 for (int e = 0; e < d; ++e) {
                     double acc = 0.0;
                     for (int64_t c = 0; c < ncand; ++c)
-                        acc += ds[c] * orc_load(kbar, kdtype, (kb0 + c) * d + e);
+                        acc += ds[c] * kt[c * d + e];
                     acc *= scale;
                     if (share_group) {
                         for (int g = 0; g < G; ++g)
@@ -782,11 +804,37 @@ void orc_select_bwd(const void *q, int qdtype, int B, int Hq, int Hkv, int nq, i
                 }
                 for (int64_t c = 0; c < ncand; ++c)
                     for (int e = 0; e < d; ++e)
-                        dkbar[(kb0 + c) * d + e] += ds[c] * qh[e] * scale;
+                        dkt[c * d + e] += ds[c] * qh[e] * scale;
+            }
+        }
+        for (int64_t c = 0; c < Ccap; ++c) {
+            if (proj_w) {
+                for (int f = 0; f < d; ++f) {
+                    double acc = 0.0;
+                    for (int e = 0; e < d; ++e)
+                        acc += (double)proj_w[e * d + f] * dkt[c * d + e];
+                    dkbar[(kb0 + c) * d + f] = acc;
+                }
+                for (int e = 0; e < d; ++e)
+                    for (int f = 0; f < d; ++f)
+                        dw_part[((size_t)t * d + e) * d + f] +=
+                            dkt[c * d + e] * orc_load(kbar, kdtype, (kb0 + c) * d + f);
+            } else {
+                for (int e = 0; e < d; ++e)
+                    dkbar[(kb0 + c) * d + e] = dkt[c * d + e];
             }
         }
         free(s);
         free(ds);
         free(qh);
+        free(kt);
+        free(dkt);
+    }
+    if (proj_w) {
+        memset(dW, 0, sizeof(double) * (size_t)d * d);
+        for (int t = 0; t < ntask; ++t)
+            for (int e = 0; e < d * d; ++e)
+                dW[e] += dw_part[(size_t)t * d * d + e];
+        free(dw_part);
     }
 }
