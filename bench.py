@@ -334,12 +334,13 @@ def run_train(reps):
         ev[1].record()
         o, lse = ops.sparse_attn_fwd(q, k, v, idx, logg, b=b, K=K, q_pos0=0, workspace=ws[1])
         ev[2].record()
-        _, _, _, dg = ops.sparse_attn_bwd(q, k, v, idx, logg, o, do, lse, b=b, K=K, q_pos0=0,
+        _, dk, _, dg = ops.sparse_attn_bwd(q, k, v, idx, logg, o, do, lse, b=b, K=K, q_pos0=0,
                                           workspace=ws[2])
         ev[3].record()
-        # selector side: dg through the gate into q and the summaries
-        ops.sparse_select_bwd(q, kb, mx, ce, idx, logg, dg, Hkv=cfg["Hkv"], b=b, K=K, q_pos0=0, gate=True,
-                              workspace=ws[3])
+        # selector side: dg through the gate into q and the summaries, and
+        # through the block means into dk
+        ops.sparse_select_bwd(q, kb, mx, ce, idx, logg, dg, dk=dk, Hkv=cfg["Hkv"], b=b, K=K, q_pos0=0,
+                              gate=True, workspace=ws[3])
         ev[4].record()
         torch.cuda.synchronize()
         return [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]

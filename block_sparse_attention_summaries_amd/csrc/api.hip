@@ -147,17 +147,27 @@ int check_bwd(const spa_attn_args* a, const void* o, const void* dout, const flo
   return SPA_OK;
 }
 
-int check_select_bwd(const spa_select_args* a, const float* dg, float* dq, float* dkbar, spa::SelectLaunch* p) {
+int check_select_bwd(const spa_select_args* a, const spa_select_grads* g, spa::SelectLaunch* p,
+                     spa::SelectGrads* sg) {
   int st = check_select(a, p);
   if (st != SPA_OK) return st;
   SPA_REQUIRE(a->gate == SPA_GATE_SOFTMAX_LOG, SPA_ERR_UNSUPPORTED,
               "the selector backward needs the softmax log gate (gate = SOFTMAX_LOG)");
-  SPA_REQUIRE(a->prefix_mode == SPA_PREFIX_CURRENT_BLOCK && a->proj_w == nullptr && a->erf_lambda == nullptr,
-              SPA_ERR_UNSUPPORTED,
-              "the selector backward supports current-block candidates without projection or erf term");
+  SPA_REQUIRE(a->prefix_mode == SPA_PREFIX_CURRENT_BLOCK && a->erf_lambda == nullptr, SPA_ERR_UNSUPPORTED,
+              "the selector backward supports current-block candidates without the erf term");
   SPA_REQUIRE(a->dtype == SPA_DTYPE_BF16, SPA_ERR_UNSUPPORTED, "the selector backward supports bf16 only");
-  SPA_REQUIRE(dg && dq && dkbar, SPA_ERR_INVALID_ARG, "dg, dq and dkbar must be non-NULL");
-  SPA_REQUIRE(aligned16(dq) && aligned16(dkbar), SPA_ERR_INVALID_ARG, "dq and dkbar must be 16-byte aligned");
+  SPA_REQUIRE(g != nullptr && g->dg && g->dq && g->dkbar, SPA_ERR_INVALID_ARG,
+              "grads, dg, dq and dkbar must be non-NULL");
+  SPA_REQUIRE(aligned16(g->dq) && aligned16(g->dkbar), SPA_ERR_INVALID_ARG, "dq and dkbar must be 16-byte aligned");
+  SPA_REQUIRE((a->proj_w != nullptr) == (g->dproj_w != nullptr), SPA_ERR_INVALID_ARG,
+              "dproj_w must be given exactly when the projection proj_w is");
+  if (g->dk != nullptr) {
+    SPA_REQUIRE(aligned16(g->dk), SPA_ERR_INVALID_ARG, "dk must be 16-byte aligned");
+    SPA_REQUIRE(g->L >= a->ccap * a->b, SPA_ERR_INVALID_ARG,
+                "dk holds L = %lld tokens but the summaries cover ccap * b = %lld", static_cast<long long>(g->L),
+                static_cast<long long>(a->ccap * a->b));
+  }
+  *sg = spa::SelectGrads{g->dg, g->dq, g->dkbar, g->dproj_w, g->dk, g->L};
   return SPA_OK;
 }
 
@@ -243,15 +253,16 @@ int sparse_attn_bwd(const spa_attn_args* a, const void* o, const void* dout, con
   return hip_status(spa::launch_attn_bwd(p, workspace, static_cast<hipStream_t>(stream)), "sparse_attn_bwd");
 }
 
-int sparse_select_bwd(const spa_select_args* a, const float* dg, float* dq, float* dkbar, void* workspace,
-                      size_t ws_bytes, spa_stream_t stream) {
+int sparse_select_bwd(const spa_select_args* a, const spa_select_grads* g, void* workspace, size_t ws_bytes,
+                      spa_stream_t stream) {
   ProfileScope profile_scope;
   spa::SelectLaunch p;
-  int st = check_select_bwd(a, dg, dq, dkbar, &p);
+  spa::SelectGrads sg;
+  int st = check_select_bwd(a, g, &p, &sg);
   if (st != SPA_OK) return st;
   st = check_ws(workspace, ws_bytes, spa::select_bwd_workspace_bytes(p));
   if (st != SPA_OK) return st;
-  return hip_status(spa::launch_select_bwd(p, dg, dq, dkbar, workspace, static_cast<hipStream_t>(stream)),
+  return hip_status(spa::launch_select_bwd(p, sg, workspace, static_cast<hipStream_t>(stream)),
                     "sparse_select_bwd");
 }
 

@@ -1,23 +1,34 @@
 // select_bwd.hip -- selector-side backward (bf16, gfx950 MFMA): the gate
-// gradient dg carried back through log g = s - LSE(s) into the query and the
-// block summaries ("SAS" review, "How it works", step 5: the loss reaches the
-// selector through g; §4.2.2 softmax gate; §4.3 Eq. 9).  With p = softmax(s)
-// over a row's candidates (so g_m = p_m) and its selection S fixed:
+// gradient dg carried back through log g = s - LSE(s) into the query, the
+// block summaries, the learned projection and the keys ("SAS" review, "How it
+// works", step 5: the loss reaches the selector through g; §4.2.2 softmax
+// gate; §4.3 Eq. 9; §3 mean-key summaries).  With p = softmax(s) over a
+// row's candidates (so g_m = p_m) and its selection S fixed:
 //   ds_c = p_c ([c in S] dg_c - sum_{m in S} p_m dg_m),
-//   dq_hat = sum_c ds_c kbar_c / sqrt(d)   (each head of a shared selection
+//   dq_hat = sum_c ds_c ktilde_c / sqrt(d)   (each head of a shared selection
 //            receives dq_hat / G),
-//   dkbar_c = sum_rows ds_c q_hat / sqrt(d).
-// Scores are recomputed from q_hat rounded to bf16 (a gradient needs ~1e-3,
-// not the ranking accuracy of the forward selection).
+//   dktilde_c = sum_rows ds_c q_hat / sqrt(d),
+// with ktilde = kbar, or W kbar under the projection.  The projection is
+// moved to the query side, where it is exact on the bf16 summaries: with
+// u = W^T q_hat the scores are u . kbar / sqrt(d), dkbar_c = W^T dktilde_c =
+// sum_rows ds_c u / sqrt(d), and with r = sum_c ds_c kbar_c / sqrt(d) per row,
+// dq_hat = W r and dW = sum_rows q_hat r^T.  Optionally dk_j += dkbar_c / b
+// for every token of block c (the summary is the block mean).
+// Scores are recomputed from q_hat (or u) rounded to bf16 (a gradient needs
+// ~1e-3, not the ranking accuracy of the forward selection).
 //
-// Two launches:
+// Launches:
 //   rows        4 waves x 32 rows of one selection head; pass 1 over the
 //               candidate tiles gives each row's LSE and sum_S p dg (saved to
-//               the workspace), pass 2 accumulates dq_hat^T += Kbar^T dS^T;
+//               the workspace), pass 2 accumulates dq_hat^T (or r^T) +=
+//               Kbar^T dS^T;
 //   candidates  one 32-candidate tile per workgroup; the four waves take the
 //               later rows 32 at a time, S = Q_hat Kbar^T puts one candidate
 //               per lane, dKbar += dS^T Q_hat, and the waves' sums are added in
-//               wave order.
+//               wave order;
+//   projection  U = Q_hat W before, dQ = R W^T and dW = Q_hat^T R (partial
+//               sums per row chunk, added in chunk order) after;
+//   mean        dk += dkbar / b over the tokens of each summarised block.
 #include "spa_device.h"
 #include "spa_launch.h"
 
@@ -98,9 +109,9 @@ struct SbRowSmem {
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void select_bwd_rows_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ kbar, int Hq, int Hkv, int Hsel, int nq,
-    int64_t q_pos0, int64_t ccap, int b, int share_group, int K, const int32_t* __restrict__ idx,
-    const float* __restrict__ dg, float* __restrict__ dq, float2* __restrict__ ws_row) {
+    const __bf16* __restrict__ q, int qHeads, int nh_in, const __bf16* __restrict__ kbar, int Hkv, int Hsel,
+    int G, int share_group, int nq, int64_t q_pos0, int64_t ccap, int b, int K, const int32_t* __restrict__ idx,
+    const float* __restrict__ dg, float* __restrict__ out, int outHeads, int nh_out, float2* __restrict__ ws_row) {
   __shared__ SbRowSmem<D> sm;
   constexpr int kKS = D / 16;
   constexpr int kDB = D / 32;
@@ -108,10 +119,9 @@ __global__ __launch_bounds__(256, 2) void select_bwd_rows_kernel(
   const int hl = lane >> 5, ql = lane & 31;
   const int bh = blockIdx.y;
   const int bi = bh / Hsel, hs = bh % Hsel;
-  const int G = Hq / Hkv;
   const int kvh = share_group ? hs : hs / G;
-  const int nh = share_group ? G : 1;
-  const int h0 = share_group ? hs * G : hs;
+  // query source rows: q_hat = mean of heads hs * nh_in .. + nh_in - 1 of q
+  const int h0 = hs * nh_in;
   const int row = (blockIdx.x * 4 + wave) * 32 + ql;
   const bool row_ok = row < nq;
   const int rowc = row_ok ? row : nq - 1;
@@ -128,9 +138,9 @@ __global__ __launch_bounds__(256, 2) void select_bwd_rows_kernel(
   // B operand q_hat^T (lane: row, k-slice 16 ks + 8 hl .. +7)
   uint4 qreg[kKS];
   {
-    const __bf16* q0 = q + ((static_cast<int64_t>(bi) * Hq + h0) * nq + rowc) * D;
+    const __bf16* q0 = q + ((static_cast<int64_t>(bi) * qHeads + h0) * nq + rowc) * D;
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) qreg[ks] = qhat8(q0, static_cast<int64_t>(nq) * D, nh, 2 * ks + hl);
+    for (int ks = 0; ks < kKS; ++ks) qreg[ks] = qhat8(q0, static_cast<int64_t>(nq) * D, nh_in, 2 * ks + hl);
   }
   // staging: 16-byte vectors x and x + 256 of the tile (key x % 32, columns 8 (x / 32) ..)
   constexpr int kLd = kST * D / 8 / 256;
@@ -259,9 +269,10 @@ __global__ __launch_bounds__(256, 2) void select_bwd_rows_kernel(
   }
   if (!row_ok) return;
   // dq_hat^T register r of block db holds d = 32 db + 8 (r / 4) + 4 hl + (r % 4)
-  const float f = scale / static_cast<float>(nh);
-  for (int g = 0; g < nh; ++g) {
-    float* orow = dq + ((static_cast<int64_t>(bi) * Hq + h0 + g) * nq + row) * D;
+  // written to heads hs * nh_out .. + nh_out - 1 of out, each / nh_out
+  const float f = scale / static_cast<float>(nh_out);
+  for (int g = 0; g < nh_out; ++g) {
+    float* orow = out + ((static_cast<int64_t>(bi) * outHeads + hs * nh_out + g) * nq + row) * D;
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
@@ -284,10 +295,9 @@ struct SbCandSmem {
 
 template <int D>
 __global__ __launch_bounds__(256) void select_bwd_cands_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ kbar, int Hq, int Hkv, int Hsel, int nq,
-    int64_t q_pos0, int64_t ccap, int64_t ncap, int b, int share_group, int K,
-    const int32_t* __restrict__ idx, const float* __restrict__ dg, const float2* __restrict__ ws_row,
-    float* __restrict__ dkbar) {
+    const __bf16* __restrict__ q, int qHeads, int nh_in, const __bf16* __restrict__ kbar, int Hkv, int Hsel,
+    int G, int share_group, int nq, int64_t q_pos0, int64_t ccap, int b, int K, const int32_t* __restrict__ idx,
+    const float* __restrict__ dg, const float2* __restrict__ ws_row, float* __restrict__ dkbar) {
   __shared__ SbCandSmem<D> sm;
   constexpr int kKS = D / 16;
   constexpr int kDB = D / 32;
@@ -296,7 +306,6 @@ __global__ __launch_bounds__(256) void select_bwd_cands_kernel(
   const int c0 = blockIdx.x * kST;                 // this candidate tile
   const int bkv = blockIdx.y;
   const int bi = bkv / Hkv, kvh = bkv % Hkv;
-  const int G = Hq / Hkv;
   const int nsel = share_group ? 1 : G;            // selection heads reading this kv head
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const float scale2 = scale * kSLog2e;
@@ -306,7 +315,7 @@ __global__ __launch_bounds__(256) void select_bwd_cands_kernel(
   // B operand Kbar^T: lane = candidate, k-slice 16 ks + 8 hl .. +7
   uint4 kreg[kKS];
   {
-    const int cc = myc < ncap ? myc : static_cast<int>(ncap) - 1;
+    const int cc = myc < ccap ? myc : static_cast<int>(ccap) - 1;
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks)
       kreg[ks] = *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(cc) * D + 16 * ks + 8 * hl);
@@ -323,8 +332,7 @@ __global__ __launch_bounds__(256) void select_bwd_cands_kernel(
   const int ntile = r0 < nq ? static_cast<int>((nq - r0 + 31) / 32) : 0;
   for (int sh = 0; sh < nsel; ++sh) {
     const int hs = share_group ? kvh : kvh * G + sh;
-    const int nh = share_group ? G : 1;
-    const int h0 = share_group ? kvh * G : hs;
+    const int h0 = hs * nh_in;
     for (int rt = wave; rt < ntile; rt += 4) {
       const int e0 = static_cast<int>(r0) + rt * 32;
       // per-row scalars and the dg table of this row tile (lane ql = tile row)
@@ -346,9 +354,9 @@ __global__ __launch_bounds__(256) void select_bwd_cands_kernel(
       const int ea = e0 + sb_perm(ql);
       uint4 qa[kKS];
       if (ea < nq) {
-        const __bf16* q0 = q + ((static_cast<int64_t>(bi) * Hq + h0) * nq + ea) * D;
+        const __bf16* q0 = q + ((static_cast<int64_t>(bi) * qHeads + h0) * nq + ea) * D;
 #pragma unroll
-        for (int ks = 0; ks < kKS; ++ks) qa[ks] = qhat8(q0, static_cast<int64_t>(nq) * D, nh, 2 * ks + hl);
+        for (int ks = 0; ks < kKS; ++ks) qa[ks] = qhat8(q0, static_cast<int64_t>(nq) * D, nh_in, 2 * ks + hl);
       } else {
 #pragma unroll
         for (int ks = 0; ks < kKS; ++ks) qa[ks] = make_uint4(0, 0, 0, 0);
@@ -409,31 +417,265 @@ __global__ __launch_bounds__(256) void select_bwd_cands_kernel(
   }
 }
 
-// ---------------------------------------------------------------- launch
-size_t select_bwd_workspace_bytes(const SelectLaunch& p) {
-  return align256(static_cast<size_t>(p.B) * p.Hsel * p.nq * sizeof(float2));
+// ---------------------------------------------------------------- projection
+// Row-times-matrix for the projection, one selection-head row n = (batch,
+// selection head, row) at a time, the d x d matrix staged in LDS:
+//   kDQ = false: u_n = q_hat_n W  (q_hat = mean of the nh heads hs * nh ..
+//                of q, fp32), written as bf16 U [B, Hsel, nq, d];
+//   kDQ = true:  dq_hat_n = W r_n, written / nh to the nh query heads.
+template <int D, bool kDQ>
+__global__ __launch_bounds__(256) void proj_rows_kernel(const __bf16* __restrict__ q, int Hq, int nh,
+                                                        const float* __restrict__ r, const float* __restrict__ W,
+                                                        int Hsel, int nq, int64_t nrows, int64_t rows_per_wg,
+                                                        __bf16* __restrict__ uout, float* __restrict__ dq) {
+  constexpr int kPitch = D + 1;
+  constexpr int kNR = 16;                       // rows per LDS batch
+  constexpr int kStep = 256 / D;                // row groups per workgroup
+  constexpr int kRPT = kNR / kStep;             // rows per thread and batch
+  __shared__ float ms[D * kPitch];              // kDQ: ms[f][e] = W[e][f]; else ms[e][f] = W[e][f]
+  __shared__ float xs[kNR][D];
+  const int tid = threadIdx.x;
+  const int j = tid % D, rsub = tid / D;
+  for (int x = tid; x < D * D; x += 256) {
+    const int e = x / D, f = x % D;
+    if (kDQ)
+      ms[f * kPitch + e] = W[x];
+    else
+      ms[e * kPitch + f] = W[x];
+  }
+  const int64_t n_begin = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
+  const int64_t n_end = n_begin + rows_per_wg < nrows ? n_begin + rows_per_wg : nrows;
+  for (int64_t nb = n_begin; nb < n_end; nb += kNR) {
+    __syncthreads();
+    for (int x = tid; x < kNR * D; x += 256) {
+      const int rr = x / D, e = x % D;
+      const int64_t n = nb + rr;
+      float v = 0.f;
+      if (n < n_end) {
+        if (kDQ) {
+          v = r[n * D + e];
+        } else {
+          const int64_t row = n % nq, bh = n / nq;
+          const int64_t hs = bh % Hsel, bi = bh / Hsel;
+          const __bf16* q0 = q + ((bi * Hq + hs * nh) * nq + row) * D + e;
+          for (int g = 0; g < nh; ++g) v += static_cast<float>(q0[static_cast<int64_t>(g) * nq * D]);
+          v = v / static_cast<float>(nh);
+        }
+      }
+      xs[rr][e] = v;
+    }
+    __syncthreads();
+    float acc[kRPT];
+#pragma unroll
+    for (int i = 0; i < kRPT; ++i) acc[i] = 0.f;
+#pragma unroll 8
+    for (int k = 0; k < D; ++k) {
+      const float m = ms[k * kPitch + j];
+#pragma unroll
+      for (int i = 0; i < kRPT; ++i) acc[i] = fmaf(xs[rsub + kStep * i][k], m, acc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kRPT; ++i) {
+      const int64_t n = nb + rsub + kStep * i;
+      if (n >= n_end) continue;
+      if (kDQ) {
+        const int64_t row = n % nq, bh = n / nq;
+        const int64_t hs = bh % Hsel, bi = bh / Hsel;
+        const float v = acc[i] / static_cast<float>(nh);
+        for (int g = 0; g < nh; ++g) dq[((bi * Hq + hs * nh + g) * nq + row) * D + j] = v;
+      } else {
+        uout[n * D + j] = static_cast<__bf16>(acc[i]);
+      }
+    }
+  }
 }
+
+// dW partial sums: part[chunk][e][f] = sum over the chunk's rows of
+// q_hat_n[e] r_n[f]; each thread owns a (D/16) x (D/16) block of dW.
+template <int D>
+__global__ __launch_bounds__(256) void proj_dw_partial_kernel(const __bf16* __restrict__ q, int Hq, int nh,
+                                                              const float* __restrict__ r, int Hsel, int nq,
+                                                              int64_t nrows, int64_t rows_per_chunk,
+                                                              float* __restrict__ part) {
+  constexpr int kTB = D / 16;
+  constexpr int kNR = 16;
+  __shared__ float qs[kNR][D];
+  __shared__ float rs[kNR][D];
+  const int tid = threadIdx.x;
+  const int e0 = kTB * (tid / 16), f0 = kTB * (tid % 16);
+  float acc[kTB * kTB];
+#pragma unroll
+  for (int i = 0; i < kTB * kTB; ++i) acc[i] = 0.f;
+  const int64_t n_begin = static_cast<int64_t>(blockIdx.x) * rows_per_chunk;
+  const int64_t n_end = n_begin + rows_per_chunk < nrows ? n_begin + rows_per_chunk : nrows;
+  for (int64_t nb = n_begin; nb < n_end; nb += kNR) {
+    __syncthreads();
+    for (int x = tid; x < kNR * D; x += 256) {
+      const int rr = x / D, e = x % D;
+      const int64_t n = nb + rr;
+      float qv = 0.f, rv = 0.f;
+      if (n < n_end) {
+        const int64_t row = n % nq, bh = n / nq;
+        const int64_t hs = bh % Hsel, bi = bh / Hsel;
+        const __bf16* q0 = q + ((bi * Hq + hs * nh) * nq + row) * D + e;
+        for (int g = 0; g < nh; ++g) qv += static_cast<float>(q0[static_cast<int64_t>(g) * nq * D]);
+        qv = qv / static_cast<float>(nh);
+        rv = r[n * D + e];
+      }
+      qs[rr][e] = qv;
+      rs[rr][e] = rv;
+    }
+    __syncthreads();
+    for (int rr = 0; rr < kNR; ++rr) {
+      float a[kTB], bv[kTB];
+#pragma unroll
+      for (int t = 0; t < kTB; ++t) {
+        a[t] = qs[rr][e0 + t];
+        bv[t] = rs[rr][f0 + t];
+      }
+#pragma unroll
+      for (int x = 0; x < kTB; ++x)
+#pragma unroll
+        for (int y = 0; y < kTB; ++y) acc[x * kTB + y] = fmaf(a[x], bv[y], acc[x * kTB + y]);
+    }
+  }
+  float* dst = part + static_cast<int64_t>(blockIdx.x) * D * D;
+#pragma unroll
+  for (int x = 0; x < kTB; ++x)
+#pragma unroll
+    for (int y = 0; y < kTB; ++y) dst[(e0 + x) * D + f0 + y] = acc[x * kTB + y];
+}
+
+// dW = sum of the chunk partials in chunk order
+__global__ __launch_bounds__(256) void proj_dw_sum_kernel(const float* __restrict__ part, int nchunk, int dd,
+                                                          float* __restrict__ dw) {
+  const int x = blockIdx.x * 256 + threadIdx.x;
+  if (x >= dd) return;
+  float s = 0.f;
+  for (int c = 0; c < nchunk; ++c) s += part[static_cast<int64_t>(c) * dd + x];
+  dw[x] = s;
+}
+
+// ---------------------------------------------------------------- mean
+// dk_j += dkbar_c / b for every token j of block c < ccap of one (batch, kv
+// head); 8 elements per thread, rounded to bf16 (nearest even) after the add.
+template <int D>
+__global__ __launch_bounds__(256) void summary_mean_bwd_kernel(const float* __restrict__ dkbar,
+                                                               __bf16* __restrict__ dk, int64_t ccap, int64_t L,
+                                                               int lb, float inv_b) {
+  constexpr int kV = D / 8;                     // 8-element vectors per token
+  const int64_t v = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (v >= (ccap << lb) * kV) return;
+  const int64_t head = blockIdx.y;
+  const int64_t t = v / kV;
+  const int e8 = static_cast<int>(v % kV);
+  const int64_t c = t >> lb;
+  uint4* dst = reinterpret_cast<uint4*>(dk + (head * L + t) * D + 8 * e8);
+  const float4* src = reinterpret_cast<const float4*>(dkbar + (head * ccap + c) * D + 8 * e8);
+  const float4 a = src[0], bq = src[1];
+  float x[8];
+  Elem<bf16_t>::unpack(*dst, x);
+  x[0] = fmaf(a.x, inv_b, x[0]);
+  x[1] = fmaf(a.y, inv_b, x[1]);
+  x[2] = fmaf(a.z, inv_b, x[2]);
+  x[3] = fmaf(a.w, inv_b, x[3]);
+  x[4] = fmaf(bq.x, inv_b, x[4]);
+  x[5] = fmaf(bq.y, inv_b, x[5]);
+  x[6] = fmaf(bq.z, inv_b, x[6]);
+  x[7] = fmaf(bq.w, inv_b, x[7]);
+  *dst = sb_pack8(x);
+}
+
+// ---------------------------------------------------------------- launch
+namespace {
+struct SbWs {
+  size_t row, u, r, part, total;
+  int64_t nrows, rows_per_chunk;
+  int nchunk;
+};
+SbWs select_bwd_ws(const SelectLaunch& p) {
+  SbWs w{};
+  w.nrows = static_cast<int64_t>(p.B) * p.Hsel * p.nq;
+  w.row = 0;
+  size_t off = align256(static_cast<size_t>(w.nrows) * sizeof(float2));
+  if (p.proj_w != nullptr) {
+    const int64_t per = (w.nrows + 255) / 256;
+    w.rows_per_chunk = per < 256 ? 256 : (per + 15) / 16 * 16;
+    w.nchunk = static_cast<int>((w.nrows + w.rows_per_chunk - 1) / w.rows_per_chunk);
+    w.u = off;
+    off += align256(static_cast<size_t>(w.nrows) * p.d * 2);
+    w.r = off;
+    off += align256(static_cast<size_t>(w.nrows) * p.d * 4);
+    w.part = off;
+    off += align256(static_cast<size_t>(w.nchunk) * p.d * p.d * 4);
+  }
+  w.total = off;
+  return w;
+}
+}  // namespace
+
+size_t select_bwd_workspace_bytes(const SelectLaunch& p) { return select_bwd_ws(p).total; }
 
 template <int D>
-static hipError_t launch_select_bwd_d(const SelectLaunch& p, const float* dg, float* dq, float* dkbar, void* ws,
-                                      hipStream_t st) {
-  float2* ws_row = static_cast<float2*>(ws);
-  hipError_t e = launch(false, select_bwd_rows_kernel<D>, dim3((p.nq + 127) / 128, static_cast<unsigned>(p.B * p.Hsel)),
-                        dim3(256), st, static_cast<const __bf16*>(p.q), static_cast<const __bf16*>(p.kbar), p.Hq,
-                        p.Hkv, p.Hsel, p.nq, p.q_pos0, p.ccap, p.b, p.share_group, p.K, p.idx, dg, dq, ws_row);
-  if (e != hipSuccess) return e;
-  // candidate tiles cover every summary slot (slots that are no row's
-  // candidate get zero gradient)
+static hipError_t launch_select_bwd_d(const SelectLaunch& p, const SelectGrads& g, void* ws, hipStream_t st) {
+  const SbWs w = select_bwd_ws(p);
+  char* base = static_cast<char*>(ws);
+  float2* ws_row = reinterpret_cast<float2*>(base + w.row);
+  const int G = p.Hq / p.Hkv;
+  const int nh = p.share_group ? G : 1;
+  const auto* q = static_cast<const __bf16*>(p.q);
+  const auto* kbar = static_cast<const __bf16*>(p.kbar);
+  const dim3 rows_grid((p.nq + 127) / 128, static_cast<unsigned>(p.B * p.Hsel));
   const int ntile = static_cast<int>((p.ccap + kST - 1) / kST);
-  return launch(true, select_bwd_cands_kernel<D>, dim3(ntile, static_cast<unsigned>(p.B * p.Hkv)), dim3(256), st,
-                static_cast<const __bf16*>(p.q), static_cast<const __bf16*>(p.kbar), p.Hq, p.Hkv, p.Hsel, p.nq,
-                p.q_pos0, p.ccap, p.ccap, p.b, p.share_group, p.K, p.idx, dg, ws_row, dkbar);
+  const dim3 cand_grid(ntile, static_cast<unsigned>(p.B * p.Hkv));
+  hipError_t e;
+  if (p.proj_w == nullptr) {
+    e = launch(false, select_bwd_rows_kernel<D>, rows_grid, dim3(256), st, q, p.Hq, nh, kbar, p.Hkv, p.Hsel, G,
+               p.share_group, p.nq, p.q_pos0, p.ccap, p.b, p.K, p.idx, g.dg, g.dq, p.Hq, nh, ws_row);
+    if (e != hipSuccess) return e;
+    // candidate tiles cover every summary slot (slots that are no row's
+    // candidate get zero gradient)
+    e = launch(g.dk == nullptr, select_bwd_cands_kernel<D>, cand_grid, dim3(256), st, q, p.Hq, nh, kbar, p.Hkv,
+               p.Hsel, G, p.share_group, p.nq, p.q_pos0, p.ccap, p.b, p.K, p.idx, g.dg, ws_row, g.dkbar);
+  } else {
+    __bf16* u = reinterpret_cast<__bf16*>(base + w.u);
+    float* r = reinterpret_cast<float*>(base + w.r);
+    float* part = reinterpret_cast<float*>(base + w.part);
+    constexpr int64_t kRowsPerWg = 128;
+    const dim3 proj_grid(static_cast<unsigned>((w.nrows + kRowsPerWg - 1) / kRowsPerWg));
+    e = launch(false, proj_rows_kernel<D, false>, proj_grid, dim3(256), st, q, p.Hq, nh,
+               static_cast<const float*>(nullptr), p.proj_w, p.Hsel, p.nq, w.nrows, kRowsPerWg, u,
+               static_cast<float*>(nullptr));
+    if (e != hipSuccess) return e;
+    // rows and candidates on u = W^T q_hat (one source head per selection head)
+    e = launch(false, select_bwd_rows_kernel<D>, rows_grid, dim3(256), st, static_cast<const __bf16*>(u), p.Hsel,
+               1, kbar, p.Hkv, p.Hsel, G, p.share_group, p.nq, p.q_pos0, p.ccap, p.b, p.K, p.idx, g.dg, r, p.Hsel,
+               1, ws_row);
+    if (e != hipSuccess) return e;
+    e = launch(false, select_bwd_cands_kernel<D>, cand_grid, dim3(256), st, static_cast<const __bf16*>(u), p.Hsel,
+               1, kbar, p.Hkv, p.Hsel, G, p.share_group, p.nq, p.q_pos0, p.ccap, p.b, p.K, p.idx, g.dg, ws_row,
+               g.dkbar);
+    if (e != hipSuccess) return e;
+    e = launch(false, proj_rows_kernel<D, true>, proj_grid, dim3(256), st, q, p.Hq, nh,
+               static_cast<const float*>(r), p.proj_w, p.Hsel, p.nq, w.nrows, kRowsPerWg,
+               static_cast<__bf16*>(nullptr), g.dq);
+    if (e != hipSuccess) return e;
+    e = launch(false, proj_dw_partial_kernel<D>, dim3(w.nchunk), dim3(256), st, q, p.Hq, nh,
+               static_cast<const float*>(r), p.Hsel, p.nq, w.nrows, w.rows_per_chunk, part);
+    if (e != hipSuccess) return e;
+    e = launch(g.dk == nullptr, proj_dw_sum_kernel, dim3((D * D + 255) / 256), dim3(256), st,
+               static_cast<const float*>(part), w.nchunk, D * D, g.dproj_w);
+  }
+  if (e != hipSuccess || g.dk == nullptr) return e;
+  const int64_t nvec = (p.ccap * p.b) * (D / 8);
+  return launch(true, summary_mean_bwd_kernel<D>, dim3(static_cast<unsigned>((nvec + 255) / 256),
+                                                       static_cast<unsigned>(p.B * p.Hkv)),
+                dim3(256), st, static_cast<const float*>(g.dkbar), static_cast<__bf16*>(g.dk), p.ccap, g.L,
+                __builtin_ctz(p.b), 1.0f / static_cast<float>(p.b));
 }
 
-hipError_t launch_select_bwd(const SelectLaunch& p, const float* dg, float* dq, float* dkbar, void* ws,
-                             hipStream_t st) {
-  return p.d == 64 ? launch_select_bwd_d<64>(p, dg, dq, dkbar, ws, st)
-                   : launch_select_bwd_d<128>(p, dg, dq, dkbar, ws, st);
+hipError_t launch_select_bwd(const SelectLaunch& p, const SelectGrads& g, void* ws, hipStream_t st) {
+  return p.d == 64 ? launch_select_bwd_d<64>(p, g, ws, st) : launch_select_bwd_d<128>(p, g, ws, st);
 }
 
 }  // namespace spa

@@ -47,6 +47,15 @@ struct SelectLaunch {
   int64_t max_cand;   // candidates of the last row (the largest count)
 };
 
+struct SelectGrads {
+  const float* dg;
+  float* dq;
+  float* dkbar;
+  float* dproj_w;
+  void* dk;          // may be NULL
+  int64_t L;
+};
+
 struct AttnLaunch {
   const void* q;
   const void* k;
@@ -120,8 +129,7 @@ size_t attn_bwd_workspace_bytes(const BwdLaunch& p);
 
 hipError_t launch_block_summaries(const SummaryLaunch& p, hipStream_t st);
 hipError_t launch_score_select(const SelectLaunch& p, void* ws, hipStream_t st);
-hipError_t launch_select_bwd(const SelectLaunch& p, const float* dg, float* dq, float* dkbar, void* ws,
-                             hipStream_t st);
+hipError_t launch_select_bwd(const SelectLaunch& p, const SelectGrads& g, void* ws, hipStream_t st);
 bool rows_select_mfma_supported(const SelectLaunch& p);
 hipError_t launch_rows_select_mfma(const SelectLaunch& p, hipStream_t st);
 hipError_t launch_attn_fwd(const AttnLaunch& p, void* ws, hipStream_t st);

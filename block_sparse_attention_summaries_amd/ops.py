@@ -40,6 +40,10 @@ class SelectArgs(ctypes.Structure):
                 ("logg", _vp), ("k_eff", _vp)]
 
 
+class SelectGrads(ctypes.Structure):
+    _fields_ = [("dg", _vp), ("dq", _vp), ("dkbar", _vp), ("dproj_w", _vp), ("dk", _vp), ("L", _i64)]
+
+
 class AttnArgs(ctypes.Structure):
     _fields_ = [("q", _vp), ("k", _vp), ("v", _vp), ("dtype", _i), ("B", _i), ("Hq", _i), ("Hkv", _i),
                 ("nq", _i), ("d", _i), ("L", _i64), ("q_pos0", _i64), ("b", _i), ("prefix_mode", _i),
@@ -81,7 +85,7 @@ def lib():
         L.sparse_attn_bwd.argtypes = [ctypes.POINTER(AttnArgs), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _sz, _vp]
         L.sparse_select_bwd.restype = _i
-        L.sparse_select_bwd.argtypes = [ctypes.POINTER(SelectArgs), _vp, _vp, _vp, _vp, _sz, _vp]
+        L.sparse_select_bwd.argtypes = [ctypes.POINTER(SelectArgs), ctypes.POINTER(SelectGrads), _vp, _sz, _vp]
         L.sparse_workspace_bytes.restype = _sz
         L.sparse_workspace_bytes.argtypes = [_i, _vp]
         L.sparse_workspace_init.restype = _i
@@ -245,17 +249,22 @@ def sparse_attn_bwd(q, k, v, idx, logg, o, dout, lse, *, dq=None, dk=None, dv=No
     return dq, dk, dv, dg
 
 
-def sparse_select_bwd(q, kbar, max_norm, centre, idx, logg, dg, *, dq=None, dkbar=None, workspace=None,
-                      stream=None, **kw):
+def sparse_select_bwd(q, kbar, max_norm, centre, idx, logg, dg, *, dq=None, dkbar=None, dproj_w=None, dk=None,
+                      workspace=None, stream=None, **kw):
     """Selector side of the backward: dg [B,Hsel,nq,K] (from sparse_attn_bwd)
-    through log g = s - LSE(s) into q and kbar.  Takes the arguments of the
-    sparse_score_select call that produced idx / logg.  Returns (dq, dkbar),
-    both fp32."""
-    _contig(dg, dq, dkbar)
+    through log g = s - LSE(s) into q, kbar and (with proj_w) the projection;
+    with dk [B,Hkv,L,d] given, dk += dkbar / b over each summarised block.
+    Takes the arguments of the sparse_score_select call that produced idx /
+    logg.  Returns (dq, dkbar, dproj_w), fp32 (dproj_w None without proj_w)."""
+    _contig(dg, dq, dkbar, dproj_w, dk)
     a, _ = select_args(q, kbar, max_norm, centre, idx=idx, logg=logg, **kw)
     dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
     dkbar = torch.empty(kbar.shape, dtype=torch.float32, device=q.device) if dkbar is None else dkbar
+    if dproj_w is None and kw.get("proj_w") is not None:
+        d = q.shape[-1]
+        dproj_w = torch.empty((d, d), dtype=torch.float32, device=q.device)
+    g = SelectGrads(dg=_p(dg), dq=_p(dq), dkbar=_p(dkbar), dproj_w=_p(dproj_w), dk=_p(dk),
+                    L=0 if dk is None else dk.shape[2])
     buf, size = _ws(workspace, SPA_OP_SELECT_BWD, a, q.device)
-    _check(lib().sparse_select_bwd(ctypes.byref(a), _p(dg), _p(dq), _p(dkbar), _p(buf), size,
-                                   _stream(stream)))
-    return dq, dkbar
+    _check(lib().sparse_select_bwd(ctypes.byref(a), ctypes.byref(g), _p(buf), size, _stream(stream)))
+    return dq, dkbar, dproj_w

@@ -220,30 +220,47 @@ int sparse_attn_bwd(const spa_attn_args *a, const void *o, const void *dout,
                     const float *lse, void *dq, void *dk, void *dv, float *dg,
                     void *workspace, size_t ws_bytes, spa_stream_t stream);
 
+typedef struct spa_select_grads {
+    const float *dg;          /* in  [B, Hsel, nq, K] fp32, the gate gradient of
+                                 sparse_attn_bwd (slots that are not candidates
+                                 of their row are ignored) */
+    float *dq;                /* out [B, Hq, nq, d] fp32, written */
+    float *dkbar;             /* out [B, Hkv, ccap, d] fp32, written (0 for
+                                 summaries that are no row's candidate) */
+    float *dproj_w;           /* out [d, d] fp32, written; required exactly when
+                                 the select arguments carry proj_w */
+    void *dk;                 /* in/out [B, Hkv, L, d] in the key dtype, or NULL:
+                                 dk_j += dkbar_c / b for each token j of block
+                                 c < ccap (the summary is the block mean) */
+    int64_t L;                /* tokens in dk (>= ccap * b when dk is given) */
+} spa_select_grads;
+
 /*
  * sparse_select_bwd -- selector side of the backward: the gate gradient dg
- * (as written by sparse_attn_bwd) carried back through log g = s - LSE(s)
- * into the query and the block summaries ("SAS" review, "How it works"
- * step 5: the loss reaches the selector only through the gates; §4.2.2
- * softmax gate; §3 Eq. 3 scores).  With p = softmax(s) over all candidates
- * of a row (so g_m = p_m) and its selected set S held fixed:
- *   ds_c   = p_c ([c in S] dg_c - sum_{m in S} p_m dg_m),
- *   dq     = sum_c ds_c kbar_c / sqrt(d), given to each of the G query heads
- *            of a shared selection as dq_hat / G (q_hat is their mean),
- *   dkbar_c = sum over rows and selection heads of ds_c q_hat / sqrt(d).
+ * carried back through log g = s - LSE(s) into the query, the block
+ * summaries, the learned projection and the keys ("SAS" review, "How it
+ * works" step 5: the loss reaches the selector only through the gates;
+ * §4.2.2 softmax gate; §3 Eq. 3 scores, mean-key summaries).  With
+ * p = softmax(s) over all candidates of a row (so g_m = p_m) and its selected
+ * set S held fixed, and ktilde = kbar (or W kbar with the projection):
+ *   ds_c     = p_c ([c in S] dg_c - sum_{m in S} p_m dg_m),
+ *   dq       = sum_c ds_c ktilde_c / sqrt(d), given to each of the G query
+ *              heads of a shared selection as dq_hat / G (q_hat is their mean),
+ *   dktilde_c = sum over rows and selection heads of ds_c q_hat / sqrt(d),
+ *   dkbar_c  = dktilde_c, or W^T dktilde_c;  dW = sum_c dktilde_c kbar_c^T,
+ *   dk_j    += dkbar_c / b (optional; the rounding of kbar to the key dtype is
+ *              passed straight through).
  * `a` is the argument struct of the sparse_score_select call that produced
- * idx, validated the same way (its outputs logg and k_eff are not read).  Supported: bf16, gate = SOFTMAX_LOG,
- * prefix_mode = CURRENT_BLOCK, no projection, no erf term; otherwise
- * SPA_ERR_UNSUPPORTED.  dg: fp32 [B, Hsel, nq, K] (entries of slots that are
- * not candidates of their row are ignored).  Outputs, written not
- * accumulated, fp32, 16-byte aligned: dq [B, Hq, nq, d]; dkbar
- * [B, Hkv, ccap, d] (0 for summaries that are no row's candidate).  Scores
- * are recomputed from q_hat rounded to bf16.  Needs a workspace of
- * sparse_workspace_bytes(SPA_OP_SELECT_BWD); caller-owned, contents on entry
- * are ignored.
+ * idx, validated the same way (its outputs logg and k_eff are not read; idx
+ * holds distinct entries per row, as that call writes them).  Supported:
+ * bf16, gate = SOFTMAX_LOG, prefix_mode = CURRENT_BLOCK, no erf term;
+ * otherwise SPA_ERR_UNSUPPORTED.  dq, dkbar and dk must be 16-byte aligned.
+ * Scores are recomputed from q_hat (or W^T q_hat) rounded to bf16.  Needs a
+ * workspace of sparse_workspace_bytes(SPA_OP_SELECT_BWD); caller-owned,
+ * contents on entry are ignored.  Deterministic: no atomics.
  */
-int sparse_select_bwd(const spa_select_args *a, const float *dg, float *dq, float *dkbar,
-                      void *workspace, size_t ws_bytes, spa_stream_t stream);
+int sparse_select_bwd(const spa_select_args *a, const spa_select_grads *g, void *workspace,
+                      size_t ws_bytes, spa_stream_t stream);
 
 /* Workspace bytes needed by `op` (spa_op) for the given argument struct
  * (spa_select_args* for SPA_OP_SCORE_SELECT and SPA_OP_SELECT_BWD,

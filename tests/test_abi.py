@@ -137,22 +137,40 @@ def test_bwd_rejects_unsupported_modes():
                                None) == ops.SPA_ERR_INVALID_ARG
 
 
+def _grads(**kw):
+    g = ops.SelectGrads(dg=FAKE, dq=FAKE, dkbar=FAKE, dproj_w=None, dk=None, L=0)
+    for k, v in kw.items():
+        setattr(g, k, v)
+    return g
+
+
 def test_select_bwd_rejects_unsupported_modes():
     lib = ops.lib()
-    def st(a, dg=FAKE, dq=FAKE, dk=FAKE):
-        return lib.sparse_select_bwd(ctypes.byref(a), dg, dq, dk, FAKE, 1 << 20, None)
+
+    def st(a, g=None, n=1 << 20):
+        g = _grads() if g is None else g
+        return lib.sparse_select_bwd(ctypes.byref(a), ctypes.byref(g), FAKE, n, None)
     base = dict(nq=8192, q_pos0=0, ccap=128)
     assert st(_sel(**base, gate=0, logg=None)) == ops.SPA_ERR_UNSUPPORTED
     assert st(_sel(**base, dtype=0)) == ops.SPA_ERR_UNSUPPORTED
     assert st(_sel(**base, prefix_mode=1, qblock=128)) == ops.SPA_ERR_UNSUPPORTED
-    assert st(_sel(**base, proj_w=FAKE)) == ops.SPA_ERR_UNSUPPORTED
-    assert st(_sel(**base), dg=None) == ops.SPA_ERR_INVALID_ARG
-    assert st(_sel(**base), dq=FAKE_ODD) == ops.SPA_ERR_INVALID_ARG
+    assert st(_sel(**base, erf_lambda=FAKE, erf_sigma=FAKE)) == ops.SPA_ERR_UNSUPPORTED
+    assert st(_sel(**base), _grads(dg=None)) == ops.SPA_ERR_INVALID_ARG
+    assert st(_sel(**base), _grads(dq=FAKE_ODD)) == ops.SPA_ERR_INVALID_ARG
+    assert st(_sel(**base, proj_w=FAKE)) == ops.SPA_ERR_INVALID_ARG          # dproj_w missing
+    assert st(_sel(**base), _grads(dproj_w=FAKE)) == ops.SPA_ERR_INVALID_ARG  # no projection
+    assert st(_sel(**base), _grads(dk=FAKE, L=128 * 64 - 1)) == ops.SPA_ERR_INVALID_ARG
+    assert st(_sel(**base), _grads(dk=FAKE_ODD, L=8192)) == ops.SPA_ERR_INVALID_ARG
     a = _sel(**base)
     # one (LSE, sum_S p dg) pair per (batch, selection head, row)
     need = lib.sparse_workspace_bytes(ops.SPA_OP_SELECT_BWD, ctypes.byref(a))
     assert need == 8 * 8192 * 8
-    assert lib.sparse_select_bwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, need - 1, None) == ops.SPA_ERR_WORKSPACE
+    assert st(a, n=need - 1) == ops.SPA_ERR_WORKSPACE
+    # with the projection: + u (bf16) and r (fp32) per row, + 256 dW partials
+    ap = _sel(**base, proj_w=FAKE)
+    rows = 8 * 8192
+    assert lib.sparse_workspace_bytes(ops.SPA_OP_SELECT_BWD, ctypes.byref(ap)) == \
+        rows * 8 + rows * 128 * 2 + rows * 128 * 4 + 256 * 128 * 128 * 4
 
 
 def test_summaries_rejects_invalid_arguments():
