@@ -77,6 +77,28 @@ __device__ __forceinline__ void sb_store_t8(uint16_t* dst, int pitch, uint4 w) {
   dst[7 * pitch] = static_cast<uint16_t>(w.w >> 16);
 }
 
+// dg of one row's selected candidates in [c0, c0 + 32) into its dg table row
+// (already zeroed); the two half-waves take alternate slots, 8 slots per
+// lane at a time with every load issued before the first is used.
+__device__ __forceinline__ void sb_fill_dg(float* __restrict__ trow, const int32_t* __restrict__ sel,
+                                           const float* __restrict__ dgr, int K, int hl, int c0, int ncand) {
+  for (int t0 = hl; t0 < K; t0 += 16) {
+    int cc[8];
+    float dd[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = t0 + 2 * u;
+      const int tc = t < K ? t : K - 1;
+      cc[u] = sel[tc];
+      dd[u] = dgr[tc];
+      if (t >= K) cc[u] = -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (cc[u] >= c0 && cc[u] < c0 + 32 && cc[u] < ncand) trow[cc[u] - c0] = dd[u];
+  }
+}
+
 // q_hat of one row as 8 bf16 (columns 8 j .. 8 j + 7): the mean of nh heads
 // (summed in head order in fp32), rounded to nearest even.
 __device__ __forceinline__ uint4 qhat8(const __bf16* __restrict__ q0, int64_t head_stride, int nh, int j) {
@@ -163,12 +185,7 @@ __global__ __launch_bounds__(256, 2) void select_bwd_rows_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) sm.dgt[wave][ql][16 * hl + e] = 0.f;
     wave_lds_sync();
-    if (row_ok) {
-      for (int t = hl; t < K; t += 2) {
-        const int c = idx[so + t];
-        if (c >= c0 && c < c0 + kST && c < ncand) sm.dgt[wave][ql][c - c0] = dg[so + t];
-      }
-    }
+    if (row_ok) sb_fill_dg(sm.dgt[wave][ql], idx + so, dg + so, K, hl, c0, ncand);
     wave_lds_sync();
   };
   // S^T = Kbar_perm q_hat^T: register r holds candidate c0 + sb_elem(r, hl)
@@ -298,6 +315,8 @@ __global__ __launch_bounds__(256) void select_bwd_cands_kernel(
     const __bf16* __restrict__ q, int qHeads, int nh_in, const __bf16* __restrict__ kbar, int Hkv, int Hsel,
     int G, int share_group, int nq, int64_t q_pos0, int64_t ccap, int b, int K, const int32_t* __restrict__ idx,
     const float* __restrict__ dg, const float2* __restrict__ ws_row, float* __restrict__ dkbar) {
+  // blockIdx.z of gridDim.z takes an equal share of the row tiles; with
+  // several shares each writes its own copy of dkbar (summed later in order)
   __shared__ SbCandSmem<D> sm;
   constexpr int kKS = D / 16;
   constexpr int kDB = D / 32;
@@ -329,38 +348,41 @@ __global__ __launch_bounds__(256) void select_bwd_cands_kernel(
   // rows that have candidate c0 as a candidate: pos >= (c0 + 1) b
   int64_t r0 = (c0 + 1) * static_cast<int64_t>(b) - q_pos0;
   r0 = r0 < 0 ? 0 : r0;
-  const int ntile = r0 < nq ? static_cast<int>((nq - r0 + 31) / 32) : 0;
+  const int ntile_all = r0 < nq ? static_cast<int>((nq - r0 + 31) / 32) : 0;
+  const int share = (ntile_all + gridDim.z - 1) / gridDim.z;
+  const int rt_begin = share * blockIdx.z;
+  const int ntile = rt_begin + share < ntile_all ? rt_begin + share : ntile_all;
+  dkbar += static_cast<int64_t>(blockIdx.z) * gridDim.y * ccap * D;
   for (int sh = 0; sh < nsel; ++sh) {
     const int hs = share_group ? kvh : kvh * G + sh;
     const int h0 = hs * nh_in;
-    for (int rt = wave; rt < ntile; rt += 4) {
+    for (int rt = rt_begin + wave; rt < ntile; rt += 4) {
       const int e0 = static_cast<int>(r0) + rt * 32;
+      // A operand: q_hat rows pi(ql) (rows past nq are zero), loads issued
+      // first; also q_hat^T into LDS below
+      const int ea = e0 + sb_perm(ql);
+      uint4 qa[kKS];
+      {
+        const bool aok = ea < nq;
+        const __bf16* q0 = q + ((static_cast<int64_t>(bi) * qHeads + h0) * nq + (aok ? ea : nq - 1)) * D;
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) {
+          qa[ks] = qhat8(q0, static_cast<int64_t>(nq) * D, nh_in, 2 * ks + hl);
+          if (!aok) qa[ks] = make_uint4(0, 0, 0, 0);
+        }
+      }
       // per-row scalars and the dg table of this row tile (lane ql = tile row)
       const int er = e0 + ql;
       const bool rok = er < nq;
       const int64_t sr = ((static_cast<int64_t>(bi) * Hsel + hs) * nq + (rok ? er : nq - 1));
-      if (hl == 0) sm.rs[wave][ql] = rok ? ws_row[sr] : make_float2(0.f, 0.f);
+      const float2 rsv_own = ws_row[sr];
+      if (hl == 0) sm.rs[wave][ql] = rok ? rsv_own : make_float2(0.f, 0.f);
 #pragma unroll
       for (int e = 0; e < 16; ++e) sm.dgt[wave][ql][16 * hl + e] = 0.f;
       wave_lds_sync();
-      if (rok) {
-        const int nc = static_cast<int>((q_pos0 + er) >> lb);
-        for (int t = hl; t < K; t += 2) {
-          const int c = idx[sr * K + t];
-          if (c >= c0 && c < c0 + kST && c < nc) sm.dgt[wave][ql][c - c0] = dg[sr * K + t];
-        }
-      }
-      // A operand: q_hat rows pi(ql) (rows past nq are zero); also q_hat^T into LDS
-      const int ea = e0 + sb_perm(ql);
-      uint4 qa[kKS];
-      if (ea < nq) {
-        const __bf16* q0 = q + ((static_cast<int64_t>(bi) * qHeads + h0) * nq + ea) * D;
-#pragma unroll
-        for (int ks = 0; ks < kKS; ++ks) qa[ks] = qhat8(q0, static_cast<int64_t>(nq) * D, nh_in, 2 * ks + hl);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < kKS; ++ks) qa[ks] = make_uint4(0, 0, 0, 0);
-      }
+      if (rok)
+        sb_fill_dg(sm.dgt[wave][ql], idx + sr * K, dg + sr * K, K, hl, c0,
+                   static_cast<int>((q_pos0 + er) >> lb));
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks)
         sb_store_t8(tw + (16 * ks + 8 * hl) * SbCandSmem<D>::kTPitch + sb_perm(ql), SbCandSmem<D>::kTPitch, qa[ks]);
@@ -417,133 +439,233 @@ __global__ __launch_bounds__(256) void select_bwd_cands_kernel(
   }
 }
 
+// ---------------------------------------------------------------- shared inputs
+// q_hat of every (batch, selection head, row) as bf16 [B, Hsel, nq, d]: the
+// mean of the nh heads hs * nh .. of q, as the row kernels would form it.
+template <int D>
+__global__ __launch_bounds__(256) void qhat_kernel(const __bf16* __restrict__ q, int Hq, int nh, int Hsel, int nq,
+                                                   int64_t nvec, __bf16* __restrict__ qh) {
+  constexpr int kV = D / 8;
+  const int64_t v = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (v >= nvec) return;
+  const int64_t n = v / kV;
+  const int j = static_cast<int>(v % kV);
+  const int64_t row = n % nq, bh = n / nq;
+  const int64_t hs = bh % Hsel, bi = bh / Hsel;
+  const __bf16* q0 = q + ((bi * Hq + hs * nh) * nq + row) * D;
+  *reinterpret_cast<uint4*>(qh + n * D + 8 * j) = qhat8(q0, static_cast<int64_t>(nq) * D, nh, j);
+}
+
+// out[x] = sum over shares s of part[s][x], in share order
+__global__ __launch_bounds__(256) void sum_shares_kernel(const float4* __restrict__ part, int nshare, int64_t n4,
+                                                         float4* __restrict__ out) {
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (x >= n4) return;
+  float4 a = part[x];
+  for (int s = 1; s < nshare; ++s) {
+    const float4 v = part[s * n4 + x];
+    a.x += v.x;
+    a.y += v.y;
+    a.z += v.z;
+    a.w += v.w;
+  }
+  out[x] = a;
+}
+
 // ---------------------------------------------------------------- projection
-// Row-times-matrix for the projection, one selection-head row n = (batch,
-// selection head, row) at a time, the d x d matrix staged in LDS:
-//   kDQ = false: u_n = q_hat_n W  (q_hat = mean of the nh heads hs * nh ..
-//                of q, fp32), written as bf16 U [B, Hsel, nq, d];
-//   kDQ = true:  dq_hat_n = W r_n, written / nh to the nh query heads.
+// Row-times-matrix for the projection, rows n = (batch, selection head,
+// row), out[n][j] = sum_k x[n][k] M[k][j]:
+//   kDQ = false: x = q_hat (mean of the nh heads hs * nh .. of q, fp32),
+//                M = W, written as bf16 U [B, Hsel, nq, d];
+//   kDQ = true:  x = r (fp32), M = W^T, written / nh to the nh query heads.
+// A workgroup takes 64 rows; k runs in chunks of 32 staged in LDS (x
+// transposed, M row-major); each thread accumulates 4 rows x d/16 columns.
 template <int D, bool kDQ>
 __global__ __launch_bounds__(256) void proj_rows_kernel(const __bf16* __restrict__ q, int Hq, int nh,
                                                         const float* __restrict__ r, const float* __restrict__ W,
-                                                        int Hsel, int nq, int64_t nrows, int64_t rows_per_wg,
-                                                        __bf16* __restrict__ uout, float* __restrict__ dq) {
-  constexpr int kPitch = D + 1;
-  constexpr int kNR = 16;                       // rows per LDS batch
-  constexpr int kStep = 256 / D;                // row groups per workgroup
-  constexpr int kRPT = kNR / kStep;             // rows per thread and batch
-  __shared__ float ms[D * kPitch];              // kDQ: ms[f][e] = W[e][f]; else ms[e][f] = W[e][f]
-  __shared__ float xs[kNR][D];
+                                                        int Hsel, int nq, int64_t nrows, __bf16* __restrict__ uout,
+                                                        float* __restrict__ dq) {
+  constexpr int kRows = 64, kKC = 32, kCW = D / 16;
+  __shared__ __align__(16) float ms[kKC][D + 4];
+  __shared__ __align__(16) float xs[kKC][kRows + 4];
   const int tid = threadIdx.x;
-  const int j = tid % D, rsub = tid / D;
-  for (int x = tid; x < D * D; x += 256) {
-    const int e = x / D, f = x % D;
-    if (kDQ)
-      ms[f * kPitch + e] = W[x];
-    else
-      ms[e * kPitch + f] = W[x];
-  }
-  const int64_t n_begin = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
-  const int64_t n_end = n_begin + rows_per_wg < nrows ? n_begin + rows_per_wg : nrows;
-  for (int64_t nb = n_begin; nb < n_end; nb += kNR) {
+  const int tcol = tid % 16, trow = tid / 16;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kRows;
+  float acc[4][kCW];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < kCW; ++c) acc[i][c] = 0.f;
+  // this thread's staging slot: row sr, 8 consecutive k from 8 * sk
+  const int sr = tid / 4, sk = tid % 4;
+  const int64_t sn = n0 + sr;
+  const bool s_ok = sn < nrows;
+  const int64_t snc = s_ok ? sn : nrows - 1;
+  for (int k0 = 0; k0 < D; k0 += kKC) {
     __syncthreads();
-    for (int x = tid; x < kNR * D; x += 256) {
-      const int rr = x / D, e = x % D;
-      const int64_t n = nb + rr;
-      float v = 0.f;
-      if (n < n_end) {
-        if (kDQ) {
-          v = r[n * D + e];
-        } else {
-          const int64_t row = n % nq, bh = n / nq;
-          const int64_t hs = bh % Hsel, bi = bh / Hsel;
-          const __bf16* q0 = q + ((bi * Hq + hs * nh) * nq + row) * D + e;
-          for (int g = 0; g < nh; ++g) v += static_cast<float>(q0[static_cast<int64_t>(g) * nq * D]);
-          v = v / static_cast<float>(nh);
-        }
-      }
-      xs[rr][e] = v;
-    }
-    __syncthreads();
-    float acc[kRPT];
-#pragma unroll
-    for (int i = 0; i < kRPT; ++i) acc[i] = 0.f;
-#pragma unroll 8
-    for (int k = 0; k < D; ++k) {
-      const float m = ms[k * kPitch + j];
-#pragma unroll
-      for (int i = 0; i < kRPT; ++i) acc[i] = fmaf(xs[rsub + kStep * i][k], m, acc[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < kRPT; ++i) {
-      const int64_t n = nb + rsub + kStep * i;
-      if (n >= n_end) continue;
+    for (int x = tid; x < kKC * D; x += 256) {
       if (kDQ) {
-        const int64_t row = n % nq, bh = n / nq;
-        const int64_t hs = bh % Hsel, bi = bh / Hsel;
-        const float v = acc[i] / static_cast<float>(nh);
-        for (int g = 0; g < nh; ++g) dq[((bi * Hq + hs * nh + g) * nq + row) * D + j] = v;
+        const int jj = x / kKC, kk = x % kKC;         // W[jj][k0 + kk] read along its row
+        ms[kk][jj] = W[jj * D + k0 + kk];
       } else {
-        uout[n * D + j] = static_cast<__bf16>(acc[i]);
+        const int kk = x / D, jj = x % D;
+        ms[kk][jj] = W[(k0 + kk) * D + jj];
+      }
+    }
+    float xv[8];
+    if (kDQ) {
+      const float4* src = reinterpret_cast<const float4*>(r + snc * D + k0 + 8 * sk);
+      const float4 a = src[0], b2 = src[1];
+      xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
+      xv[4] = b2.x; xv[5] = b2.y; xv[6] = b2.z; xv[7] = b2.w;
+    } else {
+      const int64_t row = snc % nq, bh = snc / nq;
+      const int64_t hs = bh % Hsel, bi = bh / Hsel;
+      const __bf16* q0 = q + ((bi * Hq + hs * nh) * nq + row) * D + k0 + 8 * sk;
+      Elem<bf16_t>::unpack(*reinterpret_cast<const uint4*>(q0), xv);
+      for (int g = 1; g < nh; ++g) {
+        float f[8];
+        Elem<bf16_t>::unpack(*reinterpret_cast<const uint4*>(q0 + static_cast<int64_t>(g) * nq * D), f);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) xv[t] += f[t];
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) xv[t] = xv[t] / static_cast<float>(nh);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) xs[8 * sk + t][sr] = s_ok ? xv[t] : 0.f;
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < kKC; ++kk) {
+      const float4 xr = *reinterpret_cast<const float4*>(&xs[kk][4 * trow]);
+      float m[kCW];
+#pragma unroll
+      for (int c = 0; c < kCW; c += 4) {
+        const float4 mv = *reinterpret_cast<const float4*>(&ms[kk][kCW * tcol + c]);
+        m[c] = mv.x; m[c + 1] = mv.y; m[c + 2] = mv.z; m[c + 3] = mv.w;
+      }
+#pragma unroll
+      for (int c = 0; c < kCW; ++c) {
+        acc[0][c] = fmaf(xr.x, m[c], acc[0][c]);
+        acc[1][c] = fmaf(xr.y, m[c], acc[1][c]);
+        acc[2][c] = fmaf(xr.z, m[c], acc[2][c]);
+        acc[3][c] = fmaf(xr.w, m[c], acc[3][c]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t n = n0 + 4 * trow + i;
+    if (n >= nrows) continue;
+    if (kDQ) {
+      const int64_t row = n % nq, bh = n / nq;
+      const int64_t hs = bh % Hsel, bi = bh / Hsel;
+      const float inv = 1.0f / static_cast<float>(nh);
+      for (int g = 0; g < nh; ++g) {
+        float* o = dq + ((bi * Hq + hs * nh + g) * nq + row) * D + kCW * tcol;
+#pragma unroll
+        for (int c = 0; c < kCW; c += 4)
+          *reinterpret_cast<float4*>(o + c) =
+              make_float4(acc[i][c] * inv, acc[i][c + 1] * inv, acc[i][c + 2] * inv, acc[i][c + 3] * inv);
+      }
+    } else {
+      __bf16* o = uout + n * D + kCW * tcol;
+#pragma unroll
+      for (int c = 0; c < kCW; c += 4) {
+        __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v;
+        v[0] = static_cast<__bf16>(acc[i][c]);
+        v[1] = static_cast<__bf16>(acc[i][c + 1]);
+        v[2] = static_cast<__bf16>(acc[i][c + 2]);
+        v[3] = static_cast<__bf16>(acc[i][c + 3]);
+        *reinterpret_cast<uint2*>(o + c) = __builtin_bit_cast(uint2, v);
       }
     }
   }
 }
 
 // dW partial sums: part[chunk][e][f] = sum over the chunk's rows of
-// q_hat_n[e] r_n[f]; each thread owns a (D/16) x (D/16) block of dW.
+// q_hat_n[e] r_n[f]; rows are staged 32 at a time, each thread owns a
+// (d/16) x (d/16) block of dW.
 template <int D>
 __global__ __launch_bounds__(256) void proj_dw_partial_kernel(const __bf16* __restrict__ q, int Hq, int nh,
                                                               const float* __restrict__ r, int Hsel, int nq,
                                                               int64_t nrows, int64_t rows_per_chunk,
                                                               float* __restrict__ part) {
   constexpr int kTB = D / 16;
-  constexpr int kNR = 16;
-  __shared__ float qs[kNR][D];
-  __shared__ float rs[kNR][D];
+  constexpr int kNR = 32;
+  constexpr int kQV = kNR * D / 8 / 256;         // 8-element q vectors per thread and stage
+  constexpr int kRV = kNR * D / 4 / 256;         // float4 r vectors per thread and stage
+  __shared__ __align__(16) float qs[kNR][D + 4];
+  __shared__ __align__(16) float rs[kNR][D + 4];
   const int tid = threadIdx.x;
   const int e0 = kTB * (tid / 16), f0 = kTB * (tid % 16);
-  float acc[kTB * kTB];
+  float acc[kTB][kTB];
 #pragma unroll
-  for (int i = 0; i < kTB * kTB; ++i) acc[i] = 0.f;
+  for (int x = 0; x < kTB; ++x)
+#pragma unroll
+    for (int y = 0; y < kTB; ++y) acc[x][y] = 0.f;
   const int64_t n_begin = static_cast<int64_t>(blockIdx.x) * rows_per_chunk;
   const int64_t n_end = n_begin + rows_per_chunk < nrows ? n_begin + rows_per_chunk : nrows;
   for (int64_t nb = n_begin; nb < n_end; nb += kNR) {
     __syncthreads();
-    for (int x = tid; x < kNR * D; x += 256) {
-      const int rr = x / D, e = x % D;
+#pragma unroll
+    for (int i = 0; i < kQV; ++i) {
+      const int x = tid + 256 * i;
+      const int rr = x / (D / 8), j8 = x % (D / 8);
       const int64_t n = nb + rr;
-      float qv = 0.f, rv = 0.f;
+      float v[8];
       if (n < n_end) {
         const int64_t row = n % nq, bh = n / nq;
         const int64_t hs = bh % Hsel, bi = bh / Hsel;
-        const __bf16* q0 = q + ((bi * Hq + hs * nh) * nq + row) * D + e;
-        for (int g = 0; g < nh; ++g) qv += static_cast<float>(q0[static_cast<int64_t>(g) * nq * D]);
-        qv = qv / static_cast<float>(nh);
-        rv = r[n * D + e];
+        const __bf16* q0 = q + ((bi * Hq + hs * nh) * nq + row) * D + 8 * j8;
+        Elem<bf16_t>::unpack(*reinterpret_cast<const uint4*>(q0), v);
+        for (int g = 1; g < nh; ++g) {
+          float f[8];
+          Elem<bf16_t>::unpack(*reinterpret_cast<const uint4*>(q0 + static_cast<int64_t>(g) * nq * D), f);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) v[t] += f[t];
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = v[t] / static_cast<float>(nh);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = 0.f;
       }
-      qs[rr][e] = qv;
-      rs[rr][e] = rv;
+      *reinterpret_cast<float4*>(&qs[rr][8 * j8]) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(&qs[rr][8 * j8 + 4]) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+#pragma unroll
+    for (int i = 0; i < kRV; ++i) {
+      const int x = tid + 256 * i;
+      const int rr = x / (D / 4), j4 = x % (D / 4);
+      const int64_t n = nb + rr;
+      const float4 v = n < n_end ? *reinterpret_cast<const float4*>(r + n * D + 4 * j4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(&rs[rr][4 * j4]) = v;
     }
     __syncthreads();
+#pragma unroll 2
     for (int rr = 0; rr < kNR; ++rr) {
       float a[kTB], bv[kTB];
 #pragma unroll
-      for (int t = 0; t < kTB; ++t) {
-        a[t] = qs[rr][e0 + t];
-        bv[t] = rs[rr][f0 + t];
+      for (int t = 0; t < kTB; t += 4) {
+        const float4 av = *reinterpret_cast<const float4*>(&qs[rr][e0 + t]);
+        const float4 bw = *reinterpret_cast<const float4*>(&rs[rr][f0 + t]);
+        a[t] = av.x; a[t + 1] = av.y; a[t + 2] = av.z; a[t + 3] = av.w;
+        bv[t] = bw.x; bv[t + 1] = bw.y; bv[t + 2] = bw.z; bv[t + 3] = bw.w;
       }
 #pragma unroll
       for (int x = 0; x < kTB; ++x)
 #pragma unroll
-        for (int y = 0; y < kTB; ++y) acc[x * kTB + y] = fmaf(a[x], bv[y], acc[x * kTB + y]);
+        for (int y = 0; y < kTB; ++y) acc[x][y] = fmaf(a[x], bv[y], acc[x][y]);
     }
   }
   float* dst = part + static_cast<int64_t>(blockIdx.x) * D * D;
 #pragma unroll
   for (int x = 0; x < kTB; ++x)
 #pragma unroll
-    for (int y = 0; y < kTB; ++y) dst[(e0 + x) * D + f0 + y] = acc[x * kTB + y];
+    for (int y = 0; y < kTB; y += 4)
+      *reinterpret_cast<float4*>(dst + (e0 + x) * D + f0 + y) =
+          make_float4(acc[x][y], acc[x][y + 1], acc[x][y + 2], acc[x][y + 3]);
 }
 
 // dW = sum of the chunk partials in chunk order
@@ -551,8 +673,17 @@ __global__ __launch_bounds__(256) void proj_dw_sum_kernel(const float* __restric
                                                           float* __restrict__ dw) {
   const int x = blockIdx.x * 256 + threadIdx.x;
   if (x >= dd) return;
+  // loads of 16 chunks issued together, added in chunk order
   float s = 0.f;
-  for (int c = 0; c < nchunk; ++c) s += part[static_cast<int64_t>(c) * dd + x];
+  int c = 0;
+  for (; c + 16 <= nchunk; c += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = part[static_cast<int64_t>(c + u) * dd + x];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) s += v[u];
+  }
+  for (; c < nchunk; ++c) s += part[static_cast<int64_t>(c) * dd + x];
   dw[x] = s;
 }
 
@@ -589,18 +720,37 @@ __global__ __launch_bounds__(256) void summary_mean_bwd_kernel(const float* __re
 // ---------------------------------------------------------------- launch
 namespace {
 struct SbWs {
-  size_t row, u, r, part, total;
+  size_t row, qh, dkp, u, r, part, total;
   int64_t nrows, rows_per_chunk;
-  int nchunk;
+  int nchunk, nshare;
 };
+// row shares of the candidate kernel: enough workgroups to cover the chip
+// about four times, each share at least 8 row tiles
+int cand_shares(const SelectLaunch& p) {
+  const int64_t wgs = ((p.ccap + kST - 1) / kST) * p.B * p.Hkv;
+  int64_t s = (1024 + wgs - 1) / wgs;
+  const int64_t by_rows = (p.nq / 32 + 7) / 8;
+  s = s < by_rows ? s : by_rows;
+  s = s < 16 ? s : 16;
+  return s < 1 ? 1 : static_cast<int>(s);
+}
 SbWs select_bwd_ws(const SelectLaunch& p) {
   SbWs w{};
   w.nrows = static_cast<int64_t>(p.B) * p.Hsel * p.nq;
   w.row = 0;
   size_t off = align256(static_cast<size_t>(w.nrows) * sizeof(float2));
+  w.nshare = cand_shares(p);
+  if (p.proj_w == nullptr && p.share_group && p.Hq > p.Hkv) {
+    w.qh = off;                                  // q_hat once, shared by both kernels
+    off += align256(static_cast<size_t>(w.nrows) * p.d * 2);
+  }
+  if (w.nshare > 1) {
+    w.dkp = off;
+    off += align256(static_cast<size_t>(w.nshare) * p.B * p.Hkv * p.ccap * p.d * 4);
+  }
   if (p.proj_w != nullptr) {
-    const int64_t per = (w.nrows + 255) / 256;
-    w.rows_per_chunk = per < 256 ? 256 : (per + 15) / 16 * 16;
+    const int64_t per = (w.nrows + 511) / 512;
+    w.rows_per_chunk = per < 256 ? 256 : (per + 31) / 32 * 32;
     w.nchunk = static_cast<int>((w.nrows + w.rows_per_chunk - 1) / w.rows_per_chunk);
     w.u = off;
     off += align256(static_cast<size_t>(w.nrows) * p.d * 2);
@@ -627,25 +777,43 @@ static hipError_t launch_select_bwd_d(const SelectLaunch& p, const SelectGrads& 
   const auto* kbar = static_cast<const __bf16*>(p.kbar);
   const dim3 rows_grid((p.nq + 127) / 128, static_cast<unsigned>(p.B * p.Hsel));
   const int ntile = static_cast<int>((p.ccap + kST - 1) / kST);
-  const dim3 cand_grid(ntile, static_cast<unsigned>(p.B * p.Hkv));
+  // candidate tiles cover every summary slot (slots that are no row's
+  // candidate get zero gradient); row shares write partial copies
+  const dim3 cand_grid(ntile, static_cast<unsigned>(p.B * p.Hkv), static_cast<unsigned>(w.nshare));
+  float* dkbar_c = w.nshare > 1 ? reinterpret_cast<float*>(base + w.dkp) : g.dkbar;
+  const int64_t dkbar_n4 = static_cast<int64_t>(p.B) * p.Hkv * p.ccap * D / 4;
+  const dim3 sum_grid(static_cast<unsigned>((dkbar_n4 + 255) / 256));
   hipError_t e;
   if (p.proj_w == nullptr) {
-    e = launch(false, select_bwd_rows_kernel<D>, rows_grid, dim3(256), st, q, p.Hq, nh, kbar, p.Hkv, p.Hsel, G,
-               p.share_group, p.nq, p.q_pos0, p.ccap, p.b, p.K, p.idx, g.dg, g.dq, p.Hq, nh, ws_row);
+    // query source: q itself (one head per selection) or q_hat formed once
+    const __bf16* qs = q;
+    int qs_heads = p.Hq, qs_nh = nh;
+    if (nh > 1) {
+      __bf16* qh = reinterpret_cast<__bf16*>(base + w.qh);
+      const int64_t nvec = w.nrows * (D / 8);
+      e = launch(false, qhat_kernel<D>, dim3(static_cast<unsigned>((nvec + 255) / 256)), dim3(256), st, q, p.Hq,
+                 nh, p.Hsel, p.nq, nvec, qh);
+      if (e != hipSuccess) return e;
+      qs = qh;
+      qs_heads = p.Hsel;
+      qs_nh = 1;
+    }
+    e = launch(false, select_bwd_rows_kernel<D>, rows_grid, dim3(256), st, qs, qs_heads, qs_nh, kbar, p.Hkv,
+               p.Hsel, G, p.share_group, p.nq, p.q_pos0, p.ccap, p.b, p.K, p.idx, g.dg, g.dq, p.Hq, nh, ws_row);
     if (e != hipSuccess) return e;
-    // candidate tiles cover every summary slot (slots that are no row's
-    // candidate get zero gradient)
-    e = launch(g.dk == nullptr, select_bwd_cands_kernel<D>, cand_grid, dim3(256), st, q, p.Hq, nh, kbar, p.Hkv,
-               p.Hsel, G, p.share_group, p.nq, p.q_pos0, p.ccap, p.b, p.K, p.idx, g.dg, ws_row, g.dkbar);
+    e = launch(false, select_bwd_cands_kernel<D>, cand_grid, dim3(256), st, qs, qs_heads, qs_nh, kbar, p.Hkv,
+               p.Hsel, G, p.share_group, p.nq, p.q_pos0, p.ccap, p.b, p.K, p.idx, g.dg, ws_row, dkbar_c);
+    if (e != hipSuccess) return e;
+    if (w.nshare > 1)
+      e = launch(false, sum_shares_kernel, sum_grid, dim3(256), st, reinterpret_cast<const float4*>(dkbar_c),
+                 w.nshare, dkbar_n4, reinterpret_cast<float4*>(g.dkbar));
   } else {
     __bf16* u = reinterpret_cast<__bf16*>(base + w.u);
     float* r = reinterpret_cast<float*>(base + w.r);
     float* part = reinterpret_cast<float*>(base + w.part);
-    constexpr int64_t kRowsPerWg = 128;
-    const dim3 proj_grid(static_cast<unsigned>((w.nrows + kRowsPerWg - 1) / kRowsPerWg));
+    const dim3 proj_grid(static_cast<unsigned>((w.nrows + 63) / 64));
     e = launch(false, proj_rows_kernel<D, false>, proj_grid, dim3(256), st, q, p.Hq, nh,
-               static_cast<const float*>(nullptr), p.proj_w, p.Hsel, p.nq, w.nrows, kRowsPerWg, u,
-               static_cast<float*>(nullptr));
+               static_cast<const float*>(nullptr), p.proj_w, p.Hsel, p.nq, w.nrows, u, static_cast<float*>(nullptr));
     if (e != hipSuccess) return e;
     // rows and candidates on u = W^T q_hat (one source head per selection head)
     e = launch(false, select_bwd_rows_kernel<D>, rows_grid, dim3(256), st, static_cast<const __bf16*>(u), p.Hsel,
@@ -654,11 +822,15 @@ static hipError_t launch_select_bwd_d(const SelectLaunch& p, const SelectGrads& 
     if (e != hipSuccess) return e;
     e = launch(false, select_bwd_cands_kernel<D>, cand_grid, dim3(256), st, static_cast<const __bf16*>(u), p.Hsel,
                1, kbar, p.Hkv, p.Hsel, G, p.share_group, p.nq, p.q_pos0, p.ccap, p.b, p.K, p.idx, g.dg, ws_row,
-               g.dkbar);
+               dkbar_c);
     if (e != hipSuccess) return e;
+    if (w.nshare > 1) {
+      e = launch(false, sum_shares_kernel, sum_grid, dim3(256), st, reinterpret_cast<const float4*>(dkbar_c),
+                 w.nshare, dkbar_n4, reinterpret_cast<float4*>(g.dkbar));
+      if (e != hipSuccess) return e;
+    }
     e = launch(false, proj_rows_kernel<D, true>, proj_grid, dim3(256), st, q, p.Hq, nh,
-               static_cast<const float*>(r), p.proj_w, p.Hsel, p.nq, w.nrows, kRowsPerWg,
-               static_cast<__bf16*>(nullptr), g.dq);
+               static_cast<const float*>(r), p.proj_w, p.Hsel, p.nq, w.nrows, static_cast<__bf16*>(nullptr), g.dq);
     if (e != hipSuccess) return e;
     e = launch(false, proj_dw_partial_kernel<D>, dim3(w.nchunk), dim3(256), st, q, p.Hq, nh,
                static_cast<const float*>(r), p.Hsel, p.nq, w.nrows, w.rows_per_chunk, part);

@@ -162,15 +162,22 @@ def test_select_bwd_rejects_unsupported_modes():
     assert st(_sel(**base), _grads(dk=FAKE, L=128 * 64 - 1)) == ops.SPA_ERR_INVALID_ARG
     assert st(_sel(**base), _grads(dk=FAKE_ODD, L=8192)) == ops.SPA_ERR_INVALID_ARG
     a = _sel(**base)
-    # one (LSE, sum_S p dg) pair per (batch, selection head, row)
-    need = lib.sparse_workspace_bytes(ops.SPA_OP_SELECT_BWD, ctypes.byref(a))
-    assert need == 8 * 8192 * 8
-    assert st(a, n=need - 1) == ops.SPA_ERR_WORKSPACE
-    # with the projection: + u (bf16) and r (fp32) per row, + 256 dW partials
-    ap = _sel(**base, proj_w=FAKE)
     rows = 8 * 8192
+    # one (LSE, sum_S p dg) pair per (batch, selection head, row), q_hat (bf16)
+    # per row, and 16 row shares of dkbar (4 candidate tiles x 8 heads = 32
+    # workgroups per share)
+    shares = 16 * 8 * 128 * 128 * 4
+    need = lib.sparse_workspace_bytes(ops.SPA_OP_SELECT_BWD, ctypes.byref(a))
+    assert need == rows * 8 + rows * 128 * 2 + shares
+    assert st(a, n=need - 1) == ops.SPA_ERR_WORKSPACE
+    # one head per selection: no q_hat copy
+    a1 = _sel(**base, share_group=0)
+    rows1 = 32 * 8192
+    assert lib.sparse_workspace_bytes(ops.SPA_OP_SELECT_BWD, ctypes.byref(a1)) == rows1 * 8 + shares
+    # with the projection: u (bf16) and r (fp32) per row instead, + 256 dW partials
+    ap = _sel(**base, proj_w=FAKE)
     assert lib.sparse_workspace_bytes(ops.SPA_OP_SELECT_BWD, ctypes.byref(ap)) == \
-        rows * 8 + rows * 128 * 2 + rows * 128 * 4 + 256 * 128 * 128 * 4
+        rows * 8 + shares + rows * 128 * 2 + rows * 128 * 4 + 256 * 128 * 128 * 4
 
 
 def test_summaries_rejects_invalid_arguments():
