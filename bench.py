@@ -2,10 +2,13 @@
 tokens/s (cell routing, n = 16384) and training fwd+bwd tokens/s.
 
 One decode step = the hot path for one query token of one layer:
-  score + softmax log gate + top-K select over all C = 8192 block summaries
-  (sparse_score_select), then exact attention over the current block + the
-  K = 32 selected blocks for all 32 query heads (sparse_attn_fwd), plus, on
-  every b-th step, the summary of the block that closes (sparse_block_summaries).
+  score + softmax log gate + top-K select over all C = 8192 block summaries,
+  then exact attention over the current block + the K = 32 selected blocks for
+  all 32 query heads, in one sparse_decode_step call (the same outputs as
+  sparse_score_select then sparse_attn_fwd; its top-K merge runs inside the
+  attention workgroups), plus, on every b-th step, the summary of the block
+  that closes (sparse_block_summaries).  The two-call sequence is timed the
+  same way for comparison (unfused_us_per_step).
 Steps rotate over 16 layers' KV caches (2.15 GB each) and 64 query vectors so
 that every step reads its summaries and selected K/V cold from HBM, as a
 multi-layer decoder would.  Inputs are resident in HBM before timing starts.
@@ -52,9 +55,13 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+# sources the decode kernels are built from (the HBM counters are tied to them)
+DECODE_SOURCES = ("attn.hip", "decode_merge.h", "select.hip", "spa_device.h", "spa_launch.h")
+
+
 def source_hash():
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
+    for f in DECODE_SOURCES:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -127,6 +134,7 @@ class DecodeWorkload:
         self.lse = torch.empty((B, Hq, 1), dtype=torch.float32, device="cuda")
         self.ws_sel = ops.Workspace()
         self.ws_att = ops.Workspace()
+        self.ws_dec = ops.Workspace()
         torch.cuda.synchronize()
 
     def close_block(self, layer):
@@ -143,6 +151,12 @@ class DecodeWorkload:
     def attend(self, layer, qi):
         ops.sparse_attn_fwd(self.q[qi], self.k[layer], self.v[layer], self.idx, self.logg, b=self.b,
                             K=self.K, q_pos0=self.pos, o=self.o, lse=self.lse, workspace=self.ws_att)
+
+    def decode(self, layer, qi):
+        ops.sparse_decode_step(self.q[qi], self.kbar[layer], self.mx[layer], self.ce[layer], self.k[layer],
+                               self.v[layer], Hkv=self.cfg["Hkv"], b=self.b, K=self.K, q_pos0=self.pos, gate=True,
+                               proj_w=self.w[layer], idx=self.idx, logg=self.logg, k_eff=self.keff, o=self.o,
+                               lse=self.lse, workspace=self.ws_dec)
 
     def selected_kv_bytes(self):
         c = self.cfg
@@ -178,61 +192,60 @@ def run_decode(args):
 
     # warm-up (eager), also builds the workspaces
     for s in range(args.warmup):
+        wl.decode(s % args.layers, s % args.queries)
         wl.select(s % args.layers, s % args.queries)
         wl.attend(s % args.layers, s % args.queries)
     torch.cuda.synchronize()
 
-    # capture one graph of `steps` decode steps
     steps = args.steps
+    stream = torch.cuda.Stream()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    def step(s):
-        layer, qi = s % args.layers, s % args.queries
-        if s % wl.b == wl.b - 1:
-            wl.close_block(layer)
+    def timed_graph(one_step):
+        """Capture `steps` decode steps in one graph, replay once untimed
+        (upload), then time one replay of the whole sequence."""
+        graph = torch.cuda.CUDAGraph()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            graph.capture_begin()
+            for s in range(steps):
+                layer, qi = s % args.layers, s % args.queries
+                if s % wl.b == wl.b - 1:
+                    wl.close_block(layer)
+                one_step(layer, qi)
+            graph.capture_end()
+        torch.cuda.current_stream().wait_stream(stream)
+        graph.replay()
+        torch.cuda.synchronize()
+        g0.record()
+        graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        return g0.elapsed_time(g1)
+
+    # timed region: the one-call decode step
+    total_ms = timed_graph(wl.decode)
+
+    def two_calls(layer, qi):
         wl.select(layer, qi)
         wl.attend(layer, qi)
-
-    graph = torch.cuda.CUDAGraph()
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(stream):
-        graph.capture_begin()
-        for s in range(steps):
-            step(s)
-        graph.capture_end()
-    torch.cuda.current_stream().wait_stream(stream)
-    graph.replay()                                  # untimed replay (graph upload)
-    torch.cuda.synchronize()
-
-    # timed region: one replay of the whole sequence of steps
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    g0.record()
-    graph.replay()
-    g1.record()
-    torch.cuda.synchronize()
-    total_ms = g0.elapsed_time(g1)
+    unfused_ms = timed_graph(two_calls)
 
     # per-kernel durations over the same steps (eager), from each kernel's own
     # dispatch timestamps (start/stop events attached to its launch)
     hip = HipEvents()
-    EvArr = ctypes.c_void_p * 4
-    evs = [(EvArr(*[hip.create() for _ in range(4)]), EvArr(*[hip.create() for _ in range(4)]))
-           for _ in range(steps)]
+    EvArr = ctypes.c_void_p * 6
+    evs = [EvArr(*[hip.create() for _ in range(6)]) for _ in range(steps)]
     lib = ops.lib()
     for s in range(steps):
         layer, qi = s % args.layers, s % args.queries
         if s % wl.b == wl.b - 1:
             wl.close_block(layer)
-        lib.spa_profile_next_call(evs[s][0], 2)
-        wl.select(layer, qi)
-        lib.spa_profile_next_call(evs[s][1], 2)
-        wl.attend(layer, qi)
+        lib.spa_profile_next_call(evs[s], 3)
+        wl.decode(layer, qi)
     torch.cuda.synchronize()
-    k_ms = {name: np.array([hip.elapsed(evs[s][c][2 * i], evs[s][c][2 * i + 1]) for s in range(steps)])
-            for name, c, i in (("chunk", 0, 0), ("merge", 0, 1), ("partial", 1, 0), ("combine", 1, 1))}
-    sel_ms = np.array([hip.elapsed(evs[s][0][0], evs[s][0][3]) for s in range(steps)])
-    att_ms = np.array([hip.elapsed(evs[s][1][0], evs[s][1][3]) for s in range(steps)])
+    k_ms = {name: np.array([hip.elapsed(evs[s][2 * i], evs[s][2 * i + 1]) for s in range(steps)])
+            for name, i in (("chunk", 0), ("merge_partial", 1), ("combine", 2))}
     hip.destroy_all()
 
     # a hot-cache variant (one layer, one query) for context
@@ -240,8 +253,7 @@ def run_decode(args):
     with torch.cuda.stream(stream):
         hot.capture_begin()
         for s in range(64):
-            wl.select(0, 0)
-            wl.attend(0, 0)
+            wl.decode(0, 0)
         hot.capture_end()
     torch.cuda.current_stream().wait_stream(stream)
     hot.replay()
@@ -252,21 +264,22 @@ def run_decode(args):
     torch.cuda.synchronize()
     hot_us = g0.elapsed_time(g1) * 1e3 / 64
 
-    floor_us = latency_floor_us(stream, steps)
-    return dict(wl=wl, cfg=cfg, x=x, total_ms=total_ms, sel_ms=sel_ms, att_ms=att_ms, k_ms=k_ms,
+    floor_us = latency_floor_us(stream, steps, len(k_ms))
+    return dict(wl=wl, cfg=cfg, x=x, total_ms=total_ms, unfused_ms=unfused_ms, k_ms=k_ms,
                 summ_ms=summ_ms, summ_bytes=summ_bytes, hot_us=hot_us, floor_us=floor_us)
 
 
-def latency_floor_us(stream, steps):
-    """Graph replay of `steps` x 4 dependent 256-workgroup kernels that do next
-    to nothing (the library's workspace fill of 1 MiB): the launch and
-    dependency cost a four-kernel decode step pays before moving any bytes."""
+def latency_floor_us(stream, steps, n_kernels):
+    """Graph replay of `steps` x n_kernels dependent 256-workgroup kernels that
+    do next to nothing (the library's workspace fill of 1 MiB): the launch and
+    dependency cost a decode step of that many kernels pays before moving any
+    bytes."""
     buf = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
     lib = ops.lib()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
         g.capture_begin()
-        for _ in range(4 * steps):
+        for _ in range(n_kernels * steps):
             lib.sparse_workspace_init(ctypes.c_void_p(buf.data_ptr()), buf.numel(),
                                       ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
         g.capture_end()
@@ -441,8 +454,7 @@ def write_counters(fetch_csv, write_csv):
            "copy_fetch_kib": max(cf), "copy_write_kib": max(cw),
            "fetch_scale": kib / max(cf), "write_scale": kib / max(cw), "kernels": {}}
     out["copy_scale"] = 1.0
-    for kname in ("decode_chunk_kernel", "decode_merge_kernel", "decode_attn_partial_kernel",
-                  "decode_combine_kernel"):
+    for kname in ("decode_chunk_kernel", "decode_fused_partial_kernel", "decode_combine_kernel"):
         f, w = pick(fetch, kname), pick(write, kname)
         if f is not None and w is not None:
             out["kernels"][kname] = {"fetch_kib": f, "write_kib": w,
@@ -484,20 +496,20 @@ def main():
     att_bytes, sel_bytes = wl.selected_kv_bytes(), wl.scoring_bytes()
     heads = wl.cfg["B"] * wl.cfg["Hkv"]
     nch = (wl.C + 255) // 256
+    # algorithmic bytes: the chunk winners count once per head (the merge
+    # inside every attention workgroup re-reads them from L2)
     kbytes = {
         "chunk": sel_bytes,
-        "merge": heads * nch * (wl.K * 8 + 8) + heads * wl.K * 8,
-        "partial": att_bytes,
+        "merge_partial": att_bytes + heads * nch * (wl.K * 8 + 8) + heads * wl.K * 8,
         "combine": heads * (wl.K + 1) * 4 * (wl.cfg["d"] + 2) * 4 + wl.cfg["Hq"] * wl.cfg["d"] * 2,
     }
-    names = {"chunk": "decode_chunk_kernel", "merge": "decode_merge_kernel",
-             "partial": "decode_attn_partial_kernel", "combine": "decode_combine_kernel"}
+    names = {"chunk": "decode_chunk_kernel", "merge_partial": "decode_fused_partial_kernel",
+             "combine": "decode_combine_kernel"}
     kern = {}
     for k, v in res["k_ms"].items():
         us = float(v.mean() * 1e3)
         kern[k] = dict(kernel=names[k], us=us, p99_us=float(np.percentile(v, 99) * 1e3),
                        bytes=kbytes[k], gbps=kbytes[k] / (us * 1e-6) / 1e9)
-    sel_us, att_us = float(res["sel_ms"].mean() * 1e3), float(res["att_ms"].mean() * 1e3)
     dom = max(kern, key=lambda n: kern[n]["us"])
     achieved = kern[dom]["gbps"]
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
@@ -520,17 +532,18 @@ def main():
         "config": {"workload": "decode_512k", "batch": 1, "context": wl.L - 1, "q_heads": 32,
                    "kv_heads": 8, "head_dim": 128, "block": wl.b, "K": wl.K, "gate": "softmax_log",
                    "layers_rotated": args.layers, "queries_rotated": args.queries, "graph_replay": True},
-        "selected_kv_gbps": round(att_bytes / (kern["partial"]["us"] * 1e-6) / 1e9, 1),
-        "stage_us": {"score_select": round(sel_us, 3), "attention": round(att_us, 3)},
+        "selected_kv_gbps": round(att_bytes / (kern["merge_partial"]["us"] * 1e-6) / 1e9, 1),
+        "unfused_us_per_step": round(res["unfused_ms"] * 1e3 / steps, 3),
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kern.items()},
         "hot_cache_us_per_step": round(res["hot_us"], 3),
         "summaries_512k_ms": round(res["summ_ms"], 3),
         "summaries_gbps": round(res["summ_bytes"] / (res["summ_ms"] * 1e-3) / 1e9, 1),
         "roofline": roofline,
-        # t >= (launch + dependency cost of the four kernels) + (all bytes at peak)
+        # t >= (launch + dependency cost of the step's kernels) + (all bytes at peak)
         "latency_floor": {
-            "four_kernel_step_us": round(res["floor_us"], 3),
+            "kernels_per_step": len(kern),
+            "kernel_chain_step_us": round(res["floor_us"], 3),
             "bytes_at_peak_us": round(sum(k["bytes"] for k in kern.values()) / (HBM_PEAK_GBPS * 1e3), 3),
             "bound_us": round(res["floor_us"] + sum(k["bytes"] for k in kern.values()) / (HBM_PEAK_GBPS * 1e3), 3),
         },

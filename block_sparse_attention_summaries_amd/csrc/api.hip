@@ -171,6 +171,33 @@ int check_select_bwd(const spa_select_args* a, const spa_select_grads* g, spa::S
   return SPA_OK;
 }
 
+int check_decode(const spa_decode_args* d, spa::SelectLaunch* sp, spa::AttnLaunch* ap) {
+  SPA_REQUIRE(d != nullptr && d->select != nullptr && d->attn != nullptr, SPA_ERR_INVALID_ARG,
+              "decode args, select and attn must be non-NULL");
+  int st = check_select(d->select, sp);
+  if (st != SPA_OK) return st;
+  st = check_attn(d->attn, ap);
+  if (st != SPA_OK) return st;
+  const spa_select_args* s = d->select;
+  const spa_attn_args* a = d->attn;
+  SPA_REQUIRE(s->nq == 1, SPA_ERR_UNSUPPORTED, "sparse_decode_step takes one query row (nq = %d)", s->nq);
+  SPA_REQUIRE(s->prefix_mode == SPA_PREFIX_CURRENT_BLOCK && a->prefix_mode == SPA_PREFIX_CURRENT_BLOCK,
+              SPA_ERR_UNSUPPORTED, "sparse_decode_step supports prefix_mode = CURRENT_BLOCK");
+  SPA_REQUIRE(a->local == SPA_LOCAL_CURRENT_BLOCK && a->window == 0 && a->alpha == nullptr, SPA_ERR_UNSUPPORTED,
+              "sparse_decode_step supports the current block + selected blocks mode");
+  SPA_REQUIRE(s->q == a->q && s->B == a->B && s->Hq == a->Hq && s->Hkv == a->Hkv && s->d == a->d &&
+                  s->dtype == a->dtype && s->q_pos0 == a->q_pos0 && s->b == a->b && s->K == a->K &&
+                  (s->share_group != 0) == (a->share_group != 0),
+              SPA_ERR_INVALID_ARG, "select and attn arguments describe different problems");
+  SPA_REQUIRE(a->idx == s->idx && a->logg == s->logg, SPA_ERR_INVALID_ARG,
+              "attn idx / logg must be the select outputs idx / logg");
+  return SPA_OK;
+}
+
+size_t decode_ws_bytes(const spa::SelectLaunch& sp, const spa::AttnLaunch& ap) {
+  return spa::align256(spa::select_workspace_bytes(sp)) + spa::attn_fwd_workspace_bytes(ap);
+}
+
 int check_ws(void* ws, size_t have, size_t need) {
   if (need == 0) return SPA_OK;
   SPA_REQUIRE(ws != nullptr && have >= need, SPA_ERR_WORKSPACE,
@@ -266,6 +293,23 @@ int sparse_select_bwd(const spa_select_args* a, const spa_select_grads* g, void*
                     "sparse_select_bwd");
 }
 
+int sparse_decode_step(const spa_decode_args* a, void* workspace, size_t ws_bytes, spa_stream_t stream) {
+  ProfileScope profile_scope;
+  spa::SelectLaunch sp;
+  spa::AttnLaunch ap;
+  int st = check_decode(a, &sp, &ap);
+  if (st != SPA_OK) return st;
+  st = check_ws(workspace, ws_bytes, decode_ws_bytes(sp, ap));
+  if (st != SPA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws_att = static_cast<char*>(workspace) + spa::align256(spa::select_workspace_bytes(sp));
+  if (spa::decode_fusable(sp))
+    return hip_status(spa::launch_decode_fused_attn(sp, workspace, ap, ws_att, s), "sparse_decode_step");
+  hipError_t e = spa::launch_score_select(sp, workspace, s);
+  if (e == hipSuccess) e = spa::launch_attn_fwd(ap, ws_att, s);
+  return hip_status(e, "sparse_decode_step");
+}
+
 size_t sparse_workspace_bytes(int op, const void* args) {
   switch (op) {
     case SPA_OP_SCORE_SELECT: {
@@ -283,6 +327,12 @@ size_t sparse_workspace_bytes(int op, const void* args) {
       if (check_attn(static_cast<const spa_attn_args*>(args), &p) != SPA_OK) return 0;
       spa::BwdLaunch bp{p, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
       return spa::attn_bwd_workspace_bytes(bp);
+    }
+    case SPA_OP_DECODE_STEP: {
+      spa::SelectLaunch sp;
+      spa::AttnLaunch ap;
+      if (check_decode(static_cast<const spa_decode_args*>(args), &sp, &ap) != SPA_OK) return 0;
+      return decode_ws_bytes(sp, ap);
     }
     case SPA_OP_SELECT_BWD: {
       spa::SelectLaunch p;

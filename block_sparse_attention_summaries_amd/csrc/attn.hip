@@ -21,6 +21,7 @@
 // segments 64 keys at a time with an online softmax.
 #include <type_traits>
 
+#include "decode_merge.h"
 #include "spa_device.h"
 #include "spa_launch.h"
 
@@ -158,6 +159,89 @@ __global__ __launch_bounds__(256) void decode_attn_partial_kernel(
       start = static_cast<int64_t>(c) * b + sub * kTileTok;
       ntok = b - sub * kTileTok < kTileTok ? b - sub * kTileTok : kTileTok;
       if (logg != nullptr) bias = logg[static_cast<int64_t>(bh) * K + unit];
+    }
+  } else {
+    start = c0 * b + sub * kTileTok;
+    const int64_t n = pos + 1 - start;
+    const int cap = b - sub * kTileTok < kTileTok ? b - sub * kTileTok : kTileTok;
+    ntok = n <= 0 ? 0 : (n < cap ? static_cast<int>(n) : cap);
+  }
+
+  const int64_t obase = (static_cast<int64_t>(bh) * ntiles + tile) * HPW;
+  if (ntok == 0) {
+    for (int x = tid; x < HPW * D; x += 256) ws_acc[obase * D + x] = 0.f;
+    if (tid < HPW) ws_ml[obase + tid] = make_float2(-INFINITY, 0.f);
+  } else {
+    tile_partial<T, D, HPW>(q, k, v, bi, hs, kvh, G, Hq, Hkv, share_group, L, start, ntok, bias,
+                            ws_acc, ws_ml, obase);
+  }
+}
+
+// Decode step with the top-K merge folded in: every workgroup of a kept
+// selected unit first runs the two-level merge of its head's chunk winners
+// (decode_merge.h) to learn which block its slot holds, instead of reading
+// idx written by a separate merge kernel; the workgroup of slot 0, tile 0
+// also writes the selection outputs (idx, log g, K_eff).  The current-block
+// workgroups need no merge.  Saves one dependent kernel per step; each
+// workgroup reads its head's chunk records (K x chunks x 8 bytes).
+template <typename T, int D, int HPW, int NV, int NV2>
+__global__ __launch_bounds__(256) void decode_fused_partial_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const uint64_t* __restrict__ ws_keys, const float2* __restrict__ ws_sel_ml, int nchunks, int64_t ncand,
+    int gate, int32_t* __restrict__ idx, float* __restrict__ logg, int32_t* __restrict__ k_eff, int Hq, int Hkv,
+    int Hsel, int share_group, int64_t L, int64_t pos, int b, int K, int tpu, float* __restrict__ ws_acc,
+    float2* __restrict__ ws_ml) {
+  __shared__ uint64_t s_win[4 * 64];
+  __shared__ float2 s_mlw[4];
+  __shared__ uint32_t s_lo[4];
+  __shared__ int32_t s_c;
+  __shared__ float s_lg;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int bh = blockIdx.y;
+  const int bi = bh / Hsel, hs = bh % Hsel;
+  const int G = Hq / Hkv;
+  const int kvh = share_group ? hs : hs / G;
+  const int unit = blockIdx.x / tpu, sub = blockIdx.x % tpu;
+  const int ntiles = (K + 1) * tpu;
+  const int tile = blockIdx.x;
+
+  int64_t start = 0;
+  int ntok = 0;
+  float bias = 0.f;
+  const int64_t c0 = pos / b;
+  if (unit < K) {
+    merge_level1<NV>(ws_keys + static_cast<int64_t>(bh) * nchunks * K,
+                     ws_sel_ml + static_cast<int64_t>(bh) * nchunks, nchunks, K, s_win, s_mlw, s_lo);
+    __syncthreads();
+    if (wave == 0) {
+      const bool out = unit == 0 && sub == 0;
+      const int64_t o = static_cast<int64_t>(bh) * K;      // one query row
+      const int kk = static_cast<int>(ncand < K ? ncand : K);
+      const int kept = merge_level2<NV2>(s_win, s_mlw, s_lo, K, kk, gate, [&](int slot, int32_t c, float lg) {
+        if (slot == unit) {
+          s_c = c;
+          s_lg = lg;
+        }
+        if (out) {
+          idx[o + slot] = c;
+          if (logg != nullptr) logg[o + slot] = lg;
+        }
+      });
+      if (lane == 0 && kept <= unit) s_c = -1;
+      if (out) {
+        for (int x = kept + lane; x < K; x += kWave) {
+          idx[o + x] = -1;
+          if (logg != nullptr) logg[o + x] = 0.f;
+        }
+        if (lane == 0 && k_eff != nullptr) k_eff[bh] = kk;
+      }
+    }
+    __syncthreads();
+    const int32_t c = s_c;
+    if (c >= 0 && c < c0) {
+      start = static_cast<int64_t>(c) * b + sub * kTileTok;
+      ntok = b - sub * kTileTok < kTileTok ? b - sub * kTileTok : kTileTok;
+      bias = s_lg;
     }
   } else {
     start = c0 * b + sub * kTileTok;
@@ -607,6 +691,62 @@ static hipError_t launch_decode_attn_h(const AttnLaunch& p, void* ws, hipStream_
   if (e != hipSuccess) return e;
   return launch(true, decode_combine_kernel<T, D, HPW>, dim3(HPW, static_cast<unsigned>(heads)), dim3(256), st,
                 acc, ml, p.Hq, p.Hkv, p.Hsel, p.share_group, ntiles, static_cast<T*>(p.o), p.lse);
+}
+
+template <int D, int HPW, int NV, int NV2>
+static hipError_t launch_fused_nv(const SelectLaunch& s, void* ws_sel, const AttnLaunch& p, void* ws,
+                                  hipStream_t st) {
+  const int tpu = decode_tpu(p);
+  const int ntiles = (p.K + 1) * tpu;
+  const size_t heads = static_cast<size_t>(p.B) * p.Hsel;
+  char* base = static_cast<char*>(ws);
+  float* acc = reinterpret_cast<float*>(base);
+  float2* ml = reinterpret_cast<float2*>(base + align256(heads * ntiles * HPW * p.d * sizeof(float)));
+  const DecodeSelectWs w = decode_select_ws(s, ws_sel);
+  hipError_t e = launch(false, decode_fused_partial_kernel<bf16_t, D, HPW, NV, NV2>,
+                        dim3(ntiles, static_cast<unsigned>(heads)), dim3(256), st, static_cast<const bf16_t*>(p.q),
+                        static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
+                        static_cast<const uint64_t*>(w.keys), static_cast<const float2*>(w.ml), w.nch, s.max_cand,
+                        s.gate, s.idx, s.logg, s.k_eff, p.Hq, p.Hkv, p.Hsel, p.share_group, p.L, p.q_pos0, p.b,
+                        p.K, tpu, acc, ml);
+  if (e != hipSuccess) return e;
+  return launch(true, decode_combine_kernel<bf16_t, D, HPW>, dim3(HPW, static_cast<unsigned>(heads)), dim3(256),
+                st, acc, ml, p.Hq, p.Hkv, p.Hsel, p.share_group, ntiles, static_cast<bf16_t*>(p.o), p.lse);
+}
+
+template <int D, int HPW>
+static hipError_t launch_fused_h(const SelectLaunch& s, void* ws_sel, const AttnLaunch& p, void* ws,
+                                 hipStream_t st) {
+  // level-2 survivors: 4 K records, NV2 per lane
+  const int nv = decode_merge_nv(s);
+  if (s.K <= 32) {
+    if (nv <= 2) return launch_fused_nv<D, HPW, 2, 2>(s, ws_sel, p, ws, st);
+    if (nv <= 4) return launch_fused_nv<D, HPW, 4, 2>(s, ws_sel, p, ws, st);
+    return launch_fused_nv<D, HPW, 8, 2>(s, ws_sel, p, ws, st);
+  }
+  if (nv <= 2) return launch_fused_nv<D, HPW, 2, 4>(s, ws_sel, p, ws, st);
+  if (nv <= 4) return launch_fused_nv<D, HPW, 4, 4>(s, ws_sel, p, ws, st);
+  return launch_fused_nv<D, HPW, 8, 4>(s, ws_sel, p, ws, st);
+}
+
+template <int D>
+static hipError_t launch_fused_d(const SelectLaunch& s, void* ws_sel, const AttnLaunch& p, void* ws,
+                                 hipStream_t st) {
+  switch (heads_per_wg(p)) {
+    case 1: return launch_fused_h<D, 1>(s, ws_sel, p, ws, st);
+    case 2: return launch_fused_h<D, 2>(s, ws_sel, p, ws, st);
+    case 4: return launch_fused_h<D, 4>(s, ws_sel, p, ws, st);
+    default: return launch_fused_h<D, 8>(s, ws_sel, p, ws, st);
+  }
+}
+
+// Chunk kernel, then the merge folded into the attention partials, then the
+// combine (bf16, decode_fusable selections only).
+hipError_t launch_decode_fused_attn(const SelectLaunch& s, void* ws_sel, const AttnLaunch& a, void* ws_att,
+                                    hipStream_t st) {
+  hipError_t e = launch_decode_chunks(s, ws_sel, st);
+  if (e != hipSuccess) return e;
+  return a.d == 64 ? launch_fused_d<64>(s, ws_sel, a, ws_att, st) : launch_fused_d<128>(s, ws_sel, a, ws_att, st);
 }
 
 template <typename T, int D>

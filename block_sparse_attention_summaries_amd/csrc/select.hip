@@ -24,6 +24,7 @@
 //    near ~10 is not decided by fp32 rounding.
 #include <type_traits>
 
+#include "decode_merge.h"
 #include "spa_device.h"
 #include "spa_launch.h"
 
@@ -35,25 +36,6 @@ namespace spa {
 // > T plus the lowest-index scores == T.  Candidates are laid out so that
 // position order is index order, which makes the lower-index tie rule and
 // the ascending output a single ordered compaction (ballot + mbcnt).
-
-// Ordered compaction of one wave's NV x 64 positions (position i*64 + lane):
-// keeps keys > t and the first `need_eq` keys == t; calls emit(slot, i) for
-// every kept position.  Returns the number kept.
-template <int NV, typename Emit>
-__device__ __forceinline__ int wave_select_ordered(const uint32_t (&key)[NV], uint32_t t, int need_eq,
-                                                   Emit&& emit) {
-  int kept = 0, eq_seen = 0;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const uint64_t eq = __ballot(key[i] == t && key[i] != 0u);
-    const bool take = key[i] > t || (key[i] == t && key[i] != 0u && eq_seen + lanes_below(eq) < need_eq);
-    const uint64_t tm = __ballot(take);
-    if (take) emit(kept + lanes_below(tm), i);
-    kept += __popcll(tm);
-    eq_seen += __popcll(eq);
-  }
-  return kept;
-}
 
 // One workgroup per (chunk of 256 candidate blocks, selection head).  All
 // global reads of the workgroup (the chunk's summaries, the query heads and,
@@ -200,12 +182,8 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(
   if (lane == 0) ws_ml[static_cast<int64_t>(bh) * nchunks + chunk] = make_float2(m, l);
 }
 
-// One workgroup (4 waves) per selection head.  The chunk winners are laid
-// out chunk by chunk, each in index order, so position order is index
-// order.  Wave w keeps the top-min(K, n) of its quarter of the chunks
-// (threshold search + ordered compaction), then wave 0 does the same over the
-// 4 x K survivors and writes the ascending indices and log gates; the LSE
-// comes from the chunk partials.  NV = records per lane in a quarter.
+// One workgroup (4 waves) per selection head: the two-level merge of the
+// chunk winners (decode_merge.h) writes the ascending indices and log gates.
 template <int NV, int NV2>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const uint64_t* __restrict__ ws_keys, const float2* __restrict__ ws_ml, int nchunks, int K,
@@ -213,74 +191,18 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     int32_t* __restrict__ k_eff) {
   __shared__ uint64_t s_win[4 * 64];
   __shared__ float2 s_ml[4];
+  __shared__ uint32_t s_lo[4];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int bh = blockIdx.x;
-  const uint64_t* rec = ws_keys + static_cast<int64_t>(bh) * nchunks * K;
-  // this wave's quarter of the chunks
-  const int c0 = (nchunks * wave) / 4, c1 = (nchunks * (wave + 1)) / 4;
-  const int n = (c1 - c0) * K;
-  uint64_t r[NV];
-  uint32_t key[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int pidx = i * kWave + lane;
-    r[i] = pidx < n ? rec[static_cast<int64_t>(c0) * K + pidx] : 0ull;
-  }
-  float m = -INFINITY, l = 0.f;
-  for (int ch = tid; ch < nchunks; ch += 256) {
-    const float2 v = ws_ml[static_cast<int64_t>(bh) * nchunks + ch];
-    ml_combine(m, l, v.x, v.y);
-  }
-  {
-    float m2 = xor_lanes_f<32>(m), l2 = xor_lanes_f<32>(l); ml_combine(m, l, m2, l2);
-    m2 = xor_lanes_f<16>(m); l2 = xor_lanes_f<16>(l); ml_combine(m, l, m2, l2);
-    m2 = xor_lanes_f<8>(m); l2 = xor_lanes_f<8>(l); ml_combine(m, l, m2, l2);
-    m2 = xor_lanes_f<4>(m); l2 = xor_lanes_f<4>(l); ml_combine(m, l, m2, l2);
-    m2 = xor_lanes_f<2>(m); l2 = xor_lanes_f<2>(l); ml_combine(m, l, m2, l2);
-    m2 = xor_lanes_f<1>(m); l2 = xor_lanes_f<1>(l); ml_combine(m, l, m2, l2);
-  }
-  if (lane == 0) s_ml[wave] = make_float2(m, l);
-  // level 1: this wave's top-min(K, valid) in index order
-  int nvalid = 0;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    key[i] = static_cast<uint32_t>(r[i] >> 32);
-    nvalid += __popcll(__ballot(key[i] != 0u));
-  }
-  const int k1 = nvalid < K ? nvalid : K;
-  const uint32_t t1 = wave_kth_largest<NV>(key, k1);
-  int ngt1 = 0;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) ngt1 += __popcll(__ballot(key[i] > t1));
-  const int kept1 = wave_select_ordered<NV>(key, t1, k1 - ngt1, [&](int slot, int i) {
-    s_win[wave * K + slot] = r[i];
-  });
-  for (int x = kept1 + lane; x < K; x += kWave) s_win[wave * K + x] = 0ull;
+  merge_level1<NV>(ws_keys + static_cast<int64_t>(bh) * nchunks * K, ws_ml + static_cast<int64_t>(bh) * nchunks,
+                   nchunks, K, s_win, s_ml, s_lo);
   __syncthreads();
   if (wave != 0) return;
-
-  // level 2: over the 4 x K survivors (positions in index order)
-  float mm = s_ml[0].x, ll = s_ml[0].y;
-  for (int w = 1; w < 4; ++w) ml_combine(mm, ll, s_ml[w].x, s_ml[w].y);
-  const float lse = mm + __logf(ll);
-  constexpr int kNV2 = NV2;                // 4 x K survivors: NV2 * 64 >= 4K
-  uint64_t r2[kNV2];
-  uint32_t key2[kNV2];
-#pragma unroll
-  for (int i = 0; i < kNV2; ++i) {
-    const int pidx = i * kWave + lane;
-    r2[i] = pidx < 4 * K ? s_win[pidx] : 0ull;
-    key2[i] = static_cast<uint32_t>(r2[i] >> 32);
-  }
-  const int kk = static_cast<int>(ncand < K ? ncand : K);
-  const uint32_t t = wave_kth_largest<kNV2>(key2, kk);
-  int ngt = 0;
-#pragma unroll
-  for (int i = 0; i < kNV2; ++i) ngt += __popcll(__ballot(key2[i] > t));
   const int64_t o = static_cast<int64_t>(bh) * K;          // one query row
-  const int kept = wave_select_ordered<kNV2>(key2, t, kk - ngt, [&](int slot, int i) {
-    idx[o + slot] = static_cast<int32_t>(static_cast<uint32_t>(r2[i]));
-    if (logg != nullptr) logg[o + slot] = gate ? from_orderable_f32(key2[i]) - lse : 0.f;
+  const int kk = static_cast<int>(ncand < K ? ncand : K);
+  const int kept = merge_level2<NV2>(s_win, s_ml, s_lo, K, kk, gate, [&](int slot, int32_t c, float lg) {
+    idx[o + slot] = c;
+    if (logg != nullptr) logg[o + slot] = lg;
   });
   for (int x = kept + lane; x < K; x += kWave) {
     idx[o + x] = -1;
@@ -442,22 +364,38 @@ static bool use_decode_path(const SelectLaunch& p) {
 
 size_t select_workspace_bytes(const SelectLaunch& p) {
   if (!use_decode_path(p)) return 0;
-  const int64_t nch = decode_num_chunks(p.max_cand > 0 ? p.max_cand : 1);
-  const size_t heads = static_cast<size_t>(p.B) * p.Hsel;
-  return align256(heads * nch * p.K * sizeof(uint64_t)) + align256(heads * nch * sizeof(float2));
+  return decode_select_ws(p, nullptr).bytes;
+}
+
+template <typename T, int D>
+static hipError_t launch_chunks_t(const SelectLaunch& p, void* ws, hipStream_t st) {
+  const DecodeSelectWs w = decode_select_ws(p, ws);
+  return launch(false, decode_chunk_kernel<T, D>, dim3(w.nch, static_cast<unsigned>(p.B * p.Hsel)), dim3(256),
+                st, static_cast<const T*>(p.q), static_cast<const T*>(p.kbar), p.proj_w, p.Hq, p.Hkv, p.Hsel,
+                p.share_group, p.ccap, p.max_cand, p.K, w.keys, w.ml, w.nch);
+}
+
+bool decode_fusable(const SelectLaunch& p) {
+  return use_decode_path(p) && p.dtype == kDtypeBf16 && merge_nv(p) <= kFusedMergeMaxNV;
+}
+
+int decode_merge_nv(const SelectLaunch& p) { return merge_nv(p); }
+
+hipError_t launch_decode_chunks(const SelectLaunch& p, void* ws, hipStream_t st) {
+  if (p.dtype == kDtypeBf16)
+    return p.d == 64 ? launch_chunks_t<bf16_t, 64>(p, ws, st) : launch_chunks_t<bf16_t, 128>(p, ws, st);
+  return p.d == 64 ? launch_chunks_t<float, 64>(p, ws, st) : launch_chunks_t<float, 128>(p, ws, st);
 }
 
 template <typename T, int D>
 static hipError_t launch_decode_t(const SelectLaunch& p, void* ws, hipStream_t st) {
   const int64_t ncand = p.max_cand;
-  const int nch = static_cast<int>(decode_num_chunks(ncand > 0 ? ncand : 1));
   const size_t heads = static_cast<size_t>(p.B) * p.Hsel;
-  char* base = static_cast<char*>(ws);
-  uint64_t* keys = reinterpret_cast<uint64_t*>(base);
-  float2* ml = reinterpret_cast<float2*>(base + align256(heads * nch * p.K * sizeof(uint64_t)));
-  hipError_t e = launch(false, decode_chunk_kernel<T, D>, dim3(nch, static_cast<unsigned>(heads)), dim3(256),
-                        st, static_cast<const T*>(p.q), static_cast<const T*>(p.kbar), p.proj_w, p.Hq,
-                        p.Hkv, p.Hsel, p.share_group, p.ccap, ncand, p.K, keys, ml, nch);
+  const DecodeSelectWs w = decode_select_ws(p, ws);
+  const int nch = w.nch;
+  uint64_t* keys = w.keys;
+  float2* ml = w.ml;
+  hipError_t e = launch_chunks_t<T, D>(p, ws, st);
   if (e != hipSuccess) return e;
   void (*merge)(const uint64_t*, const float2*, int, int, int64_t, int, int32_t*, float*, int32_t*);
   const bool small_k = p.K <= 32;

@@ -247,21 +247,47 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u)));
 }
 
-// Largest value T such that at least k of the wave's NV x 64 keys are >= T
-// (the k-th largest key; 0 if k == 0 or nothing qualifies).  Bitwise search
-// from the top bit; each step counts with ballots, so the count never leaves
-// the scalar unit.  Keys equal to 0 never count.
+// Top-k threshold of the wave's NV x 64 keys: returns t with
+// count(key > t) <= k <= count(key >= t), so that the keys > t plus the
+// first k - count(key > t) keys == t are exactly a top k (0xFFFFFFFF if
+// k == 0).  Bitwise search from the top bit; each step counts with ballots,
+// so the count never leaves the scalar unit.  The search stops as soon as
+// count(key >= t) == k (the kept set is then decided), and when lo <= T <= hi
+// is known for the k-th largest key T, it starts below their common top bits.
+// Keys equal to 0 never count.
 template <int NV>
-__device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t (&key)[NV], int k) {
-  uint32_t t = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+__device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t (&key)[NV], int k, uint32_t lo = 0u,
+                                                     uint32_t hi = 0xFFFFFFFFu) {
+  if (k <= 0) return 0xFFFFFFFFu;
+  const uint32_t diff = lo ^ hi;
+  if (diff == 0u) return lo;
+  const int top = 31 - __builtin_clz(diff);
+  uint32_t t = lo & ~((2u << top) - 1u);   // common prefix of lo and hi (top == 31: nothing)
+  for (int bit = top; bit >= 0; --bit) {
     const uint32_t cand = t | (1u << bit);
     int cnt = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) cnt += __popcll(__ballot(key[i] >= cand));
-    if (cnt >= k) t = cand;
+    if (cnt >= k) {
+      t = cand;
+      if (cnt == k) break;
+    }
   }
-  return k > 0 ? t : 0xFFFFFFFFu;
+  return t;
+}
+
+// Largest key of the wave (0 if none).
+template <int NV>
+__device__ __forceinline__ uint32_t wave_max_key(const uint32_t (&key)[NV]) {
+  uint32_t m = key[0];
+#pragma unroll
+  for (int i = 1; i < NV; ++i) m = key[i] > m ? key[i] : m;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off));
+    m = o > m ? o : m;
+  }
+  return m;
 }
 
 // Online-softmax combine of (m, l) pairs: result represents l e^m.

@@ -121,6 +121,29 @@ inline int64_t decode_num_chunks(int64_t max_cand) {
 // Workspace layout helpers (bytes, 256-aligned sections).
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Decode-path selection workspace: per (selection head, chunk) the chunk's
+// top-K records, then its (max, sum exp).
+struct DecodeSelectWs {
+  uint64_t* keys;
+  float2* ml;
+  int nch;
+  size_t bytes;
+};
+inline DecodeSelectWs decode_select_ws(const SelectLaunch& p, void* ws) {
+  const int64_t nch = decode_num_chunks(p.max_cand > 0 ? p.max_cand : 1);
+  const size_t heads = static_cast<size_t>(p.B) * p.Hsel;
+  const size_t kbytes = align256(heads * nch * p.K * sizeof(uint64_t));
+  char* base = static_cast<char*>(ws);
+  return DecodeSelectWs{reinterpret_cast<uint64_t*>(base), reinterpret_cast<float2*>(base + kbytes),
+                        static_cast<int>(nch), kbytes + align256(heads * nch * sizeof(float2))};
+}
+
+// Element type codes of the launch structs (the C ABI's spa_dtype values).
+constexpr int kDtypeF32 = 0, kDtypeBf16 = 1;
+
+// Largest records-per-lane of a merge wave the fused decode kernel is built for.
+constexpr int kFusedMergeMaxNV = 8;
+
 
 size_t select_workspace_bytes(const SelectLaunch& p);
 size_t select_bwd_workspace_bytes(const SelectLaunch& p);
@@ -130,6 +153,11 @@ size_t attn_bwd_workspace_bytes(const BwdLaunch& p);
 hipError_t launch_block_summaries(const SummaryLaunch& p, hipStream_t st);
 hipError_t launch_score_select(const SelectLaunch& p, void* ws, hipStream_t st);
 hipError_t launch_select_bwd(const SelectLaunch& p, const SelectGrads& g, void* ws, hipStream_t st);
+bool decode_fusable(const SelectLaunch& p);
+int decode_merge_nv(const SelectLaunch& p);
+hipError_t launch_decode_chunks(const SelectLaunch& p, void* ws, hipStream_t st);
+hipError_t launch_decode_fused_attn(const SelectLaunch& s, void* ws_sel, const AttnLaunch& a, void* ws_att,
+                                    hipStream_t st);
 bool rows_select_mfma_supported(const SelectLaunch& p);
 hipError_t launch_rows_select_mfma(const SelectLaunch& p, hipStream_t st);
 hipError_t launch_attn_fwd(const AttnLaunch& p, void* ws, hipStream_t st);

@@ -6,7 +6,8 @@ There is no fallback: if the library is missing or its call fails, these
 functions raise.
 
 Function names match the C entry points: sparse_block_summaries,
-sparse_score_select, sparse_attn_fwd, sparse_attn_bwd, sparse_select_bwd.
+sparse_score_select, sparse_attn_fwd, sparse_attn_bwd, sparse_select_bwd,
+sparse_decode_step.
 """
 from __future__ import annotations
 
@@ -23,11 +24,11 @@ SPA_DTYPE_F32, SPA_DTYPE_BF16 = 0, 1
 SPA_PREFIX_CURRENT_BLOCK, SPA_PREFIX_QUERY_BLOCK = 0, 1
 SPA_GATE_NONE, SPA_GATE_SOFTMAX_LOG = 0, 1
 SPA_LOCAL_CURRENT_BLOCK, SPA_LOCAL_NONE = 0, 1
-SPA_OP_SCORE_SELECT, SPA_OP_ATTN_FWD, SPA_OP_ATTN_BWD, SPA_OP_SELECT_BWD = 1, 2, 3, 4
+SPA_OP_SCORE_SELECT, SPA_OP_ATTN_FWD, SPA_OP_ATTN_BWD, SPA_OP_SELECT_BWD, SPA_OP_DECODE_STEP = 1, 2, 3, 4, 5
 
 EXPORTED = ["spa_abi_version", "spa_profile_next_call", "spa_last_error", "sparse_block_summaries", "sparse_score_select",
-            "sparse_attn_fwd", "sparse_attn_bwd", "sparse_select_bwd", "sparse_workspace_bytes",
-            "sparse_workspace_init"]
+            "sparse_attn_fwd", "sparse_attn_bwd", "sparse_select_bwd", "sparse_decode_step",
+            "sparse_workspace_bytes", "sparse_workspace_init"]
 
 _vp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
 
@@ -49,6 +50,10 @@ class AttnArgs(ctypes.Structure):
                 ("nq", _i), ("d", _i), ("L", _i64), ("q_pos0", _i64), ("b", _i), ("prefix_mode", _i),
                 ("qblock", _i), ("idx", _vp), ("logg", _vp), ("K", _i), ("share_group", _i),
                 ("local", _i), ("window", _i), ("alpha", _vp), ("o", _vp), ("lse", _vp)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("select", ctypes.POINTER(SelectArgs)), ("attn", ctypes.POINTER(AttnArgs))]
 
 
 class SpaError(RuntimeError):
@@ -86,6 +91,8 @@ def lib():
                                       _sz, _vp]
         L.sparse_select_bwd.restype = _i
         L.sparse_select_bwd.argtypes = [ctypes.POINTER(SelectArgs), ctypes.POINTER(SelectGrads), _vp, _sz, _vp]
+        L.sparse_decode_step.restype = _i
+        L.sparse_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp, _sz, _vp]
         L.sparse_workspace_bytes.restype = _sz
         L.sparse_workspace_bytes.argtypes = [_i, _vp]
         L.sparse_workspace_init.restype = _i
@@ -268,3 +275,20 @@ def sparse_select_bwd(q, kbar, max_norm, centre, idx, logg, dg, *, dq=None, dkba
     buf, size = _ws(workspace, SPA_OP_SELECT_BWD, a, q.device)
     _check(lib().sparse_select_bwd(ctypes.byref(a), ctypes.byref(g), _p(buf), size, _stream(stream)))
     return dq, dkbar, dproj_w
+
+
+def sparse_decode_step(q, kbar, max_norm, centre, k, v, *, Hkv, b, K, q_pos0, gate=True, share_group=True,
+                       proj_w=None, idx=None, logg=None, k_eff=None, o=None, lse=None, workspace=None,
+                       stream=None):
+    """One decode step (nq = 1): score + gate + top-K over the summaries, then
+    attention over the current block and the selected blocks.  Returns
+    (idx, logg, k_eff, o, lse)."""
+    sa, (idx, logg, k_eff) = select_args(q, kbar, max_norm, centre, Hkv=Hkv, b=b, K=K, q_pos0=q_pos0, gate=gate,
+                                         share_group=share_group, proj_w=proj_w, idx=idx, logg=logg,
+                                         k_eff=k_eff)
+    aa, (o, lse) = attn_args(q, k, v, idx, logg, b=b, K=K, q_pos0=q_pos0, share_group=share_group, o=o,
+                             lse=lse)
+    da = DecodeArgs(select=ctypes.pointer(sa), attn=ctypes.pointer(aa))
+    buf, size = _ws(workspace, SPA_OP_DECODE_STEP, da, q.device)
+    _check(lib().sparse_decode_step(ctypes.byref(da), _p(buf), size, _stream(stream)))
+    return idx, logg, k_eff, o, lse

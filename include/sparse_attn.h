@@ -86,7 +86,8 @@ typedef enum { SPA_PREFIX_CURRENT_BLOCK = 0, SPA_PREFIX_QUERY_BLOCK = 1 } spa_pr
 typedef enum { SPA_GATE_NONE = 0, SPA_GATE_SOFTMAX_LOG = 1 } spa_gate;
 typedef enum { SPA_LOCAL_CURRENT_BLOCK = 0, SPA_LOCAL_NONE = 1 } spa_local;
 typedef enum {
-    SPA_OP_SCORE_SELECT = 1, SPA_OP_ATTN_FWD = 2, SPA_OP_ATTN_BWD = 3, SPA_OP_SELECT_BWD = 4
+    SPA_OP_SCORE_SELECT = 1, SPA_OP_ATTN_FWD = 2, SPA_OP_ATTN_BWD = 3, SPA_OP_SELECT_BWD = 4,
+    SPA_OP_DECODE_STEP = 5
 } spa_op;
 
 /* Version of this ABI (SPA_ABI_VERSION). */
@@ -203,6 +204,28 @@ typedef struct spa_attn_args {
 int sparse_attn_fwd(const spa_attn_args *a, void *workspace, size_t ws_bytes,
                     spa_stream_t stream);
 
+typedef struct spa_decode_args {
+    const spa_select_args *select;   /* one query row (nq = 1), prefix_mode = CURRENT_BLOCK */
+    const spa_attn_args *attn;       /* same q, shapes, b, K and GQA mode; idx / logg are
+                                        select's outputs; local = CURRENT_BLOCK, no window */
+} spa_decode_args;
+
+/*
+ * sparse_decode_step -- one decode step of the hot path: sparse_score_select
+ * then sparse_attn_fwd on its selection ("SAS" review Alg. 1 then §4.3 Eq. 9
+ * for one new token; "Monodratic" news page: local block plus exact softmax
+ * on the selected blocks).  Same outputs, bit for bit, as the two calls made
+ * in sequence: idx, logg, k_eff of `select`, o and lse of `attn`.  For bf16
+ * with the chunked selection (up to 512 chunk winners per merge wave) the
+ * top-K merge runs inside the attention workgroups, which saves one dependent
+ * kernel per step; otherwise the two calls' kernels run in sequence.  Needs
+ * a workspace of sparse_workspace_bytes(SPA_OP_DECODE_STEP, spa_decode_args*);
+ * caller-owned, contents on entry ignored.  Errors: as the two calls, plus
+ * SPA_ERR_INVALID_ARG when select and attn disagree.
+ */
+int sparse_decode_step(const spa_decode_args *a, void *workspace, size_t ws_bytes,
+                       spa_stream_t stream);
+
 /*
  * sparse_attn_bwd -- backward of sparse_attn_fwd in the SAS mode
  * (local = CURRENT_BLOCK, window = 0, alpha = NULL), recomputing the
@@ -264,7 +287,7 @@ int sparse_select_bwd(const spa_select_args *a, const spa_select_grads *g, void 
 
 /* Workspace bytes needed by `op` (spa_op) for the given argument struct
  * (spa_select_args* for SPA_OP_SCORE_SELECT and SPA_OP_SELECT_BWD,
- * spa_attn_args* otherwise).
+ * spa_decode_args* for SPA_OP_DECODE_STEP, spa_attn_args* otherwise).
  * Returns 0 for invalid arguments (see spa_last_error()). */
 size_t sparse_workspace_bytes(int op, const void *args);
 

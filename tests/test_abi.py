@@ -180,6 +180,27 @@ def test_select_bwd_rejects_unsupported_modes():
         rows * 8 + shares + rows * 128 * 2 + rows * 128 * 4 + 256 * 128 * 128 * 4
 
 
+def test_decode_step_validation_and_workspace():
+    lib = ops.lib()
+    sel, att = _sel(), _attn()
+    da = ops.DecodeArgs(select=ctypes.pointer(sel), attn=ctypes.pointer(att))
+    need = lib.sparse_workspace_bytes(ops.SPA_OP_DECODE_STEP, ctypes.byref(da))
+    need_sel = lib.sparse_workspace_bytes(ops.SPA_OP_SCORE_SELECT, ctypes.byref(sel))
+    need_att = lib.sparse_workspace_bytes(ops.SPA_OP_ATTN_FWD, ctypes.byref(att))
+    assert need == 256 * ((need_sel + 255) // 256) + need_att
+    assert lib.sparse_decode_step(ctypes.byref(da), FAKE, need - 1, None) == ops.SPA_ERR_WORKSPACE
+
+    def status(s, a):
+        d = ops.DecodeArgs(select=ctypes.pointer(s), attn=ctypes.pointer(a))
+        return lib.sparse_decode_step(ctypes.byref(d), FAKE, 1 << 30, None)
+    assert status(_sel(), _attn(K=8)) == ops.SPA_ERR_INVALID_ARG                  # different K
+    assert status(_sel(), _attn(idx=FAKE_ODD)) == ops.SPA_ERR_INVALID_ARG         # not select's idx
+    assert status(_sel(), _attn(q=ctypes.c_void_p(0x20000))) == ops.SPA_ERR_INVALID_ARG
+    assert status(_sel(nq=2, q_pos0=32830), _attn(nq=2, q_pos0=32830)) == ops.SPA_ERR_UNSUPPORTED
+    assert status(_sel(), _attn(local=1, window=64, alpha=FAKE)) == ops.SPA_ERR_UNSUPPORTED
+    assert lib.sparse_decode_step(None, FAKE, 1 << 30, None) == ops.SPA_ERR_INVALID_ARG
+
+
 def test_summaries_rejects_invalid_arguments():
     lib = ops.lib()
     f = lib.sparse_block_summaries

@@ -113,6 +113,10 @@ def _decode_run(cfg, x, K=None):
                                                     proj_w=None if proj is None else dev(proj), **kw)
     o_g, lse_g = ops.sparse_attn_fwd(qd, kd, vd, idx_g, logg_g if gate else None, b=b, K=K,
                                      q_pos0=q_pos0, share_group=cfg["share_group"])
+    # the same step through the one-call entry point (merge folded into the
+    # attention workgroups where supported)
+    f_idx, f_logg, f_keff, f_o, f_lse = ops.sparse_decode_step(
+        qd, kb_g, mx_g, ce_g, kd, vd, proj_w=None if proj is None else dev(proj), **kw)
     # attention alone, on the oracle's selection
     lg_in = dev(ora["logg"].astype(np.float32)) if gate else None
     o_g2, lse_g2 = ops.sparse_attn_fwd(qd, kd, vd, dev(ora["idx"]), lg_in, b=b, K=K, q_pos0=q_pos0,
@@ -120,16 +124,33 @@ def _decode_run(cfg, x, K=None):
     torch.cuda.synchronize()
     return dict(ora=ora, o_o=o_o, lse_o=lse_o, idx=host(idx_g), logg=None if logg_g is None else host(logg_g),
                 keff=host(keff_g), o=host(o_g), lse=host(lse_g), o2=host(o_g2), lse2=host(lse_g2),
-                kb_o=kb_o, mx_o=mx_o, ce_o=ce_o)
+                kb_o=kb_o, mx_o=mx_o, ce_o=ce_o,
+                fused=dict(idx=host(f_idx), logg=None if f_logg is None else host(f_logg), keff=host(f_keff),
+                           o=host(f_o), lse=host(f_lse)))
 
 
 def _check_decode(cfg, x, r):
-    ora, tol = r["ora"], _tol(cfg)
-    ex = check_indices(r["idx"], ora)
-    assert np.array_equal(r["keff"], ora["k_eff"])
-    match = np.all(r["idx"] == ora["idx"], axis=-1)            # [B, Hsel, 1]
+    ex = _check_decode_chain(cfg, r, r)
+    # the one-call decode step: same checks against the oracle, and the same
+    # bits as the two calls it stands for
+    f = r["fused"]
+    _check_decode_chain(cfg, r, f)
+    for key in ("idx", "keff", "o", "lse"):
+        assert np.array_equal(f[key], r[key]), key
     if cfg["gate"]:
-        d = np.abs(r["logg"].astype(np.float64) - ora["logg"])
+        assert np.array_equal(f["logg"], r["logg"])
+    return ex
+
+
+def _check_decode_chain(cfg, r, c):
+    """Selection and end-to-end output of one GPU chain c (idx, logg, keff,
+    o) against the oracle; attention alone on the oracle's selection."""
+    ora, tol = r["ora"], _tol(cfg)
+    ex = check_indices(c["idx"], ora)
+    assert np.array_equal(c["keff"], ora["k_eff"])
+    match = np.all(c["idx"] == ora["idx"], axis=-1)            # [B, Hsel, 1]
+    if cfg["gate"]:
+        d = np.abs(c["logg"].astype(np.float64) - ora["logg"])
         assert d[match].max(initial=0.0) <= 1e-4 * max(1.0, np.abs(ora["logg"]).max())
     # attention alone (oracle selection on both sides)
     assert rel_err(r["o2"], r["o_o"]) <= tol, rel_err(r["o2"], r["o_o"])
@@ -140,7 +161,7 @@ def _check_decode(cfg, x, r):
     for bi in range(cfg["B"]):
         for h in range(cfg["Hq"]):
             if hmatch[bi, h]:
-                e = rel_err(r["o"][bi:bi + 1, h:h + 1], r["o_o"][bi:bi + 1, h:h + 1])
+                e = rel_err(c["o"][bi:bi + 1, h:h + 1], r["o_o"][bi:bi + 1, h:h + 1])
                 assert e <= tol, (bi, h, e)
     return ex
 
@@ -190,6 +211,21 @@ def test_decode_all_blocks_is_dense_attention():
     vt = torch.from_numpy(as_f64(x["v"]))
     ref = F.scaled_dot_product_attention(qt, kt, vt).numpy()
     assert rel_err(r["o"], ref) <= 1e-4
+
+
+def test_decode_ties_take_lower_indices():
+    """Every key equal: every candidate block scores the same, so the top-K
+    is the K lowest block indices (ties go to the lower index) and the gates
+    are all -log C; both the two-call chain and the one-call step."""
+    cfg = config("decode_32k", n=8192, seed=16)
+    x = make_inputs(cfg)
+    x["k"] = np.ascontiguousarray(np.broadcast_to(x["k"][:, :, :1, :], x["k"].shape))
+    r = _decode_run(cfg, x)
+    C = x["q_pos0"] // cfg["b"]
+    want = np.broadcast_to(np.arange(cfg["K"], dtype=np.int32), r["idx"].shape)
+    for c in (r, r["fused"]):
+        assert np.array_equal(c["idx"], want)
+        assert np.allclose(c["logg"], -np.log(C), rtol=0, atol=1e-5)
 
 
 def test_decode_is_deterministic():
