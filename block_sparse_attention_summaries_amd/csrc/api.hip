@@ -248,6 +248,43 @@ int sparse_block_summaries(const void* k, int dtype, int B, int Hkv, int64_t L, 
   return hip_status(spa::launch_block_summaries(p, static_cast<hipStream_t>(stream)), "sparse_block_summaries");
 }
 
+int check_pages(const spa_kv_pages* pg, int64_t blocks_needed, spa::KvPages* out) {
+  SPA_REQUIRE(pg != nullptr && pg->block_table != nullptr, SPA_ERR_INVALID_ARG, "pages and block_table must be non-NULL");
+  SPA_REQUIRE(pg->num_pages >= 1, SPA_ERR_INVALID_ARG, "num_pages must be >= 1");
+  SPA_REQUIRE(pg->table_stride >= blocks_needed, SPA_ERR_INVALID_ARG,
+              "table_stride = %lld but %lld logical blocks are addressed", static_cast<long long>(pg->table_stride),
+              static_cast<long long>(blocks_needed));
+  *out = spa::KvPages{pg->block_table, pg->table_stride, pg->num_pages};
+  return SPA_OK;
+}
+
+int sparse_block_summaries_paged(const void* k_pages, int dtype, int B, int Hkv, int64_t L, int d, int b,
+                                 const spa_kv_pages* pages, int64_t first_block, int64_t num_blocks, int64_t ccap,
+                                 void* kbar, float* max_norm, float* centre, spa_stream_t stream) {
+  ProfileScope profile_scope;
+  int st = check_heads(B, Hkv, Hkv, d, dtype);
+  if (st != SPA_OK) return st;
+  SPA_REQUIRE(k_pages && kbar && max_norm, SPA_ERR_INVALID_ARG, "k_pages, kbar and max_norm must be non-NULL");
+  SPA_REQUIRE(aligned16(k_pages), SPA_ERR_INVALID_ARG, "k_pages must be 16-byte aligned");
+  SPA_REQUIRE(pow2(b) && b >= 16 && b <= 128, SPA_ERR_UNSUPPORTED,
+              "block size b = %d not supported (power of two in [16, 128])", b);
+  SPA_REQUIRE(first_block >= 0 && num_blocks >= 0, SPA_ERR_INVALID_ARG,
+              "first_block and num_blocks must be >= 0");
+  SPA_REQUIRE((first_block + num_blocks) * b <= L, SPA_ERR_INVALID_ARG,
+              "blocks [%lld, %lld) are not all full in L = %lld", static_cast<long long>(first_block),
+              static_cast<long long>(first_block + num_blocks), static_cast<long long>(L));
+  SPA_REQUIRE(first_block + num_blocks <= ccap, SPA_ERR_INVALID_ARG, "ccap = %lld too small",
+              static_cast<long long>(ccap));
+  SPA_REQUIRE(num_blocks < (static_cast<int64_t>(1) << 31), SPA_ERR_UNSUPPORTED, "too many blocks");
+  spa::KvPages kp;
+  st = check_pages(pages, first_block + num_blocks, &kp);
+  if (st != SPA_OK) return st;
+  if (num_blocks == 0) return ok();
+  spa::SummaryLaunch p{k_pages, dtype, B, Hkv, L, d, b, first_block, num_blocks, ccap, kbar, max_norm, centre, kp};
+  return hip_status(spa::launch_block_summaries(p, static_cast<hipStream_t>(stream)),
+                    "sparse_block_summaries_paged");
+}
+
 int sparse_score_select(const spa_select_args* a, void* workspace, size_t ws_bytes, spa_stream_t stream) {
   ProfileScope profile_scope;
   spa::SelectLaunch p;
@@ -308,6 +345,26 @@ int sparse_decode_step(const spa_decode_args* a, void* workspace, size_t ws_byte
   hipError_t e = spa::launch_score_select(sp, workspace, s);
   if (e == hipSuccess) e = spa::launch_attn_fwd(ap, ws_att, s);
   return hip_status(e, "sparse_decode_step");
+}
+
+int sparse_decode_step_paged(const spa_decode_args* a, const spa_kv_pages* pages, void* workspace,
+                             size_t ws_bytes, spa_stream_t stream) {
+  ProfileScope profile_scope;
+  spa::SelectLaunch sp;
+  spa::AttnLaunch ap;
+  int st = check_decode(a, &sp, &ap);
+  if (st != SPA_OK) return st;
+  st = check_pages(pages, (ap.L + ap.b - 1) / ap.b, &ap.pages);
+  if (st != SPA_OK) return st;
+  st = check_ws(workspace, ws_bytes, decode_ws_bytes(sp, ap));
+  if (st != SPA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws_att = static_cast<char*>(workspace) + spa::align256(spa::select_workspace_bytes(sp));
+  if (spa::decode_fusable(sp))
+    return hip_status(spa::launch_decode_fused_attn(sp, workspace, ap, ws_att, s), "sparse_decode_step_paged");
+  hipError_t e = spa::launch_score_select(sp, workspace, s);
+  if (e == hipSuccess) e = spa::launch_attn_fwd(ap, ws_att, s);
+  return hip_status(e, "sparse_decode_step_paged");
 }
 
 size_t sparse_workspace_bytes(int op, const void* args) {

@@ -36,10 +36,9 @@ constexpr int kTileTok = 64;
 // global loads are unconditional (rows past ntok are clamped to the last
 // valid row and masked out of the softmax).
 template <typename T, int D, int HPW>
-__device__ __forceinline__ void tile_partial(const T* __restrict__ q, const T* __restrict__ k,
-                                             const T* __restrict__ v, int bi, int hs, int kvh, int G,
-                                             int Hq, int Hkv, int share_group, int64_t L, int64_t start,
-                                             int ntok, float bias, float* __restrict__ ws_acc,
+__device__ __forceinline__ void tile_partial(const T* __restrict__ q, const T* __restrict__ kt,
+                                             const T* __restrict__ vt, int bi, int hs, int G, int Hq,
+                                             int share_group, int ntok, float bias, float* __restrict__ ws_acc,
                                              float2* __restrict__ ws_ml, int64_t obase) {
   constexpr int kVec = Elem<T>::kVec;
   constexpr int kVPR = D / kVec;                     // 16-byte vectors per row
@@ -63,15 +62,14 @@ __device__ __forceinline__ void tile_partial(const T* __restrict__ q, const T* _
     const int hq = share_group ? hs * G + hh : hs;
     qv[it] = ld_f(q + (static_cast<int64_t>(bi) * Hq + hq) * D + e);
   }
-  const int64_t kvrow0 = (static_cast<int64_t>(bi) * Hkv + kvh) * L + start;
   uint4 rk[kIters], rv[kIters];
 #pragma unroll
   for (int it = 0; it < kIters; ++it) {
     const int x = tid + it * 256;
     const int r = x / kVPR, cv = x % kVPR;
     const int rr = r < ntok ? r : ntok - 1;
-    rk[it] = *reinterpret_cast<const uint4*>(k + (kvrow0 + rr) * D + cv * kVec);
-    rv[it] = *reinterpret_cast<const uint4*>(v + (kvrow0 + rr) * D + cv * kVec);
+    rk[it] = *reinterpret_cast<const uint4*>(kt + static_cast<int64_t>(rr) * D + cv * kVec);
+    rv[it] = *reinterpret_cast<const uint4*>(vt + static_cast<int64_t>(rr) * D + cv * kVec);
   }
 #pragma unroll
   for (int it = 0; it < kQIters; ++it) {
@@ -134,12 +132,31 @@ __device__ __forceinline__ void tile_partial(const T* __restrict__ q, const T* _
 // them with the softmax weights exp(m_t - M).
 constexpr int kMaxTiles = 130;   // (K + 1) * tiles per unit for K <= 64, b <= 128
 
+// Offset (elements) of the first of the rows [start, start + ntok) of
+// (batch bi, kv head kvh) in the K / V cache, which never cross a block:
+// contiguous [B, Hkv, L, d], or through the page table into a pool
+// [npages, Hkv, b, d].  An unmapped page (id outside the pool) empties the
+// tile (ntok = 0).
+template <int D>
+__device__ __forceinline__ int64_t kv_tile_offset(int bi, int kvh, int Hkv, int64_t L, int b, int64_t start,
+                                                  int& ntok, const int32_t* __restrict__ table, int64_t tstride,
+                                                  int64_t npages) {
+  if (table == nullptr) return ((static_cast<int64_t>(bi) * Hkv + kvh) * L + start) * D;
+  const int64_t blk = start / b;
+  const int64_t pg = table[static_cast<int64_t>(bi) * tstride + blk];
+  if (pg < 0 || pg >= npages) {
+    ntok = 0;
+    return 0;
+  }
+  return ((pg * Hkv + kvh) * b + (start - blk * b)) * D;
+}
+
 template <typename T, int D, int HPW>
 __global__ __launch_bounds__(256) void decode_attn_partial_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ logg, int Hq, int Hkv, int Hsel,
     int share_group, int64_t L, int64_t pos, int b, int K, int tpu, float* __restrict__ ws_acc,
-    float2* __restrict__ ws_ml) {
+    float2* __restrict__ ws_ml, const int32_t* __restrict__ table, int64_t tstride, int64_t npages) {
   const int tid = threadIdx.x;
   const int bh = blockIdx.y;
   const int bi = bh / Hsel, hs = bh % Hsel;
@@ -168,12 +185,12 @@ __global__ __launch_bounds__(256) void decode_attn_partial_kernel(
   }
 
   const int64_t obase = (static_cast<int64_t>(bh) * ntiles + tile) * HPW;
+  const int64_t off = ntok > 0 ? kv_tile_offset<D>(bi, kvh, Hkv, L, b, start, ntok, table, tstride, npages) : 0;
   if (ntok == 0) {
     for (int x = tid; x < HPW * D; x += 256) ws_acc[obase * D + x] = 0.f;
     if (tid < HPW) ws_ml[obase + tid] = make_float2(-INFINITY, 0.f);
   } else {
-    tile_partial<T, D, HPW>(q, k, v, bi, hs, kvh, G, Hq, Hkv, share_group, L, start, ntok, bias,
-                            ws_acc, ws_ml, obase);
+    tile_partial<T, D, HPW>(q, k + off, v + off, bi, hs, G, Hq, share_group, ntok, bias, ws_acc, ws_ml, obase);
   }
 }
 
@@ -190,7 +207,7 @@ __global__ __launch_bounds__(256) void decode_fused_partial_kernel(
     const uint64_t* __restrict__ ws_keys, const float2* __restrict__ ws_sel_ml, int nchunks, int64_t ncand,
     int gate, int32_t* __restrict__ idx, float* __restrict__ logg, int32_t* __restrict__ k_eff, int Hq, int Hkv,
     int Hsel, int share_group, int64_t L, int64_t pos, int b, int K, int tpu, float* __restrict__ ws_acc,
-    float2* __restrict__ ws_ml) {
+    float2* __restrict__ ws_ml, const int32_t* __restrict__ table, int64_t tstride, int64_t npages) {
   __shared__ uint64_t s_win[4 * 64];
   __shared__ float2 s_mlw[4];
   __shared__ uint32_t s_lo[4];
@@ -251,12 +268,12 @@ __global__ __launch_bounds__(256) void decode_fused_partial_kernel(
   }
 
   const int64_t obase = (static_cast<int64_t>(bh) * ntiles + tile) * HPW;
+  const int64_t off = ntok > 0 ? kv_tile_offset<D>(bi, kvh, Hkv, L, b, start, ntok, table, tstride, npages) : 0;
   if (ntok == 0) {
     for (int x = tid; x < HPW * D; x += 256) ws_acc[obase * D + x] = 0.f;
     if (tid < HPW) ws_ml[obase + tid] = make_float2(-INFINITY, 0.f);
   } else {
-    tile_partial<T, D, HPW>(q, k, v, bi, hs, kvh, G, Hq, Hkv, share_group, L, start, ntok, bias,
-                            ws_acc, ws_ml, obase);
+    tile_partial<T, D, HPW>(q, k + off, v + off, bi, hs, G, Hq, share_group, ntok, bias, ws_acc, ws_ml, obase);
   }
 }
 
@@ -687,7 +704,7 @@ static hipError_t launch_decode_attn_h(const AttnLaunch& p, void* ws, hipStream_
   hipError_t e = launch(false, decode_attn_partial_kernel<T, D, HPW>, dim3(ntiles, static_cast<unsigned>(heads)),
                         dim3(256), st, static_cast<const T*>(p.q), static_cast<const T*>(p.k),
                         static_cast<const T*>(p.v), p.idx, p.logg, p.Hq, p.Hkv, p.Hsel, p.share_group, p.L,
-                        p.q_pos0, p.b, p.K, tpu, acc, ml);
+                        p.q_pos0, p.b, p.K, tpu, acc, ml, p.pages.table, p.pages.tstride, p.pages.npages);
   if (e != hipSuccess) return e;
   return launch(true, decode_combine_kernel<T, D, HPW>, dim3(HPW, static_cast<unsigned>(heads)), dim3(256), st,
                 acc, ml, p.Hq, p.Hkv, p.Hsel, p.share_group, ntiles, static_cast<T*>(p.o), p.lse);
@@ -708,7 +725,7 @@ static hipError_t launch_fused_nv(const SelectLaunch& s, void* ws_sel, const Att
                         static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
                         static_cast<const uint64_t*>(w.keys), static_cast<const float2*>(w.ml), w.nch, s.max_cand,
                         s.gate, s.idx, s.logg, s.k_eff, p.Hq, p.Hkv, p.Hsel, p.share_group, p.L, p.q_pos0, p.b,
-                        p.K, tpu, acc, ml);
+                        p.K, tpu, acc, ml, p.pages.table, p.pages.tstride, p.pages.npages);
   if (e != hipSuccess) return e;
   return launch(true, decode_combine_kernel<bf16_t, D, HPW>, dim3(HPW, static_cast<unsigned>(heads)), dim3(256),
                 st, acc, ml, p.Hq, p.Hkv, p.Hsel, p.share_group, ntiles, static_cast<bf16_t*>(p.o), p.lse);

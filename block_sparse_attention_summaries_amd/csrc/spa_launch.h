@@ -16,6 +16,15 @@ __host__ __device__ inline int64_t num_candidates(int64_t pos, int b, int prefix
   return prefix_mode == 0 ? pos / b : (static_cast<int64_t>(qblock) * (pos / qblock)) / b;
 }
 
+// Paged K / V: the cache pointers are page pools [npages, Hkv, b, d] and
+// logical block c of batch bi lives in page table[bi * tstride + c].  A null
+// table means the contiguous [B, Hkv, L, d] layout.
+struct KvPages {
+  const int32_t* table = nullptr;
+  int64_t tstride = 0;
+  int64_t npages = 0;
+};
+
 struct SummaryLaunch {
   const void* k;
   int dtype, B, Hkv;
@@ -25,6 +34,7 @@ struct SummaryLaunch {
   void* kbar;
   float* max_norm;
   float* centre;
+  KvPages pages{};
 };
 
 struct SelectLaunch {
@@ -70,6 +80,7 @@ struct AttnLaunch {
   void* o;
   float* lse;
   int Hsel;
+  KvPages pages{};
 };
 
 struct BwdLaunch {

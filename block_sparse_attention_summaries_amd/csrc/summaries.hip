@@ -15,10 +15,14 @@
 
 namespace spa {
 
+// With a page table, block c of (batch, kv head) is page table[batch * tstride
+// + c] of the pool [npages, Hkv, b, d]; an unmapped page (id outside the
+// pool) reads as zero keys.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void block_summaries_kernel(
     const T* __restrict__ k, int Hkv, int64_t L, int b, int64_t first_block, int64_t num_blocks,
-    int64_t ccap, T* __restrict__ kbar, float* __restrict__ max_norm, float* __restrict__ centre) {
+    int64_t ccap, T* __restrict__ kbar, float* __restrict__ max_norm, float* __restrict__ centre,
+    const int32_t* __restrict__ table, int64_t tstride, int64_t npages) {
   constexpr int kVec = Elem<T>::kVec;
   constexpr int kLanesPerRow = D / kVec;        // lanes covering one key row
   constexpr int kRowsPerPass = 256 / kLanesPerRow;
@@ -33,13 +37,20 @@ __global__ __launch_bounds__(256) void block_summaries_kernel(
   const int cg = tid % kLanesPerRow;            // which kVec columns
   const int rg = tid / kLanesPerRow;            // which row within a pass
   const T* base = k + (bh * L + c * b) * D;
+  int nrows = b;
+  if (table != nullptr) {
+    const int64_t pg = table[(bh / Hkv) * tstride + c];
+    const bool mapped = pg >= 0 && pg < npages;
+    base = k + ((mapped ? pg : 0) * Hkv + bh % Hkv) * b * D;
+    nrows = mapped ? b : 0;
+  }
 
   double acc[kVec];
 #pragma unroll
   for (int i = 0; i < kVec; ++i) acc[i] = 0.0;
   float best = 0.f;
 
-  for (int r = rg; r < b; r += kRowsPerPass) {
+  for (int r = rg; r < nrows; r += kRowsPerPass) {
     uint4 raw = *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(r) * D + cg * kVec);
     float x[kVec];
     Elem<T>::unpack(raw, x);
@@ -85,7 +96,7 @@ static hipError_t launch_summaries_t(const SummaryLaunch& p, hipStream_t st) {
   dim3 grid(static_cast<unsigned>(p.num_blocks), static_cast<unsigned>(p.B * p.Hkv));
   return launch(true, block_summaries_kernel<T, D>, grid, dim3(256), st, static_cast<const T*>(p.k),
                 p.Hkv, p.L, p.b, p.first_block, p.num_blocks, p.ccap, static_cast<T*>(p.kbar),
-                p.max_norm, p.centre);
+                p.max_norm, p.centre, p.pages.table, p.pages.tstride, p.pages.npages);
 }
 
 hipError_t launch_block_summaries(const SummaryLaunch& p, hipStream_t st) {

@@ -28,7 +28,8 @@ SPA_OP_SCORE_SELECT, SPA_OP_ATTN_FWD, SPA_OP_ATTN_BWD, SPA_OP_SELECT_BWD, SPA_OP
 
 EXPORTED = ["spa_abi_version", "spa_profile_next_call", "spa_last_error", "sparse_block_summaries", "sparse_score_select",
             "sparse_attn_fwd", "sparse_attn_bwd", "sparse_select_bwd", "sparse_decode_step",
-            "sparse_workspace_bytes", "sparse_workspace_init"]
+            "sparse_block_summaries_paged", "sparse_decode_step_paged", "sparse_workspace_bytes",
+            "sparse_workspace_init"]
 
 _vp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
 
@@ -54,6 +55,10 @@ class AttnArgs(ctypes.Structure):
 
 class DecodeArgs(ctypes.Structure):
     _fields_ = [("select", ctypes.POINTER(SelectArgs)), ("attn", ctypes.POINTER(AttnArgs))]
+
+
+class KvPages(ctypes.Structure):
+    _fields_ = [("block_table", _vp), ("table_stride", _i64), ("num_pages", _i64)]
 
 
 class SpaError(RuntimeError):
@@ -93,6 +98,11 @@ def lib():
         L.sparse_select_bwd.argtypes = [ctypes.POINTER(SelectArgs), ctypes.POINTER(SelectGrads), _vp, _sz, _vp]
         L.sparse_decode_step.restype = _i
         L.sparse_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp, _sz, _vp]
+        L.sparse_block_summaries_paged.restype = _i
+        L.sparse_block_summaries_paged.argtypes = [_vp, _i, _i, _i, _i64, _i, _i, ctypes.POINTER(KvPages), _i64,
+                                                   _i64, _i64, _vp, _vp, _vp, _vp]
+        L.sparse_decode_step_paged.restype = _i
+        L.sparse_decode_step_paged.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(KvPages), _vp, _sz, _vp]
         L.sparse_workspace_bytes.restype = _sz
         L.sparse_workspace_bytes.argtypes = [_i, _vp]
         L.sparse_workspace_init.restype = _i
@@ -291,4 +301,53 @@ def sparse_decode_step(q, kbar, max_norm, centre, k, v, *, Hkv, b, K, q_pos0, ga
     da = DecodeArgs(select=ctypes.pointer(sa), attn=ctypes.pointer(aa))
     buf, size = _ws(workspace, SPA_OP_DECODE_STEP, da, q.device)
     _check(lib().sparse_decode_step(ctypes.byref(da), _p(buf), size, _stream(stream)))
+    return idx, logg, k_eff, o, lse
+
+
+def _pages(block_table, num_pages):
+    return KvPages(block_table=_p(block_table), table_stride=block_table.shape[-1], num_pages=num_pages)
+
+
+def sparse_block_summaries_paged(k_pages, block_table, L, b, first_block=0, num_blocks=None, ccap=None, kbar=None,
+                                 max_norm=None, centre=None, stream=None):
+    """sparse_block_summaries over a paged key cache: k_pages [num_pages, Hkv, b, d],
+    block_table [B, table_stride] int32, L logical tokens per batch row."""
+    _contig(k_pages, block_table, kbar, max_norm, centre)
+    npages, Hkv, pb, d = k_pages.shape
+    assert pb == b, "a page holds one block of b tokens"
+    B = block_table.shape[0]
+    if num_blocks is None:
+        num_blocks = L // b - first_block
+    if ccap is None:
+        ccap = kbar.shape[2] if kbar is not None else first_block + num_blocks
+    if kbar is None:
+        kbar = torch.zeros((B, Hkv, ccap, d), dtype=k_pages.dtype, device=k_pages.device)
+    if max_norm is None:
+        max_norm = torch.zeros((B, Hkv, ccap), dtype=torch.float32, device=k_pages.device)
+    if centre is None:
+        centre = torch.zeros((ccap,), dtype=torch.float32, device=k_pages.device)
+    pg = _pages(block_table, npages)
+    _check(lib().sparse_block_summaries_paged(_p(k_pages), _dtype(k_pages), B, Hkv, L, d, b, ctypes.byref(pg),
+                                              first_block, num_blocks, ccap, _p(kbar), _p(max_norm), _p(centre),
+                                              _stream(stream)))
+    return kbar, max_norm, centre
+
+
+def sparse_decode_step_paged(q, kbar, max_norm, centre, k_pages, v_pages, block_table, L, *, Hkv, b, K, q_pos0,
+                             gate=True, share_group=True, proj_w=None, idx=None, logg=None, k_eff=None, o=None,
+                             lse=None, workspace=None, stream=None):
+    """sparse_decode_step over a paged cache (pools [num_pages, Hkv, b, d],
+    block_table [B, table_stride] int32, L logical tokens).  Returns
+    (idx, logg, k_eff, o, lse)."""
+    _contig(k_pages, v_pages, block_table)
+    sa, (idx, logg, k_eff) = select_args(q, kbar, max_norm, centre, Hkv=Hkv, b=b, K=K, q_pos0=q_pos0, gate=gate,
+                                         share_group=share_group, proj_w=proj_w, idx=idx, logg=logg,
+                                         k_eff=k_eff)
+    aa, (o, lse) = attn_args(q, k_pages, v_pages, idx, logg, b=b, K=K, q_pos0=q_pos0, share_group=share_group,
+                             o=o, lse=lse)
+    aa.L = L
+    da = DecodeArgs(select=ctypes.pointer(sa), attn=ctypes.pointer(aa))
+    pg = _pages(block_table, k_pages.shape[0])
+    buf, size = _ws(workspace, SPA_OP_DECODE_STEP, da, q.device)
+    _check(lib().sparse_decode_step_paged(ctypes.byref(da), ctypes.byref(pg), _p(buf), size, _stream(stream)))
     return idx, logg, k_eff, o, lse

@@ -227,6 +227,35 @@ int sparse_decode_step(const spa_decode_args *a, void *workspace, size_t ws_byte
                        spa_stream_t stream);
 
 /*
+ * Paged K / V ("SAS" review, inference setup: a paged KV cache): the key and
+ * value caches are page pools [num_pages, Hkv, b, d] (one page = one block of
+ * b tokens of every kv head, each head's block contiguous) and logical block
+ * c of batch bi lives in page block_table[bi * table_stride + c].  Page ids
+ * outside [0, num_pages) read as empty: no key of that block is attended and
+ * its summary is zero.  The block summaries stay dense [B, Hkv, ccap, d].
+ */
+typedef struct spa_kv_pages {
+    const int32_t *block_table;   /* device [B, table_stride] page ids */
+    int64_t table_stride;         /* entries per batch row, >= the logical blocks addressed */
+    int64_t num_pages;            /* pages in each pool */
+} spa_kv_pages;
+
+/* sparse_block_summaries over a paged key cache: k_pages is the pool,
+ * L the logical tokens per batch row; otherwise as sparse_block_summaries
+ * (table_stride must cover first_block + num_blocks). */
+int sparse_block_summaries_paged(const void *k_pages, int dtype, int B, int Hkv, int64_t L, int d,
+                                 int b, const spa_kv_pages *pages, int64_t first_block,
+                                 int64_t num_blocks, int64_t ccap, void *kbar, float *max_norm,
+                                 float *centre, spa_stream_t stream);
+
+/* sparse_decode_step over a paged cache: a->attn->k and a->attn->v are the
+ * page pools and a->attn->L the logical tokens (table_stride >= ceil(L / b));
+ * same outputs as sparse_decode_step on the cache the pages describe, and the
+ * same workspace (sparse_workspace_bytes(SPA_OP_DECODE_STEP, a)). */
+int sparse_decode_step_paged(const spa_decode_args *a, const spa_kv_pages *pages, void *workspace,
+                             size_t ws_bytes, spa_stream_t stream);
+
+/*
  * sparse_attn_bwd -- backward of sparse_attn_fwd in the SAS mode
  * (local = CURRENT_BLOCK, window = 0, alpha = NULL), recomputing the
  * probabilities from lse:

@@ -1,0 +1,119 @@
+"""GPU parity of the paged decode path (sparse_block_summaries_paged,
+sparse_decode_step_paged): the K / V caches are scattered into page pools in a
+seeded random page order ("SAS" review, inference setup: paged KV cache), the
+oracle runs on the contiguous caches the pages describe, and the paged results
+must pass the same checks and equal the contiguous GPU path bit for bit."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_summaries_amd import ops
+from block_sparse_attention_summaries_amd.inputs import config, f32_to_bf16_bits, make_inputs
+from tests.gpu_util import dev, host
+from tests.test_gpu_parity import _check_decode_chain
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _paginate(caches, b, seed, spare_pages=5, spare_cols=3):
+    """Scatter [B, Hkv, L, d] caches into pools [num_pages, Hkv, b, d] in a
+    seeded random page order; unused pages and the tail of a partial last
+    block hold seeded noise; table columns past the blocks are -1."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, Hkv, L, d = caches[0].shape
+    nblk = (L + b - 1) // b
+    npages = B * nblk + spare_pages
+    order = rng.permutation(npages)[:B * nblk].astype(np.int32)
+    table = np.full((B, nblk + spare_cols), -1, np.int32)
+    table[:, :nblk] = order.reshape(B, nblk)
+    pools = []
+    for x in caches:
+        noise = rng.standard_normal((npages, Hkv, b, d)).astype(np.float32)
+        pool = np.ascontiguousarray(f32_to_bf16_bits(noise) if x.dtype == np.uint16 else noise)
+        for bi in range(B):
+            for c in range(nblk):
+                n = min(b, L - c * b)
+                pool[table[bi, c], :, :n, :] = x[bi, :, c * b:c * b + n, :]
+        pools.append(pool)
+    return pools, table, npages
+
+
+def _decode_paged(cfg, x, seed):
+    b, L, K = cfg["b"], x["L"], cfg["K"]
+    nblk_full = L // b
+    q_pos0 = x["q_pos0"]
+    gate = cfg["gate"]
+    proj = x.get("proj_w")
+    kw = dict(Hkv=cfg["Hkv"], b=b, K=K, q_pos0=q_pos0, gate=gate, share_group=cfg["share_group"])
+    kb_o, mx_o, ce_o = oracle.block_summaries(x["k"], b, nblocks=nblk_full, ccap=max(nblk_full, 1))
+    ora = oracle.score_select(x["q"], kb_o, mx_o, ce_o, proj_w=proj, **kw)
+    o_o, lse_o = oracle.attn_fwd(x["q"], x["k"], x["v"], ora["idx"], ora["logg"] if gate else None,
+                                 b=b, K=K, q_pos0=q_pos0, share_group=cfg["share_group"])
+    (kp, vp), table, npages = _paginate([x["k"], x["v"]], b, seed)
+    qd, kpd, vpd, td = dev(x["q"]), dev(kp), dev(vp), dev(table)
+    pw = None if proj is None else dev(proj)
+    ccap = max(nblk_full, 1)
+    kb, mx, ce = ops.sparse_block_summaries_paged(kpd, td, L, b, num_blocks=nblk_full, ccap=ccap)
+    idx, logg, keff, o, lse = ops.sparse_decode_step_paged(qd, kb, mx, ce, kpd, vpd, td, L, proj_w=pw, **kw)
+    # the contiguous path on the same inputs
+    kd, vd = dev(x["k"]), dev(x["v"])
+    kb_c, mx_c, ce_c = ops.sparse_block_summaries(kd, b, num_blocks=nblk_full, ccap=ccap)
+    c_idx, c_logg, c_keff, c_o, c_lse = ops.sparse_decode_step(qd, kb_c, mx_c, ce_c, kd, vd, proj_w=pw, **kw)
+    torch.cuda.synchronize()
+    r = dict(ora=ora, o_o=o_o, lse_o=lse_o)
+    paged = dict(idx=host(idx), logg=None if logg is None else host(logg), keff=host(keff), o=host(o),
+                 lse=host(lse), kb=host(kb), mx=host(mx))
+    contig = dict(idx=host(c_idx), logg=None if c_logg is None else host(c_logg), keff=host(c_keff),
+                  o=host(c_o), lse=host(c_lse))
+    return r, paged, contig, (kb_o, mx_o)
+
+
+@pytest.mark.parametrize("name,over", [
+    ("decode_32k", dict(n=8192, seed=81)),                                   # bf16, merge folded in
+    ("decode_32k", dict(n=4096, t=17, K=8, seed=82)),                        # partial current block
+    ("decode_32k", dict(n=4096, b=32, K=12, share_group=False, Hq=8, Hkv=8, seed=83)),
+    ("decode_512k", dict(n=65536, seed=84)),                                 # projection, K = 32
+    ("tiny_decode", dict(t=40, seed=85)),                                    # fp32: two-call path
+])
+def test_paged_decode_step_parity(name, over):
+    cfg = config(name, **over)
+    _say(f"[paged decode] {name} {over}")
+    x = make_inputs(cfg)
+    r, paged, contig, (kb_o, mx_o) = _decode_paged(cfg, x, seed=over["seed"] + 1000)
+    # summaries through the pages: bit-exact
+    assert np.array_equal(paged["kb"], kb_o)
+    assert np.array_equal(paged["mx"], mx_o)
+    ex = _check_decode_chain(cfg, r, paged)
+    for key in ("idx", "keff", "o", "lse"):
+        assert np.array_equal(paged[key], contig[key]), key
+    if cfg["gate"]:
+        assert np.array_equal(paged["logg"], contig["logg"])
+    _say(f"  exempt rows {ex}")
+
+
+def test_paged_summary_of_unmapped_block_is_zero():
+    """A block whose page id lies outside the pool reads as zero keys (no
+    access outside the pool); the other blocks are unaffected."""
+    cfg = config("decode_32k", n=2048, seed=86)
+    x = make_inputs(cfg)
+    b, L = cfg["b"], x["L"]
+    (kp,), table, npages = _paginate([x["k"]], b, seed=87)
+    table[0, 5] = npages + 7
+    table[0, 9] = -3
+    kb, mx, _ = ops.sparse_block_summaries_paged(dev(kp), dev(table), L, b)
+    torch.cuda.synchronize()
+    kb, mx = host(kb), host(mx)
+    kb_o, mx_o, _ = oracle.block_summaries(x["k"], b, nblocks=L // b)
+    bad = np.zeros(kb.shape[2], bool)
+    bad[[5, 9]] = True
+    assert not np.any(kb[:, :, bad]) and not np.any(mx[:, :, bad])
+    assert np.array_equal(kb[:, :, ~bad], kb_o[:, :, ~bad]) and np.array_equal(mx[:, :, ~bad], mx_o[:, :, ~bad])

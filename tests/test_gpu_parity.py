@@ -131,6 +131,10 @@ def _decode_run(cfg, x, K=None):
 
 def _check_decode(cfg, x, r):
     ex = _check_decode_chain(cfg, r, r)
+    # attention alone (oracle selection on both sides)
+    tol = _tol(cfg)
+    assert rel_err(r["o2"], r["o_o"]) <= tol, rel_err(r["o2"], r["o_o"])
+    assert np.abs(r["lse2"] - r["lse_o"]).max() <= 10 * tol
     # the one-call decode step: same checks against the oracle, and the same
     # bits as the two calls it stands for
     f = r["fused"]
@@ -144,7 +148,7 @@ def _check_decode(cfg, x, r):
 
 def _check_decode_chain(cfg, r, c):
     """Selection and end-to-end output of one GPU chain c (idx, logg, keff,
-    o) against the oracle; attention alone on the oracle's selection."""
+    o) against the oracle."""
     ora, tol = r["ora"], _tol(cfg)
     ex = check_indices(c["idx"], ora)
     assert np.array_equal(c["keff"], ora["k_eff"])
@@ -152,9 +156,6 @@ def _check_decode_chain(cfg, r, c):
     if cfg["gate"]:
         d = np.abs(c["logg"].astype(np.float64) - ora["logg"])
         assert d[match].max(initial=0.0) <= 1e-4 * max(1.0, np.abs(ora["logg"]).max())
-    # attention alone (oracle selection on both sides)
-    assert rel_err(r["o2"], r["o_o"]) <= tol, rel_err(r["o2"], r["o_o"])
-    assert np.abs(r["lse2"] - r["lse_o"]).max() <= 10 * tol
     # end-to-end, on heads whose selection matches
     G = cfg["Hq"] // cfg["Hkv"]
     hmatch = np.repeat(match[:, :, 0], G if cfg["share_group"] else 1, axis=1)
