@@ -8,7 +8,8 @@ One decode step = the hot path for one query token of one layer:
   sparse_score_select then sparse_attn_fwd; its top-K merge runs inside the
   attention workgroups), plus, on every b-th step, the summary of the block
   that closes (sparse_block_summaries).  The two-call sequence is timed the
-  same way for comparison (unfused_us_per_step).
+  same way for comparison (unfused_us_per_step), and so is the step over the
+  same caches scattered into page pools (paged_us_per_step).
 Steps rotate over 16 layers' KV caches (2.15 GB each) and 64 query vectors so
 that every step reads its summaries and selected K/V cold from HBM, as a
 multi-layer decoder would.  Inputs are resident in HBM before timing starts.
@@ -152,6 +153,36 @@ class DecodeWorkload:
         ops.sparse_attn_fwd(self.q[qi], self.k[layer], self.v[layer], self.idx, self.logg, b=self.b,
                             K=self.K, q_pos0=self.pos, o=self.o, lse=self.lse, workspace=self.ws_att)
 
+    def make_paged(self):
+        """The same caches scattered into page pools [pages, Hkv, b, d] in a
+        seeded random page order, with the block table (benchmark setup)."""
+        B, Hkv, d, b = self.cfg["B"], self.cfg["Hkv"], self.cfg["d"], self.b
+        nblk = self.L // b
+        g = torch.Generator(device="cuda")
+        g.manual_seed(self.cfg["seed"] * 7919)
+        perm = torch.randperm(B * nblk, generator=g, device="cuda")
+        self.table = perm.to(torch.int32).view(B, nblk).contiguous()
+        self.kp, self.vp = [], []
+        for layer in range(len(self.k)):
+            for src, dst in ((self.k[layer], self.kp), (self.v[layer], self.vp)):
+                pool = torch.empty((B * nblk, Hkv, b, d), dtype=src.dtype, device="cuda")
+                pool[perm] = src.view(B, Hkv, nblk, b, d).permute(0, 2, 1, 3, 4).reshape(B * nblk, Hkv, b, d)
+                dst.append(pool)
+        self.ws_pag = ops.Workspace()
+        torch.cuda.synchronize()
+
+    def close_block_paged(self, layer):
+        ops.sparse_block_summaries_paged(self.kp[layer], self.table, self.L, self.b, first_block=self.ccap - 1,
+                                         num_blocks=1, kbar=self.kbar[layer], max_norm=self.mx[layer],
+                                         centre=self.ce[layer])
+
+    def decode_paged(self, layer, qi):
+        ops.sparse_decode_step_paged(self.q[qi], self.kbar[layer], self.mx[layer], self.ce[layer], self.kp[layer],
+                                     self.vp[layer], self.table, self.L, Hkv=self.cfg["Hkv"], b=self.b, K=self.K,
+                                     q_pos0=self.pos, gate=True, proj_w=self.w[layer], idx=self.idx,
+                                     logg=self.logg, k_eff=self.keff, o=self.o, lse=self.lse,
+                                     workspace=self.ws_pag)
+
     def decode(self, layer, qi):
         ops.sparse_decode_step(self.q[qi], self.kbar[layer], self.mx[layer], self.ce[layer], self.k[layer],
                                self.v[layer], Hkv=self.cfg["Hkv"], b=self.b, K=self.K, q_pos0=self.pos, gate=True,
@@ -201,7 +232,7 @@ def run_decode(args):
     stream = torch.cuda.Stream()
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    def timed_graph(one_step):
+    def timed_graph(one_step, close=wl.close_block):
         """Capture `steps` decode steps in one graph, replay once untimed
         (upload), then time one replay of the whole sequence."""
         graph = torch.cuda.CUDAGraph()
@@ -211,7 +242,7 @@ def run_decode(args):
             for s in range(steps):
                 layer, qi = s % args.layers, s % args.queries
                 if s % wl.b == wl.b - 1:
-                    wl.close_block(layer)
+                    close(layer)
                 one_step(layer, qi)
             graph.capture_end()
         torch.cuda.current_stream().wait_stream(stream)
@@ -230,6 +261,12 @@ def run_decode(args):
         wl.select(layer, qi)
         wl.attend(layer, qi)
     unfused_ms = timed_graph(two_calls)
+
+    # the same steps over a paged cache (random page order)
+    wl.make_paged()
+    for s in range(4):
+        wl.decode_paged(s % args.layers, s % args.queries)
+    paged_ms = timed_graph(wl.decode_paged, close=wl.close_block_paged)
 
     # per-kernel durations over the same steps (eager), from each kernel's own
     # dispatch timestamps (start/stop events attached to its launch)
@@ -265,7 +302,7 @@ def run_decode(args):
     hot_us = g0.elapsed_time(g1) * 1e3 / 64
 
     floor_us = latency_floor_us(stream, steps, len(k_ms))
-    return dict(wl=wl, cfg=cfg, x=x, total_ms=total_ms, unfused_ms=unfused_ms, k_ms=k_ms,
+    return dict(wl=wl, cfg=cfg, x=x, total_ms=total_ms, unfused_ms=unfused_ms, paged_ms=paged_ms, k_ms=k_ms,
                 summ_ms=summ_ms, summ_bytes=summ_bytes, hot_us=hot_us, floor_us=floor_us)
 
 
@@ -534,6 +571,7 @@ def main():
                    "layers_rotated": args.layers, "queries_rotated": args.queries, "graph_replay": True},
         "selected_kv_gbps": round(att_bytes / (kern["merge_partial"]["us"] * 1e-6) / 1e9, 1),
         "unfused_us_per_step": round(res["unfused_ms"] * 1e3 / steps, 3),
+        "paged_us_per_step": round(res["paged_ms"] * 1e3 / steps, 3),
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kern.items()},
         "hot_cache_us_per_step": round(res["hot_us"], 3),

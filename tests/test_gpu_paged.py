@@ -26,23 +26,32 @@ def _say(*a):
 
 def _paginate(caches, b, seed, spare_pages=5, spare_cols=3):
     """Scatter [B, Hkv, L, d] caches into pools [num_pages, Hkv, b, d] in a
-    seeded random page order; unused pages and the tail of a partial last
-    block hold seeded noise; table columns past the blocks are -1."""
+    seeded random page order; the unused pages and the tail of a partial
+    last block hold seeded noise; table columns past the blocks are -1."""
     rng = np.random.Generator(np.random.PCG64(seed))
     B, Hkv, L, d = caches[0].shape
     nblk = (L + b - 1) // b
     npages = B * nblk + spare_pages
-    order = rng.permutation(npages)[:B * nblk].astype(np.int32)
+    order = rng.permutation(npages).astype(np.int32)
     table = np.full((B, nblk + spare_cols), -1, np.int32)
-    table[:, :nblk] = order.reshape(B, nblk)
+    table[:, :nblk] = order[:B * nblk].reshape(B, nblk)
+    spare = order[B * nblk:]
     pools = []
     for x in caches:
-        noise = rng.standard_normal((npages, Hkv, b, d)).astype(np.float32)
-        pool = np.ascontiguousarray(f32_to_bf16_bits(noise) if x.dtype == np.uint16 else noise)
-        for bi in range(B):
-            for c in range(nblk):
-                n = min(b, L - c * b)
-                pool[table[bi, c], :, :n, :] = x[bi, :, c * b:c * b + n, :]
+        def noise(shape):
+            z = rng.standard_normal(shape, dtype=np.float32)
+            return f32_to_bf16_bits(z) if x.dtype == np.uint16 else z
+        pool = np.empty((npages, Hkv, b, d), dtype=x.dtype)
+        pool[spare] = noise((len(spare), Hkv, b, d))
+        full = L // b
+        blocks = x[:, :, :full * b, :].reshape(B, Hkv, full, b, d).transpose(0, 2, 1, 3, 4)
+        pool[table[:, :full].reshape(-1)] = blocks.reshape(B * full, Hkv, b, d)
+        if full < nblk:                                    # partial last block
+            n = L - full * b
+            for bi in range(B):
+                pg = table[bi, full]
+                pool[pg] = noise((Hkv, b, d))
+                pool[pg, :, :n, :] = x[bi, :, full * b:, :]
         pools.append(pool)
     return pools, table, npages
 
@@ -117,3 +126,16 @@ def test_paged_summary_of_unmapped_block_is_zero():
     bad[[5, 9]] = True
     assert not np.any(kb[:, :, bad]) and not np.any(mx[:, :, bad])
     assert np.array_equal(kb[:, :, ~bad], kb_o[:, :, ~bad]) and np.array_equal(mx[:, :, ~bad], mx_o[:, :, ~bad])
+
+
+def test_paged_decode_512k_full_size():
+    """The full 512K decode workload (8193 pages of 64 tokens per kv head)."""
+    cfg = config("decode_512k")
+    _say("[paged decode] decode_512k full size")
+    x = make_inputs(cfg)
+    r, paged, contig, (kb_o, mx_o) = _decode_paged(cfg, x, seed=88)
+    assert np.array_equal(paged["kb"], kb_o) and np.array_equal(paged["mx"], mx_o)
+    ex = _check_decode_chain(cfg, r, paged)
+    for key in ("idx", "keff", "o", "lse"):
+        assert np.array_equal(paged[key], contig[key]), key
+    _say(f"  exempt rows {ex}")
