@@ -260,13 +260,14 @@ def run_decode(args):
     def two_calls(layer, qi):
         wl.select(layer, qi)
         wl.attend(layer, qi)
-    unfused_ms = timed_graph(two_calls)
-
-    # the same steps over a paged cache (random page order)
-    wl.make_paged()
-    for s in range(4):
-        wl.decode_paged(s % args.layers, s % args.queries)
-    paged_ms = timed_graph(wl.decode_paged, close=wl.close_block_paged)
+    unfused_ms = paged_ms = None
+    if not args.skip_variants:
+        unfused_ms = timed_graph(two_calls)
+        # the same steps over a paged cache (random page order)
+        wl.make_paged()
+        for s in range(4):
+            wl.decode_paged(s % args.layers, s % args.queries)
+        paged_ms = timed_graph(wl.decode_paged, close=wl.close_block_paged)
 
     # per-kernel durations over the same steps (eager), from each kernel's own
     # dispatch timestamps (start/stop events attached to its launch)
@@ -511,6 +512,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--skip-variants", action="store_true",
+                    help="time only the one-call decode step (no two-call or paged comparison); for profiling")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB device copy (for scaling rocprofv3 byte counters)")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -570,8 +573,8 @@ def main():
                    "kv_heads": 8, "head_dim": 128, "block": wl.b, "K": wl.K, "gate": "softmax_log",
                    "layers_rotated": args.layers, "queries_rotated": args.queries, "graph_replay": True},
         "selected_kv_gbps": round(att_bytes / (kern["merge_partial"]["us"] * 1e-6) / 1e9, 1),
-        "unfused_us_per_step": round(res["unfused_ms"] * 1e3 / steps, 3),
-        "paged_us_per_step": round(res["paged_ms"] * 1e3 / steps, 3),
+        "unfused_us_per_step": None if res["unfused_ms"] is None else round(res["unfused_ms"] * 1e3 / steps, 3),
+        "paged_us_per_step": None if res["paged_ms"] is None else round(res["paged_ms"] * 1e3 / steps, 3),
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kern.items()},
         "hot_cache_us_per_step": round(res["hot_us"], 3),
