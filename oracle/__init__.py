@@ -80,6 +80,11 @@ def _declare(lib):
     lib.orc_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, I, I64, I64, I, I, I, P, P, I, I, I, I,
                                  P, P, I64, P, P]
     lib.orc_attn_fwd.restype = None
+    lib.orc_retain_cells.restype = None
+    lib.orc_retain_cells.argtypes = [P, I, I, I64, I64, I, I, P, P]
+    lib.orc_score_select_subset.restype = None
+    lib.orc_score_select_subset.argtypes = [P, I, I, I, I, I, I, I64, P, I, P, P, I64, I, I, I, I, P, P, P, P,
+                                            I, I, I, P, P, P, P]
     lib.orc_select_bwd.restype = None
     lib.orc_select_bwd.argtypes = [P, I, I, I, I, I, I, I64, P, I, I64, I, I, I, P, P, P, P, P, P]
     lib.orc_attn_bwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I64, I64, I, P, P, I, I, I64,
@@ -238,6 +243,43 @@ def attn_bwd(q, k, v, dout, idx, logg, *, b, K, q_pos0, share_group=True, kv_sli
                      L, int(q_pos0), b, _ptr(idx), _ptr(logg_a), K, int(bool(share_group)),
                      int(kv_slice), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg))
     return dq, dk, dv, dg
+
+
+def retain_cells(max_norm, *, ncand, W, P):
+    """FS-L kept set per (batch, kv head): the W most recent of the ncand prefix
+    cells plus the P older cells of largest max key norm.  Returns (cells
+    [B, Hkv, W + P] ascending, -1 padded; count [B, Hkv])."""
+    lib = _load()
+    mx = _f32(max_norm)
+    B, Hkv, ccap = mx.shape
+    cells = np.full((B, Hkv, W + P), -1, np.int32)
+    count = np.zeros((B, Hkv), np.int32)
+    lib.orc_retain_cells(_ptr(mx), B, Hkv, ccap, int(ncand), int(W), int(P), _ptr(cells), _ptr(count))
+    return cells, count
+
+
+def score_select_subset(q, kbar, max_norm, centre, cells, count, *, Hkv, b, K, q_pos0, gate=True,
+                        prefix_mode=0, qblock=128, share_group=True, erf_lambda=None, erf_sigma=None):
+    """score_select restricted to the kept cells of each kv head (cells, count
+    as retain_cells returns them).  Returns dict(idx, logg, k_eff, gap)."""
+    lib = _load()
+    B, Hq, nq, d = q.shape
+    ccap = kbar.shape[2]
+    Hsel = Hkv if share_group else Hq
+    cells = np.ascontiguousarray(cells, dtype=np.int32)
+    count = np.ascontiguousarray(count, dtype=np.int32)
+    idx = np.full((B, Hsel, nq, K), -1, np.int32)
+    logg = np.zeros((B, Hsel, nq, K), np.float64)
+    keff = np.zeros((B, Hsel, nq), np.int32)
+    gap = np.zeros((B, Hsel, nq), np.float64)
+    max_norm, centre = _f32(max_norm), _f32(centre)
+    erf_lambda, erf_sigma = _f32(erf_lambda), _f32(erf_sigma)
+    lib.orc_score_select_subset(_ptr(q), _dtype_code(q), B, Hq, Hkv, nq, d, int(q_pos0), _ptr(kbar),
+                                _dtype_code(kbar), _ptr(max_norm), _ptr(centre), ccap, b, int(prefix_mode),
+                                int(qblock), int(bool(share_group)), _ptr(erf_lambda), _ptr(erf_sigma),
+                                _ptr(cells), _ptr(count), cells.shape[-1], K, int(bool(gate)), _ptr(idx),
+                                _ptr(logg), _ptr(keff), _ptr(gap))
+    return dict(idx=idx, logg=logg, k_eff=keff, gap=gap)
 
 
 def select_bwd(q, kbar, idx, dg, *, Hkv, b, K, q_pos0, share_group=True, proj_w=None):

@@ -838,3 +838,114 @@ void orc_select_bwd(const void *q, int qdtype, int B, int Hq, int Hkv, int nq, i
         free(dw_part);
     }
 }
+
+/* ------------------------------------------- next: fixed-state retention */
+/*
+ * FS-L retention ("FreeSolo" review, the two variants: before any query
+ * arrives, each head keeps only its W most recent cells and the P cells of
+ * largest max key norm, and every query picks its top K inside that set).
+ * Reading taken: of the ncand prefix cells 0 .. ncand-1, the W most recent
+ * (ncand-W .. ncand-1) plus the P older cells of largest max_norm (lower index
+ * first on equal norms), so min(ncand, W + P) cells are kept.  Per (batch, kv
+ * head): cells [B, Hkv, W + P] ascending, -1 padded; count [B, Hkv].
+ */
+void orc_retain_cells(const float *max_norm, int B, int Hkv, int64_t Ccap, int64_t ncand, int W,
+                      int P, int32_t *cells, int32_t *count)
+{
+    const int cap = W + P;
+    const int64_t n_old = ncand > W ? ncand - W : 0;
+    const int kp = (int)((int64_t)P < n_old ? P : n_old);
+    char *taken = (char *)malloc((size_t)(n_old > 0 ? n_old : 1));
+    int32_t *chosen = (int32_t *)malloc(sizeof(int32_t) * (size_t)(cap > 0 ? cap : 1));
+    for (int t = 0; t < B * Hkv; ++t) {
+        const float *a = max_norm + (int64_t)t * Ccap;
+        memset(taken, 0, (size_t)(n_old > 0 ? n_old : 1));
+        for (int j = 0; j < kp; ++j) {
+            int64_t best = -1;
+            for (int64_t c = 0; c < n_old; ++c) {
+                if (taken[c])
+                    continue;
+                if (best < 0 || a[c] > a[best])   /* strict: lower index wins ties */
+                    best = c;
+            }
+            taken[best] = 1;
+            chosen[j] = (int32_t)best;
+        }
+        /* ascending (insertion sort), then the recent cells */
+        for (int x = 1; x < kp; ++x) {
+            int32_t v = chosen[x];
+            int y = x - 1;
+            while (y >= 0 && chosen[y] > v) {
+                chosen[y + 1] = chosen[y];
+                --y;
+            }
+            chosen[y + 1] = v;
+        }
+        int n = kp;
+        for (int64_t c = n_old; c < ncand; ++c)
+            chosen[n++] = (int32_t)c;
+        for (int x = 0; x < cap; ++x)
+            cells[(int64_t)t * cap + x] = x < n ? chosen[x] : -1;
+        count[t] = n;
+    }
+    free(taken);
+    free(chosen);
+}
+
+/*
+ * Per-query selection inside a kept set: the row's scores (orc_scores_row) on
+ * the listed cells that are candidates of the row, then the same gate and
+ * top-K as orc_score_select over just those cells (the LSE runs over the kept
+ * candidates), mapped back to cell ids (ascending, -1 padded).  cells / count
+ * are per (batch, kv head) as orc_retain_cells writes them; a selection head
+ * reads the list of its kv head.
+ */
+void orc_score_select_subset(const void *q, int qdtype, int B, int Hq, int Hkv, int nq, int d,
+                             int64_t q_pos0, const void *kbar, int kdtype, const float *max_norm,
+                             const float *centre, int64_t Ccap, int b, int prefix_mode, int qblock,
+                             int share_group, const float *erf_lambda, const float *erf_sigma,
+                             const int32_t *cells, const int32_t *count, int cap, int K, int gate,
+                             int32_t *idx, double *logg, int32_t *k_eff, double *gap)
+{
+    const int Hsel = share_group ? Hkv : Hq;
+    const int G = Hq / Hkv;
+    const int64_t total = (int64_t)B * Hsel * nq;
+    int64_t w;
+#pragma omp parallel for schedule(dynamic)
+    for (w = 0; w < total; ++w) {
+        const int64_t row = w % nq;
+        const int hs = (int)((w / nq) % Hsel);
+        const int bidx = (int)(w / nq / Hsel);
+        const int kvh = share_group ? hs : hs / G;
+        const int64_t pos = q_pos0 + row;
+        const int64_t ncand = orc_num_candidates(pos, b, prefix_mode, qblock);
+        double *s = (double *)malloc(sizeof(double) * (size_t)(ncand > 0 ? ncand : 1));
+        double *sub = (double *)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
+        int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)(cap > 0 ? cap : 1));
+        int32_t *pick = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K > 0 ? K : 1));
+        orc_scores_row(q, qdtype, Hq, Hkv, nq, d, bidx, hs, row, pos, kbar, kdtype, max_norm, centre,
+                       Ccap, share_group, NULL, erf_lambda, erf_sigma, ncand, s);
+        const int32_t *lst = cells + ((int64_t)bidx * Hkv + kvh) * cap;
+        const int nl = count[(int64_t)bidx * Hkv + kvh];
+        int n = 0;
+        for (int x = 0; x < nl; ++x)
+            if (lst[x] >= 0 && lst[x] < ncand) {
+                sub[n] = s[lst[x]];
+                ids[n] = lst[x];
+                ++n;
+            }
+        const int64_t o = ((int64_t)bidx * Hsel + hs) * nq + row;
+        double gp = 0.0, lse = 0.0;
+        const int ke = orc_select_from_scores(sub, n, K, gate, pick, logg ? logg + o * K : NULL, &gp, &lse);
+        for (int k = 0; k < K; ++k)
+            idx[o * K + k] = k < ke ? ids[pick[k]] : -1;
+        if (k_eff)
+            k_eff[o] = ke;
+        if (gap)
+            gap[o] = gp;
+        free(s);
+        free(sub);
+        free(ids);
+        free(pick);
+    }
+}
