@@ -367,6 +367,34 @@ int sparse_decode_step_paged(const spa_decode_args* a, const spa_kv_pages* pages
   return hip_status(e, "sparse_decode_step_paged");
 }
 
+int sparse_retain_cells(const float* max_norm, int B, int Hkv, int64_t ccap, int64_t ncand, int W, int P,
+                        int32_t* cells, int32_t* count, spa_stream_t stream) {
+  ProfileScope profile_scope;
+  SPA_REQUIRE(max_norm && cells && count, SPA_ERR_INVALID_ARG, "max_norm, cells and count must be non-NULL");
+  SPA_REQUIRE(B >= 1 && Hkv >= 1 && static_cast<int64_t>(B) * Hkv <= (static_cast<int64_t>(1) << 31) - 1,
+              SPA_ERR_INVALID_ARG, "B and Hkv must be >= 1");
+  SPA_REQUIRE(ncand >= 0 && ncand <= ccap, SPA_ERR_INVALID_ARG, "ncand = %lld outside [0, ccap = %lld]",
+              static_cast<long long>(ncand), static_cast<long long>(ccap));
+  SPA_REQUIRE(W >= 0 && P >= 0 && P <= 64 && W + P >= 1 && W + P <= 256, SPA_ERR_UNSUPPORTED,
+              "W = %d, P = %d not supported (P <= 64, 1 <= W + P <= 256)", W, P);
+  return hip_status(spa::launch_retain_cells(max_norm, B, Hkv, ccap, ncand, W, P, cells, count,
+                                             static_cast<hipStream_t>(stream)),
+                    "sparse_retain_cells");
+}
+
+int sparse_score_select_subset(const spa_select_args* a, const int32_t* cells, const int32_t* count, int cap,
+                               spa_stream_t stream) {
+  ProfileScope profile_scope;
+  spa::SelectLaunch p;
+  int st = check_select(a, &p);
+  if (st != SPA_OK) return st;
+  SPA_REQUIRE(a->proj_w == nullptr, SPA_ERR_UNSUPPORTED, "the kept-set selection takes no projection");
+  SPA_REQUIRE(cells && count, SPA_ERR_INVALID_ARG, "cells and count must be non-NULL");
+  SPA_REQUIRE(cap >= 1 && cap <= 256, SPA_ERR_UNSUPPORTED, "cap = %d not supported (1..256)", cap);
+  return hip_status(spa::launch_score_select_subset(p, cells, count, cap, static_cast<hipStream_t>(stream)),
+                    "sparse_score_select_subset");
+}
+
 size_t sparse_workspace_bytes(int op, const void* args) {
   switch (op) {
     case SPA_OP_SCORE_SELECT: {

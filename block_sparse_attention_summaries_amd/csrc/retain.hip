@@ -1,0 +1,272 @@
+// retain.hip -- FS-L fixed-state retention and the per-query selection inside
+// the kept set, on gfx950 ("FreeSolo" review, the two variants: before any
+// query arrives each head keeps only its W most recent cells and its P cells
+// of largest max key norm; each query then takes its top K inside that set).
+//
+// Kept set of a (batch, kv head) with ncand prefix cells: the W most recent
+// cells plus the P older cells of largest max_norm, lower index first on
+// equal norms; ascending, -1 padded to W + P.
+//   retain_cells_kernel   one workgroup per (batch, kv head).  Wave w walks
+//                         its contiguous quarter of the older cells 256 at a
+//                         time and keeps a running top-P list (one record per
+//                         lane, in index order): running list + next 256
+//                         cells -> top P by a threshold search and an ordered
+//                         compaction.  Wave 0 then takes the top P of the four
+//                         lists (index order across waves too) and appends the
+//                         recent cells.
+//   select_subset_kernel  one wave per (batch, selection head, query row):
+//                         fp64 scores of the listed cells that are candidates
+//                         of the row (q_hat . kbar / sqrt(d), plus the erf
+//                         position bias), the gate over those cells, and the
+//                         top K by repeated arg-max (higher score, then lower
+//                         cell); the kept slots are written in list order,
+//                         which is ascending cell order.
+#include "spa_device.h"
+#include "spa_launch.h"
+
+namespace spa {
+
+constexpr int kRetainMaxP = 64;     // running list: one record per lane
+constexpr int kSubsetMaxCap = 256;  // listed cells per head: four per lane
+
+// Ordered compaction of NV x 64 positions (position i * 64 + lane): keeps
+// keys > t and the first need_eq keys == t (keys 0 never), calling
+// emit(slot, i).  Returns the number kept.
+template <int NV, typename Emit>
+__device__ __forceinline__ int rt_select_ordered(const uint32_t (&key)[NV], uint32_t t, int need_eq, Emit&& emit) {
+  int kept = 0, eq_seen = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const uint64_t eq = __ballot(key[i] == t && key[i] != 0u);
+    const bool take = key[i] > t || (key[i] == t && key[i] != 0u && eq_seen + lanes_below(eq) < need_eq);
+    const uint64_t tm = __ballot(take);
+    if (take) emit(kept + lanes_below(tm), i);
+    kept += __popcll(tm);
+    eq_seen += __popcll(eq);
+  }
+  return kept;
+}
+
+// Top-P of the wave's NV x 64 (key << 32 | cell) records into s_out[0 .. 63]
+// in position order (0 padded); returns the number kept.
+template <int NV>
+__device__ __forceinline__ int rt_top_p(const uint64_t (&r)[NV], int P, uint64_t* s_out) {
+  const int lane = threadIdx.x % kWave;
+  uint32_t key[NV];
+  int valid = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    key[i] = static_cast<uint32_t>(r[i] >> 32);
+    valid += __popcll(__ballot(key[i] != 0u));
+  }
+  const int k = valid < P ? valid : P;
+  const uint32_t t = wave_kth_largest<NV>(key, k);
+  int ngt = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) ngt += __popcll(__ballot(key[i] > t));
+  const int kept = rt_select_ordered<NV>(key, t, k - ngt, [&](int slot, int i) { s_out[slot] = r[i]; });
+  for (int x = kept + lane; x < kWave; x += kWave) s_out[x] = 0ull;
+  return kept;
+}
+
+__global__ __launch_bounds__(256) void retain_cells_kernel(const float* __restrict__ max_norm, int64_t ccap,
+                                                           int64_t ncand, int W, int P, int32_t* __restrict__ cells,
+                                                           int32_t* __restrict__ count) {
+  __shared__ uint64_t s_run[4][kWave];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int64_t head = blockIdx.x;
+  const float* a = max_norm + head * ccap;
+  const int cap = W + P;
+  const int64_t n_old = ncand > W ? ncand - W : 0;
+  const int64_t nch = (n_old + 255) / 256;
+  const int64_t ch0 = nch * wave / 4, ch1 = nch * (wave + 1) / 4;
+  uint64_t run = 0ull;
+  for (int64_t ch = ch0; ch < ch1; ++ch) {
+    uint64_t r[5];
+    r[0] = run;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t c = ch * 256 + i * kWave + lane;
+      const float v = a[c < n_old ? c : n_old - 1];
+      r[i + 1] = c < n_old ? (static_cast<uint64_t>(orderable_f32(v)) << 32) | static_cast<uint32_t>(c) : 0ull;
+    }
+    rt_top_p<5>(r, P, s_run[wave]);
+    wave_lds_sync();
+    run = s_run[wave][lane];
+    wave_lds_sync();
+  }
+  s_run[wave][lane] = run;
+  __syncthreads();
+  if (wave != 0) return;
+  // the four running lists in wave order are in cell order
+  uint64_t r2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r2[i] = s_run[i][lane];
+  __shared__ uint64_t s_fin[kWave];
+  const int kept = rt_top_p<4>(r2, P, s_fin);
+  wave_lds_sync();
+  int32_t* out = cells + head * cap;
+  if (lane < kept) out[lane] = static_cast<int32_t>(static_cast<uint32_t>(s_fin[lane]));
+  const int64_t nrec = ncand - n_old;
+  for (int x = lane; x < nrec; x += kWave) out[kept + x] = static_cast<int32_t>(n_old + x);
+  for (int x = kept + static_cast<int>(nrec) + lane; x < cap; x += kWave) out[x] = -1;
+  if (lane == 0) count[head] = kept + static_cast<int>(nrec);
+}
+
+// ---------------------------------------------------------------- select
+template <typename T, int D>
+__global__ __launch_bounds__(256) void select_subset_kernel(
+    const T* __restrict__ q, const T* __restrict__ kbar, const float* __restrict__ max_norm,
+    const float* __restrict__ centre, int Hq, int Hkv, int Hsel, int share_group, int nq, int64_t q_pos0,
+    int64_t ccap, int b, int prefix_mode, int qblock, const float* __restrict__ erf_lambda,
+    const float* __restrict__ erf_sigma, const int32_t* __restrict__ cells, const int32_t* __restrict__ count,
+    int cap, int K, int gate, int32_t* __restrict__ idx, float* __restrict__ logg, int32_t* __restrict__ k_eff) {
+  constexpr int kVec = Elem<T>::kVec;
+  __shared__ double s_q[4][D];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int bh = blockIdx.y;
+  const int bi = bh / Hsel, hs = bh % Hsel;
+  const int G = Hq / Hkv;
+  const int kvh = share_group ? hs : hs / G;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= nq) return;                       // whole wave leaves; no workgroup barrier below
+  const int64_t pos = q_pos0 + row;
+  const int64_t ncand = prefix_mode == 0 ? pos / b : (static_cast<int64_t>(qblock) * (pos / qblock)) / b;
+
+  // q_hat in fp64 (mean of the group's heads, summed in head order)
+  const int gq = share_group ? G : 1;
+  const int h0 = share_group ? hs * G : hs;
+  for (int e = lane; e < D; e += kWave) {
+    double s = 0.0;
+    for (int g = 0; g < gq; ++g) s += static_cast<double>(ld_f(q + ((static_cast<int64_t>(bi) * Hq + h0 + g) * nq + row) * D + e));
+    s_q[wave][e] = s / static_cast<double>(gq);
+  }
+  wave_lds_sync();
+
+  // scores of this lane's list slots j = i * 64 + lane
+  const int64_t hb = static_cast<int64_t>(bi) * Hkv + kvh;
+  const int nl = count[hb];
+  const int32_t* lst = cells + hb * cap;
+  const double inv_sqrt_d = 1.0 / sqrt(static_cast<double>(D));
+  const bool erf_on = erf_lambda != nullptr;
+  const double lam = erf_on ? static_cast<double>(erf_lambda[hs]) : 0.0;
+  const double sig = erf_on ? static_cast<double>(erf_sigma[hs]) : 1.0;
+  double sc[4];
+  int cid[4];
+  bool ok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = i * kWave + lane;
+    const int c = j < nl && j < cap ? lst[j] : -1;
+    ok[i] = c >= 0 && c < ncand;
+    cid[i] = c;
+    double s = -INFINITY;
+    if (ok[i]) {
+      const T* kr = kbar + (hb * ccap + c) * D;
+      double dot = 0.0;
+#pragma unroll 4
+      for (int v = 0; v < D / kVec; ++v) {
+        float x[kVec];
+        Elem<T>::unpack(*reinterpret_cast<const uint4*>(kr + v * kVec), x);
+#pragma unroll
+        for (int t = 0; t < kVec; ++t) dot = fma(static_cast<double>(x[t]), s_q[wave][v * kVec + t], dot);
+      }
+      s = dot * inv_sqrt_d;
+      if (erf_on) {
+        const double ac = static_cast<double>(max_norm[hb * ccap + c]);
+        const double pc = static_cast<double>(centre[c]);
+        s += lam * ac * erf((static_cast<double>(pos) - pc) / (2.0 * sig));
+      }
+    }
+    sc[i] = s;
+  }
+  // gate: LSE over the listed candidates
+  double m = -INFINITY;
+  int nv = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = ok[i] && sc[i] > m ? sc[i] : m;
+    nv += __popcll(__ballot(ok[i]));
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    const double o = __shfl_xor(m, off);
+    m = o > m ? o : m;
+  }
+  double l = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l += ok[i] ? exp(sc[i] - m) : 0.0;
+  for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+  const double lse = nv > 0 ? m + log(l) : 0.0;
+
+  // top K by repeated arg-max: higher score, then lower list slot (= lower cell)
+  const int kk = nv < K ? nv : K;
+  bool taken[4] = {false, false, false, false};   // at most kSubsetMaxCap = 4 x 64 listed cells
+  for (int t = 0; t < kk; ++t) {
+    double bv = -INFINITY;
+    int bj = 1 << 30;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = i * kWave + lane;
+      if (ok[i] && !taken[i] && (sc[i] > bv || (sc[i] == bv && j < bj))) {
+        bv = sc[i];
+        bj = j;
+      }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ov = __shfl_xor(bv, off);
+      const int oj = __shfl_xor(bj, off);
+      if (ov > bv || (ov == bv && oj < bj)) {
+        bv = ov;
+        bj = oj;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i * kWave + lane == bj) taken[i] = true;
+  }
+  // kept slots in list order (ascending cells)
+  const int64_t o = (static_cast<int64_t>(bh) * nq + row) * K;
+  int kept = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint64_t tm = __ballot(taken[i]);
+    if (taken[i]) {
+      const int slot = kept + lanes_below(tm);
+      idx[o + slot] = cid[i];
+      if (logg != nullptr) logg[o + slot] = gate ? static_cast<float>(sc[i] - lse) : 0.f;
+    }
+    kept += __popcll(tm);
+  }
+  for (int x = kept + lane; x < K; x += kWave) {
+    idx[o + x] = -1;
+    if (logg != nullptr) logg[o + x] = 0.f;
+  }
+  if (lane == 0 && k_eff != nullptr) k_eff[static_cast<int64_t>(bh) * nq + row] = kk;
+}
+
+hipError_t launch_retain_cells(const float* max_norm, int B, int Hkv, int64_t ccap, int64_t ncand, int W, int P,
+                               int32_t* cells, int32_t* count, hipStream_t st) {
+  return launch(true, retain_cells_kernel, dim3(static_cast<unsigned>(B * Hkv)), dim3(256), st, max_norm, ccap,
+                ncand, W, P, cells, count);
+}
+
+template <typename T, int D>
+static hipError_t launch_subset_t(const SelectLaunch& p, const int32_t* cells, const int32_t* count, int cap,
+                                  hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((p.nq + 3) / 4), static_cast<unsigned>(p.B * p.Hsel));
+  return launch(true, select_subset_kernel<T, D>, grid, dim3(256), st, static_cast<const T*>(p.q),
+                static_cast<const T*>(p.kbar), p.max_norm, p.centre, p.Hq, p.Hkv, p.Hsel, p.share_group, p.nq,
+                p.q_pos0, p.ccap, p.b, p.prefix_mode, p.qblock, p.erf_lambda, p.erf_sigma, cells, count, cap, p.K,
+                p.gate, p.idx, p.logg, p.k_eff);
+}
+
+hipError_t launch_score_select_subset(const SelectLaunch& p, const int32_t* cells, const int32_t* count, int cap,
+                                      hipStream_t st) {
+  if (p.dtype == kDtypeBf16)
+    return p.d == 64 ? launch_subset_t<bf16_t, 64>(p, cells, count, cap, st)
+                     : launch_subset_t<bf16_t, 128>(p, cells, count, cap, st);
+  return p.d == 64 ? launch_subset_t<float, 64>(p, cells, count, cap, st)
+                   : launch_subset_t<float, 128>(p, cells, count, cap, st);
+}
+
+}  // namespace spa

@@ -164,6 +164,10 @@ size_t attn_bwd_workspace_bytes(const BwdLaunch& p);
 hipError_t launch_block_summaries(const SummaryLaunch& p, hipStream_t st);
 hipError_t launch_score_select(const SelectLaunch& p, void* ws, hipStream_t st);
 hipError_t launch_select_bwd(const SelectLaunch& p, const SelectGrads& g, void* ws, hipStream_t st);
+hipError_t launch_retain_cells(const float* max_norm, int B, int Hkv, int64_t ccap, int64_t ncand, int W, int P,
+                               int32_t* cells, int32_t* count, hipStream_t st);
+hipError_t launch_score_select_subset(const SelectLaunch& p, const int32_t* cells, const int32_t* count, int cap,
+                                      hipStream_t st);
 bool decode_fusable(const SelectLaunch& p);
 int decode_merge_nv(const SelectLaunch& p);
 hipError_t launch_decode_chunks(const SelectLaunch& p, void* ws, hipStream_t st);

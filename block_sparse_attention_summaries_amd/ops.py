@@ -28,8 +28,8 @@ SPA_OP_SCORE_SELECT, SPA_OP_ATTN_FWD, SPA_OP_ATTN_BWD, SPA_OP_SELECT_BWD, SPA_OP
 
 EXPORTED = ["spa_abi_version", "spa_profile_next_call", "spa_last_error", "sparse_block_summaries", "sparse_score_select",
             "sparse_attn_fwd", "sparse_attn_bwd", "sparse_select_bwd", "sparse_decode_step",
-            "sparse_block_summaries_paged", "sparse_decode_step_paged", "sparse_workspace_bytes",
-            "sparse_workspace_init"]
+            "sparse_block_summaries_paged", "sparse_decode_step_paged", "sparse_retain_cells",
+            "sparse_score_select_subset", "sparse_workspace_bytes", "sparse_workspace_init"]
 
 _vp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
 
@@ -103,6 +103,10 @@ def lib():
                                                    _i64, _i64, _vp, _vp, _vp, _vp]
         L.sparse_decode_step_paged.restype = _i
         L.sparse_decode_step_paged.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(KvPages), _vp, _sz, _vp]
+        L.sparse_retain_cells.restype = _i
+        L.sparse_retain_cells.argtypes = [_vp, _i, _i, _i64, _i64, _i, _i, _vp, _vp, _vp]
+        L.sparse_score_select_subset.restype = _i
+        L.sparse_score_select_subset.argtypes = [ctypes.POINTER(SelectArgs), _vp, _vp, _i, _vp]
         L.sparse_workspace_bytes.restype = _sz
         L.sparse_workspace_bytes.argtypes = [_i, _vp]
         L.sparse_workspace_init.restype = _i
@@ -351,3 +355,28 @@ def sparse_decode_step_paged(q, kbar, max_norm, centre, k_pages, v_pages, block_
     buf, size = _ws(workspace, SPA_OP_DECODE_STEP, da, q.device)
     _check(lib().sparse_decode_step_paged(ctypes.byref(da), ctypes.byref(pg), _p(buf), size, _stream(stream)))
     return idx, logg, k_eff, o, lse
+
+
+def sparse_retain_cells(max_norm, ncand, W, P, cells=None, count=None, stream=None):
+    """FS-L kept set of every (batch, kv head) from max_norm [B, Hkv, ccap]:
+    the W most recent of the ncand prefix cells plus the P older cells of
+    largest max key norm.  Returns (cells [B, Hkv, W + P] int32, count [B, Hkv])."""
+    _contig(max_norm, cells, count)
+    B, Hkv, ccap = max_norm.shape
+    if cells is None:
+        cells = torch.empty((B, Hkv, W + P), dtype=torch.int32, device=max_norm.device)
+    if count is None:
+        count = torch.empty((B, Hkv), dtype=torch.int32, device=max_norm.device)
+    _check(lib().sparse_retain_cells(_p(max_norm), B, Hkv, ccap, ncand, W, P, _p(cells), _p(count),
+                                     _stream(stream)))
+    return cells, count
+
+
+def sparse_score_select_subset(q, kbar, max_norm, centre, cells, count, *, stream=None, **kw):
+    """sparse_score_select restricted to the kept cells (cells, count from
+    sparse_retain_cells).  Returns (idx, logg or None, k_eff)."""
+    _contig(cells, count)
+    a, outs = select_args(q, kbar, max_norm, centre, **kw)
+    _check(lib().sparse_score_select_subset(ctypes.byref(a), _p(cells), _p(count), cells.shape[-1],
+                                            _stream(stream)))
+    return outs

@@ -256,6 +256,33 @@ int sparse_decode_step_paged(const spa_decode_args *a, const spa_kv_pages *pages
                              size_t ws_bytes, spa_stream_t stream);
 
 /*
+ * sparse_retain_cells -- FS-L fixed-state retention ("FreeSolo" review, the
+ * two variants: before any query arrives each head keeps only its W most
+ * recent cells and its P cells of largest max key norm).  Of the ncand prefix
+ * cells of every (batch, kv head): the W most recent (ncand-W .. ncand-1)
+ * plus the P older cells of largest max_norm (lower index first on equal
+ * norms), min(ncand, W + P) cells in all.  max_norm: [B, Hkv, ccap] fp32 as
+ * sparse_block_summaries writes it.  Outputs: cells [B, Hkv, W + P] int32,
+ * ascending, -1 padded; count [B, Hkv] int32.  P <= 64, 1 <= W + P <= 256.
+ * No workspace.  Query-independent: run it when a cell closes.
+ */
+int sparse_retain_cells(const float *max_norm, int B, int Hkv, int64_t ccap, int64_t ncand,
+                        int W, int P, int32_t *cells, int32_t *count, spa_stream_t stream);
+
+/*
+ * sparse_score_select_subset -- sparse_score_select restricted to a kept set
+ * (the FS-L per-query top K inside the retained cells): each selection head
+ * scores the cells listed for its kv head (cells [B, Hkv, cap], count
+ * [B, Hkv], as sparse_retain_cells writes them) that are candidates of the
+ * row, and the gate's LSE runs over those cells only.  Scores are formed in
+ * fp64 (q_hat . kbar / sqrt(d) plus the erf position bias).  Same outputs and
+ * argument struct as sparse_score_select; no projection (proj_w must be
+ * NULL); 1 <= cap <= 256.  No workspace.
+ */
+int sparse_score_select_subset(const spa_select_args *a, const int32_t *cells,
+                               const int32_t *count, int cap, spa_stream_t stream);
+
+/*
  * sparse_attn_bwd -- backward of sparse_attn_fwd in the SAS mode
  * (local = CURRENT_BLOCK, window = 0, alpha = NULL), recomputing the
  * probabilities from lse:
