@@ -1,5 +1,6 @@
 """Benchmark: decode attention step at 512K context on one MI355X, plus prefill
-tokens/s (cell routing, n = 16384) and training fwd+bwd tokens/s.
+tokens/s (cell routing, n = 16384), the FS-L fixed-state decode step at 512K
+(fsl_decode_us_per_step) and training tokens/s.
 
 One decode step = the hot path for one query token of one layer:
   score + softmax log gate + top-K select over all C = 8192 block summaries,
@@ -404,6 +405,80 @@ def run_train(reps):
     return dict(ms=dict(select=t[0], fwd=t[1], bwd=t[2], select_bwd=t[3]), tokens_per_s=tokens / (t.sum() * 1e-3))
 
 
+def run_fsl_decode(steps, n_layers=4, n_queries=32):
+    """FS-L decode at 512K tokens with the cell-routing head geometry (16
+    heads, d = 64, 32-token cells, query blocks of 128, K = 4, window 512):
+    per step the selection inside the kept set (W = 8 recent cells + P = 64 of
+    largest max key norm) and the two-branch attention; when a cell closes,
+    its summary and the new kept set.  Layers and queries rotate as in the
+    main decode benchmark; graph replay is the timed region."""
+    cfg = config("prefill_cells")
+    B, H, d, b, qb, K, w = 1, cfg["Hq"], cfg["d"], cfg["b"], cfg["qblock"], cfg["K"], cfg["window"]
+    W, P = 8, 64
+    L = 524288 + b
+    pos = L - 1
+    ncand = (qb * (pos // qb)) // b
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg["seed"] * 104729)
+    ks = [torch.randn((B, H, L, d), generator=g, device="cuda").to(torch.bfloat16) for _ in range(n_layers)]
+    vs = [torch.randn((B, H, L, d), generator=g, device="cuda").to(torch.bfloat16) for _ in range(n_layers)]
+    qs = torch.randn((n_queries, B, H, 1, d), generator=g, device="cuda").to(torch.bfloat16)
+    lam = torch.rand((H,), generator=g, device="cuda")
+    sig = torch.full((H,), cfg["sigma"], device="cuda")
+    alpha = torch.rand((H,), generator=g, device="cuda")
+    summ = [ops.sparse_block_summaries(k, b) for k in ks]
+    kept = [ops.sparse_retain_cells(mx, ncand, W, P) for (_, mx, _) in summ]
+    idx = torch.empty((B, H, 1, K), dtype=torch.int32, device="cuda")
+    keff = torch.empty((B, H, 1), dtype=torch.int32, device="cuda")
+    o = torch.empty((B, H, 1, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, 1), dtype=torch.float32, device="cuda")
+    akw = dict(b=b, K=K, q_pos0=pos, share_group=False, local=1, window=w, prefix_mode=1, qblock=qb)
+
+    def step(s):
+        layer, qi = s % n_layers, s % n_queries
+        kb, mx, ce = summ[layer]
+        cells, count = kept[layer]
+        if s % b == b - 1:          # a cell closes: its summary, then the kept set
+            nblk = L // b
+            ops.sparse_block_summaries(ks[layer], b, first_block=nblk - 1, num_blocks=1, kbar=kb, max_norm=mx,
+                                       centre=ce)
+            ops.sparse_retain_cells(mx, ncand, W, P, cells=cells, count=count)
+        ops.sparse_score_select_subset(qs[qi], kb, mx, ce, cells, count, Hkv=H, b=b, K=K, q_pos0=pos, gate=False,
+                                       prefix_mode=1, qblock=qb, share_group=False, erf_lambda=lam,
+                                       erf_sigma=sig, idx=idx, k_eff=keff)
+        ops.sparse_attn_fwd(qs[qi], ks[layer], vs[layer], idx, None, alpha=alpha, o=o, lse=lse, **akw)
+
+    for s in range(8):
+        step(s)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        graph.capture_begin()
+        for s in range(steps):
+            step(s)
+        graph.capture_end()
+    torch.cuda.current_stream().wait_stream(stream)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    # the kept-set update alone (once per closing cell)
+    e0.record()
+    for _ in range(16):
+        ops.sparse_retain_cells(summ[0][1], ncand, W, P, cells=kept[0][0], count=kept[0][1])
+    e1.record()
+    torch.cuda.synchronize()
+    retain_us = e0.elapsed_time(e1) * 1e3 / 16
+    del ks, vs
+    return dict(us_per_step=us, retain_us=retain_us, cells=ncand)
+
+
 # ---------------------------------------------------------------- CPU oracle baseline
 def run_cpu_baseline(res, seconds):
     """The fp64 oracle's decode step (score + gate + top-K + attention) on the
@@ -595,6 +670,9 @@ def main():
         out["prefill_ms"] = {k: round(v, 3) for k, v in pf["ms"].items()}
         out["prefill_score_mfma_frac"] = round(pf["score_gflop"] / (pf["ms"]["score_select"] * 1e-3)
                                                / (BF16_PEAK_TFLOPS * 1e3), 5)
+        fsl = run_fsl_decode(256)
+        out["fsl_decode_us_per_step"] = round(fsl["us_per_step"], 3)
+        out["fsl_retain_us"] = round(fsl["retain_us"], 3)
         tr = run_train(2)
         out["train_tokens_per_s"] = round(tr["tokens_per_s"], 1)
         out["train_ms"] = {k: round(v, 3) for k, v in tr["ms"].items()}

@@ -328,6 +328,113 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
   if (tid == 0 && lse != nullptr) lse[orow] = lsum > 0.f ? M + __logf(lsum) : -INFINITY;
 }
 
+// Decode of the two-branch head (one query row; local = NONE, window w,
+// alpha): branch L over the selected units (tiles of 64 keys, each biased by
+// its log gate when given), branch S over the window keys pos - w < j <= pos
+// (tiles of 64 from the window's first key).  One workgroup per tile writes an
+// online-softmax partial as the SAS decode does; the combine merges each
+// branch on its own and mixes o = alpha o_L + (1 - alpha) o_S ("FreeSolo"
+// review, two-branch head).  Units that are not candidates of the row (cells
+// of the query block or later) are empty.
+template <typename T, int D, int HPW>
+__global__ __launch_bounds__(256) void decode_mix_partial_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ idx, const float* __restrict__ logg, int Hq, int Hkv, int Hsel,
+    int share_group, int64_t L, int64_t pos, int b, int prefix_mode, int qblock, int K, int tpu, int window,
+    int ntiles, float* __restrict__ ws_acc, float2* __restrict__ ws_ml) {
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.y;
+  const int bi = bh / Hsel, hs = bh % Hsel;
+  const int G = Hq / Hkv;
+  const int kvh = share_group ? hs : hs / G;
+  const int tile = blockIdx.x;
+  const int nsel = K * tpu;
+  int64_t start = 0;
+  int ntok = 0;
+  float bias = 0.f;
+  if (tile < nsel) {
+    const int unit = tile / tpu, sub = tile % tpu;
+    const int64_t ncand = prefix_mode == 0 ? pos / b : (static_cast<int64_t>(qblock) * (pos / qblock)) / b;
+    const int32_t c = idx[static_cast<int64_t>(bh) * K + unit];
+    if (c >= 0 && c < ncand) {
+      start = static_cast<int64_t>(c) * b + sub * kTileTok;
+      ntok = b - sub * kTileTok < kTileTok ? b - sub * kTileTok : kTileTok;
+      if (logg != nullptr) bias = logg[static_cast<int64_t>(bh) * K + unit];
+    }
+  } else {
+    const int64_t wlo = pos - window + 1 > 0 ? pos - window + 1 : 0;
+    start = wlo + static_cast<int64_t>(tile - nsel) * kTileTok;
+    const int64_t n = pos + 1 - start;
+    ntok = n <= 0 ? 0 : (n < kTileTok ? static_cast<int>(n) : kTileTok);
+  }
+  const int64_t obase = (static_cast<int64_t>(bh) * ntiles + tile) * HPW;
+  if (ntok == 0) {
+    for (int x = tid; x < HPW * D; x += 256) ws_acc[obase * D + x] = 0.f;
+    if (tid < HPW) ws_ml[obase + tid] = make_float2(-INFINITY, 0.f);
+  } else {
+    const int64_t off = ((static_cast<int64_t>(bi) * Hkv + kvh) * L + start) * D;
+    tile_partial<T, D, HPW>(q, k + off, v + off, bi, hs, G, Hq, share_group, ntok, bias, ws_acc, ws_ml, obase);
+  }
+}
+
+// Combine of the two branches: tiles [0, nsel) form branch L, the rest branch
+// S; each is merged with its own max, then o = alpha o_L + (1 - alpha) o_S
+// (o_L = 0 when branch L is empty); lse is branch L's.
+template <typename T, int D, int HPW>
+__global__ __launch_bounds__(256) void decode_mix_combine_kernel(const float* __restrict__ ws_acc,
+                                                                 const float2* __restrict__ ws_ml, int Hq, int Hkv,
+                                                                 int Hsel, int share_group, int nsel, int ntiles,
+                                                                 const float* __restrict__ alpha, T* __restrict__ o,
+                                                                 float* __restrict__ lse) {
+  __shared__ __align__(16) float s_acc[kMaxTiles * D];
+  __shared__ float2 s_ml[kMaxTiles];
+  __shared__ float s_wt[kMaxTiles];
+  __shared__ float s_M[2];
+  const int tid = threadIdx.x;
+  const int hh = blockIdx.x, bh = blockIdx.y;
+  const int bi = bh / Hsel, hs = bh % Hsel;
+  const int G = Hq / Hkv;
+  const int64_t base = static_cast<int64_t>(bh) * ntiles * HPW;
+  constexpr int kV4 = D / 4;
+  const int n4 = ntiles * kV4;
+#pragma unroll 8
+  for (int x = tid; x < n4; x += 256) {
+    const int t = x / kV4, c = x % kV4;
+    reinterpret_cast<float4*>(s_acc)[x] = reinterpret_cast<const float4*>(ws_acc + (base + t * HPW + hh) * D)[c];
+  }
+  for (int t = tid; t < ntiles; t += 256) s_ml[t] = ws_ml[base + t * HPW + hh];
+  __syncthreads();
+  if (tid < 2 * kWave) {
+    // wave 0: branch L, wave 1: branch S
+    const int br = tid / kWave, ln = tid % kWave;
+    const int t0 = br == 0 ? 0 : nsel, t1 = br == 0 ? nsel : ntiles;
+    float mloc = -INFINITY;
+    for (int t = t0 + ln; t < t1; t += kWave) mloc = fmaxf(mloc, s_ml[t].x);
+    const float M = wave_max(mloc);
+    for (int t = t0 + ln; t < t1; t += kWave) {
+      const float mt = s_ml[t].x;
+      s_wt[t] = (M == -INFINITY || mt == -INFINITY) ? 0.f : __expf(mt - M);
+    }
+    if (ln == 0) s_M[br] = M;
+  }
+  __syncthreads();
+  if (tid >= D) return;
+  float lsum[2] = {0.f, 0.f}, acc[2] = {0.f, 0.f};
+  for (int t = 0; t < ntiles; ++t) {
+    const int br = t < nsel ? 0 : 1;
+    const float w = s_wt[t];
+    lsum[br] = fmaf(s_ml[t].y, w, lsum[br]);
+    acc[br] = fmaf(s_acc[t * D + tid], w, acc[br]);
+  }
+  const int hq = share_group ? hs * G + hh : hs;
+  const float a = alpha[hq];
+  const float oL = lsum[0] > 0.f ? acc[0] / lsum[0] : 0.f;
+  const float oS = lsum[1] > 0.f ? acc[1] / lsum[1] : 0.f;
+  const int64_t orow = static_cast<int64_t>(bi) * Hq + hq;   // one query row
+  o[orow * D + tid] = Elem<T>::from_float(a * oL + (1.f - a) * oS);
+  if (tid == 0 && lse != nullptr) lse[orow] = lsum[0] > 0.f ? s_M[0] + __logf(lsum[0]) : -INFINITY;
+}
+
 // ======================================================== rows: forward
 struct OnlineState {
   float m, l;
@@ -679,10 +786,21 @@ static int decode_tpu(const AttnLaunch& p) { return p.b > kTileTok ? p.b / kTile
 
 static int heads_per_wg(const AttnLaunch& p) { return p.share_group ? p.Hq / p.Hkv : 1; }
 
+// two-branch decode: selected-unit tiles, then the window's tiles
+static int mix_tiles(const AttnLaunch& p) {
+  return p.K * decode_tpu(p) + (p.window + kTileTok - 1) / kTileTok;
+}
+
+static bool use_decode_mix(const AttnLaunch& p) {
+  return p.nq == 1 && p.local == 1 && p.window > 0 && p.alpha != nullptr && p.b <= 128 &&
+         p.pages.table == nullptr && mix_tiles(p) <= kMaxTiles;
+}
+
 size_t attn_fwd_workspace_bytes(const AttnLaunch& p) {
-  if (!use_decode_attn(p)) return 0;
+  const bool mix = use_decode_mix(p);
+  if (!use_decode_attn(p) && !mix) return 0;
   const size_t heads = static_cast<size_t>(p.B) * p.Hsel;
-  const size_t ntiles = static_cast<size_t>(p.K + 1) * decode_tpu(p);
+  const size_t ntiles = mix ? static_cast<size_t>(mix_tiles(p)) : static_cast<size_t>(p.K + 1) * decode_tpu(p);
   const size_t hpw = heads_per_wg(p);
   return align256(heads * ntiles * hpw * p.d * sizeof(float)) +
          align256(heads * ntiles * hpw * sizeof(float2));
@@ -766,6 +884,34 @@ hipError_t launch_decode_fused_attn(const SelectLaunch& s, void* ws_sel, const A
   return a.d == 64 ? launch_fused_d<64>(s, ws_sel, a, ws_att, st) : launch_fused_d<128>(s, ws_sel, a, ws_att, st);
 }
 
+template <typename T, int D, int HPW>
+static hipError_t launch_decode_mix_h(const AttnLaunch& p, void* ws, hipStream_t st) {
+  const int tpu = decode_tpu(p);
+  const int ntiles = mix_tiles(p);
+  const size_t heads = static_cast<size_t>(p.B) * p.Hsel;
+  char* base = static_cast<char*>(ws);
+  float* acc = reinterpret_cast<float*>(base);
+  float2* ml = reinterpret_cast<float2*>(base + align256(heads * ntiles * HPW * p.d * sizeof(float)));
+  hipError_t e = launch(false, decode_mix_partial_kernel<T, D, HPW>, dim3(ntiles, static_cast<unsigned>(heads)),
+                        dim3(256), st, static_cast<const T*>(p.q), static_cast<const T*>(p.k),
+                        static_cast<const T*>(p.v), p.idx, p.logg, p.Hq, p.Hkv, p.Hsel, p.share_group, p.L,
+                        p.q_pos0, p.b, p.prefix_mode, p.qblock, p.K, tpu, p.window, ntiles, acc, ml);
+  if (e != hipSuccess) return e;
+  return launch(true, decode_mix_combine_kernel<T, D, HPW>, dim3(HPW, static_cast<unsigned>(heads)), dim3(256),
+                st, acc, ml, p.Hq, p.Hkv, p.Hsel, p.share_group, p.K * tpu, ntiles, p.alpha, static_cast<T*>(p.o),
+                p.lse);
+}
+
+template <typename T, int D>
+static hipError_t launch_decode_mix_t(const AttnLaunch& p, void* ws, hipStream_t st) {
+  switch (heads_per_wg(p)) {
+    case 1: return launch_decode_mix_h<T, D, 1>(p, ws, st);
+    case 2: return launch_decode_mix_h<T, D, 2>(p, ws, st);
+    case 4: return launch_decode_mix_h<T, D, 4>(p, ws, st);
+    default: return launch_decode_mix_h<T, D, 8>(p, ws, st);
+  }
+}
+
 template <typename T, int D>
 static hipError_t launch_decode_attn_t(const AttnLaunch& p, void* ws, hipStream_t st) {
   switch (heads_per_wg(p)) {
@@ -789,6 +935,10 @@ hipError_t launch_attn_fwd(const AttnLaunch& p, void* ws, hipStream_t st) {
   if (use_decode_attn(p)) {
     if (p.dtype == 1) return p.d == 64 ? launch_decode_attn_t<bf16_t, 64>(p, ws, st) : launch_decode_attn_t<bf16_t, 128>(p, ws, st);
     return p.d == 64 ? launch_decode_attn_t<float, 64>(p, ws, st) : launch_decode_attn_t<float, 128>(p, ws, st);
+  }
+  if (use_decode_mix(p)) {
+    if (p.dtype == 1) return p.d == 64 ? launch_decode_mix_t<bf16_t, 64>(p, ws, st) : launch_decode_mix_t<bf16_t, 128>(p, ws, st);
+    return p.d == 64 ? launch_decode_mix_t<float, 64>(p, ws, st) : launch_decode_mix_t<float, 128>(p, ws, st);
   }
   if (attn_tile_fwd_supported(p)) return launch_attn_tile_fwd(p, st);
   if (p.dtype == 1) return p.d == 64 ? launch_rows_fwd_t<bf16_t, 64>(p, st) : launch_rows_fwd_t<bf16_t, 128>(p, st);

@@ -531,3 +531,43 @@ def test_select_rows_no_erf_parity(over, share_group, gate):
     _say(f"[select rows] {over} share_group={share_group} gate={gate}")
     x = make_inputs(cfg)
     _say(f"  exempt rows {_select_only(cfg, x, gate=gate, share_group=share_group, erf=False, prefix_mode=0)}")
+
+
+# ------------------------------------------------------------------ decode of the two-branch head
+@pytest.mark.parametrize("over,pos_frac,with_gate", [
+    (dict(n=4096, Hq=4, Hkv=4, seed=101), 1.0, False),                 # FreeSolo geometry, last row
+    (dict(n=4096, Hq=4, Hkv=4, seed=102), 0.02, False),                # first query block: no cells
+    (dict(n=4096, Hq=4, Hkv=4, seed=103), 0.07, False),                # window clipped at token 0
+    (dict(n=2048, Hq=8, Hkv=2, d=128, K=6, seed=104), 0.61, True),     # G = 4 shared, gates as bias
+    (dict(n=2048, Hq=2, Hkv=2, dtype="f32", K=3, b=64, qblock=256, window=200, seed=105), 0.8, False),
+])
+def test_decode_two_branch_parity(over, pos_frac, with_gate):
+    """One query row of the cell-routing head: selected cells (branch L) and
+    the window (branch S) mixed with alpha, on the oracle's selection."""
+    sg = over.get("Hq", 16) != over.get("Hkv", 16)
+    cfg = config("prefill_cells", share_group=sg, **over)
+    _say(f"[decode two-branch] {over} pos_frac={pos_frac} gate={with_gate}")
+    x = make_inputs(cfg)
+    b, qb, K, L = cfg["b"], cfg["qblock"], cfg["K"], x["L"]
+    pos = min(L - 1, int(pos_frac * L))
+    q1 = np.ascontiguousarray(x["q"][:, :, pos:pos + 1])
+    Hsel = cfg["Hkv"] if sg else cfg["Hq"]
+    kb, mx, ce = oracle.block_summaries(x["k"], b, nblocks=L // b)
+    kw = dict(Hkv=cfg["Hkv"], b=b, K=K, q_pos0=pos, gate=with_gate, prefix_mode=1, qblock=qb, share_group=sg)
+    lam = np.ascontiguousarray(x["erf_lambda"][:Hsel])
+    sig = np.ascontiguousarray(x["erf_sigma"][:Hsel])
+    ora = oracle.score_select(q1, kb, mx, ce, erf_lambda=lam, erf_sigma=sig, **kw)
+    logg = ora["logg"] if with_gate else None
+    akw = dict(b=b, K=K, q_pos0=pos, share_group=sg, local=1, window=cfg["window"], prefix_mode=1, qblock=qb)
+    o_o, lse_o = oracle.attn_fwd(q1, x["k"], x["v"], ora["idx"], logg, alpha=x["alpha"], **akw)
+    o, lse = ops.sparse_attn_fwd(dev(q1), dev(x["k"]), dev(x["v"]), dev(ora["idx"]),
+                                 None if logg is None else dev(logg.astype(np.float32)), alpha=dev(x["alpha"]),
+                                 **akw)
+    torch.cuda.synchronize()
+    tol = _tol(cfg)
+    e = rel_err(host(o), o_o)
+    _say(f"  o rel err {e:.2e}")
+    assert e <= tol
+    lse, fin = host(lse), np.isfinite(lse_o)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.abs(lse[fin] - lse_o[fin]).max(initial=0.0) <= 10 * tol
