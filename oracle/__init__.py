@@ -85,6 +85,16 @@ def _declare(lib):
     lib.orc_score_select_subset.restype = None
     lib.orc_score_select_subset.argtypes = [P, I, I, I, I, I, I, I64, P, I, P, P, I64, I, I, I, I, P, P, P, P,
                                             I, I, I, P, P, P, P]
+    lib.orc_forest_nodes.restype = I64
+    lib.orc_forest_nodes.argtypes = [I64, I]
+    lib.orc_forest_build.restype = None
+    lib.orc_forest_build.argtypes = [P, I, P, P, I, I, I, I64, I64, I, P, P, P, P, P, P]
+    lib.orc_forest_select.restype = None
+    lib.orc_forest_select.argtypes = [P, I, I, I, I, I, I, I64, P, I, P, P, I64, P, I64, I, I, P, P, P, P, P, P,
+                                      P, P, I64, I, I, I, P, P]
+    lib.orc_node_score.restype = ctypes.c_double
+    lib.orc_node_score.argtypes = [P, ctypes.c_double, P, ctypes.c_float, ctypes.c_float, ctypes.c_float, I,
+                                   ctypes.c_double, ctypes.c_double, ctypes.c_double, I]
     lib.orc_select_bwd.restype = None
     lib.orc_select_bwd.argtypes = [P, I, I, I, I, I, I, I64, P, I, I64, I, I, I, P, P, P, P, P, P]
     lib.orc_attn_bwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I64, I64, I, P, P, I, I, I64,
@@ -280,6 +290,65 @@ def score_select_subset(q, kbar, max_norm, centre, cells, count, *, Hkv, b, K, q
                                 _ptr(cells), _ptr(count), cells.shape[-1], K, int(bool(gate)), _ptr(idx),
                                 _ptr(logg), _ptr(keff), _ptr(gap))
     return dict(idx=idx, logg=logg, k_eff=keff, gap=gap)
+
+
+FOREST_FANOUT = 16
+FOREST_BEAM = 16
+
+
+def forest_nodes(n, F=FOREST_FANOUT):
+    """Internal nodes of a forest over n member cells."""
+    return int(_load().orc_forest_nodes(int(n), int(F)))
+
+
+def forest_build(kbar, max_norm, centre, n, F=FOREST_FANOUT):
+    """FS-B forests of every (batch, kv head) over the n prefix cells: the
+    whole prefix (forest 0) and the cells at or above the median max norm
+    (forest 1).  Returns dict(members [B,Hkv,2,n] int32 (-1 padded), nmem
+    [B,Hkv,2], mu [B,Hkv,2,NN,d] fp32, rad / amax / pmin [B,Hkv,2,NN] fp32)."""
+    lib = _load()
+    B, Hkv, ccap, d = kbar.shape
+    NN = forest_nodes(n, F)
+    out = dict(members=np.full((B, Hkv, 2, max(n, 1)), -1, np.int32), nmem=np.zeros((B, Hkv, 2), np.int32),
+               mu=np.zeros((B, Hkv, 2, max(NN, 1), d), np.float32), rad=np.zeros((B, Hkv, 2, max(NN, 1)), np.float32),
+               amax=np.zeros((B, Hkv, 2, max(NN, 1)), np.float32), pmin=np.zeros((B, Hkv, 2, max(NN, 1)), np.float32))
+    mx, ce = _f32(max_norm), _f32(centre)
+    lib.orc_forest_build(_ptr(kbar), _dtype_code(kbar), _ptr(mx), _ptr(ce), B, Hkv, d, ccap, int(n), int(F),
+                         _ptr(out["members"]), _ptr(out["nmem"]), _ptr(out["mu"]), _ptr(out["rad"]),
+                         _ptr(out["amax"]), _ptr(out["pmin"]))
+    return out
+
+
+def forest_select(q, kbar, max_norm, centre, k, forest, n, *, Hkv, b, K, q_pos0, share_group=False,
+                  erf_lambda=None, erf_sigma=None, F=FOREST_FANOUT, Wb=FOREST_BEAM):
+    """Beam search of both forests, then the logsumexp re-rank over token keys
+    of the reached cells; top K ascending.  Returns dict(idx, gap) with gap the
+    smallest score margin at any cut (beam levels and the final top K)."""
+    assert F <= 16 and Wb <= 16
+    lib = _load()
+    B, Hq, nq, d = q.shape
+    ccap = kbar.shape[2]
+    L = k.shape[2]
+    Hsel = Hkv if share_group else Hq
+    idx = np.full((B, Hsel, nq, K), -1, np.int32)
+    gap = np.zeros((B, Hsel, nq), np.float64)
+    mx, ce = _f32(max_norm), _f32(centre)
+    lam, sig = _f32(erf_lambda), _f32(erf_sigma)
+    f = {key: np.ascontiguousarray(v) for key, v in forest.items()}
+    lib.orc_forest_select(_ptr(q), _dtype_code(q), B, Hq, Hkv, nq, d, int(q_pos0), _ptr(kbar), _dtype_code(kbar),
+                          _ptr(mx), _ptr(ce), ccap, _ptr(k), L, b, int(bool(share_group)), _ptr(lam), _ptr(sig),
+                          _ptr(f["members"]), _ptr(f["nmem"]), _ptr(f["mu"]), _ptr(f["rad"]), _ptr(f["amax"]),
+                          _ptr(f["pmin"]), int(n), int(F), int(Wb), K, _ptr(idx), _ptr(gap))
+    return dict(idx=idx, gap=gap)
+
+
+def node_score(q_hat, mu, rad, amax, pmin, *, lam, sig, pos, with_erf=True):
+    """U of one node for one query vector q_hat (fp64)."""
+    qh = np.ascontiguousarray(q_hat, dtype=np.float64)
+    m = np.ascontiguousarray(mu, dtype=np.float32)
+    return float(_load().orc_node_score(_ptr(qh), float(np.sqrt((qh * qh).sum())), _ptr(m), float(rad),
+                                        float(amax), float(pmin), qh.shape[0], float(lam), float(sig),
+                                        float(pos), int(bool(with_erf))))
 
 
 def select_bwd(q, kbar, idx, dg, *, Hkv, b, K, q_pos0, share_group=True, proj_w=None):

@@ -949,3 +949,374 @@ void orc_score_select_subset(const void *q, int qdtype, int B, int Hq, int Hkv, 
         free(pick);
     }
 }
+
+/* ------------------------------------------- next: hierarchical selection */
+/*
+ * FS-B forests ("FreeSolo" review, the two variants: no cell is dropped;
+ * each head builds one forest over the whole prefix and one over the cells
+ * whose max key norm is at or above the median; nodes hold a mean key, a
+ * radius, a max norm and a min position; a beam search of width W_b per
+ * level descends them, the node score U upper-bounding the scores of the
+ * cells below; the cells reached are re-ranked by logsumexp over their token
+ * keys and the top K are read).  Readings taken:
+ *   - a forest over m member cells (ascending cell order) is a tree of fanout
+ *     F: node j of level 1 groups members [jF, jF + F), node j of level l
+ *     groups nodes [jF, jF + F) of level l - 1; levels are added until a
+ *     level has at most F nodes (none when m <= F);
+ *   - median: the ceil(n/2)-th largest max norm of the n prefix cells; the
+ *     high-norm forest holds every cell whose norm is >= it;
+ *   - node fields, rounded to fp32 (nearest): mu = (sum of the subtree's cell
+ *     mean keys, summed child by child in fp64) / cells; r = max over the
+ *     subtree's cells of ||kbar_c - mu|| (fp64); a = max a_c; p = min p_c;
+ *   - U_v = q_hat . mu / sqrt(d) + ||q_hat|| r / sqrt(d)
+ *           + lambda a erf((i - p) / (2 sigma)), an upper bound of every
+ *     cell score below v for lambda >= 0 (Cauchy-Schwarz, erf increasing);
+ *     a cell's own score (r = 0) is the FreeSolo cell score;
+ *   - beam: the frontier starts as the top level; each step keeps the W_b
+ *     children of the frontier with the largest score (lower index first on
+ *     ties) until the frontier holds cells: the forest's reached cells;
+ *   - re-rank: the union of both forests' reached cells, scored by
+ *     logsumexp over the cell's tokens j of q_hat . k_j / sqrt(d); top K
+ *     (lower index first on ties), emitted ascending.
+ */
+static int64_t orc_ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+/* internal nodes of a forest over m members, and the first index of each
+ * level (lvl_off[0] = 0 for level 1); returns the number of levels */
+int orc_forest_levels(int64_t m, int F, int64_t *lvl_n, int64_t *lvl_off, int maxlev)
+{
+    int nl = 0;
+    int64_t cur = m, off = 0;
+    while (cur > F && nl < maxlev) {
+        cur = orc_ceil_div(cur, F);
+        lvl_n[nl] = cur;
+        lvl_off[nl] = off;
+        off += cur;
+        ++nl;
+    }
+    return nl;
+}
+
+int64_t orc_forest_nodes(int64_t m, int F)
+{
+    int64_t ln[32], lo[32];
+    const int nl = orc_forest_levels(m, F, ln, lo, 32);
+    return nl ? lo[nl - 1] + ln[nl - 1] : 0;
+}
+
+/* members [B, Hkv, 2, n] (-1 padded), nmem [B, Hkv, 2]; node fields
+ * [B, Hkv, 2, NN(, d)] with NN = orc_forest_nodes(n, F) */
+void orc_forest_build(const void *kbar, int kdtype, const float *max_norm, const float *centre, int B,
+                      int Hkv, int d, int64_t Ccap, int64_t n, int F, int32_t *members, int32_t *nmem,
+                      float *mu, float *rad, float *amax, float *pmin)
+{
+    const int64_t NN = orc_forest_nodes(n, F);
+    for (int t = 0; t < B * Hkv; ++t) {
+        const float *a = max_norm + (int64_t)t * Ccap;
+        /* median: ceil(n/2)-th largest norm */
+        float thr = 0.f;
+        if (n > 0) {
+            float *srt = (float *)malloc(sizeof(float) * (size_t)n);
+            for (int64_t c = 0; c < n; ++c)
+                srt[c] = a[c];
+            /* selection sort of the largest ceil(n/2) (plain, small n) */
+            const int64_t kk = (n + 1) / 2;
+            for (int64_t x = 0; x < kk; ++x) {
+                int64_t best = x;
+                for (int64_t y = x + 1; y < n; ++y)
+                    if (srt[y] > srt[best])
+                        best = y;
+                float tmp = srt[x];
+                srt[x] = srt[best];
+                srt[best] = tmp;
+            }
+            thr = srt[kk - 1];
+            free(srt);
+        }
+        for (int f = 0; f < 2; ++f) {
+            int32_t *mem = members + ((int64_t)t * 2 + f) * n;
+            int64_t m = 0;
+            for (int64_t c = 0; c < n; ++c)
+                if (f == 0 || a[c] >= thr)
+                    mem[m++] = (int32_t)c;
+            for (int64_t x = m; x < n; ++x)
+                mem[x] = -1;
+            nmem[t * 2 + f] = (int32_t)m;
+            int64_t ln[32], lo[32];
+            const int nl = orc_forest_levels(m, F, ln, lo, 32);
+            const int64_t fb = ((int64_t)t * 2 + f) * NN;
+            const int64_t NNf = nl ? lo[nl - 1] + ln[nl - 1] : 0;
+            double *sums = (double *)calloc((size_t)(NNf > 0 ? NNf : 1) * d, sizeof(double));
+            int64_t *cnt = (int64_t *)calloc((size_t)(NNf > 0 ? NNf : 1), sizeof(int64_t));
+            for (int l = 0; l < nl; ++l) {
+                for (int64_t j = 0; j < ln[l]; ++j) {
+                    const int64_t node = lo[l] + j;
+                    double *sm = sums + node * d;
+                    float am = 0.f, pm = INFINITY;
+                    if (l == 0) {
+                        for (int64_t x = j * F; x < (j + 1) * F && x < m; ++x) {
+                            const int64_t c = mem[x];
+                            for (int e = 0; e < d; ++e)
+                                sm[e] += orc_load(kbar, kdtype, ((int64_t)t * Ccap + c) * d + e);
+                            cnt[node] += 1;
+                            if (a[c] > am)
+                                am = a[c];
+                            if (centre[c] < pm)
+                                pm = centre[c];
+                        }
+                    } else {
+                        const int64_t nprev = ln[l - 1];
+                        for (int64_t x = j * F; x < (j + 1) * F && x < nprev; ++x) {
+                            const int64_t ch = lo[l - 1] + x;
+                            for (int e = 0; e < d; ++e)
+                                sm[e] += sums[ch * d + e];
+                            cnt[node] += cnt[ch];
+                            if (amax[fb + ch] > am)
+                                am = amax[fb + ch];
+                            if (pmin[fb + ch] < pm)
+                                pm = pmin[fb + ch];
+                        }
+                    }
+                    for (int e = 0; e < d; ++e)
+                        mu[(fb + node) * d + e] = (float)(sm[e] / (double)cnt[node]);
+                    amax[fb + node] = am;
+                    pmin[fb + node] = pm;
+                }
+            }
+            /* radius: over the cells below each node */
+            for (int l = 0; l < nl; ++l) {
+                int64_t span = F;   /* members per node at this level */
+                for (int x = 0; x < l; ++x)
+                    span *= F;
+                for (int64_t j = 0; j < ln[l]; ++j) {
+                    const int64_t node = lo[l] + j;
+                    double best = 0.0;
+                    for (int64_t x = j * span; x < (j + 1) * span && x < m; ++x) {
+                        const int64_t c = mem[x];
+                        double ss = 0.0;
+                        for (int e = 0; e < d; ++e) {
+                            const double df = orc_load(kbar, kdtype, ((int64_t)t * Ccap + c) * d + e) -
+                                              (double)mu[(fb + node) * d + e];
+                            ss += df * df;
+                        }
+                        if (ss > best)
+                            best = ss;
+                    }
+                    rad[fb + node] = (float)sqrt(best);
+                }
+            }
+            for (int64_t x = NNf; x < NN; ++x) {   /* unused slots of the smaller forest */
+                for (int e = 0; e < d; ++e)
+                    mu[(fb + x) * d + e] = 0.f;
+                rad[fb + x] = 0.f;
+                amax[fb + x] = 0.f;
+                pmin[fb + x] = 0.f;
+            }
+            free(sums);
+            free(cnt);
+        }
+    }
+}
+
+/* U_v of one node for one query (q_hat, its norm, the row position) */
+double orc_node_score(const double *qh, double qn, const float *mu, float rad, float amax, float pmin, int d,
+                      double lam, double sig, double pos, int with_erf)
+{
+    double dot = 0.0;
+    for (int e = 0; e < d; ++e)
+        dot += qh[e] * (double)mu[e];
+    const double isd = 1.0 / sqrt((double)d);
+    double s = dot * isd + qn * (double)rad * isd;
+    if (with_erf)
+        s += lam * (double)amax * erf((pos - (double)pmin) / (2.0 * sig));
+    return s;
+}
+
+/* top-w of s[0..cnt) by (score desc, position asc) into keep[]; returns the
+ * number kept and the gap between the last kept and the best dropped score */
+static int orc_top_w(const double *s, int cnt, int w, int *keep, double *gap)
+{
+    char *taken = (char *)calloc((size_t)(cnt > 0 ? cnt : 1), 1);
+    const int kk = cnt < w ? cnt : w;
+    double last = INFINITY;
+    for (int t = 0; t < kk; ++t) {
+        int best = -1;
+        for (int x = 0; x < cnt; ++x)
+            if (!taken[x] && (best < 0 || s[x] > s[best]))
+                best = x;
+        taken[best] = 1;
+        keep[t] = best;
+        last = s[best];
+    }
+    double rest = -INFINITY;
+    for (int x = 0; x < cnt; ++x)
+        if (!taken[x] && s[x] > rest)
+            rest = s[x];
+    if (gap && kk < cnt && last - rest < *gap)
+        *gap = last - rest;
+    free(taken);
+    return kk;
+}
+
+void orc_forest_select(const void *q, int qdtype, int B, int Hq, int Hkv, int nq, int d, int64_t q_pos0,
+                       const void *kbar, int kdtype, const float *max_norm, const float *centre,
+                       int64_t Ccap, const void *k, int64_t L, int b, int share_group,
+                       const float *erf_lambda, const float *erf_sigma, const int32_t *members,
+                       const int32_t *nmem, const float *mu, const float *rad, const float *amax,
+                       const float *pmin, int64_t n, int F, int Wb, int K, int32_t *idx, double *gap)
+{
+    const int Hsel = share_group ? Hkv : Hq;
+    const int G = Hq / Hkv;
+    const int64_t NN = orc_forest_nodes(n, F);
+    const double isd = 1.0 / sqrt((double)d);
+    const int64_t total = (int64_t)B * Hsel * nq;
+    int64_t w;
+#pragma omp parallel for schedule(dynamic)
+    for (w = 0; w < total; ++w) {
+        const int64_t row = w % nq;
+        const int hs = (int)((w / nq) % Hsel);
+        const int bidx = (int)(w / nq / Hsel);
+        const int kvh = share_group ? hs : hs / G;
+        const int64_t t = (int64_t)bidx * Hkv + kvh;
+        const double pos = (double)(q_pos0 + row);
+        double *qh = (double *)calloc((size_t)d, sizeof(double));
+        const int gq = share_group ? G : 1;
+        const int h0 = share_group ? hs * G : hs;
+        for (int g = 0; g < gq; ++g)
+            for (int e = 0; e < d; ++e)
+                qh[e] += orc_load(q, qdtype, (((int64_t)bidx * Hq + h0 + g) * nq + row) * d + e);
+        double qn = 0.0;
+        for (int e = 0; e < d; ++e) {
+            qh[e] /= (double)gq;
+            qn += qh[e] * qh[e];
+        }
+        qn = sqrt(qn);
+        const double lam = erf_lambda ? (double)erf_lambda[hs] : 0.0;
+        const double sig = erf_sigma ? (double)erf_sigma[hs] : 1.0;
+        double g_min = INFINITY;
+        int32_t reached[64];
+        int nreach = 0;
+        int64_t cid[256];
+        double sc[256];
+        int keep[256];
+        for (int f = 0; f < 2; ++f) {
+            const int32_t *mem = members + (t * 2 + f) * n;
+            const int64_t m = nmem[t * 2 + f];
+            const int64_t fb = (t * 2 + f) * NN;
+            int64_t ln[32], lo[32];
+            const int nl = orc_forest_levels(m, F, ln, lo, 32);
+            /* frontier: ids at level `lev` (0 = member positions) */
+            int64_t front[64];
+            int nf = 0, lev = nl;
+            const int64_t ntop = nl ? ln[nl - 1] : m;
+            for (int64_t x = 0; x < ntop; ++x)
+                front[nf++] = x;
+            for (;;) {
+                /* candidates: the frontier itself at the start of a level-0 forest,
+                 * else the children of the frontier */
+                int cnt = 0;
+                const int child_lev = (lev == nl && nl == 0) ? 0 : lev - 1;
+                if (lev == nl && nl == 0) {
+                    for (int x = 0; x < nf; ++x)
+                        cid[cnt++] = front[x];
+                } else {
+                    const int64_t nchild = child_lev == 0 ? m : ln[child_lev - 1];
+                    for (int x = 0; x < nf; ++x)
+                        for (int64_t y = front[x] * F; y < (front[x] + 1) * F && y < nchild; ++y)
+                            cid[cnt++] = y;
+                }
+                for (int x = 0; x < cnt; ++x) {
+                    double s;
+                    if (child_lev == 0) {
+                        const int64_t c = mem[cid[x]];
+                        double dot = 0.0;
+                        for (int e = 0; e < d; ++e)
+                            dot += qh[e] * orc_load(kbar, kdtype, (t * Ccap + c) * d + e);
+                        s = dot * isd;
+                        if (erf_lambda)
+                            s += lam * (double)max_norm[t * Ccap + c] * erf((pos - (double)centre[c]) / (2.0 * sig));
+                    } else {
+                        const int64_t node = fb + lo[child_lev - 1] + cid[x];
+                        s = orc_node_score(qh, qn, mu + node * d, rad[node], amax[node], pmin[node], d, lam, sig,
+                                           pos, erf_lambda != NULL);
+                    }
+                    sc[x] = s;
+                }
+                const int kk = orc_top_w(sc, cnt, Wb, keep, &g_min);
+                /* keep the frontier in candidate order (ascending ids) */
+                for (int x = 1; x < kk; ++x) {
+                    int v = keep[x], y = x - 1;
+                    while (y >= 0 && keep[y] > v) {
+                        keep[y + 1] = keep[y];
+                        --y;
+                    }
+                    keep[y + 1] = v;
+                }
+                nf = kk;
+                for (int x = 0; x < kk; ++x)
+                    front[x] = cid[keep[x]];
+                if (child_lev == 0)
+                    break;
+                lev = child_lev;
+            }
+            for (int x = 0; x < nf; ++x) {
+                const int32_t c = mem[front[x]];
+                int dup = 0;
+                for (int y = 0; y < nreach; ++y)
+                    if (reached[y] == c)
+                        dup = 1;
+                if (!dup)
+                    reached[nreach++] = c;
+            }
+        }
+        /* re-rank the reached cells by logsumexp over their tokens */
+        double *lse = (double *)malloc(sizeof(double) * 64);
+        /* ascending cell order first, so that ties go to the lower cell */
+        for (int x = 1; x < nreach; ++x) {
+            int32_t v = reached[x];
+            int y = x - 1;
+            while (y >= 0 && reached[y] > v) {
+                reached[y + 1] = reached[y];
+                --y;
+            }
+            reached[y + 1] = v;
+        }
+        for (int x = 0; x < nreach; ++x) {
+            const int64_t c = reached[x];
+            double mx = -INFINITY, z[1024];
+            for (int j = 0; j < b; ++j) {
+                double dot = 0.0;
+                for (int e = 0; e < d; ++e)
+                    dot += qh[e] * orc_load(k, kdtype, (t * L + c * b + j) * d + e);
+                z[j] = dot * isd;
+                if (z[j] > mx)
+                    mx = z[j];
+            }
+            double acc = 0.0;
+            for (int j = 0; j < b; ++j)
+                acc += exp(z[j] - mx);
+            lse[x] = mx + log(acc);
+        }
+        int pick[64];
+        const int kk = orc_top_w(lse, nreach, K, pick, &g_min);
+        int32_t outc[64];
+        for (int x = 0; x < kk; ++x)
+            outc[x] = reached[pick[x]];
+        for (int x = 1; x < kk; ++x) {
+            int32_t v = outc[x];
+            int y = x - 1;
+            while (y >= 0 && outc[y] > v) {
+                outc[y + 1] = outc[y];
+                --y;
+            }
+            outc[y + 1] = v;
+        }
+        const int64_t o = ((int64_t)bidx * Hsel + hs) * nq + row;
+        for (int x = 0; x < K; ++x)
+            idx[o * K + x] = x < kk ? outc[x] : -1;
+        if (gap)
+            gap[o] = g_min;
+        free(qh);
+        free(lse);
+    }
+}
