@@ -395,6 +395,79 @@ int sparse_score_select_subset(const spa_select_args* a, const int32_t* cells, c
                     "sparse_score_select_subset");
 }
 
+int64_t sparse_forest_nodes(int64_t n) { return n < 1 ? 0 : spa::forest_nodes(n); }
+
+size_t sparse_forest_workspace_bytes(int B, int Hkv, int d, int64_t n) {
+  if (B < 1 || Hkv < 1 || d < 1 || n < 1) return 0;
+  return spa::forest_workspace_bytes(B, Hkv, d, n);
+}
+
+int check_forest(const spa_forest* fo, int B, int Hkv, int64_t ccap, int64_t n, spa::ForestLaunch* p) {
+  SPA_REQUIRE(fo != nullptr && fo->members && fo->nmem && fo->mu && fo->rad && fo->amax && fo->pmin,
+              SPA_ERR_INVALID_ARG, "forest arrays must be non-NULL");
+  SPA_REQUIRE(n >= 1 && n <= ccap && n < (static_cast<int64_t>(1) << 31), SPA_ERR_INVALID_ARG,
+              "n = %lld outside [1, ccap = %lld]", static_cast<long long>(n), static_cast<long long>(ccap));
+  SPA_REQUIRE(static_cast<int64_t>(B) * Hkv <= 65535, SPA_ERR_UNSUPPORTED, "B * Hkv exceeds 65535");
+  p->B = B;
+  p->Hkv = Hkv;
+  p->ccap = ccap;
+  p->n = n;
+  p->members = fo->members;
+  p->nmem = fo->nmem;
+  p->mu = fo->mu;
+  p->rad = fo->rad;
+  p->amax = fo->amax;
+  p->pmin = fo->pmin;
+  return SPA_OK;
+}
+
+int sparse_forest_build(const void* kbar, int dtype, const float* max_norm, const float* centre, int B, int Hkv,
+                        int d, int64_t ccap, int64_t n, const spa_forest* forest, void* workspace, size_t ws_bytes,
+                        spa_stream_t stream) {
+  ProfileScope profile_scope;
+  int st = check_heads(B, Hkv, Hkv, d, dtype);
+  if (st != SPA_OK) return st;
+  SPA_REQUIRE(kbar && max_norm && centre, SPA_ERR_INVALID_ARG, "kbar, max_norm and centre must be non-NULL");
+  spa::ForestLaunch p{};
+  st = check_forest(forest, B, Hkv, ccap, n, &p);
+  if (st != SPA_OK) return st;
+  st = check_ws(workspace, ws_bytes, spa::forest_workspace_bytes(B, Hkv, d, n));
+  if (st != SPA_OK) return st;
+  p.kbar = kbar;
+  p.dtype = dtype;
+  p.d = d;
+  p.max_norm = max_norm;
+  p.centre = centre;
+  p.ws = workspace;
+  return hip_status(spa::launch_forest_build(p, static_cast<hipStream_t>(stream)), "sparse_forest_build");
+}
+
+int sparse_forest_select(const spa_select_args* a, const void* k, int64_t L, const spa_forest* forest, int64_t n,
+                         spa_stream_t stream) {
+  ProfileScope profile_scope;
+  spa::SelectLaunch s;
+  int st = check_select(a, &s);
+  if (st != SPA_OK) return st;
+  SPA_REQUIRE(a->gate == SPA_GATE_NONE && a->proj_w == nullptr, SPA_ERR_UNSUPPORTED,
+              "the forest selection takes no gate and no projection");
+  SPA_REQUIRE(a->K <= 16, SPA_ERR_UNSUPPORTED, "K = %d not supported (<= 16)", a->K);
+  SPA_REQUIRE(a->b == 16 || a->b == 32 || a->b == 64, SPA_ERR_UNSUPPORTED, "cell size b = %d not supported", a->b);
+  SPA_REQUIRE(k != nullptr && aligned16(k), SPA_ERR_INVALID_ARG, "k must be non-NULL and 16-byte aligned");
+  SPA_REQUIRE(L >= n * a->b, SPA_ERR_INVALID_ARG, "k holds L = %lld tokens, fewer than the n cells",
+              static_cast<long long>(L));
+  const int qb = a->prefix_mode == SPA_PREFIX_QUERY_BLOCK ? a->qblock : 1;
+  const int64_t c_first = spa::num_candidates(a->q_pos0, a->b, a->prefix_mode, qb);
+  const int64_t c_last = spa::num_candidates(a->q_pos0 + a->nq - 1, a->b, a->prefix_mode, qb);
+  SPA_REQUIRE(c_first == n && c_last == n, SPA_ERR_INVALID_ARG,
+              "every row must have the n = %lld cells the forests were built over as its candidates",
+              static_cast<long long>(n));
+  spa::ForestLaunch p{};
+  st = check_forest(forest, a->B, a->Hkv, a->ccap, n, &p);
+  if (st != SPA_OK) return st;
+  return hip_status(spa::launch_forest_select(s, p, k, L, static_cast<hipStream_t>(stream)),
+                    "sparse_forest_select");
+}
+
 size_t sparse_workspace_bytes(int op, const void* args) {
   switch (op) {
     case SPA_OP_SCORE_SELECT: {

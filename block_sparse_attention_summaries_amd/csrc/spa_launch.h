@@ -66,6 +66,23 @@ struct SelectGrads {
   int64_t L;
 };
 
+// FS-B forests of every (batch, kv head): members [B, Hkv, 2, n], nmem
+// [B, Hkv, 2], node fields [B, Hkv, 2, NN(, d)], NN = forest_nodes(n).
+struct ForestLaunch {
+  const void* kbar;
+  int dtype, B, Hkv, d;
+  int64_t ccap, n;
+  const float* max_norm;
+  const float* centre;
+  int32_t* members;
+  int32_t* nmem;
+  float* mu;
+  float* rad;
+  float* amax;
+  float* pmin;
+  void* ws;
+};
+
 struct AttnLaunch {
   const void* q;
   const void* k;
@@ -168,6 +185,11 @@ hipError_t launch_retain_cells(const float* max_norm, int B, int Hkv, int64_t cc
                                int32_t* cells, int32_t* count, hipStream_t st);
 hipError_t launch_score_select_subset(const SelectLaunch& p, const int32_t* cells, const int32_t* count, int cap,
                                       hipStream_t st);
+int64_t forest_nodes(int64_t m);
+size_t forest_workspace_bytes(int B, int Hkv, int d, int64_t n);
+hipError_t launch_forest_build(const ForestLaunch& p, hipStream_t st);
+hipError_t launch_forest_select(const SelectLaunch& s, const ForestLaunch& p, const void* k, int64_t L,
+                                hipStream_t st);
 bool decode_fusable(const SelectLaunch& p);
 int decode_merge_nv(const SelectLaunch& p);
 hipError_t launch_decode_chunks(const SelectLaunch& p, void* ws, hipStream_t st);

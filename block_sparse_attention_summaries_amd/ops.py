@@ -29,7 +29,8 @@ SPA_OP_SCORE_SELECT, SPA_OP_ATTN_FWD, SPA_OP_ATTN_BWD, SPA_OP_SELECT_BWD, SPA_OP
 EXPORTED = ["spa_abi_version", "spa_profile_next_call", "spa_last_error", "sparse_block_summaries", "sparse_score_select",
             "sparse_attn_fwd", "sparse_attn_bwd", "sparse_select_bwd", "sparse_decode_step",
             "sparse_block_summaries_paged", "sparse_decode_step_paged", "sparse_retain_cells",
-            "sparse_score_select_subset", "sparse_workspace_bytes", "sparse_workspace_init"]
+            "sparse_score_select_subset", "sparse_forest_nodes", "sparse_forest_workspace_bytes",
+            "sparse_forest_build", "sparse_forest_select", "sparse_workspace_bytes", "sparse_workspace_init"]
 
 _vp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
 
@@ -59,6 +60,10 @@ class DecodeArgs(ctypes.Structure):
 
 class KvPages(ctypes.Structure):
     _fields_ = [("block_table", _vp), ("table_stride", _i64), ("num_pages", _i64)]
+
+
+class Forest(ctypes.Structure):
+    _fields_ = [("members", _vp), ("nmem", _vp), ("mu", _vp), ("rad", _vp), ("amax", _vp), ("pmin", _vp)]
 
 
 class SpaError(RuntimeError):
@@ -107,6 +112,15 @@ def lib():
         L.sparse_retain_cells.argtypes = [_vp, _i, _i, _i64, _i64, _i, _i, _vp, _vp, _vp]
         L.sparse_score_select_subset.restype = _i
         L.sparse_score_select_subset.argtypes = [ctypes.POINTER(SelectArgs), _vp, _vp, _i, _vp]
+        L.sparse_forest_nodes.restype = _i64
+        L.sparse_forest_nodes.argtypes = [_i64]
+        L.sparse_forest_workspace_bytes.restype = _sz
+        L.sparse_forest_workspace_bytes.argtypes = [_i, _i, _i, _i64]
+        L.sparse_forest_build.restype = _i
+        L.sparse_forest_build.argtypes = [_vp, _i, _vp, _vp, _i, _i, _i, _i64, _i64, ctypes.POINTER(Forest), _vp,
+                                          _sz, _vp]
+        L.sparse_forest_select.restype = _i
+        L.sparse_forest_select.argtypes = [ctypes.POINTER(SelectArgs), _vp, _i64, ctypes.POINTER(Forest), _i64, _vp]
         L.sparse_workspace_bytes.restype = _sz
         L.sparse_workspace_bytes.argtypes = [_i, _vp]
         L.sparse_workspace_init.restype = _i
@@ -380,3 +394,40 @@ def sparse_score_select_subset(q, kbar, max_norm, centre, cells, count, *, strea
     _check(lib().sparse_score_select_subset(ctypes.byref(a), _p(cells), _p(count), cells.shape[-1],
                                             _stream(stream)))
     return outs
+
+
+def sparse_forest_build(kbar, max_norm, centre, n, forest=None, workspace=None, stream=None):
+    """FS-B forests of every (batch, kv head) over the n prefix cells (summaries
+    as sparse_block_summaries writes them).  Returns a dict of the forest arrays
+    (members, nmem, mu, rad, amax, pmin); node arrays get one zero slot when a
+    forest has no internal node (n <= 16)."""
+    _contig(kbar, max_norm, centre)
+    B, Hkv, ccap, d = kbar.shape
+    NN = max(int(lib().sparse_forest_nodes(n)), 1)
+    dev_ = kbar.device
+    if forest is None:
+        forest = dict(members=torch.empty((B, Hkv, 2, n), dtype=torch.int32, device=dev_),
+                      nmem=torch.empty((B, Hkv, 2), dtype=torch.int32, device=dev_),
+                      mu=torch.zeros((B, Hkv, 2, NN, d), dtype=torch.float32, device=dev_),
+                      rad=torch.zeros((B, Hkv, 2, NN), dtype=torch.float32, device=dev_),
+                      amax=torch.zeros((B, Hkv, 2, NN), dtype=torch.float32, device=dev_),
+                      pmin=torch.zeros((B, Hkv, 2, NN), dtype=torch.float32, device=dev_))
+    fo = Forest(**{k: _p(v) for k, v in forest.items()})
+    need = lib().sparse_forest_workspace_bytes(B, Hkv, d, n)
+    if workspace is None:
+        workspace = _default_ws.setdefault((str(dev_), "forest"), Workspace(dev_))
+    buf, size = workspace.get(need)
+    _check(lib().sparse_forest_build(_p(kbar), _dtype(kbar), _p(max_norm), _p(centre), B, Hkv, d, ccap, n,
+                                     ctypes.byref(fo), _p(buf), size, _stream(stream)))
+    return forest
+
+
+def sparse_forest_select(q, kbar, max_norm, centre, k, forest, n, *, stream=None, **kw):
+    """Per-query top K cells by the beam search of both forests and the
+    logsumexp re-rank over the token keys k [B, Hkv, L, d].  Returns
+    (idx, k_eff)."""
+    kw.setdefault("gate", False)
+    a, (idx, _, k_eff) = select_args(q, kbar, max_norm, centre, **kw)
+    fo = Forest(**{key: _p(v) for key, v in forest.items()})
+    _check(lib().sparse_forest_select(ctypes.byref(a), _p(k), k.shape[2], ctypes.byref(fo), n, _stream(stream)))
+    return idx, k_eff

@@ -283,6 +283,59 @@ int sparse_score_select_subset(const spa_select_args *a, const int32_t *cells,
                                const int32_t *count, int cap, spa_stream_t stream);
 
 /*
+ * FS-B forests ("FreeSolo" review, the two variants: no cell is dropped; each
+ * head builds a forest over the whole prefix and one over the cells at or
+ * above the median max key norm; nodes hold a mean key, a radius, a max norm
+ * and a min position; a beam of width 16 per level descends them, the node
+ * score bounding the cell scores below; the reached cells are re-ranked by
+ * logsumexp over their token keys and the top K are read).
+ * A forest over m member cells (ascending) has fanout 16: node j of level 1
+ * groups members [16j, 16j+16), node j of level l groups nodes [16j, 16j+16)
+ * of level l-1, levels being added until one has at most 16 nodes.  Node
+ * fields, fp32: mu (mean of the cells' mean keys), rad (max distance of those
+ * to mu), amax (max max-norm), pmin (min centre).  Node score
+ *   U = q_hat . mu / sqrt(d) + ||q_hat|| rad / sqrt(d) + lambda amax erf((i - pmin) / (2 sigma)).
+ * Arrays (device, caller-owned), NN = sparse_forest_nodes(n), forest f = 0
+ * (whole prefix) or 1 (norm >= the ceil(n/2)-th largest):
+ *   members [B, Hkv, 2, n] int32 ascending, -1 padded; nmem [B, Hkv, 2];
+ *   mu [B, Hkv, 2, NN, d]; rad, amax, pmin [B, Hkv, 2, NN] (levels stored
+ *   bottom-up, level 1 first; unused slots 0).
+ */
+typedef struct spa_forest {
+    int32_t *members;
+    int32_t *nmem;
+    float *mu;
+    float *rad;
+    float *amax;
+    float *pmin;
+} spa_forest;
+
+/* Internal nodes of a forest over n cells (0 for n <= 16). */
+int64_t sparse_forest_nodes(int64_t n);
+
+/* Workspace bytes of sparse_forest_build (fp64 node sums). */
+size_t sparse_forest_workspace_bytes(int B, int Hkv, int d, int64_t n);
+
+/* sparse_forest_build -- both forests of every (batch, kv head) over the n
+ * prefix cells 0 .. n-1, from the cell summaries (kbar [B, Hkv, ccap, d] in
+ * dtype, max_norm [B, Hkv, ccap], centre [ccap], as sparse_block_summaries
+ * writes them).  1 <= n <= ccap.  Query-independent: build when a query
+ * block's prefix grows. */
+int sparse_forest_build(const void *kbar, int dtype, const float *max_norm, const float *centre,
+                        int B, int Hkv, int d, int64_t ccap, int64_t n, const spa_forest *forest,
+                        void *workspace, size_t ws_bytes, spa_stream_t stream);
+
+/* sparse_forest_select -- the per-query top K cells by the beam search of both
+ * forests and the logsumexp re-rank over token keys (k [B, Hkv, L, d], the
+ * cache the cells summarise, L >= n b).  `a` as for sparse_score_select, with
+ * gate NONE, no projection, K <= 16, b in {16, 32, 64}; every row must have
+ * exactly the n forest cells as candidates (same query block).  Writes idx
+ * (ascending, -1 padded) and k_eff; logg is not written.  Scores in fp64.
+ * No workspace. */
+int sparse_forest_select(const spa_select_args *a, const void *k, int64_t L,
+                         const spa_forest *forest, int64_t n, spa_stream_t stream);
+
+/*
  * sparse_attn_bwd -- backward of sparse_attn_fwd in the SAS mode
  * (local = CURRENT_BLOCK, window = 0, alpha = NULL), recomputing the
  * probabilities from lse:
