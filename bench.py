@@ -1,6 +1,7 @@
 """Benchmark: decode attention step at 512K context on one MI355X, plus prefill
-tokens/s (cell routing, n = 16384), the FS-L fixed-state decode step at 512K
-(fsl_decode_us_per_step) and training tokens/s.
+tokens/s (cell routing, n = 16384), the FS-L fixed-state and FS-B forest
+decode steps at 512K (fsl_decode_us_per_step, fsb_decode_us_per_step) and
+training tokens/s.
 
 One decode step = the hot path for one query token of one layer:
   score + softmax log gate + top-K select over all C = 8192 block summaries,
@@ -475,8 +476,47 @@ def run_fsl_decode(steps, n_layers=4, n_queries=32):
     e1.record()
     torch.cuda.synchronize()
     retain_us = e0.elapsed_time(e1) * 1e3 / 16
+
+    # FS-B on the same caches: forests over the prefix cells (once per query
+    # block), then per step the beam search + re-rank and the same attention
+    forests = [ops.sparse_forest_build(kb, mx, ce, ncand) for (kb, mx, ce) in summ]
+    torch.cuda.synchronize()
+    e0.record()
+    for layer in range(n_layers):
+        kb, mx, ce = summ[layer]
+        ops.sparse_forest_build(kb, mx, ce, ncand, forest=forests[layer])
+    e1.record()
+    torch.cuda.synchronize()
+    build_us = e0.elapsed_time(e1) * 1e3 / n_layers
+
+    def fsb_step(s):
+        layer, qi = s % n_layers, s % n_queries
+        kb, mx, ce = summ[layer]
+        ops.sparse_forest_select(qs[qi], kb, mx, ce, ks[layer], forests[layer], ncand, Hkv=H, b=b, K=K,
+                                 q_pos0=pos, prefix_mode=1, qblock=qb, share_group=False, erf_lambda=lam,
+                                 erf_sigma=sig, idx=idx, k_eff=keff)
+        ops.sparse_attn_fwd(qs[qi], ks[layer], vs[layer], idx, None, alpha=alpha, o=o, lse=lse, **akw)
+
+    for s in range(4):
+        fsb_step(s)
+    torch.cuda.synchronize()
+    graph2 = torch.cuda.CUDAGraph()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        graph2.capture_begin()
+        for s in range(steps):
+            fsb_step(s)
+        graph2.capture_end()
+    torch.cuda.current_stream().wait_stream(stream)
+    graph2.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    graph2.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    fsb_us = e0.elapsed_time(e1) * 1e3 / steps
     del ks, vs
-    return dict(us_per_step=us, retain_us=retain_us, cells=ncand)
+    return dict(us_per_step=us, retain_us=retain_us, cells=ncand, fsb_us=fsb_us, forest_build_us=build_us)
 
 
 # ---------------------------------------------------------------- CPU oracle baseline
@@ -673,6 +713,8 @@ def main():
         fsl = run_fsl_decode(256)
         out["fsl_decode_us_per_step"] = round(fsl["us_per_step"], 3)
         out["fsl_retain_us"] = round(fsl["retain_us"], 3)
+        out["fsb_decode_us_per_step"] = round(fsl["fsb_us"], 3)
+        out["fsb_forest_build_us"] = round(fsl["forest_build_us"], 3)
         tr = run_train(2)
         out["train_tokens_per_s"] = round(tr["tokens_per_s"], 1)
         out["train_ms"] = {k: round(v, 3) for k, v in tr["ms"].items()}
