@@ -14,17 +14,23 @@
 // max-norm, p = min centre.
 //   U_v = q_hat . mu / sqrt(d) + ||q_hat|| r / sqrt(d) + lambda a erf((i - p) / (2 sigma)).
 //
-//   forest_build_kernel   one workgroup per (batch, kv head, forest): the
-//                         median by a radix select (four 8-bit passes over an
-//                         LDS histogram), the members by an ordered compaction,
-//                         then the levels bottom-up (fp64 sums in the
-//                         workspace) and the radii (a thread per level-1 node,
-//                         a wave per node above).
-//   forest_select_kernel  one wave per (batch, selection head, query row):
-//                         per forest, the beam (up to 256 children scored in
-//                         fp64, the 16 best kept by repeated arg-max, lower id
-//                         first on ties), then the union of the reached cells
-//                         re-ranked by the logsumexp of their token scores.
+//   build                 forest_members_kernel, one workgroup per (batch, kv
+//                         head, forest): the median by a bitwise threshold
+//                         search (workgroup counts), the members by an
+//                         ordered compaction of ballot masks;
+//                         forest_level1_kernel and forest_level_kernel (one
+//                         launch per level above, a wave per node): fp64
+//                         sums in the workspace, child by child;
+//                         forest_radius_kernel: one thread per cell against
+//                         every node above it (maxima reduced per node, then
+//                         an integer atomic max of the fp64 squared distance).
+//   forest_select_kernel  one workgroup per (batch, selection head, query
+//                         row), a half per forest: the beam (up to 256
+//                         children scored in fp64, the 16 best kept by a
+//                         threshold search over the scores' orderable bits,
+//                         lower id first on ties), then the union of the
+//                         reached cells re-ranked by the logsumexp of their
+//                         token scores (the four waves share the cells).
 #include "spa_device.h"
 #include "spa_launch.h"
 
@@ -72,207 +78,461 @@ int64_t forest_nodes(int64_t m) {
 }
 
 // ---------------------------------------------------------------- build
-template <typename T, int D>
-__global__ __launch_bounds__(256) void forest_build_kernel(
-    const T* __restrict__ kbar, const float* __restrict__ max_norm, const float* __restrict__ centre, int64_t ccap,
-    int64_t n, int64_t NN, int32_t* __restrict__ members, int32_t* __restrict__ nmem, float* __restrict__ mu,
-    float* __restrict__ rad, float* __restrict__ amax, float* __restrict__ pmin, double* __restrict__ sums) {
-  __shared__ uint32_t s_hist[256];
-  __shared__ uint32_t s_cnt[256];
-  __shared__ uint32_t s_sel[2];
+// Members of both forests, one 1024-thread workgroup per (batch, kv head,
+// forest).  The high-norm forest's threshold is the ceil(n/2)-th largest max
+// norm, found by a bitwise search over the norms' orderable bits below the
+// common prefix of the smallest and largest (ballot counts summed over the
+// workgroup, stopping once exactly that many are at or above the candidate);
+// its members are then written in cell order from per-wave ballot masks
+// (chunks of 1024 cells, a prefix over chunks and waves).  Cells are held in
+// registers 16384 at a time.
+constexpr int kMemThreads = 1024;
+constexpr int kMemWaves = kMemThreads / kWave;
+
+__global__ __launch_bounds__(kMemThreads) void forest_members_kernel(
+    const float* __restrict__ max_norm, int64_t ccap, int64_t n, int64_t NN, int d, int32_t* __restrict__ members,
+    int32_t* __restrict__ nmem, float* __restrict__ mu, float* __restrict__ rad, float* __restrict__ amax,
+    float* __restrict__ pmin, unsigned long long* __restrict__ rbits) {
+  constexpr int kRegs = 16;                    // cells per thread in registers
+  constexpr int64_t kSpan = static_cast<int64_t>(kMemThreads) * kRegs;
+  __shared__ int s_cnt[kRegs][kMemWaves];
+  __shared__ int64_t s_wbase[kRegs][kMemWaves];
+  __shared__ uint32_t s_lohi[2][kMemWaves];
+  __shared__ int s_part[2][kMemWaves];
+  __shared__ int64_t s_tot;
   __shared__ ForestShape s_sh;                 // in LDS: its arrays are indexed by loop variables
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int64_t head = blockIdx.x;
   const int f = blockIdx.y;
   const float* a = max_norm + head * ccap;
-  const T* kb = kbar + head * ccap * D;
   int32_t* mem = members + (head * 2 + f) * n;
   const int64_t fb = (head * 2 + f) * NN;
-  double* sm = sums + fb * D;
 
-  // 1. median: the ceil(n/2)-th largest max norm (exact, by an 8-bit radix select)
-  uint32_t thr = 0u;
-  if (f == 1 && n > 0) {
-    uint32_t prefix = 0u, mask = 0u;
-    uint32_t kr = static_cast<uint32_t>((n + 1) / 2);
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      s_hist[tid] = 0u;
-      __syncthreads();
-      for (int64_t c = tid; c < n; c += 256) {
-        const uint32_t key = orderable_f32(a[c]);
-        if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t rem = kr;
-        int dg = 255;
-        for (; dg > 0; --dg) {
-          if (s_hist[dg] >= rem) break;
-          rem -= s_hist[dg];
+  int64_t m = n;
+  if (f == 0) {
+    for (int64_t c = tid; c < n; c += kMemThreads) mem[c] = static_cast<int32_t>(c);
+  } else {
+    uint32_t key[kRegs];                       // 0 marks a slot past the prefix (below every norm's key)
+    // keys of cells [s0, s0 + kSpan): cell s0 + j * 1024 + tid in key[j]
+    auto load_span = [&](int64_t s0) {
+      if (s0 + kSpan <= n) {                   // unclamped, so the loads issue together
+        float raw[kRegs];
+#pragma unroll
+        for (int j = 0; j < kRegs; ++j) raw[j] = a[s0 + j * kMemThreads + tid];
+#pragma unroll
+        for (int j = 0; j < kRegs; ++j) key[j] = orderable_f32(raw[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kRegs; ++j) {
+          const int64_t c = s0 + j * kMemThreads + tid;
+          const uint32_t kv = orderable_f32(a[c < n ? c : n - 1]);
+          key[j] = c < n ? kv : 0u;
         }
-        s_sel[0] = static_cast<uint32_t>(dg);
-        s_sel[1] = rem;
+      }
+    };
+    load_span(0);
+    // 1. threshold: the largest t with at least ceil(n/2) norms at or above
+    // it; the search starts below the common prefix of the smallest and the
+    // largest norm
+    uint32_t lo = ~0u, hi = 0u;
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+      if (j * kMemThreads + tid < n) {
+        lo = key[j] < lo ? key[j] : lo;
+        hi = key[j] > hi ? key[j] : hi;
+      }
+    }
+    for (int64_t c = kSpan + tid; c < n; c += kMemThreads) {
+      const uint32_t kv = orderable_f32(a[c]);
+      lo = kv < lo ? kv : lo;
+      hi = kv > hi ? kv : hi;
+    }
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+      const uint32_t ol = __shfl_xor(lo, o), oh = __shfl_xor(hi, o);
+      lo = ol < lo ? ol : lo;
+      hi = oh > hi ? oh : hi;
+    }
+    if (lane == 0) {
+      s_lohi[0][wave] = lo;
+      s_lohi[1][wave] = hi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kMemWaves; ++w) {
+      lo = s_lohi[0][w] < lo ? s_lohi[0][w] : lo;
+      hi = s_lohi[1][w] > hi ? s_lohi[1][w] : hi;
+    }
+    const int kr = static_cast<int>((n + 1) / 2);
+    uint32_t t = hi;                           // every norm equal: hi is the threshold
+    if (lo != hi) {
+      const int top = 31 - __clz(lo ^ hi);     // highest bit where the norms differ
+      t = hi & ~((2u << top) - 1u);            // the common prefix: every norm is at or above it
+      for (int bit = top, it = 0; bit >= 0; --bit, ++it) {
+        const uint32_t cand = t | (1u << bit);
+        int cnt = 0;                           // wave-uniform: ballot counts
+#pragma unroll
+        for (int j = 0; j < kRegs; ++j) cnt += __popcll(__ballot(key[j] >= cand));
+        for (int64_t c0 = kSpan; c0 < n; c0 += kMemThreads) {
+          const int64_t c = c0 + tid;
+          cnt += __popcll(__ballot(c < n && orderable_f32(a[c < n ? c : n - 1]) >= cand));
+        }
+        if (lane == 0) s_part[it & 1][wave] = cnt;
+        __syncthreads();
+        int tot = 0;
+#pragma unroll
+        for (int w = 0; w < kMemWaves; ++w) tot += s_part[it & 1][w];
+        if (tot >= kr) {
+          t = cand;
+          if (tot == kr) break;
+        }
+      }
+    }
+    // 2. members in cell order
+    int64_t base = 0;
+    for (int64_t s0 = 0; s0 < n; s0 += kSpan) {
+      if (s0 > 0) load_span(s0);
+#pragma unroll
+      for (int j = 0; j < kRegs; ++j) {
+        const int cj = __popcll(__ballot(key[j] >= t));
+        if (lane == 0) s_cnt[j][wave] = cj;
       }
       __syncthreads();
-      prefix |= s_sel[0] << shift;
-      mask |= 255u << shift;
-      kr = s_sel[1];
+      if (wave == 0) {                         // entries (chunk j, wave w) in cell order, four per lane
+        int v[4];
+        int run = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = lane * 4 + r;
+          v[r] = s_cnt[e / kMemWaves][e % kMemWaves];
+          run += v[r];
+        }
+        int incl = run;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int up = __shfl_up(incl, o, kWave);
+          if (lane >= o) incl += up;
+        }
+        int64_t pre = base + incl - run;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = lane * 4 + r;
+          s_wbase[e / kMemWaves][e % kMemWaves] = pre;
+          pre += v[r];
+        }
+        if (lane == kWave - 1) s_tot = incl;
+      }
       __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kRegs; ++j) {
+        const uint64_t mk = __ballot(key[j] >= t);
+        const int64_t wb = s_wbase[j][wave];
+        if (key[j] >= t) mem[wb + lanes_below(mk)] = static_cast<int32_t>(s0 + j * kMemThreads + tid);
+      }
+      base += s_tot;
+      __syncthreads();                         // counts and bases are rewritten next span
     }
-    thr = prefix;
+    m = base;
   }
-  // 2. members in cell order (ordered compaction: a contiguous range per thread)
-  const int64_t per = (n + 255) / 256;
-  const int64_t c0 = tid * per, c1 = c0 + per < n ? c0 + per : n;
-  uint32_t cnt = 0;
-  for (int64_t c = c0; c < c1; ++c) cnt += (f == 0 || orderable_f32(a[c]) >= thr) ? 1u : 0u;
-  s_cnt[tid] = cnt;
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t run = 0;
-    for (int t = 0; t < 256; ++t) {
-      const uint32_t v = s_cnt[t];
-      s_cnt[t] = run;
-      run += v;
-    }
-    s_sel[0] = run;
-  }
-  __syncthreads();
-  const int64_t m = s_sel[0];
-  {
-    int64_t w = s_cnt[tid];
-    for (int64_t c = c0; c < c1; ++c)
-      if (f == 0 || orderable_f32(a[c]) >= thr) mem[w++] = static_cast<int32_t>(c);
-  }
-  for (int64_t x = m + tid; x < n; x += 256) mem[x] = -1;
+  for (int64_t x = m + tid; x < n; x += kMemThreads) mem[x] = -1;
   if (tid == 0) {
     nmem[head * 2 + f] = static_cast<int32_t>(m);
     forest_shape_into(m, &s_sh);
   }
   __syncthreads();
 
-  // 3. node sums, means, max norms and min positions, level by level
+  // node fields come from forest_level1_kernel and forest_level_kernel, radii
+  // from forest_radius_kernel: clear their fp64 maxima here
   const ForestShape& sh = s_sh;
-  for (int l = 0; l < sh.nl; ++l) {
-    const int64_t nn = sh.n[l], off = sh.off[l];
-    const int64_t nchild = l == 0 ? m : sh.n[l - 1];
-    int64_t span = kFan;
-    for (int x = 0; x < l; ++x) span *= kFan;
-    for (int64_t x = tid; x < nn * D; x += 256) {
-      const int64_t j = x / D;
-      const int e = static_cast<int>(x % D);
-      double s = 0.0;
-      for (int64_t y = j * kFan; y < (j + 1) * kFan && y < nchild; ++y)
-        s += l == 0 ? static_cast<double>(ld_f(kb + static_cast<int64_t>(mem[y]) * D + e))
-                    : sm[(sh.off[l - 1] + y) * D + e];
-      sm[(off + j) * D + e] = s;
-      const int64_t cells = (j + 1) * span <= m ? span : m - j * span;
-      mu[(fb + off + j) * D + e] = static_cast<float>(s / static_cast<double>(cells));
-    }
-    for (int64_t j = tid; j < nn; j += 256) {
-      float am = 0.f, pm = INFINITY;
-      for (int64_t y = j * kFan; y < (j + 1) * kFan && y < nchild; ++y) {
-        const float av = l == 0 ? a[mem[y]] : amax[fb + sh.off[l - 1] + y];
-        const float pv = l == 0 ? centre[mem[y]] : pmin[fb + sh.off[l - 1] + y];
-        am = av > am ? av : am;
-        pm = pv < pm ? pv : pm;
-      }
-      amax[fb + off + j] = am;
-      pmin[fb + off + j] = pm;
-    }
-    __syncthreads();
-  }
-  // 4. radii: max distance of the cells below to the node's (fp32) mean
-  for (int l = 0; l < sh.nl; ++l) {
-    const int64_t nn = sh.n[l], off = sh.off[l];
-    int64_t span = kFan;
-    for (int x = 0; x < l; ++x) span *= kFan;
-    if (l == 0) {
-      for (int64_t j = tid; j < nn; j += 256) {
-        const float* mv = mu + (fb + off + j) * D;
-        double best = 0.0;
-        for (int64_t y = j * kFan; y < (j + 1) * kFan && y < m; ++y) {
-          const T* kr = kb + static_cast<int64_t>(mem[y]) * D;
-          double ss = 0.0;
-          for (int e = 0; e < D; ++e) {
-            const double df = static_cast<double>(ld_f(kr + e)) - static_cast<double>(mv[e]);
-            ss += df * df;
-          }
-          best = ss > best ? ss : best;
-        }
-        rad[fb + off + j] = static_cast<float>(sqrt(best));
-      }
-    } else {
-      for (int64_t j = wave; j < nn; j += 4) {
-        const float* mv = mu + (fb + off + j) * D;
-        double best = 0.0;
-        const int64_t y1 = (j + 1) * span < m ? (j + 1) * span : m;
-        for (int64_t y = j * span + lane; y < y1; y += kWave) {
-          const T* kr = kb + static_cast<int64_t>(mem[y]) * D;
-          double ss = 0.0;
-          for (int e = 0; e < D; ++e) {
-            const double df = static_cast<double>(ld_f(kr + e)) - static_cast<double>(mv[e]);
-            ss += df * df;
-          }
-          best = ss > best ? ss : best;
-        }
-        for (int o = 32; o >= 1; o >>= 1) {
-          const double ob = __shfl_xor(best, o);
-          best = ob > best ? ob : best;
-        }
-        if (lane == 0) rad[fb + off + j] = static_cast<float>(sqrt(best));
-      }
-    }
-  }
-  // 5. slots past this forest's nodes (the high-norm forest is smaller)
+  for (int64_t x = tid; x < NN; x += kMemThreads) rbits[fb + x] = 0ull;
+  // slots past this forest's nodes (the high-norm forest is smaller)
   const int64_t used = sh.nl ? sh.off[sh.nl - 1] + sh.n[sh.nl - 1] : 0;
-  for (int64_t x = used * D + tid; x < NN * D; x += 256) mu[fb * D + x] = 0.f;
-  for (int64_t x = used + tid; x < NN; x += 256) {
+  for (int64_t x = used * d + tid; x < NN * d; x += kMemThreads) mu[fb * d + x] = 0.f;
+  for (int64_t x = used + tid; x < NN; x += kMemThreads) {
     rad[fb + x] = 0.f;
     amax[fb + x] = 0.f;
     pmin[fb + x] = 0.f;
   }
 }
 
-// ---------------------------------------------------------------- select
-// Top-16 of the wave's 4 x 64 (score, slot) pairs (slot = i * 64 + lane, ok
-// marks the valid ones) by repeated arg-max, higher score then lower slot;
-// sets taken[] for the kept pairs and returns how many were kept.
-__device__ __forceinline__ int fs_top16(const double (&sc)[4], const bool (&ok)[4], int want, bool (&taken)[4]) {
-  const int lane = threadIdx.x % kWave;
+// Level 1: one wave per node, lanes over the columns: the 16 members' mean
+// keys summed in member order (fp64), the mean, and the max norm / min centre.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void forest_level1_kernel(const T* __restrict__ kbar,
+                                                            const float* __restrict__ max_norm,
+                                                            const float* __restrict__ centre, int64_t ccap, int64_t n,
+                                                            int64_t NN, const int32_t* __restrict__ members,
+                                                            const int32_t* __restrict__ nmem, float* __restrict__ mu,
+                                                            float* __restrict__ amax, float* __restrict__ pmin,
+                                                            double* __restrict__ sums) {
+  constexpr int kCols = D / kWave;             // columns per lane
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int64_t head = blockIdx.y;
+  const int f = blockIdx.z;
+  const int64_t m = nmem[head * 2 + f];
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 4 + wave;   // level-1 node
+  if (m <= kFan || j * kFan >= m) return;      // whole wave leaves
+  const int64_t fb = (head * 2 + f) * NN;
+  const int32_t* mem = members + (head * 2 + f) * n;
+  const int cnt = static_cast<int>(m - j * kFan < kFan ? m - j * kFan : kFan);
+  int32_t cell[kFan];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) taken[i] = false;
+  for (int t = 0; t < kFan; ++t) cell[t] = mem[j * kFan + (t < cnt ? t : cnt - 1)];
+  double sacc[kCols];
+#pragma unroll
+  for (int u = 0; u < kCols; ++u) sacc[u] = 0.0;
+  float vals[kFan][kCols];
+#pragma unroll
+  for (int t = 0; t < kFan; ++t)
+#pragma unroll
+    for (int u = 0; u < kCols; ++u) vals[t][u] = ld_f(kbar + (head * ccap + cell[t]) * D + u * kWave + lane);
+#pragma unroll
+  for (int t = 0; t < kFan; ++t)
+#pragma unroll
+    for (int u = 0; u < kCols; ++u)
+      if (t < cnt) sacc[u] += static_cast<double>(vals[t][u]);
+#pragma unroll
+  for (int u = 0; u < kCols; ++u) {
+    const int e = u * kWave + lane;
+    sums[(fb + j) * D + e] = sacc[u];
+    mu[(fb + j) * D + e] = static_cast<float>(sacc[u] / static_cast<double>(cnt));
+  }
+  // max norm and min centre of the members (lanes 0..15 one member each)
+  float am = 0.f, pm = INFINITY;
+  if (lane < cnt) {
+    const int32_t c = mem[j * kFan + lane];
+    am = max_norm[head * ccap + c];
+    pm = centre[c];
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) {
+    const float oa = __shfl_xor(am, o), op = __shfl_xor(pm, o);
+    am = oa > am ? oa : am;
+    pm = op < pm ? op : pm;
+  }
+  if (lane == 0) {
+    amax[fb + j] = am;
+    pmin[fb + j] = pm;
+  }
+}
+
+// Level l + 1 (l >= 1), one launch per level: a wave per node, lanes over
+// the columns, the 16 children's fp64 sums loaded together and added in order.
+template <int D>
+__global__ __launch_bounds__(256) void forest_level_kernel(int l, int64_t NN, const int32_t* __restrict__ nmem,
+                                                           float* __restrict__ mu, float* __restrict__ amax,
+                                                           float* __restrict__ pmin, double* __restrict__ sums) {
+  constexpr int kCols = D / kWave;
+  __shared__ ForestShape s_sh;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int64_t head = blockIdx.y;
+  const int f = blockIdx.z;
+  const int64_t m = nmem[head * 2 + f];
+  if (tid == 0) forest_shape_into(m, &s_sh);
+  __syncthreads();
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (l >= s_sh.nl || j >= s_sh.n[l]) return;  // whole wave leaves
+  const int64_t fb = (head * 2 + f) * NN;
+  const int64_t off = s_sh.off[l], poff = s_sh.off[l - 1], nprev = s_sh.n[l - 1];
+  int64_t span = kFan;
+  for (int x = 0; x < l; ++x) span *= kFan;     // cells under a node of this level
+  const int cnt = static_cast<int>(nprev - j * kFan < kFan ? nprev - j * kFan : kFan);
+  double v[kFan][kCols];
+#pragma unroll
+  for (int t = 0; t < kFan; ++t) {
+    const int64_t y = j * kFan + (t < cnt ? t : cnt - 1);
+#pragma unroll
+    for (int u = 0; u < kCols; ++u) v[t][u] = sums[(fb + poff + y) * D + u * kWave + lane];
+  }
+  double sacc[kCols];
+#pragma unroll
+  for (int u = 0; u < kCols; ++u) sacc[u] = 0.0;
+#pragma unroll
+  for (int t = 0; t < kFan; ++t)
+#pragma unroll
+    for (int u = 0; u < kCols; ++u)
+      if (t < cnt) sacc[u] += v[t][u];
+  const int64_t cells = (j + 1) * span <= m ? span : m - j * span;
+#pragma unroll
+  for (int u = 0; u < kCols; ++u) {
+    const int e = u * kWave + lane;
+    sums[(fb + off + j) * D + e] = sacc[u];
+    mu[(fb + off + j) * D + e] = static_cast<float>(sacc[u] / static_cast<double>(cells));
+  }
+  float am = 0.f, pm = INFINITY;
+  if (lane < cnt) {
+    am = amax[fb + poff + j * kFan + lane];
+    pm = pmin[fb + poff + j * kFan + lane];
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) {
+    const float oa = __shfl_xor(am, o), op = __shfl_xor(pm, o);
+    am = oa > am ? oa : am;
+    pm = op < pm ? op : pm;
+  }
+  if (lane == 0) {
+    amax[fb + off + j] = am;
+    pmin[fb + off + j] = pm;
+  }
+}
+
+// Radii: one thread per member cell computes its fp64 squared distance to the
+// mean of every node above it and folds it into that node's maximum (the bit
+// patterns of non-negative doubles order as unsigned integers, so an integer
+// atomic max is exact and order-independent).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void forest_radius_kernel(const T* __restrict__ kbar, int64_t ccap, int64_t n,
+                                                            int64_t NN, const int32_t* __restrict__ members,
+                                                            const int32_t* __restrict__ nmem,
+                                                            const float* __restrict__ mu,
+                                                            unsigned long long* __restrict__ rbits) {
+  constexpr int kVec = Elem<T>::kVec;
+  __shared__ ForestShape s_sh;
+  __shared__ double s_red[4];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int64_t head = blockIdx.y;
+  const int f = blockIdx.z;
+  const int64_t m = nmem[head * 2 + f];
+  if (tid == 0) forest_shape_into(m, &s_sh);
+  __syncthreads();
+  const int64_t x0 = static_cast<int64_t>(blockIdx.x) * 256;
+  if (x0 >= m || s_sh.nl == 0) return;         // whole workgroup leaves
+  const int64_t x = x0 + tid;
+  const bool in = x < m;                       // threads past the members take part with 0
+  const int64_t fb = (head * 2 + f) * NN;
+  float kv[D];
+  {
+    const int64_t c = members[(head * 2 + f) * n + (in ? x : m - 1)];
+    const T* kr = kbar + (head * ccap + c) * D;
+#pragma unroll
+    for (int v = 0; v < D / kVec; ++v) {
+      float t[kVec];
+      Elem<T>::unpack(*reinterpret_cast<const uint4*>(kr + v * kVec), t);
+#pragma unroll
+      for (int u = 0; u < kVec; ++u) kv[v * kVec + u] = t[u];
+    }
+  }
+  int64_t span = kFan;
+  for (int l = 0; l < s_sh.nl; ++l, span *= kFan) {
+    const int64_t node = fb + s_sh.off[l] + (in ? x : m - 1) / span;
+    const float4* mv = reinterpret_cast<const float4*>(mu + node * D);
+    double ss = 0.0;
+#pragma unroll
+    for (int v = 0; v < D / 4; ++v) {
+      const float4 w = mv[v];
+      double df = static_cast<double>(kv[4 * v]) - static_cast<double>(w.x);
+      ss += df * df;
+      df = static_cast<double>(kv[4 * v + 1]) - static_cast<double>(w.y);
+      ss += df * df;
+      df = static_cast<double>(kv[4 * v + 2]) - static_cast<double>(w.z);
+      ss += df * df;
+      df = static_cast<double>(kv[4 * v + 3]) - static_cast<double>(w.w);
+      ss += df * df;
+    }
+    if (!in) ss = 0.0;
+    if (span == kFan) {
+      // a level-1 node is 16 consecutive lanes
+#pragma unroll
+      for (int o = kFan / 2; o >= 1; o >>= 1) {
+        const double os = __shfl_xor(ss, o);
+        ss = os > ss ? os : ss;
+      }
+      if (in && (x % kFan) == 0) atomicMax(&rbits[node], static_cast<unsigned long long>(__double_as_longlong(ss)));
+    } else {
+      // nodes above span whole workgroups (256 members each)
+#pragma unroll
+      for (int o = kWave / 2; o >= 1; o >>= 1) {
+        const double os = __shfl_xor(ss, o);
+        ss = os > ss ? os : ss;
+      }
+      if (lane == 0) s_red[wave] = ss;
+      __syncthreads();
+      if (tid == 0) {
+        double bm = s_red[0];
+        for (int w = 1; w < 4; ++w) bm = s_red[w] > bm ? s_red[w] : bm;
+        atomicMax(&rbits[fb + s_sh.off[l] + x0 / span], static_cast<unsigned long long>(__double_as_longlong(bm)));
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void forest_radius_final_kernel(const unsigned long long* __restrict__ rbits,
+                                                                  int64_t total, float* __restrict__ rad) {
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (x < total) rad[x] = static_cast<float>(sqrt(__longlong_as_double(static_cast<long long>(rbits[x]))));
+}
+
+// ---------------------------------------------------------------- select
+__device__ __forceinline__ uint64_t fs_orderable(double v) {
+  if (v == 0.0) v = 0.0;                       // +0 and -0 compare equal
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// Top `want` of the wave's 4 x 64 (score, slot) pairs (slot = i * 64 + lane,
+// ok marks the valid ones), higher score first, lower slot on ties: a bitwise
+// search for the threshold over the scores' orderable bits below the common
+// prefix of the smallest and largest (ballot counts, stopping once the kept
+// set is decided), then every pair above it and the first ones equal to it in
+// slot order.  Sets taken[], returns how many.
+__device__ __forceinline__ int fs_top16(const double (&sc)[4], const bool (&ok)[4], int want, bool (&taken)[4]) {
+  uint64_t key[4];
   int nv = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) nv += __popcll(__ballot(ok[i]));
+  for (int i = 0; i < 4; ++i) {
+    key[i] = ok[i] ? fs_orderable(sc[i]) : 0ull;
+    nv += __popcll(__ballot(ok[i]));
+  }
   const int kk = nv < want ? nv : want;
-  for (int t = 0; t < kk; ++t) {
-    double bv = -INFINITY;
-    int bj = 1 << 30;
+  uint64_t t = ~0ull;
+  if (kk > 0) {
+    // every valid key shares the common prefix of the smallest and largest
+    uint64_t lo = ~0ull, hi = 0ull;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int j = i * kWave + lane;
-      if (ok[i] && !taken[i] && (sc[i] > bv || (sc[i] == bv && j < bj))) {
-        bv = sc[i];
-        bj = j;
-      }
-    }
-    for (int o = 32; o >= 1; o >>= 1) {
-      const double ov = __shfl_xor(bv, o);
-      const int oj = __shfl_xor(bj, o);
-      if (ov > bv || (ov == bv && oj < bj)) {
-        bv = ov;
-        bj = oj;
+      if (ok[i]) {
+        lo = key[i] < lo ? key[i] : lo;
+        hi = key[i] > hi ? key[i] : hi;
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i * kWave + lane == bj) taken[i] = true;
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+      const uint64_t ol = __shfl_xor(lo, o), oh = __shfl_xor(hi, o);
+      lo = ol < lo ? ol : lo;
+      hi = oh > hi ? oh : hi;
+    }
+    const int top = lo == hi ? -1 : 63 - __clzll(static_cast<long long>(lo ^ hi));
+    t = top < 0 ? hi : (hi & ~((2ull << top) - 1ull));
+    for (int bit = top; bit >= 0; --bit) {
+      const uint64_t cand = t | (1ull << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+      if (cnt >= kk) {
+        t = cand;
+        if (cnt == kk) break;
+      }
+    }
+  }
+  int ngt = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ngt += __popcll(__ballot(key[i] > t));
+  const int need = kk - ngt;
+  int eq_seen = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint64_t eq = __ballot(key[i] == t && key[i] != 0ull);
+    taken[i] = key[i] > t || (key[i] == t && key[i] != 0ull && eq_seen + lanes_below(eq) < need);
+    eq_seen += __popcll(eq);
   }
   return kk;
 }
 
+// One workgroup per (batch, selection head, query row): each half runs one
+// forest's beam search (its 128 threads score the up to 256 candidates of a
+// level, one wave keeps the best 16), the four waves share the re-rank (cells
+// of the reached set taken four ways), wave 0 takes the final top K.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void forest_select_kernel(
     const T* __restrict__ q, const T* __restrict__ kbar, const float* __restrict__ max_norm,
@@ -282,18 +542,23 @@ __global__ __launch_bounds__(256) void forest_select_kernel(
     const float* __restrict__ mu, const float* __restrict__ rad, const float* __restrict__ amax,
     const float* __restrict__ pmin, int64_t n, int64_t NN, int K, int32_t* __restrict__ idx,
     int32_t* __restrict__ k_eff) {
-  __shared__ double s_q[4][D];
-  __shared__ int64_t s_front[4][kBeam];
-  __shared__ int32_t s_reach[4][2 * kBeam];
-  __shared__ double s_lse[4][2 * kBeam];
-  __shared__ ForestShape s_sh[4];              // in LDS: its arrays are indexed by loop variables
+  constexpr int kVec = Elem<T>::kVec;
+  __shared__ double s_q[D];
+  __shared__ double s_qn;
+  __shared__ int64_t s_front[2][kBeam];
+  __shared__ int s_nf[2];
+  __shared__ double s_sc[2][256];
+  __shared__ int64_t s_cid[2][256];
+  __shared__ int32_t s_reach[2 * kBeam];
+  __shared__ int s_nreach;
+  __shared__ double s_lse[2 * kBeam];
+  __shared__ ForestShape s_sh[2];              // in LDS: its arrays are indexed by loop variables
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int bh = blockIdx.y;
   const int bi = bh / Hsel, hs = bh % Hsel;
   const int G = Hq / Hkv;
   const int kvh = share_group ? hs : hs / G;
-  const int row = blockIdx.x * 4 + wave;
-  if (row >= nq) return;                       // whole wave leaves; no workgroup barrier below
+  const int row = blockIdx.x;
   const int64_t head = static_cast<int64_t>(bi) * Hkv + kvh;
   const double pos = static_cast<double>(q_pos0 + row);
   const double isd = 1.0 / sqrt(static_cast<double>(D));
@@ -302,146 +567,225 @@ __global__ __launch_bounds__(256) void forest_select_kernel(
   const double sig = erf_on ? static_cast<double>(erf_sigma[hs]) : 1.0;
 
   // q_hat (fp64) and its norm
-  const int gq = share_group ? G : 1;
-  const int h0 = share_group ? hs * G : hs;
-  double qq = 0.0;
-  for (int e = lane; e < D; e += kWave) {
-    double s = 0.0;
-    for (int g = 0; g < gq; ++g)
-      s += static_cast<double>(ld_f(q + ((static_cast<int64_t>(bi) * Hq + h0 + g) * nq + row) * D + e));
-    s /= static_cast<double>(gq);
-    s_q[wave][e] = s;
-    qq += s * s;
+  if (wave == 0) {
+    const int gq = share_group ? G : 1;
+    const int h0 = share_group ? hs * G : hs;
+    double qq = 0.0;
+    for (int e = lane; e < D; e += kWave) {
+      double sq = 0.0;
+      for (int g = 0; g < gq; ++g)
+        sq += static_cast<double>(ld_f(q + ((static_cast<int64_t>(bi) * Hq + h0 + g) * nq + row) * D + e));
+      sq /= static_cast<double>(gq);
+      s_q[e] = sq;
+      qq += sq * sq;
+    }
+    for (int o = 32; o >= 1; o >>= 1) qq += __shfl_xor(qq, o);
+    if (lane == 0) s_qn = sqrt(qq);
   }
-  for (int o = 32; o >= 1; o >>= 1) qq += __shfl_xor(qq, o);
-  const double qn = sqrt(qq);
-  wave_lds_sync();
+  __syncthreads();
 
-  int nreach = 0;
-  for (int f = 0; f < 2; ++f) {
-    const int64_t m = nmem[head * 2 + f];
-    const int32_t* mem = members + (head * 2 + f) * n;
-    const int64_t fb = (head * 2 + f) * NN;
-    if (lane == 0) forest_shape_into(m, &s_sh[wave]);
-    wave_lds_sync();
-    const ForestShape& sh = s_sh[wave];
-    int nf = static_cast<int>(sh.nl ? sh.n[sh.nl - 1] : m);
-    if (lane < nf) s_front[wave][lane] = lane;
-    wave_lds_sync();
-    int lev = sh.nl;
-    bool first = true;
-    for (;;) {
-      // candidates: the frontier itself for a forest of cells only, else its children
-      const bool own = first && sh.nl == 0;
-      const int child_lev = own ? 0 : lev - 1;
-      const int64_t nchild = child_lev == 0 ? m : sh.n[child_lev - 1];
+  // both forests at once: threads [128 f, 128 f + 128) score forest f's
+  // candidates (two each), wave 2 f keeps its beam
+  const double qn = s_qn;
+  const int f = tid / 128, ht = tid % 128;
+  const int64_t m = nmem[head * 2 + f];
+  const int32_t* mem = members + (head * 2 + f) * n;
+  const int64_t fb = (head * 2 + f) * NN;
+  if (ht == 0) {
+    forest_shape_into(m, &s_sh[f]);
+    s_nf[f] = static_cast<int>(s_sh[f].nl ? s_sh[f].n[s_sh[f].nl - 1] : m);
+  }
+  __syncthreads();
+  const ForestShape& sh = s_sh[f];
+  if (ht < s_nf[f]) s_front[f][ht] = ht;
+  // rounds: one per level below the top, one for a forest of cells only; the
+  // whole-prefix forest has the most
+  const int rounds = s_sh[0].nl ? s_sh[0].nl : 1;
+  const int my_rounds = sh.nl ? sh.nl : 1;
+  for (int r = 0; r < rounds; ++r) {
+    __syncthreads();                           // frontier written
+    const bool active = r < my_rounds;
+    const int nf = s_nf[f];
+    const bool own = sh.nl == 0;               // a forest of cells only: score the frontier itself
+    const int child_lev = (own || !active) ? 0 : sh.nl - 1 - r;
+    const int64_t nchild = child_lev == 0 ? m : sh.n[child_lev - 1];
+    // candidate slots x = ht and 128 + ht (ascending id with x); all loads of
+    // both are issued before any arithmetic, from clamped (valid) addresses
+    int64_t cid[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int x = i * 128 + ht;
+      cid[i] = -1;
+      if (!active) {
+      } else if (own) {
+        cid[i] = x < nf ? s_front[f][x] : -1;
+      } else if (x / kFan < nf) {
+        const int64_t ch = s_front[f][x / kFan] * kFan + (x % kFan);
+        cid[i] = ch < nchild ? ch : -1;
+      }
+    }
+    double sv[2] = {0.0, 0.0};
+    if (child_lev == 0) {
+      int64_t c[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) c[i] = mem[cid[i] >= 0 ? cid[i] : 0];
+      uint4 raw[2][D / kVec];
+      float an[2], pc[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint4* kr = reinterpret_cast<const uint4*>(kbar + (head * ccap + c[i]) * D);
+#pragma unroll
+        for (int v = 0; v < D / kVec; ++v) raw[i][v] = kr[v];
+        an[i] = max_norm[head * ccap + c[i]];
+        pc[i] = centre[c[i]];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        double dot = 0.0;
+#pragma unroll
+        for (int v = 0; v < D / kVec; ++v) {
+          float t[kVec];
+          Elem<T>::unpack(raw[i][v], t);
+#pragma unroll
+          for (int u = 0; u < kVec; ++u) dot = fma(s_q[v * kVec + u], static_cast<double>(t[u]), dot);
+        }
+        sv[i] = dot * isd;
+        if (erf_on)
+          sv[i] += lam * static_cast<double>(an[i]) * erf((pos - static_cast<double>(pc[i])) / (2.0 * sig));
+      }
+    } else {
+      const int64_t lbase = fb + sh.off[child_lev - 1];
+      float4 w[2][D / 4];
+      float rn[2], an[2], pn[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int64_t node = lbase + (cid[i] >= 0 ? cid[i] : 0);
+        const float4* mv = reinterpret_cast<const float4*>(mu + node * D);
+#pragma unroll
+        for (int v = 0; v < D / 4; ++v) w[i][v] = mv[v];
+        rn[i] = rad[node];
+        an[i] = amax[node];
+        pn[i] = pmin[node];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        double dot = 0.0;
+#pragma unroll
+        for (int v = 0; v < D / 4; ++v) {
+          dot = fma(s_q[4 * v], static_cast<double>(w[i][v].x), dot);
+          dot = fma(s_q[4 * v + 1], static_cast<double>(w[i][v].y), dot);
+          dot = fma(s_q[4 * v + 2], static_cast<double>(w[i][v].z), dot);
+          dot = fma(s_q[4 * v + 3], static_cast<double>(w[i][v].w), dot);
+        }
+        sv[i] = dot * isd + qn * static_cast<double>(rn[i]) * isd;
+        if (erf_on)
+          sv[i] += lam * static_cast<double>(an[i]) * erf((pos - static_cast<double>(pn[i])) / (2.0 * sig));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      s_sc[f][i * 128 + ht] = sv[i];
+      s_cid[f][i * 128 + ht] = cid[i];
+    }
+    __syncthreads();                           // scores written, frontier read
+    if (active && (wave & 1) == 0) {
       double sc[4];
-      bool ok[4];
+      bool ok[4], taken[4];
       int64_t id[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int x = i * kWave + lane;
-        int64_t cid = -1;
-        if (own) {
-          cid = x < nf ? s_front[wave][x] : -1;
-        } else if (x / kFan < nf) {
-          const int64_t ch = s_front[wave][x / kFan] * kFan + (x % kFan);
-          cid = ch < nchild ? ch : -1;
-        }
-        ok[i] = cid >= 0;
-        id[i] = cid;
-        double s = -INFINITY;
-        if (ok[i]) {
-          double dot = 0.0;
-          if (child_lev == 0) {
-            const int64_t c = mem[cid];
-            const T* kr = kbar + (head * ccap + c) * D;
-            for (int e = 0; e < D; ++e) dot = fma(s_q[wave][e], static_cast<double>(ld_f(kr + e)), dot);
-            s = dot * isd;
-            if (erf_on)
-              s += lam * static_cast<double>(max_norm[head * ccap + c]) *
-                   erf((pos - static_cast<double>(centre[c])) / (2.0 * sig));
-          } else {
-            const int64_t node = fb + sh.off[child_lev - 1] + cid;
-            const float* mv = mu + node * D;
-            for (int e = 0; e < D; ++e) dot = fma(s_q[wave][e], static_cast<double>(mv[e]), dot);
-            s = dot * isd + qn * static_cast<double>(rad[node]) * isd;
-            if (erf_on)
-              s += lam * static_cast<double>(amax[node]) * erf((pos - static_cast<double>(pmin[node])) / (2.0 * sig));
-          }
-        }
-        sc[i] = s;
+        id[i] = s_cid[f][i * kWave + lane];
+        ok[i] = id[i] >= 0;
+        sc[i] = s_sc[f][i * kWave + lane];
       }
-      bool taken[4];
       fs_top16(sc, ok, kBeam, taken);
-      wave_lds_sync();
       // new frontier in candidate (ascending id) order
       int kept = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint64_t tm = __ballot(taken[i]);
-        if (taken[i]) s_front[wave][kept + lanes_below(tm)] = id[i];
+        if (taken[i]) s_front[f][kept + lanes_below(tm)] = id[i];
         kept += __popcll(tm);
       }
-      wave_lds_sync();
-      nf = kept;
-      first = false;
-      if (child_lev == 0) break;
-      lev = child_lev;
+      if (lane == 0) s_nf[f] = kept;
     }
-    // reached cells of this forest, skipping those the first forest reached
-    const int base = nreach;
-    bool add = false;
-    int32_t cell = -1;
-    if (lane < nf) {
-      cell = mem[s_front[wave][lane]];
-      add = true;
-      for (int y = 0; y < base; ++y)
-        if (s_reach[wave][y] == cell) add = false;
-    }
+  }
+  __syncthreads();                             // last frontiers written
+  if (wave == 0) {
+    // reached cells: the whole-prefix forest's, then the other's not yet there
+    const int nf0 = s_nf[0], nf1 = s_nf[1];
+    const int32_t cell0 = members[(head * 2) * n + s_front[0][lane < nf0 ? lane : 0]];
+    const int32_t cell1 = members[(head * 2 + 1) * n + s_front[1][lane < nf1 ? lane : 0]];
+    bool add = lane < nf1;
+    for (int y = 0; y < nf0; ++y)
+      if (__shfl(cell0, y) == cell1) add = false;
+    if (lane < nf0) s_reach[lane] = cell0;
     const uint64_t am = __ballot(add);
-    if (add) s_reach[wave][base + lanes_below(am)] = cell;
-    nreach = base + __popcll(am);
+    if (add) s_reach[nf0 + lanes_below(am)] = cell1;
+    if (lane == 0) s_nreach = nf0 + __popcll(am);
     wave_lds_sync();
   }
-
-  // re-rank: logsumexp of each reached cell's token scores; the cells in
-  // ascending order first (ties then go to the lower cell)
-  int32_t my = lane < nreach ? s_reach[wave][lane] : 0x7fffffff;
-  int rank = 0;
-  for (int y = 0; y < nreach; ++y) rank += s_reach[wave][y] < my ? 1 : 0;
-  wave_lds_sync();
-  if (lane < nreach) s_reach[wave][rank] = my;
-  wave_lds_sync();
-  const int per = kWave / b;                   // cells per pass (b <= 64)
-  const int grp = lane / b, tok = lane % b;
-  for (int c0 = 0; c0 < nreach; c0 += per) {
-    const int x = c0 + grp;
-    double z = -INFINITY;
-    if (x < nreach) {
-      const int64_t c = s_reach[wave][x];
-      const T* kr = kcache + (head * L + c * b + tok) * D;
-      double dot = 0.0;
-      for (int e = 0; e < D; ++e) dot = fma(s_q[wave][e], static_cast<double>(ld_f(kr + e)), dot);
-      z = dot * isd;
-    }
-    double mx = z;
-    for (int o = b / 2; o >= 1; o >>= 1) {
-      const double ov = __shfl_xor(mx, o);
-      mx = ov > mx ? ov : mx;
-    }
-    double sexp = x < nreach ? exp(z - mx) : 0.0;
-    for (int o = b / 2; o >= 1; o >>= 1) sexp += __shfl_xor(sexp, o);
-    if (x < nreach && tok == 0) s_lse[wave][x] = mx + log(sexp);
+  if (wave == 0) {
+    const int nreach = s_nreach;
+    // ascending cell order (ties in the re-rank then go to the lower cell)
+    const int32_t my = lane < nreach ? s_reach[lane] : 0x7fffffff;
+    int rank = 0;
+    for (int y = 0; y < nreach; ++y) rank += s_reach[y] < my ? 1 : 0;
+    wave_lds_sync();
+    if (lane < nreach) s_reach[rank] = my;
+    if (lane == 0) s_nreach = nreach;
   }
-  wave_lds_sync();
+  __syncthreads();
+
+  // re-rank: logsumexp of each reached cell's token scores; token rows x =
+  // cell slot * b + token spread over the workgroup, kRows per thread loaded
+  // together (clamped to a valid row), a cell's b rows in b adjacent lanes
+  const int nreach = s_nreach;
+  constexpr int kRowBytes = D * static_cast<int>(sizeof(T));
+  constexpr int kRows = kRowBytes <= 128 ? 4 : (kRowBytes <= 256 ? 2 : 1);
+  const int rows = nreach * b;
+  for (int x0 = 0; x0 < rows; x0 += 256 * kRows) {
+    uint4 raw[kRows][D / kVec];
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      const int x = x0 + k * 256 + tid;
+      const int xc = x < rows ? x : rows - 1;
+      const int64_t c = s_reach[xc / b];
+      const uint4* kr = reinterpret_cast<const uint4*>(kcache + (head * L + c * b + xc % b) * D);
+#pragma unroll
+      for (int v = 0; v < D / kVec; ++v) raw[k][v] = kr[v];
+    }
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      const int x = x0 + k * 256 + tid;        // a cell's b rows are all valid or all not
+      double dot = 0.0;
+#pragma unroll
+      for (int v = 0; v < D / kVec; ++v) {
+        float t[kVec];
+        Elem<T>::unpack(raw[k][v], t);
+#pragma unroll
+        for (int u = 0; u < kVec; ++u) dot = fma(s_q[v * kVec + u], static_cast<double>(t[u]), dot);
+      }
+      const double z = dot * isd;
+      double mx = z;
+      for (int o = b / 2; o >= 1; o >>= 1) {
+        const double ov = __shfl_xor(mx, o);
+        mx = ov > mx ? ov : mx;
+      }
+      double sexp = exp(z - mx);
+      for (int o = b / 2; o >= 1; o >>= 1) sexp += __shfl_xor(sexp, o);
+      if (x < rows && x % b == 0) s_lse[x / b] = mx + log(sexp);
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
   double sc[4];
   bool ok[4], taken[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int x = i * kWave + lane;
     ok[i] = x < nreach;
-    sc[i] = ok[i] ? s_lse[wave][x] : -INFINITY;
+    sc[i] = ok[i] ? s_lse[x] : -INFINITY;
   }
   const int kk = fs_top16(sc, ok, K, taken);
   const int64_t o = (static_cast<int64_t>(bh) * nq + row) * K;
@@ -449,7 +793,7 @@ __global__ __launch_bounds__(256) void forest_select_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint64_t tm = __ballot(taken[i]);
-    if (taken[i]) idx[o + kept + lanes_below(tm)] = s_reach[wave][i * kWave + lane];
+    if (taken[i]) idx[o + kept + lanes_below(tm)] = s_reach[i * kWave + lane];
     kept += __popcll(tm);
   }
   for (int x = kept + lane; x < K; x += kWave) idx[o + x] = -1;
@@ -457,15 +801,41 @@ __global__ __launch_bounds__(256) void forest_select_kernel(
 }
 
 // ---------------------------------------------------------------- launch
+// fp64 node sums, then the radii's fp64 squared maxima (as bits)
 size_t forest_workspace_bytes(int B, int Hkv, int d, int64_t n) {
-  return align256(static_cast<size_t>(B) * Hkv * 2 * static_cast<size_t>(forest_nodes(n)) * d * sizeof(double));
+  const size_t nodes = static_cast<size_t>(B) * Hkv * 2 * static_cast<size_t>(forest_nodes(n));
+  return align256(nodes * d * sizeof(double)) + align256(nodes * sizeof(unsigned long long));
 }
 
 template <typename T, int D>
 static hipError_t launch_build_t(const ForestLaunch& p, hipStream_t st) {
-  return launch(true, forest_build_kernel<T, D>, dim3(static_cast<unsigned>(p.B * p.Hkv), 2), dim3(256), st,
-                static_cast<const T*>(p.kbar), p.max_norm, p.centre, p.ccap, p.n, forest_nodes(p.n), p.members,
-                p.nmem, p.mu, p.rad, p.amax, p.pmin, static_cast<double*>(p.ws));
+  const int64_t NN = forest_nodes(p.n);
+  const size_t nodes = static_cast<size_t>(p.B) * p.Hkv * 2 * static_cast<size_t>(NN);
+  double* sums = static_cast<double*>(p.ws);
+  unsigned long long* rbits =
+      reinterpret_cast<unsigned long long*>(static_cast<char*>(p.ws) + align256(nodes * p.d * sizeof(double)));
+  const unsigned heads = static_cast<unsigned>(p.B * p.Hkv);
+  hipError_t e = launch(false, forest_members_kernel, dim3(heads, 2), dim3(kMemThreads), st, p.max_norm, p.ccap, p.n, NN,
+                        p.d, p.members, p.nmem, p.mu, p.rad, p.amax, p.pmin, rbits);
+  if (e != hipSuccess || NN == 0) return e;
+  const ForestShape sh = forest_shape(p.n);    // the whole-prefix forest has the most levels
+  e = launch(false, forest_level1_kernel<T, D>, dim3(static_cast<unsigned>((sh.n[0] + 3) / 4), heads, 2), dim3(256),
+             st, static_cast<const T*>(p.kbar), p.max_norm, p.centre, p.ccap, p.n, NN,
+             static_cast<const int32_t*>(p.members), static_cast<const int32_t*>(p.nmem), p.mu, p.amax, p.pmin, sums);
+  if (e != hipSuccess) return e;
+  for (int l = 1; l < sh.nl; ++l) {
+    e = launch(false, forest_level_kernel<D>, dim3(static_cast<unsigned>((sh.n[l] + 3) / 4), heads, 2), dim3(256),
+               st, l, NN, static_cast<const int32_t*>(p.nmem), p.mu, p.amax, p.pmin, sums);
+    if (e != hipSuccess) return e;
+  }
+  e = launch(false, forest_radius_kernel<T, D>,
+             dim3(static_cast<unsigned>((p.n + 255) / 256), static_cast<unsigned>(p.B * p.Hkv), 2), dim3(256), st,
+             static_cast<const T*>(p.kbar), p.ccap, p.n, NN, static_cast<const int32_t*>(p.members),
+             static_cast<const int32_t*>(p.nmem), static_cast<const float*>(p.mu), rbits);
+  if (e != hipSuccess) return e;
+  const int64_t total = static_cast<int64_t>(nodes);
+  return launch(true, forest_radius_final_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), st,
+                static_cast<const unsigned long long*>(rbits), total, p.rad);
 }
 
 hipError_t launch_forest_build(const ForestLaunch& p, hipStream_t st) {
@@ -476,7 +846,7 @@ hipError_t launch_forest_build(const ForestLaunch& p, hipStream_t st) {
 template <typename T, int D>
 static hipError_t launch_fsel_t(const SelectLaunch& s, const ForestLaunch& p, const void* k, int64_t L,
                                 hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((s.nq + 3) / 4), static_cast<unsigned>(s.B * s.Hsel));
+  const dim3 grid(static_cast<unsigned>(s.nq), static_cast<unsigned>(s.B * s.Hsel));
   return launch(true, forest_select_kernel<T, D>, grid, dim3(256), st, static_cast<const T*>(s.q),
                 static_cast<const T*>(s.kbar), s.max_norm, s.centre, static_cast<const T*>(k), L, s.Hq, s.Hkv, s.Hsel,
                 s.share_group, s.nq, s.q_pos0, s.ccap, s.b, s.erf_lambda, s.erf_sigma,
