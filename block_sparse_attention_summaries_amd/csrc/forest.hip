@@ -737,45 +737,64 @@ __global__ __launch_bounds__(256) void forest_select_kernel(
   }
   __syncthreads();
 
-  // re-rank: logsumexp of each reached cell's token scores; token rows x =
-  // cell slot * b + token spread over the workgroup, kRows per thread loaded
-  // together (clamped to a valid row), a cell's b rows in b adjacent lanes
+  // re-rank: logsumexp of each reached cell's token scores.  Eight adjacent
+  // lanes per cell (32 cells, the most two beams reach, in one pass), lane g
+  // of a cell taking tokens g, g + 8, ...; rows loaded kRows at a time from
+  // clamped (valid) addresses, the scores kept, then a max and a sum over the
+  // cell's lanes.
   const int nreach = s_nreach;
+  constexpr int kLanesPerCell = 8;
+  constexpr int kMaxTok = 64 / kLanesPerCell;  // tokens per lane for b = 64
+  static_assert(256 / kLanesPerCell >= 2 * kBeam, "one pass covers every reached cell");
   constexpr int kRowBytes = D * static_cast<int>(sizeof(T));
   constexpr int kRows = kRowBytes <= 128 ? 4 : (kRowBytes <= 256 ? 2 : 1);
-  const int rows = nreach * b;
-  for (int x0 = 0; x0 < rows; x0 += 256 * kRows) {
-    uint4 raw[kRows][D / kVec];
+  {
+    const int cs = tid / kLanesPerCell, g = tid % kLanesPerCell;
+    const int tpl = b / kLanesPerCell;         // tokens per lane
+    const int64_t c = s_reach[cs < nreach ? cs : nreach - 1];
+    const T* kc = kcache + (head * L + c * b) * D;
+    double z[kMaxTok];
 #pragma unroll
-    for (int k = 0; k < kRows; ++k) {
-      const int x = x0 + k * 256 + tid;
-      const int xc = x < rows ? x : rows - 1;
-      const int64_t c = s_reach[xc / b];
-      const uint4* kr = reinterpret_cast<const uint4*>(kcache + (head * L + c * b + xc % b) * D);
+    for (int k0 = 0; k0 < kMaxTok; k0 += kRows) {
+      if (k0 < tpl) {
+        uint4 raw[kRows][D / kVec];
 #pragma unroll
-      for (int v = 0; v < D / kVec; ++v) raw[k][v] = kr[v];
-    }
+        for (int r = 0; r < kRows; ++r) {
+          const int k = k0 + r < tpl ? k0 + r : tpl - 1;
+          const uint4* kr = reinterpret_cast<const uint4*>(kc + static_cast<int64_t>(g + kLanesPerCell * k) * D);
 #pragma unroll
-    for (int k = 0; k < kRows; ++k) {
-      const int x = x0 + k * 256 + tid;        // a cell's b rows are all valid or all not
-      double dot = 0.0;
+          for (int v = 0; v < D / kVec; ++v) raw[r][v] = kr[v];
+        }
 #pragma unroll
-      for (int v = 0; v < D / kVec; ++v) {
-        float t[kVec];
-        Elem<T>::unpack(raw[k][v], t);
+        for (int r = 0; r < kRows; ++r) {
+          double dot = 0.0;
 #pragma unroll
-        for (int u = 0; u < kVec; ++u) dot = fma(s_q[v * kVec + u], static_cast<double>(t[u]), dot);
+          for (int v = 0; v < D / kVec; ++v) {
+            float t[kVec];
+            Elem<T>::unpack(raw[r][v], t);
+#pragma unroll
+            for (int u = 0; u < kVec; ++u) dot = fma(s_q[v * kVec + u], static_cast<double>(t[u]), dot);
+          }
+          z[k0 + r] = dot * isd;
+        }
       }
-      const double z = dot * isd;
-      double mx = z;
-      for (int o = b / 2; o >= 1; o >>= 1) {
-        const double ov = __shfl_xor(mx, o);
-        mx = ov > mx ? ov : mx;
-      }
-      double sexp = exp(z - mx);
-      for (int o = b / 2; o >= 1; o >>= 1) sexp += __shfl_xor(sexp, o);
-      if (x < rows && x % b == 0) s_lse[x / b] = mx + log(sexp);
     }
+    double mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMaxTok; ++k)
+      if (k < tpl) mx = z[k] > mx ? z[k] : mx;
+#pragma unroll
+    for (int o = kLanesPerCell / 2; o >= 1; o >>= 1) {
+      const double ov = __shfl_xor(mx, o);
+      mx = ov > mx ? ov : mx;
+    }
+    double sexp = 0.0;
+#pragma unroll
+    for (int k = 0; k < kMaxTok; ++k)
+      if (k < tpl) sexp += exp(z[k] - mx);
+#pragma unroll
+    for (int o = kLanesPerCell / 2; o >= 1; o >>= 1) sexp += __shfl_xor(sexp, o);
+    if (cs < nreach && g == 0) s_lse[cs] = mx + log(sexp);
   }
   __syncthreads();
   if (wave != 0) return;
