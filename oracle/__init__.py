@@ -31,7 +31,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 
 
 def build(force: bool = True) -> str:
@@ -67,6 +67,14 @@ def _declare(lib):
     lib.orc_num_threads.restype = I
     lib.orc_block_summaries.argtypes = [P, I, I, I, I64, I, I, I64, I64, P, P, P]
     lib.orc_block_summaries.restype = None
+    lib.orc_fp8_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_fp8_decode.restype = ctypes.c_double
+    lib.orc_fp8_encode.argtypes = [ctypes.c_float]
+    lib.orc_fp8_encode.restype = ctypes.c_uint8
+    lib.orc_quantize_fp8.argtypes = [P, I, I, I, I64, I, I64, I64, P, P]
+    lib.orc_quantize_fp8.restype = None
+    lib.orc_dequantize_fp8.argtypes = [P, P, I64, I, P]
+    lib.orc_dequantize_fp8.restype = None
     lib.orc_num_candidates.argtypes = [I64, I, I, I]
     lib.orc_num_candidates.restype = I64
     lib.orc_select_from_scores.argtypes = [P, I64, I, I, P, P, P, P]
@@ -114,7 +122,9 @@ def _dtype_code(a: np.ndarray) -> int:
         return BF16
     if a.dtype == np.float32:
         return F32
-    raise TypeError(f"oracle takes float32 or bf16 bit patterns (uint16), got {a.dtype}")
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"oracle takes float32, float64 or bf16 bit patterns (uint16), got {a.dtype}")
 
 
 def num_threads() -> int:
@@ -145,6 +155,44 @@ def block_summaries(k: np.ndarray, b: int, nblocks: int | None = None, ccap: int
     lib.orc_block_summaries(_ptr(k), _dtype_code(k), B, Hkv, L, d, b, nblocks, ccap,
                             _ptr(kbar), _ptr(mx), _ptr(centre))
     return kbar, mx, centre
+
+
+def fp8_decode(code: int) -> float:
+    """Value of one OCP E4M3 code (NaN for S.1111.111)."""
+    return float(_load().orc_fp8_decode(int(code)))
+
+
+def fp8_encode(y: float) -> int:
+    """Nearest E4M3 code to the fp32 value y (ties to the even code, held at
+    +-448, sign kept)."""
+    return int(_load().orc_fp8_encode(float(np.float32(y))))
+
+
+def quantize_fp8(kbar: np.ndarray, first: int = 0, num: int | None = None):
+    """fp8 block summaries: kbar [B, Hkv, ccap, d] (float32 or bf16 bits) ->
+    codes [B, Hkv, ccap, d] uint8, scales [B, Hkv, ccap] fp32 for blocks
+    [first, first + num) (zeros elsewhere): per block scale = amax / 448, codes
+    = E4M3(kbar * (448 / amax)), single-precision scale arithmetic."""
+    lib = _load()
+    B, Hkv, ccap, d = kbar.shape
+    if num is None:
+        num = ccap - first
+    kbar = np.ascontiguousarray(kbar)
+    codes = np.zeros((B, Hkv, ccap, d), np.uint8)
+    scales = np.zeros((B, Hkv, ccap), np.float32)
+    lib.orc_quantize_fp8(_ptr(kbar), _dtype_code(kbar), B, Hkv, ccap, d, int(first), int(num),
+                         _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def dequantize_fp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """The summaries the scorer reads, exact in fp64: scale_c * decode(code)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    out = np.zeros(codes.shape, np.float64)
+    d = codes.shape[-1]
+    _load().orc_dequantize_fp8(_ptr(codes), _ptr(scales), codes.size // d, d, _ptr(out))
+    return out
 
 
 def select_from_scores(s, K: int, gate: bool = True):

@@ -48,7 +48,8 @@
  * Layouts (all row-major, contiguous):
  *   q [B, Hq, nq, d], k/v [B, Hkv, L, d], kbar [B, Hkv, Ccap, d],
  *   max_norm [B, Hkv, Ccap], centre [Ccap], idx/logg [B, Hsel, nq, K].
- *   dtype 0 = fp32, 1 = bf16 (raw uint16 bit patterns).
+ *   dtype 0 = fp32, 1 = bf16 (raw uint16 bit patterns), 2 = fp64 (summaries
+ *   rebuilt from fp8 codes, exact).
  */
 #include <math.h>
 #include <stdint.h>
@@ -61,6 +62,7 @@
 
 #define ORC_F32 0
 #define ORC_BF16 1
+#define ORC_F64 2
 
 /* ---------------------------------------------------------------- decode */
 
@@ -76,6 +78,8 @@ static double orc_load(const void *p, int dtype, int64_t i)
 {
     if (dtype == ORC_BF16)
         return orc_bf16_to_double(((const uint16_t *)p)[i]);
+    if (dtype == ORC_F64)
+        return ((const double *)p)[i];
     return (double)((const float *)p)[i];
 }
 
@@ -119,6 +123,98 @@ int orc_num_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* ------------------------------------------- fp8 summaries (decode) */
+/*
+ * Optional 8-bit block summaries for the decode scorer.  Format: OCP 8-bit
+ * floating point, E4M3 with no infinities (sign, 4 exponent bits biased by
+ * 7, 3 mantissa bits; exponent field 0 is subnormal, value m/8 2^-6; the all-
+ * ones pattern S.1111.111 is NaN, so the largest finite magnitude is
+ * 1.75 2^8 = 448).  Each block c of each (batch, kv head) is scaled by its
+ * largest magnitude: amax = max_e |kbar_c[e]|, inv = 448 / amax and
+ * scale_c = amax / 448, both single precision (IEEE division), y_e =
+ * kbar_c[e] inv (single precision product), code_e = y_e rounded to the
+ * nearest E4M3 value (ties to the even code), magnitudes past 448 held at
+ * 448, the sign kept (so -0 and negatives that round to zero give 0x80).
+ * A block of zeros has scale 0 and zero codes.  The summary the scorer reads
+ * is scale_c decode(code_e).  (The scale and code arithmetic is single
+ * precision on purpose: it decides integer codes, and both sides take that
+ * decision in the same precision.)
+ */
+double orc_fp8_decode(uint8_t code)
+{
+    int sgn = code >> 7, ex = (code >> 3) & 15, man = code & 7;
+    double v;
+    if (ex == 15 && man == 7)
+        return NAN;
+    if (ex == 0)
+        v = ldexp((double)man, -9);                   /* m/8 2^-6 */
+    else
+        v = ldexp(8.0 + man, ex - 10);                /* (1 + m/8) 2^(e-7) */
+    return sgn ? -v : v;
+}
+
+/* Nearest E4M3 magnitude code to |y| by brute force over the 127 finite
+ * non-negative codes (ties to the even code), sign from y. */
+uint8_t orc_fp8_encode(float y)
+{
+    double a = fabs((double)y);
+    int best = 0;
+    double bd = INFINITY;
+    if (a >= 448.0) {
+        best = 0x7E;
+    } else {
+        for (int c = 0; c <= 0x7E; ++c) {
+            double dlt = fabs(orc_fp8_decode((uint8_t)c) - a);
+            if (dlt < bd || (dlt == bd && (c & 1) == 0 && (best & 1) == 1)) {
+                bd = dlt;
+                best = c;
+            }
+        }
+    }
+    return (uint8_t)(best | (signbit(y) ? 0x80 : 0));
+}
+
+/* codes [B, Hkv, Ccap, d] uint8 and scales [B, Hkv, Ccap] fp32 of blocks
+ * [first, first + num) from kbar [B, Hkv, Ccap, d] (dtype). */
+void orc_quantize_fp8(const void *kbar, int dtype, int B, int Hkv, int64_t Ccap, int d, int64_t first,
+                      int64_t num, uint8_t *codes, float *scales)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t bh = 0; bh < (int64_t)B * Hkv; ++bh) {
+        for (int64_t c = first; c < first + num; ++c) {
+            const int64_t row = (bh * Ccap + c) * (int64_t)d;
+            float amax = 0.0f;
+            for (int e = 0; e < d; ++e) {
+                float x = (float)orc_load(kbar, dtype, row + e);
+                if (fabsf(x) > amax)
+                    amax = fabsf(x);
+            }
+            if (amax == 0.0f) {
+                scales[bh * Ccap + c] = 0.0f;
+                for (int e = 0; e < d; ++e)
+                    codes[row + e] = 0;
+                continue;
+            }
+            volatile float inv = 448.0f / amax;       /* single precision, as the format rule says */
+            volatile float sc = amax / 448.0f;
+            scales[bh * Ccap + c] = sc;
+            for (int e = 0; e < d; ++e) {
+                volatile float y = (float)orc_load(kbar, dtype, row + e) * inv;
+                codes[row + e] = orc_fp8_encode(y);
+            }
+        }
+    }
+}
+
+/* The summaries the scorer reads, exact in fp64: out = scale_c decode(code). */
+void orc_dequantize_fp8(const uint8_t *codes, const float *scales, int64_t rows, int d, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int e = 0; e < d; ++e)
+            out[r * d + e] = (double)scales[r] * orc_fp8_decode(codes[r * d + e]);
 }
 
 /* ------------------------------------------------------ a1: summaries */
