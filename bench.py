@@ -11,7 +11,9 @@ One decode step = the hot path for one query token of one layer:
   attention workgroups), plus, on every b-th step, the summary of the block
   that closes (sparse_block_summaries).  The two-call sequence is timed the
   same way for comparison (unfused_us_per_step), and so is the step over the
-  same caches scattered into page pools (paged_us_per_step).
+  same caches scattered into page pools (paged_us_per_step) and the step whose
+  scorer reads fp8 (E4M3) summaries with per-block scales (fp8_summaries; on
+  closing steps the new block is also quantized).
 Steps rotate over 16 layers' KV caches (2.15 GB each) and 64 query vectors so
 that every step reads its summaries and selected K/V cold from HBM, as a
 multi-layer decoder would.  Inputs are resident in HBM before timing starts.
@@ -173,6 +175,27 @@ class DecodeWorkload:
         self.ws_pag = ops.Workspace()
         torch.cuda.synchronize()
 
+    def make_fp8(self):
+        """fp8 (E4M3) copies of every layer's summaries with per-block scales."""
+        self.codes8, self.scale8 = [], []
+        for layer in range(len(self.kbar)):
+            c, sc = ops.sparse_quantize_summaries_fp8(self.kbar[layer])
+            self.codes8.append(c)
+            self.scale8.append(sc)
+        self.ws_f8 = ops.Workspace()
+        torch.cuda.synchronize()
+
+    def close_block_fp8(self, layer):
+        self.close_block(layer)
+        ops.sparse_quantize_summaries_fp8(self.kbar[layer], first_block=self.ccap - 1, num_blocks=1,
+                                          codes=self.codes8[layer], scales=self.scale8[layer])
+
+    def decode_fp8(self, layer, qi):
+        ops.sparse_decode_step(self.q[qi], self.codes8[layer], self.mx[layer], self.ce[layer], self.k[layer],
+                               self.v[layer], Hkv=self.cfg["Hkv"], b=self.b, K=self.K, q_pos0=self.pos, gate=True,
+                               proj_w=self.w[layer], idx=self.idx, logg=self.logg, k_eff=self.keff, o=self.o,
+                               lse=self.lse, workspace=self.ws_f8, kbar_scale=self.scale8[layer])
+
     def close_block_paged(self, layer):
         ops.sparse_block_summaries_paged(self.kp[layer], self.table, self.L, self.b, first_block=self.ccap - 1,
                                          num_blocks=1, kbar=self.kbar[layer], max_norm=self.mx[layer],
@@ -199,9 +222,10 @@ class DecodeWorkload:
         qo = c["B"] * c["Hq"] * c["d"] * 2 * 2 + c["B"] * c["Hkv"] * self.K * 8
         return kv + qo
 
-    def scoring_bytes(self):
+    def scoring_bytes(self, fp8=False):
         c = self.cfg
-        return c["B"] * c["Hkv"] * self.C * (c["d"] * 2) + c["d"] * c["d"] * 4 + c["B"] * c["Hq"] * c["d"] * 2
+        row = c["d"] + 4 if fp8 else c["d"] * 2          # codes + scale, or the bf16 summary
+        return c["B"] * c["Hkv"] * self.C * row + c["d"] * c["d"] * 4 + c["B"] * c["Hq"] * c["d"] * 2
 
 
 def run_decode(args):
@@ -256,37 +280,48 @@ def run_decode(args):
         torch.cuda.synchronize()
         return g0.elapsed_time(g1)
 
+    def per_kernel(one_step, close):
+        """Per-kernel durations over the same steps (eager), from each kernel's
+        own dispatch timestamps (start/stop events attached to its launch)."""
+        hip = HipEvents()
+        EvArr = ctypes.c_void_p * 6
+        evs = [EvArr(*[hip.create() for _ in range(6)]) for _ in range(steps)]
+        lib = ops.lib()
+        for s in range(steps):
+            layer, qi = s % args.layers, s % args.queries
+            if s % wl.b == wl.b - 1:
+                close(layer)
+            lib.spa_profile_next_call(evs[s], 3)
+            one_step(layer, qi)
+        torch.cuda.synchronize()
+        out = {name: np.array([hip.elapsed(evs[s][2 * i], evs[s][2 * i + 1]) for s in range(steps)])
+               for name, i in (("chunk", 0), ("merge_partial", 1), ("combine", 2))}
+        hip.destroy_all()
+        return out
+
     # timed region: the one-call decode step
     total_ms = timed_graph(wl.decode)
 
     def two_calls(layer, qi):
         wl.select(layer, qi)
         wl.attend(layer, qi)
-    unfused_ms = paged_ms = None
+    unfused_ms = paged_ms = fp8_ms = None
+    fp8_k_ms = None
     if not args.skip_variants:
         unfused_ms = timed_graph(two_calls)
+        # the same steps with fp8 summaries (the scorer reads codes + scales)
+        wl.make_fp8()
+        for s in range(4):
+            wl.decode_fp8(s % args.layers, s % args.queries)
+        fp8_ms = timed_graph(wl.decode_fp8, close=wl.close_block_fp8)
+        fp8_k_ms = per_kernel(wl.decode_fp8, wl.close_block_fp8)
         # the same steps over a paged cache (random page order)
         wl.make_paged()
         for s in range(4):
             wl.decode_paged(s % args.layers, s % args.queries)
         paged_ms = timed_graph(wl.decode_paged, close=wl.close_block_paged)
 
-    # per-kernel durations over the same steps (eager), from each kernel's own
-    # dispatch timestamps (start/stop events attached to its launch)
-    hip = HipEvents()
-    EvArr = ctypes.c_void_p * 6
-    evs = [EvArr(*[hip.create() for _ in range(6)]) for _ in range(steps)]
-    lib = ops.lib()
-    for s in range(steps):
-        layer, qi = s % args.layers, s % args.queries
-        if s % wl.b == wl.b - 1:
-            wl.close_block(layer)
-        lib.spa_profile_next_call(evs[s], 3)
-        wl.decode(layer, qi)
-    torch.cuda.synchronize()
-    k_ms = {name: np.array([hip.elapsed(evs[s][2 * i], evs[s][2 * i + 1]) for s in range(steps)])
-            for name, i in (("chunk", 0), ("merge_partial", 1), ("combine", 2))}
-    hip.destroy_all()
+    k_ms = per_kernel(wl.decode, wl.close_block)
 
     # a hot-cache variant (one layer, one query) for context
     hot = torch.cuda.CUDAGraph()
@@ -306,6 +341,7 @@ def run_decode(args):
 
     floor_us = latency_floor_us(stream, steps, len(k_ms))
     return dict(wl=wl, cfg=cfg, x=x, total_ms=total_ms, unfused_ms=unfused_ms, paged_ms=paged_ms, k_ms=k_ms,
+                fp8_ms=fp8_ms, fp8_k_ms=fp8_k_ms,
                 summ_ms=summ_ms, summ_bytes=summ_bytes, hot_us=hot_us, floor_us=floor_us)
 
 
@@ -690,6 +726,11 @@ def main():
         "selected_kv_gbps": round(att_bytes / (kern["merge_partial"]["us"] * 1e-6) / 1e9, 1),
         "unfused_us_per_step": None if res["unfused_ms"] is None else round(res["unfused_ms"] * 1e3 / steps, 3),
         "paged_us_per_step": None if res["paged_ms"] is None else round(res["paged_ms"] * 1e3 / steps, 3),
+        "fp8_summaries": None if res["fp8_ms"] is None else {
+            "us_per_step": round(res["fp8_ms"] * 1e3 / steps, 3),
+            "chunk_us": round(float(np.mean(res["fp8_k_ms"]["chunk"])) * 1e3, 3),
+            "scoring_bytes": wl.scoring_bytes(fp8=True),
+        },
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kern.items()},
         "hot_cache_us_per_step": round(res["hot_us"], 3),

@@ -95,7 +95,11 @@ int check_select(const spa_select_args* a, spa::SelectLaunch* p) {
                          a->max_norm, a->centre, a->ccap, a->b, a->prefix_mode,
                          a->prefix_mode == SPA_PREFIX_QUERY_BLOCK ? a->qblock : 1, a->share_group ? 1 : 0,
                          a->proj_w, a->erf_lambda, a->erf_sigma, a->K, a->gate, a->idx, a->logg,
-                         a->k_eff, Hsel, max_cand};
+                         a->k_eff, Hsel, max_cand, a->kbar_scale};
+  if (a->kbar_scale != nullptr)
+    SPA_REQUIRE(spa::decode_select_path(*p), SPA_ERR_UNSUPPORTED,
+                "fp8 summaries (kbar_scale) are read by the one-row decode scorer only: nq = 1, "
+                "CURRENT_BLOCK candidates, no erf term");
   return SPA_OK;
 }
 
@@ -156,6 +160,7 @@ int check_select_bwd(const spa_select_args* a, const spa_select_grads* g, spa::S
   SPA_REQUIRE(a->prefix_mode == SPA_PREFIX_CURRENT_BLOCK && a->erf_lambda == nullptr, SPA_ERR_UNSUPPORTED,
               "the selector backward supports current-block candidates without the erf term");
   SPA_REQUIRE(a->dtype == SPA_DTYPE_BF16, SPA_ERR_UNSUPPORTED, "the selector backward supports bf16 only");
+  SPA_REQUIRE(a->kbar_scale == nullptr, SPA_ERR_UNSUPPORTED, "the selector backward takes summaries in dtype");
   SPA_REQUIRE(g != nullptr && g->dg && g->dq && g->dkbar, SPA_ERR_INVALID_ARG,
               "grads, dg, dq and dkbar must be non-NULL");
   SPA_REQUIRE(aligned16(g->dq) && aligned16(g->dkbar), SPA_ERR_INVALID_ARG, "dq and dkbar must be 16-byte aligned");
@@ -296,6 +301,39 @@ int sparse_score_select(const spa_select_args* a, void* workspace, size_t ws_byt
                     "sparse_score_select");
 }
 
+int sparse_quantize_summaries_fp8(const void* kbar, int dtype, int B, int Hkv, int64_t ccap, int d,
+                                  int64_t first_block, int64_t num_blocks, uint8_t* codes, float* scales,
+                                  spa_stream_t stream) {
+  ProfileScope profile_scope;
+  int st = check_heads(B, Hkv, Hkv, d, dtype);
+  if (st != SPA_OK) return st;
+  SPA_REQUIRE(kbar && codes && scales, SPA_ERR_INVALID_ARG, "kbar, codes and scales must be non-NULL");
+  SPA_REQUIRE(aligned16(kbar) && aligned16(codes) && aligned16(scales), SPA_ERR_INVALID_ARG,
+              "kbar, codes and scales must be 16-byte aligned");
+  SPA_REQUIRE(first_block >= 0 && num_blocks >= 0 && first_block + num_blocks <= ccap, SPA_ERR_INVALID_ARG,
+              "blocks [%lld, %lld) outside [0, ccap = %lld)", static_cast<long long>(first_block),
+              static_cast<long long>(first_block + num_blocks), static_cast<long long>(ccap));
+  SPA_REQUIRE(static_cast<int64_t>(B) * Hkv * num_blocks < (static_cast<int64_t>(1) << 33), SPA_ERR_UNSUPPORTED,
+              "too many blocks");
+  if (num_blocks == 0) return SPA_OK;
+  return hip_status(spa::launch_quantize_fp8(kbar, dtype, B, Hkv, ccap, d, first_block, num_blocks, codes, scales,
+                                             static_cast<hipStream_t>(stream)),
+                    "sparse_quantize_summaries_fp8");
+}
+
+int sparse_dequantize_summaries_fp8(const uint8_t* codes, const float* scales, int64_t rows, int d, float* out,
+                                    spa_stream_t stream) {
+  ProfileScope profile_scope;
+  SPA_REQUIRE(codes && scales && out, SPA_ERR_INVALID_ARG, "codes, scales and out must be non-NULL");
+  SPA_REQUIRE(aligned16(codes) && aligned16(out), SPA_ERR_INVALID_ARG, "codes and out must be 16-byte aligned");
+  SPA_REQUIRE(d == 64 || d == 128, SPA_ERR_UNSUPPORTED, "d = %d not supported (64 or 128)", d);
+  SPA_REQUIRE(rows >= 0 && rows * (d / 16) < (static_cast<int64_t>(1) << 35), SPA_ERR_INVALID_ARG,
+              "rows = %lld out of range", static_cast<long long>(rows));
+  if (rows == 0) return SPA_OK;
+  return hip_status(spa::launch_dequantize_fp8(codes, scales, rows, d, out, static_cast<hipStream_t>(stream)),
+                    "sparse_dequantize_summaries_fp8");
+}
+
 int sparse_attn_fwd(const spa_attn_args* a, void* workspace, size_t ws_bytes, spa_stream_t stream) {
   ProfileScope profile_scope;
   spa::AttnLaunch p;
@@ -389,6 +427,7 @@ int sparse_score_select_subset(const spa_select_args* a, const int32_t* cells, c
   int st = check_select(a, &p);
   if (st != SPA_OK) return st;
   SPA_REQUIRE(a->proj_w == nullptr, SPA_ERR_UNSUPPORTED, "the kept-set selection takes no projection");
+  SPA_REQUIRE(a->kbar_scale == nullptr, SPA_ERR_UNSUPPORTED, "the kept-set selection takes summaries in dtype");
   SPA_REQUIRE(cells && count, SPA_ERR_INVALID_ARG, "cells and count must be non-NULL");
   SPA_REQUIRE(cap >= 1 && cap <= 256, SPA_ERR_UNSUPPORTED, "cap = %d not supported (1..256)", cap);
   return hip_status(spa::launch_score_select_subset(p, cells, count, cap, static_cast<hipStream_t>(stream)),
@@ -450,6 +489,7 @@ int sparse_forest_select(const spa_select_args* a, const void* k, int64_t L, con
   if (st != SPA_OK) return st;
   SPA_REQUIRE(a->gate == SPA_GATE_NONE && a->proj_w == nullptr, SPA_ERR_UNSUPPORTED,
               "the forest selection takes no gate and no projection");
+  SPA_REQUIRE(a->kbar_scale == nullptr, SPA_ERR_UNSUPPORTED, "the forest selection takes summaries in dtype");
   SPA_REQUIRE(a->K <= 16, SPA_ERR_UNSUPPORTED, "K = %d not supported (<= 16)", a->K);
   SPA_REQUIRE(a->b == 16 || a->b == 32 || a->b == 64, SPA_ERR_UNSUPPORTED, "cell size b = %d not supported", a->b);
   SPA_REQUIRE(k != nullptr && aligned16(k), SPA_ERR_INVALID_ARG, "k must be non-NULL and 16-byte aligned");

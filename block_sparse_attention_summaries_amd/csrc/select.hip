@@ -42,12 +42,14 @@ namespace spa {
 // with a projection, W) are issued before any of them is consumed.  Output:
 // the chunk's top-min(K, n) candidates in index order as 64-bit
 // (orderable score << 32 | block index) records (0 pads), and its (max, sum exp).
-template <typename T, int D>
+template <typename T, int D, bool F8>
 __global__ __launch_bounds__(256) void decode_chunk_kernel(
-    const T* __restrict__ q, const T* __restrict__ kbar, const float* __restrict__ proj_w,
-    int Hq, int Hkv, int Hsel, int share_group, int64_t ccap, int64_t ncand, int K,
-    uint64_t* __restrict__ ws_keys, float2* __restrict__ ws_ml, int nchunks) {
-  constexpr int kVec = Elem<T>::kVec;
+    const T* __restrict__ q, const void* __restrict__ kbar_v, const float* __restrict__ kscale,
+    const float* __restrict__ proj_w, int Hq, int Hkv, int Hsel, int share_group, int64_t ccap, int64_t ncand,
+    int K, uint64_t* __restrict__ ws_keys, float2* __restrict__ ws_ml, int nchunks) {
+  // F8: the summaries are E4M3 codes (16 per 16-byte load) scaled per block
+  constexpr int kVec = F8 ? 16 : Elem<T>::kVec;   // summary elements per 16-byte load
+  constexpr int kElemBytes = F8 ? 1 : static_cast<int>(sizeof(T));
   constexpr int kLPB = D / kVec;           // lanes per block row
   constexpr int kBPR = kWave / kLPB;       // blocks per load round of a wave
   constexpr int kRounds = kWave / kBPR;    // rounds to cover the wave's 64 blocks
@@ -91,13 +93,17 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(
   const int cg = lane % kLPB, bl = lane / kLPB;
   const int64_t cbase = static_cast<int64_t>(chunk) * kDecodeChunk;
   const int64_t wbase = cbase + wave * kWave;
-  const T* kb = kbar + (static_cast<int64_t>(bi) * Hkv + kvh) * ccap * D;
+  const int64_t hrow = (static_cast<int64_t>(bi) * Hkv + kvh) * ccap;
+  const char* kb = static_cast<const char*>(kbar_v) + hrow * D * kElemBytes;
   const int64_t clast = ncand > 0 ? ncand - 1 : 0;
   uint4 raw[kRounds];
+  float bscale[F8 ? kRounds : 1];
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const int64_t c = wbase + r * kBPR + bl;
-    raw[r] = *reinterpret_cast<const uint4*>(kb + (c < clast ? c : clast) * D + cg * kVec);
+    const int64_t cc = c < clast ? c : clast;
+    raw[r] = *reinterpret_cast<const uint4*>(kb + (cc * D + cg * kVec) * kElemBytes);
+    if constexpr (F8) bscale[r] = kscale[hrow + cc];
   }
   // 4. q_hat, then u = W^T q_hat from the row slices, summed over slices
   if (tid < D) {
@@ -140,11 +146,15 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     float x[kVec];
-    Elem<T>::unpack(raw[r], x);
+    if constexpr (F8)
+      fp8_e4m3_unpack16(raw[r], x);
+    else
+      Elem<T>::unpack(raw[r], x);
     float p = 0.f;
 #pragma unroll
     for (int i = 0; i < kVec; ++i) p = fmaf(x[i], uc[i], p);
     p = group_sum<kLPB>(p);
+    if constexpr (F8) p *= bscale[r];
     if (cg == 0) s_score[wave * kWave + r * kBPR + bl] = p * scale;
   }
   __syncthreads();
@@ -370,10 +380,13 @@ size_t select_workspace_bytes(const SelectLaunch& p) {
 template <typename T, int D>
 static hipError_t launch_chunks_t(const SelectLaunch& p, void* ws, hipStream_t st) {
   const DecodeSelectWs w = decode_select_ws(p, ws);
-  return launch(false, decode_chunk_kernel<T, D>, dim3(w.nch, static_cast<unsigned>(p.B * p.Hsel)), dim3(256),
-                st, static_cast<const T*>(p.q), static_cast<const T*>(p.kbar), p.proj_w, p.Hq, p.Hkv, p.Hsel,
-                p.share_group, p.ccap, p.max_cand, p.K, w.keys, w.ml, w.nch);
+  auto kern = p.kbar_scale != nullptr ? decode_chunk_kernel<T, D, true> : decode_chunk_kernel<T, D, false>;
+  return launch(false, kern, dim3(w.nch, static_cast<unsigned>(p.B * p.Hsel)), dim3(256), st,
+                static_cast<const T*>(p.q), p.kbar, p.kbar_scale, p.proj_w, p.Hq, p.Hkv, p.Hsel, p.share_group,
+                p.ccap, p.max_cand, p.K, w.keys, w.ml, w.nch);
 }
+
+bool decode_select_path(const SelectLaunch& p) { return use_decode_path(p); }
 
 bool decode_fusable(const SelectLaunch& p) {
   return use_decode_path(p) && p.dtype == kDtypeBf16 && merge_nv(p) <= kFusedMergeMaxNV;

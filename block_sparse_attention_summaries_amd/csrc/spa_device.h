@@ -79,6 +79,41 @@ __device__ __forceinline__ float ld_f(const T* p) {
   return Elem<T>::to_float(*p);
 }
 
+// ------------------------------------------------------- fp8 summaries
+// OCP 8-bit floating point, E4M3 without infinities: sign, 4 exponent bits
+// biased by 7, 3 mantissa bits; exponent field 0 holds m/8 2^-6; S.1111.111
+// is NaN, so 448 = 1.75 2^8 is the largest finite magnitude.
+//
+// Nearest code to y, ties to the even code, magnitudes at or past 448 held
+// at 448, the sign kept.  A normal magnitude a in [2^e, 2^(e+1)) has quantum
+// 2^(e-3): a 2^(3-e) lies in [8, 16) and rounds (to even) to an integer r;
+// code = ((e + 7) << 3) + r - 8, a carry to r = 16 landing on the next
+// exponent's first code.  Below 2^-6 the quantum is 2^-9 and code = rint(a 2^9).
+__device__ __forceinline__ uint32_t fp8_e4m3_encode(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (!(a < 448.0f)) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | static_cast<uint32_t>(rintf(a * 512.0f));   // exact power-of-two scale
+  const int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xFFu) - 127;
+  const int r = static_cast<int>(rintf(ldexpf(a, 3 - e)));
+  return sign | static_cast<uint32_t>(((e + 7) << 3) + r - 8);
+}
+
+// 16 E4M3 codes of a 16-byte vector (byte j of word w is element 4w + j) to
+// fp32, exact (hardware conversion, two codes per instruction).
+__device__ __forceinline__ void fp8_e4m3_unpack16(const uint4& v, float* out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), true);
+    out[4 * i] = lo[0];
+    out[4 * i + 1] = lo[1];
+    out[4 * i + 2] = hi[0];
+    out[4 * i + 3] = hi[1];
+  }
+}
+
 // --------------------------------------------------------------- score keys
 // A 64-bit key that orders (score desc, index asc) as an unsigned integer:
 // high word = order-preserving image of the fp32 score, low word = ~index.

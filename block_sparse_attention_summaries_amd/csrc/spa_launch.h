@@ -55,6 +55,7 @@ struct SelectLaunch {
   int32_t* k_eff;
   int Hsel;
   int64_t max_cand;   // candidates of the last row (the largest count)
+  const float* kbar_scale;   // non-NULL: kbar holds fp8 (E4M3) codes, one scale per block
 };
 
 struct SelectGrads {
@@ -179,6 +180,12 @@ size_t attn_fwd_workspace_bytes(const AttnLaunch& p);
 size_t attn_bwd_workspace_bytes(const BwdLaunch& p);
 
 hipError_t launch_block_summaries(const SummaryLaunch& p, hipStream_t st);
+// fp8 summaries: codes [B, Hkv, ccap, d] uint8 and scales [B, Hkv, ccap] of
+// blocks [first, first + num) from kbar (dtype); and the fp32 rebuild.
+hipError_t launch_quantize_fp8(const void* kbar, int dtype, int B, int Hkv, int64_t ccap, int d, int64_t first,
+                               int64_t num, uint8_t* codes, float* scales, hipStream_t st);
+hipError_t launch_dequantize_fp8(const uint8_t* codes, const float* scales, int64_t rows, int d, float* out,
+                                 hipStream_t st);
 hipError_t launch_score_select(const SelectLaunch& p, void* ws, hipStream_t st);
 hipError_t launch_select_bwd(const SelectLaunch& p, const SelectGrads& g, void* ws, hipStream_t st);
 hipError_t launch_retain_cells(const float* max_norm, int B, int Hkv, int64_t ccap, int64_t ncand, int W, int P,
@@ -190,6 +197,8 @@ size_t forest_workspace_bytes(int B, int Hkv, int d, int64_t n);
 hipError_t launch_forest_build(const ForestLaunch& p, hipStream_t st);
 hipError_t launch_forest_select(const SelectLaunch& s, const ForestLaunch& p, const void* k, int64_t L,
                                 hipStream_t st);
+// the one-row chunk scorer + merge handles this selection (the path that reads fp8 summaries)
+bool decode_select_path(const SelectLaunch& p);
 bool decode_fusable(const SelectLaunch& p);
 int decode_merge_nv(const SelectLaunch& p);
 hipError_t launch_decode_chunks(const SelectLaunch& p, void* ws, hipStream_t st);

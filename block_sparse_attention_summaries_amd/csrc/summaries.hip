@@ -10,6 +10,12 @@
 // coalesced loads (a block of b rows x d elements is one contiguous span),
 // fp64 column sums in registers, a cross-lane sum of squares per row and an
 // LDS reduction of the column sums.
+//
+// Optional fp8 summaries for the decode scorer (half the scoring bytes):
+// quantize_fp8_kernel turns block rows of kbar into OCP E4M3 codes with one
+// fp32 scale per block (amax / 448; codes of kbar * (448 / amax), nearest,
+// ties to even), one wave per row; dequantize_fp8_kernel rebuilds fp32
+// summaries through the same decode the scorer uses.
 #include "spa_device.h"
 #include "spa_launch.h"
 
@@ -104,6 +110,77 @@ hipError_t launch_block_summaries(const SummaryLaunch& p, hipStream_t st) {
     return p.d == 64 ? launch_summaries_t<bf16_t, 64>(p, st) : launch_summaries_t<bf16_t, 128>(p, st);
   }
   return p.d == 64 ? launch_summaries_t<float, 64>(p, st) : launch_summaries_t<float, 128>(p, st);
+}
+
+// One wave per (batch, kv head, block) row: the row's largest magnitude, then
+// scale = amax / 448 and codes of x (448 / amax), both quotients correctly
+// rounded in single precision; a zero row gets scale 0 and zero codes.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const T* __restrict__ kbar, int64_t ccap,
+                                                           int64_t first, int64_t num, int64_t rows_total,
+                                                           uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  constexpr int kPer = D / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;   // (bh, block) in the range
+  if (r >= rows_total) return;                  // whole wave leaves
+  const int64_t bh = r / num, c = first + r % num;
+  const int64_t row = (bh * ccap + c) * D;
+  float x[kPer];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    x[i] = ld_f(kbar + row + i * kWave + lane);
+    amax = fmaxf(amax, fabsf(x[i]));
+  }
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  const bool zero = amax == 0.f;
+  const float inv = zero ? 0.f : __fdiv_rn(448.0f, amax);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    codes[row + i * kWave + lane] = static_cast<uint8_t>(zero ? 0u : fp8_e4m3_encode(__fmul_rn(x[i], inv)));
+  if (lane == 0) scales[bh * ccap + c] = zero ? 0.f : __fdiv_rn(amax, 448.0f);
+}
+
+// One thread per 16 codes: out = scale * decode(code) (single-precision product).
+__global__ __launch_bounds__(256) void dequantize_fp8_kernel(const uint8_t* __restrict__ codes,
+                                                             const float* __restrict__ scales, int64_t rows,
+                                                             int d, float* __restrict__ out) {
+  const int64_t v = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int per_row = d / 16;
+  if (v >= rows * per_row) return;
+  const float s = scales[v / per_row];
+  float x[16];
+  fp8_e4m3_unpack16(reinterpret_cast<const uint4*>(codes)[v], x);
+  float4* o = reinterpret_cast<float4*>(out) + v * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = make_float4(__fmul_rn(x[4 * i], s), __fmul_rn(x[4 * i + 1], s), __fmul_rn(x[4 * i + 2], s),
+                       __fmul_rn(x[4 * i + 3], s));
+}
+
+template <typename T, int D>
+static hipError_t launch_quantize_t(const void* kbar, int B, int Hkv, int64_t ccap, int64_t first, int64_t num,
+                                    uint8_t* codes, float* scales, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(B) * Hkv * num;
+  return launch(true, quantize_fp8_kernel<T, D>, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), st,
+                static_cast<const T*>(kbar), ccap, first, num, rows, codes, scales);
+}
+
+hipError_t launch_quantize_fp8(const void* kbar, int dtype, int B, int Hkv, int64_t ccap, int d, int64_t first,
+                               int64_t num, uint8_t* codes, float* scales, hipStream_t st) {
+  if (dtype == kDtypeBf16)
+    return d == 64 ? launch_quantize_t<bf16_t, 64>(kbar, B, Hkv, ccap, first, num, codes, scales, st)
+                   : launch_quantize_t<bf16_t, 128>(kbar, B, Hkv, ccap, first, num, codes, scales, st);
+  return d == 64 ? launch_quantize_t<float, 64>(kbar, B, Hkv, ccap, first, num, codes, scales, st)
+                 : launch_quantize_t<float, 128>(kbar, B, Hkv, ccap, first, num, codes, scales, st);
+}
+
+hipError_t launch_dequantize_fp8(const uint8_t* codes, const float* scales, int64_t rows, int d, float* out,
+                                 hipStream_t st) {
+  const int64_t n = rows * (d / 16);
+  return launch(true, dequantize_fp8_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), st, codes,
+                scales, rows, d, out);
 }
 
 }  // namespace spa

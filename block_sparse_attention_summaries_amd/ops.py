@@ -30,9 +30,11 @@ EXPORTED = ["spa_abi_version", "spa_profile_next_call", "spa_last_error", "spars
             "sparse_attn_fwd", "sparse_attn_bwd", "sparse_select_bwd", "sparse_decode_step",
             "sparse_block_summaries_paged", "sparse_decode_step_paged", "sparse_retain_cells",
             "sparse_score_select_subset", "sparse_forest_nodes", "sparse_forest_workspace_bytes",
-            "sparse_forest_build", "sparse_forest_select", "sparse_workspace_bytes", "sparse_workspace_init"]
+            "sparse_forest_build", "sparse_forest_select", "sparse_quantize_summaries_fp8",
+            "sparse_dequantize_summaries_fp8", "sparse_workspace_bytes", "sparse_workspace_init"]
 
 _vp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+ABI_VERSION = 2               # layout of the argument structs below
 
 
 class SelectArgs(ctypes.Structure):
@@ -40,7 +42,7 @@ class SelectArgs(ctypes.Structure):
                 ("q_pos0", _i64), ("kbar", _vp), ("max_norm", _vp), ("centre", _vp), ("ccap", _i64),
                 ("b", _i), ("prefix_mode", _i), ("qblock", _i), ("share_group", _i), ("proj_w", _vp),
                 ("erf_lambda", _vp), ("erf_sigma", _vp), ("K", _i), ("gate", _i), ("idx", _vp),
-                ("logg", _vp), ("k_eff", _vp)]
+                ("logg", _vp), ("k_eff", _vp), ("kbar_scale", _vp)]
 
 
 class SelectGrads(ctypes.Structure):
@@ -121,10 +123,17 @@ def lib():
                                           _sz, _vp]
         L.sparse_forest_select.restype = _i
         L.sparse_forest_select.argtypes = [ctypes.POINTER(SelectArgs), _vp, _i64, ctypes.POINTER(Forest), _i64, _vp]
+        L.sparse_quantize_summaries_fp8.restype = _i
+        L.sparse_quantize_summaries_fp8.argtypes = [_vp, _i, _i, _i, _i64, _i, _i64, _i64, _vp, _vp, _vp]
+        L.sparse_dequantize_summaries_fp8.restype = _i
+        L.sparse_dequantize_summaries_fp8.argtypes = [_vp, _vp, _i64, _i, _vp, _vp]
         L.sparse_workspace_bytes.restype = _sz
         L.sparse_workspace_bytes.argtypes = [_i, _vp]
         L.sparse_workspace_init.restype = _i
         L.sparse_workspace_init.argtypes = [_vp, _sz, _vp]
+        if L.spa_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.spa_abi_version()}, this binding needs "
+                               f"{ABI_VERSION}: rebuild it with __graft_entry__.build()")
         _lib = L
     return _lib
 
@@ -212,10 +221,40 @@ def sparse_block_summaries(k, b, first_block=0, num_blocks=None, ccap=None, kbar
     return kbar, max_norm, centre
 
 
+def sparse_quantize_summaries_fp8(kbar, first_block=0, num_blocks=None, codes=None, scales=None, stream=None):
+    """fp8 (OCP E4M3) block summaries of kbar [B, Hkv, ccap, d] for blocks
+    [first_block, first_block + num_blocks): codes uint8 [B, Hkv, ccap, d] and
+    per-block scales fp32 [B, Hkv, ccap] (allocated zeroed when not given)."""
+    _contig(kbar, codes, scales)
+    B, Hkv, ccap, d = kbar.shape
+    if num_blocks is None:
+        num_blocks = ccap - first_block
+    if codes is None:
+        codes = torch.zeros((B, Hkv, ccap, d), dtype=torch.uint8, device=kbar.device)
+    if scales is None:
+        scales = torch.zeros((B, Hkv, ccap), dtype=torch.float32, device=kbar.device)
+    _check(lib().sparse_quantize_summaries_fp8(_p(kbar), _dtype(kbar), B, Hkv, ccap, d, first_block, num_blocks,
+                                               _p(codes), _p(scales), _stream(stream)))
+    return codes, scales
+
+
+def sparse_dequantize_summaries_fp8(codes, scales, out=None, stream=None):
+    """The fp32 summaries the decode scorer reads: scales * decode(codes)."""
+    _contig(codes, scales, out)
+    d = codes.shape[-1]
+    if out is None:
+        out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
+    _check(lib().sparse_dequantize_summaries_fp8(_p(codes), _p(scales), codes.numel() // d, d, _p(out),
+                                                 _stream(stream)))
+    return out
+
+
 def select_args(q, kbar, max_norm, centre, *, Hkv, b, K, q_pos0, gate=True, prefix_mode=0,
                 qblock=128, share_group=True, proj_w=None, erf_lambda=None, erf_sigma=None,
-                idx=None, logg=None, k_eff=None):
-    _contig(q, kbar, max_norm, centre, proj_w, erf_lambda, erf_sigma, idx, logg, k_eff)
+                idx=None, logg=None, k_eff=None, kbar_scale=None):
+    """kbar_scale: None, or the per-block scales of fp8 summaries (kbar then
+    holds the uint8 codes of sparse_quantize_summaries_fp8)."""
+    _contig(q, kbar, max_norm, centre, proj_w, erf_lambda, erf_sigma, idx, logg, k_eff, kbar_scale)
     B, Hq, nq, d = q.shape
     Hsel = Hkv if share_group else Hq
     dev = q.device
@@ -229,7 +268,8 @@ def select_args(q, kbar, max_norm, centre, *, Hkv, b, K, q_pos0, gate=True, pref
                    kbar=_p(kbar), max_norm=_p(max_norm), centre=_p(centre), ccap=kbar.shape[2], b=b,
                    prefix_mode=prefix_mode, qblock=qblock, share_group=int(bool(share_group)),
                    proj_w=_p(proj_w), erf_lambda=_p(erf_lambda), erf_sigma=_p(erf_sigma), K=K,
-                   gate=int(bool(gate)), idx=_p(idx), logg=_p(logg), k_eff=_p(k_eff))
+                   gate=int(bool(gate)), idx=_p(idx), logg=_p(logg), k_eff=_p(k_eff),
+                   kbar_scale=_p(kbar_scale))
     return a, (idx, logg, k_eff)
 
 
@@ -307,13 +347,13 @@ def sparse_select_bwd(q, kbar, max_norm, centre, idx, logg, dg, *, dq=None, dkba
 
 def sparse_decode_step(q, kbar, max_norm, centre, k, v, *, Hkv, b, K, q_pos0, gate=True, share_group=True,
                        proj_w=None, idx=None, logg=None, k_eff=None, o=None, lse=None, workspace=None,
-                       stream=None):
+                       stream=None, kbar_scale=None):
     """One decode step (nq = 1): score + gate + top-K over the summaries, then
     attention over the current block and the selected blocks.  Returns
-    (idx, logg, k_eff, o, lse)."""
+    (idx, logg, k_eff, o, lse).  With kbar_scale the summaries are fp8 codes."""
     sa, (idx, logg, k_eff) = select_args(q, kbar, max_norm, centre, Hkv=Hkv, b=b, K=K, q_pos0=q_pos0, gate=gate,
                                          share_group=share_group, proj_w=proj_w, idx=idx, logg=logg,
-                                         k_eff=k_eff)
+                                         k_eff=k_eff, kbar_scale=kbar_scale)
     aa, (o, lse) = attn_args(q, k, v, idx, logg, b=b, K=K, q_pos0=q_pos0, share_group=share_group, o=o,
                              lse=lse)
     da = DecodeArgs(select=ctypes.pointer(sa), attn=ctypes.pointer(aa))

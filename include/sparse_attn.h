@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define SPA_ABI_VERSION 1
+#define SPA_ABI_VERSION 2
 
 typedef void *spa_stream_t;
 
@@ -151,6 +151,11 @@ typedef struct spa_select_args {
     float *logg;              /* out [B, Hsel, nq, K]: s_c - LSE over all candidates, 0 in pads;
                                  may be NULL when gate == SPA_GATE_NONE */
     int32_t *k_eff;           /* out [B, Hsel, nq], may be NULL */
+    const float *kbar_scale;  /* NULL: kbar is in dtype.  Else [B, Hkv, ccap] fp32 block scales and kbar
+                                 holds OCP E4M3 codes (uint8, sparse_quantize_summaries_fp8); the summary
+                                 is kbar_scale[c] * decode(code).  Read only by the one-row decode scorer
+                                 (nq = 1, CURRENT_BLOCK candidates, no erf term): elsewhere
+                                 SPA_ERR_UNSUPPORTED */
 } spa_select_args;
 
 /*
@@ -164,6 +169,37 @@ typedef struct spa_select_args {
  */
 int sparse_score_select(const spa_select_args *a, void *workspace, size_t ws_bytes,
                         spa_stream_t stream);
+
+/*
+ * sparse_quantize_summaries_fp8 -- 8-bit block summaries for the decode
+ * scorer, which then reads half the bytes (the scoring pass reads every
+ * candidate's summary at every step, twice the selected K/V at 512K).  Format:
+ * OCP 8-bit floating point E4M3 without infinities (bias 7, 3 mantissa bits,
+ * largest finite 448).  For every (batch, kv head, block c) in
+ * [first_block, first_block + num_blocks):
+ *   amax = max_e |kbar_c[e]|;  scales[c] = amax / 448;
+ *   codes[c][e] = E4M3(kbar_c[e] * (448 / amax)): nearest, ties to the even
+ *   code, held at +-448, sign kept;
+ * both quotients and the product in single precision (correctly rounded); a
+ * block of zeros gets scale 0 and zero codes.  kbar [B, Hkv, ccap, d] in
+ * dtype, codes [B, Hkv, ccap, d] uint8, scales [B, Hkv, ccap] fp32 (caller-
+ * owned device buffers; rows outside the range are not touched).  Pass codes
+ * as spa_select_args.kbar and scales as kbar_scale.  (The pages do not state
+ * a summary precision; this is an optional compressed form of the mean keys
+ * of "SAS" review §3 Eq. 3.)  SPA_ERR_INVALID_ARG on null pointers, unaligned
+ * buffers or out-of-range blocks.
+ */
+int sparse_quantize_summaries_fp8(const void *kbar, int dtype, int B, int Hkv, int64_t ccap, int d,
+                                  int64_t first_block, int64_t num_blocks, uint8_t *codes, float *scales,
+                                  spa_stream_t stream);
+
+/* sparse_dequantize_summaries_fp8 -- the fp32 summaries the decode scorer
+ * reads: out[r][e] = scales[r] * decode(codes[r][e]) (single-precision
+ * product; the decode is exact), for rows r of d codes (d in {64, 128}).
+ * Uses the scorer's own decode.  SPA_ERR_INVALID_ARG on null or unaligned
+ * pointers. */
+int sparse_dequantize_summaries_fp8(const uint8_t *codes, const float *scales, int64_t rows, int d, float *out,
+                                    spa_stream_t stream);
 
 typedef struct spa_attn_args {
     const void *q;            /* [B, Hq, nq, d] */

@@ -21,7 +21,7 @@ FAKE_ODD = ctypes.c_void_p(0x10001)
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b([a-z_]+)\s*\([^;{]*\)\s*;", text)))
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(ops.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.spa_abi_version() == 1
+    assert lib.spa_abi_version() == 2
 
 
 def _sel(**kw):
@@ -210,3 +210,31 @@ def test_summaries_rejects_invalid_arguments():
     assert f(FAKE, 1, 1, 8, 4096, 100, 64, 0, 64, 64, FAKE, FAKE, None, None) == ops.SPA_ERR_UNSUPPORTED
     assert f(FAKE, 1, 1, 8, 4096, 128, 64, 0, 0, 64, FAKE, FAKE, None, None) == ops.SPA_OK  # nothing to do
     assert ops.lib().spa_last_error().decode() == ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kbar_scale=FAKE, nq=2, q_pos0=32830), ops.SPA_ERR_UNSUPPORTED),    # rows path
+    (dict(kbar_scale=FAKE, prefix_mode=1), ops.SPA_ERR_UNSUPPORTED),
+    (dict(kbar_scale=FAKE, erf_lambda=FAKE, erf_sigma=FAKE), ops.SPA_ERR_UNSUPPORTED),
+])
+def test_fp8_summaries_only_on_the_decode_scorer(kw, code):
+    assert _select_status(_sel(**kw)) == code
+    assert "fp8" in ops.lib().spa_last_error().decode()
+    # the one-row decode scorer takes them (workspace check comes next)
+    assert _select_status(_sel(kbar_scale=FAKE)) == ops.SPA_ERR_WORKSPACE
+
+
+def test_fp8_quantize_and_dequantize_reject_invalid_arguments():
+    L = ops.lib()
+    q = L.sparse_quantize_summaries_fp8
+    assert q(None, 1, 1, 8, 16, 128, 0, 16, FAKE, FAKE, None) == ops.SPA_ERR_INVALID_ARG
+    assert q(FAKE, 1, 1, 8, 16, 128, 0, 16, FAKE_ODD, FAKE, None) == ops.SPA_ERR_INVALID_ARG
+    assert q(FAKE, 1, 1, 8, 16, 128, 8, 9, FAKE, FAKE, None) == ops.SPA_ERR_INVALID_ARG      # past ccap
+    assert q(FAKE, 1, 1, 8, 16, 96, 0, 16, FAKE, FAKE, None) == ops.SPA_ERR_UNSUPPORTED
+    assert q(FAKE, 5, 1, 8, 16, 128, 0, 16, FAKE, FAKE, None) == ops.SPA_ERR_UNSUPPORTED
+    assert q(FAKE, 1, 1, 8, 16, 128, 3, 0, FAKE, FAKE, None) == ops.SPA_OK                   # nothing to do
+    dq = L.sparse_dequantize_summaries_fp8
+    assert dq(FAKE, FAKE, 4, 96, FAKE, None) == ops.SPA_ERR_UNSUPPORTED
+    assert dq(None, FAKE, 4, 128, FAKE, None) == ops.SPA_ERR_INVALID_ARG
+    assert dq(FAKE, FAKE, -1, 128, FAKE, None) == ops.SPA_ERR_INVALID_ARG
+    assert dq(FAKE, FAKE, 0, 128, FAKE, None) == ops.SPA_OK
