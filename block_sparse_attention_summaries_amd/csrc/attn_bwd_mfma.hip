@@ -119,14 +119,15 @@ __global__ __launch_bounds__(256, 2) void attn_tile_dq_kernel(
   const int hl = lane >> 5, ql = lane & 31;
   const int G = Hq / Hkv;
   const int hgroups = G / NH;
-  const int bz = blockIdx.y;
+  const uint2 bxy = xcd_block_xy();                        // XCD-aware tile order
+  const int bz = static_cast<int>(bxy.y);
   const int bi = bz / (Hkv * hgroups);
   const int kvh = (bz / hgroups) % Hkv;
   const int hg = bz % hgroups;
   const int hw = wave % NH;
   const int h = kvh * G + hg * NH + hw;                    // this wave's query head
   const int hs = share_group ? kvh : h;
-  const int tile = blockIdx.x * NT + wave / NH;            // this wave's 32-row tile
+  const int tile = static_cast<int>(bxy.x) * NT + wave / NH;   // this wave's 32-row tile
   const int row = tile * 32 + ql;
   const bool row_ok = row < nq;
   const int rowc = row_ok ? row : nq - 1;
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void attn_tile_dq_kernel(
   for (int x = tid; x < kBMaxKeyTiles / 32; x += 256) s_bits[x] = 0u;
   __syncthreads();
   {
-    const int64_t wg_row0 = static_cast<int64_t>(blockIdx.x) * NT * 32;
+    const int64_t wg_row0 = static_cast<int64_t>(bxy.x) * NT * 32;
     const int64_t wg_row1 = (wg_row0 + NT * 32 < nq ? wg_row0 + NT * 32 : nq) - 1;
     const int64_t p0 = q_pos0 + wg_row0, p1 = q_pos0 + wg_row1;
     for (int64_t t = (p0 / b) * b / kBT + tid; t <= p1 / kBT; t += 256) atomicOr(&s_bits[t >> 5], 1u << (t & 31));
@@ -405,8 +406,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_tile_dkdv_kernel(
   constexpr int kDB = D / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, ql = lane & 31;
-  const int kt = blockIdx.x;                         // key tile
-  const int bkv = blockIdx.y;
+  const uint2 bxy = xcd_block_xy();                 // XCD-aware order: a head's key tiles share an L2
+  const int kt = static_cast<int>(bxy.x);            // key tile
+  const int bkv = static_cast<int>(bxy.y);
   const int bi = bkv / Hkv, kvh = bkv % Hkv;
   const int G = Hq / Hkv;
   const int g = wave % G, stride0 = wave / G, nstride = 4 / G;

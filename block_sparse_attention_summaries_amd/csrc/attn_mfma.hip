@@ -73,13 +73,17 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
   const int hl = lane >> 5, ql = lane & 31;              // half-wave, query lane
   const int G = Hq / Hkv;
   const int hgroups = G / NH;
-  const int bz = blockIdx.y;
+  // XCD-aware order in the selected-block mode, where every tile of a head
+  // reads from the same keys (measured faster); the window mode keeps the
+  // dispatch order (measured faster there)
+  const uint2 bxy = kMix ? make_uint2(blockIdx.x, blockIdx.y) : xcd_block_xy();
+  const int bz = static_cast<int>(bxy.y);
   const int bi = bz / (Hkv * hgroups);
   const int kvh = (bz / hgroups) % Hkv;
   const int hg = bz % hgroups;
   const int h = kvh * G + hg * NH + (wave % NH);          // this wave's query head
   const int hs = share_group ? kvh : h;
-  const int tile = blockIdx.x * NT + wave / NH;            // this wave's 32-row tile
+  const int tile = static_cast<int>(bxy.x) * NT + wave / NH;   // this wave's 32-row tile
   const int row = tile * 32 + ql;
   const bool row_ok = row < nq;
   const int rowc = row_ok ? row : nq - 1;
@@ -102,7 +106,7 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
   for (int x = tid; x < 2 * (kMaxKeyTiles / 32); x += kThreads) (&s_bits[0][0])[x] = 0u;
   __syncthreads();
   // row range of the workgroup (positions)
-  const int64_t wg_row0 = static_cast<int64_t>(blockIdx.x) * NT * 32;
+  const int64_t wg_row0 = static_cast<int64_t>(bxy.x) * NT * 32;
   const int64_t wg_row1 = (wg_row0 + NT * 32 < nq ? wg_row0 + NT * 32 : nq) - 1;
   const int64_t p0 = q_pos0 + wg_row0, p1 = q_pos0 + wg_row1;
   if (local == 0) {

@@ -79,6 +79,25 @@ __device__ __forceinline__ float ld_f(const T* p) {
   return Elem<T>::to_float(*p);
 }
 
+// ------------------------------------------------------- XCD-aware order
+// Dispatch places workgroup w (linear, x fastest) on XCD w % 8, and each XCD
+// has its own L2.  Renumbering w so that XCD x runs one contiguous range of
+// logical workgroups (x per + min(x, rem) onward) lets neighbouring tiles,
+// which read the same keys, share that L2.  A bijection of [0, total).
+__device__ __forceinline__ uint32_t xcd_swizzle(uint32_t w, uint32_t total) {
+  constexpr uint32_t kXcds = 8;
+  const uint32_t per = total / kXcds, rem = total % kXcds;
+  const uint32_t x = w % kXcds, s = w / kXcds;
+  return x * per + (x < rem ? x : rem) + s;
+}
+
+// (blockIdx.x, blockIdx.y) of this workgroup's logical position under xcd_swizzle.
+__device__ __forceinline__ uint2 xcd_block_xy() {
+  const uint32_t w = blockIdx.y * gridDim.x + blockIdx.x;
+  const uint32_t l = xcd_swizzle(w, gridDim.x * gridDim.y);
+  return make_uint2(l % gridDim.x, l / gridDim.x);
+}
+
 // ------------------------------------------------------- fp8 summaries
 // OCP 8-bit floating point, E4M3 without infinities: sign, 4 exponent bits
 // biased by 7, 3 mantissa bits; exponent field 0 holds m/8 2^-6; S.1111.111
