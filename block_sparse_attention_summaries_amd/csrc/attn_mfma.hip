@@ -66,8 +66,9 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
   __shared__ uint32_t s_bits[2][kMaxKeyTiles / 32];
   __shared__ uint16_t s_list[2][kMaxKeyTiles];
   __shared__ int s_count[2];
-  __shared__ int32_t s_idx[4][32][kMaxSelK / 2 + 1];   // packed pairs of int16 units
-  __shared__ float s_lg[4][32][kMaxSelK];
+  // per wave (NW of them: with two, a workgroup fits four times in LDS)
+  __shared__ int32_t s_idx[NW][32][kMaxSelK / 2 + 1];   // packed pairs of int16 units
+  __shared__ float s_lg[NW][32][kMaxSelK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, ql = lane & 31;              // half-wave, query lane
