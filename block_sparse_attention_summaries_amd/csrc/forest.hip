@@ -464,71 +464,6 @@ __global__ __launch_bounds__(256) void forest_radius_final_kernel(const unsigned
 }
 
 // ---------------------------------------------------------------- select
-__device__ __forceinline__ uint64_t fs_orderable(double v) {
-  if (v == 0.0) v = 0.0;                       // +0 and -0 compare equal
-  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
-  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
-}
-
-// Top `want` of the wave's 4 x 64 (score, slot) pairs (slot = i * 64 + lane,
-// ok marks the valid ones), higher score first, lower slot on ties: a bitwise
-// search for the threshold over the scores' orderable bits below the common
-// prefix of the smallest and largest (ballot counts, stopping once the kept
-// set is decided), then every pair above it and the first ones equal to it in
-// slot order.  Sets taken[], returns how many.
-__device__ __forceinline__ int fs_top16(const double (&sc)[4], const bool (&ok)[4], int want, bool (&taken)[4]) {
-  uint64_t key[4];
-  int nv = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    key[i] = ok[i] ? fs_orderable(sc[i]) : 0ull;
-    nv += __popcll(__ballot(ok[i]));
-  }
-  const int kk = nv < want ? nv : want;
-  uint64_t t = ~0ull;
-  if (kk > 0) {
-    // every valid key shares the common prefix of the smallest and largest
-    uint64_t lo = ~0ull, hi = 0ull;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (ok[i]) {
-        lo = key[i] < lo ? key[i] : lo;
-        hi = key[i] > hi ? key[i] : hi;
-      }
-    }
-#pragma unroll
-    for (int o = kWave / 2; o >= 1; o >>= 1) {
-      const uint64_t ol = __shfl_xor(lo, o), oh = __shfl_xor(hi, o);
-      lo = ol < lo ? ol : lo;
-      hi = oh > hi ? oh : hi;
-    }
-    const int top = lo == hi ? -1 : 63 - __clzll(static_cast<long long>(lo ^ hi));
-    t = top < 0 ? hi : (hi & ~((2ull << top) - 1ull));
-    for (int bit = top; bit >= 0; --bit) {
-      const uint64_t cand = t | (1ull << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(key[i] >= cand));
-      if (cnt >= kk) {
-        t = cand;
-        if (cnt == kk) break;
-      }
-    }
-  }
-  int ngt = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) ngt += __popcll(__ballot(key[i] > t));
-  const int need = kk - ngt;
-  int eq_seen = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint64_t eq = __ballot(key[i] == t && key[i] != 0ull);
-    taken[i] = key[i] > t || (key[i] == t && key[i] != 0ull && eq_seen + lanes_below(eq) < need);
-    eq_seen += __popcll(eq);
-  }
-  return kk;
-}
-
 // One workgroup per (batch, selection head, query row): each half runs one
 // forest's beam search (its 128 threads score the up to 256 candidates of a
 // level, one wave keeps the best 16), the four waves share the re-rank (cells
@@ -698,7 +633,7 @@ __global__ __launch_bounds__(256) void forest_select_kernel(
         ok[i] = id[i] >= 0;
         sc[i] = s_sc[f][i * kWave + lane];
       }
-      fs_top16(sc, ok, kBeam, taken);
+      wave_top_f64x4(sc, ok, kBeam, taken);
       // new frontier in candidate (ascending id) order
       int kept = 0;
 #pragma unroll
@@ -806,7 +741,7 @@ __global__ __launch_bounds__(256) void forest_select_kernel(
     ok[i] = x < nreach;
     sc[i] = ok[i] ? s_lse[x] : -INFINITY;
   }
-  const int kk = fs_top16(sc, ok, K, taken);
+  const int kk = wave_top_f64x4(sc, ok, K, taken);
   const int64_t o = (static_cast<int64_t>(bh) * nq + row) * K;
   int kept = 0;
 #pragma unroll

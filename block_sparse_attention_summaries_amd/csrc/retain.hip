@@ -14,13 +14,14 @@
 //                         compaction.  Wave 0 then takes the top P of the four
 //                         lists (index order across waves too) and appends the
 //                         recent cells.
-//   select_subset_kernel  one wave per (batch, selection head, query row):
-//                         fp64 scores of the listed cells that are candidates
-//                         of the row (q_hat . kbar / sqrt(d), plus the erf
-//                         position bias), the gate over those cells, and the
-//                         top K by repeated arg-max (higher score, then lower
-//                         cell); the kept slots are written in list order,
-//                         which is ascending cell order.
+//   select_subset_kernel  one workgroup per (batch, selection head, query
+//                         row), a list slot per thread: fp64 scores of the
+//                         listed cells that are candidates of the row
+//                         (q_hat . kbar / sqrt(d), plus the erf position
+//                         bias), the gate over those cells, and the top K by
+//                         a threshold search over the scores' orderable bits
+//                         (higher score, then lower cell); the kept slots are
+//                         written in list order, which is ascending cell order.
 #include "spa_device.h"
 #include "spa_launch.h"
 
@@ -114,6 +115,8 @@ __global__ __launch_bounds__(256) void retain_cells_kernel(const float* __restri
 }
 
 // ---------------------------------------------------------------- select
+// One workgroup per (batch, selection head, query row); thread j scores list
+// slot j (all loads issued from clamped addresses before the arithmetic).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void select_subset_kernel(
     const T* __restrict__ q, const T* __restrict__ kbar, const float* __restrict__ max_norm,
@@ -121,110 +124,101 @@ __global__ __launch_bounds__(256) void select_subset_kernel(
     int64_t ccap, int b, int prefix_mode, int qblock, const float* __restrict__ erf_lambda,
     const float* __restrict__ erf_sigma, const int32_t* __restrict__ cells, const int32_t* __restrict__ count,
     int cap, int K, int gate, int32_t* __restrict__ idx, float* __restrict__ logg, int32_t* __restrict__ k_eff) {
+  static_assert(kSubsetMaxCap == 4 * kWave, "one list slot per thread");
   constexpr int kVec = Elem<T>::kVec;
-  __shared__ double s_q[4][D];
+  __shared__ double s_q[D];
+  __shared__ double s_sc[kSubsetMaxCap];
+  __shared__ int32_t s_cid[kSubsetMaxCap];
+  __shared__ double s_red[2][4];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int bh = blockIdx.y;
   const int bi = bh / Hsel, hs = bh % Hsel;
   const int G = Hq / Hkv;
   const int kvh = share_group ? hs : hs / G;
-  const int row = blockIdx.x * 4 + wave;
-  if (row >= nq) return;                       // whole wave leaves; no workgroup barrier below
+  const int row = blockIdx.x;
   const int64_t pos = q_pos0 + row;
   const int64_t ncand = prefix_mode == 0 ? pos / b : (static_cast<int64_t>(qblock) * (pos / qblock)) / b;
-
-  // q_hat in fp64 (mean of the group's heads, summed in head order)
-  const int gq = share_group ? G : 1;
-  const int h0 = share_group ? hs * G : hs;
-  for (int e = lane; e < D; e += kWave) {
-    double s = 0.0;
-    for (int g = 0; g < gq; ++g) s += static_cast<double>(ld_f(q + ((static_cast<int64_t>(bi) * Hq + h0 + g) * nq + row) * D + e));
-    s_q[wave][e] = s / static_cast<double>(gq);
-  }
-  wave_lds_sync();
-
-  // scores of this lane's list slots j = i * 64 + lane
   const int64_t hb = static_cast<int64_t>(bi) * Hkv + kvh;
+
+  // this slot's cell and its summary row (slot 0's cell stands in for empty slots)
   const int nl = count[hb];
   const int32_t* lst = cells + hb * cap;
-  const double inv_sqrt_d = 1.0 / sqrt(static_cast<double>(D));
+  const int j = tid;
+  const int c = j < nl && j < cap ? lst[j] : -1;
+  const bool ok = c >= 0 && c < ncand;
+  const int64_t cc = ok ? c : 0;
+  uint4 raw[D / kVec];
+  const uint4* kr = reinterpret_cast<const uint4*>(kbar + (hb * ccap + cc) * D);
+#pragma unroll
+  for (int v = 0; v < D / kVec; ++v) raw[v] = kr[v];
   const bool erf_on = erf_lambda != nullptr;
-  const double lam = erf_on ? static_cast<double>(erf_lambda[hs]) : 0.0;
-  const double sig = erf_on ? static_cast<double>(erf_sigma[hs]) : 1.0;
-  double sc[4];
-  int cid[4];
-  bool ok[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = i * kWave + lane;
-    const int c = j < nl && j < cap ? lst[j] : -1;
-    ok[i] = c >= 0 && c < ncand;
-    cid[i] = c;
-    double s = -INFINITY;
-    if (ok[i]) {
-      const T* kr = kbar + (hb * ccap + c) * D;
-      double dot = 0.0;
-#pragma unroll 4
-      for (int v = 0; v < D / kVec; ++v) {
-        float x[kVec];
-        Elem<T>::unpack(*reinterpret_cast<const uint4*>(kr + v * kVec), x);
-#pragma unroll
-        for (int t = 0; t < kVec; ++t) dot = fma(static_cast<double>(x[t]), s_q[wave][v * kVec + t], dot);
-      }
-      s = dot * inv_sqrt_d;
-      if (erf_on) {
-        const double ac = static_cast<double>(max_norm[hb * ccap + c]);
-        const double pc = static_cast<double>(centre[c]);
-        s += lam * ac * erf((static_cast<double>(pos) - pc) / (2.0 * sig));
-      }
+  const double ac = erf_on ? static_cast<double>(max_norm[hb * ccap + cc]) : 0.0;
+  const double pc = erf_on ? static_cast<double>(centre[cc]) : 0.0;
+
+  // q_hat in fp64 (mean of the group's heads, summed in head order)
+  if (wave == 0) {
+    const int gq = share_group ? G : 1;
+    const int h0 = share_group ? hs * G : hs;
+    for (int e = lane; e < D; e += kWave) {
+      double sq = 0.0;
+      for (int g = 0; g < gq; ++g)
+        sq += static_cast<double>(ld_f(q + ((static_cast<int64_t>(bi) * Hq + h0 + g) * nq + row) * D + e));
+      s_q[e] = sq / static_cast<double>(gq);
     }
-    sc[i] = s;
   }
-  // gate: LSE over the listed candidates
-  double m = -INFINITY;
-  int nv = 0;
+  __syncthreads();
+
+  const double inv_sqrt_d = 1.0 / sqrt(static_cast<double>(D));
+  double sv = -INFINITY;
+  if (ok) {
+    double dot = 0.0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m = ok[i] && sc[i] > m ? sc[i] : m;
-    nv += __popcll(__ballot(ok[i]));
+    for (int v = 0; v < D / kVec; ++v) {
+      float x[kVec];
+      Elem<T>::unpack(raw[v], x);
+#pragma unroll
+      for (int t = 0; t < kVec; ++t) dot = fma(static_cast<double>(x[t]), s_q[v * kVec + t], dot);
+    }
+    sv = dot * inv_sqrt_d;
+    if (erf_on) {
+      const double lam = static_cast<double>(erf_lambda[hs]);
+      const double sig = static_cast<double>(erf_sigma[hs]);
+      sv += lam * ac * erf((static_cast<double>(pos) - pc) / (2.0 * sig));
+    }
   }
+  s_sc[j] = sv;
+  s_cid[j] = ok ? c : -1;
+
+  // gate: LSE over the listed candidates (wave maxima and sums, then over the waves)
+  double m = sv;
   for (int off = 32; off >= 1; off >>= 1) {
     const double o = __shfl_xor(m, off);
     m = o > m ? o : m;
   }
-  double l = 0.0;
+  if (lane == 0) s_red[0][wave] = m;
+  __syncthreads();
+  m = s_red[0][0];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) l += ok[i] ? exp(sc[i] - m) : 0.0;
+  for (int w = 1; w < 4; ++w) m = s_red[0][w] > m ? s_red[0][w] : m;
+  double l = ok ? exp(sv - m) : 0.0;
   for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
-  const double lse = nv > 0 ? m + log(l) : 0.0;
+  if (lane == 0) s_red[1][wave] = l;
+  __syncthreads();
+  if (wave != 0) return;
+  l = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
 
-  // top K by repeated arg-max: higher score, then lower list slot (= lower cell)
-  const int kk = nv < K ? nv : K;
-  bool taken[4] = {false, false, false, false};   // at most kSubsetMaxCap = 4 x 64 listed cells
-  for (int t = 0; t < kk; ++t) {
-    double bv = -INFINITY;
-    int bj = 1 << 30;
+  // top K (higher score, then lower list slot = lower cell), kept in list order
+  double sc[4];
+  bool okv[4], taken[4];
+  int32_t cid[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = i * kWave + lane;
-      if (ok[i] && !taken[i] && (sc[i] > bv || (sc[i] == bv && j < bj))) {
-        bv = sc[i];
-        bj = j;
-      }
-    }
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double ov = __shfl_xor(bv, off);
-      const int oj = __shfl_xor(bj, off);
-      if (ov > bv || (ov == bv && oj < bj)) {
-        bv = ov;
-        bj = oj;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i * kWave + lane == bj) taken[i] = true;
+  for (int i = 0; i < 4; ++i) {
+    cid[i] = s_cid[i * kWave + lane];
+    okv[i] = cid[i] >= 0;
+    sc[i] = s_sc[i * kWave + lane];
   }
-  // kept slots in list order (ascending cells)
+  const int kk = wave_top_f64x4(sc, okv, K, taken);
+  const double lse = kk > 0 ? m + log(l) : 0.0;
   const int64_t o = (static_cast<int64_t>(bh) * nq + row) * K;
   int kept = 0;
 #pragma unroll
@@ -253,7 +247,7 @@ hipError_t launch_retain_cells(const float* max_norm, int B, int Hkv, int64_t cc
 template <typename T, int D>
 static hipError_t launch_subset_t(const SelectLaunch& p, const int32_t* cells, const int32_t* count, int cap,
                                   hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((p.nq + 3) / 4), static_cast<unsigned>(p.B * p.Hsel));
+  const dim3 grid(static_cast<unsigned>(p.nq), static_cast<unsigned>(p.B * p.Hsel));
   return launch(true, select_subset_kernel<T, D>, grid, dim3(256), st, static_cast<const T*>(p.q),
                 static_cast<const T*>(p.kbar), p.max_norm, p.centre, p.Hq, p.Hkv, p.Hsel, p.share_group, p.nq,
                 p.q_pos0, p.ccap, p.b, p.prefix_mode, p.qblock, p.erf_lambda, p.erf_sigma, cells, count, cap, p.K,

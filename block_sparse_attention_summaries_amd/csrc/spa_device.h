@@ -301,6 +301,73 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u)));
 }
 
+// ------------------------------------------------------- fp64 top-k of a wave
+__device__ __forceinline__ uint64_t orderable_f64(double v) {
+  if (v == 0.0) v = 0.0;                       // +0 and -0 compare equal
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// Top `want` of the wave's 4 x 64 (score, slot) pairs (slot = i * 64 + lane,
+// ok marks the valid ones), higher score first, lower slot on ties: a bitwise
+// search for the threshold over the scores' orderable bits below the common
+// prefix of the smallest and largest (ballot counts, stopping once the kept
+// set is decided), then every pair above it and the first ones equal to it in
+// slot order.  Sets taken[], returns how many.
+__device__ __forceinline__ int wave_top_f64x4(const double (&sc)[4], const bool (&ok)[4], int want, bool (&taken)[4]) {
+  uint64_t key[4];
+  int nv = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    key[i] = ok[i] ? orderable_f64(sc[i]) : 0ull;
+    nv += __popcll(__ballot(ok[i]));
+  }
+  const int kk = nv < want ? nv : want;
+  uint64_t t = ~0ull;
+  if (kk > 0) {
+    // every valid key shares the common prefix of the smallest and largest
+    uint64_t lo = ~0ull, hi = 0ull;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (ok[i]) {
+        lo = key[i] < lo ? key[i] : lo;
+        hi = key[i] > hi ? key[i] : hi;
+      }
+    }
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+      const uint64_t ol = __shfl_xor(lo, o), oh = __shfl_xor(hi, o);
+      lo = ol < lo ? ol : lo;
+      hi = oh > hi ? oh : hi;
+    }
+    const int top = lo == hi ? -1 : 63 - __clzll(static_cast<long long>(lo ^ hi));
+    t = top < 0 ? hi : (hi & ~((2ull << top) - 1ull));
+    for (int bit = top; bit >= 0; --bit) {
+      const uint64_t cand = t | (1ull << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+      if (cnt >= kk) {
+        t = cand;
+        if (cnt == kk) break;
+      }
+    }
+  }
+  int ngt = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ngt += __popcll(__ballot(key[i] > t));
+  const int need = kk - ngt;
+  int eq_seen = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint64_t eq = __ballot(key[i] == t && key[i] != 0ull);
+    taken[i] = key[i] > t || (key[i] == t && key[i] != 0ull && eq_seen + lanes_below(eq) < need);
+    eq_seen += __popcll(eq);
+  }
+  return kk;
+}
+
+
 // Top-k threshold of the wave's NV x 64 keys: returns t with
 // count(key > t) <= k <= count(key >= t), so that the keys > t plus the
 // first k - count(key > t) keys == t are exactly a top k (0xFFFFFFFF if
