@@ -86,8 +86,8 @@ int64_t forest_nodes(int64_t m) {
 // its members are then written in cell order from per-wave ballot masks
 // (chunks of 1024 cells, a prefix over chunks and waves).  Cells are held in
 // registers 16384 at a time.
-constexpr int kMemThreads = 1024;
-constexpr int kMemWaves = kMemThreads / kWave;
+constexpr int kMemThreads = kWgThreads;
+constexpr int kMemWaves = kWgWaves;
 
 __global__ __launch_bounds__(kMemThreads) void forest_members_kernel(
     const float* __restrict__ max_norm, int64_t ccap, int64_t n, int64_t NN, int d, int32_t* __restrict__ members,
@@ -131,63 +131,9 @@ __global__ __launch_bounds__(kMemThreads) void forest_members_kernel(
       }
     };
     load_span(0);
-    // 1. threshold: the largest t with at least ceil(n/2) norms at or above
-    // it; the search starts below the common prefix of the smallest and the
-    // largest norm
-    uint32_t lo = ~0u, hi = 0u;
-#pragma unroll
-    for (int j = 0; j < kRegs; ++j) {
-      if (j * kMemThreads + tid < n) {
-        lo = key[j] < lo ? key[j] : lo;
-        hi = key[j] > hi ? key[j] : hi;
-      }
-    }
-    for (int64_t c = kSpan + tid; c < n; c += kMemThreads) {
-      const uint32_t kv = orderable_f32(a[c]);
-      lo = kv < lo ? kv : lo;
-      hi = kv > hi ? kv : hi;
-    }
-#pragma unroll
-    for (int o = kWave / 2; o >= 1; o >>= 1) {
-      const uint32_t ol = __shfl_xor(lo, o), oh = __shfl_xor(hi, o);
-      lo = ol < lo ? ol : lo;
-      hi = oh > hi ? oh : hi;
-    }
-    if (lane == 0) {
-      s_lohi[0][wave] = lo;
-      s_lohi[1][wave] = hi;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < kMemWaves; ++w) {
-      lo = s_lohi[0][w] < lo ? s_lohi[0][w] : lo;
-      hi = s_lohi[1][w] > hi ? s_lohi[1][w] : hi;
-    }
-    const int kr = static_cast<int>((n + 1) / 2);
-    uint32_t t = hi;                           // every norm equal: hi is the threshold
-    if (lo != hi) {
-      const int top = 31 - __clz(lo ^ hi);     // highest bit where the norms differ
-      t = hi & ~((2u << top) - 1u);            // the common prefix: every norm is at or above it
-      for (int bit = top, it = 0; bit >= 0; --bit, ++it) {
-        const uint32_t cand = t | (1u << bit);
-        int cnt = 0;                           // wave-uniform: ballot counts
-#pragma unroll
-        for (int j = 0; j < kRegs; ++j) cnt += __popcll(__ballot(key[j] >= cand));
-        for (int64_t c0 = kSpan; c0 < n; c0 += kMemThreads) {
-          const int64_t c = c0 + tid;
-          cnt += __popcll(__ballot(c < n && orderable_f32(a[c < n ? c : n - 1]) >= cand));
-        }
-        if (lane == 0) s_part[it & 1][wave] = cnt;
-        __syncthreads();
-        int tot = 0;
-#pragma unroll
-        for (int w = 0; w < kMemWaves; ++w) tot += s_part[it & 1][w];
-        if (tot >= kr) {
-          t = cand;
-          if (tot == kr) break;
-        }
-      }
-    }
+    // 1. threshold: the largest t with at least ceil(n/2) norms at or above it
+    const uint32_t t = wg_kth_largest_f32<kRegs>(key, a, n, static_cast<int>((n + 1) / 2), &s_part[0][0],
+                                                 &s_lohi[0][0]);
     // 2. members in cell order
     int64_t base = 0;
     for (int64_t s0 = 0; s0 < n; s0 += kSpan) {

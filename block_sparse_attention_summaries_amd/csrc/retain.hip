@@ -6,14 +6,12 @@
 // Kept set of a (batch, kv head) with ncand prefix cells: the W most recent
 // cells plus the P older cells of largest max_norm, lower index first on
 // equal norms; ascending, -1 padded to W + P.
-//   retain_cells_kernel   one workgroup per (batch, kv head).  Wave w walks
-//                         its contiguous quarter of the older cells 256 at a
-//                         time and keeps a running top-P list (one record per
-//                         lane, in index order): running list + next 256
-//                         cells -> top P by a threshold search and an ordered
-//                         compaction.  Wave 0 then takes the top P of the four
-//                         lists (index order across waves too) and appends the
-//                         recent cells.
+//   retain_cells_kernel   one 1024-thread workgroup per (batch, kv head): the
+//                         P-th largest older norm by a bitwise threshold
+//                         search (workgroup ballot counts), then the older
+//                         cells above it and the first equal ones in cell
+//                         order by an ordered compaction, then the recent
+//                         cells.
 //   select_subset_kernel  one workgroup per (batch, selection head, query
 //                         row), a list slot per thread: fp64 scores of the
 //                         listed cells that are candidates of the row
@@ -27,91 +25,136 @@
 
 namespace spa {
 
-constexpr int kRetainMaxP = 64;     // running list: one record per lane
-constexpr int kSubsetMaxCap = 256;  // listed cells per head: four per lane
+constexpr int kSubsetMaxCap = 256;  // listed cells per head: one per thread
 
-// Ordered compaction of NV x 64 positions (position i * 64 + lane): keeps
-// keys > t and the first need_eq keys == t (keys 0 never), calling
-// emit(slot, i).  Returns the number kept.
-template <int NV, typename Emit>
-__device__ __forceinline__ int rt_select_ordered(const uint32_t (&key)[NV], uint32_t t, int need_eq, Emit&& emit) {
-  int kept = 0, eq_seen = 0;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const uint64_t eq = __ballot(key[i] == t && key[i] != 0u);
-    const bool take = key[i] > t || (key[i] == t && key[i] != 0u && eq_seen + lanes_below(eq) < need_eq);
-    const uint64_t tm = __ballot(take);
-    if (take) emit(kept + lanes_below(tm), i);
-    kept += __popcll(tm);
-    eq_seen += __popcll(eq);
-  }
-  return kept;
-}
-
-// Top-P of the wave's NV x 64 (key << 32 | cell) records into s_out[0 .. 63]
-// in position order (0 padded); returns the number kept.
-template <int NV>
-__device__ __forceinline__ int rt_top_p(const uint64_t (&r)[NV], int P, uint64_t* s_out) {
-  const int lane = threadIdx.x % kWave;
-  uint32_t key[NV];
-  int valid = 0;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    key[i] = static_cast<uint32_t>(r[i] >> 32);
-    valid += __popcll(__ballot(key[i] != 0u));
-  }
-  const int k = valid < P ? valid : P;
-  const uint32_t t = wave_kth_largest<NV>(key, k);
-  int ngt = 0;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) ngt += __popcll(__ballot(key[i] > t));
-  const int kept = rt_select_ordered<NV>(key, t, k - ngt, [&](int slot, int i) { s_out[slot] = r[i]; });
-  for (int x = kept + lane; x < kWave; x += kWave) s_out[x] = 0ull;
-  return kept;
-}
-
-__global__ __launch_bounds__(256) void retain_cells_kernel(const float* __restrict__ max_norm, int64_t ccap,
-                                                           int64_t ncand, int W, int P, int32_t* __restrict__ cells,
-                                                           int32_t* __restrict__ count) {
-  __shared__ uint64_t s_run[4][kWave];
+// One 1024-thread workgroup per (batch, kv head).  The older cells' norms
+// sit in registers 16384 at a time (cell s0 + j * 1024 + tid in key[j]); t is
+// the kr-th largest (kr = min(P, older cells)); every older cell above t is
+// kept, and the first kr - #(above t) cells equal to t in cell order; both
+// rank and position come from per-(chunk, wave) ballot counts and a prefix
+// over them, so the kept cells come out in cell order.
+__global__ __launch_bounds__(kWgThreads) void retain_cells_kernel(const float* __restrict__ max_norm, int64_t ccap,
+                                                                 int64_t ncand, int W, int P,
+                                                                 int32_t* __restrict__ cells,
+                                                                 int32_t* __restrict__ count) {
+  constexpr int kRegs = 16;
+  constexpr int64_t kSpan = static_cast<int64_t>(kWgThreads) * kRegs;
+  constexpr int kEnt = kRegs * kWgWaves;       // (chunk, wave) entries per span: 4 per lane of wave 0
+  static_assert(kEnt == 4 * kWave, "four entries per lane");
+  __shared__ int s_part[2 * kWgWaves];
+  __shared__ uint32_t s_lohi[2 * kWgWaves];
+  __shared__ int s_cnt[kEnt];
+  __shared__ int64_t s_base[kEnt];
+  __shared__ int64_t s_tot;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int64_t head = blockIdx.x;
   const float* a = max_norm + head * ccap;
   const int cap = W + P;
   const int64_t n_old = ncand > W ? ncand - W : 0;
-  const int64_t nch = (n_old + 255) / 256;
-  const int64_t ch0 = nch * wave / 4, ch1 = nch * (wave + 1) / 4;
-  uint64_t run = 0ull;
-  for (int64_t ch = ch0; ch < ch1; ++ch) {
-    uint64_t r[5];
-    r[0] = run;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t c = ch * 256 + i * kWave + lane;
-      const float v = a[c < n_old ? c : n_old - 1];
-      r[i + 1] = c < n_old ? (static_cast<uint64_t>(orderable_f32(v)) << 32) | static_cast<uint32_t>(c) : 0ull;
-    }
-    rt_top_p<5>(r, P, s_run[wave]);
-    wave_lds_sync();
-    run = s_run[wave][lane];
-    wave_lds_sync();
-  }
-  s_run[wave][lane] = run;
-  __syncthreads();
-  if (wave != 0) return;
-  // the four running lists in wave order are in cell order
-  uint64_t r2[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r2[i] = s_run[i][lane];
-  __shared__ uint64_t s_fin[kWave];
-  const int kept = rt_top_p<4>(r2, P, s_fin);
-  wave_lds_sync();
+  const int kr = static_cast<int>(n_old < P ? n_old : P);
   int32_t* out = cells + head * cap;
-  if (lane < kept) out[lane] = static_cast<int32_t>(static_cast<uint32_t>(s_fin[lane]));
+
+  // wave 0: exclusive prefix of the span's kEnt counts (entry e = chunk e / 16,
+  // wave e % 16, i.e. cell order) on top of `run`; the total into s_tot
+  auto scan_entries = [&](int64_t run) {
+    if (wave == 0) {
+      int v[4];
+      int sum = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = s_cnt[lane * 4 + r];
+        sum += v[r];
+      }
+      int incl = sum;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int up = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += up;
+      }
+      int64_t pre = run + incl - sum;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s_base[lane * 4 + r] = pre;
+        pre += v[r];
+      }
+      if (lane == kWave - 1) s_tot = incl;
+    }
+    __syncthreads();
+  };
+
+  int64_t kept = 0;
+  if (kr > 0) {
+    uint32_t key[kRegs];                       // 0 marks a slot past the older cells
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {          // clamped, so the loads issue together
+      const int64_t c = j * kWgThreads + tid;
+      const uint32_t kv = orderable_f32(a[c < n_old ? c : n_old - 1]);
+      key[j] = c < n_old ? kv : 0u;
+    }
+    const uint32_t t = wg_kth_largest_f32<kRegs>(key, a, n_old, kr, s_part, s_lohi);
+    // cells above t
+    int gt = 0;
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) gt += __popcll(__ballot(key[j] > t));
+    for (int64_t c0 = kSpan; c0 < n_old; c0 += kWgThreads) {
+      const int64_t c = c0 + tid;
+      gt += __popcll(__ballot(c < n_old && orderable_f32(a[c < n_old ? c : n_old - 1]) > t));
+    }
+    if (lane == 0) s_part[wave] = gt;
+    __syncthreads();
+    int ngt = 0;
+#pragma unroll
+    for (int w = 0; w < kWgWaves; ++w) ngt += s_part[w];
+    const int need_eq = kr - ngt;              // cells equal to t still to keep, lowest first
+    int64_t eq_run = 0;
+    for (int64_t s0 = 0; s0 < n_old; s0 += kSpan) {
+      if (s0 > 0) {
+#pragma unroll
+        for (int j = 0; j < kRegs; ++j) {
+          const int64_t c = s0 + j * kWgThreads + tid;
+          const uint32_t kv = orderable_f32(a[c < n_old ? c : n_old - 1]);
+          key[j] = c < n_old ? kv : 0u;
+        }
+      }
+      // ranks among the cells equal to t
+#pragma unroll
+      for (int j = 0; j < kRegs; ++j) {
+        const int ce = __popcll(__ballot(key[j] == t));
+        if (lane == 0) s_cnt[j * kWgWaves + wave] = ce;
+      }
+      __syncthreads();
+      scan_entries(eq_run);
+      bool keep[kRegs];
+#pragma unroll
+      for (int j = 0; j < kRegs; ++j) {
+        const uint64_t me = __ballot(key[j] == t);
+        const int64_t rank = s_base[j * kWgWaves + wave] + lanes_below(me);
+        keep[j] = key[j] > t || (key[j] == t && rank < need_eq);
+      }
+      eq_run += s_tot;
+      __syncthreads();                         // ranks read before the counts are rewritten
+      // positions of the kept cells
+#pragma unroll
+      for (int j = 0; j < kRegs; ++j) {
+        const int ck = __popcll(__ballot(keep[j]));
+        if (lane == 0) s_cnt[j * kWgWaves + wave] = ck;
+      }
+      __syncthreads();
+      scan_entries(kept);
+#pragma unroll
+      for (int j = 0; j < kRegs; ++j) {
+        const uint64_t mk = __ballot(keep[j]);
+        if (keep[j]) out[s_base[j * kWgWaves + wave] + lanes_below(mk)] = static_cast<int32_t>(s0 + j * kWgThreads + tid);
+      }
+      kept += s_tot;
+      __syncthreads();                         // bases read before the next span rewrites them
+    }
+  }
+  // the W recent cells, then padding
   const int64_t nrec = ncand - n_old;
-  for (int x = lane; x < nrec; x += kWave) out[kept + x] = static_cast<int32_t>(n_old + x);
-  for (int x = kept + static_cast<int>(nrec) + lane; x < cap; x += kWave) out[x] = -1;
-  if (lane == 0) count[head] = kept + static_cast<int>(nrec);
+  for (int64_t x = tid; x < nrec; x += kWgThreads) out[kept + x] = static_cast<int32_t>(n_old + x);
+  for (int64_t x = kept + nrec + tid; x < cap; x += kWgThreads) out[x] = -1;
+  if (tid == 0) count[head] = static_cast<int32_t>(kept + nrec);
 }
 
 // ---------------------------------------------------------------- select
@@ -240,7 +283,7 @@ __global__ __launch_bounds__(256) void select_subset_kernel(
 
 hipError_t launch_retain_cells(const float* max_norm, int B, int Hkv, int64_t ccap, int64_t ncand, int W, int P,
                                int32_t* cells, int32_t* count, hipStream_t st) {
-  return launch(true, retain_cells_kernel, dim3(static_cast<unsigned>(B * Hkv)), dim3(256), st, max_norm, ccap,
+  return launch(true, retain_cells_kernel, dim3(static_cast<unsigned>(B * Hkv)), dim3(kWgThreads), st, max_norm, ccap,
                 ncand, W, P, cells, count);
 }
 

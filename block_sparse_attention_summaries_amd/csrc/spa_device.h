@@ -367,6 +367,80 @@ __device__ __forceinline__ int wave_top_f64x4(const double (&sc)[4], const bool 
   return kk;
 }
 
+// ------------------------------------------- k-th largest of a workgroup
+// Workgroups of 1024 threads holding kRegs keys each in registers (cell
+// j * 1024 + tid in key[j], 0 past the n cells); cells beyond the registers
+// are read from `a` (fp32, through orderable_f32).  Returns the largest t
+// with at least kr (1 <= kr <= n) keys at or above it: a bitwise search below
+// the common prefix of the smallest and largest key, counts summed over the
+// workgroup from ballots, stopping once exactly kr keys are at or above the
+// candidate.  s_part: 2 x 16 ints, s_lohi: 2 x 16 words of LDS.
+constexpr int kWgThreads = 1024;
+constexpr int kWgWaves = kWgThreads / kWave;
+
+template <int kRegs>
+__device__ inline uint32_t wg_kth_largest_f32(const uint32_t (&key)[kRegs], const float* __restrict__ a, int64_t n,
+                                              int kr, int* s_part, uint32_t* s_lohi) {
+  constexpr int64_t kSpan = static_cast<int64_t>(kWgThreads) * kRegs;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  uint32_t lo = ~0u, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < kRegs; ++j) {
+    if (j * kWgThreads + tid < n) {
+      lo = key[j] < lo ? key[j] : lo;
+      hi = key[j] > hi ? key[j] : hi;
+    }
+  }
+  for (int64_t c = kSpan + tid; c < n; c += kWgThreads) {
+    const uint32_t kv = orderable_f32(a[c]);
+    lo = kv < lo ? kv : lo;
+    hi = kv > hi ? kv : hi;
+  }
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) {
+    const uint32_t ol = __shfl_xor(lo, o), oh = __shfl_xor(hi, o);
+    lo = ol < lo ? ol : lo;
+    hi = oh > hi ? oh : hi;
+  }
+  if (lane == 0) {
+    s_lohi[wave] = lo;
+    s_lohi[kWgWaves + wave] = hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kWgWaves; ++w) {
+    lo = s_lohi[w] < lo ? s_lohi[w] : lo;
+    hi = s_lohi[kWgWaves + w] > hi ? s_lohi[kWgWaves + w] : hi;
+  }
+  uint32_t t = hi;                             // every key equal: hi is the threshold
+  if (lo != hi) {
+    const int top = 31 - __clz(lo ^ hi);       // highest bit where the keys differ
+    t = hi & ~((2u << top) - 1u);              // the common prefix: every key is at or above it
+    for (int bit = top, it = 0; bit >= 0; --bit, ++it) {
+      const uint32_t cand = t | (1u << bit);
+      int cnt = 0;                             // wave-uniform: ballot counts
+#pragma unroll
+      for (int j = 0; j < kRegs; ++j) cnt += __popcll(__ballot(key[j] >= cand));
+      for (int64_t c0 = kSpan; c0 < n; c0 += kWgThreads) {
+        const int64_t c = c0 + tid;
+        cnt += __popcll(__ballot(c < n && orderable_f32(a[c < n ? c : n - 1]) >= cand));
+      }
+      if (lane == 0) s_part[(it & 1) * kWgWaves + wave] = cnt;
+      __syncthreads();
+      int tot = 0;
+#pragma unroll
+      for (int w = 0; w < kWgWaves; ++w) tot += s_part[(it & 1) * kWgWaves + w];
+      if (tot >= kr) {
+        t = cand;
+        if (tot == kr) break;
+      }
+    }
+  }
+  __syncthreads();                             // s_part / s_lohi free for the caller
+  return t;
+}
+
+
 
 // Top-k threshold of the wave's NV x 64 keys: returns t with
 // count(key > t) <= k <= count(key >= t), so that the keys > t plus the
