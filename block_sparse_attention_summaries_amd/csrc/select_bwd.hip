@@ -150,7 +150,8 @@ __global__ __launch_bounds__(256, 2) void select_bwd_rows_kernel(
   const int64_t pos = q_pos0 + rowc;
   const int lb = __builtin_ctz(b);          // b is a power of two
   const int ncand = row_ok ? static_cast<int>(pos >> lb) : 0;
-  const int last_row = ((blockIdx.x * 4 + 4) * 32 < nq ? (blockIdx.x * 4 + 4) * 32 : nq) - 1;
+  const int row_end = (static_cast<int>(blockIdx.x) * 4 + 4) * 32;
+  const int last_row = (row_end < nq ? row_end : nq) - 1;
   const int wg_cand = static_cast<int>((q_pos0 + last_row) >> lb);
   const __bf16* kb = kbar + (static_cast<int64_t>(bi) * Hkv + kvh) * ccap * D;
   const int64_t so = ((static_cast<int64_t>(bi) * Hsel + hs) * nq + rowc) * K;

@@ -17,7 +17,9 @@ stand in for them):
   train           batch 4, n=8192, 32 q / 8 kv heads, d=128, bf16, b=64, K=16,
                   gate on, upstream gradient dO ~ N(0, 1)
 Decode context: L = n + t tokens with the current block full by default
-(t = b), the query at position L - 1.
+(t = b), the query at position L - 1.  kind="cell_decode" (a prefill_cells
+geometry) gives one query after n + b tokens, as the FS-L / FS-B decode
+steps take it.
 """
 from __future__ import annotations
 
@@ -90,6 +92,10 @@ def make_inputs(cfg: dict) -> dict:
         L = cfg["n"] + cfg.get("t", cfg["b"])
         nq = 1
         q_pos0 = L - 1
+    elif cfg["kind"] == "cell_decode":           # one query after n + b tokens (cell-routing decode)
+        L = cfg["n"] + cfg["b"]
+        nq = 1
+        q_pos0 = L - 1
     else:
         L = cfg["n"]
         nq = L
@@ -105,7 +111,7 @@ def make_inputs(cfg: dict) -> dict:
     if cfg.get("proj"):
         out["proj_w"] = (rng.standard_normal((d, d), dtype=np.float32)
                          * np.float32(1.0 / np.sqrt(d))).astype(np.float32)
-    if cfg["kind"] == "prefill":
+    if cfg["kind"] in ("prefill", "cell_decode"):
         out["erf_lambda"] = rng.random((Hq,), dtype=np.float32)
         out["erf_sigma"] = np.full((Hq,), cfg["sigma"], dtype=np.float32)
         out["alpha"] = rng.random((Hq,), dtype=np.float32)

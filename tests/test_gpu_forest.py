@@ -115,3 +115,38 @@ def test_fsb_decode_step_end_to_end():
     e = rel_err(host(o), o_o)
     _say(f"  o rel err {e:.2e}")
     assert e <= 2e-2
+
+
+def test_fsb_decode_512k_full_size():
+    """The FS-B decode step as the benchmark times it: forests over the 16384
+    prefix cells of a 512K context, 16 heads, d = 64, one query after the last
+    full cell; beam search, re-rank and the two-branch attention against the
+    oracle."""
+    cfg = config("prefill_cells", kind="cell_decode", n=524288, seed=163)
+    _say("[fsb decode] 512K full size, 16 heads")
+    x = make_inputs(cfg)
+    b, qb, K, L, q0 = cfg["b"], cfg["qblock"], cfg["K"], x["L"], x["q_pos0"]
+    n = (qb * (q0 // qb)) // b
+    kb, mx, ce, fo, fg = _build(cfg, x, n)
+    lam, sig = x["erf_lambda"], x["erf_sigma"]
+    ora = oracle.forest_select(x["q"], kb, mx, ce, x["k"], fo, n, Hkv=cfg["Hkv"], b=b, K=K, q_pos0=q0,
+                               share_group=False, erf_lambda=lam, erf_sigma=sig)
+    forest = {k: dev(v) for k, v in fo.items()}
+    kd, vd, qd = dev(x["k"]), dev(x["v"]), dev(x["q"])
+    idx, keff = ops.sparse_forest_select(qd, dev(kb), dev(mx), dev(ce), kd, forest, n, Hkv=cfg["Hkv"], b=b, K=K,
+                                         q_pos0=q0, prefix_mode=1, qblock=qb, share_group=False,
+                                         erf_lambda=dev(lam), erf_sigma=dev(sig))
+    akw = dict(b=b, K=K, q_pos0=q0, share_group=False, local=1, window=cfg["window"], prefix_mode=1, qblock=qb)
+    o, _ = ops.sparse_attn_fwd(qd, kd, vd, idx, None, alpha=dev(x["alpha"]), **akw)
+    torch.cuda.synchronize()
+    idx = host(idx)
+    ex = check_indices(idx, ora)
+    _say(f"  exempt rows {ex}")
+    assert np.array_equal(host(keff), np.minimum(K, np.sum(ora["idx"] >= 0, axis=-1)))
+    o_o, _ = oracle.attn_fwd(x["q"], x["k"], x["v"], ora["idx"], None, alpha=x["alpha"], **akw)
+    match = np.all(idx == ora["idx"], axis=-1)[:, :, 0]
+    for h in range(cfg["Hq"]):
+        if match[0, h]:
+            e = rel_err(host(o)[:, h:h + 1], o_o[:, h:h + 1])
+            assert e <= 2e-2, (h, e)
+

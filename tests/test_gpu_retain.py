@@ -93,9 +93,21 @@ def test_fsl_decode_step_end_to_end():
     alpha; GPU chain against the oracle chain."""
     cfg = config("prefill_cells", n=65536, Hq=4, Hkv=4, seed=98)
     x = make_inputs(cfg)
-    b, qb, K, L = cfg["b"], cfg["qblock"], cfg["K"], x["L"]
-    pos = L - 1
-    q1 = np.ascontiguousarray(x["q"][:, :, pos:pos + 1])
+    pos = x["L"] - 1
+    _fsl_step(cfg, x, np.ascontiguousarray(x["q"][:, :, pos:pos + 1]), pos)
+
+
+def test_fsl_decode_512k_full_size():
+    """The FS-L decode step as the benchmark times it: 512K tokens (16384
+    cells), 16 heads, d = 64, one query after the last full cell."""
+    cfg = config("prefill_cells", kind="cell_decode", n=524288, seed=99)
+    _say("[fsl decode] 512K full size, 16 heads")
+    x = make_inputs(cfg)
+    _fsl_step(cfg, x, x["q"], x["q_pos0"])
+
+
+def _fsl_step(cfg, x, q1, pos):
+    b, qb, K = cfg["b"], cfg["qblock"], cfg["K"]
     ex, (kb, mx, ce, cells_o, count_o, ora) = _fs_case(cfg, x, False, False, rows_q=q1, q_pos0=pos)
     ncand = (qb * (pos // qb)) // b
     akw = dict(b=b, K=K, q_pos0=pos, share_group=False, local=1, window=cfg["window"], prefix_mode=1, qblock=qb)
