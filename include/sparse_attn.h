@@ -102,7 +102,12 @@ int spa_abi_version(void);
  * call whether or not it launches.  Do not use under graph capture.
  * Kernels per call: summaries 1; score_select 2 on the decode path (chunk
  * scoring, merge), else 1; attn_fwd 2 on the decode path (tile partials,
- * combine), else 1; attn_bwd 3 (D, dq and dg, dk and dv).
+ * combine), else 1; attn_bwd 3 (D, dq and dg, dk and dv); decode_step 3
+ * (chunk scoring, merge + attention partials, combine), or the kernels of
+ * score_select then attn_fwd where the merge is not folded in; forest_build
+ * 4 plus one per forest level above the first; forest_select, retain_cells,
+ * score_select_subset, quantize / dequantize_summaries_fp8 1; select_bwd one
+ * per stage it runs.
  * Returns SPA_ERR_INVALID_ARG if count < 0 or events is NULL with count > 0. */
 int spa_profile_next_call(void **events, int count);
 
@@ -299,8 +304,10 @@ int sparse_decode_step_paged(const spa_decode_args *a, const spa_kv_pages *pages
  * plus the P older cells of largest max_norm (lower index first on equal
  * norms), min(ncand, W + P) cells in all.  max_norm: [B, Hkv, ccap] fp32 as
  * sparse_block_summaries writes it.  Outputs: cells [B, Hkv, W + P] int32,
- * ascending, -1 padded; count [B, Hkv] int32.  P <= 64, 1 <= W + P <= 256.
- * No workspace.  Query-independent: run it when a cell closes.
+ * ascending, -1 padded; count [B, Hkv] int32 (caller-owned device buffers).
+ * P <= 64, 1 <= W + P <= 256, else SPA_ERR_UNSUPPORTED; SPA_ERR_INVALID_ARG
+ * on null pointers or ncand outside [0, ccap].  No workspace.
+ * Query-independent: run it when a cell closes.
  */
 int sparse_retain_cells(const float *max_norm, int B, int Hkv, int64_t ccap, int64_t ncand,
                         int W, int P, int32_t *cells, int32_t *count, spa_stream_t stream);
@@ -312,8 +319,9 @@ int sparse_retain_cells(const float *max_norm, int B, int Hkv, int64_t ccap, int
  * [B, Hkv], as sparse_retain_cells writes them) that are candidates of the
  * row, and the gate's LSE runs over those cells only.  Scores are formed in
  * fp64 (q_hat . kbar / sqrt(d) plus the erf position bias).  Same outputs and
- * argument struct as sparse_score_select; no projection (proj_w must be
- * NULL); 1 <= cap <= 256.  No workspace.
+ * argument struct (and checks) as sparse_score_select; a projection, fp8
+ * summaries or cap outside 1..256 give SPA_ERR_UNSUPPORTED, null cells /
+ * count SPA_ERR_INVALID_ARG.  No workspace.
  */
 int sparse_score_select_subset(const spa_select_args *a, const int32_t *cells,
                                const int32_t *count, int cap, spa_stream_t stream);
@@ -355,8 +363,10 @@ size_t sparse_forest_workspace_bytes(int B, int Hkv, int d, int64_t n);
 /* sparse_forest_build -- both forests of every (batch, kv head) over the n
  * prefix cells 0 .. n-1, from the cell summaries (kbar [B, Hkv, ccap, d] in
  * dtype, max_norm [B, Hkv, ccap], centre [ccap], as sparse_block_summaries
- * writes them).  1 <= n <= ccap.  Query-independent: build when a query
- * block's prefix grows. */
+ * writes them).  1 <= n <= ccap (else SPA_ERR_INVALID_ARG, as are null
+ * arrays); B Hkv <= 65535; the workspace must hold
+ * sparse_forest_workspace_bytes (else SPA_ERR_WORKSPACE).  Query-independent:
+ * build when a query block's prefix grows. */
 int sparse_forest_build(const void *kbar, int dtype, const float *max_norm, const float *centre,
                         int B, int Hkv, int d, int64_t ccap, int64_t n, const spa_forest *forest,
                         void *workspace, size_t ws_bytes, spa_stream_t stream);
@@ -367,7 +377,9 @@ int sparse_forest_build(const void *kbar, int dtype, const float *max_norm, cons
  * gate NONE, no projection, K <= 16, b in {16, 32, 64}; every row must have
  * exactly the n forest cells as candidates (same query block).  Writes idx
  * (ascending, -1 padded) and k_eff; logg is not written.  Scores in fp64.
- * No workspace. */
+ * A gate, a projection, fp8 summaries, K > 16 or another b give
+ * SPA_ERR_UNSUPPORTED; rows whose candidates are not the n cells, or L < n b,
+ * SPA_ERR_INVALID_ARG.  No workspace. */
 int sparse_forest_select(const spa_select_args *a, const void *k, int64_t L,
                          const spa_forest *forest, int64_t n, spa_stream_t stream);
 
