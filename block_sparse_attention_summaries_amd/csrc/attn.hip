@@ -798,7 +798,7 @@ static bool use_decode_mix(const AttnLaunch& p) {
 
 size_t attn_fwd_workspace_bytes(const AttnLaunch& p) {
   const bool mix = use_decode_mix(p);
-  if (!use_decode_attn(p) && !mix) return 0;
+  if (!use_decode_attn(p) && !mix) return attn_tile_fwd_supported(p) ? attn_tile_fwd_workspace_bytes(p) : 0;
   const size_t heads = static_cast<size_t>(p.B) * p.Hsel;
   const size_t ntiles = mix ? static_cast<size_t>(mix_tiles(p)) : static_cast<size_t>(p.K + 1) * decode_tpu(p);
   const size_t hpw = heads_per_wg(p);
@@ -940,7 +940,7 @@ hipError_t launch_attn_fwd(const AttnLaunch& p, void* ws, hipStream_t st) {
     if (p.dtype == 1) return p.d == 64 ? launch_decode_mix_t<bf16_t, 64>(p, ws, st) : launch_decode_mix_t<bf16_t, 128>(p, ws, st);
     return p.d == 64 ? launch_decode_mix_t<float, 64>(p, ws, st) : launch_decode_mix_t<float, 128>(p, ws, st);
   }
-  if (attn_tile_fwd_supported(p)) return launch_attn_tile_fwd(p, st);
+  if (attn_tile_fwd_supported(p)) return launch_attn_tile_fwd(p, ws, st);
   if (p.dtype == 1) return p.d == 64 ? launch_rows_fwd_t<bf16_t, 64>(p, st) : launch_rows_fwd_t<bf16_t, 128>(p, st);
   return p.d == 64 ? launch_rows_fwd_t<float, 64>(p, st) : launch_rows_fwd_t<float, 128>(p, st);
 }

@@ -55,13 +55,316 @@ struct TileSmem {
 // their log gates, read with a cursor as key tiles ascend.
 constexpr int kMaxSelK = 32;
 
+// ------------------------------------------------- routed cells, cell-major
+// Mix mode (routed cells + window) computes branch L per cell instead of per
+// row tile: a row tile's union of selected cells is ~10x the 4 a row reads,
+// while a cell's selecting rows fill whole 32-row tiles.  fwd_mark_kernel
+// sets one bit per (selection head, cell, row) for "the row selected the
+// cell"; attn_cell_partial_kernel takes one cell of one kv head per workgroup
+// (its K rows and V^T in LDS once), lists the selecting rows 32 at a time in
+// row order, and writes for each (row, slot of the cell in the row's
+// selection) the softmax of the row over the cell's keys: o normalised (bf16)
+// and (max, sum) in the log2 domain.  The tile kernel then runs the window
+// branch only and merges a row's partials into o_L before the mix.
+
+// One workgroup per (selection head, 256 rows = 8 bitmap words): the slice
+// [cell][8 words] is built in LDS (atomics stay on chip) and written whole, so
+// every word of the bitmap is written and no clearing pass is needed.
+constexpr int kMarkWords = 8;
+__global__ __launch_bounds__(256) void fwd_mark_kernel(const int32_t* __restrict__ idx, int nq, int64_t q_pos0, int b,
+                                                       int prefix_mode, int qblock, int K, int64_t nblk, int nw,
+                                                       uint32_t* __restrict__ bits) {
+  __shared__ uint32_t s_w[kMaxKeyTiles * kMarkWords];   // nblk <= kMaxKeyTiles (cells of >= 32 keys)
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int w0 = blockIdx.x * kMarkWords;
+  for (int x = tid; x < nblk * kMarkWords; x += 256) s_w[x] = 0u;
+  __syncthreads();
+  const int row = w0 * 32 + tid;
+  if (row < nq) {
+    const int64_t ncand = num_candidates(q_pos0 + row, b, prefix_mode, qblock);
+    const int32_t* ir = idx + (bh * nq + row) * K;
+    for (int t = 0; t < K; ++t) {
+      const int32_t c = ir[t];
+      if (c >= 0 && c < ncand && c < nblk) atomicOr(&s_w[c * kMarkWords + (tid >> 5)], 1u << (tid & 31));
+    }
+  }
+  __syncthreads();
+  for (int x = tid; x < nblk * kMarkWords; x += 256) {
+    const int c = x / kMarkWords, j = x % kMarkWords;
+    if (w0 + j < nw) bits[(bh * nblk + c) * nw + w0 + j] = s_w[x];
+  }
+}
+
+// Work items: a cell's selecting rows in chunks of kCellItem (row order).
+// cell_count_kernel: one wave per (selection head, cell) counts its rows;
+// cell_items_kernel (one workgroup) turns the counts into the item list
+// (entry e = head * ncell + cell, chunk j) and its length.
+constexpr int kCellItem = 128;
+constexpr int kMaxWpl = (kMaxKeyTiles * kKT / 32 + 63) / 64;   // bitmap words per lane: nq <= L <= 65536
+
+__global__ __launch_bounds__(256) void cell_count_kernel(const uint32_t* __restrict__ bits, int64_t nblk, int nw,
+                                                         int64_t ncell, int64_t heads, int32_t* __restrict__ cnt) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;   // head * ncell + cell
+  if (e >= heads * ncell) return;                // whole wave leaves
+  const int64_t bh = e / ncell, c = e % ncell;
+  const uint32_t* brow = bits + (bh * nblk + c) * nw;
+  int n = 0;
+  for (int w = lane; w < nw; w += kWave) n += __popc(brow[w]);
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) n += __shfl_xor(n, o);
+  if (lane == 0) cnt[e] = n;
+}
+
+__global__ __launch_bounds__(1024) void cell_items_kernel(const int32_t* __restrict__ cnt, int64_t nent,
+                                                          int2* __restrict__ items, int32_t* __restrict__ nitems) {
+  constexpr int kPer = 16;                      // entries loaded together per thread
+  __shared__ int32_t s_wave[16];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int64_t per = (nent + 1023) / 1024;
+  const int64_t e0 = tid * per, e1 = e0 + per < nent ? e0 + per : nent;
+  int32_t mine = 0;
+  for (int64_t b0 = e0; b0 < e1; b0 += kPer) {
+    int32_t cv[kPer];
+#pragma unroll
+    for (int x = 0; x < kPer; ++x) {
+      const int32_t ld = cnt[b0 + x < e1 ? b0 + x : e1 - 1];
+      cv[x] = b0 + x < e1 ? ld : 0;
+    }
+#pragma unroll
+    for (int x = 0; x < kPer; ++x) mine += (cv[x] + kCellItem - 1) / kCellItem;
+  }
+  // exclusive prefix of the threads' item counts: in the wave, then over the 16 waves
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int up = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += up;
+  }
+  if (lane == kWave - 1) s_wave[wave] = incl;
+  __syncthreads();
+  int32_t pos = incl - mine;
+  for (int w = 0; w < wave; ++w) pos += s_wave[w];
+  for (int64_t b0 = e0; b0 < e1; b0 += kPer) {
+    int32_t cv[kPer];
+#pragma unroll
+    for (int x = 0; x < kPer; ++x) {
+      const int32_t ld = cnt[b0 + x < e1 ? b0 + x : e1 - 1];
+      cv[x] = b0 + x < e1 ? ld : 0;
+    }
+#pragma unroll
+    for (int x = 0; x < kPer; ++x) {
+      const int32_t m = (cv[x] + kCellItem - 1) / kCellItem;
+      for (int32_t jj = 0; jj < m; ++jj) items[pos + jj] = make_int2(static_cast<int>(b0 + x), jj);
+      pos += m;
+    }
+  }
+  if (tid == 1023) {
+    int32_t tot = 0;
+    for (int w = 0; w < 16; ++w) tot += s_wave[w];
+    *nitems = tot;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_cell_partial_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const int32_t* __restrict__ idx, const float* __restrict__ logg, const uint32_t* __restrict__ bits,
+    const int2* __restrict__ items, const int32_t* __restrict__ nitems, int64_t ncell, int Hq, int Hkv, int Hsel,
+    int nq, int64_t L, int b, int K, int64_t nblk, int nw, __bf16* __restrict__ cell_o, float2* __restrict__ cell_ml) {
+  __shared__ TileSmem<D> sm;           // the cell's key tiles: b / 32 of them (b <= 64)
+  __shared__ int s_rows[kCellItem];
+  __shared__ int s_n;
+  constexpr int kKS = D / 16;
+  constexpr int kDB = D / 32;
+  constexpr int kStage = 2 * kKT * (D / 8) / 256;   // 16-byte vectors per thread for two key tiles
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, ql = lane & 31;
+  if (static_cast<int>(blockIdx.x) >= *nitems) return;   // whole workgroup: past the item list
+  const int2 item = items[blockIdx.x];
+  const int64_t e = item.x;
+  const int chunk = item.y;
+  const int64_t bkv = e / ncell;                 // Hsel == Hkv here: the selection head is the kv head
+  const int c = static_cast<int>(e % ncell);
+  const int bi = static_cast<int>(bkv / Hkv), kvh = static_cast<int>(bkv % Hkv);
+  const int G = Hq / Hkv;                        // 1, 2 or 4; the group shares the selection when G > 1
+  const int g = wave % G, stride0 = wave / G, nstride = 4 / G;
+  const int h = kvh * G + g;
+  const int hs = kvh;
+  const int ntile = b / kKT;
+  const int64_t kvbase = (static_cast<int64_t>(bi) * Hkv + kvh) * L * D;
+  const float scale2 = kLog2e / sqrtf(static_cast<float>(D));
+  const uint32_t* brow = bits + ((static_cast<int64_t>(bi) * Hsel + hs) * nblk + c) * nw;
+
+  // the cell's K and V rows, loaded while the item's rows are found (clamped addresses)
+  uint4 kv_k[kStage], kv_v[kStage];
+#pragma unroll
+  for (int i = 0; i < kStage; ++i) {
+    const int x = tid + 256 * i;
+    const int kr = x / (D / 8), cv = x % (D / 8);  // key row of the cell (two tiles' worth), column group
+    int64_t key = static_cast<int64_t>(c) * b + (kr < b ? kr : b - 1);
+    key = key < L ? key : L - 1;
+    kv_k[i] = *reinterpret_cast<const uint4*>(k + kvbase + key * D + cv * 8);
+    kv_v[i] = *reinterpret_cast<const uint4*>(v + kvbase + key * D + cv * 8);
+  }
+  // rows of rank [chunk * kCellItem, +kCellItem) among the cell's selecting rows
+  // (row order): wave 0, each lane a contiguous run of bitmap words
+  if (wave == 0) {
+    // lane l holds words l * wpl .. of the cell's row (nw <= 64 * kMaxWpl), loaded together
+    const int wpl = (nw + kWave - 1) / kWave;
+    const int w0 = lane * wpl;
+    uint32_t wd[kMaxWpl];
+    int cnt = 0;
+#pragma unroll
+    for (int x = 0; x < kMaxWpl; ++x) {
+      const int w = w0 + x;
+      const uint32_t ld = brow[w < nw ? w : nw - 1];    // unconditional (clamped): the loads issue together
+      wd[x] = (x < wpl && w < nw) ? ld : 0u;
+      cnt += __popc(wd[x]);
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int up = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += up;
+    }
+    const int lo = chunk * kCellItem, hi = lo + kCellItem;
+    int rank = incl - cnt;
+    if (rank < hi && incl > lo) {
+#pragma unroll
+      for (int x = 0; x < kMaxWpl; ++x) {
+        uint32_t m = wd[x];
+        while (m != 0u && rank < hi) {
+          const int bit = __ffs(m) - 1;
+          m &= m - 1;
+          if (rank >= lo) s_rows[rank - lo] = (w0 + x) * 32 + bit;
+          ++rank;
+        }
+      }
+    }
+    if (lane == 63) s_n = (incl < hi ? incl : hi) - lo;
+  }
+  // K rows (row-major) and V^T of the cell's key tiles into LDS
+#pragma unroll
+  for (int i = 0; i < kStage; ++i) {
+    const int x = tid + 256 * i;
+    const int kr = x / (D / 8), cv = x % (D / 8);
+    if (kr < b) {
+      const int t = kr / kKT, r = kr % kKT;
+      *reinterpret_cast<uint4*>(&sm.k[t][r * TileSmem<D>::kKPitch + cv * 8]) = kv_k[i];
+      const uint4 vw = kv_v[i];
+      uint16_t* vt = reinterpret_cast<uint16_t*>(sm.vt[t]) + (cv * 8) * TileSmem<D>::kVPitch + r;
+      vt[0 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.x);
+      vt[1 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.x >> 16);
+      vt[2 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.y);
+      vt[3 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.y >> 16);
+      vt[4 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.z);
+      vt[5 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.z >> 16);
+      vt[6 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.w);
+      vt[7 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.w >> 16);
+    }
+  }
+  __syncthreads();
+  const int n = s_n;
+  const int ntl = (n + 31) / 32;
+  for (int rt = stride0; rt < ntl; rt += nstride) {
+    const int er = rt * 32 + ql;
+    const bool ok = er < n;
+    const int r = s_rows[ok ? er : rt * 32];
+    // the row's query, and the cell's slot (first match) and gate in its selection, loaded together
+    uint4 qreg[kKS];
+    const __bf16* qrow = q + ((static_cast<int64_t>(bi) * Hq + h) * nq + r) * D;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) qreg[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hl);
+    const int64_t so = ((static_cast<int64_t>(bi) * Hsel + hs) * nq + r) * K;
+    int slot = K - 1;
+    for (int t = K - 1; t >= 0; --t) slot = idx[so + t] == c ? t : slot;
+    const float bias = logg != nullptr ? logg[so + slot] * kLog2e : 0.f;
+    floatx16_t acc[kDB];
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) acc[db][x] = 0.f;
+    float m2 = -INFINITY, lsum = 0.f;
+    for (int t = 0; t < ntile; ++t) {
+      // S^T = K Q^T: this lane's row, keys tile_key(x, hl) of the tile
+      floatx16_t st;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) st[x] = 0.f;
+      const __bf16* krow = &sm.k[t][perm_row(ql) * TileSmem<D>::kKPitch];
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        const uint4 a = *reinterpret_cast<const uint4*>(krow + 16 * ks + 8 * hl);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[ks]), st, 0, 0, 0);
+      }
+      float z[16];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        z[x] = fmaf(st[x], scale2, bias);
+        mt = fmaxf(mt, z[x]);
+      }
+      mt = fmaxf(mt, xor_lanes_f<32>(mt));
+      const float mnew = fmaxf(m2, mt);
+      const float msub = mnew == -INFINITY ? 0.f : mnew;
+      const float corr = __builtin_amdgcn_exp2f(m2 - msub);
+      float p[16], ps = 0.f;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        p[x] = __builtin_amdgcn_exp2f(z[x] - msub);
+        ps += p[x];
+      }
+      ps += xor_lanes_f<32>(ps);
+      lsum = lsum * corr + ps;
+      m2 = mnew;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) acc[db][x] *= corr;
+      // O^T += V^T P^T
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8_t pb;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) pb[x] = static_cast<__bf16>(p[8 * s2 + x]);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const uint4 a = *reinterpret_cast<const uint4*>(
+              &sm.vt[t][(32 * db + ql) * TileSmem<D>::kVPitch + 16 * s2 + 8 * hl]);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb, acc[db], 0, 0, 0);
+        }
+      }
+    }
+    if (ok) {
+      const int64_t pr = ((static_cast<int64_t>(bi) * Hq + h) * nq + r) * K + slot;
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      // O^T register x of block db holds d = 32 db + 8 (x / 4) + 4 hl + (x % 4)
+      __bf16* orow = cell_o + pr * D;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 w4;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) w4[x] = static_cast<__bf16>(acc[db][4 * a4 + x] * inv);
+          *reinterpret_cast<decltype(w4)*>(orow + 32 * db + 8 * a4 + 4 * hl) = w4;
+        }
+      if (hl == 0) cell_ml[pr] = make_float2(m2, lsum);
+    }
+  }
+}
+
 template <int D, bool kMix, int NW>
 __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ logg, const float* __restrict__ alpha,
     int Hq, int Hkv, int Hsel, int share_group, int nq, int64_t q_pos0, int64_t L, int b,
     int prefix_mode, int qblock, int K, int local, int window, __bf16* __restrict__ o,
-    float* __restrict__ lse, int NH, int NT) {
+    float* __restrict__ lse, int NH, int NT, const __bf16* __restrict__ cell_o,
+    const float2* __restrict__ cell_ml) {
+  // cell_o / cell_ml (mix mode): branch L comes from attn_cell_partial_kernel's
+  // per-(row, slot) partials instead of a walk over the selected key tiles
   __shared__ TileSmem<D> sm;
   __shared__ uint32_t s_bits[2][kMaxKeyTiles / 32];
   __shared__ uint16_t s_list[2][kMaxKeyTiles];
@@ -121,7 +424,7 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
     for (int64_t t = k0 / kKT + tid; t <= p1 / kKT; t += kThreads)
       atomicOr(&s_bits[1][t >> 5], 1u << (t & 31));
   }
-  for (int t = hl; t < K; t += 2) {
+  for (int t = hl; t < K && cell_o == nullptr; t += 2) {
     const int c = reinterpret_cast<int16_t*>(s_idx[wave][ql])[t];
     if (c >= 0) {
       const int64_t a0 = static_cast<int64_t>(c) * b, a1 = a0 + b - 1;
@@ -389,7 +692,45 @@ _Pragma("unroll")                                                               
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     if (branch == 0) lse_L = lsum > 0.f ? (m2 + __log2f(lsum)) / kLog2e : -INFINITY;
     if constexpr (kMix) {
-      if (branch == 0) {
+      if (branch == 0 && cell_o != nullptr) {
+        // o_L from the row's cell partials (each selected cell once: the first slot holding it)
+        const int16_t* ur = reinterpret_cast<const int16_t*>(s_idx[wave][ql]);
+        const int64_t pr0 = ((static_cast<int64_t>(bi) * Hq + h) * nq + rowc) * K;
+        float M = -INFINITY;
+        for (int t = 0; t < K; ++t) {
+          const int ct = ur[t];
+          bool first = ct >= 0;
+          for (int u = 0; u < t; ++u) first = first && ur[u] != ct;
+          if (first) M = fmaxf(M, cell_ml[pr0 + t].x);
+        }
+        const float msub = M == -INFINITY ? 0.f : M;
+#pragma unroll
+        for (int x = 0; x < kDB * 16; ++x) out[x] = 0.f;
+        float wsum = 0.f;
+        for (int t = 0; t < K; ++t) {
+          const int ct = ur[t];
+          bool first = ct >= 0;
+          for (int u = 0; u < t; ++u) first = first && ur[u] != ct;
+          if (!first) continue;
+          const float2 ml = cell_ml[pr0 + t];
+          const float wt = ml.y * __builtin_amdgcn_exp2f(ml.x - msub);
+          wsum += wt;
+          const __bf16* orow = cell_o + (pr0 + t) * D;
+#pragma unroll
+          for (int db = 0; db < kDB; ++db)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+              const auto w4 = *reinterpret_cast<const __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16*>(
+                  orow + 32 * db + 8 * a4 + 4 * hl);
+#pragma unroll
+              for (int x = 0; x < 4; ++x) out[db * 16 + 4 * a4 + x] = fmaf(wt, static_cast<float>(w4[x]), out[db * 16 + 4 * a4 + x]);
+            }
+        }
+        const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+        for (int x = 0; x < kDB * 16; ++x) out[x] *= winv;
+        lse_L = wsum > 0.f ? (M + __log2f(wsum)) / kLog2e : -INFINITY;
+      } else if (branch == 0) {
 #pragma unroll
         for (int db = 0; db < kDB; ++db)
 #pragma unroll
@@ -430,31 +771,115 @@ bool attn_tile_fwd_supported(const AttnLaunch& p) {
          (p.L + kKT - 1) / kKT <= kMaxKeyTiles && (p.d == 64 || p.d == 128);
 }
 
-template <int D, bool kMix, int NW>
-static hipError_t launch_tile_fwd_k(const AttnLaunch& p, int NH, int NT, hipStream_t st) {
+// The cell-major branch L: mix mode, cells of one or two key tiles, and a
+// selection shared by the kv head's query heads (or one query head per kv head).
+static bool use_cell_path(const AttnLaunch& p) {
   const int G = p.Hq / p.Hkv;
+  return p.window > 0 && p.alpha != nullptr && (p.b == 32 || p.b == 64) && G <= 4 && (p.share_group || G == 1) &&
+         p.K >= 1;
+}
+
+struct CellWs {
+  uint32_t* bits;      // [B Hsel, nblk, nw] row-selected-cell bitmap
+  int32_t* cnt;        // [B Hsel ncell] selecting rows per cell
+  int2* items;         // [max_items] (head * ncell + cell, chunk)
+  int32_t* nitems;
+  __bf16* o;           // [B, Hq, nq, K, d] per-(row, slot) normalised o of the cell
+  float2* ml;          // [B, Hq, nq, K] (max, sum), log2 domain
+  int64_t nblk, ncell, max_items;
+  int nw;
+  size_t bytes;
+};
+
+static CellWs cell_ws(const AttnLaunch& p, void* ws) {
+  CellWs w{};
+  w.nblk = (p.L + p.b - 1) / p.b;
+  w.nw = (p.nq + 31) / 32;
+  w.ncell = num_candidates(p.q_pos0 + p.nq - 1, p.b, p.prefix_mode, p.qblock);
+  const int64_t heads = static_cast<int64_t>(p.B) * p.Hsel;
+  // items: at most one partial chunk per (head, cell) plus one per kCellItem (row, slot) pairs
+  w.max_items = heads * w.ncell + (heads * p.nq * p.K + kCellItem - 1) / kCellItem;
+  const size_t parts = static_cast<size_t>(p.B) * p.Hq * p.nq * p.K;
+  const size_t sz[6] = {static_cast<size_t>(heads) * w.nblk * w.nw * sizeof(uint32_t),
+                        static_cast<size_t>(heads) * (w.ncell > 0 ? w.ncell : 1) * sizeof(int32_t),
+                        static_cast<size_t>(w.max_items > 0 ? w.max_items : 1) * sizeof(int2), sizeof(int32_t),
+                        parts * p.d * sizeof(__bf16), parts * sizeof(float2)};
+  char* base = static_cast<char*>(ws);
+  size_t off[6];
+  size_t total = 0;
+  for (int x = 0; x < 6; ++x) {
+    off[x] = total;
+    total += align256(sz[x]);
+  }
+  w.bits = reinterpret_cast<uint32_t*>(base + off[0]);
+  w.cnt = reinterpret_cast<int32_t*>(base + off[1]);
+  w.items = reinterpret_cast<int2*>(base + off[2]);
+  w.nitems = reinterpret_cast<int32_t*>(base + off[3]);
+  w.o = reinterpret_cast<__bf16*>(base + off[4]);
+  w.ml = reinterpret_cast<float2*>(base + off[5]);
+  w.bytes = total;
+  return w;
+}
+
+size_t attn_tile_fwd_workspace_bytes(const AttnLaunch& p) {
+  return use_cell_path(p) ? cell_ws(p, nullptr).bytes : 0;
+}
+
+template <int D, bool kMix, int NW>
+static hipError_t launch_tile_fwd_k(const AttnLaunch& p, int NH, int NT, void* ws, hipStream_t st) {
+  const int G = p.Hq / p.Hkv;
+  const __bf16* cell_o = nullptr;
+  const float2* cell_ml = nullptr;
+  if (kMix && use_cell_path(p)) {
+    const CellWs w = cell_ws(p, ws);
+    const int64_t heads = static_cast<int64_t>(p.B) * p.Hsel;
+    hipError_t e = launch(false, fwd_mark_kernel,
+                          dim3(static_cast<unsigned>((w.nw + kMarkWords - 1) / kMarkWords), static_cast<unsigned>(heads)),
+                          dim3(256), st, p.idx, p.nq, p.q_pos0, p.b, p.prefix_mode, p.qblock, p.K, w.nblk, w.nw, w.bits);
+    if (e != hipSuccess) return e;
+    // cells that are candidates of some row: those before the last row's query block
+    const int64_t ncell = num_candidates(p.q_pos0 + p.nq - 1, p.b, p.prefix_mode, p.qblock);
+    if (ncell > 0) {
+      const int64_t nent = heads * ncell;
+      e = launch(false, cell_count_kernel, dim3(static_cast<unsigned>((nent + 3) / 4)), dim3(256), st,
+                 static_cast<const uint32_t*>(w.bits), w.nblk, w.nw, ncell, heads, w.cnt);
+      if (e != hipSuccess) return e;
+      e = launch(false, cell_items_kernel, dim3(1), dim3(1024), st, static_cast<const int32_t*>(w.cnt), nent, w.items,
+                 w.nitems);
+      if (e != hipSuccess) return e;
+      e = launch(false, attn_cell_partial_kernel<D>, dim3(static_cast<unsigned>(w.max_items)), dim3(256), st,
+                 static_cast<const __bf16*>(p.q), static_cast<const __bf16*>(p.k), static_cast<const __bf16*>(p.v),
+                 p.idx, p.logg, static_cast<const uint32_t*>(w.bits), static_cast<const int2*>(w.items),
+                 static_cast<const int32_t*>(w.nitems), ncell, p.Hq, p.Hkv, p.Hsel, p.nq, p.L, p.b, p.K, w.nblk, w.nw,
+                 w.o, w.ml);
+      if (e != hipSuccess) return e;
+    }
+    cell_o = w.o;
+    cell_ml = w.ml;
+  }
   const int ntiles = (p.nq + 31) / 32;
   dim3 grid((ntiles + NT - 1) / NT, static_cast<unsigned>(p.B * p.Hkv * (G / NH)));
   return launch(true, attn_tile_fwd_kernel<D, kMix, NW>, grid, dim3(64 * NW), st, static_cast<const __bf16*>(p.q),
                 static_cast<const __bf16*>(p.k), static_cast<const __bf16*>(p.v), p.idx, p.logg, p.alpha,
                 p.Hq, p.Hkv, p.Hsel, p.share_group, p.nq, p.q_pos0, p.L, p.b, p.prefix_mode, p.qblock,
-                p.K, p.local, p.window, static_cast<__bf16*>(p.o), p.lse, NH, NT);
+                p.K, p.local, p.window, static_cast<__bf16*>(p.o), p.lse, NH, NT, cell_o, cell_ml);
 }
 
 // Heads of a group share K / V tiles: up to 4 of them in a workgroup, one wave
 // each.  A single head (d = 64) takes two row tiles per workgroup: the
 // workgroup walks the union of its rows' key tiles, so fewer rows per union
 // mean fewer tiles a wave waits through without needing them.
-hipError_t launch_attn_tile_fwd(const AttnLaunch& p, hipStream_t st) {
+hipError_t launch_attn_tile_fwd(const AttnLaunch& p, void* ws, hipStream_t st) {
   const int G = p.Hq / p.Hkv;
   const bool mix = p.window > 0 && p.alpha != nullptr;
   if (G == 1 && p.d == 64) {
-    return mix ? launch_tile_fwd_k<64, true, 2>(p, 1, 2, st) : launch_tile_fwd_k<64, false, 2>(p, 1, 2, st);
+    return mix ? launch_tile_fwd_k<64, true, 2>(p, 1, 2, ws, st) : launch_tile_fwd_k<64, false, 2>(p, 1, 2, ws, st);
   }
   const int NH = G < 4 ? G : 4;
   const int NT = 4 / NH;
-  if (p.d == 64) return mix ? launch_tile_fwd_k<64, true, 4>(p, NH, NT, st) : launch_tile_fwd_k<64, false, 4>(p, NH, NT, st);
-  return mix ? launch_tile_fwd_k<128, true, 4>(p, NH, NT, st) : launch_tile_fwd_k<128, false, 4>(p, NH, NT, st);
+  if (p.d == 64)
+    return mix ? launch_tile_fwd_k<64, true, 4>(p, NH, NT, ws, st) : launch_tile_fwd_k<64, false, 4>(p, NH, NT, ws, st);
+  return mix ? launch_tile_fwd_k<128, true, 4>(p, NH, NT, ws, st) : launch_tile_fwd_k<128, false, 4>(p, NH, NT, ws, st);
 }
 
 }  // namespace spa

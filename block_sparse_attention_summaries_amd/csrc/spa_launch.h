@@ -208,7 +208,9 @@ bool rows_select_mfma_supported(const SelectLaunch& p);
 hipError_t launch_rows_select_mfma(const SelectLaunch& p, hipStream_t st);
 hipError_t launch_attn_fwd(const AttnLaunch& p, void* ws, hipStream_t st);
 bool attn_tile_fwd_supported(const AttnLaunch& p);
-hipError_t launch_attn_tile_fwd(const AttnLaunch& p, hipStream_t st);
+hipError_t launch_attn_tile_fwd(const AttnLaunch& p, void* ws, hipStream_t st);
+// workspace of the tile forward (the cell-major branch L of the mix mode; 0 otherwise)
+size_t attn_tile_fwd_workspace_bytes(const AttnLaunch& p);
 hipError_t launch_attn_bwd(const BwdLaunch& p, void* ws, hipStream_t st);
 bool attn_tile_bwd_supported(const BwdLaunch& p);
 size_t attn_tile_bwd_bitmap_bytes(const BwdLaunch& p);

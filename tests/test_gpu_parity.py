@@ -243,20 +243,23 @@ def _prefill_run(cfg, x, rows=None):
     b, qb = cfg["b"], cfg["qblock"]
     L = x["L"]
     nblk = L // b
-    kw = dict(Hkv=cfg["Hkv"], b=b, K=cfg["K"], q_pos0=0, gate=False, prefix_mode=1, qblock=qb,
-              share_group=False)
+    sg, gate = bool(cfg["share_group"]), bool(cfg["gate"])
+    Hsel = cfg["Hkv"] if sg else cfg["Hq"]
+    lam = np.ascontiguousarray(x["erf_lambda"][:Hsel])
+    sig = np.ascontiguousarray(x["erf_sigma"][:Hsel])
+    kw = dict(Hkv=cfg["Hkv"], b=b, K=cfg["K"], q_pos0=0, gate=gate, prefix_mode=1, qblock=qb, share_group=sg)
     kb_o, mx_o, ce_o = oracle.block_summaries(x["k"], b, nblocks=nblk)
-    ora = oracle.score_select(x["q"], kb_o, mx_o, ce_o, erf_lambda=x["erf_lambda"],
-                              erf_sigma=x["erf_sigma"], rows=rows, **kw)
-    akw = dict(b=b, K=cfg["K"], q_pos0=0, share_group=False, local=1, window=cfg["window"],
-               prefix_mode=1, qblock=qb)
-    o_o, _ = oracle.attn_fwd(x["q"], x["k"], x["v"], ora["idx"], None, alpha=x["alpha"], rows=rows, **akw)
+    ora = oracle.score_select(x["q"], kb_o, mx_o, ce_o, erf_lambda=lam, erf_sigma=sig, rows=rows, **kw)
+    akw = dict(b=b, K=cfg["K"], q_pos0=0, share_group=sg, local=1, window=cfg["window"], prefix_mode=1, qblock=qb)
+    o_o, _ = oracle.attn_fwd(x["q"], x["k"], x["v"], ora["idx"], ora["logg"] if gate else None, alpha=x["alpha"],
+                             rows=rows, **akw)
     qd, kd, vd = dev(x["q"]), dev(x["k"]), dev(x["v"])
     kb_g, mx_g, ce_g = ops.sparse_block_summaries(kd, b)
-    idx_g, _, keff_g = ops.sparse_score_select(qd, kb_g, mx_g, ce_g, erf_lambda=dev(x["erf_lambda"]),
-                                               erf_sigma=dev(x["erf_sigma"]), **kw)
-    o_g, _ = ops.sparse_attn_fwd(qd, kd, vd, idx_g, None, alpha=dev(x["alpha"]), **akw)
-    o_g2, _ = ops.sparse_attn_fwd(qd, kd, vd, dev(ora["idx"]), None, alpha=dev(x["alpha"]), **akw)
+    idx_g, logg_g, keff_g = ops.sparse_score_select(qd, kb_g, mx_g, ce_g, erf_lambda=dev(lam), erf_sigma=dev(sig),
+                                                    **kw)
+    o_g, _ = ops.sparse_attn_fwd(qd, kd, vd, idx_g, logg_g if gate else None, alpha=dev(x["alpha"]), **akw)
+    lg_o = dev(ora["logg"].astype(np.float32)) if gate else None
+    o_g2, _ = ops.sparse_attn_fwd(qd, kd, vd, dev(ora["idx"]), lg_o, alpha=dev(x["alpha"]), **akw)
     torch.cuda.synchronize()
     return ora, o_o, host(idx_g), host(keff_g), host(o_g), host(o_g2)
 
@@ -271,6 +274,8 @@ def _check_prefill(cfg, x, rows=None):
     tol = _tol(cfg)
     assert rel_err(o2[:, :, sel], o_o[:, :, sel]) <= tol
     match = np.all(r_idx == sub["idx"], axis=-1)
+    if cfg["share_group"]:
+        match = np.repeat(match, cfg["Hq"] // cfg["Hkv"], axis=1)
     for h in range(cfg["Hq"]):
         m = match[0, h]
         e = rel_err(o[:, h:h + 1, sel][:, :, m], o_o[:, h:h + 1, sel][:, :, m])
@@ -283,6 +288,9 @@ def _check_prefill(cfg, x, rows=None):
     dict(n=1000, Hq=2, Hkv=2, seed=21),                  # ragged tail (n not a multiple of 128)
     dict(n=1024, Hq=2, Hkv=2, d=128, window=100, K=7, seed=22),
     dict(n=640, Hq=2, Hkv=2, dtype="f32", seed=23),
+    dict(n=1024, Hq=8, Hkv=2, share_group=True, seed=24),            # a group of 4 sharing the selection
+    dict(n=768, Hq=4, Hkv=2, share_group=True, b=64, seed=25),       # cells of two key tiles, group of 2
+    dict(n=1024, Hq=2, Hkv=2, gate=True, seed=26),                   # log-gate bias on the cells
 ])
 def test_prefill_cells_parity(over):
     cfg = config("prefill_cells", **over)
