@@ -60,9 +60,9 @@ constexpr int kMaxSelK = 32;
 // row tile: a row tile's union of selected cells is ~10x the 4 a row reads,
 // while a cell's selecting rows fill whole 32-row tiles.  fwd_mark_kernel
 // sets one bit per (selection head, cell, row) for "the row selected the
-// cell"; attn_cell_partial_kernel takes one cell of one kv head per workgroup
-// (its K rows and V^T in LDS once), lists the selecting rows 32 at a time in
-// row order, and writes for each (row, slot of the cell in the row's
+// cell"; the count / scan / fill kernels turn the bitmap into units of 32
+// selecting rows of one cell (row order); attn_cell_partial_kernel takes one
+// unit per wave and writes for each (row, slot of the cell in the row's
 // selection) the softmax of the row over the cell's keys: o normalised (bf16)
 // and (max, sum) in the log2 domain.  The tile kernel then runs the window
 // branch only and merges a row's partials into o_L before the mix.
@@ -96,12 +96,14 @@ __global__ __launch_bounds__(256) void fwd_mark_kernel(const int32_t* __restrict
   }
 }
 
-// Work items: a cell's selecting rows in chunks of kCellItem (row order).
-// cell_count_kernel: one wave per (selection head, cell) counts its rows;
-// cell_items_kernel (one workgroup) turns the counts into the item list
-// (entry e = head * ncell + cell, chunk j) and its length.
-constexpr int kCellItem = 128;
-constexpr int kMaxWpl = (kMaxKeyTiles * kKT / 32 + 63) / 64;   // bitmap words per lane: nq <= L <= 65536
+// Work units: a cell's selecting rows in tiles of 32 (row order), one unit
+// per wave.  cell_count_kernel: one wave per (selection head, cell) counts its
+// rows; cell_scan_kernel (one workgroup) gives each entry (head * ncell + cell)
+// the index of its first unit and the total; cell_fill_kernel: one wave per
+// entry lists the rows, 32 per unit (the last unit padded with -1), and
+// writes the units' (entry, tile).
+constexpr int kCellUnit = 32;
+constexpr int kFillChunk = 8;                    // bitmap words per lane loaded together
 
 __global__ __launch_bounds__(256) void cell_count_kernel(const uint32_t* __restrict__ bits, int64_t nblk, int nw,
                                                          int64_t ncell, int64_t heads, int32_t* __restrict__ cnt) {
@@ -117,187 +119,216 @@ __global__ __launch_bounds__(256) void cell_count_kernel(const uint32_t* __restr
   if (lane == 0) cnt[e] = n;
 }
 
-__global__ __launch_bounds__(1024) void cell_items_kernel(const int32_t* __restrict__ cnt, int64_t nent,
-                                                          int2* __restrict__ items, int32_t* __restrict__ nitems) {
-  constexpr int kPer = 16;                      // entries loaded together per thread
+__global__ __launch_bounds__(1024) void cell_scan_kernel(const int32_t* __restrict__ cnt, int64_t nent,
+                                                         int32_t* __restrict__ first, int32_t* __restrict__ nunits) {
+  constexpr int kPer = 16;                      // entries per thread per chunk
+  constexpr int kChunk = 1024 * kPer;
+  __shared__ int32_t s_c[kChunk];               // a chunk's unit counts, then its offsets
   __shared__ int32_t s_wave[16];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int64_t per = (nent + 1023) / 1024;
-  const int64_t e0 = tid * per, e1 = e0 + per < nent ? e0 + per : nent;
-  int32_t mine = 0;
-  for (int64_t b0 = e0; b0 < e1; b0 += kPer) {
-    int32_t cv[kPer];
+  int32_t base = 0;
+  for (int64_t c0 = 0; c0 < nent; c0 += kChunk) {
+    // coalesced loads (entry c0 + 1024 x + tid), issued together
+    int32_t ld[kPer];
 #pragma unroll
     for (int x = 0; x < kPer; ++x) {
-      const int32_t ld = cnt[b0 + x < e1 ? b0 + x : e1 - 1];
-      cv[x] = b0 + x < e1 ? ld : 0;
-    }
-#pragma unroll
-    for (int x = 0; x < kPer; ++x) mine += (cv[x] + kCellItem - 1) / kCellItem;
-  }
-  // exclusive prefix of the threads' item counts: in the wave, then over the 16 waves
-  int incl = mine;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int up = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += up;
-  }
-  if (lane == kWave - 1) s_wave[wave] = incl;
-  __syncthreads();
-  int32_t pos = incl - mine;
-  for (int w = 0; w < wave; ++w) pos += s_wave[w];
-  for (int64_t b0 = e0; b0 < e1; b0 += kPer) {
-    int32_t cv[kPer];
-#pragma unroll
-    for (int x = 0; x < kPer; ++x) {
-      const int32_t ld = cnt[b0 + x < e1 ? b0 + x : e1 - 1];
-      cv[x] = b0 + x < e1 ? ld : 0;
+      const int64_t e = c0 + 1024 * x + tid;
+      ld[x] = cnt[e < nent ? e : nent - 1];
     }
 #pragma unroll
     for (int x = 0; x < kPer; ++x) {
-      const int32_t m = (cv[x] + kCellItem - 1) / kCellItem;
-      for (int32_t jj = 0; jj < m; ++jj) items[pos + jj] = make_int2(static_cast<int>(b0 + x), jj);
-      pos += m;
+      const int64_t e = c0 + 1024 * x + tid;
+      s_c[1024 * x + tid] = e < nent ? (ld[x] + kCellUnit - 1) / kCellUnit : 0;
     }
-  }
-  if (tid == 1023) {
+    __syncthreads();
+    // this thread's run of kPer consecutive entries
+    int32_t run[kPer];
+    int32_t mine = 0;
+#pragma unroll
+    for (int x = 0; x < kPer; ++x) {
+      run[x] = s_c[tid * kPer + x];
+      mine += run[x];
+    }
+    int incl = mine;                             // exclusive prefix: in the wave, then over the 16 waves
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int up = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += up;
+    }
+    if (lane == kWave - 1) s_wave[wave] = incl;
+    __syncthreads();
+    int32_t pos = base + incl - mine;
     int32_t tot = 0;
-    for (int w = 0; w < 16; ++w) tot += s_wave[w];
-    *nitems = tot;
+    for (int w = 0; w < 16; ++w) {
+      pos += w < wave ? s_wave[w] : 0;
+      tot += s_wave[w];
+    }
+#pragma unroll
+    for (int x = 0; x < kPer; ++x) {
+      s_c[tid * kPer + x] = pos;
+      pos += run[x];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < kPer; ++x) {
+      const int64_t e = c0 + 1024 * x + tid;
+      if (e < nent) first[e] = s_c[1024 * x + tid];
+    }
+    base += tot;
+    __syncthreads();                             // s_c and s_wave are rewritten by the next chunk
+  }
+  if (tid == 0) *nunits = base;
+}
+
+__global__ __launch_bounds__(256) void cell_fill_kernel(const uint32_t* __restrict__ bits,
+                                                        const int32_t* __restrict__ cnt,
+                                                        const int32_t* __restrict__ first, int64_t nblk, int nw,
+                                                        int64_t ncell, int64_t nent, int2* __restrict__ units,
+                                                        int32_t* __restrict__ rows) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  if (e >= nent) return;                         // whole wave leaves
+  const int64_t bh = e / ncell, c = e % ncell;
+  const uint32_t* brow = bits + (bh * nblk + c) * nw;
+  const int n = cnt[e];
+  const int32_t u0 = first[e];
+  const int m = (n + kCellUnit - 1) / kCellUnit;
+  int32_t* rw = rows + static_cast<int64_t>(u0) * kCellUnit;
+  for (int x = n + lane; x < m * kCellUnit; x += kWave) rw[x] = -1;
+  for (int j = lane; j < m; j += kWave) units[u0 + j] = make_int2(static_cast<int>(e), j);
+  // word w = x * 64 + lane: a run of consecutive rows spreads over the lanes
+  int base = 0;
+  for (int x0 = 0; x0 * kWave < nw; x0 += kFillChunk) {
+    uint32_t wd[kFillChunk];
+#pragma unroll
+    for (int x = 0; x < kFillChunk; ++x) {
+      const int w = (x0 + x) * kWave + lane;
+      const uint32_t ld = brow[w < nw ? w : nw - 1];   // unconditional (clamped): the loads issue together
+      wd[x] = w < nw ? ld : 0u;
+    }
+#pragma unroll
+    for (int x = 0; x < kFillChunk; ++x) {
+      const int pc = __popc(wd[x]);
+      int incl = pc;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int up = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += up;
+      }
+      int rank = base + incl - pc;
+      const int row0 = ((x0 + x) * kWave + lane) * 32;
+      uint32_t mm = wd[x];
+      while (mm != 0u) {
+        rw[rank++] = row0 + __ffs(mm) - 1;
+        mm &= mm - 1;
+      }
+      base += __shfl(incl, kWave - 1);
+    }
   }
 }
 
-template <int D>
+// One unit per wave (four independent waves per workgroup): 32 rows that
+// selected one cell of NT key tiles.  The lane's K operand rows come straight
+// from memory; V^T goes through the wave's own LDS slice.  For each query head
+// of the group the rows' softmax over the cell's keys is written per
+// (row, slot of the cell in the row's selection).
+template <int D, int NT>
 __global__ __launch_bounds__(256) void attn_cell_partial_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const int32_t* __restrict__ idx, const float* __restrict__ logg, const uint32_t* __restrict__ bits,
-    const int2* __restrict__ items, const int32_t* __restrict__ nitems, int64_t ncell, int Hq, int Hkv, int Hsel,
-    int nq, int64_t L, int b, int K, int64_t nblk, int nw, __bf16* __restrict__ cell_o, float2* __restrict__ cell_ml) {
-  __shared__ TileSmem<D> sm;           // the cell's key tiles: b / 32 of them (b <= 64)
-  __shared__ int s_rows[kCellItem];
-  __shared__ int s_n;
+    const int32_t* __restrict__ idx, const float* __restrict__ logg, const int2* __restrict__ units,
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ nunits, int64_t ncell, int Hq, int Hkv, int Hsel,
+    int nq, int64_t L, int K, __bf16* __restrict__ cell_o, float2* __restrict__ cell_ml) {
+  constexpr int kVPitch = kKT + 8;
   constexpr int kKS = D / 16;
   constexpr int kDB = D / 32;
-  constexpr int kStage = 2 * kKT * (D / 8) / 256;   // 16-byte vectors per thread for two key tiles
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kLd = NT * kKT * (D / 8) / kWave;  // 16-byte vectors of V per lane
+  constexpr int b = NT * kKT;                       // keys of a cell
+  __shared__ __bf16 s_vt[4][NT][D * kVPitch];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hl = lane >> 5, ql = lane & 31;
-  if (static_cast<int>(blockIdx.x) >= *nitems) return;   // whole workgroup: past the item list
-  const int2 item = items[blockIdx.x];
-  const int64_t e = item.x;
-  const int chunk = item.y;
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (u >= *nunits) return;                      // whole wave leaves; no workgroup barrier below
+  const int2 unit = units[u];
+  const int r0 = rows[u * kCellUnit + ql];       // -1 past the cell's last row
+  const int64_t e = unit.x;
   const int64_t bkv = e / ncell;                 // Hsel == Hkv here: the selection head is the kv head
   const int c = static_cast<int>(e % ncell);
   const int bi = static_cast<int>(bkv / Hkv), kvh = static_cast<int>(bkv % Hkv);
-  const int G = Hq / Hkv;                        // 1, 2 or 4; the group shares the selection when G > 1
-  const int g = wave % G, stride0 = wave / G, nstride = 4 / G;
-  const int h = kvh * G + g;
-  const int hs = kvh;
-  const int ntile = b / kKT;
+  const int G = Hq / Hkv;                        // the group's query heads share the selection
   const int64_t kvbase = (static_cast<int64_t>(bi) * Hkv + kvh) * L * D;
-  const float scale2 = kLog2e / sqrtf(static_cast<float>(D));
-  const uint32_t* brow = bits + ((static_cast<int64_t>(bi) * Hsel + hs) * nblk + c) * nw;
-
-  // the cell's K and V rows, loaded while the item's rows are found (clamped addresses)
-  uint4 kv_k[kStage], kv_v[kStage];
+  // loads issued together: the K operand (key perm_row(ql) of each tile) and the V rows
+  uint4 ka[NT][kKS];
 #pragma unroll
-  for (int i = 0; i < kStage; ++i) {
-    const int x = tid + 256 * i;
-    const int kr = x / (D / 8), cv = x % (D / 8);  // key row of the cell (two tiles' worth), column group
-    int64_t key = static_cast<int64_t>(c) * b + (kr < b ? kr : b - 1);
+  for (int t = 0; t < NT; ++t) {
+    int64_t key = static_cast<int64_t>(c) * b + t * kKT + perm_row(ql);
     key = key < L ? key : L - 1;
-    kv_k[i] = *reinterpret_cast<const uint4*>(k + kvbase + key * D + cv * 8);
-    kv_v[i] = *reinterpret_cast<const uint4*>(v + kvbase + key * D + cv * 8);
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) ka[t][ks] = *reinterpret_cast<const uint4*>(k + kvbase + key * D + 16 * ks + 8 * hl);
   }
-  // rows of rank [chunk * kCellItem, +kCellItem) among the cell's selecting rows
-  // (row order): wave 0, each lane a contiguous run of bitmap words
-  if (wave == 0) {
-    // lane l holds words l * wpl .. of the cell's row (nw <= 64 * kMaxWpl), loaded together
-    const int wpl = (nw + kWave - 1) / kWave;
-    const int w0 = lane * wpl;
-    uint32_t wd[kMaxWpl];
-    int cnt = 0;
+  uint4 vv[kLd];
 #pragma unroll
-    for (int x = 0; x < kMaxWpl; ++x) {
-      const int w = w0 + x;
-      const uint32_t ld = brow[w < nw ? w : nw - 1];    // unconditional (clamped): the loads issue together
-      wd[x] = (x < wpl && w < nw) ? ld : 0u;
-      cnt += __popc(wd[x]);
-    }
-    int incl = cnt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int up = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += up;
-    }
-    const int lo = chunk * kCellItem, hi = lo + kCellItem;
-    int rank = incl - cnt;
-    if (rank < hi && incl > lo) {
-#pragma unroll
-      for (int x = 0; x < kMaxWpl; ++x) {
-        uint32_t m = wd[x];
-        while (m != 0u && rank < hi) {
-          const int bit = __ffs(m) - 1;
-          m &= m - 1;
-          if (rank >= lo) s_rows[rank - lo] = (w0 + x) * 32 + bit;
-          ++rank;
-        }
-      }
-    }
-    if (lane == 63) s_n = (incl < hi ? incl : hi) - lo;
+  for (int i = 0; i < kLd; ++i) {
+    const int x = lane + kWave * i;
+    int64_t key = static_cast<int64_t>(c) * b + x / (D / 8);
+    key = key < L ? key : L - 1;
+    vv[i] = *reinterpret_cast<const uint4*>(v + kvbase + key * D + (x % (D / 8)) * 8);
   }
-  // K rows (row-major) and V^T of the cell's key tiles into LDS
+  const bool ok = r0 >= 0;
+  const int r = ok ? r0 : __shfl(r0, 0);         // a unit holds at least one row
+  // the cell's slot (first match) and gate in the row's selection
+  const int64_t so = ((static_cast<int64_t>(bi) * Hsel + kvh) * nq + r) * K;
+  int slot = -1;
+  float lg = 0.f;
+#pragma unroll 4
+  for (int t = 0; t < K; ++t) {
+    const int32_t it = idx[so + t];
+    const float lt = logg != nullptr ? logg[so + t] : 0.f;
+    if (slot < 0 && it == c) {
+      slot = t;
+      lg = lt;
+    }
+  }
+  slot = slot < 0 ? 0 : slot;                    // the bitmap marks only rows that selected the cell
+  const float bias = lg * kLog2e;
+  // V^T of the cell's key tiles into the wave's slice
 #pragma unroll
-  for (int i = 0; i < kStage; ++i) {
-    const int x = tid + 256 * i;
+  for (int i = 0; i < kLd; ++i) {
+    const int x = lane + kWave * i;
     const int kr = x / (D / 8), cv = x % (D / 8);
-    if (kr < b) {
-      const int t = kr / kKT, r = kr % kKT;
-      *reinterpret_cast<uint4*>(&sm.k[t][r * TileSmem<D>::kKPitch + cv * 8]) = kv_k[i];
-      const uint4 vw = kv_v[i];
-      uint16_t* vt = reinterpret_cast<uint16_t*>(sm.vt[t]) + (cv * 8) * TileSmem<D>::kVPitch + r;
-      vt[0 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.x);
-      vt[1 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.x >> 16);
-      vt[2 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.y);
-      vt[3 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.y >> 16);
-      vt[4 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.z);
-      vt[5 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.z >> 16);
-      vt[6 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.w);
-      vt[7 * TileSmem<D>::kVPitch] = static_cast<uint16_t>(vw.w >> 16);
-    }
+    const uint4 vw = vv[i];
+    uint16_t* vt = reinterpret_cast<uint16_t*>(s_vt[wave][kr / kKT]) + (cv * 8) * kVPitch + kr % kKT;
+    vt[0 * kVPitch] = static_cast<uint16_t>(vw.x);
+    vt[1 * kVPitch] = static_cast<uint16_t>(vw.x >> 16);
+    vt[2 * kVPitch] = static_cast<uint16_t>(vw.y);
+    vt[3 * kVPitch] = static_cast<uint16_t>(vw.y >> 16);
+    vt[4 * kVPitch] = static_cast<uint16_t>(vw.z);
+    vt[5 * kVPitch] = static_cast<uint16_t>(vw.z >> 16);
+    vt[6 * kVPitch] = static_cast<uint16_t>(vw.w);
+    vt[7 * kVPitch] = static_cast<uint16_t>(vw.w >> 16);
   }
-  __syncthreads();
-  const int n = s_n;
-  const int ntl = (n + 31) / 32;
-  for (int rt = stride0; rt < ntl; rt += nstride) {
-    const int er = rt * 32 + ql;
-    const bool ok = er < n;
-    const int r = s_rows[ok ? er : rt * 32];
-    // the row's query, and the cell's slot (first match) and gate in its selection, loaded together
+  wave_lds_sync();
+  const float scale2 = kLog2e / sqrtf(static_cast<float>(D));
+  for (int g = 0; g < G; ++g) {
+    const int h = kvh * G + g;
     uint4 qreg[kKS];
     const __bf16* qrow = q + ((static_cast<int64_t>(bi) * Hq + h) * nq + r) * D;
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) qreg[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hl);
-    const int64_t so = ((static_cast<int64_t>(bi) * Hsel + hs) * nq + r) * K;
-    int slot = K - 1;
-    for (int t = K - 1; t >= 0; --t) slot = idx[so + t] == c ? t : slot;
-    const float bias = logg != nullptr ? logg[so + slot] * kLog2e : 0.f;
     floatx16_t acc[kDB];
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
       for (int x = 0; x < 16; ++x) acc[db][x] = 0.f;
     float m2 = -INFINITY, lsum = 0.f;
-    for (int t = 0; t < ntile; ++t) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
       // S^T = K Q^T: this lane's row, keys tile_key(x, hl) of the tile
       floatx16_t st;
 #pragma unroll
       for (int x = 0; x < 16; ++x) st[x] = 0.f;
-      const __bf16* krow = &sm.k[t][perm_row(ql) * TileSmem<D>::kKPitch];
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(krow + 16 * ks + 8 * hl);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[ks]), st, 0, 0, 0);
-      }
+      for (int ks = 0; ks < kKS; ++ks)
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[t][ks]), as_bf16x8(qreg[ks]), st, 0, 0, 0);
       float z[16];
       float mt = -INFINITY;
 #pragma unroll
@@ -330,8 +361,7 @@ __global__ __launch_bounds__(256) void attn_cell_partial_kernel(
         for (int x = 0; x < 8; ++x) pb[x] = static_cast<__bf16>(p[8 * s2 + x]);
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
-          const uint4 a = *reinterpret_cast<const uint4*>(
-              &sm.vt[t][(32 * db + ql) * TileSmem<D>::kVPitch + 16 * s2 + 8 * hl]);
+          const uint4 a = *reinterpret_cast<const uint4*>(&s_vt[wave][t][(32 * db + ql) * kVPitch + 16 * s2 + 8 * hl]);
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb, acc[db], 0, 0, 0);
         }
       }
@@ -355,7 +385,10 @@ __global__ __launch_bounds__(256) void attn_cell_partial_kernel(
   }
 }
 
-template <int D, bool kMix, int NW>
+// kMode 0: selected blocks (SAS); 1: routed cells walked per row tile + window;
+// 2: window walk only, branch L merged from attn_cell_partial_kernel's
+// per-(row, slot) partials (cell_o / cell_ml).
+template <int D, int kMode, int NW>
 __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ logg, const float* __restrict__ alpha,
@@ -363,8 +396,8 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
     int prefix_mode, int qblock, int K, int local, int window, __bf16* __restrict__ o,
     float* __restrict__ lse, int NH, int NT, const __bf16* __restrict__ cell_o,
     const float2* __restrict__ cell_ml) {
-  // cell_o / cell_ml (mix mode): branch L comes from attn_cell_partial_kernel's
-  // per-(row, slot) partials instead of a walk over the selected key tiles
+  constexpr bool kMix = kMode != 0;
+  constexpr bool kCells = kMode == 2;
   __shared__ TileSmem<D> sm;
   __shared__ uint32_t s_bits[2][kMaxKeyTiles / 32];
   __shared__ uint16_t s_list[2][kMaxKeyTiles];
@@ -424,7 +457,7 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
     for (int64_t t = k0 / kKT + tid; t <= p1 / kKT; t += kThreads)
       atomicOr(&s_bits[1][t >> 5], 1u << (t & 31));
   }
-  for (int t = hl; t < K && cell_o == nullptr; t += 2) {
+  for (int t = hl; t < K && !kCells; t += 2) {
     const int c = reinterpret_cast<int16_t*>(s_idx[wave][ql])[t];
     if (c >= 0) {
       const int64_t a0 = static_cast<int64_t>(c) * b, a1 = a0 + b - 1;
@@ -473,7 +506,7 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
   float out[kMix ? kDB * 16 : 1];
   float lse_L = -INFINITY;
 
-  for (int branch = 0; branch < (mix ? 2 : 1); ++branch) {
+  for (int branch = kCells ? 1 : 0; branch < (mix ? 2 : 1); ++branch) {
     const int ntl = s_count[branch];
     const uint16_t* list = s_list[branch];
     floatx16_t acc[kDB];
@@ -691,46 +724,51 @@ _Pragma("unroll")                                                               
 #undef SPA_STAGE_ONE
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     if (branch == 0) lse_L = lsum > 0.f ? (m2 + __log2f(lsum)) / kLog2e : -INFINITY;
-    if constexpr (kMix) {
-      if (branch == 0 && cell_o != nullptr) {
-        // o_L from the row's cell partials (each selected cell once: the first slot holding it)
-        const int16_t* ur = reinterpret_cast<const int16_t*>(s_idx[wave][ql]);
-        const int64_t pr0 = ((static_cast<int64_t>(bi) * Hq + h) * nq + rowc) * K;
-        float M = -INFINITY;
-        for (int t = 0; t < K; ++t) {
-          const int ct = ur[t];
-          bool first = ct >= 0;
-          for (int u = 0; u < t; ++u) first = first && ur[u] != ct;
-          if (first) M = fmaxf(M, cell_ml[pr0 + t].x);
-        }
-        const float msub = M == -INFINITY ? 0.f : M;
+    if constexpr (kCells) {
+      // o = alpha o_L + (1 - alpha) o_S, o_L from the row's cell partials (each
+      // selected cell once: the first slot holding it)
+      const int16_t* ur = reinterpret_cast<const int16_t*>(s_idx[wave][ql]);
+      const int64_t pr0 = ((static_cast<int64_t>(bi) * Hq + h) * nq + rowc) * K;
+      float M = -INFINITY;
+      for (int t = 0; t < K; ++t) {
+        const int ct = ur[t];
+        bool first = ct >= 0;
+        for (int u = 0; u < t; ++u) first = first && ur[u] != ct;
+        if (first) M = fmaxf(M, cell_ml[pr0 + t].x);
+      }
+      const float msub = M == -INFINITY ? 0.f : M;
+      float ol[kDB * 16];
 #pragma unroll
-        for (int x = 0; x < kDB * 16; ++x) out[x] = 0.f;
-        float wsum = 0.f;
-        for (int t = 0; t < K; ++t) {
-          const int ct = ur[t];
-          bool first = ct >= 0;
-          for (int u = 0; u < t; ++u) first = first && ur[u] != ct;
-          if (!first) continue;
-          const float2 ml = cell_ml[pr0 + t];
-          const float wt = ml.y * __builtin_amdgcn_exp2f(ml.x - msub);
-          wsum += wt;
-          const __bf16* orow = cell_o + (pr0 + t) * D;
+      for (int x = 0; x < kDB * 16; ++x) ol[x] = 0.f;
+      float wsum = 0.f;
+      for (int t = 0; t < K; ++t) {
+        const int ct = ur[t];
+        bool first = ct >= 0;
+        for (int u = 0; u < t; ++u) first = first && ur[u] != ct;
+        if (!first) continue;
+        const float2 ml = cell_ml[pr0 + t];
+        const float wt = ml.y * __builtin_amdgcn_exp2f(ml.x - msub);
+        wsum += wt;
+        const __bf16* orow = cell_o + (pr0 + t) * D;
 #pragma unroll
-          for (int db = 0; db < kDB; ++db)
+        for (int db = 0; db < kDB; ++db)
 #pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-              const auto w4 = *reinterpret_cast<const __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16*>(
-                  orow + 32 * db + 8 * a4 + 4 * hl);
+          for (int a4 = 0; a4 < 4; ++a4) {
+            const auto w4 = *reinterpret_cast<const __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16*>(
+                orow + 32 * db + 8 * a4 + 4 * hl);
 #pragma unroll
-              for (int x = 0; x < 4; ++x) out[db * 16 + 4 * a4 + x] = fmaf(wt, static_cast<float>(w4[x]), out[db * 16 + 4 * a4 + x]);
-            }
-        }
-        const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
+            for (int x = 0; x < 4; ++x) ol[db * 16 + 4 * a4 + x] = fmaf(wt, static_cast<float>(w4[x]), ol[db * 16 + 4 * a4 + x]);
+          }
+      }
+      const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
+      lse_L = wsum > 0.f ? (M + __log2f(wsum)) / kLog2e : -INFINITY;
+      const float a = alpha[h];
 #pragma unroll
-        for (int x = 0; x < kDB * 16; ++x) out[x] *= winv;
-        lse_L = wsum > 0.f ? (M + __log2f(wsum)) / kLog2e : -INFINITY;
-      } else if (branch == 0) {
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = a * (ol[db * 16 + r] * winv) + (1.f - a) * (acc[db][r] * inv);
+    } else if constexpr (kMix) {
+      if (branch == 0) {
 #pragma unroll
         for (int db = 0; db < kDB; ++db)
 #pragma unroll
@@ -782,11 +820,13 @@ static bool use_cell_path(const AttnLaunch& p) {
 struct CellWs {
   uint32_t* bits;      // [B Hsel, nblk, nw] row-selected-cell bitmap
   int32_t* cnt;        // [B Hsel ncell] selecting rows per cell
-  int2* items;         // [max_items] (head * ncell + cell, chunk)
-  int32_t* nitems;
+  int32_t* first;      // [B Hsel ncell] index of the cell's first unit
+  int2* units;         // [max_units] (head * ncell + cell, tile of 32 rows)
+  int32_t* rows;       // [max_units, 32] the units' rows, -1 past a cell's last row
+  int32_t* nunits;
   __bf16* o;           // [B, Hq, nq, K, d] per-(row, slot) normalised o of the cell
   float2* ml;          // [B, Hq, nq, K] (max, sum), log2 domain
-  int64_t nblk, ncell, max_items;
+  int64_t nblk, ncell, max_units;
   int nw;
   size_t bytes;
 };
@@ -797,26 +837,34 @@ static CellWs cell_ws(const AttnLaunch& p, void* ws) {
   w.nw = (p.nq + 31) / 32;
   w.ncell = num_candidates(p.q_pos0 + p.nq - 1, p.b, p.prefix_mode, p.qblock);
   const int64_t heads = static_cast<int64_t>(p.B) * p.Hsel;
-  // items: at most one partial chunk per (head, cell) plus one per kCellItem (row, slot) pairs
-  w.max_items = heads * w.ncell + (heads * p.nq * p.K + kCellItem - 1) / kCellItem;
+  const int64_t nent = heads * (w.ncell > 0 ? w.ncell : 1);
+  // units: one partial tile per (head, cell) at most, plus one per 32 (row, cell) marks
+  w.max_units = nent + (heads * p.nq * p.K + kCellUnit - 1) / kCellUnit;
   const size_t parts = static_cast<size_t>(p.B) * p.Hq * p.nq * p.K;
-  const size_t sz[6] = {static_cast<size_t>(heads) * w.nblk * w.nw * sizeof(uint32_t),
-                        static_cast<size_t>(heads) * (w.ncell > 0 ? w.ncell : 1) * sizeof(int32_t),
-                        static_cast<size_t>(w.max_items > 0 ? w.max_items : 1) * sizeof(int2), sizeof(int32_t),
-                        parts * p.d * sizeof(__bf16), parts * sizeof(float2)};
+  constexpr int kParts = 8;
+  const size_t sz[kParts] = {static_cast<size_t>(heads) * w.nblk * w.nw * sizeof(uint32_t),
+                             static_cast<size_t>(nent) * sizeof(int32_t),
+                             static_cast<size_t>(nent) * sizeof(int32_t),
+                             static_cast<size_t>(w.max_units) * sizeof(int2),
+                             static_cast<size_t>(w.max_units) * kCellUnit * sizeof(int32_t),
+                             sizeof(int32_t),
+                             parts * p.d * sizeof(__bf16),
+                             parts * sizeof(float2)};
   char* base = static_cast<char*>(ws);
-  size_t off[6];
+  size_t off[kParts];
   size_t total = 0;
-  for (int x = 0; x < 6; ++x) {
+  for (int x = 0; x < kParts; ++x) {
     off[x] = total;
     total += align256(sz[x]);
   }
   w.bits = reinterpret_cast<uint32_t*>(base + off[0]);
   w.cnt = reinterpret_cast<int32_t*>(base + off[1]);
-  w.items = reinterpret_cast<int2*>(base + off[2]);
-  w.nitems = reinterpret_cast<int32_t*>(base + off[3]);
-  w.o = reinterpret_cast<__bf16*>(base + off[4]);
-  w.ml = reinterpret_cast<float2*>(base + off[5]);
+  w.first = reinterpret_cast<int32_t*>(base + off[2]);
+  w.units = reinterpret_cast<int2*>(base + off[3]);
+  w.rows = reinterpret_cast<int32_t*>(base + off[4]);
+  w.nunits = reinterpret_cast<int32_t*>(base + off[5]);
+  w.o = reinterpret_cast<__bf16*>(base + off[6]);
+  w.ml = reinterpret_cast<float2*>(base + off[7]);
   w.bytes = total;
   return w;
 }
@@ -825,61 +873,91 @@ size_t attn_tile_fwd_workspace_bytes(const AttnLaunch& p) {
   return use_cell_path(p) ? cell_ws(p, nullptr).bytes : 0;
 }
 
-template <int D, bool kMix, int NW>
-static hipError_t launch_tile_fwd_k(const AttnLaunch& p, int NH, int NT, void* ws, hipStream_t st) {
-  const int G = p.Hq / p.Hkv;
-  const __bf16* cell_o = nullptr;
-  const float2* cell_ml = nullptr;
-  if (kMix && use_cell_path(p)) {
-    const CellWs w = cell_ws(p, ws);
-    const int64_t heads = static_cast<int64_t>(p.B) * p.Hsel;
-    hipError_t e = launch(false, fwd_mark_kernel,
-                          dim3(static_cast<unsigned>((w.nw + kMarkWords - 1) / kMarkWords), static_cast<unsigned>(heads)),
-                          dim3(256), st, p.idx, p.nq, p.q_pos0, p.b, p.prefix_mode, p.qblock, p.K, w.nblk, w.nw, w.bits);
+// The cell-major branch L: mark, count, scan and fill build the units, then
+// attn_cell_partial_kernel writes the per-(row, slot) partials into the workspace.
+template <int D>
+static hipError_t launch_cell_partials(const AttnLaunch& p, void* ws, hipStream_t st, const __bf16** cell_o,
+                                       const float2** cell_ml) {
+  const CellWs w = cell_ws(p, ws);
+  const int64_t heads = static_cast<int64_t>(p.B) * p.Hsel;
+  hipError_t e = launch(false, fwd_mark_kernel,
+                        dim3(static_cast<unsigned>((w.nw + kMarkWords - 1) / kMarkWords), static_cast<unsigned>(heads)),
+                        dim3(256), st, p.idx, p.nq, p.q_pos0, p.b, p.prefix_mode, p.qblock, p.K, w.nblk, w.nw, w.bits);
+  if (e != hipSuccess) return e;
+  // cells that are candidates of some row: those before the last row's query block
+  const int64_t ncell = num_candidates(p.q_pos0 + p.nq - 1, p.b, p.prefix_mode, p.qblock);
+  if (ncell > 0) {
+    const int64_t nent = heads * ncell;
+    const unsigned wave_grid = static_cast<unsigned>((nent + 3) / 4);   // one wave per entry
+    e = launch(false, cell_count_kernel, dim3(wave_grid), dim3(256), st, static_cast<const uint32_t*>(w.bits), w.nblk,
+               w.nw, ncell, heads, w.cnt);
     if (e != hipSuccess) return e;
-    // cells that are candidates of some row: those before the last row's query block
-    const int64_t ncell = num_candidates(p.q_pos0 + p.nq - 1, p.b, p.prefix_mode, p.qblock);
-    if (ncell > 0) {
-      const int64_t nent = heads * ncell;
-      e = launch(false, cell_count_kernel, dim3(static_cast<unsigned>((nent + 3) / 4)), dim3(256), st,
-                 static_cast<const uint32_t*>(w.bits), w.nblk, w.nw, ncell, heads, w.cnt);
-      if (e != hipSuccess) return e;
-      e = launch(false, cell_items_kernel, dim3(1), dim3(1024), st, static_cast<const int32_t*>(w.cnt), nent, w.items,
-                 w.nitems);
-      if (e != hipSuccess) return e;
-      e = launch(false, attn_cell_partial_kernel<D>, dim3(static_cast<unsigned>(w.max_items)), dim3(256), st,
-                 static_cast<const __bf16*>(p.q), static_cast<const __bf16*>(p.k), static_cast<const __bf16*>(p.v),
-                 p.idx, p.logg, static_cast<const uint32_t*>(w.bits), static_cast<const int2*>(w.items),
-                 static_cast<const int32_t*>(w.nitems), ncell, p.Hq, p.Hkv, p.Hsel, p.nq, p.L, p.b, p.K, w.nblk, w.nw,
-                 w.o, w.ml);
-      if (e != hipSuccess) return e;
-    }
-    cell_o = w.o;
-    cell_ml = w.ml;
+    e = launch(false, cell_scan_kernel, dim3(1), dim3(1024), st, static_cast<const int32_t*>(w.cnt), nent, w.first,
+               w.nunits);
+    if (e != hipSuccess) return e;
+    e = launch(false, cell_fill_kernel, dim3(wave_grid), dim3(256), st, static_cast<const uint32_t*>(w.bits),
+               static_cast<const int32_t*>(w.cnt), static_cast<const int32_t*>(w.first), w.nblk, w.nw, ncell, nent,
+               w.units, w.rows);
+    if (e != hipSuccess) return e;
+    const dim3 ugrid(static_cast<unsigned>((w.max_units + 3) / 4));     // one unit per wave
+    const auto* q = static_cast<const __bf16*>(p.q);
+    const auto* kk = static_cast<const __bf16*>(p.k);
+    const auto* vv = static_cast<const __bf16*>(p.v);
+    const auto* un = static_cast<const int2*>(w.units);
+    const auto* rw = static_cast<const int32_t*>(w.rows);
+    const auto* nu = static_cast<const int32_t*>(w.nunits);
+    e = p.b == 32 ? launch(false, attn_cell_partial_kernel<D, 1>, ugrid, dim3(256), st, q, kk, vv, p.idx, p.logg, un,
+                           rw, nu, ncell, p.Hq, p.Hkv, p.Hsel, p.nq, p.L, p.K, w.o, w.ml)
+                  : launch(false, attn_cell_partial_kernel<D, 2>, ugrid, dim3(256), st, q, kk, vv, p.idx, p.logg, un,
+                           rw, nu, ncell, p.Hq, p.Hkv, p.Hsel, p.nq, p.L, p.K, w.o, w.ml);
+    if (e != hipSuccess) return e;
   }
+  *cell_o = w.o;
+  *cell_ml = w.ml;
+  return hipSuccess;
+}
+
+template <int D, int kMode, int NW>
+static hipError_t launch_tile_fwd_k(const AttnLaunch& p, int NH, int NT, const __bf16* cell_o, const float2* cell_ml,
+                                    hipStream_t st) {
+  const int G = p.Hq / p.Hkv;
   const int ntiles = (p.nq + 31) / 32;
   dim3 grid((ntiles + NT - 1) / NT, static_cast<unsigned>(p.B * p.Hkv * (G / NH)));
-  return launch(true, attn_tile_fwd_kernel<D, kMix, NW>, grid, dim3(64 * NW), st, static_cast<const __bf16*>(p.q),
+  return launch(true, attn_tile_fwd_kernel<D, kMode, NW>, grid, dim3(64 * NW), st, static_cast<const __bf16*>(p.q),
                 static_cast<const __bf16*>(p.k), static_cast<const __bf16*>(p.v), p.idx, p.logg, p.alpha,
                 p.Hq, p.Hkv, p.Hsel, p.share_group, p.nq, p.q_pos0, p.L, p.b, p.prefix_mode, p.qblock,
                 p.K, p.local, p.window, static_cast<__bf16*>(p.o), p.lse, NH, NT, cell_o, cell_ml);
 }
 
 // Heads of a group share K / V tiles: up to 4 of them in a workgroup, one wave
-// each.  A single head (d = 64) takes two row tiles per workgroup: the
-// workgroup walks the union of its rows' key tiles, so fewer rows per union
-// mean fewer tiles a wave waits through without needing them.
+// each.  In the selected-block modes a single head (d = 64) takes two row tiles
+// per workgroup: the workgroup walks the union of its rows' key tiles, so fewer
+// rows per union mean fewer tiles a wave waits through without needing them.
+// With the cells computed apart, the walk is the window alone (contiguous), and
+// a single head takes four row tiles: each staged key tile serves four waves.
 hipError_t launch_attn_tile_fwd(const AttnLaunch& p, void* ws, hipStream_t st) {
   const int G = p.Hq / p.Hkv;
-  const bool mix = p.window > 0 && p.alpha != nullptr;
-  if (G == 1 && p.d == 64) {
-    return mix ? launch_tile_fwd_k<64, true, 2>(p, 1, 2, ws, st) : launch_tile_fwd_k<64, false, 2>(p, 1, 2, ws, st);
-  }
   const int NH = G < 4 ? G : 4;
   const int NT = 4 / NH;
+  const bool mix = p.window > 0 && p.alpha != nullptr;
+  if (mix && use_cell_path(p)) {
+    const __bf16* cell_o = nullptr;
+    const float2* cell_ml = nullptr;
+    const hipError_t e = p.d == 64 ? launch_cell_partials<64>(p, ws, st, &cell_o, &cell_ml)
+                                   : launch_cell_partials<128>(p, ws, st, &cell_o, &cell_ml);
+    if (e != hipSuccess) return e;
+    if (p.d == 64) return launch_tile_fwd_k<64, 2, 4>(p, NH, NT, cell_o, cell_ml, st);
+    return launch_tile_fwd_k<128, 2, 4>(p, NH, NT, cell_o, cell_ml, st);
+  }
+  if (G == 1 && p.d == 64) {
+    return mix ? launch_tile_fwd_k<64, 1, 2>(p, 1, 2, nullptr, nullptr, st)
+               : launch_tile_fwd_k<64, 0, 2>(p, 1, 2, nullptr, nullptr, st);
+  }
   if (p.d == 64)
-    return mix ? launch_tile_fwd_k<64, true, 4>(p, NH, NT, ws, st) : launch_tile_fwd_k<64, false, 4>(p, NH, NT, ws, st);
-  return mix ? launch_tile_fwd_k<128, true, 4>(p, NH, NT, ws, st) : launch_tile_fwd_k<128, false, 4>(p, NH, NT, ws, st);
+    return mix ? launch_tile_fwd_k<64, 1, 4>(p, NH, NT, nullptr, nullptr, st)
+               : launch_tile_fwd_k<64, 0, 4>(p, NH, NT, nullptr, nullptr, st);
+  return mix ? launch_tile_fwd_k<128, 1, 4>(p, NH, NT, nullptr, nullptr, st)
+             : launch_tile_fwd_k<128, 0, 4>(p, NH, NT, nullptr, nullptr, st);
 }
 
 }  // namespace spa

@@ -310,6 +310,19 @@ def test_prefill_cells_full_size_sampled_rows():
     _say(f"  exempt rows {_check_prefill(cfg, x, rows)}")
 
 
+def test_prefill_cells_many_heads_sampled_rows():
+    # 2 x 40 heads x 252 candidate cells: more (head, cell) entries than one
+    # pass of the unit scan holds (16384), so its chunk loop runs twice
+    cfg = config("prefill_cells", B=2, Hq=40, Hkv=40, n=8192, seed=27)
+    _say("[prefill] 2 x 40 heads, n = 8192, sampled rows")
+    x = make_inputs(cfg)
+    rng = np.random.Generator(np.random.PCG64(98))
+    n = x["L"]
+    rows = np.unique(np.concatenate([np.arange(0, 130), np.arange(n - 130, n),
+                                     rng.integers(0, n, 300)])).astype(np.int64)
+    _say(f"  exempt rows {_check_prefill(cfg, x, rows)}")
+
+
 # ------------------------------------------------------------------ training fwd + bwd
 def _train_case(cfg, x, kv_slice=-1, fwd_rows=None):
     b, K = cfg["b"], cfg["K"]
