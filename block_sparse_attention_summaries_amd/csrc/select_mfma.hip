@@ -83,26 +83,22 @@ __device__ __forceinline__ double erf_exact(double x) {
 // NTERM = 1: one head's bf16 query; NTERM = 3: split group-mean query.
 // List length: KMAX (no erf; fp32 ranking is final) or 2 KMAX (erf).
 template <int D, int KMAX, int NTERM, bool kErf>
-__global__ __launch_bounds__(256) void rows_select_mfma_kernel(
+__global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ? 3 : 1) void rows_select_mfma_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kbar, const float* __restrict__ max_norm,
     const float* __restrict__ centre, const float* __restrict__ erf_lambda,
     const float* __restrict__ erf_sigma, int Hq, int Hkv, int Hsel, int nq, int64_t q_pos0,
     int64_t ccap, int b, int prefix_mode, int qblock, int share_group, int K, int gate,
     int32_t* __restrict__ idx, float* __restrict__ logg, int32_t* __restrict__ k_eff) {
   constexpr int kT = 32;                  // candidates per tile
-  constexpr int kPitch = D + 8;           // LDS row pitch (bf16), breaks bank aliasing
   constexpr int kKS = D / 16;             // MFMA k-steps
-  constexpr int kVecs = kT * D / 8;       // 16-byte vectors per tile
-  constexpr int kPer = kVecs / 256;       // per thread
   constexpr int KL = kErf ? 2 * KMAX : KMAX;
-  static_assert(kVecs % 256 == 0 && (kPer == 1 || kPer == 2), "tile vectors split over 256 threads");
+  constexpr int kErfTab = 6144;           // filter table entries (24 KB): x = 4 within it for sigma <= ~766
   static_assert(!kErf || KL <= 16, "list staging uses 16 LDS slots per lane");
-  __shared__ __align__(16) __bf16 s_kb[kT * kPitch];
-  __shared__ float s_beta32[kT];
-  __shared__ float s_p[kT];
-  __shared__ float s_amax[kT];
+  __shared__ __align__(16) float s_beta32[4][kT];   // per wave: lambda a_c of the tile's candidates
+  __shared__ float s_p[4][kT];            // per wave: their centres (filter per score)
   __shared__ float s_sc[4][16][64];       // per wave: candidate slot r x lane
   __shared__ double s_x[4][64];           // per wave: half-row dot products
+  __shared__ float s_erf[kErf ? kErfTab : 1];   // filter erf by row - cell b (see below)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, ql = lane & 31;
@@ -120,16 +116,39 @@ __global__ __launch_bounds__(256) void rows_select_mfma_kernel(
   const int64_t ncand = row_ok ? num_candidates(pos, b, prefix_mode, qblock) : 0;
   const int last_row = ((rt * 4 + 4) * 32 < nq ? (rt * 4 + 4) * 32 : nq) - 1;
   const int64_t wg_cand = num_candidates(q_pos0 + last_row, b, prefix_mode, qblock);
+  // the wave walks the candidates of its own rows (its last row has the most)
+  const int wave_last = ((rt * 4 + wave + 1) * 32 < nq ? (rt * 4 + wave + 1) * 32 : nq) - 1;
+  const int64_t wave_cand = wave_last >= (rt * 4 + wave) * 32 ? num_candidates(q_pos0 + wave_last, b, prefix_mode, qblock) : 0;
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const __bf16* kb = kbar + (static_cast<int64_t>(bi) * Hkv + kvh) * ccap * D;
   const float* mn = max_norm + (static_cast<int64_t>(bi) * Hkv + kvh) * ccap;
   double lam = 0.0, inv2sig = 0.0;
   float lam32 = 0.f, inv2sig32 = 0.f;
+  bool use_tab = false;
   if constexpr (kErf) {
     lam = static_cast<double>(erf_lambda[hs]);
     lam32 = erf_lambda[hs];
     inv2sig = 1.0 / (2.0 * static_cast<double>(erf_sigma[hs]));
     inv2sig32 = static_cast<float>(inv2sig);
+    // With the centres c b + (b - 1) / 2 the filter's argument is
+    // ((row - c b) - (b - 1) / 2) / (2 sigma), both differences exact in fp32:
+    // the filter value is a function of j = row - c b, tabulated in LDS with
+    // the same fp32 arithmetic (bit-identical scores).  j past the table holds
+    // x >= 4, where the filter is 1.  Other centres, or a sigma whose x = 4
+    // lies past the table, take the filter per score.
+    const float hb = static_cast<float>(b - 1) * 0.5f;
+    int ok = 1;
+    for (int64_t c = tid; c < wg_cand; c += 256)
+      ok &= centre[c] == static_cast<float>(c * b) + hb ? 1 : 0;
+    ok &= (static_cast<float>(kErfTab - 1) - hb) * inv2sig32 >= 4.0f ? 1 : 0;
+    ok &= static_cast<int64_t>(wg_cand) * b < (1 << 23) && q_pos0 + nq < (1 << 23) ? 1 : 0;
+    use_tab = __builtin_amdgcn_readfirstlane(__syncthreads_and(ok)) != 0;
+    if (use_tab) {
+      for (int j = tid; j < kErfTab; j += 256) {
+        const float x32 = (static_cast<float>(j) - hb) * inv2sig32;
+        s_erf[j] = x32 < 4.0f ? erf_filter(x32) : 1.0f;
+      }
+    }
   }
 
   // this lane's query slices (k = 16 ks + 8 hl .. +7) as NTERM bf16 terms
@@ -195,52 +214,47 @@ __global__ __launch_bounds__(256) void rows_select_mfma_kernel(
     li[t] = 0x7FFFFFFF;
   }
   float m_run = -INFINITY, l_run = 0.f;   // gate LSE over this lane's candidates
-  float amax_t = 0.f;                     // staging threads: largest max-norm seen
+  float amax_t = 0.f;                     // lanes 0..31: largest max norm staged
 
-  // next tile's summaries, fetched one tile ahead (rows clamped in range);
-  // thread tid moves 16-byte vectors tid and tid + 256 of the tile
-  uint4 pre0, pre1 = make_uint4(0, 0, 0, 0);
+  // Each wave runs on its own (no workgroup barrier in the walk): the lane's
+  // A operand (candidate c0 + ql, columns 16 ks + 8 hl .. +7) comes straight
+  // from memory, one tile ahead; lanes 0..31 stage the tile's lambda a_c (and
+  // centres) in the wave's LDS slice.
+  uint4 ka[kKS];
   float pre_a = 0.f, pre_p = 0.f;
-  const int v_row0 = tid / (D / 8), v_row1 = (tid + 256) / (D / 8), v_col = (tid % (D / 8)) * 8;
 #define SPA_FETCH_TILE(C0)                                                                    \
   do {                                                                                        \
-    int64_t c = (C0) + v_row0;                                                                \
-    pre0 = *reinterpret_cast<const uint4*>(kb + (c < wg_cand ? c : wg_cand - 1) * D + v_col); \
-    if constexpr (kPer == 2) {                                                                \
-      c = (C0) + v_row1;                                                                      \
-      pre1 = *reinterpret_cast<const uint4*>(kb + (c < wg_cand ? c : wg_cand - 1) * D + v_col); \
-    }                                                                                         \
-    if (kErf && tid < kT) {                                                                   \
-      c = (C0) + tid;                                                                         \
-      c = c < wg_cand ? c : wg_cand - 1;                                                      \
+    int64_t c = (C0) + ql;                                                                    \
+    c = c < wave_cand ? c : wave_cand - 1;                                                    \
+    _Pragma("unroll") for (int ks = 0; ks < kKS; ++ks)                                        \
+      ka[ks] = *reinterpret_cast<const uint4*>(kb + c * D + 16 * ks + 8 * hl);                \
+    if constexpr (kErf) {                                                                     \
       pre_a = mn[c];                                                                          \
       pre_p = centre[c];                                                                      \
     }                                                                                         \
   } while (0)
-  if (wg_cand > 0) SPA_FETCH_TILE(0);
+  if (wave_cand > 0) SPA_FETCH_TILE(0);
 
-  for (int64_t c0 = 0; c0 < wg_cand; c0 += kT) {
-    lds_barrier();                        // readers of the previous tile are done
-    *reinterpret_cast<uint4*>(&s_kb[v_row0 * kPitch + v_col]) = pre0;
-    if constexpr (kPer == 2) *reinterpret_cast<uint4*>(&s_kb[v_row1 * kPitch + v_col]) = pre1;
-    if (kErf && tid < kT) {
-      s_beta32[tid] = lam32 * pre_a;
-      s_p[tid] = pre_p;
-      amax_t = fmaxf(amax_t, fabsf(pre_a));
+  for (int64_t c0 = 0; c0 < wave_cand; c0 += kT) {
+    if constexpr (kErf) {
+      wave_lds_sync();                    // the previous tile's readers are done
+      if (hl == 0) {
+        s_beta32[wave][ql] = lam32 * pre_a;
+        s_p[wave][ql] = pre_p;
+        amax_t = fmaxf(amax_t, fabsf(pre_a));
+      }
+      wave_lds_sync();
     }
-    lds_barrier();
-    SPA_FETCH_TILE(c0 + kT < wg_cand ? c0 + kT : c0);
-
     sfloatx16_t st;
 #pragma unroll
     for (int r = 0; r < 16; ++r) st[r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      const uint4 a = *reinterpret_cast<const uint4*>(&s_kb[ql * kPitch + 16 * ks + 8 * hl]);
 #pragma unroll
       for (int t = 0; t < NTERM; ++t)
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sel_bf16x8(a), sel_bf16x8(qt[t][ks]), st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sel_bf16x8(ka[ks]), sel_bf16x8(qt[t][ks]), st, 0, 0, 0);
     }
+    if (c0 + kT < wave_cand) SPA_FETCH_TILE(c0 + kT);
 
     // register r holds candidate c0 + 8 (r / 4) + 4 hl + (r % 4) of this lane's
     // row.  Pass 1 (unrolled): scores, gate terms and the admission mask
@@ -248,15 +262,36 @@ __global__ __launch_bounds__(256) void rows_select_mfma_kernel(
     float sv[16];
     uint32_t mask = 0;
     const float thr = ls[KL - 1];
+    // erf bias terms of the lane's 16 candidates, their loads issued together:
+    // m = 8 (r / 4) + 4 hl + (r % 4), so lambda a_c comes as four 16-byte reads
+    float e32[16];
+    float4 bet[4];
+    if constexpr (kErf) {
+      const int jb = static_cast<int>(pos - (c0 + 4 * hl) * b);   // j of candidate m = 4 hl
+      if (use_tab) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = jb - (8 * (r >> 2) + (r & 3)) * b;
+          e32[r] = s_erf[j < 0 ? 0 : (j < kErfTab ? j : kErfTab - 1)];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x32 = (static_cast<float>(pos) - s_p[wave][8 * (r >> 2) + 4 * hl + (r & 3)]) * inv2sig32;
+          e32[r] = x32 < 4.0f ? erf_filter(x32) : 1.0f;
+        }
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) bet[q4] = *reinterpret_cast<const float4*>(&s_beta32[wave][8 * q4 + 4 * hl]);
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = 8 * (r >> 2) + 4 * hl + (r & 3);
       float s = st[r] * scale;
       if constexpr (kErf) {
-        const float x32 = (static_cast<float>(pos) - s_p[m]) * inv2sig32;
-        float e32 = 1.0f;
-        if (x32 < 4.0f) e32 = erf_filter(x32);
-        s = fmaf(s_beta32[m], e32, s);
+        const float4 bq = bet[r >> 2];
+        const float bm = (r & 3) == 0 ? bq.x : (r & 3) == 1 ? bq.y : (r & 3) == 2 ? bq.z : bq.w;
+        s = fmaf(bm, e32[r], s);
       }
       s_sc[wave][r][lane] = s;
       const bool valid = c0 + m < ncand;
@@ -277,11 +312,21 @@ __global__ __launch_bounds__(256) void rows_select_mfma_kernel(
     }
     // within a lane candidates arrive in increasing index, so a tie keeps the
     // entry already held
-    while (mask != 0) {
-      const int r = __builtin_ctz(mask);
+    // (the next admitted slot's LDS read is issued before the current insert)
+    if (mask != 0) {
+      int r = __builtin_ctz(mask);
       mask &= mask - 1;
-      const float v = s_sc[wave][r][lane];
-      if (v > ls[KL - 1]) topk_push_later(ls, li, v, static_cast<int>(c0) + 8 * (r >> 2) + 4 * hl + (r & 3));
+      float v = s_sc[wave][r][lane];
+      while (true) {
+        const bool more = mask != 0;
+        const int rn = more ? __builtin_ctz(mask) : r;
+        mask &= mask - 1;
+        const float vn = s_sc[wave][rn][lane];
+        if (v > ls[KL - 1]) topk_push_later(ls, li, v, static_cast<int>(c0) + 8 * (r >> 2) + 4 * hl + (r & 3));
+        if (!more) break;
+        r = rn;
+        v = vn;
+      }
     }
   }
 #undef SPA_FETCH_TILE
@@ -307,10 +352,6 @@ __global__ __launch_bounds__(256) void rows_select_mfma_kernel(
     bitonic_clean_best_first(ls, li);
     const float m2 = xor_lanes_f<32>(m_run), l2 = xor_lanes_f<32>(l_run);
     ml_combine(m_run, l_run, m2, l2);
-  }
-  if constexpr (kErf) {
-    if (tid < kT) s_amax[tid] = amax_t;
-    lds_barrier();
   }
   // both half-waves of a row hold the same merged list from here on
   if (!row_ok) return;
@@ -339,9 +380,7 @@ __global__ __launch_bounds__(256) void rows_select_mfma_kernel(
     // fp32 accumulation of d NTERM products (<= (d NTERM + 2) 2^-24 |q|
     // |kbar_c| / sqrt(d), with |kbar_c| <= a_c).  E takes each term at least
     // 4x wider.
-    float amax = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < kT; ++i) amax = fmaxf(amax, s_amax[i]);
+    const float amax = wave_max(amax_t);   // every candidate this wave's rows scored
     float smax = 0.f;
 #pragma unroll
     for (int t = 0; t < KL; ++t)
@@ -353,6 +392,10 @@ __global__ __launch_bounds__(256) void rows_select_mfma_kernel(
     // a dropped candidate scored at most ls[KL - 1]: if that is inside the band,
     // the list may be missing one of the exact top-K
     const bool rescan = ncand > KL && ls[KL - 1] >= cut;
+    // gate off: only the set matters.  If the (K+1)-th listed score is below
+    // the band, every candidate outside the first K scores exactly below every
+    // one inside (|exact - fp32| <= err), so the first K are the exact top-K.
+    const bool decided = !gate && (ncand <= K || ls[K] < cut);
     // the qualifying entries are a prefix of the best-first list
     int* slot = reinterpret_cast<int*>(&s_sc[wave][0][0]);
     int n_ok = 0;
@@ -374,7 +417,7 @@ __global__ __launch_bounds__(256) void rows_select_mfma_kernel(
       ei[t] = 0x7FFFFFFF;
     }
     const double inv_sqrt_d = 1.0 / sqrt(static_cast<double>(D));
-    const int64_t nsrc = rescan ? ncand : n_ok;
+    const int64_t nsrc = decided ? 0 : (rescan ? ncand : n_ok);
     uint4 kv[kKS];
     float cen = 0.f, anorm = 0.f;
     int c = 0;
@@ -421,6 +464,13 @@ __global__ __launch_bounds__(256) void rows_select_mfma_kernel(
     }
 #undef SPA_LOAD_CAND
     if (hl != 0) return;
+    if (decided) {
+#pragma unroll
+      for (int t = 0; t < KMAX; ++t) {
+        es[t] = t < K ? static_cast<double>(ls[t]) : -INFINITY;
+        ei[t] = t < K ? li[t] : 0x7FFFFFFF;
+      }
+    }
 #pragma unroll
     for (int t = 0; t < KMAX; ++t)
       if (t >= keff) ei[t] = 0x7FFFFFFF;

@@ -487,7 +487,7 @@ def test_one_workspace_shared_across_shapes_and_entry_points():
 
 
 # ------------------------------------------------------------------ selection alone (row kernels)
-def _select_only(cfg, x, *, gate, share_group, erf=True, prefix_mode=1, rows=None):
+def _select_only(cfg, x, *, gate, share_group, erf=True, prefix_mode=1, rows=None, centre_shift=None):
     b, qb, K = cfg["b"], cfg.get("qblock", 128), cfg["K"]
     Hsel = cfg["Hkv"] if share_group else cfg["Hq"]
     kw = dict(Hkv=cfg["Hkv"], b=b, K=K, q_pos0=0, gate=gate, prefix_mode=prefix_mode, qblock=qb,
@@ -498,8 +498,12 @@ def _select_only(cfg, x, *, gate, share_group, erf=True, prefix_mode=1, rows=Non
         sig = np.ascontiguousarray(x["erf_sigma"][:Hsel])
         ekw = dict(erf_lambda=lam, erf_sigma=sig)
     kb_o, mx_o, ce_o = oracle.block_summaries(x["k"], b, nblocks=x["L"] // b)
+    if centre_shift is not None:
+        ce_o = (ce_o + np.float32(centre_shift)).astype(np.float32)
     ora = oracle.score_select(x["q"], kb_o, mx_o, ce_o, rows=rows, **kw, **ekw)
     kb_g, mx_g, ce_g = ops.sparse_block_summaries(dev(x["k"]), b)
+    if centre_shift is not None:
+        ce_g = dev(ce_o)
     idx_g, logg_g, keff_g = ops.sparse_score_select(dev(x["q"]), kb_g, mx_g, ce_g, **kw,
                                                     **{k: dev(v) for k, v in ekw.items()})
     torch.cuda.synchronize()
@@ -528,6 +532,19 @@ def test_select_erf_group_gate_parity(over):
     _say(f"[select erf group gate] {over}")
     x = make_inputs(cfg)
     _say(f"  exempt rows {_select_only(cfg, x, gate=True, share_group=True)}")
+
+
+@pytest.mark.parametrize("over,shift", [
+    (dict(n=1536, Hq=2, Hkv=2, seed=58), 0.25),                 # centres off c b + (b - 1) / 2
+    (dict(n=1536, Hq=2, Hkv=2, sigma=3000.0, seed=59), None),  # x = 4 past the filter table
+])
+def test_select_erf_filter_per_score(over, shift):
+    """The erf filter evaluated per score instead of read from the table of
+    row - cell b (centres not at the cell middles, or a sigma too wide)."""
+    cfg = config("prefill_cells", **over)
+    _say(f"[select erf per score] {over} shift={shift}")
+    x = make_inputs(cfg)
+    _say(f"  exempt rows {_select_only(cfg, x, gate=False, share_group=False, centre_shift=shift)}")
 
 
 def test_select_erf_identical_keys():
