@@ -380,10 +380,14 @@ def run_prefill(reps):
     ws1, ws2 = ops.Workspace(), ops.Workspace()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     times = []
+    kb, mx, ce = ops.sparse_block_summaries(k, b)      # output buffers, rewritten in full by every call
 
     def once():
+        # a spin kernel ahead of the timed calls lets the host queue them all,
+        # so the events time the GPU work, not Python's launch overhead
+        torch.cuda._sleep(1_000_000)
         ev[0].record()
-        kb, mx, ce = ops.sparse_block_summaries(k, b)
+        ops.sparse_block_summaries(k, b, kbar=kb, max_norm=mx, centre=ce)
         ev[1].record()
         idx, _, _ = ops.sparse_score_select(q, kb, mx, ce, Hkv=cfg["Hkv"], b=b, K=K, q_pos0=0, gate=False,
                                             prefix_mode=1, qblock=qb, share_group=False,
@@ -415,9 +419,12 @@ def run_train(reps):
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     times = []
 
+    kb, mx, ce = ops.sparse_block_summaries(k, b)      # output buffers, rewritten in full by every call
+
     def once():
+        torch.cuda._sleep(1_000_000)                   # the host queues the calls ahead of the GPU
         ev[0].record()
-        kb, mx, ce = ops.sparse_block_summaries(k, b)
+        ops.sparse_block_summaries(k, b, kbar=kb, max_norm=mx, centre=ce)
         idx, logg, _ = ops.sparse_score_select(q, kb, mx, ce, Hkv=cfg["Hkv"], b=b, K=K, q_pos0=0,
                                                gate=True, workspace=ws[0])
         ev[1].record()

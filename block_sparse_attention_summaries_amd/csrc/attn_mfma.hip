@@ -410,10 +410,12 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
   const int hl = lane >> 5, ql = lane & 31;              // half-wave, query lane
   const int G = Hq / Hkv;
   const int hgroups = G / NH;
-  // XCD-aware order in the selected-block mode, where every tile of a head
-  // reads from the same keys (measured faster); the window mode keeps the
-  // dispatch order (measured faster there)
-  const uint2 bxy = kMix ? make_uint2(blockIdx.x, blockIdx.y) : xcd_block_xy();
+  // XCD-aware order (a head's consecutive row tiles on one XCD share its L2):
+  // the selected-block mode, where every tile of a head reads from the same
+  // keys, and the window walk with the cells apart, where consecutive tiles'
+  // windows overlap; the per-tile cell walk keeps the dispatch order
+  // (measured faster there)
+  const uint2 bxy = kMode == 1 ? make_uint2(blockIdx.x, blockIdx.y) : xcd_block_xy();
   const int bz = static_cast<int>(bxy.y);
   const int bi = bz / (Hkv * hgroups);
   const int kvh = (bz / hgroups) % Hkv;
