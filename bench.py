@@ -674,6 +674,8 @@ def main():
                     help="time only the one-call decode step (no two-call or paged comparison); for profiling")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB device copy (for scaling rocprofv3 byte counters)")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="run only the prefill_cells pipeline --steps times and print its figures; for profiling")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM counters file from two rocprofv3 --pmc CSVs and exit")
     args = ap.parse_args()
@@ -685,6 +687,13 @@ def main():
                  "(see the sharding note in the design document); run with --gpus 1")
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     ops.lib()
+    if args.only_prefill:
+        if args.calibrate_copy:
+            calibrate_copy()
+        pf = run_prefill(args.steps)
+        print(json.dumps({"prefill_tokens_per_s": round(pf["tokens_per_s"], 1),
+                          "prefill_ms": {k: round(float(v), 4) for k, v in pf["ms"].items()}}))
+        return
 
     res = run_decode(args)
     if args.calibrate_copy:
