@@ -582,9 +582,58 @@ def run_cpu_baseline(res, seconds):
         oracle.attn_fwd(qn, x["k"], x["v"], sel["idx"], sel["logg"], b=b, K=K, q_pos0=pos)
         n += 1
     dt = time.time() - t0
+    # the same step at shorter contexts (the query earlier in the same cache):
+    # the fitted exponent of time against context length
+    ctx, ts = [], []
+    for lg in range(15, 20):                     # 32K .. 512K tokens before the current block
+        p_ctx = (1 << lg) + b - 1
+        if p_ctx >= x["L"]:
+            break
+        m, t1 = 0, time.time()
+        while m < 2 or time.time() - t1 < seconds / 10:
+            qn = np.ascontiguousarray(qs[m % 64])
+            sel = oracle.score_select(qn, kb, mx, ce, Hkv=cfg["Hkv"], b=b, K=K, q_pos0=p_ctx, gate=True,
+                                      proj_w=x["proj_w"])
+            oracle.attn_fwd(qn, x["k"], x["v"], sel["idx"], sel["logg"], b=b, K=K, q_pos0=p_ctx)
+            m += 1
+        ctx.append(p_ctx + 1)
+        ts.append((time.time() - t1) / m)
+    expo = float(np.polyfit(np.log(ctx), np.log(ts), 1)[0])
     return dict(value=dt / n * 1e6, unit="us/step", cores=oracle.num_threads(), kind="oracle",
                 sample=f"{n} decode steps of layer 0 (512K context, 8 kv heads, C=8192, K=32), "
-                       f"rotating 64 queries; block summaries precomputed")
+                       f"rotating 64 queries; block summaries precomputed",
+                context_scaling={"contexts": ctx, "us_per_step": [round(t * 1e6, 1) for t in ts],
+                                 "fitted_exponent": round(expo, 3)})
+
+
+def measure_device_peaks():
+    """Measured references next to the vendor peaks: a 1 GiB device copy
+    (read + write bytes per second) and a bf16 8192^3 GEMM (torch / hipBLASLt)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    a = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
+    bm = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
+
+    def best(fn, reps=5):
+        fn()
+        out = []
+        for _ in range(reps):
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            out.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        return min(out)
+
+    t_copy = best(lambda: dst.copy_(src))
+    t_gemm = best(lambda: torch.mm(a, bm))
+    res = {"hbm_copy_gbps": round(2 * src.numel() * 2 / t_copy / 1e9, 1),
+           "bf16_gemm_tflops": round(2 * 8192 ** 3 / t_gemm / 1e12, 1),
+           "vendor_hbm_gbps": HBM_PEAK_GBPS, "vendor_bf16_tflops": BF16_PEAK_TFLOPS}
+    del src, dst, a, bm
+    torch.cuda.empty_cache()
+    return res
 
 
 def hbm_traffic(kernel, algorithmic):
@@ -775,6 +824,7 @@ def main():
         tr = run_train(2)
         out["train_tokens_per_s"] = round(tr["tokens_per_s"], 1)
         out["train_ms"] = {k: round(v, 3) for k, v in tr["ms"].items()}
+    out["device_peaks_measured"] = measure_device_peaks()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = run_cpu_baseline(res, args.cpu_seconds)
     print(json.dumps(out), flush=True)

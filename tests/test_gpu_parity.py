@@ -291,6 +291,7 @@ def _check_prefill(cfg, x, rows=None):
     dict(n=1024, Hq=8, Hkv=2, share_group=True, seed=24),            # a group of 4 sharing the selection
     dict(n=768, Hq=4, Hkv=2, share_group=True, b=64, seed=25),       # cells of two key tiles, group of 2
     dict(n=1024, Hq=2, Hkv=2, gate=True, seed=26),                   # log-gate bias on the cells
+    dict(n=100, Hq=2, Hkv=2, seed=28),                               # inside the first query block: no cells
 ])
 def test_prefill_cells_parity(over):
     cfg = config("prefill_cells", **over)
