@@ -406,8 +406,13 @@ def run_prefill(reps):
     n = x["L"]
     # algorithmic work: 2d flops per causal (query, cell) score; 4d per (q, k) pair
     scores = sum((qb * (i // qb)) // b for i in range(n)) * cfg["Hq"]      # causal (query, cell) pairs
+    # attention: 4d flops per (query, key) pair of branch L (K cells of b keys
+    # once there are that many candidates) and of the window
+    routed = sum(min(cfg["K"], (qb * (i // qb)) // b) * b for i in range(n))
+    window = sum(min(cfg["window"], i + 1) for i in range(n))
+    attn_gflop = 4 * cfg["d"] * (routed + window) * cfg["Hq"] / 1e9
     return dict(ms=dict(summaries=t[0], score_select=t[1], attention=t[2]),
-                tokens_per_s=n / (t.sum() * 1e-3), score_gflop=2 * cfg["d"] * scores / 1e9)
+                tokens_per_s=n / (t.sum() * 1e-3), score_gflop=2 * cfg["d"] * scores / 1e9, attn_gflop=attn_gflop)
 
 
 def run_train(reps):
@@ -446,7 +451,13 @@ def run_train(reps):
         times.append(once())
     t = np.median(np.array(times), axis=0)
     tokens = cfg["B"] * x["L"]
-    return dict(ms=dict(select=t[0], fwd=t[1], bwd=t[2], select_bwd=t[3]), tokens_per_s=tokens / (t.sum() * 1e-3))
+    # kept (query, key) pairs: the causal part of the current block plus the
+    # K_eff = min(K, blocks before it) selected blocks; fwd 4d flops per pair,
+    # bwd 14d (dq: S, dP, dQ; dk/dv: S, dP, dV, dK)
+    n = x["L"]
+    pairs = sum(i % b + 1 + min(K, i // b) * b for i in range(n)) * cfg["B"] * cfg["Hq"]
+    return dict(ms=dict(select=t[0], fwd=t[1], bwd=t[2], select_bwd=t[3]), tokens_per_s=tokens / (t.sum() * 1e-3),
+                fwd_tflop=4 * cfg["d"] * pairs / 1e12, bwd_tflop=14 * cfg["d"] * pairs / 1e12)
 
 
 def run_fsl_decode(steps, n_layers=4, n_queries=32):
@@ -824,6 +835,12 @@ def main():
         tr = run_train(2)
         out["train_tokens_per_s"] = round(tr["tokens_per_s"], 1)
         out["train_ms"] = {k: round(v, 3) for k, v in tr["ms"].items()}
+        # algorithmic flops / time / dense bf16 peak (the kernels also execute
+        # masked tile work: the union of a row tile's selections)
+        out["mfma_frac"] = {
+            "prefill_attention": round(pf["attn_gflop"] / (pf["ms"]["attention"] * 1e-3) / (BF16_PEAK_TFLOPS * 1e3), 5),
+            "train_fwd": round(tr["fwd_tflop"] / (tr["ms"]["fwd"] * 1e-3) / BF16_PEAK_TFLOPS, 5),
+            "train_bwd": round(tr["bwd_tflop"] / (tr["ms"]["bwd"] * 1e-3) / BF16_PEAK_TFLOPS, 5)}
     out["device_peaks_measured"] = measure_device_peaks()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = run_cpu_baseline(res, args.cpu_seconds)
