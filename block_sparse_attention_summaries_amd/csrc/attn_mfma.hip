@@ -811,12 +811,16 @@ bool attn_tile_fwd_supported(const AttnLaunch& p) {
          (p.L + kKT - 1) / kKT <= kMaxKeyTiles && (p.d == 64 || p.d == 128);
 }
 
-// The cell-major branch L: mix mode, cells of one or two key tiles, and a
-// selection shared by the kv head's query heads (or one query head per kv head).
+// The cell-major branch L: mix mode, cells of one or two key tiles, a
+// selection shared by the kv head's query heads (or one query head per kv
+// head), and partials (K per row and query head) of at most 16 GiB; otherwise
+// the tile kernel walks each row tile's cells itself.
+constexpr size_t kMaxCellPartialBytes = static_cast<size_t>(16) << 30;
 static bool use_cell_path(const AttnLaunch& p) {
   const int G = p.Hq / p.Hkv;
+  const size_t parts = static_cast<size_t>(p.B) * p.Hq * p.nq * p.K;
   return p.window > 0 && p.alpha != nullptr && (p.b == 32 || p.b == 64) && G <= 4 && (p.share_group || G == 1) &&
-         p.K >= 1;
+         p.K >= 1 && parts * (p.d * sizeof(__bf16) + sizeof(float2)) <= kMaxCellPartialBytes;
 }
 
 struct CellWs {

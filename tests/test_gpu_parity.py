@@ -292,6 +292,9 @@ def _check_prefill(cfg, x, rows=None):
     dict(n=768, Hq=4, Hkv=2, share_group=True, b=64, seed=25),       # cells of two key tiles, group of 2
     dict(n=1024, Hq=2, Hkv=2, gate=True, seed=26),                   # log-gate bias on the cells
     dict(n=100, Hq=2, Hkv=2, seed=28),                               # inside the first query block: no cells
+    # the cells walked per row tile (no cell-major branch L):
+    dict(n=1024, Hq=4, Hkv=2, share_group=False, seed=29),           # a group's heads select independently
+    dict(n=768, Hq=2, Hkv=2, b=16, qblock=64, seed=30),              # cells of 16 keys
 ])
 def test_prefill_cells_parity(over):
     cfg = config("prefill_cells", **over)
