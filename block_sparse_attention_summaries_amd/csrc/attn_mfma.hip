@@ -54,6 +54,9 @@ struct TileSmem {
 // Selection data of one (wave) query tile: per row the ascending units and
 // their log gates, read with a cursor as key tiles ascend.
 constexpr int kMaxSelK = 32;
+// Online softmax of the tile walk: largest exponent (log2) a probability may
+// take above the reference max before the reference moves.
+constexpr float kLazyMax = 8.0f;
 
 // ------------------------------------------------- routed cells, cell-major
 // Mix mode (routed cells + window) computes branch L per cell instead of per
@@ -669,7 +672,10 @@ _Pragma("unroll")                                                               
 _Pragma("unroll")                                                                                        \
         for (int r = 1; r < 16; ++r) mt = fmaxf(mt, z[r]);                                               \
         mt = fmaxf(mt, xor_lanes_f<32>(mt));                                                             \
-        const float mnew = fmaxf(m2, mt);                                                                \
+        /* the reference max moves only when the tile's max passes it by more */                       \
+        /* than kLazyMax (log2 domain): p <= 2^kLazyMax, and most tiles skip */                          \
+        /* the accumulator rescale (corr = 1) */                                                         \
+        const float mnew = mt > m2 + kLazyMax ? mt : m2;                                                 \
         /* hardware exp2 (exp2(-inf) = 0); a row with no key yet keeps zeros */                          \
         const float msub = mnew == -INFINITY ? 0.f : mnew;                                               \
         const float corr = __builtin_amdgcn_exp2f(m2 - msub);                                            \
