@@ -18,6 +18,13 @@
 // B operand of O^T += V^T P^T for keys 16s + 8h .. +7 (h = half-wave), whose
 // A operand is then one 16-byte read of the transposed V tile.  Per-row
 // masks / biases come from a cursor walk over the row's ascending selection.
+//
+// Window mode with routed cells of 32 or 64 keys: branch L is computed
+// cell-major instead (the cells a row tile's rows select are ~10x the 4 a row
+// reads): the rows that selected each cell are listed, 32 at a time, and one
+// wave per such unit writes each row's softmax partial over the cell; the
+// tile kernel then walks the window band alone and merges a row's partials
+// into o_L before the mix (kMode 2; see the routed-cells section below).
 #include <type_traits>
 
 #include "spa_device.h"

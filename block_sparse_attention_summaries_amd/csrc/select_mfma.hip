@@ -6,10 +6,12 @@
 // position bias lambda_h a_c erf((i - p_c)/(2 sigma_h))).
 //
 // A workgroup of 4 waves covers 128 query rows (4 tiles of 32) of one
-// selection head.  Per tile of 32 candidates, S^T = Kbar Q^T (candidates x
-// queries) gives each lane one query row and 16 candidates, so every lane
-// keeps its row's running top list and gate (max, sum exp) in registers; the
-// two half-waves of a row merge at the end.
+// selection head; each wave walks its own rows' candidates without workgroup
+// barriers (the A operand rows come straight from memory, one tile ahead).
+// Per tile of 32 candidates, S^T = Kbar Q^T (candidates x queries) gives each
+// lane one query row and 16 candidates, so every lane keeps its row's running
+// top list and gate (max, sum exp) in registers; the two half-waves of a row
+// merge at the end.
 //
 // Group selection scores with the mean query of the G heads, which is not a
 // bf16 value: it is formed in fp32 and split into three bf16 terms
@@ -17,12 +19,14 @@
 // fp32 dot product to within fp32 rounding.
 //
 // erf term: the bias reaches ~10, where fp32 cannot rank to 1e-6.  The scan
-// ranks fp32 scores (a branch-free erf approximation) in a list twice the
-// budget long.  At the
-// end, list entries within twice a proven error bound of the fp32 K-th best
-// are re-scored exactly (fp64 dot product and bias) and the exact top-K is
-// taken from them.  If the list's last entry is itself within that band, a
-// candidate may have been dropped, and the row is re-scored exactly in full.
+// ranks fp32 scores (a branch-free erf approximation, read from a per-
+// workgroup table of row - cell b when the centres are the cell middles) in a
+// list twice the budget long.  At the end, list entries within twice a proven
+// error bound of the fp32 K-th best are re-scored exactly (fp64 dot product
+// and bias) and the exact top-K is taken from them; with the gate off, a row
+// whose (K+1)-th entry lies below that band keeps its first K entries as they
+// are.  If the list's last entry is itself within the band, a candidate may
+// have been dropped, and the row is re-scored exactly in full.
 #include "spa_device.h"
 #include "spa_launch.h"
 
