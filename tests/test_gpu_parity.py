@@ -238,6 +238,50 @@ def test_decode_is_deterministic():
     assert np.array_equal(a["o"], b["o"])
 
 
+def test_prefill_and_training_are_deterministic():
+    """Two runs of the prefill pipeline (cells + window) and of training fwd +
+    bwd give bit-identical outputs: no atomics reach an output, and the
+    cell-major branch L lists its rows in row order."""
+    cfg = config("prefill_cells", n=4096, Hq=4, Hkv=4, seed=31)
+    _say("[determinism] prefill_cells n=4096, 4 heads; train B=1 n=1024")
+    x = make_inputs(cfg)
+    b, qb, K = cfg["b"], cfg["qblock"], cfg["K"]
+    qd, kd, vd = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    lam, sig, alpha = dev(x["erf_lambda"]), dev(x["erf_sigma"]), dev(x["alpha"])
+
+    def prefill():
+        kb, mx, ce = ops.sparse_block_summaries(kd, b)
+        idx, _, _ = ops.sparse_score_select(qd, kb, mx, ce, Hkv=cfg["Hkv"], b=b, K=K, q_pos0=0, gate=False,
+                                            prefix_mode=1, qblock=qb, share_group=False, erf_lambda=lam,
+                                            erf_sigma=sig)
+        o, lse = ops.sparse_attn_fwd(qd, kd, vd, idx, None, b=b, K=K, q_pos0=0, share_group=False, local=1,
+                                     window=cfg["window"], alpha=alpha, prefix_mode=1, qblock=qb)
+        torch.cuda.synchronize()
+        return [host(t) for t in (idx, o, lse)]
+
+    a, c = prefill(), prefill()
+    for u, w in zip(a, c):
+        assert np.array_equal(u.view(np.uint8), w.view(np.uint8))
+    cfg = config("train", B=1, n=1024, Hq=8, Hkv=2, seed=32)
+    x = make_inputs(cfg)
+    b, K = cfg["b"], cfg["K"]
+    qd, kd, vd, dod = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["dout"])
+
+    def train():
+        kb, mx, ce = ops.sparse_block_summaries(kd, b)
+        idx, logg, _ = ops.sparse_score_select(qd, kb, mx, ce, Hkv=cfg["Hkv"], b=b, K=K, q_pos0=0, gate=True,
+                                               share_group=True)
+        akw = dict(b=b, K=K, q_pos0=0, share_group=True)
+        o, lse = ops.sparse_attn_fwd(qd, kd, vd, idx, logg, **akw)
+        dq, dk, dv, dg = ops.sparse_attn_bwd(qd, kd, vd, idx, logg, o, dod, lse, **akw)
+        torch.cuda.synchronize()
+        return [host(t) for t in (idx, logg, o, lse, dq, dk, dv, dg)]
+
+    a, c = train(), train()
+    for u, w in zip(a, c):
+        assert np.array_equal(u.view(np.uint8), w.view(np.uint8))
+
+
 # ------------------------------------------------------------------ prefill with cells
 def _prefill_run(cfg, x, rows=None):
     b, qb = cfg["b"], cfg["qblock"]
