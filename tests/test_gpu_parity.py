@@ -282,6 +282,53 @@ def test_prefill_and_training_are_deterministic():
         assert np.array_equal(u.view(np.uint8), w.view(np.uint8))
 
 
+def test_gpu_no_future_leak():
+    """Rows up to i give bit-identical selections and outputs when every token
+    after i is redrawn (prefill with cells, training forward): no kernel lets
+    a later token reach an earlier row, also through a workgroup's shared
+    tiles, units or bounds."""
+    rng = np.random.Generator(np.random.PCG64(33))
+    for name, over in (("prefill_cells", dict(n=4096, Hq=4, Hkv=4, seed=34)),
+                       ("train", dict(B=1, n=1024, Hq=8, Hkv=2, seed=35))):
+        cfg = config(name, **over)
+        _say(f"[causality] {name} {over}")
+        x = make_inputs(cfg)
+        b, K = cfg["b"], cfg["K"]
+        n = x["L"]
+        pre = name == "prefill_cells"
+
+        def run(x):
+            qd, kd, vd = dev(x["q"]), dev(x["k"]), dev(x["v"])
+            kb, mx, ce = ops.sparse_block_summaries(kd, b)
+            if pre:
+                skw = dict(Hkv=cfg["Hkv"], b=b, K=K, q_pos0=0, gate=False, prefix_mode=1, qblock=cfg["qblock"],
+                           share_group=False, erf_lambda=dev(x["erf_lambda"]), erf_sigma=dev(x["erf_sigma"]))
+                idx, logg, _ = ops.sparse_score_select(qd, kb, mx, ce, **skw)
+                o, lse = ops.sparse_attn_fwd(qd, kd, vd, idx, None, b=b, K=K, q_pos0=0, share_group=False,
+                                             local=1, window=cfg["window"], alpha=dev(x["alpha"]), prefix_mode=1,
+                                             qblock=cfg["qblock"])
+            else:
+                idx, logg, _ = ops.sparse_score_select(qd, kb, mx, ce, Hkv=cfg["Hkv"], b=b, K=K, q_pos0=0,
+                                                       gate=True, share_group=True)
+                o, lse = ops.sparse_attn_fwd(qd, kd, vd, idx, logg, b=b, K=K, q_pos0=0, share_group=True)
+            torch.cuda.synchronize()
+            return [host(t) for t in (idx, o, lse)] + ([] if logg is None else [host(logg)])
+
+        base = run(x)
+        for i in (n // 3, n // 2 + 17, n - 40):
+            x2 = dict(x)
+            for key in ("q", "k", "v"):
+                a = x[key].copy()
+                tail = rng.standard_normal(a[:, :, i + 1:].shape).astype(np.float32)
+                if a.dtype == np.uint16:
+                    tail = np.array([oracle.round_bf16(float(t)) for t in tail.ravel()], np.uint16).reshape(tail.shape)
+                a[:, :, i + 1:] = tail
+                x2[key] = a
+            got = run(x2)
+            for u, w in zip(base, got):
+                assert np.array_equal(u[:, :, :i + 1].view(np.uint8), w[:, :, :i + 1].view(np.uint8)), (name, i)
+
+
 # ------------------------------------------------------------------ prefill with cells
 def _prefill_run(cfg, x, rows=None):
     b, qb = cfg["b"], cfg["qblock"]
