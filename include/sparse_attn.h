@@ -244,6 +244,13 @@ typedef struct spa_attn_args {
  * Supported modes: (local = CURRENT_BLOCK, window = 0, alpha = NULL) and
  * (local = NONE, window > 0, alpha != NULL).  A row with no key in branch L
  * gets o_L = 0 and lse = -inf.  nq = 1 uses the split-K decode kernels.
+ * Workspace: sparse_workspace_bytes(SPA_OP_ATTN_FWD, a).  For many rows in
+ * the window mode with routed cells of 32 or 64 keys it holds the cell-major
+ * branch L: a bitmap of B Hsel x cells x ceil(nq/32) words, the row lists,
+ * and per (row, query head, slot) a bf16 partial of d values plus 8 bytes
+ * (about B Hq nq K (2d + 8) bytes; 143 MB at 16 heads, nq = 16384, K = 4,
+ * d = 64); beyond 16 GiB of partials the call walks the cells per row tile
+ * instead and needs no workspace.
  */
 int sparse_attn_fwd(const spa_attn_args *a, void *workspace, size_t ws_bytes,
                     spa_stream_t stream);
