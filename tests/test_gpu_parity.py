@@ -642,6 +642,19 @@ def test_select_erf_filter_per_score(over, shift):
     _say(f"  exempt rows {_select_only(cfg, x, gate=False, share_group=False, centre_shift=shift)}")
 
 
+def test_select_erf_filter_per_score_full_size_sampled_rows():
+    """The per-score filter at the full prefill_cells size (16 heads, n =
+    16384; sigma = 3000 puts x = 4 past the table), on sampled rows."""
+    cfg = config("prefill_cells", sigma=3000.0, seed=61)
+    _say("[select erf per score] full size, sigma 3000, sampled rows")
+    x = make_inputs(cfg)
+    rng = np.random.Generator(np.random.PCG64(97))
+    n = x["L"]
+    rows = np.unique(np.concatenate([np.arange(0, 130), np.arange(n - 130, n),
+                                     rng.integers(0, n, 1000)])).astype(np.int64)
+    _say(f"  exempt rows {_select_only(cfg, x, gate=False, share_group=False, rows=rows)}")
+
+
 def test_select_erf_identical_keys():
     """Every key equal: all cells tie in fp32 far from the query, so the fp32
     list cannot separate the budget from the rest and rows are re-scored
