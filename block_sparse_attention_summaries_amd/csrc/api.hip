@@ -16,7 +16,7 @@ namespace {
 thread_local std::string g_last_error;
 thread_local spa::ProfileEvents g_profile = {nullptr, 0, 0};
 
-int fail(int code, const char* fmt, ...) {
+spa_status fail(spa_status code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -26,7 +26,7 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-int ok() {
+spa_status ok() {
   g_last_error.clear();
   return SPA_OK;
 }
@@ -44,7 +44,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
     if (!(cond)) return fail((code), __VA_ARGS__); \
   } while (0)
 
-int check_heads(int B, int Hq, int Hkv, int d, int dtype) {
+spa_status check_heads(int B, int Hq, int Hkv, int d, int dtype) {
   SPA_REQUIRE(dtype == SPA_DTYPE_F32 || dtype == SPA_DTYPE_BF16, SPA_ERR_UNSUPPORTED,
               "dtype %d not supported (0 = fp32, 1 = bf16)", dtype);
   SPA_REQUIRE(d == 64 || d == 128, SPA_ERR_UNSUPPORTED, "head dim d = %d not supported (64 or 128)", d);
@@ -57,9 +57,9 @@ int check_heads(int B, int Hq, int Hkv, int d, int dtype) {
   return SPA_OK;
 }
 
-int check_select(const spa_select_args* a, spa::SelectLaunch* p) {
+spa_status check_select(const spa_select_args* a, spa::SelectLaunch* p) {
   SPA_REQUIRE(a != nullptr, SPA_ERR_INVALID_ARG, "args is NULL");
-  int st = check_heads(a->B, a->Hq, a->Hkv, a->d, a->dtype);
+  spa_status st = check_heads(a->B, a->Hq, a->Hkv, a->d, a->dtype);
   if (st != SPA_OK) return st;
   SPA_REQUIRE(a->q && a->kbar && a->idx, SPA_ERR_INVALID_ARG, "q, kbar and idx must be non-NULL");
   SPA_REQUIRE(aligned16(a->q) && aligned16(a->kbar), SPA_ERR_INVALID_ARG, "q and kbar must be 16-byte aligned");
@@ -103,9 +103,9 @@ int check_select(const spa_select_args* a, spa::SelectLaunch* p) {
   return SPA_OK;
 }
 
-int check_attn(const spa_attn_args* a, spa::AttnLaunch* p) {
+spa_status check_attn(const spa_attn_args* a, spa::AttnLaunch* p) {
   SPA_REQUIRE(a != nullptr, SPA_ERR_INVALID_ARG, "args is NULL");
-  int st = check_heads(a->B, a->Hq, a->Hkv, a->d, a->dtype);
+  spa_status st = check_heads(a->B, a->Hq, a->Hkv, a->d, a->dtype);
   if (st != SPA_OK) return st;
   SPA_REQUIRE(a->q && a->k && a->v && a->o && a->idx, SPA_ERR_INVALID_ARG,
               "q, k, v, o and idx must be non-NULL");
@@ -135,10 +135,10 @@ int check_attn(const spa_attn_args* a, spa::AttnLaunch* p) {
   return SPA_OK;
 }
 
-int check_bwd(const spa_attn_args* a, const void* o, const void* dout, const float* lse, void* dq, void* dk,
+spa_status check_bwd(const spa_attn_args* a, const void* o, const void* dout, const float* lse, void* dq, void* dk,
               void* dv, float* dg, spa::BwdLaunch* p) {
   spa::AttnLaunch al;
-  int st = check_attn(a, &al);
+  spa_status st = check_attn(a, &al);
   if (st != SPA_OK) return st;
   SPA_REQUIRE(a->local == SPA_LOCAL_CURRENT_BLOCK && a->window == 0 && a->alpha == nullptr,
               SPA_ERR_UNSUPPORTED, "the backward supports the current-block + selected-blocks mode only");
@@ -151,9 +151,9 @@ int check_bwd(const spa_attn_args* a, const void* o, const void* dout, const flo
   return SPA_OK;
 }
 
-int check_select_bwd(const spa_select_args* a, const spa_select_grads* g, spa::SelectLaunch* p,
+spa_status check_select_bwd(const spa_select_args* a, const spa_select_grads* g, spa::SelectLaunch* p,
                      spa::SelectGrads* sg) {
-  int st = check_select(a, p);
+  spa_status st = check_select(a, p);
   if (st != SPA_OK) return st;
   SPA_REQUIRE(a->gate == SPA_GATE_SOFTMAX_LOG, SPA_ERR_UNSUPPORTED,
               "the selector backward needs the softmax log gate (gate = SOFTMAX_LOG)");
@@ -176,10 +176,10 @@ int check_select_bwd(const spa_select_args* a, const spa_select_grads* g, spa::S
   return SPA_OK;
 }
 
-int check_decode(const spa_decode_args* d, spa::SelectLaunch* sp, spa::AttnLaunch* ap) {
+spa_status check_decode(const spa_decode_args* d, spa::SelectLaunch* sp, spa::AttnLaunch* ap) {
   SPA_REQUIRE(d != nullptr && d->select != nullptr && d->attn != nullptr, SPA_ERR_INVALID_ARG,
               "decode args, select and attn must be non-NULL");
-  int st = check_select(d->select, sp);
+  spa_status st = check_select(d->select, sp);
   if (st != SPA_OK) return st;
   st = check_attn(d->attn, ap);
   if (st != SPA_OK) return st;
@@ -203,14 +203,14 @@ size_t decode_ws_bytes(const spa::SelectLaunch& sp, const spa::AttnLaunch& ap) {
   return spa::align256(spa::select_workspace_bytes(sp)) + spa::attn_fwd_workspace_bytes(ap);
 }
 
-int check_ws(void* ws, size_t have, size_t need) {
+spa_status check_ws(void* ws, size_t have, size_t need) {
   if (need == 0) return SPA_OK;
   SPA_REQUIRE(ws != nullptr && have >= need, SPA_ERR_WORKSPACE,
               "workspace of %zu bytes needed, %zu given%s", need, have, ws ? "" : " (NULL)");
   return SPA_OK;
 }
 
-int hip_status(hipError_t e, const char* what) {
+spa_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(SPA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
 }
@@ -219,22 +219,24 @@ int hip_status(hipError_t e, const char* what) {
 
 extern "C" {
 
+int sparse_abi_version(void) { return SPA_ABI_VERSION; }
 int spa_abi_version(void) { return SPA_ABI_VERSION; }
 
-int spa_profile_next_call(void** events, int count) {
+spa_status spa_profile_next_call(void** events, int count) {
   SPA_REQUIRE(count >= 0 && (count == 0 || events != nullptr), SPA_ERR_INVALID_ARG,
               "events must hold 2 * count handles");
   g_profile = spa::ProfileEvents{reinterpret_cast<hipEvent_t*>(events), count, 0};
   return ok();
 }
 
+const char* sparse_last_error(void) { return g_last_error.c_str(); }
 const char* spa_last_error(void) { return g_last_error.c_str(); }
 
-int sparse_block_summaries(const void* k, int dtype, int B, int Hkv, int64_t L, int d, int b,
+spa_status sparse_block_summaries(const void* k, int dtype, int B, int Hkv, int64_t L, int d, int b,
                            int64_t first_block, int64_t num_blocks, int64_t ccap, void* kbar,
                            float* max_norm, float* centre, spa_stream_t stream) {
   ProfileScope profile_scope;
-  int st = check_heads(B, Hkv, Hkv, d, dtype);
+  spa_status st = check_heads(B, Hkv, Hkv, d, dtype);
   if (st != SPA_OK) return st;
   SPA_REQUIRE(k && kbar && max_norm, SPA_ERR_INVALID_ARG, "k, kbar and max_norm must be non-NULL");
   SPA_REQUIRE(aligned16(k), SPA_ERR_INVALID_ARG, "k must be 16-byte aligned");
@@ -253,7 +255,7 @@ int sparse_block_summaries(const void* k, int dtype, int B, int Hkv, int64_t L, 
   return hip_status(spa::launch_block_summaries(p, static_cast<hipStream_t>(stream)), "sparse_block_summaries");
 }
 
-int check_pages(const spa_kv_pages* pg, int64_t blocks_needed, spa::KvPages* out) {
+spa_status check_pages(const spa_kv_pages* pg, int64_t blocks_needed, spa::KvPages* out) {
   SPA_REQUIRE(pg != nullptr && pg->block_table != nullptr, SPA_ERR_INVALID_ARG, "pages and block_table must be non-NULL");
   SPA_REQUIRE(pg->num_pages >= 1, SPA_ERR_INVALID_ARG, "num_pages must be >= 1");
   SPA_REQUIRE(pg->table_stride >= blocks_needed, SPA_ERR_INVALID_ARG,
@@ -263,11 +265,11 @@ int check_pages(const spa_kv_pages* pg, int64_t blocks_needed, spa::KvPages* out
   return SPA_OK;
 }
 
-int sparse_block_summaries_paged(const void* k_pages, int dtype, int B, int Hkv, int64_t L, int d, int b,
+spa_status sparse_block_summaries_paged(const void* k_pages, int dtype, int B, int Hkv, int64_t L, int d, int b,
                                  const spa_kv_pages* pages, int64_t first_block, int64_t num_blocks, int64_t ccap,
                                  void* kbar, float* max_norm, float* centre, spa_stream_t stream) {
   ProfileScope profile_scope;
-  int st = check_heads(B, Hkv, Hkv, d, dtype);
+  spa_status st = check_heads(B, Hkv, Hkv, d, dtype);
   if (st != SPA_OK) return st;
   SPA_REQUIRE(k_pages && kbar && max_norm, SPA_ERR_INVALID_ARG, "k_pages, kbar and max_norm must be non-NULL");
   SPA_REQUIRE(aligned16(k_pages), SPA_ERR_INVALID_ARG, "k_pages must be 16-byte aligned");
@@ -290,10 +292,10 @@ int sparse_block_summaries_paged(const void* k_pages, int dtype, int B, int Hkv,
                     "sparse_block_summaries_paged");
 }
 
-int sparse_score_select(const spa_select_args* a, void* workspace, size_t ws_bytes, spa_stream_t stream) {
+spa_status sparse_score_select(const spa_select_args* a, void* workspace, size_t ws_bytes, spa_stream_t stream) {
   ProfileScope profile_scope;
   spa::SelectLaunch p;
-  int st = check_select(a, &p);
+  spa_status st = check_select(a, &p);
   if (st != SPA_OK) return st;
   st = check_ws(workspace, ws_bytes, spa::select_workspace_bytes(p));
   if (st != SPA_OK) return st;
@@ -301,11 +303,11 @@ int sparse_score_select(const spa_select_args* a, void* workspace, size_t ws_byt
                     "sparse_score_select");
 }
 
-int sparse_quantize_summaries_fp8(const void* kbar, int dtype, int B, int Hkv, int64_t ccap, int d,
+spa_status sparse_quantize_summaries_fp8(const void* kbar, int dtype, int B, int Hkv, int64_t ccap, int d,
                                   int64_t first_block, int64_t num_blocks, uint8_t* codes, float* scales,
                                   spa_stream_t stream) {
   ProfileScope profile_scope;
-  int st = check_heads(B, Hkv, Hkv, d, dtype);
+  spa_status st = check_heads(B, Hkv, Hkv, d, dtype);
   if (st != SPA_OK) return st;
   SPA_REQUIRE(kbar && codes && scales, SPA_ERR_INVALID_ARG, "kbar, codes and scales must be non-NULL");
   SPA_REQUIRE(aligned16(kbar) && aligned16(codes) && aligned16(scales), SPA_ERR_INVALID_ARG,
@@ -321,7 +323,7 @@ int sparse_quantize_summaries_fp8(const void* kbar, int dtype, int B, int Hkv, i
                     "sparse_quantize_summaries_fp8");
 }
 
-int sparse_dequantize_summaries_fp8(const uint8_t* codes, const float* scales, int64_t rows, int d, float* out,
+spa_status sparse_dequantize_summaries_fp8(const uint8_t* codes, const float* scales, int64_t rows, int d, float* out,
                                     spa_stream_t stream) {
   ProfileScope profile_scope;
   SPA_REQUIRE(codes && scales && out, SPA_ERR_INVALID_ARG, "codes, scales and out must be non-NULL");
@@ -334,33 +336,33 @@ int sparse_dequantize_summaries_fp8(const uint8_t* codes, const float* scales, i
                     "sparse_dequantize_summaries_fp8");
 }
 
-int sparse_attn_fwd(const spa_attn_args* a, void* workspace, size_t ws_bytes, spa_stream_t stream) {
+spa_status sparse_attn_fwd(const spa_attn_args* a, void* workspace, size_t ws_bytes, spa_stream_t stream) {
   ProfileScope profile_scope;
   spa::AttnLaunch p;
-  int st = check_attn(a, &p);
+  spa_status st = check_attn(a, &p);
   if (st != SPA_OK) return st;
   st = check_ws(workspace, ws_bytes, spa::attn_fwd_workspace_bytes(p));
   if (st != SPA_OK) return st;
   return hip_status(spa::launch_attn_fwd(p, workspace, static_cast<hipStream_t>(stream)), "sparse_attn_fwd");
 }
 
-int sparse_attn_bwd(const spa_attn_args* a, const void* o, const void* dout, const float* lse, void* dq,
+spa_status sparse_attn_bwd(const spa_attn_args* a, const void* o, const void* dout, const float* lse, void* dq,
                     void* dk, void* dv, float* dg, void* workspace, size_t ws_bytes, spa_stream_t stream) {
   ProfileScope profile_scope;
   spa::BwdLaunch p;
-  int st = check_bwd(a, o, dout, lse, dq, dk, dv, dg, &p);
+  spa_status st = check_bwd(a, o, dout, lse, dq, dk, dv, dg, &p);
   if (st != SPA_OK) return st;
   st = check_ws(workspace, ws_bytes, spa::attn_bwd_workspace_bytes(p));
   if (st != SPA_OK) return st;
   return hip_status(spa::launch_attn_bwd(p, workspace, static_cast<hipStream_t>(stream)), "sparse_attn_bwd");
 }
 
-int sparse_select_bwd(const spa_select_args* a, const spa_select_grads* g, void* workspace, size_t ws_bytes,
+spa_status sparse_select_bwd(const spa_select_args* a, const spa_select_grads* g, void* workspace, size_t ws_bytes,
                       spa_stream_t stream) {
   ProfileScope profile_scope;
   spa::SelectLaunch p;
   spa::SelectGrads sg;
-  int st = check_select_bwd(a, g, &p, &sg);
+  spa_status st = check_select_bwd(a, g, &p, &sg);
   if (st != SPA_OK) return st;
   st = check_ws(workspace, ws_bytes, spa::select_bwd_workspace_bytes(p));
   if (st != SPA_OK) return st;
@@ -368,11 +370,11 @@ int sparse_select_bwd(const spa_select_args* a, const spa_select_grads* g, void*
                     "sparse_select_bwd");
 }
 
-int sparse_decode_step(const spa_decode_args* a, void* workspace, size_t ws_bytes, spa_stream_t stream) {
+spa_status sparse_decode_step(const spa_decode_args* a, void* workspace, size_t ws_bytes, spa_stream_t stream) {
   ProfileScope profile_scope;
   spa::SelectLaunch sp;
   spa::AttnLaunch ap;
-  int st = check_decode(a, &sp, &ap);
+  spa_status st = check_decode(a, &sp, &ap);
   if (st != SPA_OK) return st;
   st = check_ws(workspace, ws_bytes, decode_ws_bytes(sp, ap));
   if (st != SPA_OK) return st;
@@ -385,12 +387,12 @@ int sparse_decode_step(const spa_decode_args* a, void* workspace, size_t ws_byte
   return hip_status(e, "sparse_decode_step");
 }
 
-int sparse_decode_step_paged(const spa_decode_args* a, const spa_kv_pages* pages, void* workspace,
+spa_status sparse_decode_step_paged(const spa_decode_args* a, const spa_kv_pages* pages, void* workspace,
                              size_t ws_bytes, spa_stream_t stream) {
   ProfileScope profile_scope;
   spa::SelectLaunch sp;
   spa::AttnLaunch ap;
-  int st = check_decode(a, &sp, &ap);
+  spa_status st = check_decode(a, &sp, &ap);
   if (st != SPA_OK) return st;
   st = check_pages(pages, (ap.L + ap.b - 1) / ap.b, &ap.pages);
   if (st != SPA_OK) return st;
@@ -405,7 +407,7 @@ int sparse_decode_step_paged(const spa_decode_args* a, const spa_kv_pages* pages
   return hip_status(e, "sparse_decode_step_paged");
 }
 
-int sparse_retain_cells(const float* max_norm, int B, int Hkv, int64_t ccap, int64_t ncand, int W, int P,
+spa_status sparse_retain_cells(const float* max_norm, int B, int Hkv, int64_t ccap, int64_t ncand, int W, int P,
                         int32_t* cells, int32_t* count, spa_stream_t stream) {
   ProfileScope profile_scope;
   SPA_REQUIRE(max_norm && cells && count, SPA_ERR_INVALID_ARG, "max_norm, cells and count must be non-NULL");
@@ -420,11 +422,11 @@ int sparse_retain_cells(const float* max_norm, int B, int Hkv, int64_t ccap, int
                     "sparse_retain_cells");
 }
 
-int sparse_score_select_subset(const spa_select_args* a, const int32_t* cells, const int32_t* count, int cap,
+spa_status sparse_score_select_subset(const spa_select_args* a, const int32_t* cells, const int32_t* count, int cap,
                                spa_stream_t stream) {
   ProfileScope profile_scope;
   spa::SelectLaunch p;
-  int st = check_select(a, &p);
+  spa_status st = check_select(a, &p);
   if (st != SPA_OK) return st;
   SPA_REQUIRE(a->proj_w == nullptr, SPA_ERR_UNSUPPORTED, "the kept-set selection takes no projection");
   SPA_REQUIRE(a->kbar_scale == nullptr, SPA_ERR_UNSUPPORTED, "the kept-set selection takes summaries in dtype");
@@ -441,7 +443,7 @@ size_t sparse_forest_workspace_bytes(int B, int Hkv, int d, int64_t n) {
   return spa::forest_workspace_bytes(B, Hkv, d, n);
 }
 
-int check_forest(const spa_forest* fo, int B, int Hkv, int64_t ccap, int64_t n, spa::ForestLaunch* p) {
+spa_status check_forest(const spa_forest* fo, int B, int Hkv, int64_t ccap, int64_t n, spa::ForestLaunch* p) {
   SPA_REQUIRE(fo != nullptr && fo->members && fo->nmem && fo->mu && fo->rad && fo->amax && fo->pmin,
               SPA_ERR_INVALID_ARG, "forest arrays must be non-NULL");
   SPA_REQUIRE(n >= 1 && n <= ccap && n < (static_cast<int64_t>(1) << 31), SPA_ERR_INVALID_ARG,
@@ -460,11 +462,11 @@ int check_forest(const spa_forest* fo, int B, int Hkv, int64_t ccap, int64_t n, 
   return SPA_OK;
 }
 
-int sparse_forest_build(const void* kbar, int dtype, const float* max_norm, const float* centre, int B, int Hkv,
+spa_status sparse_forest_build(const void* kbar, int dtype, const float* max_norm, const float* centre, int B, int Hkv,
                         int d, int64_t ccap, int64_t n, const spa_forest* forest, void* workspace, size_t ws_bytes,
                         spa_stream_t stream) {
   ProfileScope profile_scope;
-  int st = check_heads(B, Hkv, Hkv, d, dtype);
+  spa_status st = check_heads(B, Hkv, Hkv, d, dtype);
   if (st != SPA_OK) return st;
   SPA_REQUIRE(kbar && max_norm && centre, SPA_ERR_INVALID_ARG, "kbar, max_norm and centre must be non-NULL");
   spa::ForestLaunch p{};
@@ -481,11 +483,11 @@ int sparse_forest_build(const void* kbar, int dtype, const float* max_norm, cons
   return hip_status(spa::launch_forest_build(p, static_cast<hipStream_t>(stream)), "sparse_forest_build");
 }
 
-int sparse_forest_select(const spa_select_args* a, const void* k, int64_t L, const spa_forest* forest, int64_t n,
+spa_status sparse_forest_select(const spa_select_args* a, const void* k, int64_t L, const spa_forest* forest, int64_t n,
                          spa_stream_t stream) {
   ProfileScope profile_scope;
   spa::SelectLaunch s;
-  int st = check_select(a, &s);
+  spa_status st = check_select(a, &s);
   if (st != SPA_OK) return st;
   SPA_REQUIRE(a->gate == SPA_GATE_NONE && a->proj_w == nullptr, SPA_ERR_UNSUPPORTED,
               "the forest selection takes no gate and no projection");
@@ -543,7 +545,7 @@ size_t sparse_workspace_bytes(int op, const void* args) {
   }
 }
 
-int sparse_workspace_init(void* workspace, size_t ws_bytes, spa_stream_t stream) {
+spa_status sparse_workspace_init(void* workspace, size_t ws_bytes, spa_stream_t stream) {
   ProfileScope profile_scope;
   if (ws_bytes == 0) return ok();
   SPA_REQUIRE(workspace != nullptr, SPA_ERR_INVALID_ARG, "workspace is NULL");

@@ -26,7 +26,8 @@ SPA_GATE_NONE, SPA_GATE_SOFTMAX_LOG = 0, 1
 SPA_LOCAL_CURRENT_BLOCK, SPA_LOCAL_NONE = 0, 1
 SPA_OP_SCORE_SELECT, SPA_OP_ATTN_FWD, SPA_OP_ATTN_BWD, SPA_OP_SELECT_BWD, SPA_OP_DECODE_STEP = 1, 2, 3, 4, 5
 
-EXPORTED = ["spa_abi_version", "spa_profile_next_call", "spa_last_error", "sparse_block_summaries", "sparse_score_select",
+EXPORTED = ["sparse_abi_version", "sparse_last_error", "spa_abi_version", "spa_profile_next_call", "spa_last_error",
+            "sparse_block_summaries", "sparse_score_select",
             "sparse_attn_fwd", "sparse_attn_bwd", "sparse_select_bwd", "sparse_decode_step",
             "sparse_block_summaries_paged", "sparse_decode_step_paged", "sparse_retain_cells",
             "sparse_score_select_subset", "sparse_forest_nodes", "sparse_forest_workspace_bytes",
@@ -85,12 +86,14 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                                "(hipcc --offload-arch=gfx950); there is no CPU fallback")
         L = ctypes.CDLL(LIB_PATH)
-        L.spa_abi_version.restype = _i
-        L.spa_abi_version.argtypes = []
+        for name in ("sparse_abi_version", "spa_abi_version"):
+            getattr(L, name).restype = _i
+            getattr(L, name).argtypes = []
         L.spa_profile_next_call.restype = _i
         L.spa_profile_next_call.argtypes = [ctypes.POINTER(_vp), _i]
-        L.spa_last_error.restype = ctypes.c_char_p
-        L.spa_last_error.argtypes = []
+        for name in ("sparse_last_error", "spa_last_error"):
+            getattr(L, name).restype = ctypes.c_char_p
+            getattr(L, name).argtypes = []
         L.sparse_block_summaries.restype = _i
         L.sparse_block_summaries.argtypes = [_vp, _i, _i, _i, _i64, _i, _i, _i64, _i64, _i64, _vp, _vp,
                                              _vp, _vp]
@@ -131,8 +134,8 @@ def lib():
         L.sparse_workspace_bytes.argtypes = [_i, _vp]
         L.sparse_workspace_init.restype = _i
         L.sparse_workspace_init.argtypes = [_vp, _sz, _vp]
-        if L.spa_abi_version() != ABI_VERSION:
-            raise RuntimeError(f"{LIB_PATH} has ABI version {L.spa_abi_version()}, this binding needs "
+        if L.sparse_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.sparse_abi_version()}, this binding needs "
                                f"{ABI_VERSION}: rebuild it with __graft_entry__.build()")
         _lib = L
     return _lib
@@ -140,7 +143,7 @@ def lib():
 
 def _check(code):
     if code != SPA_OK:
-        raise SpaError(code, lib().spa_last_error().decode())
+        raise SpaError(code, lib().sparse_last_error().decode())
 
 
 def _p(t):

@@ -49,7 +49,7 @@
  *
  * Errors: every entry point validates its arguments before launching
  * anything and returns a spa_status.  On error nothing is launched and
- * spa_last_error() returns a message (per calling thread).  Launch failures
+ * sparse_last_error() returns a message (per calling thread).  Launch failures
  * reported by the HIP runtime return SPA_ERR_HIP.  Kernels never trap: block
  * indices outside a row's candidate set are ignored.  NaN/Inf inputs give
  * unspecified values but never out-of-bounds accesses.
@@ -91,6 +91,9 @@ typedef enum {
 } spa_op;
 
 /* Version of this ABI (SPA_ABI_VERSION). */
+int sparse_abi_version(void);
+/* The same value under the library's short prefix (kept for callers built
+ * against it). */
 int spa_abi_version(void);
 
 /* Kernel timing for callers that measure it (benchmarks, profilers).  Per
@@ -112,10 +115,12 @@ int spa_abi_version(void);
  * score_select_subset, quantize / dequantize_summaries_fp8 1; select_bwd one
  * per stage it runs.
  * Returns SPA_ERR_INVALID_ARG if count < 0 or events is NULL with count > 0. */
-int spa_profile_next_call(void **events, int count);
+spa_status spa_profile_next_call(void **events, int count);
 
 /* Message describing the last failed call made by this thread ("" if none).
  * The pointer stays valid until the next call on the same thread. */
+const char *sparse_last_error(void);
+/* The same message under the library's short prefix. */
 const char *spa_last_error(void);
 
 /*
@@ -132,7 +137,7 @@ const char *spa_last_error(void);
  * when a block closes.  Output rows outside the range are not touched.
  * Returns SPA_ERR_INVALID_ARG on null pointers or out-of-range sizes.
  */
-int sparse_block_summaries(const void *k, int dtype, int B, int Hkv, int64_t L, int d,
+spa_status sparse_block_summaries(const void *k, int dtype, int B, int Hkv, int64_t L, int d,
                            int b, int64_t first_block, int64_t num_blocks, int64_t ccap,
                            void *kbar, float *max_norm, float *centre,
                            spa_stream_t stream);
@@ -175,7 +180,7 @@ typedef struct spa_select_args {
  * q_hat = q_hs or the mean of the G query heads of kv head hs; ktilde = kbar
  * or W kbar.  Needs a workspace of sparse_workspace_bytes(SPA_OP_SCORE_SELECT).
  */
-int sparse_score_select(const spa_select_args *a, void *workspace, size_t ws_bytes,
+spa_status sparse_score_select(const spa_select_args *a, void *workspace, size_t ws_bytes,
                         spa_stream_t stream);
 
 /*
@@ -197,7 +202,7 @@ int sparse_score_select(const spa_select_args *a, void *workspace, size_t ws_byt
  * of "SAS" review §3 Eq. 3.)  SPA_ERR_INVALID_ARG on null pointers, unaligned
  * buffers or out-of-range blocks.
  */
-int sparse_quantize_summaries_fp8(const void *kbar, int dtype, int B, int Hkv, int64_t ccap, int d,
+spa_status sparse_quantize_summaries_fp8(const void *kbar, int dtype, int B, int Hkv, int64_t ccap, int d,
                                   int64_t first_block, int64_t num_blocks, uint8_t *codes, float *scales,
                                   spa_stream_t stream);
 
@@ -206,7 +211,7 @@ int sparse_quantize_summaries_fp8(const void *kbar, int dtype, int B, int Hkv, i
  * product; the decode is exact), for rows r of d codes (d in {64, 128}).
  * Uses the scorer's own decode.  SPA_ERR_INVALID_ARG on null or unaligned
  * pointers. */
-int sparse_dequantize_summaries_fp8(const uint8_t *codes, const float *scales, int64_t rows, int d, float *out,
+spa_status sparse_dequantize_summaries_fp8(const uint8_t *codes, const float *scales, int64_t rows, int d, float *out,
                                     spa_stream_t stream);
 
 typedef struct spa_attn_args {
@@ -252,7 +257,7 @@ typedef struct spa_attn_args {
  * d = 64); beyond 16 GiB of partials the call walks the cells per row tile
  * instead and needs no workspace.
  */
-int sparse_attn_fwd(const spa_attn_args *a, void *workspace, size_t ws_bytes,
+spa_status sparse_attn_fwd(const spa_attn_args *a, void *workspace, size_t ws_bytes,
                     spa_stream_t stream);
 
 typedef struct spa_decode_args {
@@ -274,7 +279,7 @@ typedef struct spa_decode_args {
  * caller-owned, contents on entry ignored.  Errors: as the two calls, plus
  * SPA_ERR_INVALID_ARG when select and attn disagree.
  */
-int sparse_decode_step(const spa_decode_args *a, void *workspace, size_t ws_bytes,
+spa_status sparse_decode_step(const spa_decode_args *a, void *workspace, size_t ws_bytes,
                        spa_stream_t stream);
 
 /*
@@ -294,7 +299,7 @@ typedef struct spa_kv_pages {
 /* sparse_block_summaries over a paged key cache: k_pages is the pool,
  * L the logical tokens per batch row; otherwise as sparse_block_summaries
  * (table_stride must cover first_block + num_blocks). */
-int sparse_block_summaries_paged(const void *k_pages, int dtype, int B, int Hkv, int64_t L, int d,
+spa_status sparse_block_summaries_paged(const void *k_pages, int dtype, int B, int Hkv, int64_t L, int d,
                                  int b, const spa_kv_pages *pages, int64_t first_block,
                                  int64_t num_blocks, int64_t ccap, void *kbar, float *max_norm,
                                  float *centre, spa_stream_t stream);
@@ -303,7 +308,7 @@ int sparse_block_summaries_paged(const void *k_pages, int dtype, int B, int Hkv,
  * page pools and a->attn->L the logical tokens (table_stride >= ceil(L / b));
  * same outputs as sparse_decode_step on the cache the pages describe, and the
  * same workspace (sparse_workspace_bytes(SPA_OP_DECODE_STEP, a)). */
-int sparse_decode_step_paged(const spa_decode_args *a, const spa_kv_pages *pages, void *workspace,
+spa_status sparse_decode_step_paged(const spa_decode_args *a, const spa_kv_pages *pages, void *workspace,
                              size_t ws_bytes, spa_stream_t stream);
 
 /*
@@ -319,7 +324,7 @@ int sparse_decode_step_paged(const spa_decode_args *a, const spa_kv_pages *pages
  * on null pointers or ncand outside [0, ccap].  No workspace.
  * Query-independent: run it when a cell closes.
  */
-int sparse_retain_cells(const float *max_norm, int B, int Hkv, int64_t ccap, int64_t ncand,
+spa_status sparse_retain_cells(const float *max_norm, int B, int Hkv, int64_t ccap, int64_t ncand,
                         int W, int P, int32_t *cells, int32_t *count, spa_stream_t stream);
 
 /*
@@ -333,7 +338,7 @@ int sparse_retain_cells(const float *max_norm, int B, int Hkv, int64_t ccap, int
  * summaries or cap outside 1..256 give SPA_ERR_UNSUPPORTED, null cells /
  * count SPA_ERR_INVALID_ARG.  No workspace.
  */
-int sparse_score_select_subset(const spa_select_args *a, const int32_t *cells,
+spa_status sparse_score_select_subset(const spa_select_args *a, const int32_t *cells,
                                const int32_t *count, int cap, spa_stream_t stream);
 
 /*
@@ -377,7 +382,7 @@ size_t sparse_forest_workspace_bytes(int B, int Hkv, int d, int64_t n);
  * arrays); B Hkv <= 65535; the workspace must hold
  * sparse_forest_workspace_bytes (else SPA_ERR_WORKSPACE).  Query-independent:
  * build when a query block's prefix grows. */
-int sparse_forest_build(const void *kbar, int dtype, const float *max_norm, const float *centre,
+spa_status sparse_forest_build(const void *kbar, int dtype, const float *max_norm, const float *centre,
                         int B, int Hkv, int d, int64_t ccap, int64_t n, const spa_forest *forest,
                         void *workspace, size_t ws_bytes, spa_stream_t stream);
 
@@ -390,7 +395,7 @@ int sparse_forest_build(const void *kbar, int dtype, const float *max_norm, cons
  * A gate, a projection, fp8 summaries, K > 16 or another b give
  * SPA_ERR_UNSUPPORTED; rows whose candidates are not the n cells, or L < n b,
  * SPA_ERR_INVALID_ARG.  No workspace. */
-int sparse_forest_select(const spa_select_args *a, const void *k, int64_t L,
+spa_status sparse_forest_select(const spa_select_args *a, const void *k, int64_t L,
                          const spa_forest *forest, int64_t n, spa_stream_t stream);
 
 /*
@@ -406,7 +411,7 @@ int sparse_forest_select(const spa_select_args *a, const void *k, int64_t L,
  * dq, dk, dv are written (not accumulated) in the input dtype; dg in fp32
  * (0 in padded slots; with logg NULL the gradient is taken at g = 1).
  */
-int sparse_attn_bwd(const spa_attn_args *a, const void *o, const void *dout,
+spa_status sparse_attn_bwd(const spa_attn_args *a, const void *o, const void *dout,
                     const float *lse, void *dq, void *dk, void *dv, float *dg,
                     void *workspace, size_t ws_bytes, spa_stream_t stream);
 
@@ -449,7 +454,7 @@ typedef struct spa_select_grads {
  * workspace of sparse_workspace_bytes(SPA_OP_SELECT_BWD); caller-owned,
  * contents on entry are ignored.  Deterministic: no atomics.
  */
-int sparse_select_bwd(const spa_select_args *a, const spa_select_grads *g, void *workspace,
+spa_status sparse_select_bwd(const spa_select_args *a, const spa_select_grads *g, void *workspace,
                       size_t ws_bytes, spa_stream_t stream);
 
 /* Workspace bytes needed by `op` (spa_op) for the given argument struct
@@ -461,7 +466,7 @@ size_t sparse_workspace_bytes(int op, const void *args);
 /* Zero-fill a workspace with a kernel on `stream` (graph-capture safe).  Not
  * required by any entry point; provided for callers that want deterministic
  * scratch contents. */
-int sparse_workspace_init(void *workspace, size_t ws_bytes, spa_stream_t stream);
+spa_status sparse_workspace_init(void *workspace, size_t ws_bytes, spa_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -108,6 +108,8 @@ def _declare(lib):
     lib.orc_attn_bwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I64, I64, I, P, P, I, I, I64,
                                  P, P, P, P]
     lib.orc_attn_bwd.restype = None
+    lib.orc_cell_token_lse.restype = None
+    lib.orc_cell_token_lse.argtypes = [P, I, I, I, I, I, I, P, I, I64, I, I, I, I, I64, I64, P]
 
 
 def _ptr(a):
@@ -388,6 +390,19 @@ def forest_select(q, kbar, max_norm, centre, k, forest, n, *, Hkv, b, K, q_pos0,
                           _ptr(f["members"]), _ptr(f["nmem"]), _ptr(f["mu"]), _ptr(f["rad"]), _ptr(f["amax"]),
                           _ptr(f["pmin"]), int(n), int(F), int(Wb), K, _ptr(idx), _ptr(gap))
     return dict(idx=idx, gap=gap)
+
+
+def cell_token_lse(q, k, *, Hkv, b, bidx, hs, row, ncells, share_group=False):
+    """Re-rank score of cells 0..ncells-1 for one row and selection head: the
+    logsumexp over each cell's b token keys of qhat.k/sqrt(d) (fp64)."""
+    lib = _load()
+    B, Hq, nq, d = q.shape
+    L = k.shape[2]
+    assert k.dtype == q.dtype and ncells * b <= L
+    out = np.zeros((max(int(ncells), 1),), np.float64)
+    lib.orc_cell_token_lse(_ptr(q), _dtype_code(q), B, Hq, Hkv, nq, d, _ptr(k), _dtype_code(k), L, b,
+                           int(bool(share_group)), int(bidx), int(hs), int(row), int(ncells), _ptr(out))
+    return out[:ncells]
 
 
 def node_score(q_hat, mu, rad, amax, pmin, *, lam, sig, pos, with_erf=True):

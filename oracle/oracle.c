@@ -1416,3 +1416,48 @@ void orc_forest_select(const void *q, int qdtype, int B, int Hq, int Hkv, int nq
         free(lse);
     }
 }
+
+/*
+ * [FS] "How it works", the FS-B variant: the re-rank score of a cell for one
+ * row and selection head is the logsumexp over the cell's b token keys of
+ * qhat.k_j / sqrt(d) (qhat = the group mean with share_group=1, no bias), for
+ * every cell c < ncells.  The same quantity orc_forest_select ranks its
+ * reached cells by, written out for all cells so that a different valid
+ * re-rank (a cut whose margin is below 1e-6) can be checked.
+ */
+void orc_cell_token_lse(const void *q, int qdtype, int B, int Hq, int Hkv, int nq, int d, const void *k,
+                        int kdtype, int64_t L, int b, int share_group, int bidx, int hs, int64_t row,
+                        int64_t ncells, double *out)
+{
+    const int G = Hq / Hkv;
+    const int kvh = share_group ? hs : hs / G;
+    const int gq = share_group ? G : 1;
+    const int h0 = share_group ? hs * G : hs;
+    const int64_t t = (int64_t)bidx * Hkv + kvh;
+    const double isd = 1.0 / sqrt((double)d);
+    double *qh = (double *)calloc((size_t)d, sizeof(double));
+    double *z = (double *)malloc(sizeof(double) * (size_t)b);
+    (void)B;
+    for (int g = 0; g < gq; ++g)
+        for (int e = 0; e < d; ++e)
+            qh[e] += orc_load(q, qdtype, (((int64_t)bidx * Hq + h0 + g) * nq + row) * d + e);
+    for (int e = 0; e < d; ++e)
+        qh[e] /= (double)gq;
+    for (int64_t c = 0; c < ncells; ++c) {
+        double mx = -INFINITY;
+        for (int j = 0; j < b; ++j) {
+            double dot = 0.0;
+            for (int e = 0; e < d; ++e)
+                dot += qh[e] * orc_load(k, kdtype, (t * L + c * b + j) * d + e);
+            z[j] = dot * isd;
+            if (z[j] > mx)
+                mx = z[j];
+        }
+        double acc = 0.0;
+        for (int j = 0; j < b; ++j)
+            acc += exp(z[j] - mx);
+        out[c] = mx + log(acc);
+    }
+    free(qh);
+    free(z);
+}

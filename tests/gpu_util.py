@@ -3,6 +3,8 @@ device, compare results with the oracle, and the index-match rule with the
 K-boundary gap exemption."""
 from __future__ import annotations
 
+from dataclasses import dataclass, field
+
 import numpy as np
 import torch
 
@@ -43,11 +45,33 @@ def rel_err(x: np.ndarray, y: np.ndarray, lead: int = 2) -> float:
     return float((num / den).max())
 
 
-def check_indices(gpu_idx, ora, score_fn=None):
+@dataclass
+class IndexCheck:
+    """Outcome of check_indices.
+
+    n_exempt: rows whose oracle K-boundary gap is below 1e-6.
+    alt: positions (batch, head, row) where the GPU took a different, valid
+         top-K in such a row.
+    idx, logg: the oracle's selection with the GPU's set put in the alt rows
+         (logg recomputed in fp64 from the oracle's scores of that row:
+         log g_c = s_c - LSE over the row's candidates), so that outputs of
+         those rows can be compared with the oracle run on the same set."""
+    n_exempt: int
+    alt: list = field(default_factory=list)
+    idx: np.ndarray | None = None
+    logg: np.ndarray | None = None
+
+    def __str__(self):
+        return f"{self.n_exempt} (different valid top-K: {len(self.alt)})"
+
+
+def check_indices(gpu_idx, ora, score_fn) -> IndexCheck:
     """Selected indices must equal the oracle's, except in rows whose oracle
-    K-boundary gap is below 1e-6; there the GPU set must still be a valid
-    top-K within 1e-6 of the oracle's scores (checked with score_fn(pos) ->
-    (b, h, r) score vector when given).  Returns the number of exempted rows."""
+    K-boundary gap is below 1e-6.  A GPU row that differs there must still be
+    a valid top-K of that row: score_fn(pos) -> fp64 scores indexed by block
+    (or cell) id, -inf (or past the end) for ids that are not candidates of
+    the row; the GPU's ids are K_eff distinct candidates in ascending order,
+    -1 padded, and each scores at least the oracle's K-th minus 1e-6."""
     oi = ora["idx"]
     gap = ora["gap"]
     assert gpu_idx.shape == oi.shape, (gpu_idx.shape, oi.shape)
@@ -58,14 +82,33 @@ def check_indices(gpu_idx, ora, score_fn=None):
         where = np.argwhere(bad)[:5]
         msg = [f"{tuple(w)}: gpu {gpu_idx[tuple(w)]} oracle {oi[tuple(w)]} gap {gap[tuple(w)]}" for w in where]
         raise AssertionError(f"{int(bad.sum())} rows select different blocks:\n" + "\n".join(msg))
-    n_ex = int((diff & exempt).sum())
-    if score_fn is not None:
-        for w in np.argwhere(diff & exempt):
-            s = score_fn(tuple(w))
-            ke = int(ora["k_eff"][tuple(w)])
-            o_sel = [c for c in oi[tuple(w)] if c >= 0]
-            g_sel = [c for c in gpu_idx[tuple(w)] if c >= 0]
-            assert len(g_sel) == ke == len(o_sel)
-            kth = min(s[c] for c in o_sel)
-            assert all(s[c] >= kth - GAP_EXEMPT for c in g_sel)
-    return n_ex
+    out = IndexCheck(n_exempt=int(exempt.sum()), idx=oi.copy(),
+                     logg=None if ora.get("logg") is None else np.array(ora["logg"], np.float64))
+    K = oi.shape[-1]
+    for w in np.argwhere(diff & exempt):
+        pos = tuple(int(t) for t in w)
+        s = np.asarray(score_fn(pos), np.float64)
+        g = gpu_idx[pos]
+        o_sel = [int(c) for c in oi[pos] if c >= 0]
+        ke = len(o_sel)
+        if "k_eff" in ora:
+            assert ke == int(ora["k_eff"][pos]), (pos, ke, ora["k_eff"][pos])
+        g_sel = [int(c) for c in g[:ke]]
+        assert all(c == -1 for c in g[ke:]), f"{pos}: gpu row {g} pads past K_eff = {ke}"
+        assert all(c >= 0 for c in g_sel), f"{pos}: gpu row {g} pads inside K_eff = {ke}"
+        assert all(a < c for a, c in zip(g_sel, g_sel[1:])), f"{pos}: gpu row {g} not strictly ascending"
+        assert all(0 <= c < s.shape[0] and np.isfinite(s[c]) for c in g_sel), \
+            f"{pos}: gpu row {g} holds a non-candidate"
+        kth = min(s[c] for c in o_sel)
+        low = [(c, s[c]) for c in g_sel if s[c] < kth - GAP_EXEMPT]
+        assert not low, f"{pos}: gpu row {g} keeps {low} below the oracle's K-th score {kth}"
+        out.alt.append(pos)
+        out.idx[pos] = g
+        if out.logg is not None:
+            fin = s[np.isfinite(s)]
+            m = fin.max()
+            lse = m + np.log(np.exp(fin - m).sum())
+            lg = np.zeros(K, np.float64)
+            lg[:ke] = [s[c] - lse for c in g_sel]
+            out.logg[pos] = lg
+    return out

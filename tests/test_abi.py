@@ -30,7 +30,14 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(ops.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.spa_abi_version() == 2
+    assert lib.sparse_abi_version() == 2 and lib.spa_abi_version() == 2
+    # the four entry points and the helpers under the names the boundary
+    # specifies, the entry points typed spa_status
+    text = open(HEADER).read()
+    for n in ("sparse_block_summaries", "sparse_score_select", "sparse_attn_fwd", "sparse_attn_bwd"):
+        assert re.search(r"^spa_status " + n + r"\(", text, flags=re.M), n
+    for n in ("sparse_workspace_bytes", "sparse_last_error", "sparse_abi_version"):
+        assert n in names, n
 
 
 def _sel(**kw):
@@ -81,7 +88,7 @@ def _attn_status(a, ws=None, n=0):
 ])
 def test_select_rejects_invalid_arguments(kw, code):
     assert _select_status(_sel(**kw)) == code
-    assert ops.lib().spa_last_error().decode() != ""
+    assert ops.lib().sparse_last_error().decode() != ""
 
 
 def test_select_workspace_too_small():
@@ -209,7 +216,7 @@ def test_summaries_rejects_invalid_arguments():
     assert f(FAKE, 1, 1, 8, 4096, 128, 64, 0, 64, 63, FAKE, FAKE, None, None) == ops.SPA_ERR_INVALID_ARG
     assert f(FAKE, 1, 1, 8, 4096, 100, 64, 0, 64, 64, FAKE, FAKE, None, None) == ops.SPA_ERR_UNSUPPORTED
     assert f(FAKE, 1, 1, 8, 4096, 128, 64, 0, 0, 64, FAKE, FAKE, None, None) == ops.SPA_OK  # nothing to do
-    assert ops.lib().spa_last_error().decode() == ""
+    assert ops.lib().sparse_last_error().decode() == ""
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -219,7 +226,7 @@ def test_summaries_rejects_invalid_arguments():
 ])
 def test_fp8_summaries_only_on_the_decode_scorer(kw, code):
     assert _select_status(_sel(**kw)) == code
-    assert "fp8" in ops.lib().spa_last_error().decode()
+    assert "fp8" in ops.lib().sparse_last_error().decode()
     # the one-row decode scorer takes them (workspace check comes next)
     assert _select_status(_sel(kbar_scale=FAKE)) == ops.SPA_ERR_WORKSPACE
 

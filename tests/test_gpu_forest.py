@@ -80,9 +80,20 @@ def _select_case(cfg, x, nrows, share_group=False):
                                          share_group=share_group, erf_lambda=dev(lam), erf_sigma=dev(sig))
     torch.cuda.synchronize()
     idx = host(idx)
-    ex = check_indices(idx, ora)
+    ex = check_indices(idx, ora, _rerank_fn(q, x["k"], cfg, n, share_group))
     assert np.array_equal(host(keff), np.minimum(K, np.sum(ora["idx"] >= 0, axis=-1)))
     return ex, (kb, mx, ce, fo, n, q0, ora, idx)
+
+
+def _rerank_fn(q, k, cfg, n, share_group):
+    """Scores for the gap rule of the forest selection: each prefix cell's
+    re-rank score (logsumexp over its token keys).  A row whose oracle cut
+    margin is below 1e-6 may end on another set, but every cell it keeps must
+    re-rank within 1e-6 of the oracle's K-th."""
+    def score_fn(pos):
+        return oracle.cell_token_lse(q, k, Hkv=cfg["Hkv"], b=cfg["b"], bidx=pos[0], hs=pos[1], row=pos[2],
+                                     ncells=n, share_group=share_group)
+    return score_fn
 
 
 @pytest.mark.parametrize("over,nrows,share_group", [
@@ -105,11 +116,11 @@ def test_fsb_decode_step_end_to_end():
     cfg = config("prefill_cells", n=65536, Hq=2, Hkv=2, seed=161)
     x = make_inputs(cfg)
     ex, (kb, mx, ce, fo, n, q0, ora, idx) = _select_case(cfg, x, 1)
-    assert ex == 0 and np.array_equal(idx, ora["idx"])
+    assert np.array_equal(idx, ex.idx)
     b, qb, K = cfg["b"], cfg["qblock"], cfg["K"]
     q1 = np.ascontiguousarray(x["q"][:, :, q0:])
     akw = dict(b=b, K=K, q_pos0=q0, share_group=False, local=1, window=cfg["window"], prefix_mode=1, qblock=qb)
-    o_o, _ = oracle.attn_fwd(q1, x["k"], x["v"], ora["idx"], None, alpha=x["alpha"], **akw)
+    o_o, _ = oracle.attn_fwd(q1, x["k"], x["v"], ex.idx, None, alpha=x["alpha"], **akw)
     o, _ = ops.sparse_attn_fwd(dev(q1), dev(x["k"]), dev(x["v"]), dev(idx), None, alpha=dev(x["alpha"]), **akw)
     torch.cuda.synchronize()
     e = rel_err(host(o), o_o)
@@ -140,13 +151,11 @@ def test_fsb_decode_512k_full_size():
     o, _ = ops.sparse_attn_fwd(qd, kd, vd, idx, None, alpha=dev(x["alpha"]), **akw)
     torch.cuda.synchronize()
     idx = host(idx)
-    ex = check_indices(idx, ora)
+    ex = check_indices(idx, ora, _rerank_fn(x["q"], x["k"], cfg, n, False))
     _say(f"  exempt rows {ex}")
     assert np.array_equal(host(keff), np.minimum(K, np.sum(ora["idx"] >= 0, axis=-1)))
-    o_o, _ = oracle.attn_fwd(x["q"], x["k"], x["v"], ora["idx"], None, alpha=x["alpha"], **akw)
-    match = np.all(idx == ora["idx"], axis=-1)[:, :, 0]
+    o_o, _ = oracle.attn_fwd(x["q"], x["k"], x["v"], ex.idx, None, alpha=x["alpha"], **akw)
     for h in range(cfg["Hq"]):
-        if match[0, h]:
-            e = rel_err(host(o)[:, h:h + 1], o_o[:, h:h + 1])
-            assert e <= 2e-2, (h, e)
+        e = rel_err(host(o)[:, h:h + 1], o_o[:, h:h + 1])
+        assert e <= 2e-2, (h, e)
 

@@ -78,7 +78,16 @@ def _decode_paged(cfg, x, seed):
     kb_c, mx_c, ce_c = ops.sparse_block_summaries(kd, b, num_blocks=nblk_full, ccap=ccap)
     c_idx, c_logg, c_keff, c_o, c_lse = ops.sparse_decode_step(qd, kb_c, mx_c, ce_c, kd, vd, proj_w=pw, **kw)
     torch.cuda.synchronize()
-    r = dict(ora=ora, o_o=o_o, lse_o=lse_o)
+
+    def score_fn(pos):
+        return oracle.scores_one_row(x["q"], kb_o, mx_o, ce_o, Hkv=cfg["Hkv"], b=b, q_pos0=q_pos0, bidx=pos[0],
+                                     hs=pos[1], row=pos[2], share_group=cfg["share_group"], proj_w=proj)
+
+    def oracle_attn(idx_a, logg_a):
+        return oracle.attn_fwd(x["q"], x["k"], x["v"], idx_a, logg_a if gate else None, b=b, K=K, q_pos0=q_pos0,
+                               share_group=cfg["share_group"])[0]
+
+    r = dict(ora=ora, o_o=o_o, lse_o=lse_o, score_fn=score_fn, oracle_attn=oracle_attn)
     paged = dict(idx=host(idx), logg=None if logg is None else host(logg), keff=host(keff), o=host(o),
                  lse=host(lse), kb=host(kb), mx=host(mx))
     contig = dict(idx=host(c_idx), logg=None if c_logg is None else host(c_logg), keff=host(c_keff),

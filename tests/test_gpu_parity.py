@@ -122,9 +122,18 @@ def _decode_run(cfg, x, K=None):
     o_g2, lse_g2 = ops.sparse_attn_fwd(qd, kd, vd, dev(ora["idx"]), lg_in, b=b, K=K, q_pos0=q_pos0,
                                        share_group=cfg["share_group"])
     torch.cuda.synchronize()
+
+    def score_fn(pos):
+        return oracle.scores_one_row(x["q"], kb_o, mx_o, ce_o, Hkv=cfg["Hkv"], b=b, q_pos0=q_pos0, bidx=pos[0],
+                                     hs=pos[1], row=pos[2], share_group=cfg["share_group"], proj_w=proj)
+
+    def oracle_attn(idx, logg):
+        return oracle.attn_fwd(x["q"], x["k"], x["v"], idx, logg if gate else None, b=b, K=K, q_pos0=q_pos0,
+                               share_group=cfg["share_group"])[0]
+
     return dict(ora=ora, o_o=o_o, lse_o=lse_o, idx=host(idx_g), logg=None if logg_g is None else host(logg_g),
                 keff=host(keff_g), o=host(o_g), lse=host(lse_g), o2=host(o_g2), lse2=host(lse_g2),
-                kb_o=kb_o, mx_o=mx_o, ce_o=ce_o,
+                kb_o=kb_o, mx_o=mx_o, ce_o=ce_o, score_fn=score_fn, oracle_attn=oracle_attn,
                 fused=dict(idx=host(f_idx), logg=None if f_logg is None else host(f_logg), keff=host(f_keff),
                            o=host(f_o), lse=host(f_lse)))
 
@@ -150,20 +159,18 @@ def _check_decode_chain(cfg, r, c):
     """Selection and end-to-end output of one GPU chain c (idx, logg, keff,
     o) against the oracle."""
     ora, tol = r["ora"], _tol(cfg)
-    ex = check_indices(c["idx"], ora)
+    ex = check_indices(c["idx"], ora, r["score_fn"])
     assert np.array_equal(c["keff"], ora["k_eff"])
-    match = np.all(c["idx"] == ora["idx"], axis=-1)            # [B, Hsel, 1]
     if cfg["gate"]:
-        d = np.abs(c["logg"].astype(np.float64) - ora["logg"])
-        assert d[match].max(initial=0.0) <= 1e-4 * max(1.0, np.abs(ora["logg"]).max())
-    # end-to-end, on heads whose selection matches
-    G = cfg["Hq"] // cfg["Hkv"]
-    hmatch = np.repeat(match[:, :, 0], G if cfg["share_group"] else 1, axis=1)
+        d = np.abs(c["logg"].astype(np.float64) - ex.logg)
+        assert d.max(initial=0.0) <= 1e-4 * max(1.0, np.abs(ex.logg).max())
+    # end-to-end, every head: against the oracle's attention on the same
+    # selection (the GPU's valid alternative where a row's gap is below 1e-6)
+    o_ref = r["o_o"] if not ex.alt else r["oracle_attn"](ex.idx, ex.logg)
     for bi in range(cfg["B"]):
         for h in range(cfg["Hq"]):
-            if hmatch[bi, h]:
-                e = rel_err(c["o"][bi:bi + 1, h:h + 1], r["o_o"][bi:bi + 1, h:h + 1])
-                assert e <= tol, (bi, h, e)
+            e = rel_err(c["o"][bi:bi + 1, h:h + 1], o_ref[bi:bi + 1, h:h + 1])
+            assert e <= tol, (bi, h, e)
     return ex
 
 
@@ -352,24 +359,42 @@ def _prefill_run(cfg, x, rows=None):
     lg_o = dev(ora["logg"].astype(np.float32)) if gate else None
     o_g2, _ = ops.sparse_attn_fwd(qd, kd, vd, dev(ora["idx"]), lg_o, alpha=dev(x["alpha"]), **akw)
     torch.cuda.synchronize()
-    return ora, o_o, host(idx_g), host(keff_g), host(o_g), host(o_g2)
+    row_of = np.arange(L) if rows is None else np.asarray(rows)
+
+    def score_fn(pos):
+        return oracle.scores_one_row(x["q"], kb_o, mx_o, ce_o, Hkv=cfg["Hkv"], b=b, q_pos0=0, bidx=pos[0],
+                                     hs=pos[1], row=int(row_of[pos[2]]), prefix_mode=1, qblock=qb,
+                                     share_group=sg, erf_lambda=lam, erf_sigma=sig)
+
+    def oracle_attn(idx, logg, rows_alt):
+        return oracle.attn_fwd(x["q"], x["k"], x["v"], idx, logg if gate else None, alpha=x["alpha"],
+                               rows=rows_alt, **akw)[0]
+
+    return ora, o_o, host(idx_g), host(keff_g), host(o_g), host(o_g2), score_fn, oracle_attn
 
 
 def _check_prefill(cfg, x, rows=None):
-    ora, o_o, idx, keff, o, o2 = _prefill_run(cfg, x, rows)
+    ora, o_o, idx, keff, o, o2, score_fn, oracle_attn = _prefill_run(cfg, x, rows)
     sel = slice(None) if rows is None else rows
     r_idx = idx[:, :, sel]
-    sub = {k: v[:, :, sel] for k, v in ora.items() if k in ("idx", "gap", "k_eff")}
-    ex = check_indices(r_idx, sub)
+    sub = {k: v[:, :, sel] for k, v in ora.items() if k in ("idx", "gap", "k_eff", "logg")}
+    ex = check_indices(r_idx, sub, score_fn)
     assert np.array_equal(keff[:, :, sel], sub["k_eff"])
     tol = _tol(cfg)
     assert rel_err(o2[:, :, sel], o_o[:, :, sel]) <= tol
-    match = np.all(r_idx == sub["idx"], axis=-1)
-    if cfg["share_group"]:
-        match = np.repeat(match, cfg["Hq"] // cfg["Hkv"], axis=1)
+    o_ref = o_o
+    if ex.alt:
+        # rows where the GPU took a different valid top-K: the oracle's
+        # attention on that set
+        idx_f, lg_f = ora["idx"].copy(), ora["logg"].copy()
+        idx_f[:, :, sel], lg_f[:, :, sel] = ex.idx, ex.logg
+        row_of = np.arange(x["L"]) if rows is None else np.asarray(rows)
+        rows_alt = np.unique(row_of[[p[2] for p in ex.alt]]).astype(np.int64)
+        o_alt = oracle_attn(idx_f, lg_f, rows_alt)
+        o_ref = o_o.copy()
+        o_ref[:, :, rows_alt] = o_alt[:, :, rows_alt]
     for h in range(cfg["Hq"]):
-        m = match[0, h]
-        e = rel_err(o[:, h:h + 1, sel][:, :, m], o_o[:, h:h + 1, sel][:, :, m])
+        e = rel_err(o[:, h:h + 1, sel], o_ref[:, h:h + 1, sel])
         assert e <= tol, (h, e)
     return ex
 
@@ -441,18 +466,22 @@ def _train_case(cfg, x, kv_slice=-1, fwd_rows=None):
     o_g, lse_g = ops.sparse_attn_fwd(qd, kd, vd, idx_in, lg_in, **akw)
     dq, dk, dv, dg = ops.sparse_attn_bwd(qd, kd, vd, idx_in, lg_in, o_g, dod, lse_g, **akw)
     torch.cuda.synchronize()
-    return dict(ora=ora, o_o=o_o, lse_o=lse_o, dq_o=dq_o, dk_o=dk_o, dv_o=dv_o, dg_o=dg_o,
+
+    def score_fn(pos):
+        return oracle.scores_one_row(x["q"], kb_o, mx_o, ce_o, Hkv=cfg["Hkv"], b=b, q_pos0=0, bidx=pos[0],
+                                     hs=pos[1], row=pos[2], share_group=sg)
+
+    return dict(ora=ora, o_o=o_o, lse_o=lse_o, dq_o=dq_o, dk_o=dk_o, dv_o=dv_o, dg_o=dg_o, score_fn=score_fn,
                 idx=host(idx_g), logg=None if logg_g is None else host(logg_g), o=host(o_g),
                 lse=host(lse_g), dq=host(dq), dk=host(dk), dv=host(dv), dg=host(dg))
 
 
 def _check_train(cfg, r, kv_slice=-1, fwd_rows=None):
     tol = _tol(cfg)
-    ex = check_indices(r["idx"], r["ora"])
+    ex = check_indices(r["idx"], r["ora"], r["score_fn"])
     if cfg["gate"]:
-        m = np.all(r["idx"] == r["ora"]["idx"], axis=-1)
-        d = np.abs(r["logg"].astype(np.float64) - r["ora"]["logg"])
-        assert d[m].max(initial=0.0) <= 1e-4 * max(1.0, np.abs(r["ora"]["logg"]).max())
+        d = np.abs(r["logg"].astype(np.float64) - ex.logg)
+        assert d.max(initial=0.0) <= 1e-4 * max(1.0, np.abs(ex.logg).max())
     rs = slice(None) if fwd_rows is None else fwd_rows
     assert rel_err(r["o"][:, :, rs], r["o_o"][:, :, rs]) <= tol
     assert np.abs(r["lse"][:, :, rs] - r["lse_o"][:, :, rs]).max() <= 10 * tol
@@ -524,7 +553,9 @@ def test_chunked_prefill_rows_after_offset():
     idx_g, logg_g, _ = ops.sparse_score_select(dev(q), kb_g, mx_g, ce_g, **kw)
     o_g, lse_g = ops.sparse_attn_fwd(dev(q), kd, dev(x["v"]), dev(ora["idx"]),
                                      dev(ora["logg"].astype(np.float32)), b=b, K=K, q_pos0=q_pos0)
-    check_indices(host(idx_g), ora)
+    ex = check_indices(host(idx_g), ora, lambda p: oracle.scores_one_row(
+        q, kb_o, mx_o, ce_o, Hkv=2, b=b, q_pos0=q_pos0, bidx=p[0], hs=p[1], row=p[2]))
+    assert np.abs(host(logg_g).astype(np.float64) - ex.logg).max() <= 1e-4 * max(1.0, np.abs(ex.logg).max())
     assert rel_err(host(o_g), o_o) <= 2e-2
 
 
@@ -577,7 +608,9 @@ def test_one_workspace_shared_across_shapes_and_entry_points():
         o, _ = ops.sparse_attn_fwd(dev(x["q"]), kd, dev(x["v"]), dev(ora["idx"]), lg, b=b, K=K, q_pos0=pos,
                                    share_group=sg, workspace=ws)
         torch.cuda.synchronize()
-        check_indices(host(idx), ora)
+        check_indices(host(idx), ora, lambda p: oracle.scores_one_row(
+            x["q"], kb_o, mx_o, ce_o, Hkv=cfg["Hkv"], b=b, q_pos0=pos, bidx=p[0], hs=p[1], row=p[2],
+            share_group=sg))
         assert rel_err(host(o), o_o) <= _tol(cfg), (name, over)
 
 
@@ -605,13 +638,19 @@ def _select_only(cfg, x, *, gate, share_group, erf=True, prefix_mode=1, rows=Non
     idx, keff = host(idx_g), host(keff_g)
     sel = slice(None) if rows is None else rows
     sub = {k: v[:, :, sel] for k, v in ora.items() if k in ("idx", "gap", "k_eff", "logg")}
-    n_ex = check_indices(idx[:, :, sel], sub)
+    row_of = np.arange(x["L"]) if rows is None else np.asarray(rows)
+
+    def score_fn(pos):
+        return oracle.scores_one_row(x["q"], kb_o, mx_o, ce_o, Hkv=cfg["Hkv"], b=b, q_pos0=0, bidx=pos[0],
+                                     hs=pos[1], row=int(row_of[pos[2]]), prefix_mode=prefix_mode, qblock=qb,
+                                     share_group=share_group, **ekw)
+
+    n_ex = check_indices(idx[:, :, sel], sub, score_fn)
     assert np.array_equal(keff[:, :, sel], sub["k_eff"])
     if gate:
         lg = host(logg_g)[:, :, sel].astype(np.float64)
-        m = np.all(idx[:, :, sel] == sub["idx"], axis=-1)
-        d = np.abs(lg - sub["logg"])[m]
-        assert d.max(initial=0.0) <= 1e-4 * max(1.0, np.abs(sub["logg"]).max())
+        d = np.abs(lg - n_ex.logg)
+        assert d.max(initial=0.0) <= 1e-4 * max(1.0, np.abs(n_ex.logg).max())
     return n_ex
 
 

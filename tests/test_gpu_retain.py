@@ -64,12 +64,25 @@ def _fs_case(cfg, x, share_group, gate, rows_q=None, q_pos0=0):
                                                      erf_lambda=dev(lam), erf_sigma=dev(sig), **kw)
     torch.cuda.synchronize()
     idx, keff = host(idx), host(keff)
-    ex = check_indices(idx, ora)
+
+    def score_fn(pos):
+        # the row's scores on its kept candidate cells; every other cell is
+        # not a candidate of the subset selection
+        s = oracle.scores_one_row(q, kb, mx, ce, Hkv=cfg["Hkv"], b=b, q_pos0=q_pos0, bidx=pos[0], hs=pos[1],
+                                  row=pos[2], prefix_mode=1, qblock=qb, share_group=share_group,
+                                  erf_lambda=lam, erf_sigma=sig)
+        kvh = pos[1] if share_group else pos[1] // (cfg["Hq"] // cfg["Hkv"])
+        kept = cells[pos[0], kvh, :count[pos[0], kvh]]
+        out = np.full(s.shape, -np.inf)
+        kept = kept[(kept >= 0) & (kept < s.shape[0])]
+        out[kept] = s[kept]
+        return out
+
+    ex = check_indices(idx, ora, score_fn)
     assert np.array_equal(keff, ora["k_eff"])
     if gate:
-        m = np.all(idx == ora["idx"], axis=-1)
-        d = np.abs(host(logg).astype(np.float64) - ora["logg"])
-        assert d[m].max(initial=0.0) <= 1e-4 * max(1.0, np.abs(ora["logg"]).max())
+        d = np.abs(host(logg).astype(np.float64) - ex.logg)
+        assert d.max(initial=0.0) <= 1e-4 * max(1.0, np.abs(ex.logg).max())
     return ex, (kb, mx, ce, cells, count, ora)
 
 
@@ -111,7 +124,9 @@ def _fsl_step(cfg, x, q1, pos):
     ex, (kb, mx, ce, cells_o, count_o, ora) = _fs_case(cfg, x, False, False, rows_q=q1, q_pos0=pos)
     ncand = (qb * (pos // qb)) // b
     akw = dict(b=b, K=K, q_pos0=pos, share_group=False, local=1, window=cfg["window"], prefix_mode=1, qblock=qb)
-    o_o, _ = oracle.attn_fwd(q1, x["k"], x["v"], ora["idx"], None, alpha=x["alpha"], **akw)
+    # the oracle's attention on the oracle's selection, or on the GPU's where
+    # a row with a K-boundary gap below 1e-6 took another valid top-K
+    o_o, _ = oracle.attn_fwd(q1, x["k"], x["v"], ex.idx, None, alpha=x["alpha"], **akw)
     # GPU chain from the keys: summaries, kept set, selection, attention
     kd, vd, qd = dev(x["k"]), dev(x["v"]), dev(q1)
     kb_g, mx_g, ce_g = ops.sparse_block_summaries(kd, b)
@@ -122,7 +137,7 @@ def _fsl_step(cfg, x, q1, pos):
     o, _ = ops.sparse_attn_fwd(qd, kd, vd, idx, None, alpha=dev(x["alpha"]), **akw)
     torch.cuda.synchronize()
     assert np.array_equal(host(cells), cells_o) and np.array_equal(host(count), count_o)
-    assert ex == 0 and np.array_equal(host(idx), ora["idx"])
+    assert np.array_equal(host(idx), ex.idx)
     e = rel_err(host(o), o_o)
     _say(f"  o rel err {e:.2e}")
     assert e <= 2e-2

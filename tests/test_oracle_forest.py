@@ -123,3 +123,44 @@ def test_full_beam_is_the_brute_force_rerank(n, F, K):
         want = np.full(K, -1, np.int32)
         want[:len(order)] = sorted(order)
         assert np.array_equal(r["idx"][0, h, 0], want)
+
+
+def test_cell_token_lse_closed_forms():
+    """The re-rank score of a cell (logsumexp over its b token keys of
+    qhat.k/sqrt(d)) on keys with closed forms: b identical keys give
+    s + log b; a cell of two distinct keys, each b/2 times, gives
+    log((b/2)(e^s1 + e^s2)); with a shared group qhat is the heads' mean."""
+    d, b = 4, 8
+    q = np.array([[[[1.0, -0.5, 2.0, 0.25]], [[3.0, 0.5, 0.0, -0.25]]]], np.float32)     # [1, 2, 1, d]
+    k1 = np.array([0.5, 1.0, -1.0, 2.0], np.float32)
+    k2 = np.array([-2.0, 0.25, 1.5, 0.0], np.float32)
+    k = np.zeros((1, 1, 3 * b, d), np.float32)
+    k[0, 0, 0:b] = k1
+    k[0, 0, b:2 * b:2] = k1
+    k[0, 0, b + 1:2 * b:2] = k2
+    k[0, 0, 2 * b:] = k2
+    for hs in (0, 1):
+        qh = q[0, hs, 0].astype(np.float64)
+        s1, s2 = qh @ k1 / 2.0, qh @ k2 / 2.0                     # sqrt(d) = 2
+        got = oracle.cell_token_lse(q, k, Hkv=1, b=b, bidx=0, hs=hs, row=0, ncells=3)
+        assert got[0] == pytest.approx(s1 + np.log(b), abs=1e-13)
+        assert got[1] == pytest.approx(np.log(b / 2 * (np.exp(s1) + np.exp(s2))), abs=1e-13)
+        assert got[2] == pytest.approx(s2 + np.log(b), abs=1e-13)
+    qm = q[0, :, 0].astype(np.float64).mean(axis=0)
+    got = oracle.cell_token_lse(q, k, Hkv=1, b=b, bidx=0, hs=0, row=0, ncells=1, share_group=True)
+    assert got[0] == pytest.approx(qm @ k1 / 2.0 + np.log(b), abs=1e-13)
+
+
+def test_cell_token_lse_ranks_like_the_full_beam_search():
+    """With at most 16 cells a forest scores its cells directly and the beam of
+    16 reaches every cell, so the selection is the top K of the per-cell
+    re-rank scores that cell_token_lse writes out."""
+    n, K, b = 16, 5, 4
+    k, kb, mx, ce, q, L = _inputs(777, n, b=b)
+    fo = oracle.forest_build(kb, mx, ce, n, F=16)
+    pos = L - 1
+    ora = oracle.forest_select(q, kb, mx, ce, k, fo, n, Hkv=2, b=b, K=K, q_pos0=pos, F=16, Wb=16)
+    for hs in range(2):
+        s = oracle.cell_token_lse(q, k, Hkv=2, b=b, bidx=0, hs=hs, row=0, ncells=n)
+        want, _, _, _, _ = oracle.select_from_scores(s, K, gate=False)
+        assert np.array_equal(ora["idx"][0, hs, 0], want)
