@@ -6,10 +6,19 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <string>
 
 #include "spa_launch.h"
 #include "../../include/sparse_attn.h"
+
+// Device memory of sparse_decode_step_noalloc: the chunk winners and split-K
+// partials that sparse_decode_step keeps in the caller's workspace.  Every
+// GPU the library runs on holds its own copy until the process ends.  In host
+// code this name is not a device address: the kernels get the address that
+// hipGetSymbolAddress returns for the current device (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[SPA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -215,6 +224,33 @@ spa_status hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Address of `scratch` on each device, resolved once per device (with that
+// device current) on the first no-alloc call made there.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+spa_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, "sparse_decode_step_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  SPA_REQUIRE(dev >= 0 && dev < kMaxDevices, SPA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr)
+        return fail(SPA_ERR_HIP, "sparse_decode_step_noalloc: hipGetSymbolAddress on device %d: %s", dev,
+                    hipGetErrorString(e));
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SPA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -385,6 +421,30 @@ spa_status sparse_decode_step(const spa_decode_args* a, void* workspace, size_t 
   hipError_t e = spa::launch_score_select(sp, workspace, s);
   if (e == hipSuccess) e = spa::launch_attn_fwd(ap, ws_att, s);
   return hip_status(e, "sparse_decode_step");
+}
+
+spa_status sparse_decode_step_noalloc(const spa_decode_args* a, spa_stream_t stream) {
+  ProfileScope profile_scope;
+  spa::SelectLaunch sp;
+  spa::AttnLaunch ap;
+  spa_status st = check_decode(a, &sp, &ap);
+  if (st != SPA_OK) return st;
+  const size_t need = decode_ws_bytes(sp, ap);
+  SPA_REQUIRE(need <= SPA_NOALLOC_SCRATCH_BYTES, SPA_ERR_WORKSPACE,
+              "sparse_decode_step_noalloc: this step needs %zu bytes of scratch, the library holds %zu "
+              "(use sparse_decode_step with a workspace)", need, static_cast<size_t>(SPA_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (need > 0) {
+    st = noalloc_scratch(&ws);
+    if (st != SPA_OK) return st;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws_att = static_cast<char*>(ws) + spa::align256(spa::select_workspace_bytes(sp));
+  if (spa::decode_fusable(sp))
+    return hip_status(spa::launch_decode_fused_attn(sp, ws, ap, ws_att, s), "sparse_decode_step_noalloc");
+  hipError_t e = spa::launch_score_select(sp, ws, s);
+  if (e == hipSuccess) e = spa::launch_attn_fwd(ap, ws_att, s);
+  return hip_status(e, "sparse_decode_step_noalloc");
 }
 
 spa_status sparse_decode_step_paged(const spa_decode_args* a, const spa_kv_pages* pages, void* workspace,

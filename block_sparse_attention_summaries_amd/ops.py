@@ -28,7 +28,7 @@ SPA_OP_SCORE_SELECT, SPA_OP_ATTN_FWD, SPA_OP_ATTN_BWD, SPA_OP_SELECT_BWD, SPA_OP
 
 EXPORTED = ["sparse_abi_version", "sparse_last_error", "spa_abi_version", "spa_profile_next_call", "spa_last_error",
             "sparse_block_summaries", "sparse_score_select",
-            "sparse_attn_fwd", "sparse_attn_bwd", "sparse_select_bwd", "sparse_decode_step",
+            "sparse_attn_fwd", "sparse_attn_bwd", "sparse_select_bwd", "sparse_decode_step", "sparse_decode_step_noalloc",
             "sparse_block_summaries_paged", "sparse_decode_step_paged", "sparse_retain_cells",
             "sparse_score_select_subset", "sparse_forest_nodes", "sparse_forest_workspace_bytes",
             "sparse_forest_build", "sparse_forest_select", "sparse_quantize_summaries_fp8",
@@ -108,6 +108,8 @@ def lib():
         L.sparse_select_bwd.argtypes = [ctypes.POINTER(SelectArgs), ctypes.POINTER(SelectGrads), _vp, _sz, _vp]
         L.sparse_decode_step.restype = _i
         L.sparse_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp, _sz, _vp]
+        L.sparse_decode_step_noalloc.restype = _i
+        L.sparse_decode_step_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
         L.sparse_block_summaries_paged.restype = _i
         L.sparse_block_summaries_paged.argtypes = [_vp, _i, _i, _i, _i64, _i, _i, ctypes.POINTER(KvPages), _i64,
                                                    _i64, _i64, _vp, _vp, _vp, _vp]
@@ -362,6 +364,22 @@ def sparse_decode_step(q, kbar, max_norm, centre, k, v, *, Hkv, b, K, q_pos0, ga
     da = DecodeArgs(select=ctypes.pointer(sa), attn=ctypes.pointer(aa))
     buf, size = _ws(workspace, SPA_OP_DECODE_STEP, da, q.device)
     _check(lib().sparse_decode_step(ctypes.byref(da), _p(buf), size, _stream(stream)))
+    return idx, logg, k_eff, o, lse
+
+
+def sparse_decode_step_noalloc(q, kbar, max_norm, centre, k, v, *, Hkv, b, K, q_pos0, gate=True, share_group=True,
+                               proj_w=None, idx=None, logg=None, k_eff=None, o=None, lse=None, stream=None,
+                               kbar_scale=None):
+    """sparse_decode_step with the library's own device scratch instead of a
+    workspace (no device allocation by the library; outputs allocated here
+    when not given).  Returns (idx, logg, k_eff, o, lse)."""
+    sa, (idx, logg, k_eff) = select_args(q, kbar, max_norm, centre, Hkv=Hkv, b=b, K=K, q_pos0=q_pos0, gate=gate,
+                                         share_group=share_group, proj_w=proj_w, idx=idx, logg=logg,
+                                         k_eff=k_eff, kbar_scale=kbar_scale)
+    aa, (o, lse) = attn_args(q, k, v, idx, logg, b=b, K=K, q_pos0=q_pos0, share_group=share_group, o=o,
+                             lse=lse)
+    da = DecodeArgs(select=ctypes.pointer(sa), attn=ctypes.pointer(aa))
+    _check(lib().sparse_decode_step_noalloc(ctypes.byref(da), _stream(stream)))
     return idx, logg, k_eff, o, lse
 
 

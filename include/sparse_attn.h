@@ -283,6 +283,27 @@ spa_status sparse_decode_step(const spa_decode_args *a, void *workspace, size_t 
                        spa_stream_t stream);
 
 /*
+ * sparse_decode_step_noalloc -- sparse_decode_step without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc.  The
+ * step's scratch (chunk winners and split-K partials) lives in a device array
+ * of SPA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends; nothing is allocated or freed by the call.  Arguments,
+ * outputs and results are those of sparse_decode_step (the same kernels).
+ *  - Returns SPA_ERR_WORKSPACE, launching nothing, when the step needs more
+ *    than SPA_NOALLOC_SCRATCH_BYTES (sparse_workspace_bytes(SPA_OP_DECODE_STEP,
+ *    a) tells; about 0.6 MiB for one sequence of 8 kv heads, K = 32, d = 128).
+ *  - The first call on a device looks up that device's copy of the array
+ *    (hipGetSymbolAddress with the device current): make it outside graph
+ *    capture.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents (the step needs no zeroed scratch): calls that overlap
+ *    in time on one GPU, on any streams, race.  Serialise them.
+ */
+#define SPA_NOALLOC_SCRATCH_BYTES (8u << 20)
+spa_status sparse_decode_step_noalloc(const spa_decode_args *a, spa_stream_t stream);
+
+/*
  * Paged K / V ("SAS" review, inference setup: a paged KV cache): the key and
  * value caches are page pools [num_pages, Hkv, b, d] (one page = one block of
  * b tokens of every kv head, each head's block contiguous) and logical block

@@ -208,6 +208,26 @@ def test_decode_step_validation_and_workspace():
     assert lib.sparse_decode_step(None, FAKE, 1 << 30, None) == ops.SPA_ERR_INVALID_ARG
 
 
+def test_decode_step_noalloc_rejects_before_launch():
+    """The no-alloc step validates like sparse_decode_step and refuses a step
+    whose scratch exceeds the library's array, before any HIP call."""
+    lib = ops.lib()
+    cap = 8 << 20                                   # SPA_NOALLOC_SCRATCH_BYTES
+    # 64 sequences x 8 kv heads, K = 64: the split-K partials alone exceed it
+    sel = _sel(B=64, K=64, q_pos0=(1 << 20) + 63, ccap=1 << 14)
+    att = _attn(B=64, K=64, q_pos0=(1 << 20) + 63, L=(1 << 20) + 64)
+    da = ops.DecodeArgs(select=ctypes.pointer(sel), attn=ctypes.pointer(att))
+    assert lib.sparse_workspace_bytes(ops.SPA_OP_DECODE_STEP, ctypes.byref(da)) > cap
+    assert lib.sparse_decode_step_noalloc(ctypes.byref(da), None) == ops.SPA_ERR_WORKSPACE
+    assert "scratch" in lib.sparse_last_error().decode()
+    # the decode_32k step fits
+    da = ops.DecodeArgs(select=ctypes.pointer(_sel()), attn=ctypes.pointer(_attn()))
+    assert lib.sparse_workspace_bytes(ops.SPA_OP_DECODE_STEP, ctypes.byref(da)) <= cap
+    assert lib.sparse_decode_step_noalloc(None, None) == ops.SPA_ERR_INVALID_ARG
+    bad = ops.DecodeArgs(select=ctypes.pointer(_sel()), attn=ctypes.pointer(_attn(K=8)))
+    assert lib.sparse_decode_step_noalloc(ctypes.byref(bad), None) == ops.SPA_ERR_INVALID_ARG
+
+
 def test_summaries_rejects_invalid_arguments():
     lib = ops.lib()
     f = lib.sparse_block_summaries
