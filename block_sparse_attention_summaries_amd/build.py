@@ -9,7 +9,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsparse_attn.so")
-SOURCES = ["api.hip", "summaries.hip", "select.hip", "select_mfma.hip", "select_bwd.hip", "retain.hip", "forest.hip", "attn.hip", "attn_mfma.hip", "attn_bwd_mfma.hip"]
+SOURCES = ["api.hip", "summaries.hip", "select.hip", "select_mfma.hip", "select_bwd.hip", "retain.hip", "forest.hip", "attn.hip", "decode_step.hip", "attn_mfma.hip", "attn_bwd_mfma.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -208,8 +208,29 @@ spa_status check_decode(const spa_decode_args* d, spa::SelectLaunch* sp, spa::At
   return SPA_OK;
 }
 
+// Selection part of the one-call step's workspace.  The flag block of the
+// one-call scorer sits at offset 0 on both paths: the two-call fallback keeps
+// its scratch after it, so a workspace can serve steps of either path in turn
+// without disturbing the flags (zero between calls).
+size_t decode_sel_bytes(const spa::SelectLaunch& sp) {
+  const size_t two = spa::kStepFlagBytes + spa::select_workspace_bytes(sp);
+  const size_t one = spa::decode_fusable(sp) ? spa::decode_step_select_bytes(sp) : 0;
+  return spa::align256(two > one ? two : one);
+}
+
+static_assert(SPA_DECODE_FLAG_BYTES == spa::kStepFlagBytes, "the decode step's flag block");
+
+hipError_t run_decode_step(const spa::SelectLaunch& sp, const spa::AttnLaunch& ap, void* ws, hipStream_t s) {
+  char* base = static_cast<char*>(ws);
+  char* ws_att = base + decode_sel_bytes(sp);
+  if (spa::decode_fusable(sp)) return spa::launch_decode_fused_attn(sp, ws, ap, ws_att, s);
+  hipError_t e = spa::launch_score_select(sp, base + spa::kStepFlagBytes, s);
+  if (e == hipSuccess) e = spa::launch_attn_fwd(ap, ws_att, s);
+  return e;
+}
+
 size_t decode_ws_bytes(const spa::SelectLaunch& sp, const spa::AttnLaunch& ap) {
-  return spa::align256(spa::select_workspace_bytes(sp)) + spa::attn_fwd_workspace_bytes(ap);
+  return decode_sel_bytes(sp) + spa::decode_step_workspace_bytes(ap);
 }
 
 spa_status check_ws(void* ws, size_t have, size_t need) {
@@ -414,13 +435,7 @@ spa_status sparse_decode_step(const spa_decode_args* a, void* workspace, size_t 
   if (st != SPA_OK) return st;
   st = check_ws(workspace, ws_bytes, decode_ws_bytes(sp, ap));
   if (st != SPA_OK) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws_att = static_cast<char*>(workspace) + spa::align256(spa::select_workspace_bytes(sp));
-  if (spa::decode_fusable(sp))
-    return hip_status(spa::launch_decode_fused_attn(sp, workspace, ap, ws_att, s), "sparse_decode_step");
-  hipError_t e = spa::launch_score_select(sp, workspace, s);
-  if (e == hipSuccess) e = spa::launch_attn_fwd(ap, ws_att, s);
-  return hip_status(e, "sparse_decode_step");
+  return hip_status(run_decode_step(sp, ap, workspace, static_cast<hipStream_t>(stream)), "sparse_decode_step");
 }
 
 spa_status sparse_decode_step_noalloc(const spa_decode_args* a, spa_stream_t stream) {
@@ -438,13 +453,7 @@ spa_status sparse_decode_step_noalloc(const spa_decode_args* a, spa_stream_t str
     st = noalloc_scratch(&ws);
     if (st != SPA_OK) return st;
   }
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws_att = static_cast<char*>(ws) + spa::align256(spa::select_workspace_bytes(sp));
-  if (spa::decode_fusable(sp))
-    return hip_status(spa::launch_decode_fused_attn(sp, ws, ap, ws_att, s), "sparse_decode_step_noalloc");
-  hipError_t e = spa::launch_score_select(sp, ws, s);
-  if (e == hipSuccess) e = spa::launch_attn_fwd(ap, ws_att, s);
-  return hip_status(e, "sparse_decode_step_noalloc");
+  return hip_status(run_decode_step(sp, ap, ws, static_cast<hipStream_t>(stream)), "sparse_decode_step_noalloc");
 }
 
 spa_status sparse_decode_step_paged(const spa_decode_args* a, const spa_kv_pages* pages, void* workspace,
@@ -458,13 +467,7 @@ spa_status sparse_decode_step_paged(const spa_decode_args* a, const spa_kv_pages
   if (st != SPA_OK) return st;
   st = check_ws(workspace, ws_bytes, decode_ws_bytes(sp, ap));
   if (st != SPA_OK) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws_att = static_cast<char*>(workspace) + spa::align256(spa::select_workspace_bytes(sp));
-  if (spa::decode_fusable(sp))
-    return hip_status(spa::launch_decode_fused_attn(sp, workspace, ap, ws_att, s), "sparse_decode_step_paged");
-  hipError_t e = spa::launch_score_select(sp, workspace, s);
-  if (e == hipSuccess) e = spa::launch_attn_fwd(ap, ws_att, s);
-  return hip_status(e, "sparse_decode_step_paged");
+  return hip_status(run_decode_step(sp, ap, workspace, static_cast<hipStream_t>(stream)), "sparse_decode_step_paged");
 }
 
 spa_status sparse_retain_cells(const float* max_norm, int B, int Hkv, int64_t ccap, int64_t ncand, int W, int P,
@@ -613,6 +616,18 @@ spa_status sparse_workspace_init(void* workspace, size_t ws_bytes, spa_stream_t 
               "workspace must be 16-byte aligned with a size multiple of 16");
   return hip_status(spa::launch_zero_fill(workspace, ws_bytes, static_cast<hipStream_t>(stream)),
                     "sparse_workspace_init");
+}
+
+spa_status sparse_probe_load_chase(const uint32_t* next, int64_t n, int steps, uint32_t start, uint32_t* out,
+                                   spa_stream_t stream) {
+  ProfileScope profile_scope;
+  SPA_REQUIRE(next != nullptr && out != nullptr, SPA_ERR_INVALID_ARG, "next and out must be device pointers");
+  SPA_REQUIRE(n >= 1 && n <= (int64_t{1} << 32) && (n & (n - 1)) == 0, SPA_ERR_INVALID_ARG,
+              "n = %lld: a power of two in [1, 2^32]", static_cast<long long>(n));
+  SPA_REQUIRE(steps >= 1, SPA_ERR_INVALID_ARG, "steps = %d: at least 1", steps);
+  return hip_status(spa::launch_load_chase(next, static_cast<uint32_t>(n - 1), steps, start, out,
+                                           static_cast<hipStream_t>(stream)),
+                    "sparse_probe_load_chase");
 }
 
 }  // extern "C"

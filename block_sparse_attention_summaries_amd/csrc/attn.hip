@@ -22,6 +22,7 @@
 #include <type_traits>
 
 #include "decode_merge.h"
+#include "decode_tile.h"
 #include "spa_device.h"
 #include "spa_launch.h"
 
@@ -29,13 +30,14 @@ namespace spa {
 
 
 // ======================================================== decode: split-K
-constexpr int kTileTok = 64;
 
 // Online-softmax partial of one K/V tile for the HPW query heads of a group:
 // loads the tile into LDS once, then scores, (m, l) and acc per head.  All
 // global loads are unconditional (rows past ntok are clamped to the last
 // valid row and masked out of the softmax).
-template <typename T, int D, int HPW>
+// kPublish: the partial is stored with agent-scope write-through stores (it
+// is read back in the same kernel by the head's last workgroup).
+template <typename T, int D, int HPW, bool kPublish = false>
 __device__ __forceinline__ void tile_partial(const T* __restrict__ q, const T* __restrict__ kt,
                                              const T* __restrict__ vt, int bi, int hs, int G, int Hq,
                                              int share_group, int ntok, float bias, float* __restrict__ ws_acc,
@@ -103,7 +105,12 @@ __device__ __forceinline__ void tile_partial(const T* __restrict__ q, const T* _
       const float p = j < ntok ? __expf(z - m) : 0.f;
       const float l = wave_sum(p);
       s_p[hh][j] = p;
-      if (lane == 0) ws_ml[obase + hh] = make_float2(m, l);
+      if (lane == 0) {
+        if constexpr (kPublish)
+          publish_f2(ws_ml + obase + hh, m, l);
+        else
+          ws_ml[obase + hh] = make_float2(m, l);
+      }
     }
   }
   __syncthreads();
@@ -120,8 +127,17 @@ __device__ __forceinline__ void tile_partial(const T* __restrict__ q, const T* _
 #pragma unroll
         for (int c = 0; c < kCPL; ++c) acc[c] = fmaf(pj, ld_f(&s_v[j * D + kCPL * lane + c]), acc[c]);
       }
+      float* out = ws_acc + (obase + hh) * D + kCPL * lane;
+      if constexpr (kPublish) {
+        static_assert(kCPL == 1 || kCPL == 2, "columns per lane");
+        if constexpr (kCPL == 2)
+          publish_f2(out, acc[0], acc[1]);
+        else
+          publish_u32(out, __float_as_uint(acc[0]));
+      } else {
 #pragma unroll
-      for (int c = 0; c < kCPL; ++c) ws_acc[(obase + hh) * D + kCPL * lane + c] = acc[c];
+        for (int c = 0; c < kCPL; ++c) out[c] = acc[c];
+      }
     }
   }
 }
@@ -130,7 +146,6 @@ __device__ __forceinline__ void tile_partial(const T* __restrict__ q, const T* _
 // group).  All ntiles partial accumulators of that query head are staged in
 // LDS with one round of independent loads, then each output element sums
 // them with the softmax weights exp(m_t - M).
-constexpr int kMaxTiles = 130;   // (K + 1) * tiles per unit for K <= 64, b <= 128
 
 // Offset (elements) of the first of the rows [start, start + ntok) of
 // (batch bi, kv head kvh) in the K / V cache, which never cross a block:
@@ -189,89 +204,10 @@ __global__ __launch_bounds__(256) void decode_attn_partial_kernel(
   if (ntok == 0) {
     for (int x = tid; x < HPW * D; x += 256) ws_acc[obase * D + x] = 0.f;
     if (tid < HPW) ws_ml[obase + tid] = make_float2(-INFINITY, 0.f);
-  } else {
-    tile_partial<T, D, HPW>(q, k + off, v + off, bi, hs, G, Hq, share_group, ntok, bias, ws_acc, ws_ml, obase);
-  }
-}
-
-// Decode step with the top-K merge folded in: every workgroup of a kept
-// selected unit first runs the two-level merge of its head's chunk winners
-// (decode_merge.h) to learn which block its slot holds, instead of reading
-// idx written by a separate merge kernel; the workgroup of slot 0, tile 0
-// also writes the selection outputs (idx, log g, K_eff).  The current-block
-// workgroups need no merge.  Saves one dependent kernel per step; each
-// workgroup reads its head's chunk records (K x chunks x 8 bytes).
-template <typename T, int D, int HPW, int NV, int NV2>
-__global__ __launch_bounds__(256) void decode_fused_partial_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const uint64_t* __restrict__ ws_keys, const float2* __restrict__ ws_sel_ml, int nchunks, int64_t ncand,
-    int gate, int32_t* __restrict__ idx, float* __restrict__ logg, int32_t* __restrict__ k_eff, int Hq, int Hkv,
-    int Hsel, int share_group, int64_t L, int64_t pos, int b, int K, int tpu, float* __restrict__ ws_acc,
-    float2* __restrict__ ws_ml, const int32_t* __restrict__ table, int64_t tstride, int64_t npages) {
-  __shared__ uint64_t s_win[4 * 64];
-  __shared__ float2 s_mlw[4];
-  __shared__ uint32_t s_lo[4];
-  __shared__ int32_t s_c;
-  __shared__ float s_lg;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int bh = blockIdx.y;
-  const int bi = bh / Hsel, hs = bh % Hsel;
-  const int G = Hq / Hkv;
-  const int kvh = share_group ? hs : hs / G;
-  const int unit = blockIdx.x / tpu, sub = blockIdx.x % tpu;
-  const int ntiles = (K + 1) * tpu;
-  const int tile = blockIdx.x;
-
-  int64_t start = 0;
-  int ntok = 0;
-  float bias = 0.f;
-  const int64_t c0 = pos / b;
-  if (unit < K) {
-    merge_level1<NV>(ws_keys + static_cast<int64_t>(bh) * nchunks * K,
-                     ws_sel_ml + static_cast<int64_t>(bh) * nchunks, nchunks, K, s_win, s_mlw, s_lo);
-    __syncthreads();
-    if (wave == 0) {
-      const bool out = unit == 0 && sub == 0;
-      const int64_t o = static_cast<int64_t>(bh) * K;      // one query row
-      const int kk = static_cast<int>(ncand < K ? ncand : K);
-      const int kept = merge_level2<NV2>(s_win, s_mlw, s_lo, K, kk, gate, [&](int slot, int32_t c, float lg) {
-        if (slot == unit) {
-          s_c = c;
-          s_lg = lg;
-        }
-        if (out) {
-          idx[o + slot] = c;
-          if (logg != nullptr) logg[o + slot] = lg;
-        }
-      });
-      if (lane == 0 && kept <= unit) s_c = -1;
-      if (out) {
-        for (int x = kept + lane; x < K; x += kWave) {
-          idx[o + x] = -1;
-          if (logg != nullptr) logg[o + x] = 0.f;
-        }
-        if (lane == 0 && k_eff != nullptr) k_eff[bh] = kk;
-      }
-    }
-    __syncthreads();
-    const int32_t c = s_c;
-    if (c >= 0 && c < c0) {
-      start = static_cast<int64_t>(c) * b + sub * kTileTok;
-      ntok = b - sub * kTileTok < kTileTok ? b - sub * kTileTok : kTileTok;
-      bias = s_lg;
-    }
-  } else {
-    start = c0 * b + sub * kTileTok;
-    const int64_t n = pos + 1 - start;
-    const int cap = b - sub * kTileTok < kTileTok ? b - sub * kTileTok : kTileTok;
-    ntok = n <= 0 ? 0 : (n < cap ? static_cast<int>(n) : cap);
-  }
-
-  const int64_t obase = (static_cast<int64_t>(bh) * ntiles + tile) * HPW;
-  const int64_t off = ntok > 0 ? kv_tile_offset<D>(bi, kvh, Hkv, L, b, start, ntok, table, tstride, npages) : 0;
-  if (ntok == 0) {
-    for (int x = tid; x < HPW * D; x += 256) ws_acc[obase * D + x] = 0.f;
-    if (tid < HPW) ws_ml[obase + tid] = make_float2(-INFINITY, 0.f);
+  } else if constexpr (std::is_same<T, bf16_t>::value) {
+    const int hq0 = share_group ? hs * G : hs;
+    tile_partial_bf16<D, HPW, false>(q + (static_cast<int64_t>(bi) * Hq + hq0) * D, k + off, v + off, ntok, bias,
+                                     ws_acc, ws_ml, obase);
   } else {
     tile_partial<T, D, HPW>(q, k + off, v + off, bi, hs, G, Hq, share_group, ntok, bias, ws_acc, ws_ml, obase);
   }
@@ -782,7 +718,7 @@ static bool use_decode_attn(const AttnLaunch& p) {
   return p.nq == 1 && p.local == 0 && p.window == 0 && p.alpha == nullptr && p.b <= 128;
 }
 
-static int decode_tpu(const AttnLaunch& p) { return p.b > kTileTok ? p.b / kTileTok : 1; }
+static int decode_tpu(const AttnLaunch& p) { return decode_step_tpu(p); }
 
 static int heads_per_wg(const AttnLaunch& p) { return p.share_group ? p.Hq / p.Hkv : 1; }
 
@@ -806,6 +742,10 @@ size_t attn_fwd_workspace_bytes(const AttnLaunch& p) {
          align256(heads * ntiles * hpw * sizeof(float2));
 }
 
+size_t decode_step_workspace_bytes(const AttnLaunch& p) {
+  return attn_fwd_workspace_bytes(p) + align256(static_cast<size_t>(p.B) * p.Hsel * sizeof(uint32_t));
+}
+
 size_t attn_bwd_workspace_bytes(const BwdLaunch& p) {
   const size_t dbuf = align256(static_cast<size_t>(p.a.B) * p.a.Hq * p.a.nq * sizeof(float));
   return attn_tile_bwd_supported(p) ? dbuf + attn_tile_bwd_bitmap_bytes(p) : dbuf;
@@ -826,62 +766,6 @@ static hipError_t launch_decode_attn_h(const AttnLaunch& p, void* ws, hipStream_
   if (e != hipSuccess) return e;
   return launch(true, decode_combine_kernel<T, D, HPW>, dim3(HPW, static_cast<unsigned>(heads)), dim3(256), st,
                 acc, ml, p.Hq, p.Hkv, p.Hsel, p.share_group, ntiles, static_cast<T*>(p.o), p.lse);
-}
-
-template <int D, int HPW, int NV, int NV2>
-static hipError_t launch_fused_nv(const SelectLaunch& s, void* ws_sel, const AttnLaunch& p, void* ws,
-                                  hipStream_t st) {
-  const int tpu = decode_tpu(p);
-  const int ntiles = (p.K + 1) * tpu;
-  const size_t heads = static_cast<size_t>(p.B) * p.Hsel;
-  char* base = static_cast<char*>(ws);
-  float* acc = reinterpret_cast<float*>(base);
-  float2* ml = reinterpret_cast<float2*>(base + align256(heads * ntiles * HPW * p.d * sizeof(float)));
-  const DecodeSelectWs w = decode_select_ws(s, ws_sel);
-  hipError_t e = launch(false, decode_fused_partial_kernel<bf16_t, D, HPW, NV, NV2>,
-                        dim3(ntiles, static_cast<unsigned>(heads)), dim3(256), st, static_cast<const bf16_t*>(p.q),
-                        static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
-                        static_cast<const uint64_t*>(w.keys), static_cast<const float2*>(w.ml), w.nch, s.max_cand,
-                        s.gate, s.idx, s.logg, s.k_eff, p.Hq, p.Hkv, p.Hsel, p.share_group, p.L, p.q_pos0, p.b,
-                        p.K, tpu, acc, ml, p.pages.table, p.pages.tstride, p.pages.npages);
-  if (e != hipSuccess) return e;
-  return launch(true, decode_combine_kernel<bf16_t, D, HPW>, dim3(HPW, static_cast<unsigned>(heads)), dim3(256),
-                st, acc, ml, p.Hq, p.Hkv, p.Hsel, p.share_group, ntiles, static_cast<bf16_t*>(p.o), p.lse);
-}
-
-template <int D, int HPW>
-static hipError_t launch_fused_h(const SelectLaunch& s, void* ws_sel, const AttnLaunch& p, void* ws,
-                                 hipStream_t st) {
-  // level-2 survivors: 4 K records, NV2 per lane
-  const int nv = decode_merge_nv(s);
-  if (s.K <= 32) {
-    if (nv <= 2) return launch_fused_nv<D, HPW, 2, 2>(s, ws_sel, p, ws, st);
-    if (nv <= 4) return launch_fused_nv<D, HPW, 4, 2>(s, ws_sel, p, ws, st);
-    return launch_fused_nv<D, HPW, 8, 2>(s, ws_sel, p, ws, st);
-  }
-  if (nv <= 2) return launch_fused_nv<D, HPW, 2, 4>(s, ws_sel, p, ws, st);
-  if (nv <= 4) return launch_fused_nv<D, HPW, 4, 4>(s, ws_sel, p, ws, st);
-  return launch_fused_nv<D, HPW, 8, 4>(s, ws_sel, p, ws, st);
-}
-
-template <int D>
-static hipError_t launch_fused_d(const SelectLaunch& s, void* ws_sel, const AttnLaunch& p, void* ws,
-                                 hipStream_t st) {
-  switch (heads_per_wg(p)) {
-    case 1: return launch_fused_h<D, 1>(s, ws_sel, p, ws, st);
-    case 2: return launch_fused_h<D, 2>(s, ws_sel, p, ws, st);
-    case 4: return launch_fused_h<D, 4>(s, ws_sel, p, ws, st);
-    default: return launch_fused_h<D, 8>(s, ws_sel, p, ws, st);
-  }
-}
-
-// Chunk kernel, then the merge folded into the attention partials, then the
-// combine (bf16, decode_fusable selections only).
-hipError_t launch_decode_fused_attn(const SelectLaunch& s, void* ws_sel, const AttnLaunch& a, void* ws_att,
-                                    hipStream_t st) {
-  hipError_t e = launch_decode_chunks(s, ws_sel, st);
-  if (e != hipSuccess) return e;
-  return a.d == 64 ? launch_fused_d<64>(s, ws_sel, a, ws_att, st) : launch_fused_d<128>(s, ws_sel, a, ws_att, st);
 }
 
 template <typename T, int D, int HPW>

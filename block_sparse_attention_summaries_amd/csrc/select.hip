@@ -37,41 +37,26 @@ namespace spa {
 // position order is index order, which makes the lower-index tie rule and
 // the ascending output a single ordered compaction (ballot + mbcnt).
 
-// One workgroup per (chunk of 256 candidate blocks, selection head).  All
-// global reads of the workgroup (the chunk's summaries, the query heads and,
-// with a projection, W) are issued before any of them is consumed.  Output:
-// the chunk's top-min(K, n) candidates in index order as 64-bit
-// (orderable score << 32 | block index) records (0 pads), and its (max, sum exp).
-template <typename T, int D, bool F8>
-__global__ __launch_bounds__(256) void decode_chunk_kernel(
-    const T* __restrict__ q, const void* __restrict__ kbar_v, const float* __restrict__ kscale,
-    const float* __restrict__ proj_w, int Hq, int Hkv, int Hsel, int share_group, int64_t ccap, int64_t ncand,
-    int K, uint64_t* __restrict__ ws_keys, float2* __restrict__ ws_ml, int nchunks) {
-  // F8: the summaries are E4M3 codes (16 per 16-byte load) scaled per block
-  constexpr int kVec = F8 ? 16 : Elem<T>::kVec;   // summary elements per 16-byte load
-  constexpr int kElemBytes = F8 ? 1 : static_cast<int>(sizeof(T));
-  constexpr int kLPB = D / kVec;           // lanes per block row
-  constexpr int kBPR = kWave / kLPB;       // blocks per load round of a wave
-  constexpr int kRounds = kWave / kBPR;    // rounds to cover the wave's 64 blocks
+// Per-selection-head query of the scores: u = W^T q_hat with the projection,
+// q_hat without; q_hat is the mean of the G query heads of a shared
+// selection (fp32, summed in head order), else the head's query.  Formed by
+// the whole workgroup into s_uv[D] (synchronised on return).  The same
+// arithmetic wherever it is formed: thread slices of kEPG rows of W, then the
+// kEGroups slice sums added in order.
+template <typename T, int D>
+__device__ __forceinline__ void form_u(const T* __restrict__ q, const float* __restrict__ proj_w, int Hq, int Hkv,
+                                       int Hsel, int share_group, int bh, float* s_uv) {
   constexpr int kQuads = D / 4;             // float4 column groups of W
   constexpr int kEGroups = 256 / kQuads;    // row groups (one per thread slice)
   constexpr int kEPG = D / kEGroups;        // rows of W per thread
+  constexpr int kGMax = 8;
   __shared__ float s_q[D];
   __shared__ float s_u[kEGroups][D];
-  __shared__ float s_score[kDecodeChunk];
-
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int chunk = blockIdx.x;
-  const int bh = blockIdx.y;               // b * Hsel + hs
+  const int tid = threadIdx.x;
   const int bi = bh / Hsel, hs = bh % Hsel;
   const int G = Hq / Hkv;
-  const int kvh = share_group ? hs : hs / G;
   const bool proj = proj_w != nullptr;
-
-  // All loads are unconditional (clamped addresses) and issued in the order
-  // they are consumed: query heads, projection rows, then summaries.
-  // 1. query heads (q_hat = their mean when the selection is shared)
-  constexpr int kGMax = 8;
+  // query heads and this thread's slice of W (rows eg*kEPG .., columns 4jq ..)
   const int gq = share_group ? G : 1;
   const int hq0 = share_group ? hs * G : hs;
   const int eq = tid % D;
@@ -81,7 +66,6 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(
     const int h = hq0 + (g < gq ? g : gq - 1);
     qv[g] = ld_f(q + (static_cast<int64_t>(bi) * Hq + h) * D + eq);
   }
-  // 2. this thread's slice of W: rows eg*kEPG .. +kEPG, columns 4j .. 4j+3
   const int jq = tid % kQuads, eg = tid / kQuads;
   float4 wq[kEPG];
   if (proj) {
@@ -89,23 +73,6 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(
     for (int i = 0; i < kEPG; ++i)
       wq[i] = reinterpret_cast<const float4*>(proj_w + static_cast<int64_t>(eg * kEPG + i) * D)[jq];
   }
-  // 3. the chunk's summaries (rows beyond the candidates are zeroed later)
-  const int cg = lane % kLPB, bl = lane / kLPB;
-  const int64_t cbase = static_cast<int64_t>(chunk) * kDecodeChunk;
-  const int64_t wbase = cbase + wave * kWave;
-  const int64_t hrow = (static_cast<int64_t>(bi) * Hkv + kvh) * ccap;
-  const char* kb = static_cast<const char*>(kbar_v) + hrow * D * kElemBytes;
-  const int64_t clast = ncand > 0 ? ncand - 1 : 0;
-  uint4 raw[kRounds];
-  float bscale[F8 ? kRounds : 1];
-#pragma unroll
-  for (int r = 0; r < kRounds; ++r) {
-    const int64_t c = wbase + r * kBPR + bl;
-    const int64_t cc = c < clast ? c : clast;
-    raw[r] = *reinterpret_cast<const uint4*>(kb + (cc * D + cg * kVec) * kElemBytes);
-    if constexpr (F8) bscale[r] = kscale[hrow + cc];
-  }
-  // 4. q_hat, then u = W^T q_hat from the row slices, summed over slices
   if (tid < D) {
     float qsum = 0.f;
 #pragma unroll
@@ -125,38 +92,112 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(
       a.w = fmaf(wq[i].w, qe, a.w);
     }
     reinterpret_cast<float4*>(s_u[eg])[jq] = a;
+    lds_barrier();
+    if (tid < D) {
+      float u = 0.f;
+#pragma unroll
+      for (int g = 0; g < kEGroups; ++g) u += s_u[g][tid];
+      s_uv[tid] = u;
+    }
+  } else if (tid < D) {
+    s_uv[tid] = s_q[tid];
   }
   lds_barrier();
-  float uc[kVec];
+}
+
+// Summary layout of the chunk scorer: a wave covers 64 candidate blocks,
+// kLPB lanes per block reading 16-byte vectors (kVec elements), kRounds load
+// rounds.
+template <typename T, int D, bool F8>
+struct ChunkLoads {
+  static constexpr int kVec = F8 ? 16 : Elem<T>::kVec;   // summary elements per 16-byte load
+  static constexpr int kElemBytes = F8 ? 1 : static_cast<int>(sizeof(T));
+  static constexpr int kLPB = D / kVec;           // lanes per block row
+  static constexpr int kBPR = kWave / kLPB;       // blocks per load round of a wave
+  static constexpr int kRounds = kWave / kBPR;    // rounds to cover the wave's 64 blocks
+  uint4 raw[kRounds];
+  float bscale[F8 ? kRounds : 1];
+
+  // Requests the chunk's summaries (unconditional: rows past the candidates
+  // read the last candidate and are masked by the callers).
+  __device__ __forceinline__ void issue(const void* __restrict__ kbar_v, const float* __restrict__ kscale,
+                                        int Hkv, int Hsel, int share_group, int G, int64_t ccap, int64_t ncand,
+                                        int chunk, int bh) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int bi = bh / Hsel, hs = bh % Hsel;
+    const int kvh = share_group ? hs : hs / G;
+    const int cg = lane % kLPB, bl = lane / kLPB;
+    const int64_t wbase = static_cast<int64_t>(chunk) * kDecodeChunk + wave * kWave;
+    const int64_t hrow = (static_cast<int64_t>(bi) * Hkv + kvh) * ccap;
+    const char* kb = static_cast<const char*>(kbar_v) + hrow * D * kElemBytes;
+    const int64_t clast = ncand > 0 ? ncand - 1 : 0;
 #pragma unroll
-  for (int i = 0; i < kVec; ++i) {
-    const int e = cg * kVec + i;
-    float u = 0.f;
-    if (proj) {
-#pragma unroll
-      for (int g = 0; g < kEGroups; ++g) u += s_u[g][e];
-    } else {
-      u = s_q[e];
+    for (int r = 0; r < kRounds; ++r) {
+      const int64_t c = wbase + r * kBPR + bl;
+      const int64_t cc = c < clast ? c : clast;
+      raw[r] = *reinterpret_cast<const uint4*>(kb + (cc * D + cg * kVec) * kElemBytes);
+      if constexpr (F8) bscale[r] = kscale[hrow + cc];
     }
-    uc[i] = u;
   }
 
-  // 4. scores of the chunk's blocks
-  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+  // Scores q.ktilde / sqrt(D) of the wave's blocks into s_score[wave * 64 ..],
+  // u from s_uv.
+  __device__ __forceinline__ void score(const float* s_uv, float* s_score) const {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int cg = lane % kLPB, bl = lane / kLPB;
+    float uc[kVec];
 #pragma unroll
-  for (int r = 0; r < kRounds; ++r) {
-    float x[kVec];
-    if constexpr (F8)
-      fp8_e4m3_unpack16(raw[r], x);
-    else
-      Elem<T>::unpack(raw[r], x);
-    float p = 0.f;
+    for (int i = 0; i < kVec; ++i) uc[i] = s_uv[cg * kVec + i];
+    const float scale = 1.0f / sqrtf(static_cast<float>(D));
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) p = fmaf(x[i], uc[i], p);
-    p = group_sum<kLPB>(p);
-    if constexpr (F8) p *= bscale[r];
-    if (cg == 0) s_score[wave * kWave + r * kBPR + bl] = p * scale;
+    for (int r = 0; r < kRounds; ++r) {
+      float x[kVec];
+      if constexpr (F8)
+        fp8_e4m3_unpack16(raw[r], x);
+      else
+        Elem<T>::unpack(raw[r], x);
+      float p = 0.f;
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) p = fmaf(x[i], uc[i], p);
+      p = group_sum<kLPB>(p);
+      if constexpr (F8) p *= bscale[r];
+      if (cg == 0) s_score[wave * kWave + r * kBPR + bl] = p * scale;
+    }
   }
+};
+
+// Scores of one chunk of 256 candidate blocks of one selection head (block
+// cbase + x in s_score[x]; blocks past the candidates get garbage, callers
+// mask them): u first (the query heads and, with a projection, W), then the
+// chunk's summaries.  Ends with the scores in LDS, not yet synchronised.
+template <typename T, int D, bool F8>
+__device__ __forceinline__ void chunk_scores(
+    const T* __restrict__ q, const void* __restrict__ kbar_v, const float* __restrict__ kscale,
+    const float* __restrict__ proj_w, int Hq, int Hkv, int Hsel, int share_group, int64_t ccap, int64_t ncand,
+    int chunk, int bh, float* s_score) {
+  __shared__ float s_uv[D];
+  form_u<T, D>(q, proj_w, Hq, Hkv, Hsel, share_group, bh, s_uv);
+  __builtin_amdgcn_sched_barrier(0);
+  ChunkLoads<T, D, F8> ld;
+  ld.issue(kbar_v, kscale, Hkv, Hsel, share_group, Hq / Hkv, ccap, ncand, chunk, bh);
+  ld.score(s_uv, s_score);
+}
+
+// One workgroup per (chunk of 256 candidate blocks, selection head).  Output:
+// the chunk's top-min(K, n) candidates in index order as 64-bit
+// (orderable score << 32 | block index) records (0 pads), and its (max, sum exp).
+template <typename T, int D, bool F8>
+__global__ __launch_bounds__(256) void decode_chunk_kernel(
+    const T* __restrict__ q, const void* __restrict__ kbar_v, const float* __restrict__ kscale,
+    const float* __restrict__ proj_w, int Hq, int Hkv, int Hsel, int share_group, int64_t ccap, int64_t ncand,
+    int K, uint64_t* __restrict__ ws_keys, float2* __restrict__ ws_ml, int nchunks) {
+  __shared__ float s_score[kDecodeChunk];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int chunk = blockIdx.x;
+  const int bh = blockIdx.y;               // b * Hsel + hs
+  const int64_t cbase = static_cast<int64_t>(chunk) * kDecodeChunk;
+  (void)tid;
+  chunk_scores<T, D, F8>(q, kbar_v, kscale, proj_w, Hq, Hkv, Hsel, share_group, ccap, ncand, chunk, bh, s_score);
   __syncthreads();
   if (wave != 0) return;
 
@@ -189,6 +230,98 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(
     out[slot] = (static_cast<uint64_t>(key[i]) << 32) | static_cast<uint32_t>(cbase + i * kWave + lane);
   });
   for (int x = kept + lane; x < K; x += kWave) out[x] = 0ull;
+  if (lane == 0) ws_ml[static_cast<int64_t>(bh) * nchunks + chunk] = make_float2(m, l);
+}
+
+// The one-call decode step's scorer.  With a projection, workgroup x = 0 of
+// each selection head forms u = W^T q_hat once and publishes it (agent-scope
+// stores, then a flag); the scoring workgroups x = 1 .. nch request their
+// chunk's summaries first and wait for the flag (a bounded wait: past it they
+// form u themselves, with the same arithmetic), so that 256 workgroups do not
+// all read W while the summaries stream in.  Without a projection every
+// scoring workgroup forms q_hat itself.  A scoring workgroup writes every
+// score of its chunk of 256 candidate blocks (-inf past the candidates), the
+// chunk's (max, sum exp) with the same arithmetic as decode_chunk_kernel, and
+// the largest score of each 64-block group (-inf for a group without
+// candidates): the K-th largest of these group maxima bounds the K-th largest
+// score from below for the selection in the attention kernel.  It also clears
+// the attention kernel's arrival counters (the kernel boundary publishes
+// them); the attention kernel clears the flags for the next call.
+constexpr int kUFlagSpin = 4096;
+
+template <typename T, int D, bool F8>
+__global__ __launch_bounds__(256) void decode_score_kernel(
+    const T* __restrict__ q, const void* __restrict__ kbar_v, const float* __restrict__ kscale,
+    const float* __restrict__ proj_w, int Hq, int Hkv, int Hsel, int share_group, int64_t ccap, int64_t ncand,
+    float* __restrict__ ws_scores, float2* __restrict__ ws_ml, float* __restrict__ ws_t2, int nchunks,
+    uint32_t* __restrict__ zero_ctr, int nzero, float* __restrict__ ws_u, uint32_t* __restrict__ uflag) {
+  __shared__ float s_score[kDecodeChunk];
+  __shared__ float s_uv[D];
+  __shared__ uint32_t s_ok;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int bh = blockIdx.y;               // b * Hsel + hs
+  const bool proj = proj_w != nullptr;
+  const int uw = proj ? 1 : 0;
+  if (proj && blockIdx.x == 0) {
+    // u of this selection head, for the head's scoring workgroups
+    form_u<T, D>(q, proj_w, Hq, Hkv, Hsel, share_group, bh, s_uv);
+    if (tid < D) publish_u32(ws_u + static_cast<int64_t>(bh) * D + tid, __float_as_uint(s_uv[tid]));
+    wait_published();
+    __syncthreads();
+    if (tid == 0) publish_u32(uflag + bh, 1u);
+    return;
+  }
+  const int chunk = blockIdx.x - uw;
+  if (chunk == 0 && bh == 0)
+    for (int x = tid; x < nzero; x += 256) zero_ctr[x] = 0u;
+  const int64_t cbase = static_cast<int64_t>(chunk) * kDecodeChunk;
+  ChunkLoads<T, D, F8> ld;
+  ld.issue(kbar_v, kscale, Hkv, Hsel, share_group, Hq / Hkv, ccap, ncand, chunk, bh);
+  if (proj) {
+    if (tid == 0) {
+      uint32_t f = 0u;
+      for (int it = 0; it < kUFlagSpin; ++it) {
+        f = __hip_atomic_load(uflag + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (f != 0u) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      s_ok = f;
+    }
+    __syncthreads();
+    if (s_ok != 0u) {
+      if (tid < D) s_uv[tid] = acquire_f32(ws_u + static_cast<int64_t>(bh) * D + tid);
+      lds_barrier();
+    } else {
+      form_u<T, D>(q, proj_w, Hq, Hkv, Hsel, share_group, bh, s_uv);
+    }
+  } else {
+    form_u<T, D>(q, proj_w, Hq, Hkv, Hsel, share_group, bh, s_uv);
+  }
+  ld.score(s_uv, s_score);
+  __syncthreads();
+  const int nvalid = static_cast<int>(ncand - cbase < kDecodeChunk ? ncand - cbase : kDecodeChunk);
+  // every thread: one score (its 64-block group is its wave)
+  const bool ok = tid < nvalid;
+  const float sv = ok ? s_score[tid] : -INFINITY;
+  ws_scores[(static_cast<int64_t>(bh) * nchunks + chunk) * kDecodeChunk + tid] = sv;
+  const float gmax = wave_max(sv);
+  if (lane == 0) ws_t2[(static_cast<int64_t>(bh) * nchunks + chunk) * 4 + wave] = gmax;
+  if (wave != 0) return;
+  // wave 0: the chunk's (max, sum exp), as decode_chunk_kernel forms it
+  float sc[4];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pidx = i * kWave + lane;
+    sc[i] = s_score[pidx];
+    if (pidx < nvalid) mloc = fmaxf(mloc, sc[i]);
+  }
+  const float m = wave_max(mloc);
+  float lloc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i * kWave + lane < nvalid) lloc += __expf(sc[i] - m);
+  const float l = m == -INFINITY ? 0.f : wave_sum(lloc);
   if (lane == 0) ws_ml[static_cast<int64_t>(bh) * nchunks + chunk] = make_float2(m, l);
 }
 
@@ -389,7 +522,23 @@ static hipError_t launch_chunks_t(const SelectLaunch& p, void* ws, hipStream_t s
 bool decode_select_path(const SelectLaunch& p) { return use_decode_path(p); }
 
 bool decode_fusable(const SelectLaunch& p) {
-  return use_decode_path(p) && p.dtype == kDtypeBf16 && merge_nv(p) <= kFusedMergeMaxNV;
+  return use_decode_path(p) && p.dtype == kDtypeBf16 && p.K <= kStepMaxK &&
+         static_cast<int64_t>(p.B) * p.Hsel <= kStepMaxHeads &&
+         decode_num_chunks(p.max_cand > 0 ? p.max_cand : 1) <= kStepMaxChunks;
+}
+
+template <typename T, int D>
+static hipError_t launch_step_scores_t(const SelectLaunch& p, const DecodeStepWs& w, hipStream_t st) {
+  auto kern = p.kbar_scale != nullptr ? decode_score_kernel<T, D, true> : decode_score_kernel<T, D, false>;
+  const unsigned gx = static_cast<unsigned>(w.nch + (p.proj_w != nullptr ? 1 : 0));
+  return launch(false, kern, dim3(gx, static_cast<unsigned>(p.B * p.Hsel)), dim3(256), st,
+                static_cast<const T*>(p.q), p.kbar, p.kbar_scale, p.proj_w, p.Hq, p.Hkv, p.Hsel, p.share_group,
+                p.ccap, p.max_cand, w.scores, w.ml, w.t2, w.nch, w.ctr, static_cast<int>(p.B * p.Hsel), w.u,
+                w.uflag);
+}
+
+hipError_t launch_decode_step_scores(const SelectLaunch& p, const DecodeStepWs& w, hipStream_t st) {
+  return p.d == 64 ? launch_step_scores_t<bf16_t, 64>(p, w, st) : launch_step_scores_t<bf16_t, 128>(p, w, st);
 }
 
 int decode_merge_nv(const SelectLaunch& p) { return merge_nv(p); }

@@ -251,6 +251,32 @@ __device__ __forceinline__ float xor_lanes_f(float v) {
   return __uint_as_float(xor_lanes<M>(__float_as_uint(v)));
 }
 
+// One compare-exchange stage of a bitonic network over the wave's lanes:
+// lane pairs (l, l ^ J); the lower lane keeps the larger key when desc.
+template <int J>
+__device__ __forceinline__ uint32_t bitonic_cx_u32(uint32_t key, bool desc, int lane) {
+  const uint32_t other = xor_lanes<J>(key);
+  const bool lower = (lane & J) == 0;
+  const uint32_t hi = key > other ? key : other;
+  const uint32_t lo = key > other ? other : key;
+  return (lower == desc) ? hi : lo;
+}
+
+// Sort one 32-bit key per lane across the wave, descending (lane 0 =
+// largest), with DPP / permlane exchanges only.
+__device__ __forceinline__ uint32_t wave_sort_desc_u32(uint32_t key) {
+  const int lane = static_cast<int>(__lane_id());
+#define SPA_CX(K, J) key = bitonic_cx_u32<J>(key, (lane & (K)) == 0, lane)
+  SPA_CX(2, 1);
+  SPA_CX(4, 2); SPA_CX(4, 1);
+  SPA_CX(8, 4); SPA_CX(8, 2); SPA_CX(8, 1);
+  SPA_CX(16, 8); SPA_CX(16, 4); SPA_CX(16, 2); SPA_CX(16, 1);
+  SPA_CX(32, 16); SPA_CX(32, 8); SPA_CX(32, 4); SPA_CX(32, 2); SPA_CX(32, 1);
+  SPA_CX(64, 32); SPA_CX(64, 16); SPA_CX(64, 8); SPA_CX(64, 4); SPA_CX(64, 2); SPA_CX(64, 1);
+#undef SPA_CX
+  return key;
+}
+
 // ----------------------------------------------------------- wave reductions
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, xor_lanes_f<32>(v));
@@ -293,6 +319,46 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ------------------------------------------- hand-off between workgroups
+// Agent-scope relaxed atomic stores and loads are write-through / coherent
+// accesses (sc1): a value stored this way is visible to every XCD once the
+// store completes, and a load this way never returns a stale L2 copy.  A
+// workgroup publishes its results with publish_* , waits for them to
+// complete (wait_published), and only then counts itself done with an
+// agent-scope atomic; the workgroup that sees the last count reads the
+// results with acquire_* loads.  This is the release / acquire pattern
+// without the L2 write-back (buffer_wbl2) and invalidation a fence would do,
+// valid because every value handed over travels through these accesses.
+__device__ __forceinline__ void publish_u64(void* p, uint64_t v) {
+  __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void publish_u32(void* p, uint32_t v) {
+  __hip_atomic_store(static_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void publish_f2(void* p, float a, float b) {
+  publish_u64(p, (static_cast<uint64_t>(__float_as_uint(b)) << 32) | __float_as_uint(a));
+}
+__device__ __forceinline__ uint64_t acquire_u64(const void* p) {
+  return __hip_atomic_load(static_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 acquire_f2(const void* p) {
+  const uint64_t u = acquire_u64(p);
+  return make_float2(__uint_as_float(static_cast<uint32_t>(u)), __uint_as_float(static_cast<uint32_t>(u >> 32)));
+}
+__device__ __forceinline__ float acquire_f32(const void* p) {
+  return __uint_as_float(
+      __hip_atomic_load(static_cast<const uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+// Wait until this thread's stores (and loads) have completed.
+__device__ __forceinline__ void wait_published() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ uint32_t count_arrival(uint32_t* ctr) {
+  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Number of set bits of a wave-uniform mask held by lanes below this one.

@@ -167,16 +167,61 @@ inline DecodeSelectWs decode_select_ws(const SelectLaunch& p, void* ws) {
                         static_cast<int>(nch), kbytes + align256(heads * nch * sizeof(float2))};
 }
 
+// The one-call decode step (bf16): a scorer kernel writes every candidate's
+// score, each chunk's (max, sum exp) and each 64-block group's largest score;
+// the attention kernel selects from them, attends and combines.  Workspace:
+// the ready flags of u [kStepMaxHeads] u32 at offset 0 (every call leaves
+// them zero: the attention kernel clears the ones the scorer set), scores
+// [heads, nch * 256] fp32, ml [heads, nch] float2, group maxima t2
+// [heads, nch * 4] fp32, u = W^T q_hat [heads, d] fp32, then the split-K
+// partials and one arrival counter per selection head
+// (decode_step_workspace_bytes).
+constexpr int kStepMaxChunks = 64;   // candidates per row <= 16384
+constexpr int kStepMaxK = 64;
+constexpr int kStepMaxHeads = 4096;  // batch x selection heads
+constexpr size_t kStepFlagBytes = kStepMaxHeads * sizeof(uint32_t);   // 256-aligned
+struct DecodeStepWs {
+  float* scores;
+  float2* ml;
+  float* t2;
+  float* u;
+  uint32_t* uflag;
+  uint32_t* ctr;
+  int nch;
+  size_t sel_bytes;   // bytes of the flags, scores, ml, t2 and u
+};
+inline DecodeStepWs decode_step_ws(const SelectLaunch& p, void* ws_sel, void* ctr) {
+  const int64_t nch = decode_num_chunks(p.max_cand > 0 ? p.max_cand : 1);
+  const size_t heads = static_cast<size_t>(p.B) * p.Hsel;
+  const size_t fb = kStepFlagBytes;
+  const size_t sb = align256(heads * nch * 256 * sizeof(float));
+  const size_t mb = align256(heads * nch * sizeof(float2));
+  const size_t tb = align256(heads * nch * 4 * sizeof(float));
+  const size_t ub = align256(heads * p.d * sizeof(float));
+  char* base = static_cast<char*>(ws_sel);
+  return DecodeStepWs{reinterpret_cast<float*>(base + fb), reinterpret_cast<float2*>(base + fb + sb),
+                      reinterpret_cast<float*>(base + fb + sb + mb), reinterpret_cast<float*>(base + fb + sb + mb + tb),
+                      reinterpret_cast<uint32_t*>(base), static_cast<uint32_t*>(ctr), static_cast<int>(nch),
+                      fb + sb + mb + tb + ub};
+}
+hipError_t launch_decode_step_scores(const SelectLaunch& p, const DecodeStepWs& w, hipStream_t st);
+size_t decode_step_select_bytes(const SelectLaunch& p);
+
+// 64-key tiles per kept block of the decode attention (blocks of b <= 64 keys
+// are one tile).
+inline int decode_step_tpu(const AttnLaunch& p) { return p.b > 64 ? p.b / 64 : 1; }
+
 // Element type codes of the launch structs (the C ABI's spa_dtype values).
 constexpr int kDtypeF32 = 0, kDtypeBf16 = 1;
 
-// Largest records-per-lane of a merge wave the fused decode kernel is built for.
-constexpr int kFusedMergeMaxNV = 8;
 
 
 size_t select_workspace_bytes(const SelectLaunch& p);
 size_t select_bwd_workspace_bytes(const SelectLaunch& p);
 size_t attn_fwd_workspace_bytes(const AttnLaunch& p);
+// attention part of the one-call decode step's workspace: the split-K
+// partials (as attn_fwd) plus one arrival counter per selection head
+size_t decode_step_workspace_bytes(const AttnLaunch& p);
 size_t attn_bwd_workspace_bytes(const BwdLaunch& p);
 
 hipError_t launch_block_summaries(const SummaryLaunch& p, hipStream_t st);
@@ -216,5 +261,10 @@ bool attn_tile_bwd_supported(const BwdLaunch& p);
 size_t attn_tile_bwd_bitmap_bytes(const BwdLaunch& p);
 hipError_t launch_attn_tile_bwd(const BwdLaunch& p, const float* Dbuf, uint32_t* bits, hipStream_t st);
 hipError_t launch_zero_fill(void* ptr, size_t bytes, hipStream_t st);
+
+// probe.hip: dependent-load chain over next[0 .. mask] (one lane), final
+// index to out[0].
+hipError_t launch_load_chase(const uint32_t* next, uint32_t mask, int steps, uint32_t start, uint32_t* out,
+                             hipStream_t st);
 
 }  // namespace spa

@@ -32,7 +32,8 @@ EXPORTED = ["sparse_abi_version", "sparse_last_error", "spa_abi_version", "spa_p
             "sparse_block_summaries_paged", "sparse_decode_step_paged", "sparse_retain_cells",
             "sparse_score_select_subset", "sparse_forest_nodes", "sparse_forest_workspace_bytes",
             "sparse_forest_build", "sparse_forest_select", "sparse_quantize_summaries_fp8",
-            "sparse_dequantize_summaries_fp8", "sparse_workspace_bytes", "sparse_workspace_init"]
+            "sparse_dequantize_summaries_fp8", "sparse_workspace_bytes", "sparse_workspace_init",
+            "sparse_probe_load_chase"]
 
 _vp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
 ABI_VERSION = 2               # layout of the argument structs below
@@ -136,6 +137,8 @@ def lib():
         L.sparse_workspace_bytes.argtypes = [_i, _vp]
         L.sparse_workspace_init.restype = _i
         L.sparse_workspace_init.argtypes = [_vp, _sz, _vp]
+        L.sparse_probe_load_chase.restype = _i
+        L.sparse_probe_load_chase.argtypes = [_vp, _i64, _i, ctypes.c_uint32, _vp, _vp]
         if L.sparse_abi_version() != ABI_VERSION:
             raise RuntimeError(f"{LIB_PATH} has ABI version {L.sparse_abi_version()}, this binding needs "
                                f"{ABI_VERSION}: rebuild it with __graft_entry__.build()")
@@ -172,20 +175,28 @@ def _contig(*ts):
             raise ValueError("tensors passed to libsparse_attn must be contiguous")
 
 
+SPA_DECODE_FLAG_BYTES = 16384     # the decode step's ready flags at the workspace's start
+
+
 class Workspace:
     """A zero-initialised device buffer reused across calls (grown on demand).
-    Calls that share one Workspace must not overlap in time."""
+    Calls that share one Workspace must not overlap in time.  A decode step
+    after another entry point's call clears the step's flag block first."""
 
     def __init__(self, device="cuda"):
         self.device = device
         self.buf = None
+        self.last_op = None
 
-    def get(self, nbytes):
+    def get(self, nbytes, op=None):
         if nbytes == 0:
             return None, 0
         if self.buf is None or self.buf.numel() < nbytes:
             n = (nbytes + 255) // 256 * 256
             self.buf = torch.zeros(n, dtype=torch.uint8, device=self.device)
+        elif op == SPA_OP_DECODE_STEP and self.last_op not in (None, SPA_OP_DECODE_STEP):
+            self.buf[:min(SPA_DECODE_FLAG_BYTES, self.buf.numel())].zero_()
+        self.last_op = 0 if op is None else op
         return self.buf, self.buf.numel()
 
 
@@ -199,7 +210,7 @@ def _ws(workspace, op, args, device):
     if workspace is None:
         key = (str(device), op)
         workspace = _default_ws.setdefault(key, Workspace(device))
-    buf, size = workspace.get(need)
+    buf, size = workspace.get(need, op)
     return buf, size
 
 
@@ -492,3 +503,15 @@ def sparse_forest_select(q, kbar, max_norm, centre, k, forest, n, *, stream=None
     fo = Forest(**{key: _p(v) for key, v in forest.items()})
     _check(lib().sparse_forest_select(ctypes.byref(a), _p(k), k.shape[2], ctypes.byref(fo), n, _stream(stream)))
     return idx, k_eff
+
+
+def sparse_probe_load_chase(next_idx, steps, start=0, out=None, stream=None):
+    """Measurement aid: one lane follows the cyclic index list next_idx (int32
+    on the device, length a power of two) for `steps` dependent loads; time
+    the call with events for the memory level's round-trip latency.  Returns
+    out (one int32: the last index)."""
+    if out is None:
+        out = torch.empty(1, dtype=torch.int32, device=next_idx.device)
+    _check(lib().sparse_probe_load_chase(_p(next_idx), next_idx.numel(), steps, start, _p(out), _stream(stream)))
+    return out
+

@@ -270,15 +270,24 @@ typedef struct spa_decode_args {
  * sparse_decode_step -- one decode step of the hot path: sparse_score_select
  * then sparse_attn_fwd on its selection ("SAS" review Alg. 1 then §4.3 Eq. 9
  * for one new token; "Monodratic" news page: local block plus exact softmax
- * on the selected blocks).  Same outputs, bit for bit, as the two calls made
- * in sequence: idx, logg, k_eff of `select`, o and lse of `attn`.  For bf16
- * with the chunked selection (up to 512 chunk winners per merge wave) the
- * top-K merge runs inside the attention workgroups, which saves one dependent
- * kernel per step; otherwise the two calls' kernels run in sequence.  Needs
- * a workspace of sparse_workspace_bytes(SPA_OP_DECODE_STEP, spa_decode_args*);
- * caller-owned, contents on entry ignored.  Errors: as the two calls, plus
+ * on the selected blocks).  Outputs: idx, logg, k_eff of `select`, o and
+ * lse of `attn`, as the two calls made in sequence give them (the same
+ * selection; o and lse to fp32 rounding).  With bf16 (or fp8) summaries,
+ * B * Hsel <= 4096, K <= 64 and at most 16384 candidates per row, the step
+ * takes two kernels: the scorer, then one workgroup per (selection head,
+ * kept tile) that selects the head's top-K from the scores, attends to its
+ * tile and publishes a split-K partial, the head's last workgroup combining
+ * them; otherwise the two calls' kernels run in sequence.  Needs a workspace
+ * of sparse_workspace_bytes(SPA_OP_DECODE_STEP, spa_decode_args*),
+ * caller-owned.  Its first SPA_DECODE_FLAG_BYTES bytes hold per-head ready
+ * flags that must read zero on the first decode step with that workspace (a
+ * zero-filled allocation, or sparse_workspace_init); every decode step leaves
+ * them zero again, but other entry points given the same workspace may not,
+ * so clear them before going back to decode steps.  The rest of the
+ * workspace's contents on entry are ignored.  Errors: as the two calls, plus
  * SPA_ERR_INVALID_ARG when select and attn disagree.
  */
+#define SPA_DECODE_FLAG_BYTES 16384u
 spa_status sparse_decode_step(const spa_decode_args *a, void *workspace, size_t ws_bytes,
                        spa_stream_t stream);
 
@@ -297,8 +306,10 @@ spa_status sparse_decode_step(const spa_decode_args *a, void *workspace, size_t 
  *    (hipGetSymbolAddress with the device current): make it outside graph
  *    capture.
  *  - Every call on one GPU shares that GPU's array, which keeps the last
- *    call's contents (the step needs no zeroed scratch): calls that overlap
- *    in time on one GPU, on any streams, race.  Serialise them.
+ *    call's contents: the array starts zero when the library loads and each
+ *    call leaves its ready flags (the first SPA_DECODE_FLAG_BYTES bytes) zero
+ *    again, as the next call needs them.  Calls that overlap in time on one
+ *    GPU, on any streams, race.  Serialise them.
  */
 #define SPA_NOALLOC_SCRATCH_BYTES (8u << 20)
 spa_status sparse_decode_step_noalloc(const spa_decode_args *a, spa_stream_t stream);
@@ -488,6 +499,17 @@ size_t sparse_workspace_bytes(int op, const void *args);
  * required by any entry point; provided for callers that want deterministic
  * scratch contents. */
 spa_status sparse_workspace_init(void *workspace, size_t ws_bytes, spa_stream_t stream);
+
+/* Measurement aid, not part of the attention path: one lane follows the
+ * cyclic index list `next` (device, n uint32 entries, n a power of two in
+ * [1, 2^32]) for `steps` >= 1 dependent loads from `start`, each index masked
+ * to n - 1 (any contents stay in bounds), and writes the last index to out[0]
+ * (device).  Timed with events on `stream`, the launch gives the round-trip
+ * latency of the memory level the list occupies: a decode step is a short
+ * chain of such round trips.  The caller owns both buffers.  Bad arguments
+ * return SPA_ERR_INVALID_ARG. */
+spa_status sparse_probe_load_chase(const uint32_t *next, int64_t n, int steps, uint32_t start, uint32_t *out,
+                                   spa_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -194,7 +194,14 @@ def test_decode_step_validation_and_workspace():
     need = lib.sparse_workspace_bytes(ops.SPA_OP_DECODE_STEP, ctypes.byref(da))
     need_sel = lib.sparse_workspace_bytes(ops.SPA_OP_SCORE_SELECT, ctypes.byref(sel))
     need_att = lib.sparse_workspace_bytes(ops.SPA_OP_ATTN_FWD, ctypes.byref(att))
-    assert need == 256 * ((need_sel + 255) // 256) + need_att
+    # the one-call scorer's ready flags (4096 u32 at offset 0), scores
+    # [8 heads, 2 chunks, 256] fp32, chunk (max, sum exp), group maxima and u
+    # [8, 128] fp32 (larger than the two-call records), then split-K partials
+    # and one arrival counter per selection head
+    r256 = lambda x: 256 * ((x + 255) // 256)
+    scorer = 4096 * 4 + r256(8 * 2 * 256 * 4) + r256(8 * 2 * 8) + r256(8 * 2 * 4 * 4) + r256(8 * 128 * 4)
+    assert scorer > need_sel
+    assert need == scorer + need_att + 256
     assert lib.sparse_decode_step(ctypes.byref(da), FAKE, need - 1, None) == ops.SPA_ERR_WORKSPACE
 
     def status(s, a):
@@ -265,3 +272,28 @@ def test_fp8_quantize_and_dequantize_reject_invalid_arguments():
     assert dq(None, FAKE, 4, 128, FAKE, None) == ops.SPA_ERR_INVALID_ARG
     assert dq(FAKE, FAKE, -1, 128, FAKE, None) == ops.SPA_ERR_INVALID_ARG
     assert dq(FAKE, FAKE, 0, 128, FAKE, None) == ops.SPA_OK
+
+
+def test_load_chase_probe_rejects_invalid_arguments():
+    lib = ops.lib()
+    out = FAKE
+    for n, steps in ((3, 10), (0, 10), (1 << 33, 10), (1024, 0)):
+        assert lib.sparse_probe_load_chase(FAKE, n, steps, 0, out, None) == -1, (n, steps)
+        assert b"sparse_probe_load_chase" in lib.sparse_last_error() or b"n =" in lib.sparse_last_error() \
+            or b"steps" in lib.sparse_last_error()
+    assert lib.sparse_probe_load_chase(None, 1024, 10, 0, out, None) == -1
+
+
+def test_workspace_clears_the_decode_flags_after_other_calls():
+    """A Workspace handed to another entry point and then to a decode step
+    has the step's flag block zeroed first (host buffer, no GPU)."""
+    ws = ops.Workspace(device="cpu")
+    buf, _ = ws.get(1 << 16, ops.SPA_OP_SCORE_SELECT)
+    buf.fill_(7)
+    buf, _ = ws.get(1 << 16, ops.SPA_OP_DECODE_STEP)
+    assert int(buf[:ops.SPA_DECODE_FLAG_BYTES].sum()) == 0
+    assert int(buf[ops.SPA_DECODE_FLAG_BYTES]) == 7          # the rest is left as it is
+    buf[:ops.SPA_DECODE_FLAG_BYTES].fill_(3)                 # decode steps keep it (they restore it)
+    buf, _ = ws.get(1 << 16, ops.SPA_OP_DECODE_STEP)
+    assert int(buf[0]) == 3
+    assert ops.SPA_DECODE_FLAG_BYTES == 16384

@@ -614,6 +614,44 @@ def test_one_workspace_shared_across_shapes_and_entry_points():
         assert rel_err(host(o), o_o) <= _tol(cfg), (name, over)
 
 
+def test_decode_step_workspace_alternating_paths():
+    """One workspace serves one-call decode steps on the fused path (bf16, a
+    projection, u formed once per head and handed over through a flag block
+    at the workspace's start) and on the two-call path (fp32) in turn, with
+    different shapes and queries: neither path may disturb the other's state
+    (every step checked against the oracle).  Between steps a plain selection
+    call writes its own scratch over the same workspace's start, which the
+    binding clears before the next step."""
+    ws = ops.Workspace()
+    cases = [("decode_512k", dict(n=65536, seed=61)), ("tiny_decode", dict(t=40, seed=62)),
+             ("decode_512k", dict(n=131072, seed=63)), ("decode_32k", dict(d=64, dtype="f32", n=4096, Hq=8, Hkv=4,
+                                                                         proj=True, seed=64)),
+             ("decode_512k", dict(n=65536, seed=65)), ("decode_32k", dict(n=4096, seed=66))]
+    for name, over in cases:
+        cfg = config(name, **over)
+        _say(f"[decode alternating paths] {name} {over}")
+        x = make_inputs(cfg)
+        b, K, pos, gate, sg = cfg["b"], cfg["K"], x["q_pos0"], cfg["gate"], cfg["share_group"]
+        proj = x.get("proj_w")
+        nblk = x["L"] // b
+        kw = dict(Hkv=cfg["Hkv"], b=b, K=K, q_pos0=pos, gate=gate, share_group=sg)
+        kb_o, mx_o, ce_o = oracle.block_summaries(x["k"], b, nblocks=nblk)
+        ora = oracle.score_select(x["q"], kb_o, mx_o, ce_o, proj_w=proj, **kw)
+        kd, vd, qd = dev(x["k"]), dev(x["v"]), dev(x["q"])
+        kb, mx, ce = ops.sparse_block_summaries(kd, b)
+        idx, logg, keff, o, lse = ops.sparse_decode_step(qd, kb, mx, ce, kd, vd, workspace=ws,
+                                                         proj_w=None if proj is None else dev(proj), **kw)
+        torch.cuda.synchronize()
+        ex = check_indices(host(idx), ora, lambda p: oracle.scores_one_row(
+            x["q"], kb_o, mx_o, ce_o, Hkv=cfg["Hkv"], b=b, q_pos0=pos, bidx=p[0], hs=p[1], row=p[2],
+            share_group=sg, proj_w=proj))
+        o_o, _ = oracle.attn_fwd(x["q"], x["k"], x["v"], ex.idx, ex.logg if gate else None, b=b, K=K, q_pos0=pos,
+                                 share_group=sg)
+        assert rel_err(host(o), o_o) <= _tol(cfg), (name, over)
+        ops.sparse_score_select(qd, kb, mx, ce, workspace=ws, proj_w=None if proj is None else dev(proj), **kw)
+        torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ selection alone (row kernels)
 def _select_only(cfg, x, *, gate, share_group, erf=True, prefix_mode=1, rows=None, centre_shift=None):
     b, qb, K = cfg["b"], cfg.get("qblock", 128), cfg["K"]
