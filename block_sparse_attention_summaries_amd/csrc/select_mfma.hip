@@ -11,7 +11,8 @@
 // Per tile of 32 candidates, S^T = Kbar Q^T (candidates x queries) gives each
 // lane one query row and 16 candidates, so every lane keeps its row's running
 // top list and gate (max, sum exp) in registers; the two half-waves of a row
-// merge at the end.
+// merge at the end.  The MFMA accumulates onto the bias, so a score costs no
+// arithmetic after it: scores run in units of 1/scale until the walk ends.
 //
 // Group selection scores with the mean query of the G heads, which is not a
 // bf16 value: it is formed in fp32 and split into three bf16 terms
@@ -20,8 +21,11 @@
 //
 // erf term: the bias reaches ~10, where fp32 cannot rank to 1e-6.  The scan
 // ranks fp32 scores (a branch-free erf approximation, read from a per-
-// workgroup table of row - cell b when the centres are the cell middles) in a
-// list twice the budget long.  At the end, list entries within twice a proven
+// workgroup table of row - cell b when the centres are the cell middles; a
+// tile whose every (row, cell) pair lies where the table is 1 skips it) in a
+// list twice the budget long, admitting only scores within the largest
+// possible band of the lane's running K-th best.  At the end, list entries
+// within twice a proven
 // error bound of the fp32 K-th best are re-scored exactly (fp64 dot product
 // and bias) and the exact top-K is taken from them; with the gate off, a row
 // whose (K+1)-th entry lies below that band keeps its first K entries as they
@@ -103,6 +107,7 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
   __shared__ float s_sc[4][16][64];       // per wave: candidate slot r x lane
   __shared__ double s_x[4][64];           // per wave: half-row dot products
   __shared__ float s_erf[kErf ? kErfTab : 1];   // filter erf by row - cell b (see below)
+  __shared__ float s_jl[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, ql = lane & 31;
@@ -129,6 +134,7 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
   double lam = 0.0, inv2sig = 0.0;
   float lam32 = 0.f, inv2sig32 = 0.f;
   bool use_tab = false;
+  int jsat = 0x7FFFFFFF;
   if constexpr (kErf) {
     lam = static_cast<double>(erf_lambda[hs]);
     lam32 = erf_lambda[hs];
@@ -148,10 +154,19 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
     ok &= static_cast<int64_t>(wg_cand) * b < (1 << 23) && q_pos0 + nq < (1 << 23) ? 1 : 0;
     use_tab = __builtin_amdgcn_readfirstlane(__syncthreads_and(ok)) != 0;
     if (use_tab) {
+      // jsat: every entry from jsat on (and every j past the table) is 1
+      float jl = -1.f;
       for (int j = tid; j < kErfTab; j += 256) {
         const float x32 = (static_cast<float>(j) - hb) * inv2sig32;
-        s_erf[j] = x32 < 4.0f ? erf_filter(x32) : 1.0f;
+        float e = 1.0f;
+        if (x32 < 4.0f) e = erf_filter(x32);
+        s_erf[j] = e;
+        if (e != 1.0f) jl = static_cast<float>(j);
       }
+      jl = wave_max(jl);
+      if (lane == 0) s_jl[wave] = jl;
+      __syncthreads();
+      jsat = static_cast<int>(fmaxf(fmaxf(s_jl[0], s_jl[1]), fmaxf(s_jl[2], s_jl[3]))) + 1;
     }
   }
 
@@ -210,20 +225,28 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
   }
   if constexpr (kErf) qsq += xor_lanes_f<32>(qsq);
 
-  float ls[KL];                           // fp32 scores, best first
+  // The walk runs in units of 1/scale (the MFMA's own q.kbar, the bias
+  // staged as lambda a_c / scale); list scores and the gate's max take the
+  // scale once it ends.
+  const float inv_scale = sqrtf(static_cast<float>(D));
+  const float lam_s = lam32 * inv_scale;
+  const float k2 = scale * 1.4426950408889634f;     // exp(x scale) = exp2(x k2)
+  float ls[KL];                           // scores (1/scale units), best first
   int li[KL];
-#pragma unroll
-  for (int t = 0; t < KL; ++t) {
-    ls[t] = -INFINITY;
-    li[t] = 0x7FFFFFFF;
-  }
   float m_run = -INFINITY, l_run = 0.f;   // gate LSE over this lane's candidates
   float amax_t = 0.f;                     // lanes 0..31: largest max norm staged
 
+  // Tiles before ncand_min hold valid candidates for every row of the wave;
+  // a tile whose candidates all lie jsat or more before the wave's first row
+  // has erf = 1 for every score (its bias is the accumulator's initial value).
+  const int64_t row0 = static_cast<int64_t>(rt * 4 + wave) * 32;
+  const bool rows_all_ok = __ballot(!row_ok) == 0ull;
+  const int64_t ncand_min = rows_all_ok ? num_candidates(q_pos0 + row0, b, prefix_mode, qblock) : 0;
+
   // Each wave runs on its own (no workgroup barrier in the walk): the lane's
   // A operand (candidate c0 + ql, columns 16 ks + 8 hl .. +7) comes straight
-  // from memory, one tile ahead; lanes 0..31 stage the tile's lambda a_c (and
-  // centres) in the wave's LDS slice.
+  // from memory, one tile ahead; lanes 0..31 stage the tile's lambda a_c / scale
+  // (and centres) in the wave's LDS slice.
   uint4 ka[kKS];
   float pre_a = 0.f, pre_p = 0.f;
 #define SPA_FETCH_TILE(C0)                                                                    \
@@ -237,103 +260,151 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
       pre_p = centre[c];                                                                      \
     }                                                                                         \
   } while (0)
-  if (wave_cand > 0) SPA_FETCH_TILE(0);
 
-  for (int64_t c0 = 0; c0 < wave_cand; c0 += kT) {
-    if constexpr (kErf) {
-      wave_lds_sync();                    // the previous tile's readers are done
-      if (hl == 0) {
-        s_beta32[wave][ql] = lam32 * pre_a;
-        s_p[wave][ql] = pre_p;
-        amax_t = fmaxf(amax_t, fabsf(pre_a));
+#pragma unroll
+  for (int t = 0; t < KL; ++t) {
+    ls[t] = -INFINITY;
+    li[t] = 0x7FFFFFFF;
+  }
+  // erf path: the list only has to hold every score within the final error
+  // band of the row's K-th best (and flag a rescan when it may not).  The
+  // band is at most twice err_max, the error bound below evaluated with
+  // |score| <= |q| a_max / sqrt(d) + |lambda| a_max over the wave's largest
+  // max norm a_max, so a score under the lane's current K-th best minus that
+  // can be left out; 1/scale units, with 25 % to spare.
+  float band = INFINITY;
+  if constexpr (kErf) {
+    float am = 0.f;
+    for (int64_t c = lane; c < wave_cand; c += 64) am = fmaxf(am, fabsf(mn[c]));
+    am = wave_max(am);
+    const float qn = sqrtf(qsq);
+    const float sb = qn * am * scale + fabsf(lam32) * am;
+    const float err_max = 5e-6f * (1.f + sb) + 2.5e-5f * fabsf(lam32) * am +
+                          4.f * static_cast<float>(D * NTERM + 2) * 5.97e-8f * qn * am * scale;
+    band = 2.5f * err_max * inv_scale;
+  }
+  {
+    if (wave_cand > 0) SPA_FETCH_TILE(0);
+    for (int64_t c0 = 0; c0 < wave_cand; c0 += kT) {
+      if constexpr (kErf) {
+        wave_lds_sync();                  // the previous tile's readers are done
+        if (hl == 0) {
+          s_beta32[wave][ql] = lam_s * pre_a;
+          s_p[wave][ql] = pre_p;
+          amax_t = fmaxf(amax_t, fabsf(pre_a));
+        }
+        wave_lds_sync();
       }
-      wave_lds_sync();
-    }
-    sfloatx16_t st;
+      // register r holds candidate c0 + 8 (r / 4) + 4 hl + (r % 4) of this
+      // lane's row.  The accumulator starts at the bias: lambda a_c / scale
+      // (four 16-byte reads), times the filter erf unless the tile is
+      // saturated; the MFMA adds q.kbar.
+      const bool sat = kErf && use_tab && q_pos0 + row0 - (c0 + kT - 1) * b >= jsat;
+      sfloatx16_t st;
+      if constexpr (kErf) {
+        float4 bet[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st[r] = 0.f;
+        for (int q4 = 0; q4 < 4; ++q4)
+          bet[q4] = *reinterpret_cast<const float4*>(&s_beta32[wave][8 * q4 + 4 * hl]);
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
+        for (int q4 = 0; q4 < 4; ++q4) {
+          st[4 * q4] = bet[q4].x;
+          st[4 * q4 + 1] = bet[q4].y;
+          st[4 * q4 + 2] = bet[q4].z;
+          st[4 * q4 + 3] = bet[q4].w;
+        }
+        if (!sat) {
+          const int jb = static_cast<int>(pos - (c0 + 4 * hl) * b);   // j of candidate m = 4 hl
+          if (use_tab) {
 #pragma unroll
-      for (int t = 0; t < NTERM; ++t)
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sel_bf16x8(ka[ks]), sel_bf16x8(qt[t][ks]), st, 0, 0, 0);
-    }
-    if (c0 + kT < wave_cand) SPA_FETCH_TILE(c0 + kT);
-
-    // register r holds candidate c0 + 8 (r / 4) + 4 hl + (r % 4) of this lane's
-    // row.  Pass 1 (unrolled): scores, gate terms and the admission mask
-    // against the tile-start list end; pass 2 walks the admitted slots only.
-    float sv[16];
-    uint32_t mask = 0;
-    const float thr = ls[KL - 1];
-    // erf bias terms of the lane's 16 candidates, their loads issued together:
-    // m = 8 (r / 4) + 4 hl + (r % 4), so lambda a_c comes as four 16-byte reads
-    float e32[16];
-    float4 bet[4];
-    if constexpr (kErf) {
-      const int jb = static_cast<int>(pos - (c0 + 4 * hl) * b);   // j of candidate m = 4 hl
-      if (use_tab) {
+            for (int r = 0; r < 16; ++r) {
+              const int j = jb - (8 * (r >> 2) + (r & 3)) * b;
+              st[r] *= s_erf[j < 0 ? 0 : (j < kErfTab ? j : kErfTab - 1)];
+            }
+          } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = jb - (8 * (r >> 2) + (r & 3)) * b;
-          e32[r] = s_erf[j < 0 ? 0 : (j < kErfTab ? j : kErfTab - 1)];
+            for (int r = 0; r < 16; ++r) {
+              const float x32 =
+                  (static_cast<float>(pos) - s_p[wave][8 * (r >> 2) + 4 * hl + (r & 3)]) * inv2sig32;
+              st[r] *= x32 < 4.0f ? erf_filter(x32) : 1.0f;
+            }
+          }
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x32 = (static_cast<float>(pos) - s_p[wave][8 * (r >> 2) + 4 * hl + (r & 3)]) * inv2sig32;
-          e32[r] = x32 < 4.0f ? erf_filter(x32) : 1.0f;
+        for (int r = 0; r < 16; ++r) st[r] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+#pragma unroll
+        for (int t = 0; t < NTERM; ++t)
+          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sel_bf16x8(ka[ks]), sel_bf16x8(qt[t][ks]), st, 0, 0, 0);
+      }
+      if (c0 + kT < wave_cand) SPA_FETCH_TILE(c0 + kT);
+      float sv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[r] = st[r];
+      if (c0 + kT > ncand_min) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (c0 + 8 * (r >> 2) + 4 * hl + (r & 3) >= ncand) sv[r] = -INFINITY;
+      }
+      if (gate) {
+        float tm = m_run;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tm = fmaxf(tm, sv[r]);
+        if (tm != -INFINITY) {
+          float acc = l_run * __builtin_amdgcn_exp2f((m_run - tm) * k2);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc += __builtin_amdgcn_exp2f((sv[r] - tm) * k2);
+          l_run = acc;
+          m_run = tm;
         }
       }
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) bet[q4] = *reinterpret_cast<const float4*>(&s_beta32[wave][8 * q4 + 4 * hl]);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = 8 * (r >> 2) + 4 * hl + (r & 3);
-      float s = st[r] * scale;
+      // admission against the tile-start list end: the wave enters the
+      // insert only when one of its lanes holds a qualifying score
+      float thr = ls[KL - 1];
       if constexpr (kErf) {
-        const float4 bq = bet[r >> 2];
-        const float bm = (r & 3) == 0 ? bq.x : (r & 3) == 1 ? bq.y : (r & 3) == 2 ? bq.z : bq.w;
-        s = fmaf(bm, e32[r], s);
-      }
-      s_sc[wave][r][lane] = s;
-      const bool valid = c0 + m < ncand;
-      sv[r] = valid ? s : -INFINITY;
-      mask |= (valid && s > thr) ? (1u << r) : 0u;
-    }
-    if (gate) {
-      float tm = m_run;
+        float lk = ls[0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tm = fmaxf(tm, sv[r]);
-      if (tm != -INFINITY) {
-        float acc = l_run * __expf(m_run - tm);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc += __expf(sv[r] - tm);
-        l_run = acc;
-        m_run = tm;
+        for (int t = 1; t < KMAX; ++t) lk = t == K - 1 ? ls[t] : lk;
+        thr = fmaxf(thr, lk - band);
       }
-    }
-    // within a lane candidates arrive in increasing index, so a tie keeps the
-    // entry already held
-    // (the next admitted slot's LDS read is issued before the current insert)
-    if (mask != 0) {
-      int r = __builtin_ctz(mask);
-      mask &= mask - 1;
-      float v = s_sc[wave][r][lane];
-      while (true) {
-        const bool more = mask != 0;
-        const int rn = more ? __builtin_ctz(mask) : r;
+      float tmax = sv[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sv[r]);
+      if (__ballot(tmax > thr) == 0ull) continue;
+      uint32_t mask = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s_sc[wave][r][lane] = sv[r];
+        mask |= sv[r] > thr ? (1u << r) : 0u;
+      }
+      // within a lane candidates arrive in increasing index, so a tie keeps
+      // the entry already held (the next admitted slot's LDS read is issued
+      // before the current insert)
+      if (mask != 0) {
+        int r = __builtin_ctz(mask);
         mask &= mask - 1;
-        const float vn = s_sc[wave][rn][lane];
-        if (v > ls[KL - 1]) topk_push_later(ls, li, v, static_cast<int>(c0) + 8 * (r >> 2) + 4 * hl + (r & 3));
-        if (!more) break;
-        r = rn;
-        v = vn;
+        float v = s_sc[wave][r][lane];
+        while (true) {
+          const bool more = mask != 0;
+          const int rn = more ? __builtin_ctz(mask) : r;
+          mask &= mask - 1;
+          const float vn = s_sc[wave][rn][lane];
+          if (v > thr && v > ls[KL - 1])
+            topk_push_later(ls, li, v, static_cast<int>(c0) + 8 * (r >> 2) + 4 * hl + (r & 3));
+          if (!more) break;
+          r = rn;
+          v = vn;
+        }
       }
     }
   }
 #undef SPA_FETCH_TILE
+#pragma unroll
+  for (int t = 0; t < KL; ++t) ls[t] *= scale;
+  m_run *= scale;
 
   // merge the two half-waves of each row: the better of each entry and the
   // partner's mirrored entry forms a bitonic sequence holding the top KL of
@@ -379,17 +450,17 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
     }
   } else {
     // Error bound of an fp32 score against the exact one, for any candidate of
-    // this row: the filter erf and its fp32 argument (<= 1.2e-6 |lambda a_c|),
-    // the final fma and operand roundings (<= 1.2e-7 |score|), and the MFMA's
-    // fp32 accumulation of d NTERM products (<= (d NTERM + 2) 2^-24 |q|
-    // |kbar_c| / sqrt(d), with |kbar_c| <= a_c).  E takes each term at least
-    // 4x wider.
+    // this row: the filter erf and its fp32 argument (<= 1.2e-6 |lambda a_c|);
+    // the MFMA's fp32 accumulation of d NTERM products onto the bias
+    // (<= (d NTERM + 2) 2^-24 (|q| |kbar_c| / sqrt(d) + |lambda a_c|), with
+    // |kbar_c| <= a_c); the bias and scale roundings (<= 2.4e-7 (|score| +
+    // |lambda a_c|)).  E takes each term at least 4x wider.
     const float amax = wave_max(amax_t);   // every candidate this wave's rows scored
     float smax = 0.f;
 #pragma unroll
     for (int t = 0; t < KL; ++t)
       if (li[t] != 0x7FFFFFFF) smax = fmaxf(smax, fabsf(ls[t]));
-    const float err = 5e-6f * (1.f + smax + fabsf(lam32) * amax) +
+    const float err = 5e-6f * (1.f + smax) + 2.5e-5f * fabsf(lam32) * amax +
                       4.f * static_cast<float>(D * NTERM + 2) * 5.97e-8f * sqrtf(qsq) * amax * scale;
     const float kth32 = ncand >= K ? ls[K - 1] : -INFINITY;
     const float cut = kth32 - 2.f * err;
