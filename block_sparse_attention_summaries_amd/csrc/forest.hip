@@ -24,13 +24,14 @@
 //                         forest_radius_kernel: one thread per cell against
 //                         every node above it (maxima reduced per node, then
 //                         an integer atomic max of the fp64 squared distance).
-//   forest_select_kernel  one workgroup per (batch, selection head, query
-//                         row), a half per forest: the beam (up to 256
-//                         children scored in fp64, the 16 best kept by a
-//                         threshold search over the scores' orderable bits,
-//                         lower id first on ties), then the union of the
-//                         reached cells re-ranked by the logsumexp of their
-//                         token scores (the four waves share the cells).
+//   forest_select_kernel  one 1024-thread workgroup per (batch, selection
+//                         head, query row), a half per forest: the beam (up
+//                         to 256 children scored in fp64, two lanes each;
+//                         the 16 best kept by a threshold search over the
+//                         scores' orderable bits, lower id first on ties),
+//                         then the union
+//                         of the reached cells re-ranked by the logsumexp of
+//                         their token scores (32 lanes per cell).
 #include "spa_device.h"
 #include "spa_launch.h"
 
@@ -410,12 +411,18 @@ __global__ __launch_bounds__(256) void forest_radius_final_kernel(const unsigned
 }
 
 // ---------------------------------------------------------------- select
-// One workgroup per (batch, selection head, query row): each half runs one
-// forest's beam search (its 128 threads score the up to 256 candidates of a
-// level, one wave keeps the best 16), the four waves share the re-rank (cells
-// of the reached set taken four ways), wave 0 takes the final top K.
+// One 1024-thread workgroup per (batch, selection head, query row); each
+// half runs one forest's beam search.  A level's up to 256 candidates take
+// two lanes each (half of the columns apiece, the halves added in a fixed
+// order), so every load of the level is in flight at once; the forest's
+// first wave keeps the best 16 (a threshold search over the scores'
+// orderable bits, lower id first on ties).  The reached cells are re-ranked
+// with 32 lanes per cell (tokens g, g + 32, ...), and the final top K is
+// found by counting, for each cell, the cells that beat it.
+constexpr int kSelThreads = 1024;
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void forest_select_kernel(
+__global__ __launch_bounds__(kSelThreads) void forest_select_kernel(
     const T* __restrict__ q, const T* __restrict__ kbar, const float* __restrict__ max_norm,
     const float* __restrict__ centre, const T* __restrict__ kcache, int64_t L, int Hq, int Hkv, int Hsel,
     int share_group, int nq, int64_t q_pos0, int64_t ccap, int b, const float* __restrict__ erf_lambda,
@@ -424,6 +431,7 @@ __global__ __launch_bounds__(256) void forest_select_kernel(
     const float* __restrict__ pmin, int64_t n, int64_t NN, int K, int32_t* __restrict__ idx,
     int32_t* __restrict__ k_eff) {
   constexpr int kVec = Elem<T>::kVec;
+  constexpr int kHalf = D / 2;                 // columns per lane of a candidate
   __shared__ double s_q[D];
   __shared__ double s_qn;
   __shared__ int64_t s_front[2][kBeam];
@@ -463,12 +471,10 @@ __global__ __launch_bounds__(256) void forest_select_kernel(
     for (int o = 32; o >= 1; o >>= 1) qq += __shfl_xor(qq, o);
     if (lane == 0) s_qn = sqrt(qq);
   }
-  __syncthreads();
 
-  // both forests at once: threads [128 f, 128 f + 128) score forest f's
-  // candidates (two each), wave 2 f keeps its beam
-  const double qn = s_qn;
-  const int f = tid / 128, ht = tid % 128;
+  // threads [512 f, 512 f + 512) run forest f: candidate x = ht / 2, column
+  // half hf = ht % 2
+  const int f = tid / 512, ht = tid % 512, x = ht >> 1, hf = ht & 1, fw = ht / kWave;
   const int64_t m = nmem[head * 2 + f];
   const int32_t* mem = members + (head * 2 + f) * n;
   const int64_t fb = (head * 2 + f) * NN;
@@ -477,6 +483,7 @@ __global__ __launch_bounds__(256) void forest_select_kernel(
     s_nf[f] = static_cast<int>(s_sh[f].nl ? s_sh[f].n[s_sh[f].nl - 1] : m);
   }
   __syncthreads();
+  const double qn = s_qn;
   const ForestShape& sh = s_sh[f];
   if (ht < s_nf[f]) s_front[f][ht] = ht;
   // rounds: one per level below the top, one for a forest of cells only; the
@@ -490,86 +497,69 @@ __global__ __launch_bounds__(256) void forest_select_kernel(
     const bool own = sh.nl == 0;               // a forest of cells only: score the frontier itself
     const int child_lev = (own || !active) ? 0 : sh.nl - 1 - r;
     const int64_t nchild = child_lev == 0 ? m : sh.n[child_lev - 1];
-    // candidate slots x = ht and 128 + ht (ascending id with x); all loads of
-    // both are issued before any arithmetic, from clamped (valid) addresses
-    int64_t cid[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int x = i * 128 + ht;
-      cid[i] = -1;
-      if (!active) {
-      } else if (own) {
-        cid[i] = x < nf ? s_front[f][x] : -1;
-      } else if (x / kFan < nf) {
-        const int64_t ch = s_front[f][x / kFan] * kFan + (x % kFan);
-        cid[i] = ch < nchild ? ch : -1;
-      }
+    int64_t cid = -1;                          // candidate x (ascending id with x)
+    if (!active) {
+    } else if (own) {
+      cid = x < nf ? s_front[f][x] : -1;
+    } else if (x / kFan < nf) {
+      const int64_t ch = s_front[f][x / kFan] * kFan + (x % kFan);
+      cid = ch < nchild ? ch : -1;
     }
-    double sv[2] = {0.0, 0.0};
+    // this lane's half of the candidate's dot product, loads issued first
+    // from clamped (valid) addresses
+    double part = 0.0, extra = 0.0, ew = 0.0, ex = 0.0;   // extra: the radius and erf terms
     if (child_lev == 0) {
-      int64_t c[2];
+      const int64_t c = mem[cid >= 0 ? cid : 0];
+      uint4 raw[kHalf / kVec];
+      const uint4* kr = reinterpret_cast<const uint4*>(kbar + (head * ccap + c) * D + hf * kHalf);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) c[i] = mem[cid[i] >= 0 ? cid[i] : 0];
-      uint4 raw[2][D / kVec];
-      float an[2], pc[2];
+      for (int v = 0; v < kHalf / kVec; ++v) raw[v] = kr[v];
+      const float an = max_norm[head * ccap + c], pc = centre[c];
+      double pc4[4] = {0.0, 0.0, 0.0, 0.0};    // four independent chains
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint4* kr = reinterpret_cast<const uint4*>(kbar + (head * ccap + c[i]) * D);
+      for (int v = 0; v < kHalf / kVec; ++v) {
+        float t[kVec];
+        Elem<T>::unpack(raw[v], t);
 #pragma unroll
-        for (int v = 0; v < D / kVec; ++v) raw[i][v] = kr[v];
-        an[i] = max_norm[head * ccap + c[i]];
-        pc[i] = centre[c[i]];
+        for (int u = 0; u < kVec; ++u)
+          pc4[u & 3] = fma(s_q[hf * kHalf + v * kVec + u], static_cast<double>(t[u]), pc4[u & 3]);
       }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        double dot = 0.0;
-#pragma unroll
-        for (int v = 0; v < D / kVec; ++v) {
-          float t[kVec];
-          Elem<T>::unpack(raw[i][v], t);
-#pragma unroll
-          for (int u = 0; u < kVec; ++u) dot = fma(s_q[v * kVec + u], static_cast<double>(t[u]), dot);
-        }
-        sv[i] = dot * isd;
-        if (erf_on)
-          sv[i] += lam * static_cast<double>(an[i]) * erf((pos - static_cast<double>(pc[i])) / (2.0 * sig));
-      }
+      part = (pc4[0] + pc4[1]) + (pc4[2] + pc4[3]);
+      ew = lam * static_cast<double>(an);
+      ex = (pos - static_cast<double>(pc)) / (2.0 * sig);
     } else {
-      const int64_t lbase = fb + sh.off[child_lev - 1];
-      float4 w[2][D / 4];
-      float rn[2], an[2], pn[2];
+      const int64_t node = fb + sh.off[child_lev - 1] + (cid >= 0 ? cid : 0);
+      float4 w[kHalf / 4];
+      const float4* mv = reinterpret_cast<const float4*>(mu + node * D + hf * kHalf);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int64_t node = lbase + (cid[i] >= 0 ? cid[i] : 0);
-        const float4* mv = reinterpret_cast<const float4*>(mu + node * D);
+      for (int v = 0; v < kHalf / 4; ++v) w[v] = mv[v];
+      const float rn = rad[node], an = amax[node], pn = pmin[node];
+      double pn4[4] = {0.0, 0.0, 0.0, 0.0};    // four independent chains
 #pragma unroll
-        for (int v = 0; v < D / 4; ++v) w[i][v] = mv[v];
-        rn[i] = rad[node];
-        an[i] = amax[node];
-        pn[i] = pmin[node];
+      for (int v = 0; v < kHalf / 4; ++v) {
+        const int e = hf * kHalf + 4 * v;
+        pn4[0] = fma(s_q[e], static_cast<double>(w[v].x), pn4[0]);
+        pn4[1] = fma(s_q[e + 1], static_cast<double>(w[v].y), pn4[1]);
+        pn4[2] = fma(s_q[e + 2], static_cast<double>(w[v].z), pn4[2]);
+        pn4[3] = fma(s_q[e + 3], static_cast<double>(w[v].w), pn4[3]);
       }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        double dot = 0.0;
-#pragma unroll
-        for (int v = 0; v < D / 4; ++v) {
-          dot = fma(s_q[4 * v], static_cast<double>(w[i][v].x), dot);
-          dot = fma(s_q[4 * v + 1], static_cast<double>(w[i][v].y), dot);
-          dot = fma(s_q[4 * v + 2], static_cast<double>(w[i][v].z), dot);
-          dot = fma(s_q[4 * v + 3], static_cast<double>(w[i][v].w), dot);
-        }
-        sv[i] = dot * isd + qn * static_cast<double>(rn[i]) * isd;
-        if (erf_on)
-          sv[i] += lam * static_cast<double>(an[i]) * erf((pos - static_cast<double>(pn[i])) / (2.0 * sig));
-      }
+      part = (pn4[0] + pn4[1]) + (pn4[2] + pn4[3]);
+      extra = qn * static_cast<double>(rn) * isd;
+      ew = lam * static_cast<double>(an);
+      ex = (pos - static_cast<double>(pn)) / (2.0 * sig);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      s_sc[f][i * 128 + ht] = sv[i];
-      s_cid[f][i * 128 + ht] = cid[i];
+    if (erf_on && hf == 0) extra += ew * erf_exact(ex);
+    const double other = __shfl_xor(part, 1);
+    const double odd_extra = __shfl_xor(extra, 1);
+    const double dot = hf == 0 ? part + other : other + part;
+    const double sv = dot * isd + (hf == 0 ? extra : odd_extra);
+    if (hf == 0) {
+      s_sc[f][x] = sv;
+      s_cid[f][x] = cid;
     }
     __syncthreads();                           // scores written, frontier read
-    if (active && (wave & 1) == 0) {
+    if (active && fw == 0) {
+      // the forest's first wave keeps the best 16 (score, then lower id)
       double sc[4];
       bool ok[4], taken[4];
       int64_t id[4];
@@ -595,19 +585,15 @@ __global__ __launch_bounds__(256) void forest_select_kernel(
   if (wave == 0) {
     // reached cells: the whole-prefix forest's, then the other's not yet there
     const int nf0 = s_nf[0], nf1 = s_nf[1];
-    const int32_t cell0 = members[(head * 2) * n + s_front[0][lane < nf0 ? lane : 0]];
+    if (lane < nf0) s_reach[lane] = members[(head * 2) * n + s_front[0][lane]];
+    wave_lds_sync();
     const int32_t cell1 = members[(head * 2 + 1) * n + s_front[1][lane < nf1 ? lane : 0]];
     bool add = lane < nf1;
-    for (int y = 0; y < nf0; ++y)
-      if (__shfl(cell0, y) == cell1) add = false;
-    if (lane < nf0) s_reach[lane] = cell0;
+    for (int y = 0; y < nf0; ++y) add = add && s_reach[y] != cell1;
     const uint64_t am = __ballot(add);
     if (add) s_reach[nf0 + lanes_below(am)] = cell1;
-    if (lane == 0) s_nreach = nf0 + __popcll(am);
+    const int nreach = nf0 + __popcll(am);
     wave_lds_sync();
-  }
-  if (wave == 0) {
-    const int nreach = s_nreach;
     // ascending cell order (ties in the re-rank then go to the lower cell)
     const int32_t my = lane < nreach ? s_reach[lane] : 0x7fffffff;
     int rank = 0;
@@ -618,85 +604,71 @@ __global__ __launch_bounds__(256) void forest_select_kernel(
   }
   __syncthreads();
 
-  // re-rank: logsumexp of each reached cell's token scores.  Eight adjacent
-  // lanes per cell (32 cells, the most two beams reach, in one pass), lane g
-  // of a cell taking tokens g, g + 8, ...; rows loaded kRows at a time from
-  // clamped (valid) addresses, the scores kept, then a max and a sum over the
-  // cell's lanes.
+  // re-rank: logsumexp of each reached cell's token scores, 32 lanes per cell
+  // (tokens g, g + 32, ...), the max and the sum over the cell's lanes
   const int nreach = s_nreach;
-  constexpr int kLanesPerCell = 8;
-  constexpr int kMaxTok = 64 / kLanesPerCell;  // tokens per lane for b = 64
-  static_assert(256 / kLanesPerCell >= 2 * kBeam, "one pass covers every reached cell");
-  constexpr int kRowBytes = D * static_cast<int>(sizeof(T));
-  constexpr int kRows = kRowBytes <= 128 ? 4 : (kRowBytes <= 256 ? 2 : 1);
   {
-    const int cs = tid / kLanesPerCell, g = tid % kLanesPerCell;
-    const int tpl = b / kLanesPerCell;         // tokens per lane
+    const int cs = tid / 32, g = tid % 32;
     const int64_t c = s_reach[cs < nreach ? cs : nreach - 1];
     const T* kc = kcache + (head * L + c * b) * D;
+    constexpr int kMaxTok = 128 / 32;
     double z[kMaxTok];
 #pragma unroll
-    for (int k0 = 0; k0 < kMaxTok; k0 += kRows) {
-      if (k0 < tpl) {
-        uint4 raw[kRows][D / kVec];
+    for (int k = 0; k < kMaxTok; ++k) {
+      z[k] = -INFINITY;
+      // q_hat is read from LDS per token: held in registers it would take D
+      // doubles per lane
+      asm volatile("" ::: "memory");
+      if (32 * k < b) {
+        const int tok = g + 32 * k;
+        const uint4* kr = reinterpret_cast<const uint4*>(kc + static_cast<int64_t>(tok < b ? tok : b - 1) * D);
+        uint4 raw[D / kVec];
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-          const int k = k0 + r < tpl ? k0 + r : tpl - 1;
-          const uint4* kr = reinterpret_cast<const uint4*>(kc + static_cast<int64_t>(g + kLanesPerCell * k) * D);
+        for (int v = 0; v < D / kVec; ++v) raw[v] = kr[v];
+        double d4[4] = {0.0, 0.0, 0.0, 0.0};  // four independent chains
 #pragma unroll
-          for (int v = 0; v < D / kVec; ++v) raw[r][v] = kr[v];
+        for (int v = 0; v < D / kVec; ++v) {
+          float t[kVec];
+          Elem<T>::unpack(raw[v], t);
+#pragma unroll
+          for (int u = 0; u < kVec; ++u) d4[u & 3] = fma(s_q[v * kVec + u], static_cast<double>(t[u]), d4[u & 3]);
         }
-#pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-          double dot = 0.0;
-#pragma unroll
-          for (int v = 0; v < D / kVec; ++v) {
-            float t[kVec];
-            Elem<T>::unpack(raw[r][v], t);
-#pragma unroll
-            for (int u = 0; u < kVec; ++u) dot = fma(s_q[v * kVec + u], static_cast<double>(t[u]), dot);
-          }
-          z[k0 + r] = dot * isd;
-        }
+        if (tok < b) z[k] = ((d4[0] + d4[1]) + (d4[2] + d4[3])) * isd;
       }
     }
-    double mx = -INFINITY;
+    double mx = z[0];
 #pragma unroll
-    for (int k = 0; k < kMaxTok; ++k)
-      if (k < tpl) mx = z[k] > mx ? z[k] : mx;
+    for (int k = 1; k < kMaxTok; ++k) mx = z[k] > mx ? z[k] : mx;
 #pragma unroll
-    for (int o = kLanesPerCell / 2; o >= 1; o >>= 1) {
+    for (int o = 16; o >= 1; o >>= 1) {
       const double ov = __shfl_xor(mx, o);
       mx = ov > mx ? ov : mx;
     }
     double sexp = 0.0;
 #pragma unroll
     for (int k = 0; k < kMaxTok; ++k)
-      if (k < tpl) sexp += exp(z[k] - mx);
+      if (z[k] != -INFINITY) sexp += exp(z[k] - mx);
 #pragma unroll
-    for (int o = kLanesPerCell / 2; o >= 1; o >>= 1) sexp += __shfl_xor(sexp, o);
+    for (int o = 16; o >= 1; o >>= 1) sexp += __shfl_xor(sexp, o);
     if (cs < nreach && g == 0) s_lse[cs] = mx + log(sexp);
   }
   __syncthreads();
   if (wave != 0) return;
-  double sc[4];
-  bool ok[4], taken[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int x = i * kWave + lane;
-    ok[i] = x < nreach;
-    sc[i] = ok[i] ? s_lse[x] : -INFINITY;
+  // top K of the reached cells (higher logsumexp, then lower cell), written
+  // in ascending cell order
+  const bool okc = lane < nreach;
+  const double mine = okc ? s_lse[lane] : -INFINITY;
+  int beat = 0;
+  for (int y = 0; y < nreach; ++y) {
+    const double o = s_lse[y];
+    beat += (o > mine || (o == mine && y < lane)) ? 1 : 0;
   }
-  const int kk = wave_top_f64x4(sc, ok, K, taken);
+  const int kk = nreach < K ? nreach : K;
+  const bool take = okc && beat < K;
   const int64_t o = (static_cast<int64_t>(bh) * nq + row) * K;
-  int kept = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint64_t tm = __ballot(taken[i]);
-    if (taken[i]) idx[o + kept + lanes_below(tm)] = s_reach[i * kWave + lane];
-    kept += __popcll(tm);
-  }
-  for (int x = kept + lane; x < K; x += kWave) idx[o + x] = -1;
+  const uint64_t tm = __ballot(take);
+  if (take) idx[o + lanes_below(tm)] = s_reach[lane];
+  for (int xx = kk + lane; xx < K; xx += kWave) idx[o + xx] = -1;
   if (lane == 0 && k_eff != nullptr) k_eff[static_cast<int64_t>(bh) * nq + row] = kk;
 }
 
@@ -747,7 +719,7 @@ template <typename T, int D>
 static hipError_t launch_fsel_t(const SelectLaunch& s, const ForestLaunch& p, const void* k, int64_t L,
                                 hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(s.nq), static_cast<unsigned>(s.B * s.Hsel));
-  return launch(true, forest_select_kernel<T, D>, grid, dim3(256), st, static_cast<const T*>(s.q),
+  return launch(true, forest_select_kernel<T, D>, grid, dim3(kSelThreads), st, static_cast<const T*>(s.q),
                 static_cast<const T*>(s.kbar), s.max_norm, s.centre, static_cast<const T*>(k), L, s.Hq, s.Hkv, s.Hsel,
                 s.share_group, s.nq, s.q_pos0, s.ccap, s.b, s.erf_lambda, s.erf_sigma,
                 static_cast<const int32_t*>(p.members), static_cast<const int32_t*>(p.nmem),

@@ -367,6 +367,39 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u)));
 }
 
+// erf in fp64 to within 3e-14 (absolute) with few live registers:
+// |x| < 2.5: the positive-term series erf(x) = 2/sqrt(pi) exp(-x^2)
+//   sum_n 2^n x^(2n+1) / (1 3 5 ... (2n+1)) (Abramowitz & Stegun 7.1.6), 33 terms;
+// 2.5 <= |x| < 6: the continued fraction for erfc (A&S 7.1.14), 20 levels,
+//   evaluated from the tail as one numerator/denominator pair;
+// |x| >= 6: +-1 (erfc(6) < 2.2e-17).
+__device__ __forceinline__ double erf_exact(double x) {
+  const double ax = fabs(x);
+  if (ax >= 6.0) return copysign(1.0, x);
+  const double g = exp(-ax * ax);
+  double r;
+  if (ax < 2.5) {
+    const double y = 2.0 * ax * ax;
+    double t = ax, s = ax;
+#pragma unroll
+    for (int n = 1; n <= 32; ++n) {
+      t *= y * (1.0 / (2 * n + 1));
+      s += t;
+    }
+    r = 1.1283791670955126 * g * s;               // 2 / sqrt(pi)
+  } else {
+    double num = ax, den = 1.0;
+#pragma unroll
+    for (int k = 20; k >= 1; --k) {
+      const double nn = fma(ax, num, 0.5 * k * den);
+      den = num;
+      num = nn;
+    }
+    r = 1.0 - g * den / (1.7724538509055159 * num);  // sqrt(pi)
+  }
+  return copysign(r, x);
+}
+
 // ------------------------------------------------------- fp64 top-k of a wave
 __device__ __forceinline__ uint64_t orderable_f64(double v) {
   if (v == 0.0) v = 0.0;                       // +0 and -0 compare equal
