@@ -378,6 +378,16 @@ def run_decode(args):
             "warm": step_latencies([(0, 0)], args.replays)}
     sweep = run_decode_sweep(wl, args, stream) if not args.skip_variants else None
 
+    # the summary of a closing block (once per b steps): timed alone, so that
+    # its share per step is known whatever --steps is
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(32):
+        wl.close_block(s % args.layers)
+    e1.record()
+    torch.cuda.synchronize()
+    close_us = e0.elapsed_time(e1) * 1e3 / 32
+
     # a hot-cache variant (one layer, one query) for context
     hot = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
@@ -396,7 +406,7 @@ def run_decode(args):
 
     floor_us = latency_floor_us(stream, steps, len(k_ms))
     return dict(wl=wl, cfg=cfg, x=x, total_ms=total_ms, unfused_ms=unfused_ms, paged_ms=paged_ms, k_ms=k_ms,
-                fp8_ms=fp8_ms, fp8_k_ms=fp8_k_ms, dist=dist, sweep=sweep,
+                fp8_ms=fp8_ms, fp8_k_ms=fp8_k_ms, dist=dist, sweep=sweep, close_us=close_us,
                 summ_ms=summ_ms, summ_bytes=summ_bytes, hot_us=hot_us, floor_us=floor_us)
 
 
@@ -836,44 +846,50 @@ def calibrate_copy():
     torch.cuda.synchronize()
 
 
-def _read_pmc_csv(path, counter):
-    """Mean counter value (KiB) per dispatch, keyed by kernel name, from a
-    rocprofv3 counter_collection.csv."""
+def _read_pmc_rows(path, counter):
+    """(kernel name, dispatch id, value in KiB) of every dispatch of a
+    rocprofv3 counter_collection.csv for one counter."""
     import csv
-    vals = {}
+    out = []
     with open(path) as fh:
         for row in csv.DictReader(fh):
             name = row.get("Kernel_Name") or row.get("Kernel-Name") or ""
             cname = row.get("Counter_Name") or row.get("Counter-Name") or ""
             if cname != counter:
                 continue
-            v = float(row.get("Counter_Value") or row.get("Counter-Value") or 0.0)
-            vals.setdefault(name, []).append(v)
-    return {k: sum(v) / len(v) for k, v in vals.items()}
+            did = int(row.get("Dispatch_Id") or row.get("Dispatch-Id") or 0)
+            out.append((name, did, float(row.get("Counter_Value") or row.get("Counter-Value") or 0.0)))
+    return out
 
 
 def write_counters(fetch_csv, write_csv):
     """profiles/decode_512k_hbm_counters.json from two rocprofv3 --pmc runs
-    (FETCH_SIZE, then WRITE_SIZE) of `bench.py --calibrate-copy ...`."""
-    fetch = _read_pmc_csv(fetch_csv, "FETCH_SIZE")
-    write = _read_pmc_csv(write_csv, "WRITE_SIZE")
-
-    def pick(table, key):
-        hits = [v for k, v in table.items() if key in k]
-        return hits[0] if hits else None
-
+    (FETCH_SIZE, then WRITE_SIZE) of `bench.py --calibrate-copy ...`.  The
+    calibration is the device copy whose WRITE_SIZE is nearest COPY_BYTES (the
+    runs hold other copies of other sizes); a kernel's figures are the means
+    over its dispatches."""
+    fetch = _read_pmc_rows(fetch_csv, "FETCH_SIZE")
+    write = _read_pmc_rows(write_csv, "WRITE_SIZE")
     copy_key = "copyBuffer"          # the runtime's device-to-device copy kernel
-    cf = [v for k, v in fetch.items() if copy_key in k]
-    cw = [v for k, v in write.items() if copy_key in k]
-    if not cf or not cw:
-        raise SystemExit("no copy kernel found in the counter files")
     kib = COPY_BYTES / 1024.0
-    out = {"source_sha": source_hash(), "copy_bytes": COPY_BYTES,
-           "copy_fetch_kib": max(cf), "copy_write_kib": max(cw),
-           "fetch_scale": kib / max(cf), "write_scale": kib / max(cw), "kernels": {}}
+    cw = [(abs(v - kib), did, v) for n, did, v in write if copy_key in n]
+    if not cw:
+        raise SystemExit("no copy kernel found in the counter files")
+    _, cal_id, cal_w = min(cw)
+    cf = [v for n, did, v in fetch if copy_key in n and did == cal_id]
+    if not cf:
+        raise SystemExit("the calibration copy is missing from the FETCH_SIZE run")
+
+    def mean_of(rows, key):
+        vals = [v for n, _, v in rows if key in n]
+        return sum(vals) / len(vals) if vals else None
+
+    out = {"source_sha": source_hash(), "copy_bytes": COPY_BYTES, "copy_dispatch": cal_id,
+           "copy_fetch_kib": cf[0], "copy_write_kib": cal_w,
+           "fetch_scale": kib / cf[0], "write_scale": kib / cal_w, "kernels": {}}
     out["copy_scale"] = 1.0
     for kname in [k for _, k in STEP_KERNELS + TWO_CALL_KERNELS]:
-        f, w = pick(fetch, kname), pick(write, kname)
+        f, w = mean_of(fetch, kname), mean_of(write, kname)
         if f is not None and w is not None:
             out["kernels"][kname] = {"fetch_kib": f, "write_kib": w,
                                      "traffic_bytes": f * 1024 * out["fetch_scale"] + w * 1024 * out["write_scale"]}
@@ -986,6 +1002,12 @@ def main():
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kern.items()},
         "hot_cache_us_per_step": round(res["hot_us"], 3),
+        # the timed steps include a block close every b steps only when
+        # --steps reaches b; the close alone and its share per step:
+        "block_close_us": round(res["close_us"], 3),
+        "closes_in_timed_steps": steps // wl.b,
+        "us_per_step_with_amortised_close": round(
+            (res["total_ms"] * 1e3 - (steps // wl.b) * res["close_us"]) / steps + res["close_us"] / wl.b, 3),
         "summaries_512k_ms": round(res["summ_ms"], 3),
         "summaries_gbps": round(res["summ_bytes"] / (res["summ_ms"] * 1e-3) / 1e9, 1),
         "roofline": roofline,
