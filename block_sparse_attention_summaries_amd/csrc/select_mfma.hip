@@ -55,6 +55,68 @@ __device__ __forceinline__ float erf_filter(float x) {
   return copysignf(fmaf(-poly, g, 1.0f), x);
 }
 
+// First tile of the erf walk: the lane's list is empty, so its KL best of
+// the tile's 16 scores come from a sorting network instead of 16 inserts.
+// Each score becomes a key with its tile slot r in the low 4 mantissa bits
+// (keys are distinct; a key is within 16 ulp, 2^-19 relative, of its score,
+// which the error bounds below include); -inf (no candidate) becomes the
+// finite -3.4e38 (the largest finite negative) first, so no key is a NaN.  Batcher's bitonic sort orders
+// the two halves, the better of each mirrored pair of the halves forms a
+// bitonic sequence holding the best 8 of 16, and a half-cleaner cascade sorts
+// it; KL = 16 sorts all 16 with the full network.
+__device__ __forceinline__ void key_ce(float& a, float& b) {
+  const float hi = __builtin_fmaxf(a, b);
+  b = __builtin_fminf(a, b);
+  a = hi;
+}
+
+template <int N>
+__device__ __forceinline__ void bitonic_sort_keys(float* k) {
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1)
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          if ((i & size) == 0)
+            key_ce(k[i], k[j]);
+          else
+            key_ce(k[j], k[i]);
+        }
+      }
+}
+
+template <int KL>
+__device__ __forceinline__ void first_tile_list(const float (&sv)[16], int c_lane, float (&ls)[KL], int (&li)[KL]) {
+  static_assert(KL == 8 || KL == 16, "first-tile network: lists of 8 or 16");
+  float k[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    k[r] = __uint_as_float((__float_as_uint(__builtin_fmaxf(sv[r], -3.40282347e38f)) & ~15u) | static_cast<uint32_t>(r));
+  if constexpr (KL == 16) {
+    bitonic_sort_keys<16>(k);
+  } else {
+    bitonic_sort_keys<8>(k);
+    bitonic_sort_keys<8>(k + 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) k[i] = __builtin_fmaxf(k[i], k[15 - i]);
+#pragma unroll
+    for (int stride = 4; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if ((i & stride) == 0) key_ce(k[i], k[i + stride]);
+  }
+#pragma unroll
+  for (int t = 0; t < KL; ++t) {
+    const uint32_t r = __float_as_uint(k[t]) & 15u;
+    const bool ok = k[t] > -1e38f;
+    ls[t] = ok ? k[t] : -INFINITY;
+    li[t] = ok ? c_lane + static_cast<int>(((r & 12u) << 1) | (r & 3u)) : 0x7FFFFFFF;
+  }
+}
+
 // NTERM = 1: one head's bf16 query; NTERM = 3: split group-mean query.
 // List length: KMAX (no erf; fp32 ranking is final) or 2 KMAX (erf).
 template <int D, int KMAX, int NTERM, bool kErf>
@@ -246,7 +308,7 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
     am = wave_max(am);
     const float qn = sqrtf(qsq);
     const float sb = qn * am * scale + fabsf(lam32) * am;
-    const float err_max = 5e-6f * (1.f + sb) + 2.5e-5f * fabsf(lam32) * am +
+    const float err_max = 5e-6f + 7e-6f * sb + 2.5e-5f * fabsf(lam32) * am +
                           4.f * static_cast<float>(D * NTERM + 2) * 5.97e-8f * qn * am * scale;
     band = 2.5f * err_max * inv_scale;
   }
@@ -326,6 +388,12 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
           for (int r = 0; r < 16; ++r) acc += __builtin_amdgcn_exp2f((sv[r] - tm) * k2);
           l_run = acc;
           m_run = tm;
+        }
+      }
+      if constexpr (kErf) {
+        if (c0 == 0) {
+          first_tile_list<KL>(sv, 4 * hl, ls, li);
+          continue;
         }
       }
       // admission against the tile-start list end: the wave enters the
@@ -421,13 +489,14 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
     // the MFMA's fp32 accumulation of d NTERM products onto the bias
     // (<= (d NTERM + 2) 2^-24 (|q| |kbar_c| / sqrt(d) + |lambda a_c|), with
     // |kbar_c| <= a_c); the bias and scale roundings (<= 2.4e-7 (|score| +
-    // |lambda a_c|)).  E takes each term at least 4x wider.
+    // |lambda a_c|)); the first tile's keys (<= 2^-19 |score|, taken as
+    // 2e-6 |score|).  E takes the other terms at least 4x wider.
     const float amax = wave_max(amax_t);   // every candidate this wave's rows scored
     float smax = 0.f;
 #pragma unroll
     for (int t = 0; t < KL; ++t)
       if (li[t] != 0x7FFFFFFF) smax = fmaxf(smax, fabsf(ls[t]));
-    const float err = 5e-6f * (1.f + smax) + 2.5e-5f * fabsf(lam32) * amax +
+    const float err = 5e-6f + 7e-6f * smax + 2.5e-5f * fabsf(lam32) * amax +
                       4.f * static_cast<float>(D * NTERM + 2) * 5.97e-8f * sqrtf(qsq) * amax * scale;
     const float kth32 = ncand >= K ? ls[K - 1] : -INFINITY;
     const float cut = kth32 - 2.f * err;
