@@ -24,7 +24,8 @@
 // workgroup table of row - cell b when the centres are the cell middles; a
 // tile whose every (row, cell) pair lies where the table is 1 skips it) in a
 // list twice the budget long, admitting only scores within the largest
-// possible band of the lane's running K-th best.  At the end, list entries
+// possible band of the row's running K-th best (over both half-waves'
+// lists).  At the end, list entries
 // within twice a proven
 // error bound of the fp32 K-th best are re-scored exactly (fp64 dot product
 // and bias) and the exact top-K is taken from them; with the gate off, a row
@@ -400,9 +401,23 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
       // insert only when one of its lanes holds a qualifying score
       float thr = ls[KL - 1];
       if constexpr (kErf) {
-        float lk = ls[0];
+        // the row's running K-th best: the K-th of the union of this lane's
+        // list and its partner half's (lane ^ 32).  The better of each
+        // mirrored pair of the two sorted lists' first KMAX entries forms a
+        // bitonic sequence holding the union's best KMAX; a half-cleaner
+        // cascade sorts it.  A score below it minus the band cannot reach
+        // the row's final top-K, whichever half holds it.
+        float u[KMAX];
 #pragma unroll
-        for (int t = 1; t < KMAX; ++t) lk = t == K - 1 ? ls[t] : lk;
+        for (int t = 0; t < KMAX; ++t) u[t] = __builtin_fmaxf(ls[t], xor_lanes_f<32>(ls[KMAX - 1 - t]));
+#pragma unroll
+        for (int stride = KMAX / 2; stride > 0; stride >>= 1)
+#pragma unroll
+          for (int t = 0; t < KMAX; ++t)
+            if ((t & stride) == 0) key_ce(u[t], u[t + stride]);
+        float lk = u[0];
+#pragma unroll
+        for (int t = 1; t < KMAX; ++t) lk = t == K - 1 ? u[t] : lk;
         thr = fmaxf(thr, lk - band);
       }
       float tmax = sv[0];
