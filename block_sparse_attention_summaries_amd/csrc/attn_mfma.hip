@@ -397,7 +397,9 @@ __global__ __launch_bounds__(256) void attn_cell_partial_kernel(
 
 // kMode 0: selected blocks (SAS); 1: routed cells walked per row tile + window;
 // 2: window walk only, branch L merged from attn_cell_partial_kernel's
-// per-(row, slot) partials (cell_o / cell_ml).
+// per-(row, slot) partials (cell_o / cell_ml); 3: SAS with the selected
+// blocks computed block-major (the same partials): the walk covers the rows'
+// current blocks only, and the row's partials join its softmax.
 template <int D, int kMode, int NW>
 __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -406,8 +408,10 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
     int prefix_mode, int qblock, int K, int local, int window, __bf16* __restrict__ o,
     float* __restrict__ lse, int NH, int NT, const __bf16* __restrict__ cell_o,
     const float2* __restrict__ cell_ml) {
-  constexpr bool kMix = kMode != 0;
+  constexpr bool kMix = kMode == 1 || kMode == 2;
   constexpr bool kCells = kMode == 2;
+  constexpr bool kSasCells = kMode == 3;
+  constexpr bool kUnitsApart = kCells || kSasCells;     // selected units come as partials
   __shared__ TileSmem<D> sm;
   __shared__ uint32_t s_bits[2][kMaxKeyTiles / 32];
   __shared__ uint16_t s_list[2][kMaxKeyTiles];
@@ -469,7 +473,7 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
     for (int64_t t = k0 / kKT + tid; t <= p1 / kKT; t += kThreads)
       atomicOr(&s_bits[1][t >> 5], 1u << (t & 31));
   }
-  for (int t = hl; t < K && !kCells; t += 2) {
+  for (int t = hl; t < K && !kUnitsApart; t += 2) {
     const int c = reinterpret_cast<int16_t*>(s_idx[wave][ql])[t];
     if (c >= 0) {
       const int64_t a0 = static_cast<int64_t>(c) * b, a1 = a0 + b - 1;
@@ -626,6 +630,8 @@ _Pragma("unroll")                                                               
           float bv = -INFINITY;                                                                          \
           if (local == 0 && uv == c_cur) {                                                               \
             bv = 0.f;   /* causal mask applied per key below */                                          \
+          } else if (kSasCells) {                                                                        \
+            /* another row's current block: this row's selected blocks come as partials */              \
           } else {                                                                                       \
             while (nu < uv) {   /* advance past smaller units (unused slots hold -1) */                  \
               ++cur; nu = cur < K ? ur[cur] : 0x7FFFFFFF; nlg = cur < K ? s_lg[wave][ql][cur] * kLog2e : 0.f; }\
@@ -782,6 +788,51 @@ _Pragma("unroll")                                                               
       for (int db = 0; db < kDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = a * (ol[db * 16 + r] * winv) + (1.f - a) * (acc[db][r] * inv);
+    } else if constexpr (kSasCells) {
+      // one softmax over the current block (this walk: acc and lsum relative
+      // to m2) and the row's selected blocks (partials: o normalised, (max,
+      // sum) in the log2 domain), each selected block once (its first slot)
+      const int16_t* ur = reinterpret_cast<const int16_t*>(s_idx[wave][ql]);
+      const int64_t pr0 = ((static_cast<int64_t>(bi) * Hq + h) * nq + rowc) * K;
+      float M = m2;
+      for (int t = 0; t < K; ++t) {
+        const int ct = ur[t];
+        bool first = ct >= 0;
+        for (int u = 0; u < t; ++u) first = first && ur[u] != ct;
+        if (first) M = fmaxf(M, cell_ml[pr0 + t].x);
+      }
+      const float msub = M == -INFINITY ? 0.f : M;
+      const float cw = __builtin_amdgcn_exp2f(m2 - msub);
+      float den = lsum * cw;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= cw;
+      for (int t = 0; t < K; ++t) {
+        const int ct = ur[t];
+        bool first = ct >= 0;
+        for (int u = 0; u < t; ++u) first = first && ur[u] != ct;
+        if (!first) continue;
+        const float2 ml = cell_ml[pr0 + t];
+        const float wt = ml.y * __builtin_amdgcn_exp2f(ml.x - msub);
+        den += wt;
+        const __bf16* orow = cell_o + (pr0 + t) * D;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+            const auto w4 = *reinterpret_cast<const __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16*>(
+                orow + 32 * db + 8 * a4 + 4 * hl);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) acc[db][4 * a4 + x] = fmaf(wt, static_cast<float>(w4[x]), acc[db][4 * a4 + x]);
+          }
+      }
+      const float dinv = den > 0.f ? 1.f / den : 0.f;
+      lse_L = den > 0.f ? (M + __log2f(den)) / kLog2e : -INFINITY;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= dinv;
     } else if constexpr (kMix) {
       if (branch == 0) {
 #pragma unroll
@@ -829,11 +880,34 @@ bool attn_tile_fwd_supported(const AttnLaunch& p) {
 // head), and partials (K per row and query head) of at most 16 GiB; otherwise
 // the tile kernel walks each row tile's cells itself.
 constexpr size_t kMaxCellPartialBytes = static_cast<size_t>(16) << 30;
-static bool use_cell_path(const AttnLaunch& p) {
+static bool cell_partials_fit(const AttnLaunch& p) {
   const int G = p.Hq / p.Hkv;
   const size_t parts = static_cast<size_t>(p.B) * p.Hq * p.nq * p.K;
-  return p.window > 0 && p.alpha != nullptr && (p.b == 32 || p.b == 64) && G <= 4 && (p.share_group || G == 1) &&
-         p.K >= 1 && parts * (p.d * sizeof(__bf16) + sizeof(float2)) <= kMaxCellPartialBytes;
+  return (p.b == 32 || p.b == 64) && G <= 4 && (p.share_group || G == 1) && p.K >= 1 &&
+         parts * (p.d * sizeof(__bf16) + sizeof(float2)) <= kMaxCellPartialBytes;
+}
+static bool use_cell_path(const AttnLaunch& p) {
+  return p.window > 0 && p.alpha != nullptr && cell_partials_fit(p);
+}
+// SAS with the selected blocks block-major (the current block walked per row
+// tile, the selected blocks as per-(row, slot) partials) where the masked-tile
+// walk would waste the most: a 32-row tile walks the union of its rows'
+// selected blocks (at most the prefix, at most 32 K blocks) plus the current
+// one, while a row keeps K + 1.  Measured at 32 query / 8 kv heads, d = 128,
+// b = 64, K = 16 (forward ms, masked tiles vs block-major): 4 x 8K (union /
+// kept 3.8) 3.7 vs 5.4; 1 x 32K (15.1) 10.2 vs 5.8; 1 x 64K (30.1) 27.3 vs
+// 12.0.  The partials (K d bf16 per row and query head, written and read
+// back) and the per-slot q reads are what the block-major form pays.
+constexpr double kSasBlockMajorWaste = 7.0;   // the measured break-even, interpolated
+static double sas_masked_waste(const AttnLaunch& p) {
+  const double pmid = static_cast<double>(num_candidates(p.q_pos0 + p.nq / 2, p.b, p.prefix_mode, p.qblock));
+  const double uni = pmid < 32.0 * p.K ? pmid : 32.0 * p.K;
+  const double kept = pmid < p.K ? pmid : p.K;
+  return (uni + 1.0) / (kept + 1.0);
+}
+static bool use_sas_cell_path(const AttnLaunch& p) {
+  return !(p.window > 0 && p.alpha != nullptr) && p.local == 0 && cell_partials_fit(p) &&
+         sas_masked_waste(p) >= kSasBlockMajorWaste;
 }
 
 struct CellWs {
@@ -889,7 +963,7 @@ static CellWs cell_ws(const AttnLaunch& p, void* ws) {
 }
 
 size_t attn_tile_fwd_workspace_bytes(const AttnLaunch& p) {
-  return use_cell_path(p) ? cell_ws(p, nullptr).bytes : 0;
+  return (use_cell_path(p) || use_sas_cell_path(p)) ? cell_ws(p, nullptr).bytes : 0;
 }
 
 // The cell-major branch L: mark, count, scan and fill build the units, then
@@ -967,6 +1041,15 @@ hipError_t launch_attn_tile_fwd(const AttnLaunch& p, void* ws, hipStream_t st) {
     if (e != hipSuccess) return e;
     if (p.d == 64) return launch_tile_fwd_k<64, 2, 4>(p, NH, NT, cell_o, cell_ml, st);
     return launch_tile_fwd_k<128, 2, 4>(p, NH, NT, cell_o, cell_ml, st);
+  }
+  if (!mix && use_sas_cell_path(p)) {
+    const __bf16* cell_o = nullptr;
+    const float2* cell_ml = nullptr;
+    const hipError_t e = p.d == 64 ? launch_cell_partials<64>(p, ws, st, &cell_o, &cell_ml)
+                                   : launch_cell_partials<128>(p, ws, st, &cell_o, &cell_ml);
+    if (e != hipSuccess) return e;
+    if (p.d == 64) return launch_tile_fwd_k<64, 3, 4>(p, NH, NT, cell_o, cell_ml, st);
+    return launch_tile_fwd_k<128, 3, 4>(p, NH, NT, cell_o, cell_ml, st);
   }
   if (G == 1 && p.d == 64) {
     return mix ? launch_tile_fwd_k<64, 1, 2>(p, 1, 2, nullptr, nullptr, st)

@@ -255,7 +255,13 @@ typedef struct spa_attn_args {
  * and per (row, query head, slot) a bf16 partial of d values plus 8 bytes
  * (about B Hq nq K (2d + 8) bytes; 143 MB at 16 heads, nq = 16384, K = 4,
  * d = 64); beyond 16 GiB of partials the call walks the cells per row tile
- * instead and needs no workspace.
+ * instead and needs no workspace.  The selected-block mode takes the same
+ * block-major form (partials of the selected blocks, the current block walked
+ * per row tile, joined into one softmax) when a 32-row tile's union of
+ * selected blocks would be at least 7x the K + 1 blocks a row keeps (at the
+ * middle row: min(candidates, 32 K) + 1 over min(candidates, K) + 1), with
+ * b of 32 or 64, at most 4 query heads per kv head sharing the selection (or
+ * one) and at most 16 GiB of partials; otherwise it needs no workspace.
  */
 spa_status sparse_attn_fwd(const spa_attn_args *a, void *workspace, size_t ws_bytes,
                     spa_stream_t stream);

@@ -11,6 +11,7 @@ selection matches.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 import sys
 
@@ -520,6 +521,40 @@ def test_train_fwd_bwd_parity(over):
     x = make_inputs(cfg)
     r = _train_case(cfg, x)
     _say(f"  exempt rows {_check_train(cfg, r)}")
+
+
+@pytest.mark.parametrize("over", [
+    dict(B=1, n=4096, Hq=8, Hkv=2, b=32, K=4, seed=38),                   # union / kept 13: block-major
+    dict(B=1, n=3000, Hq=4, Hkv=4, b=32, K=4, share_group=False, seed=39),  # per-head selection, ragged
+])
+def test_train_block_major_forward(over):
+    """Sparse enough for the block-major forward (the selected blocks as
+    per-(row, slot) partials, the current block walked per row tile): the
+    forward needs the partials' workspace, and fwd + bwd match the oracle."""
+    cfg = config("train", **over)
+    _say(f"[train block-major] {over}")
+    x = make_inputs(cfg)
+    akw = dict(b=cfg["b"], K=cfg["K"], q_pos0=0, share_group=cfg["share_group"])
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    idx = torch.zeros((cfg["B"], cfg["Hq"] if not cfg["share_group"] else cfg["Hkv"], x["L"], cfg["K"]),
+                      dtype=torch.int32, device=q.device)
+    a, _ = ops.attn_args(q, k, v, idx, None, **akw)
+    assert ops.lib().sparse_workspace_bytes(ops.SPA_OP_ATTN_FWD, ctypes.byref(a)) > 0
+    r = _train_case(cfg, x)
+    _say(f"  exempt rows {_check_train(cfg, r)}")
+
+
+def test_train_config_keeps_masked_tiles():
+    """At 4 x 8K with K = 16 of <= 128 blocks the masked-tile walk is faster:
+    the forward needs no partials' workspace."""
+    cfg = config("train")
+    akw = dict(b=cfg["b"], K=cfg["K"], q_pos0=0, share_group=True)
+    B, Hq, Hkv, n, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["n"], cfg["d"]
+    q = torch.empty((B, Hq, n, d), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((B, Hkv, n, d), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((B, Hkv, n, cfg["K"]), dtype=torch.int32, device="cuda")
+    a, _ = ops.attn_args(q, k, k, idx, None, **akw)
+    assert ops.lib().sparse_workspace_bytes(ops.SPA_OP_ATTN_FWD, ctypes.byref(a)) == 0
 
 
 def test_train_full_size_one_slice():
