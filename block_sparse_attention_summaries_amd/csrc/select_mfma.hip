@@ -25,13 +25,13 @@
 // tile whose every (row, cell) pair lies where the table is 1 skips it) in a
 // list twice the budget long, admitting only scores within the largest
 // possible band of the row's running K-th best (over both half-waves'
-// lists).  At the end, list entries
-// within twice a proven
-// error bound of the fp32 K-th best are re-scored exactly (fp64 dot product
-// and bias) and the exact top-K is taken from them; with the gate off, a row
-// whose (K+1)-th entry lies below that band keeps its first K entries as they
-// are.  If the list's last entry is itself within the band, a candidate may
-// have been dropped, and the row is re-scored exactly in full.
+// lists).  At the end, list entries within twice a proven error bound of the
+// fp32 K-th best are re-scored exactly (fp64 dot product and bias) and the
+// exact top-K is taken from them; with the gate off, a row whose (K+1)-th
+// entry lies below that band keeps its first K entries as they are, and
+// otherwise re-scores only the entries not certainly inside.  If the list's
+// last entry is itself within the band, a candidate may have been dropped,
+// and the row is re-scored exactly in full.
 #include "spa_device.h"
 #include "spa_launch.h"
 
@@ -522,6 +522,16 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
     // the band, every candidate outside the first K scores exactly below every
     // one inside (|exact - fp32| <= err), so the first K are the exact top-K.
     const bool decided = !gate && (ncand <= K || ls[K] < cut);
+    // gate off, not decided: an entry whose fp32 score passes the (K+1)-th
+    // listed one (at least every fp32 score outside the first K) by more than
+    // 2 err scores exactly above every candidate outside the first K, so it is
+    // in the exact top-K; those entries (a prefix) keep their place and only
+    // the rest of the qualifying prefix is scored exactly, for the other slots
+    int m_sure = 0;
+    if (!gate && !decided && !rescan) {
+#pragma unroll
+      for (int t = 0; t < KMAX; ++t) m_sure += (t < K && ls[t] > ls[K] + 2.f * err) ? 1 : 0;
+    }
     // the qualifying entries are a prefix of the best-first list
     int* slot = reinterpret_cast<int*>(&s_sc[wave][0][0]);
     int n_ok = 0;
@@ -543,13 +553,13 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
       ei[t] = 0x7FFFFFFF;
     }
     const double inv_sqrt_d = 1.0 / sqrt(static_cast<double>(D));
-    const int64_t nsrc = decided ? 0 : (rescan ? ncand : n_ok);
+    const int64_t nsrc = decided ? 0 : (rescan ? ncand : n_ok - m_sure);
     uint4 kv[kKS];
     float cen = 0.f, anorm = 0.f;
     int c = 0;
 #define SPA_LOAD_CAND(J)                                                                      \
   do {                                                                                        \
-    c = rescan ? static_cast<int>(J) : slot[(J) * 64 + lane];                                 \
+    c = rescan ? static_cast<int>(J) : slot[((J) + m_sure) * 64 + lane];                      \
     _Pragma("unroll") for (int ks = 0; ks < kKS; ++ks)                                        \
       kv[ks] = *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(c) * D + 16 * ks + 8 * hl); \
     cen = centre[c];                                                                          \
@@ -595,6 +605,29 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
       for (int t = 0; t < KMAX; ++t) {
         es[t] = t < K ? static_cast<double>(ls[t]) : -INFINITY;
         ei[t] = t < K ? li[t] : 0x7FFFFFFF;
+      }
+    } else if (m_sure > 0) {
+      // the certain entries, then the best of the exactly scored ones
+      double fe[KMAX];
+      int fi[KMAX];
+#pragma unroll
+      for (int t = 0; t < KMAX; ++t) {
+        double e = -INFINITY;
+        int ix = 0x7FFFFFFF;
+#pragma unroll
+        for (int u = 0; u < KMAX; ++u) {
+          if (u == t - m_sure) {
+            e = es[u];
+            ix = ei[u];
+          }
+        }
+        fe[t] = t < m_sure ? static_cast<double>(ls[t]) : e;
+        fi[t] = t < m_sure ? li[t] : ix;
+      }
+#pragma unroll
+      for (int t = 0; t < KMAX; ++t) {
+        es[t] = fe[t];
+        ei[t] = fi[t];
       }
     }
 #pragma unroll
