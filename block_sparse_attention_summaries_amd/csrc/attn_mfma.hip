@@ -70,7 +70,7 @@ constexpr float kLazyMax = 8.0f;
 // row tile: a row tile's union of selected cells is ~10x the 4 a row reads,
 // while a cell's selecting rows fill whole 32-row tiles.  fwd_mark_kernel
 // sets one bit per (selection head, cell, row) for "the row selected the
-// cell"; the count / scan / fill kernels turn the bitmap into units of 32
+// cell"; the count and fill kernels turn the bitmap into units of 32
 // selecting rows of one cell (row order); attn_cell_partial_kernel takes one
 // unit per wave and writes for each (row, slot of the cell in the row's
 // selection) the softmax of the row over the cell's keys: o normalised (bf16)
@@ -107,11 +107,13 @@ __global__ __launch_bounds__(256) void fwd_mark_kernel(const int32_t* __restrict
 }
 
 // Work units: a cell's selecting rows in tiles of 32 (row order), one unit
-// per wave.  cell_count_kernel: one wave per (selection head, cell) counts its
-// rows; cell_scan_kernel (one workgroup) gives each entry (head * ncell + cell)
-// the index of its first unit and the total; cell_fill_kernel: one wave per
-// entry lists the rows, 32 per unit (the last unit padded with -1), and
-// writes the units' (entry, tile).
+// per wave.  Each selection head has a region of `cap` unit slots (at most
+// ncell + nq K / 32 units); its cells' units follow in cell order.
+// cell_count_kernel: one wave per entry (head * ncell + cell) counts its rows;
+// cell_fill_kernel: one wave per entry finds its first unit by summing the
+// unit counts of the head's earlier cells, lists the rows, 32 per unit (the
+// last unit padded with -1), writes the units' (entry, tile), and the head's
+// last cell writes the head's unit count.
 constexpr int kCellUnit = 32;
 constexpr int kFillChunk = 8;                    // bitmap words per lane loaded together
 
@@ -129,80 +131,25 @@ __global__ __launch_bounds__(256) void cell_count_kernel(const uint32_t* __restr
   if (lane == 0) cnt[e] = n;
 }
 
-__global__ __launch_bounds__(1024) void cell_scan_kernel(const int32_t* __restrict__ cnt, int64_t nent,
-                                                         int32_t* __restrict__ first, int32_t* __restrict__ nunits) {
-  constexpr int kPer = 16;                      // entries per thread per chunk
-  constexpr int kChunk = 1024 * kPer;
-  __shared__ int32_t s_c[kChunk];               // a chunk's unit counts, then its offsets
-  __shared__ int32_t s_wave[16];
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  int32_t base = 0;
-  for (int64_t c0 = 0; c0 < nent; c0 += kChunk) {
-    // coalesced loads (entry c0 + 1024 x + tid), issued together
-    int32_t ld[kPer];
-#pragma unroll
-    for (int x = 0; x < kPer; ++x) {
-      const int64_t e = c0 + 1024 * x + tid;
-      ld[x] = cnt[e < nent ? e : nent - 1];
-    }
-#pragma unroll
-    for (int x = 0; x < kPer; ++x) {
-      const int64_t e = c0 + 1024 * x + tid;
-      s_c[1024 * x + tid] = e < nent ? (ld[x] + kCellUnit - 1) / kCellUnit : 0;
-    }
-    __syncthreads();
-    // this thread's run of kPer consecutive entries
-    int32_t run[kPer];
-    int32_t mine = 0;
-#pragma unroll
-    for (int x = 0; x < kPer; ++x) {
-      run[x] = s_c[tid * kPer + x];
-      mine += run[x];
-    }
-    int incl = mine;                             // exclusive prefix: in the wave, then over the 16 waves
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int up = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += up;
-    }
-    if (lane == kWave - 1) s_wave[wave] = incl;
-    __syncthreads();
-    int32_t pos = base + incl - mine;
-    int32_t tot = 0;
-    for (int w = 0; w < 16; ++w) {
-      pos += w < wave ? s_wave[w] : 0;
-      tot += s_wave[w];
-    }
-#pragma unroll
-    for (int x = 0; x < kPer; ++x) {
-      s_c[tid * kPer + x] = pos;
-      pos += run[x];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int x = 0; x < kPer; ++x) {
-      const int64_t e = c0 + 1024 * x + tid;
-      if (e < nent) first[e] = s_c[1024 * x + tid];
-    }
-    base += tot;
-    __syncthreads();                             // s_c and s_wave are rewritten by the next chunk
-  }
-  if (tid == 0) *nunits = base;
-}
-
 __global__ __launch_bounds__(256) void cell_fill_kernel(const uint32_t* __restrict__ bits,
-                                                        const int32_t* __restrict__ cnt,
-                                                        const int32_t* __restrict__ first, int64_t nblk, int nw,
-                                                        int64_t ncell, int64_t nent, int2* __restrict__ units,
-                                                        int32_t* __restrict__ rows) {
+                                                        const int32_t* __restrict__ cnt, int64_t nblk, int nw,
+                                                        int64_t ncell, int64_t nent, int64_t cap,
+                                                        int2* __restrict__ units, int32_t* __restrict__ rows,
+                                                        int32_t* __restrict__ nunits) {
   const int lane = threadIdx.x % kWave;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
   if (e >= nent) return;                         // whole wave leaves
   const int64_t bh = e / ncell, c = e % ncell;
   const uint32_t* brow = bits + (bh * nblk + c) * nw;
   const int n = cnt[e];
-  const int32_t u0 = first[e];
+  // units of the head's earlier cells
+  int before = 0;
+  for (int64_t x = lane; x < c; x += kWave) before += (cnt[bh * ncell + x] + kCellUnit - 1) / kCellUnit;
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) before += __shfl_xor(before, o);
+  const int64_t u0 = bh * cap + before;
   const int m = (n + kCellUnit - 1) / kCellUnit;
+  if (c == ncell - 1 && lane == 0) nunits[bh] = before + m;
   int32_t* rw = rows + static_cast<int64_t>(u0) * kCellUnit;
   for (int x = n + lane; x < m * kCellUnit; x += kWave) rw[x] = -1;
   for (int j = lane; j < m; j += kWave) units[u0 + j] = make_int2(static_cast<int>(e), j);
@@ -246,7 +193,8 @@ template <int D, int NT>
 __global__ __launch_bounds__(256) void attn_cell_partial_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ logg, const int2* __restrict__ units,
-    const int32_t* __restrict__ rows, const int32_t* __restrict__ nunits, int64_t ncell, int Hq, int Hkv, int Hsel,
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ nunits, int64_t cap, int64_t nheads, int64_t ncell,
+    int Hq, int Hkv, int Hsel,
     int nq, int64_t L, int K, __bf16* __restrict__ cell_o, float2* __restrict__ cell_ml) {
   constexpr int kVPitch = kKT + 8;
   constexpr int kKS = D / 16;
@@ -257,7 +205,7 @@ __global__ __launch_bounds__(256) void attn_cell_partial_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hl = lane >> 5, ql = lane & 31;
   const int64_t u = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  if (u >= *nunits) return;                      // whole wave leaves; no workgroup barrier below
+  if (u >= nheads * cap || u % cap >= nunits[u / cap]) return;   // whole wave leaves; no workgroup barrier below
   const int2 unit = units[u];
   const int r0 = rows[u * kCellUnit + ql];       // -1 past the cell's last row
   const int64_t e = unit.x;
@@ -913,13 +861,12 @@ static bool use_sas_cell_path(const AttnLaunch& p) {
 struct CellWs {
   uint32_t* bits;      // [B Hsel, nblk, nw] row-selected-cell bitmap
   int32_t* cnt;        // [B Hsel ncell] selecting rows per cell
-  int32_t* first;      // [B Hsel ncell] index of the cell's first unit
-  int2* units;         // [max_units] (head * ncell + cell, tile of 32 rows)
-  int32_t* rows;       // [max_units, 32] the units' rows, -1 past a cell's last row
-  int32_t* nunits;
+  int2* units;         // [B Hsel, cap] (head * ncell + cell, tile of 32 rows)
+  int32_t* rows;       // [B Hsel, cap, 32] the units' rows, -1 past a cell's last row
+  int32_t* nunits;     // [B Hsel] units of each head
   __bf16* o;           // [B, Hq, nq, K, d] per-(row, slot) normalised o of the cell
   float2* ml;          // [B, Hq, nq, K] (max, sum), log2 domain
-  int64_t nblk, ncell, max_units;
+  int64_t nblk, ncell, cap, max_units;
   int nw;
   size_t bytes;
 };
@@ -931,16 +878,16 @@ static CellWs cell_ws(const AttnLaunch& p, void* ws) {
   w.ncell = num_candidates(p.q_pos0 + p.nq - 1, p.b, p.prefix_mode, p.qblock);
   const int64_t heads = static_cast<int64_t>(p.B) * p.Hsel;
   const int64_t nent = heads * (w.ncell > 0 ? w.ncell : 1);
-  // units: one partial tile per (head, cell) at most, plus one per 32 (row, cell) marks
-  w.max_units = nent + (heads * p.nq * p.K + kCellUnit - 1) / kCellUnit;
+  // units of a head: one partial tile per cell at most, plus one per 32 (row, cell) marks
+  w.cap = (w.ncell > 0 ? w.ncell : 1) + (static_cast<int64_t>(p.nq) * p.K + kCellUnit - 1) / kCellUnit;
+  w.max_units = heads * w.cap;
   const size_t parts = static_cast<size_t>(p.B) * p.Hq * p.nq * p.K;
-  constexpr int kParts = 8;
+  constexpr int kParts = 7;
   const size_t sz[kParts] = {static_cast<size_t>(heads) * w.nblk * w.nw * sizeof(uint32_t),
-                             static_cast<size_t>(nent) * sizeof(int32_t),
                              static_cast<size_t>(nent) * sizeof(int32_t),
                              static_cast<size_t>(w.max_units) * sizeof(int2),
                              static_cast<size_t>(w.max_units) * kCellUnit * sizeof(int32_t),
-                             sizeof(int32_t),
+                             static_cast<size_t>(heads) * sizeof(int32_t),
                              parts * p.d * sizeof(__bf16),
                              parts * sizeof(float2)};
   char* base = static_cast<char*>(ws);
@@ -952,12 +899,11 @@ static CellWs cell_ws(const AttnLaunch& p, void* ws) {
   }
   w.bits = reinterpret_cast<uint32_t*>(base + off[0]);
   w.cnt = reinterpret_cast<int32_t*>(base + off[1]);
-  w.first = reinterpret_cast<int32_t*>(base + off[2]);
-  w.units = reinterpret_cast<int2*>(base + off[3]);
-  w.rows = reinterpret_cast<int32_t*>(base + off[4]);
-  w.nunits = reinterpret_cast<int32_t*>(base + off[5]);
-  w.o = reinterpret_cast<__bf16*>(base + off[6]);
-  w.ml = reinterpret_cast<float2*>(base + off[7]);
+  w.units = reinterpret_cast<int2*>(base + off[2]);
+  w.rows = reinterpret_cast<int32_t*>(base + off[3]);
+  w.nunits = reinterpret_cast<int32_t*>(base + off[4]);
+  w.o = reinterpret_cast<__bf16*>(base + off[5]);
+  w.ml = reinterpret_cast<float2*>(base + off[6]);
   w.bytes = total;
   return w;
 }
@@ -966,7 +912,7 @@ size_t attn_tile_fwd_workspace_bytes(const AttnLaunch& p) {
   return (use_cell_path(p) || use_sas_cell_path(p)) ? cell_ws(p, nullptr).bytes : 0;
 }
 
-// The cell-major branch L: mark, count, scan and fill build the units, then
+// The cell-major branch L: mark, count and fill build the units, then
 // attn_cell_partial_kernel writes the per-(row, slot) partials into the workspace.
 template <int D>
 static hipError_t launch_cell_partials(const AttnLaunch& p, void* ws, hipStream_t st, const __bf16** cell_o,
@@ -985,12 +931,8 @@ static hipError_t launch_cell_partials(const AttnLaunch& p, void* ws, hipStream_
     e = launch(false, cell_count_kernel, dim3(wave_grid), dim3(256), st, static_cast<const uint32_t*>(w.bits), w.nblk,
                w.nw, ncell, heads, w.cnt);
     if (e != hipSuccess) return e;
-    e = launch(false, cell_scan_kernel, dim3(1), dim3(1024), st, static_cast<const int32_t*>(w.cnt), nent, w.first,
-               w.nunits);
-    if (e != hipSuccess) return e;
     e = launch(false, cell_fill_kernel, dim3(wave_grid), dim3(256), st, static_cast<const uint32_t*>(w.bits),
-               static_cast<const int32_t*>(w.cnt), static_cast<const int32_t*>(w.first), w.nblk, w.nw, ncell, nent,
-               w.units, w.rows);
+               static_cast<const int32_t*>(w.cnt), w.nblk, w.nw, ncell, nent, w.cap, w.units, w.rows, w.nunits);
     if (e != hipSuccess) return e;
     const dim3 ugrid(static_cast<unsigned>((w.max_units + 3) / 4));     // one unit per wave
     const auto* q = static_cast<const __bf16*>(p.q);
@@ -1000,9 +942,9 @@ static hipError_t launch_cell_partials(const AttnLaunch& p, void* ws, hipStream_
     const auto* rw = static_cast<const int32_t*>(w.rows);
     const auto* nu = static_cast<const int32_t*>(w.nunits);
     e = p.b == 32 ? launch(false, attn_cell_partial_kernel<D, 1>, ugrid, dim3(256), st, q, kk, vv, p.idx, p.logg, un,
-                           rw, nu, ncell, p.Hq, p.Hkv, p.Hsel, p.nq, p.L, p.K, w.o, w.ml)
+                           rw, nu, w.cap, heads, ncell, p.Hq, p.Hkv, p.Hsel, p.nq, p.L, p.K, w.o, w.ml)
                   : launch(false, attn_cell_partial_kernel<D, 2>, ugrid, dim3(256), st, q, kk, vv, p.idx, p.logg, un,
-                           rw, nu, ncell, p.Hq, p.Hkv, p.Hsel, p.nq, p.L, p.K, w.o, w.ml);
+                           rw, nu, w.cap, heads, ncell, p.Hq, p.Hkv, p.Hsel, p.nq, p.L, p.K, w.o, w.ml);
     if (e != hipSuccess) return e;
   }
   *cell_o = w.o;

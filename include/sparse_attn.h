@@ -105,12 +105,12 @@ int spa_abi_version(void);
  * call whether or not it launches.  Do not use under graph capture.
  * Kernels per call: summaries 1; score_select 2 on the decode path (chunk
  * scoring, merge), else 1; attn_fwd 2 on the decode path (tile partials,
- * combine), 6 for many rows in the window mode with routed cells of 32 or 64
- * keys (mark, count, scan, fill, cell partials, window tiles; 2 when no row
- * has a candidate cell: mark, window tiles), else 1; attn_bwd 3 (D, dq and
- * dg, dk and dv); decode_step 3
- * (chunk scoring, merge + attention partials, combine), or the kernels of
- * score_select then attn_fwd where the merge is not folded in; forest_build
+ * combine), 5 for many rows where the selected units go block-major (mark,
+ * count, fill, cell partials, tiles; 2 when no row has a candidate unit:
+ * mark, tiles), else 1; attn_bwd 4 for bf16 with many rows (D, mark, dq and dg,
+ * dk and dv), else 3 (D, dq and dg, dk and dv); decode_step 2 (scoring,
+ * selection + attention + combine), or the kernels of score_select then
+ * attn_fwd where the selection is not folded in; forest_build
  * 4 plus one per forest level above the first; forest_select, retain_cells,
  * score_select_subset, quantize / dequantize_summaries_fp8 1; select_bwd one
  * per stage it runs.
