@@ -632,6 +632,36 @@ def run_train(reps):
                 bwd_exec_tflop=14 * cfg["d"] * pairs / 1e12)
 
 
+def run_sas_fwd_long(n=32768, reps=3):
+    """SAS forward (selection, then attention) on one sequence of n tokens with
+    the train workload's heads (32 query / 8 kv, d = 128, b = 64, K = 16,
+    gate on); device-side seeded N(0, 1) bf16 inputs.  At this length a row
+    tile's union of selections is ~15x the kept blocks, so the attention runs
+    block-major (selected blocks as per-(row, slot) partials)."""
+    cfg = config("train")
+    Hq, Hkv, d, b, K = cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["b"], cfg["K"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg["seed"] * 7919 + n)
+    q = torch.randn((1, Hq, n, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((1, Hkv, n, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((1, Hkv, n, d), generator=g, device="cuda").to(torch.bfloat16)
+    kb, mx, ce = ops.sparse_block_summaries(k, b)
+    idx, logg, _ = ops.sparse_score_select(q, kb, mx, ce, Hkv=Hkv, b=b, K=K, q_pos0=0, gate=True)
+    ws = ops.Workspace()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(reps + 1):
+        torch.cuda._sleep(1_000_000)
+        e0.record()
+        ops.sparse_attn_fwd(q, k, v, idx, logg, b=b, K=K, q_pos0=0, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts[1:]))
+    pairs = sum(i % b + 1 + min(K, i // b) * b for i in range(n)) * Hq
+    return dict(ms=ms, tflop=4 * d * pairs / 1e12)
+
+
 def run_fsl_decode(steps, n_layers=4, n_queries=32):
     """FS-L decode at 512K tokens with the cell-routing head geometry (16
     heads, d = 64, 32-token cells, query blocks of 128, K = 4, window 512):
@@ -1041,6 +1071,9 @@ def main():
         tr = run_train(2)
         out["train_tokens_per_s"] = round(tr["tokens_per_s"], 1)
         out["train_ms"] = {k: round(v, 3) for k, v in tr["ms"].items()}
+        sl = run_sas_fwd_long()
+        out["sas_fwd_32k_ms"] = round(sl["ms"], 3)
+        out["sas_fwd_32k_mfma_frac"] = round(sl["tflop"] / (sl["ms"] * 1e-3) / BF16_PEAK_TFLOPS, 5)
         # algorithmic flops / time / dense bf16 peak (the kernels also execute
         # masked tile work: the union of a row tile's selections)
         out["mfma_frac"] = {
