@@ -395,7 +395,7 @@ struct DkvSmem {
 };
 
 template <int D>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_tile_dkdv_kernel(
+__global__ __launch_bounds__(256, 2) void attn_tile_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dbuf,
     const int32_t* __restrict__ idx, const float* __restrict__ logg, const uint32_t* __restrict__ bits,
@@ -431,13 +431,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_tile_dkdv_kernel(
         *reinterpret_cast<const uint4*>(v + kvbase + key * D + cv * 8);
   }
   __syncthreads();
-  // B operands K^T, V^T: lane = key ql, k-slice 16 ks + 8 hl .. +7 (kept in registers)
-  uint4 kreg[kKS], vreg[kKS];
-#pragma unroll
-  for (int ks = 0; ks < kKS; ++ks) {
-    kreg[ks] = *reinterpret_cast<const uint4*>(&sm.k[ql * DkvSmem<D>::kKPitch + 16 * ks + 8 * hl]);
-    vreg[ks] = *reinterpret_cast<const uint4*>(&sm.v[ql * DkvSmem<D>::kKPitch + 16 * ks + 8 * hl]);
-  }
+  // B operands K^T, V^T: lane = key ql, k-slice 16 ks + 8 hl .. +7, read from
+  // the LDS tile per row tile (held in registers they would take 64 VGPRs and
+  // leave room for one wave per SIMD at d = 128)
+  const __bf16* krow_l = &sm.k[ql * DkvSmem<D>::kKPitch + 8 * hl];
+  const __bf16* vrow_l = &sm.v[ql * DkvSmem<D>::kKPitch + 8 * hl];
   const int mykey = key0 + ql;
 
   bfloatx16_t dka[kDB], dva[kDB];
@@ -560,8 +558,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_tile_dkdv_kernel(
       }
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b_as_bf16x8(qa[ks]), b_as_bf16x8(kreg[ks]), s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b_as_bf16x8(da[ks]), b_as_bf16x8(vreg[ks]), dp, 0, 0, 0);
+        const uint4 kb = *reinterpret_cast<const uint4*>(krow_l + 16 * ks);
+        const uint4 vb = *reinterpret_cast<const uint4*>(vrow_l + 16 * ks);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b_as_bf16x8(qa[ks]), b_as_bf16x8(kb), s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b_as_bf16x8(da[ks]), b_as_bf16x8(vb), dp, 0, 0, 0);
       }
       wave_lds_sync();
       float pr[16], ds[16];
