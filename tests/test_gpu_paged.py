@@ -14,7 +14,7 @@ import torch
 import oracle
 from block_sparse_attention_summaries_amd import ops
 from block_sparse_attention_summaries_amd.inputs import config, f32_to_bf16_bits, make_inputs
-from tests.gpu_util import dev, host
+from tests.gpu_util import dev, host, rel_err
 from tests.test_gpu_parity import _check_decode_chain
 
 pytestmark = pytest.mark.gpu
@@ -148,3 +148,36 @@ def test_paged_decode_512k_full_size():
     for key in ("idx", "keff", "o", "lse"):
         assert np.array_equal(paged[key], contig[key]), key
     _say(f"  exempt rows {ex}")
+
+
+def test_paged_decode_with_unmapped_selected_block():
+    """A selected block whose page id lies outside the pool is attended as
+    empty: the selection (from the summaries the caller passes) is unchanged,
+    and o / lse equal the oracle's attention with that block left out of every
+    head's selection."""
+    cfg = config("decode_32k", n=4096, K=8, seed=88)
+    _say("[paged decode] unmapped selected block")
+    x = make_inputs(cfg)
+    b, L, K = cfg["b"], x["L"], cfg["K"]
+    nblk_full = L // b
+    kw = dict(Hkv=cfg["Hkv"], b=b, K=K, q_pos0=x["q_pos0"], gate=cfg["gate"], share_group=cfg["share_group"])
+    (kp, vp), table, npages = _paginate([x["k"], x["v"]], b, seed=89)
+    qd, kpd, vpd = dev(x["q"]), dev(kp), dev(vp)
+    kb, mx, ce = ops.sparse_block_summaries(dev(x["k"]), b, num_blocks=nblk_full, ccap=nblk_full)
+    idx0, logg0, _, _, _ = ops.sparse_decode_step_paged(qd, kb, mx, ce, kpd, vpd, dev(table), L, **kw)
+    torch.cuda.synchronize()
+    idx0 = host(idx0)
+    c_drop = int(idx0[0, 0, 0, 0])
+    assert 0 <= c_drop < nblk_full
+    table[0, c_drop] = npages + 3
+    idx1, logg1, _, o1, lse1 = ops.sparse_decode_step_paged(qd, kb, mx, ce, kpd, vpd, dev(table), L, **kw)
+    torch.cuda.synchronize()
+    idx1, logg1 = host(idx1), host(logg1)
+    assert np.array_equal(idx1, idx0)
+    idx_kept = np.where(idx1 == c_drop, -1, idx1).astype(np.int32)
+    o_ref, lse_ref = oracle.attn_fwd(x["q"], x["k"], x["v"], idx_kept, logg1.astype(np.float64), b=b, K=K,
+                                     q_pos0=x["q_pos0"], share_group=cfg["share_group"])
+    err = rel_err(host(o1), o_ref)
+    assert err <= 2e-2, err
+    assert np.abs(host(lse1) - lse_ref).max() <= 2e-1
+    _say(f"  block {c_drop} unmapped: o rel err {err:.2e}")
