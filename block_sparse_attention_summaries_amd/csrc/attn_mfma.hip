@@ -343,6 +343,160 @@ __global__ __launch_bounds__(256) void attn_cell_partial_kernel(
   }
 }
 
+// One unit per workgroup when the group has four query heads: wave g takes
+// head g of the group.  The unit's rows and their slots are looked up once
+// and the cell's K rows and V^T staged once in LDS for the four waves
+// (attn_cell_partial_kernel stages them per wave, for four units).  Per head
+// the arithmetic is that of attn_cell_partial_kernel.
+template <int D, int NT>
+__global__ __launch_bounds__(256, 2) void attn_unit_partial_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const int32_t* __restrict__ idx, const float* __restrict__ logg, const int2* __restrict__ units,
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ nunits, int64_t cap, int64_t nheads, int64_t ncell,
+    int Hq, int Hkv, int Hsel, int nq, int64_t L, int K, __bf16* __restrict__ cell_o, float2* __restrict__ cell_ml) {
+  constexpr int kKPitch = D + 8;                    // K rows (bf16)
+  constexpr int kVPitch = kKT + 8;                  // V^T rows: the keys of one tile
+  constexpr int kKS = D / 16;
+  constexpr int kDB = D / 32;
+  constexpr int b = NT * kKT;                       // keys of a cell
+  __shared__ __align__(16) __bf16 s_k[b * kKPitch];
+  __shared__ __align__(16) __bf16 s_vt[NT][D * kVPitch];
+  __shared__ int s_row[32];
+  __shared__ int s_slot[32];
+  __shared__ float s_bias[32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, ql = lane & 31;
+  const int64_t u = blockIdx.x;
+  if (u >= nheads * cap || u % cap >= nunits[u / cap]) return;   // the whole workgroup leaves
+  const int2 unit = units[u];
+  const int64_t e = unit.x;
+  const int64_t bkv = e / ncell;                 // Hsel == Hkv: the selection head is the kv head
+  const int c = static_cast<int>(e % ncell);
+  const int bi = static_cast<int>(bkv / Hkv), kvh = static_cast<int>(bkv % Hkv);
+  const int G = Hq / Hkv;
+  const int64_t kvbase = (static_cast<int64_t>(bi) * Hkv + kvh) * L * D;
+  // the cell's K rows and V^T (V staged transposed, one tile of keys per slice)
+  for (int x = tid; x < b * (D / 8); x += 256) {
+    const int kr = x / (D / 8), cv = x % (D / 8);
+    int64_t key = static_cast<int64_t>(c) * b + kr;
+    key = key < L ? key : L - 1;
+    *reinterpret_cast<uint4*>(&s_k[kr * kKPitch + cv * 8]) =
+        *reinterpret_cast<const uint4*>(k + kvbase + key * D + cv * 8);
+    const uint4 vw = *reinterpret_cast<const uint4*>(v + kvbase + key * D + cv * 8);
+    uint16_t* vt = reinterpret_cast<uint16_t*>(s_vt[kr / kKT]) + (cv * 8) * kVPitch + kr % kKT;
+    vt[0 * kVPitch] = static_cast<uint16_t>(vw.x);
+    vt[1 * kVPitch] = static_cast<uint16_t>(vw.x >> 16);
+    vt[2 * kVPitch] = static_cast<uint16_t>(vw.y);
+    vt[3 * kVPitch] = static_cast<uint16_t>(vw.y >> 16);
+    vt[4 * kVPitch] = static_cast<uint16_t>(vw.z);
+    vt[5 * kVPitch] = static_cast<uint16_t>(vw.z >> 16);
+    vt[6 * kVPitch] = static_cast<uint16_t>(vw.w);
+    vt[7 * kVPitch] = static_cast<uint16_t>(vw.w >> 16);
+  }
+  // the unit's rows, the cell's slot (first match) and gate in each row's selection
+  if (tid < 32) {
+    const int r0 = rows[u * kCellUnit + tid];    // -1 past the cell's last row
+    const int rfirst = rows[u * kCellUnit];      // a unit holds at least one row
+    const int r = r0 >= 0 ? r0 : rfirst;
+    const int64_t so = ((static_cast<int64_t>(bi) * Hsel + kvh) * nq + r) * K;
+    int slot = -1;
+    float lg = 0.f;
+    for (int t = 0; t < K; ++t) {
+      const int32_t it = idx[so + t];
+      const float lt = logg != nullptr ? logg[so + t] : 0.f;
+      if (slot < 0 && it == c) {
+        slot = t;
+        lg = lt;
+      }
+    }
+    s_row[tid] = r0 >= 0 ? r : -1 - r;           // -1 - r: a padding lane reads row r, writes nothing
+    s_slot[tid] = slot < 0 ? 0 : slot;
+    s_bias[tid] = lg * kLog2e;
+  }
+  __syncthreads();
+  const int rs = s_row[ql];
+  const bool ok = rs >= 0;
+  const int r = ok ? rs : -1 - rs;
+  const int slot = s_slot[ql];
+  const float bias = s_bias[ql];
+  const float scale2 = kLog2e / sqrtf(static_cast<float>(D));
+  const int h = kvh * G + wave;
+  uint4 qreg[kKS];
+  const __bf16* qrow = q + ((static_cast<int64_t>(bi) * Hq + h) * nq + r) * D;
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) qreg[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hl);
+  floatx16_t acc[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) acc[db][x] = 0.f;
+  float m2 = -INFINITY, lsum = 0.f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    // S^T = K Q^T: this lane's row, keys tile_key(x, hl) of the tile
+    floatx16_t st;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) st[x] = 0.f;
+    const __bf16* krow = &s_k[(t * kKT + perm_row(ql)) * kKPitch + 8 * hl];
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks)
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(krow + 16 * ks)),
+                                                   as_bf16x8(qreg[ks]), st, 0, 0, 0);
+    float z[16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      z[x] = fmaf(st[x], scale2, bias);
+      mt = fmaxf(mt, z[x]);
+    }
+    mt = fmaxf(mt, xor_lanes_f<32>(mt));
+    const float mnew = fmaxf(m2, mt);
+    const float msub = mnew == -INFINITY ? 0.f : mnew;
+    const float corr = __builtin_amdgcn_exp2f(m2 - msub);
+    float p[16], ps = 0.f;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      p[x] = __builtin_amdgcn_exp2f(z[x] - msub);
+      ps += p[x];
+    }
+    ps += xor_lanes_f<32>(ps);
+    lsum = lsum * corr + ps;
+    m2 = mnew;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) acc[db][x] *= corr;
+    // O^T += V^T P^T
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      bf16x8_t pb;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) pb[x] = static_cast<__bf16>(p[8 * s2 + x]);
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&s_vt[t][(32 * db + ql) * kVPitch + 16 * s2 + 8 * hl]);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb, acc[db], 0, 0, 0);
+      }
+    }
+  }
+  if (ok) {
+    const int64_t pr = ((static_cast<int64_t>(bi) * Hq + h) * nq + r) * K + slot;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    // O^T register x of block db holds d = 32 db + 8 (x / 4) + 4 hl + (x % 4)
+    __bf16* orow = cell_o + pr * D;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 w4;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) w4[x] = static_cast<__bf16>(acc[db][4 * a4 + x] * inv);
+        *reinterpret_cast<decltype(w4)*>(orow + 32 * db + 8 * a4 + 4 * hl) = w4;
+      }
+    if (hl == 0) cell_ml[pr] = make_float2(m2, lsum);
+  }
+}
+
 // kMode 0: selected blocks (SAS); 1: routed cells walked per row tile + window;
 // 2: window walk only, branch L merged from attn_cell_partial_kernel's
 // per-(row, slot) partials (cell_o / cell_ml); 3: SAS with the selected
@@ -934,6 +1088,23 @@ static hipError_t launch_cell_partials(const AttnLaunch& p, void* ws, hipStream_
     e = launch(false, cell_fill_kernel, dim3(wave_grid), dim3(256), st, static_cast<const uint32_t*>(w.bits),
                static_cast<const int32_t*>(w.cnt), w.nblk, w.nw, ncell, nent, w.cap, w.units, w.rows, w.nunits);
     if (e != hipSuccess) return e;
+    if (p.Hq / p.Hkv == 4) {                      // one unit per workgroup, one head per wave
+      const dim3 wgrid(static_cast<unsigned>(w.max_units));
+      e = p.b == 32 ? launch(false, attn_unit_partial_kernel<D, 1>, wgrid, dim3(256), st,
+                             static_cast<const __bf16*>(p.q), static_cast<const __bf16*>(p.k),
+                             static_cast<const __bf16*>(p.v), p.idx, p.logg, static_cast<const int2*>(w.units),
+                             static_cast<const int32_t*>(w.rows), static_cast<const int32_t*>(w.nunits), w.cap,
+                             heads, ncell, p.Hq, p.Hkv, p.Hsel, p.nq, p.L, p.K, w.o, w.ml)
+                    : launch(false, attn_unit_partial_kernel<D, 2>, wgrid, dim3(256), st,
+                             static_cast<const __bf16*>(p.q), static_cast<const __bf16*>(p.k),
+                             static_cast<const __bf16*>(p.v), p.idx, p.logg, static_cast<const int2*>(w.units),
+                             static_cast<const int32_t*>(w.rows), static_cast<const int32_t*>(w.nunits), w.cap,
+                             heads, ncell, p.Hq, p.Hkv, p.Hsel, p.nq, p.L, p.K, w.o, w.ml);
+      if (e != hipSuccess) return e;
+      *cell_o = w.o;
+      *cell_ml = w.ml;
+      return hipSuccess;
+    }
     const dim3 ugrid(static_cast<unsigned>((w.max_units + 3) / 4));     // one unit per wave
     const auto* q = static_cast<const __bf16*>(p.q);
     const auto* kk = static_cast<const __bf16*>(p.k);
