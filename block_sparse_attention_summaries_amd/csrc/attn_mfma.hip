@@ -72,9 +72,10 @@ constexpr float kLazyMax = 8.0f;
 // sets one bit per (selection head, cell, row) for "the row selected the
 // cell"; the count and fill kernels turn the bitmap into units of 32
 // selecting rows of one cell (row order); attn_cell_partial_kernel takes one
-// unit per wave and writes for each (row, slot of the cell in the row's
-// selection) the softmax of the row over the cell's keys: o normalised (bf16)
-// and (max, sum) in the log2 domain.  The tile kernel then runs the window
+// unit per wave (attn_unit_partial_kernel one unit per workgroup, a wave per
+// query head, when a group has four heads) and writes for each (row, slot of
+// the cell in the row's selection) the softmax of the row over the cell's
+// keys: o normalised (bf16) and (max, sum) in the log2 domain.  The tile kernel then runs the window
 // branch only and merges a row's partials into o_L before the mix.
 
 // One workgroup per (selection head, 256 rows = 8 bitmap words): the slice
