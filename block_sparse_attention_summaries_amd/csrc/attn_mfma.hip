@@ -997,9 +997,10 @@ static bool use_cell_path(const AttnLaunch& p) {
 // walk would waste the most: a 32-row tile walks the union of its rows'
 // selected blocks (at most the prefix, at most 32 K blocks) plus the current
 // one, while a row keeps K + 1.  Measured at 32 query / 8 kv heads, d = 128,
-// b = 64, K = 16 (forward ms, masked tiles vs block-major): 4 x 8K (union /
-// kept 3.8) 3.7 vs 5.4; 1 x 32K (15.1) 10.2 vs 5.8; 1 x 64K (30.1) 27.3 vs
-// 12.0.  The partials (K d bf16 per row and query head, written and read
+// b = 64, K = 16 (forward ms, masked tiles vs block-major with the per-wave
+// partial kernel): 4 x 8K (union / kept 3.8) 3.7 vs 5.4; 1 x 32K (15.1) 10.2
+// vs 5.8; 1 x 64K (30.1) 27.3 vs 12.0 (5.1 and 10.6 with the per-workgroup
+// one).  The partials (K d bf16 per row and query head, written and read
 // back) and the per-slot q reads are what the block-major form pays.
 constexpr double kSasBlockMajorWaste = 7.0;   // the measured break-even, interpolated
 static double sas_masked_waste(const AttnLaunch& p) {
