@@ -506,7 +506,7 @@ static bool use_decode_path(const SelectLaunch& p) {
 }
 
 size_t select_workspace_bytes(const SelectLaunch& p) {
-  if (!use_decode_path(p)) return 0;
+  if (!use_decode_path(p)) return rows_select_mfma_supported(p) ? rows_select_mfma_ws_bytes(p) : 0;
   return decode_select_ws(p, nullptr).bytes;
 }
 
@@ -601,7 +601,7 @@ hipError_t launch_score_select(const SelectLaunch& p, void* ws, hipStream_t st) 
     if (p.dtype == 1) return p.d == 64 ? launch_decode_t<bf16_t, 64>(p, ws, st) : launch_decode_t<bf16_t, 128>(p, ws, st);
     return p.d == 64 ? launch_decode_t<float, 64>(p, ws, st) : launch_decode_t<float, 128>(p, ws, st);
   }
-  if (rows_select_mfma_supported(p)) return launch_rows_select_mfma(p, st);
+  if (rows_select_mfma_supported(p)) return launch_rows_select_mfma(p, ws, st);
   if (p.dtype == 1) return p.d == 64 ? launch_rows_t<bf16_t, 64>(p, st) : launch_rows_t<bf16_t, 128>(p, st);
   return p.d == 64 ? launch_rows_t<float, 64>(p, st) : launch_rows_t<float, 128>(p, st);
 }

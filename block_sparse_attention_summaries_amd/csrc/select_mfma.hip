@@ -118,6 +118,67 @@ __device__ __forceinline__ void first_tile_list(const float (&sv)[16], int c_lan
   }
 }
 
+// Per-head tables of the FreeSolo filter erf((i - p_c)/(2 sigma_h)).  With
+// the centres at the cell middles p_c = c b + (b - 1)/2 the argument is
+// x_j = (j - (b - 1)/2)/(2 sigma) for the integer j = i - c b, so the filter
+// is a function of j.  tab64 holds erf_exact(x_j) for j in [-neg, n64 - neg)
+// (entry j + neg): the fp64 value the exact re-score uses, with x formed as
+// it forms it.  tab32 holds the same values rounded to fp32 for the MFMA walk,
+// laid out by residue: j = (q - qoff) b + res sits at res * qs + q, so the
+// 16 candidates a lane scores in one tile (cells c0 + m, m in four runs of
+// four) are four runs of neighbouring entries at fixed offsets from one base.
+// From jsat on (x >= 4) every fp32 entry is 1 (1 - erf(4) < 2^-25).
+constexpr int kTab32Cap = 8192;           // fp32 entries per head (32 KB of LDS in the scorer)
+constexpr int kTab64Cap = 16384;          // fp64 entries per head
+constexpr size_t kErfTabBytes = kTab32Cap * sizeof(float) + kTab64Cap * sizeof(double);
+
+struct ErfTabGeom {
+  int neg, qoff, qs, n64, jsat;
+  bool ok32, ok64;
+};
+
+// The same arithmetic in the table kernel and the scorer.  j >= -neg covers
+// every (row, cell) pair a tile walk forms (cells up to one tile past a row's
+// candidates); tab32 reaches 32 b + 64 past jsat, the farthest pair of a tile
+// that is not wholly past jsat; tab64 reaches x = 6, past which erf_exact is 1.
+__device__ __forceinline__ ErfTabGeom erf_tab_geom(int b, float sigma) {
+  ErfTabGeom g;
+  const double hb = 0.5 * static_cast<double>(b - 1);
+  const double x4 = hb + 8.0 * static_cast<double>(sigma);
+  const double x6 = hb + 12.0 * static_cast<double>(sigma);
+  g.neg = 40 * b + 64;
+  g.qoff = (g.neg + b - 1) / b + 1;
+  const bool fin4 = x4 < static_cast<double>(1 << 20), fin6 = x6 < static_cast<double>(1 << 20);
+  g.jsat = fin4 ? static_cast<int>(ceil(x4)) : 0x7FFFFFFF;
+  g.qs = fin4 ? (((g.jsat + 32 * b + 64) / b + g.qoff + 2) | 1) : 0;
+  g.ok32 = fin4 && b * g.qs <= kTab32Cap;
+  g.n64 = fin6 ? g.neg + static_cast<int>(ceil(x6)) + 2 : 0;
+  g.ok64 = fin6 && g.n64 <= kTab64Cap;
+  return g;
+}
+
+// One thread per j = e - neg, e in [0, kTab64Cap): grid (kTab64Cap / 256,
+// Hsel).  A thread evaluates its filter value once and writes it to tab64
+// (e < n64) and, rounded, to its tab32 entry (when j has one; the entries of
+// tab32 below j = -neg are never read).  kTab64Cap - neg covers every j of
+// tab32, since b qs <= kTab32Cap.
+__global__ __launch_bounds__(256) void erf_table_kernel(const float* __restrict__ erf_sigma, int b,
+                                                        float* __restrict__ tab32, double* __restrict__ tab64) {
+  const int hs = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const ErfTabGeom g = erf_tab_geom(b, erf_sigma[hs]);
+  const double hb = 0.5 * static_cast<double>(b - 1);
+  const double inv2sig = 1.0 / (2.0 * static_cast<double>(erf_sigma[hs]));
+  const int j = e - g.neg;
+  const int q = (j >= 0 ? j / b : -((-j + b - 1) / b)) + g.qoff;   // floor(j / b) + qoff
+  const int res = j - (q - g.qoff) * b;
+  const bool in64 = g.ok64 && e < g.n64, in32 = g.ok32 && q >= 0 && q < g.qs;
+  if (!in64 && !in32) return;
+  const double v = erf_exact((static_cast<double>(j) - hb) * inv2sig);
+  if (in64) tab64[static_cast<int64_t>(hs) * kTab64Cap + e] = v;
+  if (in32) tab32[static_cast<int64_t>(hs) * kTab32Cap + res * g.qs + q] = static_cast<float>(v);
+}
+
 // NTERM = 1: one head's bf16 query; NTERM = 3: split group-mean query.
 // List length: KMAX (no erf; fp32 ranking is final) or 2 KMAX (erf).
 template <int D, int KMAX, int NTERM, bool kErf>
@@ -126,23 +187,24 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
     const float* __restrict__ centre, const float* __restrict__ erf_lambda,
     const float* __restrict__ erf_sigma, int Hq, int Hkv, int Hsel, int nq, int64_t q_pos0,
     int64_t ccap, int b, int prefix_mode, int qblock, int share_group, int K, int gate,
-    int32_t* __restrict__ idx, float* __restrict__ logg, int32_t* __restrict__ k_eff) {
+    int32_t* __restrict__ idx, float* __restrict__ logg, int32_t* __restrict__ k_eff,
+    const float* __restrict__ tab32, const double* __restrict__ tab64) {
   constexpr int kT = 32;                  // candidates per tile
   constexpr int kKS = D / 16;             // MFMA k-steps
   constexpr int KL = kErf ? 2 * KMAX : KMAX;
-  constexpr int kErfTab = 6144;           // filter table entries (24 KB): x = 4 within it for sigma <= ~766
   static_assert(!kErf || KL <= 16, "list staging uses 16 LDS slots per lane");
   __shared__ __align__(16) float s_beta32[4][kT];   // per wave: lambda a_c of the tile's candidates
   __shared__ float s_p[4][kT];            // per wave: their centres (filter per score)
   __shared__ float s_sc[4][16][64];       // per wave: candidate slot r x lane
   __shared__ double s_x[4][64];           // per wave: half-row dot products
-  __shared__ float s_erf[kErf ? kErfTab : 1];   // filter erf by row - cell b (see below)
-  __shared__ float s_jl[4];
+  __shared__ __align__(16) float s_erf[kErf ? kTab32Cap : 4];   // the head's tab32 (see erf_tab_geom)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, ql = lane & 31;
-  const int rt = static_cast<int>(gridDim.x) - 1 - static_cast<int>(blockIdx.x);  // long rows first
-  const int bh = blockIdx.y;
+  // x = (batch, selection head), y = row tile from the last: dispatch runs
+  // every head's longest rows first, and a head's workgroups share an XCD
+  const int rt = static_cast<int>(gridDim.y) - 1 - static_cast<int>(blockIdx.y);
+  const int bh = blockIdx.x;
   const int bi = bh / Hsel, hs = bh % Hsel;
   const int G = Hq / Hkv;
   const int kvh = share_group ? hs : hs / G;
@@ -163,43 +225,9 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
   const float* mn = max_norm + (static_cast<int64_t>(bi) * Hkv + kvh) * ccap;
   double lam = 0.0, inv2sig = 0.0;
   float lam32 = 0.f, inv2sig32 = 0.f;
-  bool use_tab = false;
+  bool use_tab = false, use_t64 = false;
+  ErfTabGeom tg{};
   int jsat = 0x7FFFFFFF;
-  if constexpr (kErf) {
-    lam = static_cast<double>(erf_lambda[hs]);
-    lam32 = erf_lambda[hs];
-    inv2sig = 1.0 / (2.0 * static_cast<double>(erf_sigma[hs]));
-    inv2sig32 = static_cast<float>(inv2sig);
-    // With the centres c b + (b - 1) / 2 the filter's argument is
-    // ((row - c b) - (b - 1) / 2) / (2 sigma), both differences exact in fp32:
-    // the filter value is a function of j = row - c b, tabulated in LDS with
-    // the same fp32 arithmetic (bit-identical scores).  j past the table holds
-    // x >= 4, where the filter is 1.  Other centres, or a sigma whose x = 4
-    // lies past the table, take the filter per score.
-    const float hb = static_cast<float>(b - 1) * 0.5f;
-    int ok = 1;
-    for (int64_t c = tid; c < wg_cand; c += 256)
-      ok &= centre[c] == static_cast<float>(c * b) + hb ? 1 : 0;
-    ok &= (static_cast<float>(kErfTab - 1) - hb) * inv2sig32 >= 4.0f ? 1 : 0;
-    ok &= static_cast<int64_t>(wg_cand) * b < (1 << 23) && q_pos0 + nq < (1 << 23) ? 1 : 0;
-    use_tab = __builtin_amdgcn_readfirstlane(__syncthreads_and(ok)) != 0;
-    if (use_tab) {
-      // jsat: every entry from jsat on (and every j past the table) is 1
-      float jl = -1.f;
-      for (int j = tid; j < kErfTab; j += 256) {
-        const float x32 = (static_cast<float>(j) - hb) * inv2sig32;
-        float e = 1.0f;
-        if (x32 < 4.0f) e = erf_filter(x32);
-        s_erf[j] = e;
-        if (e != 1.0f) jl = static_cast<float>(j);
-      }
-      jl = wave_max(jl);
-      if (lane == 0) s_jl[wave] = jl;
-      __syncthreads();
-      jsat = static_cast<int>(fmaxf(fmaxf(s_jl[0], s_jl[1]), fmaxf(s_jl[2], s_jl[3]))) + 1;
-    }
-  }
-
   // this lane's query slices (k = 16 ks + 8 hl .. +7) as NTERM bf16 terms
   uint4 qt[NTERM][kKS];
   float qsq = 0.f;                        // squared norm of this lane's query half
@@ -208,12 +236,6 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
       qt[0][ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hl);
-      if constexpr (kErf) {
-        float f[8];
-        Elem<bf16_t>::unpack(qt[0][ks], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qsq = fmaf(f[e], f[e], qsq);
-      }
     }
   } else {
     float acc[kKS][8];
@@ -253,26 +275,6 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
       for (int t = 0; t < NTERM; ++t) qt[t][ks] = make_uint4(w[t][0], w[t][1], w[t][2], w[t][3]);
     }
   }
-  if constexpr (kErf) qsq += xor_lanes_f<32>(qsq);
-
-  // The walk runs in units of 1/scale (the MFMA's own q.kbar, the bias
-  // staged as lambda a_c / scale); list scores and the gate's max take the
-  // scale once it ends.
-  const float inv_scale = sqrtf(static_cast<float>(D));
-  const float lam_s = lam32 * inv_scale;
-  const float k2 = scale * 1.4426950408889634f;     // exp(x scale) = exp2(x k2)
-  float ls[KL];                           // scores (1/scale units), best first
-  int li[KL];
-  float m_run = -INFINITY, l_run = 0.f;   // gate LSE over this lane's candidates
-  float amax_t = 0.f;                     // lanes 0..31: largest max norm staged
-
-  // Tiles before ncand_min hold valid candidates for every row of the wave;
-  // a tile whose candidates all lie jsat or more before the wave's first row
-  // has erf = 1 for every score (its bias is the accumulator's initial value).
-  const int64_t row0 = static_cast<int64_t>(rt * 4 + wave) * 32;
-  const bool rows_all_ok = __ballot(!row_ok) == 0ull;
-  const int64_t ncand_min = rows_all_ok ? num_candidates(q_pos0 + row0, b, prefix_mode, qblock) : 0;
-
   // Each wave runs on its own (no workgroup barrier in the walk): the lane's
   // A operand (candidate c0 + ql, columns 16 ks + 8 hl .. +7) comes straight
   // from memory, one tile ahead; lanes 0..31 stage the tile's lambda a_c / scale
@@ -291,6 +293,90 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
     }                                                                                         \
   } while (0)
 
+  if (wave_cand > 0) SPA_FETCH_TILE(0);
+
+  // erf setup.  With the centres at the cell middles the filter is a function
+  // of j = row - c b, read from the head's tables (erf_table_kernel); other
+  // centres take the filter per score and erf_exact in the re-score.  Every
+  // load here (the fp32 table, the wave's max norms, the workgroup's centres)
+  // is issued before the first is waited for.
+  float am = 0.f;                         // largest |a_c| over the wave's candidates
+  if constexpr (kErf) {
+    lam = static_cast<double>(erf_lambda[hs]);
+    lam32 = erf_lambda[hs];
+    inv2sig = 1.0 / (2.0 * static_cast<double>(erf_sigma[hs]));
+    inv2sig32 = static_cast<float>(inv2sig);
+    tg = erf_tab_geom(b, erf_sigma[hs]);
+    constexpr int kTL = kTab32Cap / 4 / 256;      // 16-byte table loads per thread
+    const int n4 = tg.ok32 ? (b * tg.qs + 3) / 4 : 0;
+    const float4* src = reinterpret_cast<const float4*>(tab32 + static_cast<int64_t>(hs) * kTab32Cap);
+    float4 tl[kTL];
+#pragma unroll
+    for (int u = 0; u < kTL; ++u) tl[u] = src[tid + 256 * u < n4 ? tid + 256 * u : 0];
+    float av[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int64_t c = lane + 64 * t;
+      av[t] = mn[c < wave_cand ? c : 0];
+    }
+    float cv[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t c = tid + 256 * t;
+      cv[t] = centre[c < wg_cand ? c : 0];
+    }
+    const float hb = static_cast<float>(b - 1) * 0.5f;
+    int ok = 1;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t c = tid + 256 * t;
+      ok &= c >= wg_cand || cv[t] == static_cast<float>(c * b) + hb ? 1 : 0;
+    }
+    for (int64_t c = tid + 512; c < wg_cand; c += 256) ok &= centre[c] == static_cast<float>(c * b) + hb ? 1 : 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if (lane + 64 * t < wave_cand) am = fmaxf(am, fabsf(av[t]));
+    for (int64_t c = lane + 512; c < wave_cand; c += 64) am = fmaxf(am, fabsf(mn[c]));
+    am = wave_max(am);
+    ok &= static_cast<int64_t>(wg_cand) * b < (1 << 23) && q_pos0 + nq < (1 << 23) ? 1 : 0;
+    // the table goes to LDS whether or not the centres allow it (it is read
+    // only when they do); the barrier below publishes it
+#pragma unroll
+    for (int u = 0; u < kTL; ++u)
+      if (tid + 256 * u < n4) reinterpret_cast<float4*>(s_erf)[tid + 256 * u] = tl[u];
+    ok = __builtin_amdgcn_readfirstlane(__syncthreads_and(ok));
+    use_tab = ok != 0 && tg.ok32;
+    use_t64 = ok != 0 && tg.ok64;
+    if (use_tab) jsat = tg.jsat;
+  }
+  if constexpr (kErf && NTERM == 1) {
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      float f[8];
+      Elem<bf16_t>::unpack(qt[0][ks], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qsq = fmaf(f[e], f[e], qsq);
+    }
+  }
+  if constexpr (kErf) qsq += xor_lanes_f<32>(qsq);
+
+  // The walk runs in units of 1/scale (the MFMA's own q.kbar, the bias
+  // staged as lambda a_c / scale); list scores and the gate's max take the
+  // scale once it ends.
+  const float inv_scale = sqrtf(static_cast<float>(D));
+  const float lam_s = lam32 * inv_scale;
+  const float k2 = scale * 1.4426950408889634f;     // exp(x scale) = exp2(x k2)
+  float ls[KL];                           // scores (1/scale units), best first
+  int li[KL];
+  float m_run = -INFINITY, l_run = 0.f;   // gate LSE over this lane's candidates
+
+  // Tiles before ncand_min hold valid candidates for every row of the wave;
+  // a tile whose candidates all lie jsat or more before the wave's first row
+  // has erf = 1 for every score (its bias is the accumulator's initial value).
+  const int64_t row0 = static_cast<int64_t>(rt * 4 + wave) * 32;
+  const bool rows_all_ok = __ballot(!row_ok) == 0ull;
+  const int64_t ncand_min = rows_all_ok ? num_candidates(q_pos0 + row0, b, prefix_mode, qblock) : 0;
+
 #pragma unroll
   for (int t = 0; t < KL; ++t) {
     ls[t] = -INFINITY;
@@ -303,67 +389,39 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
   // max norm a_max, so a score under the lane's current K-th best minus that
   // can be left out; 1/scale units, with 25 % to spare.
   float band = INFINITY;
+  // relative error of the walk's bias lambda a_c erf / scale (taken 4x wider):
+  // the fp32 products and roundings of lambda / scale and a_c, the table's
+  // rounding to fp32 (2^-25), or the per-score filter's 1.2e-6
+  const float bias_rel = use_tab ? 1.4e-6f : 6.2e-6f;
+  // tab32 base of this lane's row: entry of candidate c0 + m is
+  // t_base - c0 + 27 - (m - 4 hl); t_top keeps the 28 entries in the table
+  const int t_base = use_tab ? static_cast<int>(pos % b) * tg.qs + static_cast<int>(pos / b) + tg.qoff - 4 * hl - 27 : 0;
+  const int t_top = use_tab ? b * tg.qs - 28 : 0;
   if constexpr (kErf) {
-    float am = 0.f;
-    for (int64_t c = lane; c < wave_cand; c += 64) am = fmaxf(am, fabsf(mn[c]));
-    am = wave_max(am);
     const float qn = sqrtf(qsq);
     const float sb = qn * am * scale + fabsf(lam32) * am;
-    const float err_max = 5e-6f + 7e-6f * sb + 2.5e-5f * fabsf(lam32) * am +
+    const float err_max = 5e-6f + 2.4e-6f * sb + bias_rel * fabsf(lam32) * am +
                           4.f * static_cast<float>(D * NTERM + 2) * 5.97e-8f * qn * am * scale;
     band = 2.5f * err_max * inv_scale;
   }
   {
-    if (wave_cand > 0) SPA_FETCH_TILE(0);
     for (int64_t c0 = 0; c0 < wave_cand; c0 += kT) {
       if constexpr (kErf) {
         wave_lds_sync();                  // the previous tile's readers are done
         if (hl == 0) {
           s_beta32[wave][ql] = lam_s * pre_a;
           s_p[wave][ql] = pre_p;
-          amax_t = fmaxf(amax_t, fabsf(pre_a));
         }
         wave_lds_sync();
       }
       // register r holds candidate c0 + 8 (r / 4) + 4 hl + (r % 4) of this
-      // lane's row.  The accumulator starts at the bias: lambda a_c / scale
-      // (four 16-byte reads), times the filter erf unless the tile is
-      // saturated; the MFMA adds q.kbar.
+      // lane's row.  The MFMA forms q.kbar from zero; the bias lambda a_c /
+      // scale (four 16-byte reads), times the filter erf unless the tile is
+      // saturated, is added to it after, with one rounding.
       const bool sat = kErf && use_tab && q_pos0 + row0 - (c0 + kT - 1) * b >= jsat;
       sfloatx16_t st;
-      if constexpr (kErf) {
-        float4 bet[4];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          bet[q4] = *reinterpret_cast<const float4*>(&s_beta32[wave][8 * q4 + 4 * hl]);
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          st[4 * q4] = bet[q4].x;
-          st[4 * q4 + 1] = bet[q4].y;
-          st[4 * q4 + 2] = bet[q4].z;
-          st[4 * q4 + 3] = bet[q4].w;
-        }
-        if (!sat) {
-          const int jb = static_cast<int>(pos - (c0 + 4 * hl) * b);   // j of candidate m = 4 hl
-          if (use_tab) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int j = jb - (8 * (r >> 2) + (r & 3)) * b;
-              st[r] *= s_erf[j < 0 ? 0 : (j < kErfTab ? j : kErfTab - 1)];
-            }
-          } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float x32 =
-                  (static_cast<float>(pos) - s_p[wave][8 * (r >> 2) + 4 * hl + (r & 3)]) * inv2sig32;
-              st[r] *= x32 < 4.0f ? erf_filter(x32) : 1.0f;
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[r] = 0.f;
-      }
+      for (int r = 0; r < 16; ++r) st[r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
 #pragma unroll
@@ -372,8 +430,38 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
       }
       if (c0 + kT < wave_cand) SPA_FETCH_TILE(c0 + kT);
       float sv[16];
+      if constexpr (kErf) {
+        float bet[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sv[r] = st[r];
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(&s_beta32[wave][8 * q4 + 4 * hl]);
+          bet[4 * q4] = v4.x;
+          bet[4 * q4 + 1] = v4.y;
+          bet[4 * q4 + 2] = v4.z;
+          bet[4 * q4 + 3] = v4.w;
+        }
+        if (sat) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[r] = st[r] + bet[r];
+        } else if (use_tab) {
+          // tab32 entry of candidate m: t_base - c0 + 27 - (m - 4 hl)
+          int tb = t_base - static_cast<int>(c0);
+          tb = tb < 0 ? 0 : (tb > t_top ? t_top : tb);
+          const float* te = s_erf + tb;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[r] = fmaf(bet[r], te[27 - (8 * (r >> 2) + (r & 3))], st[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float x32 =
+                (static_cast<float>(pos) - s_p[wave][8 * (r >> 2) + 4 * hl + (r & 3)]) * inv2sig32;
+            sv[r] = fmaf(bet[r], x32 < 4.0f ? erf_filter(x32) : 1.0f, st[r]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv[r] = st[r];
+      }
       if (c0 + kT > ncand_min) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -500,18 +588,20 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
     }
   } else {
     // Error bound of an fp32 score against the exact one, for any candidate of
-    // this row: the filter erf and its fp32 argument (<= 1.2e-6 |lambda a_c|);
-    // the MFMA's fp32 accumulation of d NTERM products onto the bias
-    // (<= (d NTERM + 2) 2^-24 (|q| |kbar_c| / sqrt(d) + |lambda a_c|), with
-    // |kbar_c| <= a_c); the bias and scale roundings (<= 2.4e-7 (|score| +
-    // |lambda a_c|)); the first tile's keys (<= 2^-19 |score|, taken as
-    // 2e-6 |score|).  E takes the other terms at least 4x wider.
-    const float amax = wave_max(amax_t);   // every candidate this wave's rows scored
+    // this row: the MFMA's fp32 sum of d NTERM exact products from zero
+    // (<= (d NTERM + 2) 2^-24 |q| |kbar_c| / sqrt(d), with |kbar_c| <= a_c);
+    // the bias lambda a_c erf / scale (relative error <= 3.3e-7 with the
+    // table: the roundings of sqrt(d), lambda / scale, its product with a_c,
+    // the scale and the table's own 2^-25; the per-score filter adds its
+    // 1.2e-6); the fma that adds it and the final scaling (<= 2 2^-24 |score|);
+    // the first tile's keys (<= 15 2^-23 |score|, exact).  E takes the terms
+    // other than the keys' 4x wider.
+    const float amax = am;                 // every candidate this wave's rows scored
     float smax = 0.f;
 #pragma unroll
     for (int t = 0; t < KL; ++t)
       if (li[t] != 0x7FFFFFFF) smax = fmaxf(smax, fabsf(ls[t]));
-    const float err = 5e-6f + 7e-6f * smax + 2.5e-5f * fabsf(lam32) * amax +
+    const float err = 5e-6f + 2.4e-6f * smax + bias_rel * fabsf(lam32) * amax +
                       4.f * static_cast<float>(D * NTERM + 2) * 5.97e-8f * sqrtf(qsq) * amax * scale;
     const float kth32 = ncand >= K ? ls[K - 1] : -INFINITY;
     const float cut = kth32 - 2.f * err;
@@ -556,7 +646,10 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
     const int64_t nsrc = decided ? 0 : (rescan ? ncand : n_ok - m_sure);
     uint4 kv[kKS];
     float cen = 0.f, anorm = 0.f;
+    double t64v = 0.0;                      // tab64 entry of the candidate (when in the table)
+    bool t64ok = false;
     int c = 0;
+    const double* t64 = tab64 + static_cast<int64_t>(hs) * kTab64Cap;
 #define SPA_LOAD_CAND(J)                                                                      \
   do {                                                                                        \
     c = rescan ? static_cast<int>(J) : slot[((J) + m_sure) * 64 + lane];                      \
@@ -564,6 +657,9 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
       kv[ks] = *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(c) * D + 16 * ks + 8 * hl); \
     cen = centre[c];                                                                          \
     anorm = mn[c];                                                                            \
+    const int64_t te = pos - static_cast<int64_t>(c) * b + tg.neg;                            \
+    t64ok = use_t64 && te >= 0 && te < tg.n64;                                                \
+    t64v = t64[t64ok ? te : 0];                                                               \
   } while (0)
     if (nsrc > 0) SPA_LOAD_CAND(0);
 #pragma unroll 1
@@ -589,13 +685,15 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
       }
       const double x = (static_cast<double>(pos) - static_cast<double>(cen)) * inv2sig;
       const double beta = lam * static_cast<double>(anorm);
+      const bool cj_t64 = t64ok;
+      const double cj_erf = t64v;
       if (j + 1 < nsrc) SPA_LOAD_CAND(j + 1);
       s_x[wave][lane] = part;
       wave_lds_sync();
       const double other = s_x[wave][lane ^ 32];
       wave_lds_sync();
       const double dot = hl == 0 ? part + other : other + part;
-      const double sc = dot * inv_sqrt_d + beta * erf_exact(x);
+      const double sc = dot * inv_sqrt_d + beta * (cj_t64 ? cj_erf : erf_exact(x));
       if (sel_better(sc, cj, es[KMAX - 1], ei[KMAX - 1])) topk_push(es, ei, sc, cj);
     }
 #undef SPA_LOAD_CAND
@@ -648,38 +746,54 @@ __global__ __launch_bounds__(256, (kErf && D == 64 && NTERM == 1 && KMAX == 4) ?
 
 bool rows_select_mfma_supported(const SelectLaunch& p) {
   const int kmax = p.erf_lambda != nullptr ? 8 : 32;
-  return p.dtype == 1 && p.proj_w == nullptr && p.K <= kmax && (p.d == 64 || p.d == 128);
+  return p.dtype == 1 && p.proj_w == nullptr && p.K <= kmax && (p.d == 64 || p.d == 128) &&
+         (p.nq + 127) / 128 <= 65535;
+}
+
+// With the erf term: the per-head tables (tab32, then tab64) in the workspace.
+size_t rows_select_mfma_ws_bytes(const SelectLaunch& p) {
+  return p.erf_lambda != nullptr ? static_cast<size_t>(p.Hsel) * kErfTabBytes : 0;
 }
 
 template <int D, int KMAX, int NTERM, bool kErf>
-static hipError_t launch_mfma_k(const SelectLaunch& p, hipStream_t st) {
-  dim3 grid((p.nq + 127) / 128, static_cast<unsigned>(p.B * p.Hsel));
+static hipError_t launch_mfma_k(const SelectLaunch& p, void* ws, hipStream_t st) {
+  float* tab32 = nullptr;
+  double* tab64 = nullptr;
+  if constexpr (kErf) {
+    tab32 = static_cast<float*>(ws);
+    tab64 = reinterpret_cast<double*>(static_cast<char*>(ws) + static_cast<size_t>(p.Hsel) * kTab32Cap * sizeof(float));
+    const hipError_t e = launch(false, erf_table_kernel, dim3(kTab64Cap / 256, static_cast<unsigned>(p.Hsel)),
+                                dim3(256), st, p.erf_sigma, p.b, tab32, tab64);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(static_cast<unsigned>(p.B * p.Hsel), (p.nq + 127) / 128);
   return launch(true, rows_select_mfma_kernel<D, KMAX, NTERM, kErf>, grid, dim3(256), st,
                 static_cast<const __bf16*>(p.q), static_cast<const __bf16*>(p.kbar), p.max_norm, p.centre,
                 p.erf_lambda, p.erf_sigma, p.Hq, p.Hkv, p.Hsel, p.nq, p.q_pos0, p.ccap, p.b, p.prefix_mode,
-                p.qblock, p.share_group, p.K, p.gate, p.idx, p.logg, p.k_eff);
+                p.qblock, p.share_group, p.K, p.gate, p.idx, p.logg, p.k_eff,
+                static_cast<const float*>(tab32), static_cast<const double*>(tab64));
 }
 
 template <int D, int NTERM>
-static hipError_t launch_mfma_n(const SelectLaunch& p, hipStream_t st) {
+static hipError_t launch_mfma_n(const SelectLaunch& p, void* ws, hipStream_t st) {
   if (p.erf_lambda != nullptr) {
-    if (p.K <= 4) return launch_mfma_k<D, 4, NTERM, true>(p, st);
-    return launch_mfma_k<D, 8, NTERM, true>(p, st);
+    if (p.K <= 4) return launch_mfma_k<D, 4, NTERM, true>(p, ws, st);
+    return launch_mfma_k<D, 8, NTERM, true>(p, ws, st);
   }
-  if (p.K <= 4) return launch_mfma_k<D, 4, NTERM, false>(p, st);
-  if (p.K <= 8) return launch_mfma_k<D, 8, NTERM, false>(p, st);
-  if (p.K <= 16) return launch_mfma_k<D, 16, NTERM, false>(p, st);
-  return launch_mfma_k<D, 32, NTERM, false>(p, st);
+  if (p.K <= 4) return launch_mfma_k<D, 4, NTERM, false>(p, ws, st);
+  if (p.K <= 8) return launch_mfma_k<D, 8, NTERM, false>(p, ws, st);
+  if (p.K <= 16) return launch_mfma_k<D, 16, NTERM, false>(p, ws, st);
+  return launch_mfma_k<D, 32, NTERM, false>(p, ws, st);
 }
 
 template <int D>
-static hipError_t launch_mfma_d(const SelectLaunch& p, hipStream_t st) {
+static hipError_t launch_mfma_d(const SelectLaunch& p, void* ws, hipStream_t st) {
   const bool group_mean = p.share_group && p.Hq / p.Hkv > 1;
-  return group_mean ? launch_mfma_n<D, 3>(p, st) : launch_mfma_n<D, 1>(p, st);
+  return group_mean ? launch_mfma_n<D, 3>(p, ws, st) : launch_mfma_n<D, 1>(p, ws, st);
 }
 
-hipError_t launch_rows_select_mfma(const SelectLaunch& p, hipStream_t st) {
-  return p.d == 64 ? launch_mfma_d<64>(p, st) : launch_mfma_d<128>(p, st);
+hipError_t launch_rows_select_mfma(const SelectLaunch& p, void* ws, hipStream_t st) {
+  return p.d == 64 ? launch_mfma_d<64>(p, ws, st) : launch_mfma_d<128>(p, ws, st);
 }
 
 }  // namespace spa

@@ -250,7 +250,8 @@ hipError_t launch_decode_chunks(const SelectLaunch& p, void* ws, hipStream_t st)
 hipError_t launch_decode_fused_attn(const SelectLaunch& s, void* ws_sel, const AttnLaunch& a, void* ws_att,
                                     hipStream_t st);
 bool rows_select_mfma_supported(const SelectLaunch& p);
-hipError_t launch_rows_select_mfma(const SelectLaunch& p, hipStream_t st);
+hipError_t launch_rows_select_mfma(const SelectLaunch& p, void* ws, hipStream_t st);
+size_t rows_select_mfma_ws_bytes(const SelectLaunch& p);
 hipError_t launch_attn_fwd(const AttnLaunch& p, void* ws, hipStream_t st);
 bool attn_tile_fwd_supported(const AttnLaunch& p);
 hipError_t launch_attn_tile_fwd(const AttnLaunch& p, void* ws, hipStream_t st);

@@ -178,7 +178,10 @@ typedef struct spa_select_args {
  * position bias).  Score of candidate c for row i and selection head hs:
  *   s_c = q_hat . ktilde_c / sqrt(d)  [+ lambda_hs a_c erf((i - p_c)/(2 sigma_hs))]
  * q_hat = q_hs or the mean of the G query heads of kv head hs; ktilde = kbar
- * or W kbar.  Needs a workspace of sparse_workspace_bytes(SPA_OP_SCORE_SELECT).
+ * or W kbar.  Needs a workspace of sparse_workspace_bytes(SPA_OP_SCORE_SELECT):
+ * the one-row decode path keeps its chunk results there; many bf16 rows with
+ * the erf term keep per-head tables of the filter there (160 KiB per
+ * selection head); other row selections need none (0 bytes).
  */
 spa_status sparse_score_select(const spa_select_args *a, void *workspace, size_t ws_bytes,
                         spa_stream_t stream);
