@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256, 2) void attn_tile_dq_kernel(
   const int hl = lane >> 5, ql = lane & 31;
   const int G = Hq / Hkv;
   const int hgroups = G / NH;
-  const uint2 bxy = xcd_block_xy();                        // XCD-aware tile order
+  const uint2 bxy = xcd_block_xy_last_first();             // XCD-aware, longest row tiles first
   const int bz = static_cast<int>(bxy.y);
   const int bi = bz / (Hkv * hgroups);
   const int kvh = (bz / hgroups) % Hkv;

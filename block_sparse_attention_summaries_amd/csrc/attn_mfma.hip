@@ -531,8 +531,10 @@ __global__ __launch_bounds__(256, 2) void attn_tile_fwd_kernel(
   // the selected-block mode, where every tile of a head reads from the same
   // keys, and the window walk with the cells apart, where consecutive tiles'
   // windows overlap; the per-tile cell walk keeps the dispatch order
-  // (measured faster there)
-  const uint2 bxy = kMode == 1 ? make_uint2(blockIdx.x, blockIdx.y) : xcd_block_xy();
+  // (measured faster there).  The selected-block walk's tiles grow with the
+  // row (the union of the rows' selections), so it takes them last first.
+  const uint2 bxy = kMode == 1 ? make_uint2(blockIdx.x, blockIdx.y)
+                               : (kMode == 0 ? xcd_block_xy_last_first() : xcd_block_xy());
   const int bz = static_cast<int>(bxy.y);
   const int bi = bz / (Hkv * hgroups);
   const int kvh = (bz / hgroups) % Hkv;

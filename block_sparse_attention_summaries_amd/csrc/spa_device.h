@@ -98,6 +98,13 @@ __device__ __forceinline__ uint2 xcd_block_xy() {
   return make_uint2(l % gridDim.x, l / gridDim.x);
 }
 
+// As xcd_block_xy with x counted from the last: where x is a causal row tile
+// (work growing with x), every XCD starts on its longest tiles.
+__device__ __forceinline__ uint2 xcd_block_xy_last_first() {
+  const uint2 v = xcd_block_xy();
+  return make_uint2(gridDim.x - 1 - v.x, v.y);
+}
+
 // ------------------------------------------------------- fp8 summaries
 // OCP 8-bit floating point, E4M3 without infinities: sign, 4 exponent bits
 // biased by 7, 3 mantissa bits; exponent field 0 holds m/8 2^-6; S.1111.111
