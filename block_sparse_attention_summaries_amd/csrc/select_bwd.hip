@@ -139,18 +139,22 @@ __global__ __launch_bounds__(256, 2) void select_bwd_rows_kernel(
   constexpr int kDB = D / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, ql = lane & 31;
-  const int bh = blockIdx.y;
+  // dispatch order w runs the heads fastest and the row tiles from the last
+  // (the longest: a row's candidates grow with it) to the first
+  const uint32_t wid = blockIdx.y * gridDim.x + blockIdx.x;
+  const int bh = static_cast<int>(wid % gridDim.y);
+  const int rtile = static_cast<int>(gridDim.x - 1 - wid / gridDim.y);
   const int bi = bh / Hsel, hs = bh % Hsel;
   const int kvh = share_group ? hs : hs / G;
   // query source rows: q_hat = mean of heads hs * nh_in .. + nh_in - 1 of q
   const int h0 = hs * nh_in;
-  const int row = (blockIdx.x * 4 + wave) * 32 + ql;
+  const int row = (rtile * 4 + wave) * 32 + ql;
   const bool row_ok = row < nq;
   const int rowc = row_ok ? row : nq - 1;
   const int64_t pos = q_pos0 + rowc;
   const int lb = __builtin_ctz(b);          // b is a power of two
   const int ncand = row_ok ? static_cast<int>(pos >> lb) : 0;
-  const int row_end = (static_cast<int>(blockIdx.x) * 4 + 4) * 32;
+  const int row_end = (rtile * 4 + 4) * 32;
   const int last_row = (row_end < nq ? row_end : nq) - 1;
   const int wg_cand = static_cast<int>((q_pos0 + last_row) >> lb);
   const __bf16* kb = kbar + (static_cast<int64_t>(bi) * Hkv + kvh) * ccap * D;
