@@ -11,8 +11,9 @@
 // Per tile of 32 candidates, S^T = Kbar Q^T (candidates x queries) gives each
 // lane one query row and 16 candidates, so every lane keeps its row's running
 // top list and gate (max, sum exp) in registers; the two half-waves of a row
-// merge at the end.  The MFMA accumulates onto the bias, so a score costs no
-// arithmetic after it: scores run in units of 1/scale until the walk ends.
+// merge at the end.  The MFMA forms q.kbar from zero and one fma adds the
+// bias; scores run in units of 1/scale until the walk ends.  The grid runs
+// every head's longest rows first (row tiles from the last).
 //
 // Group selection scores with the mean query of the G heads, which is not a
 // bf16 value: it is formed in fp32 and split into three bf16 terms
@@ -20,10 +21,10 @@
 // fp32 dot product to within fp32 rounding.
 //
 // erf term: the bias reaches ~10, where fp32 cannot rank to 1e-6.  The scan
-// ranks fp32 scores (a branch-free erf approximation, read from a per-
-// workgroup table of row - cell b when the centres are the cell middles; a
-// tile whose every (row, cell) pair lies where the table is 1 skips it) in a
-// list twice the budget long, admitting only scores within the largest
+// ranks fp32 scores (the filter read from the head's table of row - cell b,
+// erf_table_kernel, when the centres are the cell middles, else a
+// branch-free erf approximation per score; a tile whose every (row, cell)
+// pair lies where the filter is 1 skips it) in a list twice the budget long, admitting only scores within the largest
 // possible band of the row's running K-th best (over both half-waves'
 // lists).  At the end, list entries within twice a proven error bound of the
 // fp32 K-th best are re-scored exactly (fp64 dot product and bias) and the
