@@ -8,7 +8,9 @@
 //
 // Three launches after the D_i pass:
 //   mark     one bit per (selection head, block, row) for "row selected block"
-//            (a bitmap, so the dk / dv pass can list a block's rows in order);
+//            (a bitmap, so the dk / dv pass can list a block's rows in order),
+//            built per 256-row slice in LDS and written whole
+//            (launch_mark_rows, shared with the routed-cell forward);
 //   dq / dg  like the forward tile kernel: a workgroup holds 32-row tiles of
 //            the heads sharing a selection, walks the ascending union of their
 //            key tiles, S^T = K Q^T and dP^T = V dO^T put one row per lane,
@@ -70,24 +72,8 @@ __device__ __forceinline__ void store_transposed8(uint16_t* dst, int pitch, uint
 
 }  // namespace
 
-// ---------------------------------------------------------------- mark
-// bits[((b Hsel + hs) nblk + c) nw + row / 32] bit row % 32 = row selected c.
-__global__ __launch_bounds__(256) void bwd_mark_kernel(const int32_t* __restrict__ idx, int nq, int64_t q_pos0,
-                                                       int b, int K, int64_t nblk, int nw, int64_t heads,
-                                                       uint32_t* __restrict__ bits) {
-  const int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (x >= heads * nq) return;
-  const int64_t bh = x / nq;
-  const int row = static_cast<int>(x % nq);
-  const int64_t ncand = (q_pos0 + row) / b;
-  const int32_t* ir = idx + x * K;
-  for (int t = 0; t < K; ++t) {
-    const int32_t c = ir[t];
-    if (c >= 0 && c < ncand && c < nblk)
-      atomicOr(&bits[(bh * nblk + c) * nw + row / 32], 1u << (row % 32));
-  }
-}
-
+// The mark bitmap: bits[((b Hsel + hs) nblk + c) nw + row / 32] bit row % 32
+// = row selected c (launch_mark_rows).
 // ---------------------------------------------------------------- dq / dg
 template <int D>
 struct DqSmem {
@@ -674,10 +660,9 @@ static hipError_t launch_tile_bwd_d(const BwdLaunch& p, const float* Dbuf, uint3
   const int64_t nblk = (a.L + a.b - 1) / a.b;
   const int nw = (a.nq + 31) / 32;
   const int64_t heads = static_cast<int64_t>(a.B) * a.Hsel;
-  hipError_t e = launch_zero_fill(bits, attn_tile_bwd_bitmap_bytes(p), st);
-  if (e != hipSuccess) return e;
-  e = launch(false, bwd_mark_kernel, dim3(static_cast<unsigned>((heads * a.nq + 255) / 256)), dim3(256), st,
-             a.idx, a.nq, a.q_pos0, a.b, a.K, nblk, nw, heads, bits);
+  // the readers of every block: the SAS candidate rule (blocks before the
+  // row's own), every bitmap word written (no clearing pass)
+  hipError_t e = launch_mark_rows(a.idx, a.nq, a.q_pos0, a.b, 0, 1, a.K, nblk, nw, heads, bits, st);
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;
   const int NH = G < 4 ? G : 4;

@@ -107,6 +107,17 @@ __global__ __launch_bounds__(256) void fwd_mark_kernel(const int32_t* __restrict
   }
 }
 
+// The bitmap of every (selection head, unit, row) for the candidate rule
+// prefix_mode: the routed-cell pipeline here, and the backward's readers of a
+// block (nblk <= kMaxKeyTiles).  Writes every word.
+hipError_t launch_mark_rows(const int32_t* idx, int nq, int64_t q_pos0, int b, int prefix_mode, int qblock, int K,
+                            int64_t nblk, int nw, int64_t heads, uint32_t* bits, hipStream_t st) {
+  if (nblk > kMaxKeyTiles) return hipErrorInvalidValue;
+  return launch(false, fwd_mark_kernel,
+                dim3(static_cast<unsigned>((nw + kMarkWords - 1) / kMarkWords), static_cast<unsigned>(heads)),
+                dim3(256), st, idx, nq, q_pos0, b, prefix_mode, qblock, K, nblk, nw, bits);
+}
+
 // Work units: a cell's selecting rows in tiles of 32 (row order), one unit
 // per wave.  Each selection head has a region of `cap` unit slots (at most
 // ncell + nq K / 32 units); its cells' units follow in cell order.
@@ -1077,9 +1088,8 @@ static hipError_t launch_cell_partials(const AttnLaunch& p, void* ws, hipStream_
                                        const float2** cell_ml) {
   const CellWs w = cell_ws(p, ws);
   const int64_t heads = static_cast<int64_t>(p.B) * p.Hsel;
-  hipError_t e = launch(false, fwd_mark_kernel,
-                        dim3(static_cast<unsigned>((w.nw + kMarkWords - 1) / kMarkWords), static_cast<unsigned>(heads)),
-                        dim3(256), st, p.idx, p.nq, p.q_pos0, p.b, p.prefix_mode, p.qblock, p.K, w.nblk, w.nw, w.bits);
+  hipError_t e = launch_mark_rows(p.idx, p.nq, p.q_pos0, p.b, p.prefix_mode, p.qblock, p.K, w.nblk, w.nw, heads,
+                                  w.bits, st);
   if (e != hipSuccess) return e;
   // cells that are candidates of some row: those before the last row's query block
   const int64_t ncell = num_candidates(p.q_pos0 + p.nq - 1, p.b, p.prefix_mode, p.qblock);

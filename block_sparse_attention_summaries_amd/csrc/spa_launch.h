@@ -262,6 +262,10 @@ bool attn_tile_bwd_supported(const BwdLaunch& p);
 size_t attn_tile_bwd_bitmap_bytes(const BwdLaunch& p);
 hipError_t launch_attn_tile_bwd(const BwdLaunch& p, const float* Dbuf, uint32_t* bits, hipStream_t st);
 hipError_t launch_zero_fill(void* ptr, size_t bytes, hipStream_t st);
+// Bitmap [heads, nblk, nw] of "row selected unit c" (bit row % 32 of word
+// row / 32), every word written; nblk <= 2048.
+hipError_t launch_mark_rows(const int32_t* idx, int nq, int64_t q_pos0, int b, int prefix_mode, int qblock, int K,
+                            int64_t nblk, int nw, int64_t heads, uint32_t* bits, hipStream_t st);
 
 // probe.hip: dependent-load chain over next[0 .. mask] (one lane), final
 // index to out[0].
