@@ -156,6 +156,8 @@ spa_status check_bwd(const spa_attn_args* a, const void* o, const void* dout, co
   SPA_REQUIRE(a->b <= 64, SPA_ERR_UNSUPPORTED, "the backward supports b <= 64");
   SPA_REQUIRE(o && dout && lse && dq && dk && dv && dg, SPA_ERR_INVALID_ARG,
               "o, dout, lse, dq, dk, dv and dg must be non-NULL");
+  SPA_REQUIRE(aligned16(o) && aligned16(dout) && aligned16(dq) && aligned16(dk) && aligned16(dv),
+              SPA_ERR_INVALID_ARG, "o, dout, dq, dk and dv must be 16-byte aligned");
   *p = spa::BwdLaunch{al, o, dout, lse, dq, dk, dv, dg};
   return SPA_OK;
 }

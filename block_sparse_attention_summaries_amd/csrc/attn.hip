@@ -481,16 +481,27 @@ __global__ __launch_bounds__(256) void rows_attn_fwd_kernel(
 }
 
 // ======================================================== rows: backward
+// D_i = do_i . o_i: D / kVec lanes per row, one 16-byte vector of o and of
+// dout each, summed over the row's lanes.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dout,
                                                       int64_t rows, float* __restrict__ Dbuf) {
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  if (r >= rows) return;
+  constexpr int kVec = Elem<T>::kVec;
+  constexpr int kLPR = D / kVec;            // lanes per row
+  constexpr int kRPB = 256 / kLPR;          // rows per workgroup
+  const int tid = threadIdx.x;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * kRPB + tid / kLPR;
+  const int cg = tid % kLPR;
   float a = 0.f;
-  for (int e = lane; e < D; e += kWave) a = fmaf(ld_f(o + r * D + e), ld_f(dout + r * D + e), a);
-  a = wave_sum(a);
-  if (lane == 0) Dbuf[r] = a;
+  if (r < rows) {
+    float x[kVec], y[kVec];
+    Elem<T>::unpack(*reinterpret_cast<const uint4*>(o + r * D + cg * kVec), x);
+    Elem<T>::unpack(*reinterpret_cast<const uint4*>(dout + r * D + cg * kVec), y);
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) a = fmaf(x[i], y[i], a);
+  }
+  a = group_sum<kLPR>(a);
+  if (r < rows && cg == 0) Dbuf[r] = a;
 }
 
 // dq and the block sums of dS for one segment of keys (one wave)
@@ -834,8 +845,9 @@ static hipError_t launch_bwd_t(const BwdLaunch& p, void* ws, hipStream_t st) {
   const AttnLaunch& a = p.a;
   float* Dbuf = static_cast<float*>(ws);
   const int64_t rows = static_cast<int64_t>(a.B) * a.Hq * a.nq;
-  hipError_t e = launch(false, bwd_pre_kernel<T, D>, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256),
-                        st, static_cast<const T*>(p.o), static_cast<const T*>(p.dout), rows, Dbuf);
+  constexpr int kPreRows = 256 / (D / Elem<T>::kVec);
+  hipError_t e = launch(false, bwd_pre_kernel<T, D>, dim3(static_cast<unsigned>((rows + kPreRows - 1) / kPreRows)),
+                        dim3(256), st, static_cast<const T*>(p.o), static_cast<const T*>(p.dout), rows, Dbuf);
   if (e != hipSuccess) return e;
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (attn_tile_bwd_supported(p)) {

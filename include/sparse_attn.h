@@ -451,6 +451,7 @@ spa_status sparse_forest_select(const spa_select_args *a, const void *k, int64_t
  * o and lse are the outputs of sparse_attn_fwd on the same arguments.
  * dq, dk, dv are written (not accumulated) in the input dtype; dg in fp32
  * (0 in padded slots; with logg NULL the gradient is taken at g = 1).
+ * o, dout, dq, dk and dv must be 16-byte aligned (SPA_ERR_INVALID_ARG).
  */
 spa_status sparse_attn_bwd(const spa_attn_args *a, const void *o, const void *dout,
                     const float *lse, void *dq, void *dk, void *dv, float *dg,
