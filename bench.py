@@ -13,7 +13,9 @@ One decode step = the hot path for one query token of one layer:
   same way for comparison (unfused_us_per_step), and so is the step over the
   same caches scattered into page pools (paged_us_per_step) and the step whose
   scorer reads fp8 (E4M3) summaries with per-block scales (fp8_summaries; on
-  closing steps the new block is also quantized).
+  closing steps the new block is also quantized).  The 32K decode workload
+runs as configured as well (decode_32k: K = 16, 1 % outlier keys, no
+projection).
 Steps rotate over 16 layers' KV caches (2.15 GB each) and 64 query vectors so
 that every step reads its summaries and selected K/V cold from HBM, as a
 multi-layer decoder would.  Inputs are resident in HBM before timing starts.
@@ -126,12 +128,19 @@ class DecodeWorkload:
         self.C = self.pos // b                      # historical candidates of the query
         self.K, self.b = cfg["K"], b
         g = torch.Generator(device="cuda")
-        self.k, self.v, self.w = [dev(x["k"])], [dev(x["v"])], [dev(x["proj_w"])]
+        proj = x.get("proj_w") is not None
+        self.k, self.v = [dev(x["k"])], [dev(x["v"])]
+        self.w = [dev(x["proj_w"]) if proj else None]
         for layer in range(1, n_layers):
             g.manual_seed(cfg["seed"] * 1000 + layer)
-            self.k.append(torch.randn((B, Hkv, self.L, d), generator=g, device="cuda").to(torch.bfloat16))
+            kf = torch.randn((B, Hkv, self.L, d), generator=g, device="cuda")
+            if cfg.get("outlier_p", 0.0) > 0.0:
+                # the same outlier rule as layer 0: whole keys scaled before rounding
+                hit = torch.rand((B, Hkv, self.L, 1), generator=g, device="cuda") < cfg["outlier_p"]
+                kf = torch.where(hit, kf * cfg["outlier_scale"], kf)
+            self.k.append(kf.to(torch.bfloat16))
             self.v.append(torch.randn((B, Hkv, self.L, d), generator=g, device="cuda").to(torch.bfloat16))
-            self.w.append(torch.randn((d, d), generator=g, device="cuda") / float(np.sqrt(d)))
+            self.w.append(torch.randn((d, d), generator=g, device="cuda") / float(np.sqrt(d)) if proj else None)
         self.q = dev(decode_queries(cfg, n_queries))  # [nQ, B, Hq, 1, d]
         self.kbar, self.mx, self.ce = [], [], []
         for layer in range(n_layers):
@@ -243,7 +252,8 @@ class DecodeWorkload:
     def scoring_bytes(self, fp8=False):
         c = self.cfg
         row = c["d"] + 4 if fp8 else c["d"] * 2          # codes + scale, or the bf16 summary
-        return c["B"] * c["Hkv"] * self.C * row + c["d"] * c["d"] * 4 + c["B"] * c["Hq"] * c["d"] * 2
+        w = c["d"] * c["d"] * 4 if self.w[0] is not None else 0
+        return c["B"] * c["Hkv"] * self.C * row + w + c["B"] * c["Hq"] * c["d"] * 2
 
 
 def run_decode(args):
@@ -408,6 +418,50 @@ def run_decode(args):
     return dict(wl=wl, cfg=cfg, x=x, total_ms=total_ms, unfused_ms=unfused_ms, paged_ms=paged_ms, k_ms=k_ms,
                 fp8_ms=fp8_ms, fp8_k_ms=fp8_k_ms, dist=dist, sweep=sweep, close_us=close_us,
                 summ_ms=summ_ms, summ_bytes=summ_bytes, hot_us=hot_us, floor_us=floor_us)
+
+
+def run_decode_32k(args, steps=256):
+    """The 32K decode workload as configured (32 q / 8 kv heads, K = 16, 1 %
+    outlier keys x8, log gate on, no projection) over 16 layers and rotating
+    queries: one-call steps replayed as one graph, µs per step, and the
+    selected K/V rate over the step kernel's event-timed duration."""
+    cfg = config("decode_32k")
+    wl = DecodeWorkload(cfg, args.layers, args.queries, make_inputs(cfg))
+    for s in range(8):
+        wl.decode(s % args.layers, s % args.queries)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        g.capture_begin()
+        for s in range(steps):
+            wl.decode(s % args.layers, s % args.queries)
+        g.capture_end()
+    torch.cuda.current_stream().wait_stream(stream)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del g
+    hip = HipEvents()
+    lib = ops.lib()
+    nk = len(STEP_KERNELS)
+    evs = [(ctypes.c_void_p * (2 * nk))(*[hip.create() for _ in range(2 * nk)]) for _ in range(64)]
+    for s in range(64):
+        lib.spa_profile_next_call(evs[s], nk)
+        wl.decode(s % args.layers, s % args.queries)
+    torch.cuda.synchronize()
+    kern = {n: round(float(np.mean([hip.elapsed(ev[2 * i], ev[2 * i + 1]) for ev in evs])) * 1e3, 3)
+            for i, (n, _) in enumerate(STEP_KERNELS)}
+    hip.destroy_all()
+    kv = wl.selected_kv_bytes()
+    return dict(us_per_step=round(us, 3), context=wl.L, candidates=wl.C, K=wl.K, kernels_us=kern,
+                selected_kv_bytes=kv, selected_kv_gbps=round(kv / (kern["step"] * 1e-6) / 1e9, 1))
 
 
 def run_decode_sweep(wl, args, stream, contexts=(32768, 65536, 131072, 262144, 524288), steps=64):
@@ -1057,6 +1111,8 @@ def main():
                               + sum(k["bytes"] for k in kern.values()) / (HBM_PEAK_GBPS * 1e3), 3),
         },
     }
+    # the 32K decode workload as configured (K = 16, outlier keys, no projection)
+    out["decode_32k"] = run_decode_32k(args)
     if not args.no_prefill:
         pf = run_prefill(3)
         out["prefill_tokens_per_s"] = round(pf["tokens_per_s"], 1)

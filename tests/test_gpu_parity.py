@@ -744,10 +744,13 @@ def test_select_erf_group_gate_parity(over):
 @pytest.mark.parametrize("over,shift", [
     (dict(n=1536, Hq=2, Hkv=2, seed=58), 0.25),                 # centres off c b + (b - 1) / 2
     (dict(n=1536, Hq=2, Hkv=2, sigma=3000.0, seed=59), None),  # x = 4 past the filter table
+    (dict(n=2048, Hq=2, Hkv=2, sigma=1000.0, seed=60), None),  # fp32 table too small, fp64 table used
 ])
 def test_select_erf_filter_per_score(over, shift):
-    """The erf filter evaluated per score instead of read from the table of
-    row - cell b (centres not at the cell middles, or a sigma too wide)."""
+    """The erf filter evaluated per score instead of read from the fp32 table
+    of row - cell b (centres not at the cell middles, or a sigma too wide);
+    with sigma = 1000 the exact re-score still reads the fp64 table, with
+    sigma = 3000 it evaluates the series."""
     cfg = config("prefill_cells", **over)
     _say(f"[select erf per score] {over} shift={shift}")
     x = make_inputs(cfg)
