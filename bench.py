@@ -931,8 +931,8 @@ def calibrate_copy():
 
 
 def _read_pmc_rows(path, counter):
-    """(kernel name, dispatch id, value in KiB) of every dispatch of a
-    rocprofv3 counter_collection.csv for one counter."""
+    """(kernel name, dispatch id, value in KiB, grid size) of every dispatch of
+    a rocprofv3 counter_collection.csv for one counter."""
     import csv
     out = []
     with open(path) as fh:
@@ -942,7 +942,8 @@ def _read_pmc_rows(path, counter):
             if cname != counter:
                 continue
             did = int(row.get("Dispatch_Id") or row.get("Dispatch-Id") or 0)
-            out.append((name, did, float(row.get("Counter_Value") or row.get("Counter-Value") or 0.0)))
+            grid = int(row.get("Grid_Size") or row.get("Grid-Size") or 0)
+            out.append((name, did, float(row.get("Counter_Value") or row.get("Counter-Value") or 0.0), grid))
     return out
 
 
@@ -951,22 +952,27 @@ def write_counters(fetch_csv, write_csv):
     (FETCH_SIZE, then WRITE_SIZE) of `bench.py --calibrate-copy ...`.  The
     calibration is the device copy whose WRITE_SIZE is nearest COPY_BYTES (the
     runs hold other copies of other sizes); a kernel's figures are the means
-    over its dispatches."""
+    over its dispatches at the 512K workload, the largest grid it was launched
+    with (the same run also times the 32K decode workload)."""
     fetch = _read_pmc_rows(fetch_csv, "FETCH_SIZE")
     write = _read_pmc_rows(write_csv, "WRITE_SIZE")
     copy_key = "copyBuffer"          # the runtime's device-to-device copy kernel
     kib = COPY_BYTES / 1024.0
-    cw = [(abs(v - kib), did, v) for n, did, v in write if copy_key in n]
+    cw = [(abs(v - kib), did, v) for n, did, v, _ in write if copy_key in n]
     if not cw:
         raise SystemExit("no copy kernel found in the counter files")
     _, cal_id, cal_w = min(cw)
-    cf = [v for n, did, v in fetch if copy_key in n and did == cal_id]
+    cf = [v for n, did, v, _ in fetch if copy_key in n and did == cal_id]
     if not cf:
         raise SystemExit("the calibration copy is missing from the FETCH_SIZE run")
 
     def mean_of(rows, key):
-        vals = [v for n, _, v in rows if key in n]
-        return sum(vals) / len(vals) if vals else None
+        sel = [(v, g) for n, _, v, g in rows if key in n]
+        if not sel:
+            return None
+        gmax = max(g for _, g in sel)
+        vals = [v for v, g in sel if g == gmax]
+        return sum(vals) / len(vals)
 
     out = {"source_sha": source_hash(), "copy_bytes": COPY_BYTES, "copy_dispatch": cal_id,
            "copy_fetch_kib": cf[0], "copy_write_kib": cal_w,
