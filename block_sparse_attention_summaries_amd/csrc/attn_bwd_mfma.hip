@@ -481,18 +481,24 @@ __global__ __launch_bounds__(256, 2) void attn_tile_dkdv_kernel(
     }
     __syncthreads();
     const int n = sm.nrows;
-    // gate of each selecting row for block c
+    // gate of each selecting row for block c: the row's entries are loaded
+    // eight at a time, then the slot holding c gives the log gate
     for (int x = tid; x < n; x += 256) {
       if (x < base) continue;
       const int r = sm.rows[x];
       float lg = 0.f;
       if (logg != nullptr) {
         const int64_t so = ((static_cast<int64_t>(bi) * Hsel + hs) * nq + r) * K;
-        for (int t = 0; t < K; ++t)
-          if (idx[so + t] == c) {
-            lg = logg[so + t];
-            break;
-          }
+        int slot = -1;
+        for (int t0 = 0; t0 < K && slot < 0; t0 += 8) {
+          int32_t iv[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) iv[t] = idx[so + (t0 + t < K ? t0 + t : 0)];
+#pragma unroll
+          for (int t = 7; t >= 0; --t)
+            if (t0 + t < K && iv[t] == c) slot = t0 + t;
+        }
+        if (slot >= 0) lg = logg[so + slot];
       }
       sm.bias[x] = lg;
     }
