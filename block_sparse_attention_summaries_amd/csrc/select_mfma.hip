@@ -24,9 +24,9 @@
 // ranks fp32 scores (the filter read from the head's table of row - cell b,
 // erf_table_kernel, when the centres are the cell middles, else a
 // branch-free erf approximation per score; a tile whose every (row, cell)
-// pair lies where the filter is 1 skips it) in a list twice the budget long, admitting only scores within the largest
-// possible band of the row's running K-th best (over both half-waves'
-// lists).  At the end, list entries within twice a proven error bound of the
+// pair lies where the filter is 1 skips it) in a list twice the budget long,
+// admitting only scores within the largest possible band of the row's
+// running K-th best (over both half-waves' lists).  At the end, list entries within twice a proven error bound of the
 // fp32 K-th best are re-scored exactly (fp64 dot product and bias) and the
 // exact top-K is taken from them; with the gate off, a row whose (K+1)-th
 // entry lies below that band keeps its first K entries as they are, and
