@@ -6,10 +6,10 @@
 // summaries read by the selector; "FreeSolo" review, "How it works": mean
 // key, centre position and max key norm of each cell.)
 //
-// HBM-bound streaming reduction: one 256-thread workgroup per block, 16-byte
-// coalesced loads (a block of b rows x d elements is one contiguous span),
-// fp64 column sums in registers, a cross-lane sum of squares per row and an
-// LDS reduction of the column sums.
+// HBM-bound streaming reduction: one wave per block, 16-byte coalesced loads
+// (a block of b rows x d elements is one contiguous span), fp64 column sums
+// in registers, a cross-lane sum of squares per row and lane exchanges for the
+// column sums.
 //
 // Optional fp8 summaries for the decode scorer (half the scoring bytes):
 // quantize_fp8_kernel turns block rows of kbar into OCP E4M3 codes with one
@@ -24,24 +24,41 @@ namespace spa {
 // With a page table, block c of (batch, kv head) is page table[batch * tstride
 // + c] of the pool [npages, Hkv, b, d]; an unmapped page (id outside the
 // pool) reads as zero keys.
+//
+// One wave per block, four per workgroup: kLPR lanes cover a key row with
+// 16-byte loads and a pass covers kRPW rows; the loads of kChunk passes are
+// in flight together.  A lane sums its column slice over its rows in fp64;
+// each row's sum of squares is added over the row's lanes and the largest is
+// kept (the norm is its square root, taken once: sqrt and the rounding to
+// fp32 are monotone); at the end the column sums are added across the row
+// groups by lane exchanges (every sum is exact in fp64 for key values within
+// 2^40 of each other, so the order does not change the mean).
+template <int M>
+__device__ __forceinline__ double xor_lanes_d(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint64_t r = (static_cast<uint64_t>(xor_lanes<M>(static_cast<uint32_t>(u >> 32))) << 32) |
+                     xor_lanes<M>(static_cast<uint32_t>(u));
+  return __longlong_as_double(static_cast<long long>(r));
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void block_summaries_kernel(
     const T* __restrict__ k, int Hkv, int64_t L, int b, int64_t first_block, int64_t num_blocks,
     int64_t ccap, T* __restrict__ kbar, float* __restrict__ max_norm, float* __restrict__ centre,
     const int32_t* __restrict__ table, int64_t tstride, int64_t npages) {
   constexpr int kVec = Elem<T>::kVec;
-  constexpr int kLanesPerRow = D / kVec;        // lanes covering one key row
-  constexpr int kRowsPerPass = 256 / kLanesPerRow;
-  static_assert(kLanesPerRow <= kWave, "row must fit in one wave");
+  constexpr int kLPR = D / kVec;                // lanes covering one key row
+  constexpr int kRPW = kWave / kLPR;            // rows per pass of a wave
+  constexpr int kChunk = 8;                     // passes with their loads in flight together
+  static_assert(kLPR <= kWave, "row must fit in one wave");
 
-  __shared__ double s_col[kRowsPerPass][D];
-  __shared__ float s_max[256 / kWave];
-
-  const int64_t c = first_block + blockIdx.x;
+  const int lane = threadIdx.x % kWave;
+  const int64_t blk = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  if (blk >= num_blocks) return;                // whole wave leaves
+  const int64_t c = first_block + blk;
   const int64_t bh = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int cg = tid % kLanesPerRow;            // which kVec columns
-  const int rg = tid / kLanesPerRow;            // which row within a pass
+  const int cg = lane % kLPR;                   // which kVec columns
+  const int rg = lane / kLPR;                   // which row of a pass
   const T* base = k + (bh * L + c * b) * D;
   int nrows = b;
   if (table != nullptr) {
@@ -54,44 +71,58 @@ __global__ __launch_bounds__(256) void block_summaries_kernel(
   double acc[kVec];
 #pragma unroll
   for (int i = 0; i < kVec; ++i) acc[i] = 0.0;
-  float best = 0.f;
-
-  for (int r = rg; r < nrows; r += kRowsPerPass) {
-    uint4 raw = *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(r) * D + cg * kVec);
-    float x[kVec];
-    Elem<T>::unpack(raw, x);
-    double ss = 0.0;
+  double best2 = 0.0;                           // largest row sum of squares
+  for (int r0 = 0; r0 < nrows; r0 += kRPW * kChunk) {
+    uint4 raw[kChunk];
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) {
-      double xd = static_cast<double>(x[i]);
-      acc[i] += xd;
-      ss = fma(xd, xd, ss);
+    for (int u = 0; u < kChunk; ++u) {
+      const int r = r0 + u * kRPW + rg;
+      raw[u] = r < nrows ? *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(r) * D + cg * kVec)
+                         : make_uint4(0u, 0u, 0u, 0u);
     }
-    // sum of squares over the lanes of this row (aligned groups of kLanesPerRow)
 #pragma unroll
-    for (int m = kLanesPerRow / 2; m > 0; m >>= 1) ss += __shfl_xor(ss, m, kWave);
-    float nrm = __double2float_rn(sqrt(ss));
-    best = fmaxf(best, nrm);
+    for (int u = 0; u < kChunk; ++u) {
+      if (r0 + u * kRPW >= nrows) break;        // the same for every lane: nrows is a multiple of kRPW
+      float x[kVec];
+      Elem<T>::unpack(raw[u], x);
+      double ss = 0.0;
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) {
+        const double xd = static_cast<double>(x[i]);
+        acc[i] += xd;
+        ss = fma(xd, xd, ss);
+      }
+      // sum of squares over the lanes of this row (aligned groups of kLPR)
+      if constexpr (kLPR >= 32) ss += xor_lanes_d<16>(ss);
+      if constexpr (kLPR >= 16) ss += xor_lanes_d<8>(ss);
+      ss += xor_lanes_d<4>(ss);
+      ss += xor_lanes_d<2>(ss);
+      ss += xor_lanes_d<1>(ss);
+      best2 = ss > best2 ? ss : best2;
+    }
   }
-  // rows not covered when b < kRowsPerPass leave acc = 0 and best = 0: harmless.
+  // column sums over the row groups
 #pragma unroll
-  for (int i = 0; i < kVec; ++i) s_col[rg][cg * kVec + i] = acc[i];
-  best = wave_max(best);
-  if ((tid % kWave) == 0) s_max[tid / kWave] = best;
-  __syncthreads();
+  for (int i = 0; i < kVec; ++i) {
+    if constexpr (kLPR <= 8) acc[i] += xor_lanes_d<8>(acc[i]);
+    if constexpr (kLPR <= 16) acc[i] += xor_lanes_d<16>(acc[i]);
+    acc[i] += xor_lanes_d<32>(acc[i]);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const double o = __shfl_xor(best2, m, kWave);
+    best2 = o > best2 ? o : best2;
+  }
+  const float best = __double2float_rn(sqrt(best2));
 
   const int64_t out = bh * ccap + c;
-  if (tid < D) {
-    double sum = 0.0;
-    const int groups = b < kRowsPerPass ? b : kRowsPerPass;
-    for (int g = 0; g < groups; ++g) sum += s_col[g][tid];
-    kbar[out * D + tid] = Elem<T>::from_double(sum * (1.0 / static_cast<double>(b)));
-  }
-  if (tid == 0) {
-    float m = s_max[0];
+  if (rg == 0) {
 #pragma unroll
-    for (int w = 1; w < 256 / kWave; ++w) m = fmaxf(m, s_max[w]);
-    max_norm[out] = m;
+    for (int i = 0; i < kVec; ++i)
+      kbar[out * D + cg * kVec + i] = Elem<T>::from_double(acc[i] * (1.0 / static_cast<double>(b)));
+  }
+  if (lane == 0) {
+    max_norm[out] = best;
     if (centre != nullptr && bh == 0)
       centre[c] = static_cast<float>(static_cast<double>(c) * b + 0.5 * (b - 1));
   }
@@ -99,7 +130,7 @@ __global__ __launch_bounds__(256) void block_summaries_kernel(
 
 template <typename T, int D>
 static hipError_t launch_summaries_t(const SummaryLaunch& p, hipStream_t st) {
-  dim3 grid(static_cast<unsigned>(p.num_blocks), static_cast<unsigned>(p.B * p.Hkv));
+  dim3 grid(static_cast<unsigned>((p.num_blocks + 3) / 4), static_cast<unsigned>(p.B * p.Hkv));
   return launch(true, block_summaries_kernel<T, D>, grid, dim3(256), st, static_cast<const T*>(p.k),
                 p.Hkv, p.L, p.b, p.first_block, p.num_blocks, p.ccap, static_cast<T*>(p.kbar),
                 p.max_norm, p.centre, p.pages.table, p.pages.tstride, p.pages.npages);
