@@ -100,6 +100,21 @@ def test_select_workspace_too_small():
     assert _select_status(a, FAKE, need - 1) == ops.SPA_ERR_WORKSPACE
 
 
+def test_select_rows_erf_workspace():
+    """Many bf16 rows with the erf term keep one fp32 and one fp64 filter table
+    per selection head in the workspace (160 KiB each); without the erf term
+    the row selection needs none."""
+    rows = dict(nq=16384, q_pos0=0, Hq=16, Hkv=16, d=64, ccap=512, b=32, prefix_mode=1, qblock=128,
+                share_group=0, K=4, gate=0, logg=None)
+    a = _sel(**rows, erf_lambda=FAKE, erf_sigma=FAKE)
+    need = ops.lib().sparse_workspace_bytes(ops.SPA_OP_SCORE_SELECT, ctypes.byref(a))
+    assert need == 16 * (8192 * 4 + 16384 * 8)
+    assert _select_status(a, None, 0) == ops.SPA_ERR_WORKSPACE
+    assert _select_status(a, FAKE, need - 256) == ops.SPA_ERR_WORKSPACE
+    plain = _sel(**rows)
+    assert ops.lib().sparse_workspace_bytes(ops.SPA_OP_SCORE_SELECT, ctypes.byref(plain)) == 0
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(v=None), ops.SPA_ERR_INVALID_ARG),
     (dict(o=None), ops.SPA_ERR_INVALID_ARG),
