@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     int Hq, int Hkv, int Hsel, int share_group, int64_t L, int64_t pos, int b, int K, int tpu,
     float* __restrict__ ws_acc, float2* __restrict__ ws_ml, const int32_t* __restrict__ table, int64_t tstride,
     int64_t npages, uint32_t* __restrict__ ctr, bf16_t* __restrict__ o, float* __restrict__ lse,
-    uint32_t* __restrict__ uflag) {
+    uint64_t* __restrict__ ws_u) {
   __shared__ int32_t s_idx[kStepMaxK];
   __shared__ float s_lg[kStepMaxK];
   __shared__ uint32_t s_last;
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   __syncthreads();
   if (s_last == 0u) return;
   // every workgroup of the head (and the whole scorer) is done with u
-  if (tid == 0) uflag[bh] = 0u;
+  if (ws_u != nullptr && tid < D) ws_u[static_cast<int64_t>(bh) * D + tid] = 0ull;
   combine_partials<bf16_t, D, HPW>(ws_acc, ws_ml, bh, bi, hs, G, Hq, share_group, ntiles, o, lse);
 }
 
@@ -392,7 +392,7 @@ static hipError_t launch_step_h(const SelectLaunch& s, const DecodeStepWs& w, co
                 static_cast<const float*>(w.scores), static_cast<const float2*>(w.ml), static_cast<const float*>(w.t2),
                 w.nch, s.max_cand, s.gate, s.idx, s.logg, s.k_eff, p.Hq, p.Hkv, p.Hsel, p.share_group, p.L,
                 p.q_pos0, p.b, p.K, tpu, acc, ml, p.pages.table, p.pages.tstride, p.pages.npages, w.ctr,
-                static_cast<bf16_t*>(p.o), p.lse, w.uflag);
+                static_cast<bf16_t*>(p.o), p.lse, w.u);
 }
 
 template <int D, int HPW>

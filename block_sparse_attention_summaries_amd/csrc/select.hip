@@ -234,41 +234,44 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(
 }
 
 // The one-call decode step's scorer.  With a projection, workgroup x = 0 of
-// each selection head forms u = W^T q_hat once and publishes it (agent-scope
-// stores, then a flag); the scoring workgroups x = 1 .. nch request their
-// chunk's summaries first and wait for the flag (a bounded wait: past it they
-// form u themselves, with the same arithmetic), so that 256 workgroups do not
-// all read W while the summaries stream in.  Without a projection every
-// scoring workgroup forms q_hat itself.  A scoring workgroup writes every
+// each selection head forms u = W^T q_hat once and publishes each element as
+// a 64-bit word with a ready mark beside its fp32 bits (agent-scope stores:
+// the mark travels in the same single-copy-atomic store as the value, so no
+// separate flag and no wait for the values' completion are needed); the
+// scoring workgroups x = 1 .. nch request their chunk's summaries first and
+// poll their elements of u until every one is marked (a bounded wait: past
+// it they form u themselves, with the same arithmetic), so that 256
+// workgroups do not all read W while the summaries stream in.  Where the
+// words do not fit their block (ws_u null), and without a projection, every
+// scoring workgroup forms u (q_hat) itself.  A scoring workgroup writes every
 // score of its chunk of 256 candidate blocks (-inf past the candidates), the
 // chunk's (max, sum exp) with the same arithmetic as decode_chunk_kernel, and
 // the largest score of each 64-block group (-inf for a group without
 // candidates): the K-th largest of these group maxima bounds the K-th largest
 // score from below for the selection in the attention kernel.  It also clears
 // the attention kernel's arrival counters (the kernel boundary publishes
-// them); the attention kernel clears the flags for the next call.
+// them); the attention kernel clears the marked words for the next call.
 constexpr int kUFlagSpin = 4096;
+constexpr uint64_t kUReady = 1ull << 32;   // ready mark beside each published element of u
 
 template <typename T, int D, bool F8>
 __global__ __launch_bounds__(256) void decode_score_kernel(
     const T* __restrict__ q, const void* __restrict__ kbar_v, const float* __restrict__ kscale,
     const float* __restrict__ proj_w, int Hq, int Hkv, int Hsel, int share_group, int64_t ccap, int64_t ncand,
     float* __restrict__ ws_scores, float2* __restrict__ ws_ml, float* __restrict__ ws_t2, int nchunks,
-    uint32_t* __restrict__ zero_ctr, int nzero, float* __restrict__ ws_u, uint32_t* __restrict__ uflag) {
+    uint32_t* __restrict__ zero_ctr, int nzero, uint64_t* __restrict__ ws_u) {
   __shared__ float s_score[kDecodeChunk];
   __shared__ float s_uv[D];
-  __shared__ uint32_t s_ok;
+  __shared__ uint32_t s_miss;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int bh = blockIdx.y;               // b * Hsel + hs
   const bool proj = proj_w != nullptr;
-  const int uw = proj ? 1 : 0;
-  if (proj && blockIdx.x == 0) {
+  const bool handoff = proj && ws_u != nullptr;
+  const int uw = handoff ? 1 : 0;
+  if (handoff && blockIdx.x == 0) {
     // u of this selection head, for the head's scoring workgroups
     form_u<T, D>(q, proj_w, Hq, Hkv, Hsel, share_group, bh, s_uv);
-    if (tid < D) publish_u32(ws_u + static_cast<int64_t>(bh) * D + tid, __float_as_uint(s_uv[tid]));
-    wait_published();
-    __syncthreads();
-    if (tid == 0) publish_u32(uflag + bh, 1u);
+    if (tid < D) publish_u64(ws_u + static_cast<int64_t>(bh) * D + tid, kUReady | __float_as_uint(s_uv[tid]));
     return;
   }
   const int chunk = blockIdx.x - uw;
@@ -277,23 +280,22 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
   const int64_t cbase = static_cast<int64_t>(chunk) * kDecodeChunk;
   ChunkLoads<T, D, F8> ld;
   ld.issue(kbar_v, kscale, Hkv, Hsel, share_group, Hq / Hkv, ccap, ncand, chunk, bh);
-  if (proj) {
-    if (tid == 0) {
-      uint32_t f = 0u;
+  if (handoff) {
+    if (tid == 0) s_miss = 0u;
+    __syncthreads();
+    if (tid < D) {
+      // each element of u carries its own ready mark: no separate flag to wait for
+      uint64_t w = 0ull;
       for (int it = 0; it < kUFlagSpin; ++it) {
-        f = __hip_atomic_load(uflag + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (f != 0u) break;
+        w = acquire_u64(ws_u + static_cast<int64_t>(bh) * D + tid);
+        if (__builtin_amdgcn_read_exec() == __builtin_amdgcn_ballot_w64((w & kUReady) != 0ull)) break;
         __builtin_amdgcn_s_sleep(2);
       }
-      s_ok = f;
+      if ((w & kUReady) == 0ull) s_miss = 1u;
+      s_uv[tid] = __uint_as_float(static_cast<uint32_t>(w));
     }
     __syncthreads();
-    if (s_ok != 0u) {
-      if (tid < D) s_uv[tid] = acquire_f32(ws_u + static_cast<int64_t>(bh) * D + tid);
-      lds_barrier();
-    } else {
-      form_u<T, D>(q, proj_w, Hq, Hkv, Hsel, share_group, bh, s_uv);
-    }
+    if (s_miss != 0u) form_u<T, D>(q, proj_w, Hq, Hkv, Hsel, share_group, bh, s_uv);
   } else {
     form_u<T, D>(q, proj_w, Hq, Hkv, Hsel, share_group, bh, s_uv);
   }
@@ -530,11 +532,10 @@ bool decode_fusable(const SelectLaunch& p) {
 template <typename T, int D>
 static hipError_t launch_step_scores_t(const SelectLaunch& p, const DecodeStepWs& w, hipStream_t st) {
   auto kern = p.kbar_scale != nullptr ? decode_score_kernel<T, D, true> : decode_score_kernel<T, D, false>;
-  const unsigned gx = static_cast<unsigned>(w.nch + (p.proj_w != nullptr ? 1 : 0));
+  const unsigned gx = static_cast<unsigned>(w.nch + (p.proj_w != nullptr && w.u != nullptr ? 1 : 0));
   return launch(false, kern, dim3(gx, static_cast<unsigned>(p.B * p.Hsel)), dim3(256), st,
                 static_cast<const T*>(p.q), p.kbar, p.kbar_scale, p.proj_w, p.Hq, p.Hkv, p.Hsel, p.share_group,
-                p.ccap, p.max_cand, w.scores, w.ml, w.t2, w.nch, w.ctr, static_cast<int>(p.B * p.Hsel), w.u,
-                w.uflag);
+                p.ccap, p.max_cand, w.scores, w.ml, w.t2, w.nch, w.ctr, static_cast<int>(p.B * p.Hsel), w.u);
 }
 
 hipError_t launch_decode_step_scores(const SelectLaunch& p, const DecodeStepWs& w, hipStream_t st) {

@@ -170,25 +170,27 @@ inline DecodeSelectWs decode_select_ws(const SelectLaunch& p, void* ws) {
 // The one-call decode step (bf16): a scorer kernel writes every candidate's
 // score, each chunk's (max, sum exp) and each 64-block group's largest score;
 // the attention kernel selects from them, attends and combines.  Workspace:
-// the ready flags of u [kStepMaxHeads] u32 at offset 0 (every call leaves
-// them zero: the attention kernel clears the ones the scorer set), scores
-// [heads, nch * 256] fp32, ml [heads, nch] float2, group maxima t2
-// [heads, nch * 4] fp32, u = W^T q_hat [heads, d] fp32, then the split-K
-// partials and one arrival counter per selection head
-// (decode_step_workspace_bytes).
+// the u block [kStepFlagBytes] at offset 0, then scores [heads, nch * 256]
+// fp32, ml [heads, nch] float2, group maxima t2 [heads, nch * 4] fp32, then
+// the split-K partials and one arrival counter per selection head
+// (decode_step_workspace_bytes).  The u block holds u = W^T q_hat as
+// [heads, d] 64-bit words (fp32 bits, ready mark in bit 32) when heads * d
+// fits (kStepUWords); it reads zero between calls (the attention kernel
+// clears the words the scorer set).  Its place and size do not depend on
+// the problem's shape, so stale words can never read as ready.
 constexpr int kStepMaxChunks = 64;   // candidates per row <= 16384
 constexpr int kStepMaxK = 64;
 constexpr int kStepMaxHeads = 4096;  // batch x selection heads
-constexpr size_t kStepFlagBytes = kStepMaxHeads * sizeof(uint32_t);   // 256-aligned
+constexpr size_t kStepFlagBytes = 16384;                       // 256-aligned
+constexpr int64_t kStepUWords = kStepFlagBytes / sizeof(uint64_t);
 struct DecodeStepWs {
   float* scores;
   float2* ml;
   float* t2;
-  float* u;
-  uint32_t* uflag;
+  uint64_t* u;   // null when heads * d > kStepUWords: every scorer forms u itself
   uint32_t* ctr;
   int nch;
-  size_t sel_bytes;   // bytes of the flags, scores, ml, t2 and u
+  size_t sel_bytes;   // bytes of the u block, scores, ml and t2
 };
 inline DecodeStepWs decode_step_ws(const SelectLaunch& p, void* ws_sel, void* ctr) {
   const int64_t nch = decode_num_chunks(p.max_cand > 0 ? p.max_cand : 1);
@@ -197,12 +199,12 @@ inline DecodeStepWs decode_step_ws(const SelectLaunch& p, void* ws_sel, void* ct
   const size_t sb = align256(heads * nch * 256 * sizeof(float));
   const size_t mb = align256(heads * nch * sizeof(float2));
   const size_t tb = align256(heads * nch * 4 * sizeof(float));
-  const size_t ub = align256(heads * p.d * sizeof(float));
   char* base = static_cast<char*>(ws_sel);
+  const bool u_fits = static_cast<int64_t>(heads) * p.d <= kStepUWords;
   return DecodeStepWs{reinterpret_cast<float*>(base + fb), reinterpret_cast<float2*>(base + fb + sb),
-                      reinterpret_cast<float*>(base + fb + sb + mb), reinterpret_cast<float*>(base + fb + sb + mb + tb),
-                      reinterpret_cast<uint32_t*>(base), static_cast<uint32_t*>(ctr), static_cast<int>(nch),
-                      fb + sb + mb + tb + ub};
+                      reinterpret_cast<float*>(base + fb + sb + mb),
+                      u_fits ? reinterpret_cast<uint64_t*>(base) : nullptr, static_cast<uint32_t*>(ctr),
+                      static_cast<int>(nch), fb + sb + mb + tb};
 }
 hipError_t launch_decode_step_scores(const SelectLaunch& p, const DecodeStepWs& w, hipStream_t st);
 size_t decode_step_select_bytes(const SelectLaunch& p);

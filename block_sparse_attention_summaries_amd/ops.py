@@ -175,7 +175,7 @@ def _contig(*ts):
             raise ValueError("tensors passed to libsparse_attn must be contiguous")
 
 
-SPA_DECODE_FLAG_BYTES = 16384     # the decode step's ready flags at the workspace's start
+SPA_DECODE_FLAG_BYTES = 16384     # the decode step's ready-marked words at the workspace's start
 
 
 class Workspace:

@@ -288,11 +288,12 @@ typedef struct spa_decode_args {
  * tile and publishes a split-K partial, the head's last workgroup combining
  * them; otherwise the two calls' kernels run in sequence.  Needs a workspace
  * of sparse_workspace_bytes(SPA_OP_DECODE_STEP, spa_decode_args*),
- * caller-owned.  Its first SPA_DECODE_FLAG_BYTES bytes hold per-head ready
- * flags that must read zero on the first decode step with that workspace (a
- * zero-filled allocation, or sparse_workspace_init); every decode step leaves
- * them zero again, but other entry points given the same workspace may not,
- * so clear them before going back to decode steps.  The rest of the
+ * caller-owned.  Its first SPA_DECODE_FLAG_BYTES bytes hold the scorer's
+ * query u, each element marked ready when published; they must read zero on
+ * the first decode step with that workspace (a zero-filled allocation, or
+ * sparse_workspace_init); every decode step leaves them zero again, but other
+ * entry points given the same workspace may not, so clear them before going
+ * back to decode steps.  The rest of the
  * workspace's contents on entry are ignored.  Errors: as the two calls, plus
  * SPA_ERR_INVALID_ARG when select and attn disagree.
  */
@@ -316,7 +317,7 @@ spa_status sparse_decode_step(const spa_decode_args *a, void *workspace, size_t 
  *    capture.
  *  - Every call on one GPU shares that GPU's array, which keeps the last
  *    call's contents: the array starts zero when the library loads and each
- *    call leaves its ready flags (the first SPA_DECODE_FLAG_BYTES bytes) zero
+ *    call leaves its ready-marked words (the first SPA_DECODE_FLAG_BYTES bytes) zero
  *    again, as the next call needs them.  Calls that overlap in time on one
  *    GPU, on any streams, race.  Serialise them.
  */

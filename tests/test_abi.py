@@ -209,14 +209,14 @@ def test_decode_step_validation_and_workspace():
     need = lib.sparse_workspace_bytes(ops.SPA_OP_DECODE_STEP, ctypes.byref(da))
     need_sel = lib.sparse_workspace_bytes(ops.SPA_OP_SCORE_SELECT, ctypes.byref(sel))
     need_att = lib.sparse_workspace_bytes(ops.SPA_OP_ATTN_FWD, ctypes.byref(att))
-    # the one-call scorer's ready flags (4096 u32 at offset 0), scores
-    # [8 heads, 2 chunks, 256] fp32, chunk (max, sum exp), group maxima and u
-    # [8, 128] fp32 (larger than the two-call records), then split-K partials
-    # and one arrival counter per selection head
+    # the one-call scorer's u block (16 KiB at offset 0, u [8, 128] as
+    # ready-marked 64-bit words), scores [8 heads, 2 chunks, 256] fp32, chunk
+    # (max, sum exp) and group maxima, or the two-call selection's scratch
+    # after the same block, whichever is larger; then split-K partials and one
+    # arrival counter per selection head
     r256 = lambda x: 256 * ((x + 255) // 256)
-    scorer = 4096 * 4 + r256(8 * 2 * 256 * 4) + r256(8 * 2 * 8) + r256(8 * 2 * 4 * 4) + r256(8 * 128 * 4)
-    assert scorer > need_sel
-    assert need == scorer + need_att + 256
+    scorer = 16384 + r256(8 * 2 * 256 * 4) + r256(8 * 2 * 8) + r256(8 * 2 * 4 * 4)
+    assert need == r256(max(scorer, 16384 + need_sel)) + need_att + 256
     assert lib.sparse_decode_step(ctypes.byref(da), FAKE, need - 1, None) == ops.SPA_ERR_WORKSPACE
 
     def status(s, a):

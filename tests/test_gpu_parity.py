@@ -187,6 +187,8 @@ def _check_decode_chain(cfg, r, c):
     ("decode_32k", dict(n=256, K=16, seed=12)),           # K > candidates -> K_eff = 4
     ("decode_32k", dict(n=0, t=40, seed=13)),             # first block: no candidates
     ("decode_512k", dict(n=65536, seed=14)),
+    ("decode_512k", dict(n=16384, B=2, seed=18)),         # u words fill the 16 KiB block exactly
+    ("decode_512k", dict(n=16384, share_group=False, seed=19)),   # they do not fit: scorers form u
     ("decode_32k", dict(d=64, dtype="f32", n=4096, Hq=8, Hkv=4, proj=True, seed=15)),
 ])
 def test_decode_step_parity(name, over):
@@ -651,7 +653,7 @@ def test_one_workspace_shared_across_shapes_and_entry_points():
 
 def test_decode_step_workspace_alternating_paths():
     """One workspace serves one-call decode steps on the fused path (bf16, a
-    projection, u formed once per head and handed over through a flag block
+    projection, u formed once per head and handed over as ready-marked words
     at the workspace's start) and on the two-call path (fp32) in turn, with
     different shapes and queries: neither path may disturb the other's state
     (every step checked against the oracle).  Between steps a plain selection
@@ -661,7 +663,8 @@ def test_decode_step_workspace_alternating_paths():
     cases = [("decode_512k", dict(n=65536, seed=61)), ("tiny_decode", dict(t=40, seed=62)),
              ("decode_512k", dict(n=131072, seed=63)), ("decode_32k", dict(d=64, dtype="f32", n=4096, Hq=8, Hkv=4,
                                                                          proj=True, seed=64)),
-             ("decode_512k", dict(n=65536, seed=65)), ("decode_32k", dict(n=4096, seed=66))]
+             ("decode_512k", dict(n=65536, seed=65)), ("decode_512k", dict(n=16384, share_group=False, seed=67)),
+             ("decode_512k", dict(n=16384, B=2, seed=68)), ("decode_32k", dict(n=4096, seed=66))]
     for name, over in cases:
         cfg = config(name, **over)
         _say(f"[decode alternating paths] {name} {over}")
