@@ -104,15 +104,33 @@ __device__ __forceinline__ void wave_emit(M m, const float* s_sc, uint64_t* s_li
   }
 }
 
+__device__ __forceinline__ int ascending_place(const int32_t* win, int kk, int32_t cw);
+
+// What step_select leaves for its workgroup: the block of the workgroup's
+// slot and its log gate, the slot's place in ascending block order, and the
+// LDS state step_order reads.
+struct StepPick {
+  int32_t c;            // the slot's block, -1 for an empty slot
+  float bias;           // its log gate (0 with the gate off)
+  int at;               // its place among the K slots in ascending block order
+  const int32_t* win;   // the winners by score rank (LDS), INT32_MAX from kk on
+  const float* sc;      // every candidate's score (LDS)
+  float lse;            // LSE over every candidate
+  int kk;
+};
+
 // Exact top-kk of one selection head: scores [nch * 256] (-inf past the
 // candidates; candidate x at x), the chunks' (max, sum exp) and the groups'
-// maxima gmax [nch * 4].  Leaves in s_idx[0 .. kk) the selected blocks in
-// ascending order and in s_lg their log gates (score - LSE over every
-// candidate; 0 with the gate off), -1 / 0 in slots kk .. K - 1.
+// maxima gmax [nch * 4].  Slot `unit` takes the winner of score rank unit
+// (slots kk .. K - 1 are empty); its partial goes to the slot's place in
+// ascending block order, the count of winners below it, so that the split-K
+// partials lie in ascending block order whichever workgroup made them.  The
+// order of every slot (the selection's output) is left to step_order, which
+// only the workgroup that writes the output needs.
 template <int NCH>
 __device__ __forceinline__ void step_select(const float* __restrict__ scores, const float2* __restrict__ cml,
                                             const float* __restrict__ gmax, int nch, int64_t ncand, int K,
-                                            int gate, int32_t* s_idx, float* s_lg) {
+                                            int unit, StepPick& pick) {
   using mask_t = typename std::conditional<(NCH > 32), uint64_t, uint32_t>::type;
   constexpr int kBits = NCH >= 64 ? 7 : NCH >= 32 ? 6 : NCH >= 16 ? 5 : 3;   // bits of a lane's count
   constexpr int kSurvMax = 256;        // one survivor per thread in the ranking
@@ -269,23 +287,46 @@ __device__ __forceinline__ void step_select(const float* __restrict__ scores, co
     if (rank < kk) s_win[rank] = static_cast<int32_t>(~static_cast<uint32_t>(key));
   }
   __syncthreads();
-  if (wave == 0 && lane < K) {
-    // the winners in ascending block order: each one's place is the count
-    // of winners below it
-    if (lane < kk) {
-      const int32_t cw = s_win[lane];
-      int at = 0;
-      const int4* wp = reinterpret_cast<const int4*>(s_win);
+  pick.win = s_win;
+  pick.sc = s_sc;
+  pick.lse = s_lse;
+  pick.kk = kk;
+  pick.c = -1;
+  pick.bias = 0.f;
+  pick.at = unit;
+  if (unit < kk) {
+    pick.c = s_win[unit];
+    pick.bias = s_sc[pick.c] - s_lse;
+    pick.at = ascending_place(s_win, kk, pick.c);
+  }
+}
+
+// A winner's place in ascending block order: the count of winners below it
+// (winners are distinct blocks; the entries from kk on are INT32_MAX).
+__device__ __forceinline__ int ascending_place(const int32_t* win, int kk, int32_t cw) {
+  int at = 0;
+  const int4* wp = reinterpret_cast<const int4*>(win);
 #pragma unroll 4
-      for (int i = 0; i < (kk + 3) / 4; ++i) {
-        const int4 w = wp[i];
-        at += (w.x < cw ? 1 : 0) + (w.y < cw ? 1 : 0) + (w.z < cw ? 1 : 0) + (w.w < cw ? 1 : 0);
-      }
+  for (int i = 0; i < (kk + 3) / 4; ++i) {
+    const int4 w = wp[i];
+    at += (w.x < cw ? 1 : 0) + (w.y < cw ? 1 : 0) + (w.z < cw ? 1 : 0) + (w.w < cw ? 1 : 0);
+  }
+  return at;
+}
+
+// Every slot of the selection in ascending block order into s_idx / s_lg
+// (log gates; 0 with the gate off), -1 / 0 in slots kk .. K - 1.
+__device__ __forceinline__ void step_order(const StepPick& pk, int K, int gate, int32_t* s_idx, float* s_lg) {
+  const int tid = threadIdx.x;
+  if (tid < K) {
+    if (tid < pk.kk) {
+      const int32_t cw = pk.win[tid];
+      const int at = ascending_place(pk.win, pk.kk, cw);
       s_idx[at] = cw;
-      s_lg[at] = gate ? s_sc[cw] - s_lse : 0.f;
+      s_lg[at] = gate ? pk.sc[cw] - pk.lse : 0.f;
     } else {
-      s_idx[lane] = -1;
-      s_lg[lane] = 0.f;
+      s_idx[tid] = -1;
+      s_lg[tid] = 0.f;
     }
   }
   __syncthreads();
@@ -318,22 +359,17 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   int ntok = 0;
   float bias = 0.f;
   const int64_t c0 = pos / b;
+  StepPick pk{};
+  int place = tile;   // where the tile's partial goes: slots in ascending block order, then the current block
   if (unit < K) {
     step_select<NCH>(scores + static_cast<int64_t>(bh) * nch * kDecodeChunk, cml + static_cast<int64_t>(bh) * nch,
-                     gmax + static_cast<int64_t>(bh) * nch * 4, nch, ncand, K, gate, s_idx, s_lg);
-    if (unit == 0 && sub == 0) {
-      const int64_t o0 = static_cast<int64_t>(bh) * K;      // one query row
-      for (int x = tid; x < K; x += 256) {
-        idx[o0 + x] = s_idx[x];
-        if (logg != nullptr) logg[o0 + x] = s_lg[x];
-      }
-      if (tid == 0 && k_eff != nullptr) k_eff[bh] = static_cast<int32_t>(ncand < K ? ncand : K);
-    }
-    const int32_t c = s_idx[unit];
+                     gmax + static_cast<int64_t>(bh) * nch * 4, nch, ncand, K, unit, pk);
+    place = pk.at * tpu + sub;
+    const int32_t c = pk.c;
     if (c >= 0 && c < c0) {
       start = static_cast<int64_t>(c) * b + sub * kTileTok;
       ntok = b - sub * kTileTok < kTileTok ? b - sub * kTileTok : kTileTok;
-      bias = s_lg[unit];
+      bias = gate ? pk.bias : 0.f;
     }
   } else {
     start = c0 * b + sub * kTileTok;
@@ -342,7 +378,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     ntok = n <= 0 ? 0 : (n < cap ? static_cast<int>(n) : cap);
   }
 
-  const int64_t obase = (static_cast<int64_t>(bh) * ntiles + tile) * HPW;
+  const int64_t obase = (static_cast<int64_t>(bh) * ntiles + place) * HPW;
   int64_t off = 0;
   if (ntok > 0) {
     if (table == nullptr) {
@@ -371,6 +407,16 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   wait_published();
   __syncthreads();
   if (tid == 0) s_last = count_arrival(ctr + bh) == static_cast<uint32_t>(ntiles - 1) ? 1u : 0u;
+  if (unit == 0 && sub == 0) {
+    // the selection's output, off the tiles' path
+    step_order(pk, K, gate, s_idx, s_lg);
+    const int64_t o0 = static_cast<int64_t>(bh) * K;      // one query row
+    for (int x = tid; x < K; x += 256) {
+      idx[o0 + x] = s_idx[x];
+      if (logg != nullptr) logg[o0 + x] = s_lg[x];
+    }
+    if (tid == 0 && k_eff != nullptr) k_eff[bh] = static_cast<int32_t>(ncand < K ? ncand : K);
+  }
   __syncthreads();
   if (s_last == 0u) return;
   // every workgroup of the head (and the whole scorer) is done with u
