@@ -210,17 +210,17 @@ spa_status check_decode(const spa_decode_args* d, spa::SelectLaunch* sp, spa::At
   return SPA_OK;
 }
 
-// Selection part of the one-call step's workspace.  The flag block of the
+// Selection part of the one-call step's workspace.  The u block of the
 // one-call scorer sits at offset 0 on both paths: the two-call fallback keeps
 // its scratch after it, so a workspace can serve steps of either path in turn
-// without disturbing the flags (zero between calls).
+// without disturbing the u block's ready-marked words (zero between calls).
 size_t decode_sel_bytes(const spa::SelectLaunch& sp) {
   const size_t two = spa::kStepFlagBytes + spa::select_workspace_bytes(sp);
   const size_t one = spa::decode_fusable(sp) ? spa::decode_step_select_bytes(sp) : 0;
   return spa::align256(two > one ? two : one);
 }
 
-static_assert(SPA_DECODE_FLAG_BYTES == spa::kStepFlagBytes, "the decode step's flag block");
+static_assert(SPA_DECODE_FLAG_BYTES == spa::kStepFlagBytes, "the decode step's u block");
 
 hipError_t run_decode_step(const spa::SelectLaunch& sp, const spa::AttnLaunch& ap, void* ws, hipStream_t s) {
   char* base = static_cast<char*>(ws);

@@ -181,7 +181,7 @@ SPA_DECODE_FLAG_BYTES = 16384     # the decode step's ready-marked words at the 
 class Workspace:
     """A zero-initialised device buffer reused across calls (grown on demand).
     Calls that share one Workspace must not overlap in time.  A decode step
-    after another entry point's call clears the step's flag block first."""
+    after another entry point's call clears the step's u block (ready-marked words) first."""
 
     def __init__(self, device="cuda"):
         self.device = device

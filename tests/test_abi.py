@@ -301,7 +301,7 @@ def test_load_chase_probe_rejects_invalid_arguments():
 
 def test_workspace_clears_the_decode_flags_after_other_calls():
     """A Workspace handed to another entry point and then to a decode step
-    has the step's flag block zeroed first (host buffer, no GPU)."""
+    has the step's u block (ready-marked words) zeroed first (host buffer, no GPU)."""
     ws = ops.Workspace(device="cpu")
     buf, _ = ws.get(1 << 16, ops.SPA_OP_SCORE_SELECT)
     buf.fill_(7)
